@@ -1,0 +1,267 @@
+"""Plain float64 CPU oracle for proxy-query token eviction: score -> select -> compact.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this module: only the test
+suite, the smoke check and the benchmark's CPU-baseline leg use it. It shares no code with the
+HIP library; both sides read the same stored input bytes, produced by ``workloads``.
+
+Sources (page titles as they appear on the pages):
+  [TE]  "Practical Online KV Cache Compaction for LLM Agents: An Empirical Study"
+        (agifrontier tutorial page), section on the design space, the Token Eviction score
+        equation: s_j(Q, K) = ((1/q) * sum_i alpha_ij^2)^(1/2) over q proxy queries, then keep
+        the top-m positions with their original keys and values.
+  [ACT] "ActKV" analysis page (zhichai.net topic), paragraph on the paged-memory system
+        component: attention recovered block by block as exp(logit - LSE) with the LSE a
+        byproduct of paged attention; conflict-free slot plan where the tail X logical blocks
+        become the target region, kept entries outside it are paired one-to-one with holes
+        inside it, all pairs are copied in one parallel pass and the emptied blocks go back
+        to the scheduler.
+
+Readings where the pages leave a step open (each is listed with its reason in the design notes):
+  * alpha_ij = softmax_j(c * q_i . k_j + b_j) with c = 1/sqrt(d) unless the caller gives another
+    scale; b is an optional per-key additive logit bias (0 when absent).
+  * GQA: the G*q proxy rows of the G query heads that share a KV head are stacked and the mean
+    in the score runs over all R = G*q rows.
+  * A supplied LSE is used as given (natural log, one value per proxy row).
+  * Ties in the score go to the lower position; the kept list is returned ascending.
+  * Paged: N = ceil(n/B), X = ceil(m/B), window W = [(N-X)*B, (N-X)*B + m); sources are kept
+    positions outside W, holes are positions of W that are not kept, both ascending, the i-th
+    source fills the i-th hole. The new block table is old[N-X .. N), entries X .. N-1 become
+    -1, and old[0 .. N-X) are freed, i.e. ceil(n/B) - ceil(m/B) blocks.
+
+Every function below has pins in the CPU test suite (worked examples, closed forms, brute
+force and invariants); none is "parity unpinned".
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------- inputs
+
+def widen(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored values -> float64, exactly. bf16 arrives as 16-bit patterns."""
+    if dtype == "bf16":
+        u32 = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16
+        return u32.view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+# ----------------------------------------------------------------------------- scoring
+
+def logits(Q: np.ndarray, K: np.ndarray, scale: float, bias: np.ndarray | None = None) -> np.ndarray:
+    """l_rj = c * (q_r . k_j) + b_j for proxy rows Q [R][d] and keys K [n][d] ([TE] alpha's argument)."""
+    L = scale * (Q @ K.T)
+    if bias is not None:
+        L = L + bias[None, :]
+    return L
+
+
+def lse(Q: np.ndarray, K: np.ndarray, scale: float, bias: np.ndarray | None = None,
+        row_chunk: int = 256) -> np.ndarray:
+    """Per proxy row, LSE_r = ln sum_j exp(l_rj) over the same n keys ([ACT] softmax normaliser).
+
+    Written as max + ln(sum exp(l - max)) so it does not overflow; rows are independent, so the
+    logits are formed a slab of rows at a time only to bound memory.
+    """
+    R = Q.shape[0]
+    out = np.empty(R, dtype=np.float64)
+    for r0 in range(0, R, row_chunk):
+        L = logits(Q[r0:r0 + row_chunk], K, scale, bias)
+        mx = L.max(axis=1)
+        out[r0:r0 + row_chunk] = mx + np.log(np.exp(L - mx[:, None]).sum(axis=1))
+    return out
+
+
+def te_scores(Q: np.ndarray, K: np.ndarray, scale: float, lse_rows: np.ndarray | None = None,
+              bias: np.ndarray | None = None, row_chunk: int = 256) -> np.ndarray:
+    """Token Eviction score of every key ([TE] score equation).
+
+    alpha_rj = exp(l_rj - LSE_r) (the softmax weight, [ACT] LSE recovery),
+    s_j = sqrt((1/R) * sum_r alpha_rj^2). The row sum is accumulated a slab of rows at a time.
+    """
+    R, n = Q.shape[0], K.shape[0]
+    if lse_rows is None:
+        lse_rows = lse(Q, K, scale, bias, row_chunk)
+    lse_rows = np.asarray(lse_rows, dtype=np.float64)
+    acc = np.zeros(n, dtype=np.float64)
+    for r0 in range(0, R, row_chunk):
+        L = logits(Q[r0:r0 + row_chunk], K, scale, bias)
+        alpha = np.exp(L - lse_rows[r0:r0 + row_chunk, None])
+        acc += (alpha * alpha).sum(axis=0)
+    return np.sqrt(acc / R)
+
+
+# ----------------------------------------------------------------------------- selection
+
+def select_topm(s: np.ndarray, m: int) -> np.ndarray:
+    """Top-m positions by score, ties to the lower position, returned ascending ([TE] top-m)."""
+    n = s.shape[0]
+    if not 0 <= m <= n:
+        raise ValueError("need 0 <= m <= n")
+    order = np.lexsort((np.arange(n), -np.asarray(s, dtype=np.float64)))  # s desc, then j asc
+    return np.sort(order[:m]).astype(np.int64)
+
+
+# ----------------------------------------------------------------------------- compaction
+
+def gather(X: np.ndarray, kept: np.ndarray) -> np.ndarray:
+    """Contiguous compaction: row r of the output is the stored row kept[r] ([TE] keep original K, V)."""
+    return np.ascontiguousarray(X[np.asarray(kept, dtype=np.int64)])
+
+
+@dataclass
+class PagedPlan:
+    n: int
+    m: int
+    B: int
+    N: int            # logical blocks before compaction
+    X: int            # logical blocks kept (the target region)
+    start: int        # first logical slot of the window
+    src: list         # kept positions outside the window, ascending
+    dst: list         # holes of the window, ascending
+
+    @property
+    def freed_count(self) -> int:
+        return self.N - self.X
+
+
+def paged_plan(n: int, m: int, B: int, kept) -> PagedPlan:
+    """Conflict-free slot plan for one (sequence, head) ([ACT] paged compaction paragraph).
+
+    Built with plain sets, independently of how a parallel planner would locate pairs.
+    """
+    if not 0 <= m <= n:
+        raise ValueError("need 0 <= m <= n")
+    N = -(-n // B)
+    X = -(-m // B)
+    start = (N - X) * B
+    kept_set = set(int(j) for j in kept)
+    if len(kept_set) != m or any(j < 0 or j >= n for j in kept_set):
+        raise ValueError("kept must hold m distinct positions in [0, n)")
+    window = set(range(start, start + m))
+    src = sorted(kept_set - window)
+    dst = sorted(window - kept_set)
+    if len(src) != len(dst):
+        raise AssertionError("plan is unbalanced")
+    if set(src) & set(dst):
+        raise AssertionError("a slot is both read and written")
+    return PagedPlan(n, m, B, N, X, start, src, dst)
+
+
+def apply_paged_copy(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray, h: int,
+                     plan: PagedPlan) -> None:
+    """Copy K and V rows of head h from each source slot to its paired hole, in place.
+
+    Pools are [num_blocks][B][H][d]; table_row maps logical block -> physical block. Sources
+    are never holes and holes are never read, so the order of the copies does not matter.
+    """
+    B = plan.B
+    for a, b in zip(plan.src, plan.dst):
+        pa, sa = int(table_row[a // B]), a % B
+        pb, sb = int(table_row[b // B]), b % B
+        k_pool[pb, sb, h, :] = k_pool[pa, sa, h, :]
+        v_pool[pb, sb, h, :] = v_pool[pa, sa, h, :]
+
+
+def table_update(table_row: np.ndarray, n: int, m: int, B: int) -> tuple[np.ndarray, np.ndarray]:
+    """New block table and the freed physical blocks (logical order) for one sequence."""
+    N = -(-n // B)
+    X = -(-m // B)
+    old = np.asarray(table_row, dtype=np.int32)
+    new = old.copy()
+    new[:X] = old[N - X:N]
+    new[X:N] = -1
+    freed = old[:N - X].copy()
+    return new, freed
+
+
+# ----------------------------------------------------------------------------- whole batches
+
+def unit_rows(Q: np.ndarray, s: int, h: int, G: int) -> np.ndarray:
+    """The R = G*q proxy rows of KV head h: query heads h*G .. h*G+G-1 of Q [S][H*G][q][d]."""
+    sub = Q[s, h * G:(h + 1) * G]
+    return sub.reshape(-1, sub.shape[-1])
+
+
+def unit_lse(Q, s, h, G, lse_all) -> np.ndarray | None:
+    if lse_all is None:
+        return None
+    return np.asarray(lse_all[s, h * G:(h + 1) * G], dtype=np.float64).reshape(-1)
+
+
+def score_unit(Qs, Ks, dtype, scale, bias=None, lse_rows=None):
+    """Scores of one unit from stored rows/keys (widened exactly to float64)."""
+    Qd = widen(Qs, dtype)
+    Kd = widen(Ks, dtype)
+    b = None if bias is None else np.asarray(bias, dtype=np.float64)
+    return te_scores(Qd, Kd, scale, lse_rows=lse_rows, bias=b)
+
+
+def lse_unit(Qs, Ks, dtype, scale, bias=None):
+    Qd = widen(Qs, dtype)
+    Kd = widen(Ks, dtype)
+    b = None if bias is None else np.asarray(bias, dtype=np.float64)
+    return lse(Qd, Kd, scale, b)
+
+
+def paged_unit_keys(k_pool, table_row, n, h, B):
+    """Stored keys [n][d] of head h, read through the block table."""
+    blocks = np.asarray(table_row[:-(-n // B)], dtype=np.int64)
+    rows = k_pool[blocks, :, h, :].reshape(-1, k_pool.shape[-1])
+    return rows[:n]
+
+
+def run_contiguous(data: dict, G: int, dtype: str, scale: float, lse_all=None, units=None):
+    """score -> select -> gather for every (s, h) of a contiguous batch.
+
+    Returns per-unit dicts with scores, kept, K_c and V_c. ``units`` limits the work to a list
+    of (s, h) pairs.
+    """
+    K, V, Q, n, m = data["K"], data["V"], data["Q"], data["n"], data["m"]
+    S, H = K.shape[0], K.shape[1]
+    bias = data.get("bias")
+    out = {}
+    for s, h in (units if units is not None else [(s, h) for s in range(S) for h in range(H)]):
+        ns = int(n[s])
+        b = None if bias is None else bias[s, :ns]
+        sc = score_unit(unit_rows(Q, s, h, G), K[s, h, :ns], dtype, scale, b, unit_lse(Q, s, h, G, lse_all))
+        kept = select_topm(sc, int(m[s]))
+        out[(s, h)] = dict(scores=sc, kept=kept, K_c=gather(K[s, h, :ns], kept), V_c=gather(V[s, h, :ns], kept))
+    return out
+
+
+def run_paged(data: dict, G: int, dtype: str, scale: float, B: int, lse_all=None, seqs=None):
+    """score -> select -> paged plan/copy -> table update for whole sequences (all heads).
+
+    Works on copies of the pools and table; returns them with per-unit scores and kept sets and
+    per-sequence freed lists.
+    """
+    k_pool = data["k_pool"].copy()
+    v_pool = data["v_pool"].copy()
+    table = data["table"].copy()
+    Q, n, m = data["Q"], data["n"], data["m"]
+    bias = data.get("bias")
+    H = k_pool.shape[2]
+    S = table.shape[0]
+    res = dict(units={}, freed={})
+    for s in (seqs if seqs is not None else range(S)):
+        ns, ms = int(n[s]), int(m[s])
+        b = None if bias is None else bias[s, :ns]
+        plans = []
+        for h in range(H):
+            Ks = paged_unit_keys(k_pool, table[s], ns, h, B)
+            sc = score_unit(unit_rows(Q, s, h, G), Ks, dtype, scale, b, unit_lse(Q, s, h, G, lse_all))
+            kept = select_topm(sc, ms)
+            plans.append(paged_plan(ns, ms, B, kept))
+            res["units"][(s, h)] = dict(scores=sc, kept=kept, plan=plans[-1])
+        for h in range(H):
+            apply_paged_copy(k_pool, v_pool, table[s], h, plans[h])
+        new, freed = table_update(table[s], ns, ms, B)
+        table[s] = new
+        res["freed"][s] = freed
+    res.update(k_pool=k_pool, v_pool=v_pool, table=table)
+    return res
