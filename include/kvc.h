@@ -1,0 +1,166 @@
+/*
+ * kvc.h -- C ABI of libkvc: proxy-query Token Eviction on AMD Instinct MI355X (gfx950).
+ *
+ * The library scores every cached key of every KV head with the proxy queries that attend to
+ * it, keeps the top-m positions and compacts the kept K/V, either into a contiguous buffer or
+ * in place inside a paged pool. Sources (titles as they appear on the pages):
+ *   [TE]  "Practical Online KV Cache Compaction for LLM Agents: An Empirical Study", design-space
+ *         section, Token Eviction score equation: s_j = ((1/q) sum_i alpha_ij^2)^(1/2), then keep
+ *         the top-m positions with their original keys and values.
+ *   [ACT] ActKV analysis page (zhichai.net), paragraph on paged memory management: attention is
+ *         recovered block by block as exp(logit - LSE), the LSE being a byproduct of paged
+ *         attention; eviction holes are closed by a conflict-free slot plan (tail X logical blocks
+ *         are the target region, kept entries outside it are paired one-to-one with holes inside
+ *         it, all pairs are copied in one parallel pass) and the emptied blocks are returned.
+ *
+ * Conventions shared by every entry point
+ *   unit        one (sequence s, KV head h). A "sequence" may also be one layer of a trajectory or
+ *               one serving session; units never interact.
+ *   R = G * q   proxy rows of a unit: the q queries of each of the G query heads h*G .. h*G+G-1
+ *               that share KV head h, stacked head-major. The mean in the score runs over all R.
+ *   logit       l_rj = scale * (q_r . k_j) + bias_j  (bias optional, 0 when NULL).
+ *   LSE         natural log: LSE_r = ln sum_{j<n_s} exp(l_rj).
+ *   score       s_j = sqrt((1/R) sum_r exp(2 (l_rj - LSE_r)))  in [0, 1] when the LSE is exact.
+ *   ties        equal scores (equal float32 bit patterns) are ordered by lower position first.
+ *
+ * Memory: every pointer marked "device" is HIP device memory; "host" arrays are read (or, for
+ * freed_counts, written) synchronously during the call. The library never allocates or frees
+ * memory, keeps no pointer after returning, holds no state between calls and never
+ * synchronises the stream: device work is enqueued on `stream` (a hipStream_t, NULL = the
+ * default stream) and runs asynchronously. All functions are thread-safe.
+ *
+ * Errors: arguments are validated before anything is enqueued; on an error nothing is launched
+ * and no output is touched. Inputs must be finite (unchecked). kvc_last_error() returns a
+ * thread-local description of the last failure.
+ */
+#ifndef KVC_H_
+#define KVC_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVC_OK = 0,
+  KVC_ERR_INVALID_ARGUMENT = 1,   /* a pointer, size or layout is inconsistent            */
+  KVC_ERR_UNSUPPORTED = 2,        /* a valid request this build does not implement        */
+  KVC_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes < the matching *_workspace_size()           */
+  KVC_ERR_HIP = 4                 /* a kernel launch failed; see kvc_last_error()         */
+} kvc_status;
+
+typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
+
+/* Problem shape (host memory). */
+typedef struct {
+  int32_t num_seqs;        /* S >= 1                                                         */
+  int32_t num_kv_heads;    /* H >= 1                                                         */
+  int32_t group;           /* G >= 1 query heads per KV head                                 */
+  int32_t num_queries;     /* q >= 1 proxy queries per query head                            */
+  int32_t head_dim;        /* d; this build supports 128 only (else KVC_ERR_UNSUPPORTED)     */
+  int32_t n_max;           /* token stride of contiguous K/V, of bias and of scores; >= n_s  */
+  const int32_t* seq_lens; /* host [S]: n_s >= 1 keys in sequence s                          */
+  float scale;             /* logit scale c (1/sqrt(d) in the usual attention)               */
+} kvc_shape;
+
+/* How keys are addressed. Contiguous: data is [S][H][n_max][d]. Paged (vLLM-style pool):
+ * data is [num_blocks][block_size][H][d] and position j of sequence s lives in physical block
+ * block_table[s * max_blocks + j / block_size], slot j % block_size. */
+typedef struct {
+  const void* data;            /* device                                                  */
+  kvc_dtype dtype;             /* element type of K (and of the queries)                  */
+  int32_t block_size;          /* 0 = contiguous; else B (this build: 16)                 */
+  const int32_t* block_table;  /* device [S][max_blocks] (paged only, else NULL)          */
+  int32_t max_blocks;          /* row stride of block_table; ceil(n_s / B) <= max_blocks  */
+} kvc_kv_view;
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_lse -- per proxy row, the log-sum-exp of its logits over the n_s keys ([ACT] LSE; the
+ * normaliser of alpha in [TE]). This is what paged attention produces as a byproduct; callers
+ * that have it skip this call.
+ *   q       device [S][H*G][q][d], dtype of K
+ *   k       key view
+ *   bias    device [S][n_max] float32 additive logit bias, or NULL
+ *   lse_out device out [S][H*G][q] float32, natural log
+ *   ws      device workspace of at least kvc_lse_workspace_size(shape, k) bytes (any alignment
+ *           of 256 bytes or more); its contents are scratch
+ * Result is deterministic (fixed reduction order) and within ~1e-6 relative of the exact LSE.
+ * ------------------------------------------------------------------------------------------- */
+size_t kvc_lse_workspace_size(const kvc_shape* shape, const kvc_kv_view* k);
+kvc_status kvc_lse(const kvc_shape* shape, const void* q, const kvc_kv_view* k, const float* bias,
+                   float* lse_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_score -- Token Eviction score of every key ([TE] score equation, alpha recovered from the
+ * LSE as in [ACT]). The attention matrix is never materialised.
+ *   lse     device [S][H*G][q] float32 natural-log LSE per proxy row, or NULL to compute it
+ *           (then ws must hold kvc_score_workspace_size(shape, k, 0) bytes). A supplied LSE is
+ *           used as given, e.g. one covering more keys makes the weights sum to less than 1.
+ *           It must not lie more than ~5 below the exact value (the weights' squares are
+ *           accumulated with a 2^100 offset and would overflow float32).
+ *   scores  device out [S][H][n_max] float32; entries j >= n_s are not written.
+ * Accuracy: within 1e-3 relative of the float64 definition for every score >= 1e-30
+ * (squared weights below 2^-226 are flushed to zero). Deterministic.
+ * ------------------------------------------------------------------------------------------- */
+size_t kvc_score_workspace_size(const kvc_shape* shape, const kvc_kv_view* k, int lse_supplied);
+kvc_status kvc_score(const kvc_shape* shape, const void* q, const kvc_kv_view* k, const float* lse,
+                     const float* bias, float* scores, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_select_topm -- per unit, the m_s positions with the largest scores, ties to the lower
+ * position, written in ascending position order ([TE] top-m).
+ *   scores  device [S][H][n_max] float32, non-negative and finite
+ *   m       host [S]: 0 <= m_s <= n_s
+ *   m_max   row stride of kept, >= max m_s
+ *   kept    device out [S][H][m_max] int32; entries r >= m_s are not written
+ * Exact: the same float32 scores always give the same kept set.
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_select_topm(const kvc_shape* shape, const float* scores, const int32_t* m, int32_t m_max,
+                           int32_t* kept, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_compact_contig -- order-preserving gather of the kept rows ([TE] keep the original K, V):
+ * k_out[s][h][r] = k[s][h][kept[s][h][r]] for r < m_s, and the same for V, bit for bit.
+ *   k, v          device [S][H][n_max][d] of dtype
+ *   kept          device [S][H][m_max] int32, strictly ascending, < n_s (as from select)
+ *   k_out, v_out  device out [S][H][m_max][d]; rows r >= m_s are not written
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_compact_contig(const kvc_shape* shape, kvc_dtype dtype, const void* k, const void* v,
+                              const int32_t* kept, const int32_t* m, int32_t m_max, void* k_out,
+                              void* v_out, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_compact_paged -- in-place conflict-free compaction of a paged pool ([ACT] slot plan).
+ * Per sequence: N = ceil(n_s/B), X = ceil(m_s/B), window W = [(N-X)B, (N-X)B + m_s). Per head:
+ * sources = kept positions outside W, holes = positions of W not kept (both ascending); the
+ * i-th source's K and V rows are copied to the i-th hole, all pairs in one parallel pass (a
+ * source is never a hole, so no slot is both read and written). Kept positions inside W stay
+ * where they are, so the compacted order is not the original order. Afterwards:
+ *   block_table[s][0..X)  = old block_table[s][N-X..N)   (new length m_s)
+ *   block_table[s][X..N)  = -1; entries >= N untouched
+ *   freed_blocks[s][0..N-X) = old block_table[s][0..N-X) (logical order); rest untouched
+ *   freed_counts[s] (host, written during the call) = N - X = ceil(n_s/B) - ceil(m_s/B)
+ * Source slots keep their bytes (copy, not move).
+ *   k_pool, v_pool  device [num_blocks][B][H][d] of dtype, modified in place
+ *   block_table     device in/out [S][max_blocks] int32 (valid, distinct ids for j < n_s)
+ *   kept            device [S][H][m_max] int32, strictly ascending, < n_s
+ *   m               host [S]
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_compact_paged(const kvc_shape* shape, kvc_dtype dtype, void* k_pool, void* v_pool,
+                             int32_t block_size, int32_t* block_table, int32_t max_blocks,
+                             const int32_t* kept, const int32_t* m, int32_t m_max,
+                             int32_t* freed_blocks, int32_t* freed_counts, void* stream);
+
+/* Static text for a status code; never NULL. */
+const char* kvc_status_string(kvc_status status);
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* kvc_last_error(void);
+/* Library version as an integer (major * 10000 + minor * 100 + patch). */
+int kvc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVC_H_ */

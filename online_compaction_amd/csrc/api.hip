@@ -1,0 +1,372 @@
+// Host side of libkvc: argument validation, workspace sizing, work tables and kernel dispatch.
+// Declarations and the contract of every entry point are in include/kvc.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+// kernel launchers (score_mfma.hip, score_valu.hip, select.hip, compact.hip)
+int score_mfma_tiles(int n);
+int lse_mfma_row_blocks(int R);
+int score_valu_tiles(int n);
+int contig_tiles(int m, bool f32);
+int paged_tiles(int m);
+hipError_t launch_score_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+                             int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
+                             int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
+hipError_t launch_lse_partials_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+                                    int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
+                                    float scale, int kchunk, const SeqTable& T, hipStream_t st);
+hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int R, int kchunk, const SeqTable& T,
+                              hipStream_t st);
+hipError_t launch_score_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+                             int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
+                             int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
+hipError_t launch_lse_partials_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k,
+                                    const int32_t* table, int max_blocks, const float* bias, float2* partials, int H,
+                                    int R, int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
+hipError_t launch_select(const float* scores, int32_t* kept, int H, int64_t n_max, int m_max, const SeqTable& T,
+                         hipStream_t st);
+hipError_t launch_compact_contig(bool f32, const void* k, const void* v, const int32_t* kept, void* ko, void* vo, int H,
+                                 int64_t n_max, int m_max, const SeqTable& T, hipStream_t st);
+hipError_t launch_paged_copy(bool f32, void* kp, void* vp, const int32_t* table, int max_blocks, const int32_t* kept,
+                             int H, int m_max, int B, const SeqTable& T, hipStream_t st);
+hipError_t launch_table_update(int32_t* table, int max_blocks, int32_t* freed, int B, const SeqTable& T,
+                               hipStream_t st);
+}  // namespace kvc
+
+using namespace kvc;
+
+namespace {
+
+thread_local std::string g_err;
+
+constexpr int kVersion = 100;          // 0.1.0
+constexpr int kBlockSize = 16;         // the one page size this build supports
+constexpr int kMfmaMinRows = 16;       // bf16 units with fewer proxy rows use the VALU path
+constexpr int64_t kMaxRows = 1 << 24;  // proxy rows per unit
+constexpr int kMaxLen = 1 << 28;       // keys per sequence
+constexpr size_t kAlign = 256;
+
+kvc_status fail(kvc_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+kvc_status fail(kvc_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+kvc_status ok() {
+  g_err.clear();
+  return KVC_OK;
+}
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+kvc_status check_shape(const kvc_shape* sh) {
+  if (!sh) return fail(KVC_ERR_INVALID_ARGUMENT, "shape is NULL");
+  if (sh->num_seqs < 1 || sh->num_kv_heads < 1 || sh->group < 1 || sh->num_queries < 1)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "num_seqs, num_kv_heads, group and num_queries must be >= 1");
+  if (sh->head_dim != kHeadDim)
+    return fail(KVC_ERR_UNSUPPORTED, "head_dim %d: this build supports %d only", sh->head_dim, kHeadDim);
+  if ((int64_t)sh->group * sh->num_queries > kMaxRows)
+    return fail(KVC_ERR_UNSUPPORTED, "group * num_queries exceeds %lld proxy rows", (long long)kMaxRows);
+  if (!sh->seq_lens) return fail(KVC_ERR_INVALID_ARGUMENT, "seq_lens is NULL");
+  if (sh->n_max < 1 || sh->n_max > kMaxLen) return fail(KVC_ERR_INVALID_ARGUMENT, "n_max %d out of range", sh->n_max);
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    const int n = sh->seq_lens[s];
+    if (n < 1 || n > sh->n_max)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d outside [1, n_max = %d]", s, n, sh->n_max);
+  }
+  return KVC_OK;
+}
+
+kvc_status check_dtype(kvc_dtype dt) {
+  if (dt != KVC_F32 && dt != KVC_BF16) return fail(KVC_ERR_INVALID_ARGUMENT, "unknown dtype %d", (int)dt);
+  return KVC_OK;
+}
+
+kvc_status check_paging(const kvc_shape* sh, int32_t block_size, const int32_t* table, int32_t max_blocks,
+                        const char* what) {
+  if (block_size != kBlockSize)
+    return fail(KVC_ERR_UNSUPPORTED, "%s: block_size %d: this build supports %d", what, block_size, kBlockSize);
+  if (!table) return fail(KVC_ERR_INVALID_ARGUMENT, "%s: block_table is NULL", what);
+  if (max_blocks < 1) return fail(KVC_ERR_INVALID_ARGUMENT, "%s: max_blocks must be >= 1", what);
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    const int nb = (sh->seq_lens[s] + block_size - 1) / block_size;
+    if (nb > max_blocks)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "%s: sequence %d needs %d blocks > max_blocks %d", what, s, nb,
+                  max_blocks);
+  }
+  return KVC_OK;
+}
+
+kvc_status check_view(const kvc_shape* sh, const kvc_kv_view* kv) {
+  if (!kv) return fail(KVC_ERR_INVALID_ARGUMENT, "key view is NULL");
+  if (!kv->data) return fail(KVC_ERR_INVALID_ARGUMENT, "key data is NULL");
+  if (kvc_status st = check_dtype(kv->dtype)) return st;
+  if (kv->block_size == 0) return KVC_OK;
+  return check_paging(sh, kv->block_size, kv->block_table, kv->max_blocks, "keys");
+}
+
+bool use_mfma(const kvc_shape* sh, const kvc_kv_view* kv) {
+  return kv->dtype == KVC_BF16 && sh->group * sh->num_queries >= kMfmaMinRows;
+}
+
+// Key-chunk length of the MFMA LSE pass: the longest chunk that still gives >= 2048 workgroups.
+int mfma_kchunk(const kvc_shape* sh) {
+  const int R = sh->group * sh->num_queries;
+  const int64_t rb = lse_mfma_row_blocks(R);
+  for (int kc : {4096, 2048, 1024}) {
+    int64_t wg = 0;
+    for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
+    if (wg >= 2048) return kc;
+  }
+  return 512;
+}
+
+int lse_kchunk(const kvc_shape* sh, const kvc_kv_view* kv) {
+  return use_mfma(sh, kv) ? mfma_kchunk(sh) : 256;  // VALU: a chunk is one 256-key tile
+}
+
+// float2 partial slots of sequence s in the LSE workspace
+int64_t partial_slots(const kvc_shape* sh, int s, int kchunk) {
+  const int64_t R = (int64_t)sh->group * sh->num_queries;
+  return (int64_t)sh->num_kv_heads * ((sh->seq_lens[s] + kchunk - 1) / kchunk) * R;
+}
+
+size_t partials_bytes(const kvc_shape* sh, int kchunk) {
+  int64_t slots = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) slots += partial_slots(sh, s, kchunk);
+  return align_up((size_t)slots * sizeof(float2));
+}
+
+size_t lse_bytes(const kvc_shape* sh) {
+  return align_up((size_t)sh->num_seqs * sh->num_kv_heads * sh->group * sh->num_queries * sizeof(float));
+}
+
+// Run `body(T)` for consecutive slices of at most kChunkSeqs sequences; `items(s)` is the number
+// of work items (workgroups) of sequence s and `offset(s)` a kernel-specific per-sequence value.
+template <class Items, class Offset, class Body>
+hipError_t for_each_chunk(const kvc_shape* sh, const int32_t* m, Items&& items, Offset&& offset, Body&& body) {
+  for (int s0 = 0; s0 < sh->num_seqs; s0 += kChunkSeqs) {
+    SeqTable T{};
+    T.count = std::min(kChunkSeqs, sh->num_seqs - s0);
+    T.first = s0;
+    int64_t total = 0;
+    for (int i = 0; i < T.count; ++i) {
+      T.start[i] = (int32_t)total;
+      T.n[i] = sh->seq_lens[s0 + i];
+      T.m[i] = m ? m[s0 + i] : 0;
+      T.off[i] = offset(s0 + i);
+      total += items(s0 + i);
+    }
+    if (total > INT32_MAX) return hipErrorInvalidConfiguration;
+    T.start[T.count] = (int32_t)total;
+    T.total = (int32_t)total;
+    if (total > 0) {
+      const hipError_t e = body(T);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+auto no_offset = [](int) -> int64_t { return 0; };
+
+kvc_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Internal LSE: per-chunk partials into ws_partials, then combined into lse_out.
+kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, const float* bias, float* lse_out,
+                   void* ws_partials, hipStream_t st) {
+  const int H = sh->num_kv_heads;
+  const int R = sh->group * sh->num_queries;
+  const bool mf = use_mfma(sh, kv);
+  const bool paged = kv->block_size != 0;
+  const bool has_bias = bias != nullptr;
+  const int kc = lse_kchunk(sh, kv);
+  std::vector<int64_t> off(sh->num_seqs);
+  int64_t acc = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    off[s] = acc;
+    acc += partial_slots(sh, s, kc);
+  }
+  auto* parts = static_cast<float2*>(ws_partials);
+  const int rb = mf ? lse_mfma_row_blocks(R) : 1;
+  auto offset = [&](int s) -> int64_t { return off[s]; };
+  hipError_t e = for_each_chunk(
+      sh, nullptr, [&](int s) { return H * rb * ((sh->seq_lens[s] + kc - 1) / kc); }, offset,
+      [&](const SeqTable& T) {
+        if (mf)
+          return launch_lse_partials_mfma(paged, has_bias, q, kv->data, kv->block_table, kv->max_blocks, bias, parts,
+                                          H, R, sh->n_max, sh->scale, kc, T, st);
+        return launch_lse_partials_valu(kv->dtype == KVC_F32, paged, has_bias, q, kv->data, kv->block_table,
+                                        kv->max_blocks, bias, parts, H, R, sh->n_max, sh->scale, T, st);
+      });
+  if (e != hipSuccess) return hip_fail(e, "lse partial kernel");
+  e = for_each_chunk(
+      sh, nullptr, [&](int) { return H * ((R + 255) / 256); }, offset,
+      [&](const SeqTable& T) { return launch_lse_combine(parts, lse_out, H, R, kc, T, st); });
+  if (e != hipSuccess) return hip_fail(e, "lse combine kernel");
+  return KVC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvc_status_string(kvc_status st) {
+  switch (st) {
+    case KVC_OK: return "ok";
+    case KVC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KVC_ERR_UNSUPPORTED: return "unsupported";
+    case KVC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KVC_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* kvc_last_error(void) { return g_err.c_str(); }
+
+int kvc_version(void) { return kVersion; }
+
+size_t kvc_lse_workspace_size(const kvc_shape* sh, const kvc_kv_view* k) {
+  if (check_shape(sh) != KVC_OK || check_view(sh, k) != KVC_OK) return 0;
+  return partials_bytes(sh, lse_kchunk(sh, k));
+}
+
+kvc_status kvc_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* bias, float* lse_out,
+                   void* ws, size_t ws_bytes, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_view(sh, k)) return st;
+  if (!q || !lse_out) return fail(KVC_ERR_INVALID_ARGUMENT, "q and lse_out must be non-NULL");
+  if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
+  const size_t need = partials_bytes(sh, lse_kchunk(sh, k));
+  if (!ws || ws_bytes < need)
+    return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "lse needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (kvc_status st = run_lse(sh, q, k, bias, lse_out, ws, static_cast<hipStream_t>(stream))) return st;
+  return ok();
+}
+
+size_t kvc_score_workspace_size(const kvc_shape* sh, const kvc_kv_view* k, int lse_supplied) {
+  if (check_shape(sh) != KVC_OK || check_view(sh, k) != KVC_OK) return 0;
+  if (lse_supplied) return 0;
+  return partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+}
+
+kvc_status kvc_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse, const float* bias,
+                     float* scores, void* ws, size_t ws_bytes, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_view(sh, k)) return st;
+  if (!q || !scores) return fail(KVC_ERR_INVALID_ARGUMENT, "q and scores must be non-NULL");
+  if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int R = sh->group * sh->num_queries;
+  const float* lse_rows = lse;
+  if (!lse) {
+    const size_t pb = partials_bytes(sh, lse_kchunk(sh, k));
+    const size_t need = pb + lse_bytes(sh);
+    if (!ws || ws_bytes < need)
+      return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "score needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+    float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pb);
+    if (kvc_status s2 = run_lse(sh, q, k, bias, lse_ws, ws, st)) return s2;
+    lse_rows = lse_ws;
+  }
+  const bool mf = use_mfma(sh, k);
+  const bool paged = k->block_size != 0;
+  const int H = sh->num_kv_heads;
+  const hipError_t e = for_each_chunk(
+      sh, nullptr,
+      [&](int s) { return H * (mf ? score_mfma_tiles(sh->seq_lens[s]) : score_valu_tiles(sh->seq_lens[s])); },
+      no_offset, [&](const SeqTable& T) {
+        if (mf)
+          return launch_score_mfma(paged, bias != nullptr, q, k->data, k->block_table, k->max_blocks, lse_rows, bias,
+                                   scores, H, R, sh->n_max, sh->scale, T, st);
+        return launch_score_valu(k->dtype == KVC_F32, paged, bias != nullptr, q, k->data, k->block_table,
+                                 k->max_blocks, lse_rows, bias, scores, H, R, sh->n_max, sh->scale, T, st);
+      });
+  if (e != hipSuccess) return hip_fail(e, "score kernel");
+  return ok();
+}
+
+static kvc_status check_budgets(const kvc_shape* sh, const int32_t* m, int32_t m_max) {
+  if (!m) return fail(KVC_ERR_INVALID_ARGUMENT, "m is NULL");
+  int mm = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    if (m[s] < 0 || m[s] > sh->seq_lens[s])
+      return fail(KVC_ERR_INVALID_ARGUMENT, "m[%d] = %d outside [0, n = %d]", s, m[s], sh->seq_lens[s]);
+    mm = std::max(mm, m[s]);
+  }
+  if (m_max < mm || m_max < 1)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "m_max %d must be >= 1 and >= max m (%d)", m_max, mm);
+  return KVC_OK;
+}
+
+kvc_status kvc_select_topm(const kvc_shape* sh, const float* scores, const int32_t* m, int32_t m_max, int32_t* kept,
+                           void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (!scores || !kept) return fail(KVC_ERR_INVALID_ARGUMENT, "scores and kept must be non-NULL");
+  const hipError_t err = for_each_chunk(
+      sh, m, [&](int) { return sh->num_kv_heads; }, no_offset, [&](const SeqTable& T) {
+        return launch_select(scores, kept, sh->num_kv_heads, sh->n_max, m_max, T, static_cast<hipStream_t>(stream));
+      });
+  if (err != hipSuccess) return hip_fail(err, "select kernel");
+  return ok();
+}
+
+kvc_status kvc_compact_contig(const kvc_shape* sh, kvc_dtype dtype, const void* k, const void* v, const int32_t* kept,
+                              const int32_t* m, int32_t m_max, void* k_out, void* v_out, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_dtype(dtype)) return st;
+  if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (!k || !v || !kept || !k_out || !v_out)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "k, v, kept, k_out and v_out must be non-NULL");
+  const hipError_t err = for_each_chunk(
+      sh, m, [&](int s) { return sh->num_kv_heads * contig_tiles(m[s], dtype == KVC_F32); }, no_offset, [&](const SeqTable& T) {
+        return launch_compact_contig(dtype == KVC_F32, k, v, kept, k_out, v_out, sh->num_kv_heads, sh->n_max, m_max,
+                                     T, static_cast<hipStream_t>(stream));
+      });
+  if (err != hipSuccess) return hip_fail(err, "contiguous compaction kernel");
+  return ok();
+}
+
+kvc_status kvc_compact_paged(const kvc_shape* sh, kvc_dtype dtype, void* k_pool, void* v_pool, int32_t block_size,
+                             int32_t* block_table, int32_t max_blocks, const int32_t* kept, const int32_t* m,
+                             int32_t m_max, int32_t* freed_blocks, int32_t* freed_counts, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_dtype(dtype)) return st;
+  if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (kvc_status st = check_paging(sh, block_size, block_table, max_blocks, "pool")) return st;
+  if (!k_pool || !v_pool || !kept || !freed_blocks || !freed_counts)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool, v_pool, kept, freed_blocks and freed_counts must be non-NULL");
+  if (k_pool == v_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool and v_pool must be distinct");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err = for_each_chunk(
+      sh, m, [&](int s) { return sh->num_kv_heads * paged_tiles(m[s]); }, no_offset, [&](const SeqTable& T) {
+        return launch_paged_copy(dtype == KVC_F32, k_pool, v_pool, block_table, max_blocks, kept, sh->num_kv_heads,
+                                 m_max, block_size, T, st);
+      });
+  if (err != hipSuccess) return hip_fail(err, "paged copy kernel");
+  err = for_each_chunk(sh, m, [](int) { return 1; }, no_offset, [&](const SeqTable& T) {
+    return launch_table_update(block_table, max_blocks, freed_blocks, block_size, T, st);
+  });
+  if (err != hipSuccess) return hip_fail(err, "block table kernel");
+  for (int s = 0; s < sh->num_seqs; ++s)
+    freed_counts[s] = (sh->seq_lens[s] + block_size - 1) / block_size - (m[s] + block_size - 1) / block_size;
+  return ok();
+}
+
+}  // extern "C"

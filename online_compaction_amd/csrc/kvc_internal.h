@@ -1,0 +1,60 @@
+// Internal definitions shared by the libkvc kernels and the host entry points (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvc.h"
+
+namespace kvc {
+
+constexpr int kHeadDim = 128;
+constexpr int kChunkSeqs = 128;     // sequences described per launch (kernel-argument table)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Squared weights are accumulated as exp2(2*log2(alpha) + kSqOffset) so that alpha down to
+// 2^-113 survives float32's normal range; the offset is removed after the square root.
+constexpr float kSqOffset = 100.0f;
+constexpr float kSqUnscale = 8.8817841970012523e-16f;  // 2^-50
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Per-launch description of up to kChunkSeqs sequences, passed by value as a kernel argument
+// (so a launch never needs a host-to-device copy). `start[i]` is the first work item of
+// sequence i; work items of one sequence are contiguous.
+struct SeqTable {
+  int32_t count;                  // sequences in this launch
+  int32_t first;                  // global index of sequence 0 of this launch
+  int32_t total;                  // work items in this launch (grid size)
+  int32_t per_head;               // unused by some kernels
+  int32_t start[kChunkSeqs + 1];
+  int32_t n[kChunkSeqs];
+  int32_t m[kChunkSeqs];
+  int64_t off[kChunkSeqs];        // kernel-specific per-sequence offset (workspace slots)
+};
+
+// Map a dispatch-ordered block index to a logical work index so that logically consecutive
+// work items run on the same XCD (blocks are dispatched round-robin over the 8 XCDs, each with
+// its own L2): neighbours then share the operands they re-read.
+__device__ __forceinline__ int xcd_remap(int b, int nb) {
+  const int q = nb >> 3, r = nb & 7;
+  const int x = b & 7, i = b >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + i;
+}
+
+// Wave-uniform search: the sequence whose work range holds item t.
+__device__ __forceinline__ int find_seq(const SeqTable& T, int t) {
+  int lo = 0, hi = T.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (T.start[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+}  // namespace kvc

@@ -1,0 +1,140 @@
+"""The whole hot path over one batch: score -> select -> compact, through the C ABI.
+
+Torch only provides device memory and the stream. `Batch` holds device-resident inputs,
+`Outputs` the preallocated outputs and workspace, and `run` enqueues kvc_score,
+kvc_select_topm and kvc_compact_contig / kvc_compact_paged on the current stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+from . import _abi as A
+
+
+def device_tensor(arr: np.ndarray, device="cuda") -> torch.Tensor:
+    """Upload a numpy array; uint16 arrays are bfloat16 bit patterns."""
+    arr = np.ascontiguousarray(arr)
+    if arr.dtype == np.uint16:
+        return torch.from_numpy(arr.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(arr).to(device)
+
+
+def host_array(t: torch.Tensor) -> np.ndarray:
+    """Download a tensor; bfloat16 comes back as uint16 bit patterns."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@dataclass
+class Batch:
+    shape: A.Shape
+    dtype: int
+    q: torch.Tensor
+    m: np.ndarray
+    m_max: int
+    k: torch.Tensor = None            # contiguous [S][H][n_max][d]
+    v: torch.Tensor = None
+    k_pool: torch.Tensor = None       # paged [num_blocks][B][H][d]
+    v_pool: torch.Tensor = None
+    table: torch.Tensor = None        # paged [S][max_blocks] int32
+    block_size: int = 0
+    max_blocks: int = 0
+    bias: torch.Tensor = None
+    lse: torch.Tensor = None          # supplied LSE [S][H*G][q] or None
+
+    @property
+    def paged(self) -> bool:
+        return self.block_size != 0
+
+    def kview(self) -> A.KView:
+        if self.paged:
+            return A.KView(self.k_pool, self.dtype, self.block_size, self.table, self.max_blocks)
+        return A.KView(self.k, self.dtype)
+
+
+def _dtype_of(arr: np.ndarray) -> int:
+    return A.KVC_BF16 if arr.dtype == np.uint16 else A.KVC_F32
+
+
+def contiguous_batch(Q, K, V, n, m, group: int, scale: float, bias=None, lse=None, device="cuda") -> Batch:
+    S, H, n_max, d = K.shape
+    q = Q.shape[2]
+    shape = A.Shape(S, H, group, q, d, n_max, np.asarray(n, dtype=np.int32), scale)
+    m = np.asarray(m, dtype=np.int32)
+    return Batch(shape, _dtype_of(K), device_tensor(Q, device), m, max(1, int(m.max())),
+                 k=device_tensor(K, device), v=device_tensor(V, device),
+                 bias=None if bias is None else device_tensor(np.asarray(bias, dtype=np.float32), device),
+                 lse=None if lse is None else device_tensor(np.asarray(lse, dtype=np.float32), device))
+
+
+def paged_batch(Q, k_pool, v_pool, table, n, m, group: int, scale: float, block_size: int, n_max=None, bias=None,
+                lse=None, device="cuda") -> Batch:
+    S, max_blocks = table.shape
+    H, d = k_pool.shape[2], k_pool.shape[3]
+    q = Q.shape[2]
+    n = np.asarray(n, dtype=np.int32)
+    n_max = int(n_max if n_max is not None else (bias.shape[1] if bias is not None else n.max()))
+    shape = A.Shape(S, H, group, q, d, n_max, n, scale)
+    m = np.asarray(m, dtype=np.int32)
+    return Batch(shape, _dtype_of(k_pool), device_tensor(Q, device), m, max(1, int(m.max())),
+                 k_pool=device_tensor(k_pool, device), v_pool=device_tensor(v_pool, device),
+                 table=device_tensor(np.asarray(table, dtype=np.int32), device), block_size=block_size,
+                 max_blocks=max_blocks,
+                 bias=None if bias is None else device_tensor(np.asarray(bias, dtype=np.float32), device),
+                 lse=None if lse is None else device_tensor(np.asarray(lse, dtype=np.float32), device))
+
+
+@dataclass
+class Outputs:
+    scores: torch.Tensor
+    kept: torch.Tensor
+    ws: torch.Tensor = None
+    k_out: torch.Tensor = None
+    v_out: torch.Tensor = None
+    freed: torch.Tensor = None
+    freed_counts: np.ndarray = field(default=None)
+
+
+def allocate(b: Batch) -> Outputs:
+    sh = b.shape
+    dev = b.q.device
+    scores = torch.zeros((sh.num_seqs, sh.num_kv_heads, sh.n_max), dtype=torch.float32, device=dev)
+    kept = torch.full((sh.num_seqs, sh.num_kv_heads, b.m_max), -1, dtype=torch.int32, device=dev)
+    wsb = A.kvc_score_workspace_size(sh, b.kview(), b.lse is not None)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev) if wsb else None
+    out = Outputs(scores, kept, ws)
+    if b.paged:
+        out.freed = torch.full((sh.num_seqs, b.max_blocks), -1, dtype=torch.int32, device=dev)
+    else:
+        el = b.k.dtype
+        out.k_out = torch.zeros((sh.num_seqs, sh.num_kv_heads, b.m_max, sh.head_dim), dtype=el, device=dev)
+        out.v_out = torch.zeros_like(out.k_out)
+    return out
+
+
+def run_score(b: Batch, o: Outputs, stream=None) -> None:
+    A.kvc_score(b.shape, b.q, b.kview(), b.lse, b.bias, o.scores, o.ws, stream)
+
+
+def run_select(b: Batch, o: Outputs, stream=None) -> None:
+    A.kvc_select_topm(b.shape, o.scores, b.m, b.m_max, o.kept, stream)
+
+
+def run_compact(b: Batch, o: Outputs, stream=None) -> None:
+    if b.paged:
+        o.freed_counts = A.kvc_compact_paged(b.shape, b.dtype, b.k_pool, b.v_pool, b.block_size, b.table,
+                                             b.max_blocks, o.kept, b.m, b.m_max, o.freed, stream)
+    else:
+        A.kvc_compact_contig(b.shape, b.dtype, b.k, b.v, o.kept, b.m, b.m_max, o.k_out, o.v_out, stream)
+
+
+def run(b: Batch, o: Outputs, stream=None) -> None:
+    """One pass of the hot path over the batch (asynchronous on the stream)."""
+    run_score(b, o, stream)
+    run_select(b, o, stream)
+    run_compact(b, o, stream)

@@ -1,0 +1,139 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point, sizes workspaces,
+and rejects bad arguments before anything is enqueued (no call here reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import online_compaction_amd as oc
+from online_compaction_amd import _abi as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvc.h")
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvc_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(A.LIB_PATH):
+        pytest.fail("libkvc.so is not built (run __graft_entry__.build())")
+    return A.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared()
+    assert {"kvc_score", "kvc_lse", "kvc_select_topm", "kvc_compact_contig", "kvc_compact_paged"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(A._SIGS), "binding and header disagree"
+
+
+def test_version_and_status_strings(lib):
+    assert oc.kvc_version() == 100
+    assert oc.kvc_status_string(0) == "ok"
+    assert oc.kvc_status_string(3) == "workspace too small"
+    assert oc.kvc_status_string(99) == "unknown status"
+
+
+def _shape(S=2, H=8, G=4, q=1024, d=128, n=(33000, 20000), n_max=33000, scale=0.088):
+    return A.Shape(S, H, G, q, d, n_max, np.array(n, dtype=np.int32), scale)
+
+
+def test_workspace_sizes():
+    kv = A.KView(FAKE, A.KVC_BF16)
+    sh = _shape()
+    assert oc.kvc_score_workspace_size(sh, kv, True) == 0
+    full = oc.kvc_score_workspace_size(sh, kv, False)
+    lse_only = oc.kvc_lse_workspace_size(sh, kv)
+    assert full > lse_only > 0 and full % 256 == 0
+    # computed LSE needs one float per proxy row on top of the partials
+    assert full - lse_only >= 2 * 8 * 4 * 1024 * 4
+    # VALU path (float32) uses 256-key chunks
+    kvf = A.KView(FAKE, A.KVC_F32)
+    shf = _shape(S=1, H=1, G=1, q=32, n=(4096,), n_max=4096)
+    assert oc.kvc_lse_workspace_size(shf, kvf) == 16 * 32 * 8
+    # invalid shapes size to 0
+    assert oc.kvc_lse_workspace_size(_shape(d=64), kv) == 0
+
+
+def _raw_status(fn, *args):
+    return fn(*args)
+
+
+def test_score_validation(lib):
+    kv = A.KView(FAKE, A.KVC_BF16).c()
+    cases = [
+        (_shape(d=64), A.KVC_ERR_UNSUPPORTED),
+        (_shape(n=(0, 5)), A.KVC_ERR_INVALID_ARGUMENT),
+        (_shape(n=(40000, 5)), A.KVC_ERR_INVALID_ARGUMENT),
+        (_shape(G=0), A.KVC_ERR_INVALID_ARGUMENT),
+    ]
+    for shp, want in cases:
+        sh, keep = shp.c()
+        st = lib.kvc_score(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, FAKE, None, 0, None)
+        assert st == want, (shp, st, lib.kvc_last_error())
+    sh, keep = _shape().c()
+    # NULL scores
+    assert lib.kvc_score(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, None, None, 0, None) == 1
+    # LSE to be computed but no workspace
+    st = lib.kvc_score(ctypes.byref(sh), FAKE, ctypes.byref(kv), None, None, FAKE, FAKE, 16, None)
+    assert st == A.KVC_ERR_WORKSPACE_TOO_SMALL
+    assert b"workspace" in lib.kvc_last_error()
+    # unsupported page size, missing table, too few table columns
+    for view, want in ((A.KView(FAKE, A.KVC_BF16, 32, FAKE, 4096), A.KVC_ERR_UNSUPPORTED),
+                       (A.KView(FAKE, A.KVC_BF16, 16, None, 4096), A.KVC_ERR_INVALID_ARGUMENT),
+                       (A.KView(FAKE, A.KVC_BF16, 16, FAKE, 100), A.KVC_ERR_INVALID_ARGUMENT),
+                       (A.KView(FAKE, 7), A.KVC_ERR_INVALID_ARGUMENT)):
+        v = view.c()
+        assert lib.kvc_score(ctypes.byref(sh), FAKE, ctypes.byref(v), FAKE, None, FAKE, None, 0, None) == want
+
+
+def test_select_and_compact_validation(lib):
+    sh, keep = _shape().c()
+    m_bad = (ctypes.c_int32 * 2)(40000, 10)
+    m_ok = (ctypes.c_int32 * 2)(6600, 4000)
+    assert lib.kvc_select_topm(ctypes.byref(sh), FAKE, m_bad, 40000, FAKE, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_select_topm(ctypes.byref(sh), FAKE, m_ok, 100, FAKE, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_select_topm(ctypes.byref(sh), None, m_ok, 6600, FAKE, None) == A.KVC_ERR_INVALID_ARGUMENT
+    m_neg = (ctypes.c_int32 * 2)(-1, 0)
+    assert lib.kvc_compact_contig(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE, FAKE, m_neg, 10, FAKE, FAKE,
+                                  None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_compact_contig(ctypes.byref(sh), 5, FAKE, FAKE, FAKE, m_ok, 6600, FAKE, FAKE,
+                                  None) == A.KVC_ERR_INVALID_ARGUMENT
+    counts = (ctypes.c_int32 * 2)(-7, -7)
+    # same pool for K and V, and an unsupported page size: rejected, counts untouched
+    assert lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE, 16, FAKE, 4096, FAKE, m_ok, 6600, FAKE,
+                                 counts, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE + 64, 8, FAKE, 4096, FAKE, m_ok, 6600,
+                                 FAKE, counts, None) == A.KVC_ERR_UNSUPPORTED
+    assert list(counts) == [-7, -7]
+
+
+def test_binding_refuses_host_tensors():
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4)
+    with pytest.raises(ValueError):
+        A._ptr(t)
+
+
+def test_binding_refuses_short_buffers():
+    torch = pytest.importorskip("torch")
+
+    class Fake:
+        def numel(self):
+            return 10
+
+        def element_size(self):
+            return 4
+    with pytest.raises(ValueError):
+        A._need(Fake(), 41, "x")
+    A._need(Fake(), 40, "x")
