@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Benchmark of the proxy-query Token Eviction hot path (score -> select -> compact) on one GPU.
+
+Default workload: one 33 000-token agent trajectory across 36 layers x 8 KV heads (32 query
+heads, 1024 delayed future-turn proxy queries per query head, d = 128, bf16, keep ratio 0.2,
+so m = 6600 per KV head), per-query LSE supplied as float32, contiguous compaction of every
+layer in one launch per stage. A step is one pass of kvc_score + kvc_select_topm +
+kvc_compact_contig over the whole trajectory; inputs are resident in HBM before timing starts.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
+SCORE_SRC = os.path.join(ROOT, "online_compaction_amd", "csrc", "score_mfma.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def describe(w) -> str:
+    lay = "paged B=%d" % w.block_size if w.paged else "contiguous"
+    lse = "supplied LSE" if w.lse_supplied else "computed LSE"
+    n = f"n={w.n[0]}" if len(set(w.n)) == 1 else f"n={min(w.n)}..{max(w.n)}"
+    return (f"{w.name}: {w.S} seqs x {w.H} KV heads, G={w.G}, q={w.q}, R={w.R}, {n}, d={w.d}, {w.dtype}, "
+            f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}")
+
+
+def trajectory_tokens(w) -> int:
+    """Token positions compacted per step: the 36 sequences of the default workload are layers of
+    one trajectory, so it counts 33 000; elsewhere sequences are distinct."""
+    if w.name == "c3":
+        return w.n[0]
+    return int(sum(w.n))
+
+
+def algorithmic_bytes(w, moved_rows=None) -> dict:
+    """Bytes the method must move per step (reads + writes), per stage."""
+    el = 2 if w.dtype == "bf16" else 4
+    row = w.d * el
+    entries = sum(w.n) * w.H
+    kept = sum(w.m) * w.H
+    rows_q = w.S * w.H * w.R
+    score = entries * row + rows_q * row + entries * 4 + (rows_q * 4 if w.lse_supplied else 0)
+    if not w.lse_supplied:
+        score += entries * row + rows_q * row  # LSE pass reads K and Q once more
+    select = entries * 4 + kept * 4
+    if w.paged:
+        moved = kept if moved_rows is None else moved_rows
+        compact = kept * 4 + moved * 2 * row * 2
+    else:
+        compact = kept * 4 + kept * 2 * row * 2
+    return dict(score=score, select=select, compact=compact, total=score + select + compact)
+
+
+def score_flops(w) -> float:
+    passes = 1 if w.lse_supplied else 2
+    return float(passes) * 2.0 * w.R * w.d * sum(w.n) * w.H
+
+
+# ---------------------------------------------------------------------------------- CPU baseline
+
+def _oracle_unit(args):
+    w, s, h, bias_row = args
+    from oracle import oracle as O
+    from workloads import unit_keys, unit_queries, unit_values
+    K = unit_keys(w, s, h)
+    V = unit_values(w, s, h)
+    Qr = unit_queries(w, s, h)
+    lse_rows = None
+    if w.lse_supplied:  # the supplied input, prepared outside the timed region
+        lse_rows = O.lse_unit(Qr, K, w.dtype, w.logit_scale, bias_row).astype(np.float32).astype(np.float64)
+    t0 = time.perf_counter()
+    sc = O.score_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
+    kept = O.select_topm(sc, w.m[s])
+    O.gather(K, kept)
+    O.gather(V, kept)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline(w, budget_s: float) -> dict:
+    from concurrent.futures import ProcessPoolExecutor
+    import multiprocessing as mp
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = W.gen.default_workers()
+    units = [(s, h) for s in range(w.S) for h in range(w.H)]
+    # a first unit calibrates how many fit the budget
+    ctx = mp.get_context("fork")
+    if threadpool_limits:
+        threadpool_limits(1)
+    t_first = _oracle_unit((w, 0, 0, W.bias_row(w, 0)))
+    per_wave = max(1, int(budget_s / max(t_first, 1e-3)))
+    rng = np.random.default_rng(0)
+    if len(units) > 1:
+        count = max(1, min(len(units) - 1, per_wave * cores))
+        pick = [units[i] for i in sorted(rng.choice(np.arange(1, len(units)), size=count, replace=False))]
+    else:  # a single unit: time repeats of it
+        count = max(1, min(per_wave * cores, 64))
+        pick = units * count
+    log(f"[cpu] oracle: first unit {t_first:.2f} s; timing {count} more units on {cores} processes")
+    t0 = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
+        busy = list(ex.map(_oracle_unit, [(w, s, h, W.bias_row(w, s)) for s, h in pick]))
+    wall = time.perf_counter() - t0
+    # units of one workload cost about the same, so a step takes units / count times the sample
+    step_s = wall * len(units) / count
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": trajectory_tokens(w) / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": (f"{count} of {len(units)} (layer, KV head) units, float64 NumPy oracle score (supplied "
+                       f"LSE) + top-m + gather, one unit per process with 1 BLAS thread; "
+                       f"wall {wall:.1f} s (busy {sum(busy):.1f} s) scaled by {len(units)}/{count}"),
+            "cpu_model": model}
+
+
+# ---------------------------------------------------------------------------------- roofline
+
+def traffic_from_profile(launch_s: float):
+    """HBM bytes per launch of the score kernel from the committed PMC summary, or None if the
+    summary is missing or the kernel source changed since the counters were taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    src = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+    if kv.get("source_sha256") != src:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c3", help="c3 (default) or another named workload, for study")
+    ap.add_argument("--k", type=int, default=6, help="budget index for the paged action-token workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="approximate CPU baseline budget")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (units never interact, so "
+              f"more GPUs would each run this same benchmark on their own share)", file=sys.stderr)
+        sys.exit(2)
+
+    w = W.spec(args.workload, args.k) if args.workload == "c4" else W.spec(args.workload)
+    log(f"[bench] workload {describe(w)}")
+    t0 = time.perf_counter()
+    workers = W.gen.default_workers()
+    data = W.build_paged(w, workers) if w.paged else W.build_contiguous(w, workers)
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+        log(f"[cpu] oracle baseline {cpu['value']:.4g} tokens/s on {cpu['cores']} cores")
+
+    import torch
+    from online_compaction_amd import _abi as A
+    from online_compaction_amd import path as P
+    A.load()  # fails loudly when libkvc.so is missing
+
+    if w.paged:
+        b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], data["n"], data["m"], w.G,
+                          w.logit_scale, w.block_size, n_max=w.n_max, bias=data["bias"])
+        pristine = (b.k_pool.clone(), b.v_pool.clone(), b.table.clone())
+    else:
+        b = P.contiguous_batch(data["Q"], data["K"], data["V"], data["n"], data["m"], w.G, w.logit_scale,
+                               bias=data["bias"])
+        pristine = None
+    del data
+    if w.lse_supplied:  # the harness computes the supplied LSE with the library's own LSE pass
+        lse = torch.empty((w.S, w.H * w.G, w.q), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(256, A.kvc_lse_workspace_size(b.shape, b.kview())), dtype=torch.uint8, device="cuda")
+        A.kvc_lse(b.shape, b.q, b.kview(), b.bias, lse, ws)
+        b.lse = lse
+        del ws
+    o = P.allocate(b)
+    torch.cuda.synchronize()
+    log("[bench] inputs resident on the GPU")
+
+    if args.calib_copy_mib:
+        src = torch.empty(args.calib_copy_mib << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
+
+    def restore():
+        if pristine is not None:
+            b.k_pool.copy_(pristine[0])
+            b.v_pool.copy_(pristine[1])
+            b.table.copy_(pristine[2])
+
+    for _ in range(args.warmup):
+        restore()
+        P.run(b, o)
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    stage_ms = np.zeros((args.steps, 3))
+    wall = 0.0
+    if pristine is None:
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            e = ev[i]
+            e[0].record()
+            P.run_score(b, o)
+            e[1].record()
+            P.run_select(b, o)
+            e[2].record()
+            P.run_compact(b, o)
+            e[3].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    else:  # paged: restore the pristine pool before each step, outside the timed region
+        for i in range(args.steps):
+            restore()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e = ev[i]
+            e[0].record()
+            P.run_score(b, o)
+            e[1].record()
+            P.run_select(b, o)
+            e[2].record()
+            P.run_compact(b, o)
+            e[3].record()
+            torch.cuda.synchronize()
+            wall += time.perf_counter() - t0
+    for i in range(args.steps):
+        e = ev[i]
+        stage_ms[i] = [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+    ms_step = wall * 1e3 / args.steps
+    avg = stage_ms.mean(axis=0)
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (score {avg[0]:.3f}, select {avg[1]:.3f}, "
+        f"compact {avg[2]:.3f} ms)")
+
+    moved = None
+    if w.paged:
+        kept = P.host_array(o.kept)
+        moved = 0
+        for s in range(w.S):
+            n, m = w.n[s], w.m[s]
+            start = (-(-n // w.block_size) - -(-m // w.block_size)) * w.block_size
+            for h in range(w.H):
+                k = kept[s, h, :m]
+                moved += int(np.count_nonzero((k < start) | (k >= start + m)))
+    ab = algorithmic_bytes(w, moved)
+    tokens = trajectory_tokens(w)
+    flops = score_flops(w)
+    score_s = avg[0] * 1e-3
+    achieved_tf = flops / score_s / 1e12
+    step_s = ms_step * 1e-3
+    traffic = traffic_from_profile(score_s) if (w.name == "c3") else None
+    line = {
+        "metric": "compacted KV tokens/sec (score+select+compact) and % of peak HBM GB/s, 1 GPU",
+        "value": tokens / step_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded generators shaped like the pages' agent trajectories)",
+        "config": {
+            "workload": describe(w),
+            "tokens_per_step": tokens,
+            "kv_entries_per_step": int(sum(w.n) * w.H),
+            "entries_per_s": sum(w.n) * w.H / step_s,
+            "stage_ms": {"score": avg[0], "select": avg[1], "compact": avg[2]},
+            "hbm_algorithmic_bytes_per_step": ab["total"],
+            "hbm_algorithmic_gbps": ab["total"] / step_s / 1e9,
+            "hbm_frac_of_peak": ab["total"] / step_s / 1e9 / HBM_PEAK_GBPS,
+            "select_compact_hbm_gbps": (ab["select"] + ab["compact"]) / ((avg[1] + avg[2]) * 1e-3) / 1e9,
+            "mfma_util": achieved_tf / MFMA_BF16_PEAK_TFLOPS,
+        },
+        "roofline": {
+            "kernel": "score_mfma (kvc_score)",
+            "bound": "mfma",
+            "achieved": achieved_tf,
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_tf / MFMA_BF16_PEAK_TFLOPS,
+            "traffic": traffic,
+            "flops_per_launch": flops,
+            "launch_ms": avg[0],
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

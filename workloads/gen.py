@@ -27,8 +27,9 @@ trajectory uses the ratchet budget m_k = min(30000, floor(512 * 1.75**k)).
 from __future__ import annotations
 
 import math
-from concurrent.futures import ProcessPoolExecutor
 from dataclasses import dataclass, replace
+import mmap
+import multiprocessing
 import os
 
 import numpy as np
@@ -47,8 +48,10 @@ def _rng(cfg_id: int, s: int, h: int, tag: int) -> np.random.Generator:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (nearest, ties to even) and return the 16-bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    r = u + np.uint32(0x7FFF)          # finite inputs: cannot wrap (largest is 0xFF7FFFFF)
+    r += (u >> 16) & np.uint32(1)
+    r >>= 16
     return r.astype(np.uint16)
 
 
@@ -246,21 +249,33 @@ def block_tables(w: Workload) -> tuple[np.ndarray, int]:
     return t, total
 
 
-def _unit_kv(args):
-    w, s, h = args
-    return unit_keys(w, s, h), unit_values(w, s, h)
+def _shared_zeros(shape, dtype) -> np.ndarray:
+    """Zeroed array in an anonymous shared mapping, so forked workers can fill it in place."""
+    count = int(np.prod(shape))
+    nbytes = count * np.dtype(dtype).itemsize
+    mm = mmap.mmap(-1, max(nbytes, 1))
+    return np.frombuffer(mm, dtype=dtype, count=count).reshape(shape)
 
 
-def _unit_q(args):
-    w, s, h = args
-    return unit_queries(w, s, h)
+def _run_all(fn, items):
+    for x in items:
+        fn(x)
 
 
-def _pmap(fn, items, workers):
+def _pfill(fn, items, workers):
+    """Run fn over items in forked worker processes that write into shared arrays."""
     if workers <= 1 or len(items) <= 1:
-        return [fn(x) for x in items]
-    with ProcessPoolExecutor(max_workers=workers) as ex:
-        return list(ex.map(fn, items, chunksize=max(1, len(items) // (4 * workers))))
+        _run_all(fn, items)
+        return
+    ctx = multiprocessing.get_context("fork")
+    procs = [ctx.Process(target=_run_all, args=(fn, items[i::workers])) for i in range(min(workers, len(items)))]
+    for p in procs:
+        p.start()
+    for p in procs:
+        p.join()
+    bad = [p.exitcode for p in procs if p.exitcode != 0]
+    if bad:
+        raise RuntimeError(f"input generation worker failed with exit codes {bad}")
 
 
 def default_workers() -> int:
@@ -276,9 +291,13 @@ def _storage_dtype(w: Workload):
 
 
 def _queries_and_bias(w: Workload, workers: int):
-    units = [(w, s, h) for s in range(w.S) for h in range(w.H)]
-    qs = _pmap(_unit_q, units, workers)
-    Q = np.stack(qs).reshape(w.S, w.H * w.G, w.q, w.d)
+    Q = _shared_zeros((w.S, w.H * w.G, w.q, w.d), _storage_dtype(w))
+
+    def fill(args):
+        _, s, h = args
+        Q[s, h * w.G:(h + 1) * w.G] = unit_queries(w, s, h).reshape(w.G, w.q, w.d)
+
+    _pfill(fill, [(w, s, h) for s in range(w.S) for h in range(w.H)], workers)
     bias = None
     if w.bias_tail:
         bias = np.zeros((w.S, w.n_max), dtype=np.float32)
@@ -289,15 +308,16 @@ def _queries_and_bias(w: Workload, workers: int):
 
 def build_contiguous(w: Workload, workers: int = 1) -> dict:
     """Contiguous layout: K, V [S][H][n_max][d]; Q [S][H*G][q][d]; bias [S][n_max] or None."""
-    units = [(w, s, h) for s in range(w.S) for h in range(w.H)]
-    kv = _pmap(_unit_kv, units, workers)
     dt = _storage_dtype(w)
-    K = np.zeros((w.S, w.H, w.n_max, w.d), dtype=dt)
-    V = np.zeros((w.S, w.H, w.n_max, w.d), dtype=dt)
-    for (_, s, h), (k, v) in zip(units, kv):
-        K[s, h, :w.n[s]] = k
-        V[s, h, :w.n[s]] = v
-    del kv
+    K = _shared_zeros((w.S, w.H, w.n_max, w.d), dt)
+    V = _shared_zeros((w.S, w.H, w.n_max, w.d), dt)
+
+    def fill(args):
+        _, s, h = args
+        K[s, h, :w.n[s]] = unit_keys(w, s, h)
+        V[s, h, :w.n[s]] = unit_values(w, s, h)
+
+    _pfill(fill, [(w, s, h) for s in range(w.S) for h in range(w.H)], workers)
     Q, bias = _queries_and_bias(w, workers)
     return dict(K=K, V=V, Q=Q, bias=bias, n=np.array(w.n, dtype=np.int32), m=np.array(w.m, dtype=np.int32))
 
@@ -307,19 +327,19 @@ def build_paged(w: Workload, workers: int = 1) -> dict:
     table, total = block_tables(w)
     B = w.block_size
     dt = _storage_dtype(w)
-    k_pool = np.zeros((total, B, w.H, w.d), dtype=dt)
-    v_pool = np.zeros((total, B, w.H, w.d), dtype=dt)
-    for s in range(w.S):
-        units = [(w, s, h) for h in range(w.H)]
-        kv = _pmap(_unit_kv, units, workers)
+    k_pool = _shared_zeros((total, B, w.H, w.d), dt)
+    v_pool = _shared_zeros((total, B, w.H, w.d), dt)
+    def fill(args):
+        _, s, h = args
         nb, n = w.blocks_of(s), w.n[s]
         blk = table[s, :nb]
-        for (_, _, h), (k, v) in zip(units, kv):
-            kp = np.zeros((nb * B, w.d), dtype=dt)
-            vp = np.zeros((nb * B, w.d), dtype=dt)
-            kp[:n], vp[:n] = k, v
-            k_pool[blk, :, h, :] = kp.reshape(nb, B, w.d)
-            v_pool[blk, :, h, :] = vp.reshape(nb, B, w.d)
+        for pool, x in ((k_pool, unit_keys(w, s, h)), (v_pool, unit_values(w, s, h))):
+            xp = np.zeros((nb * B, w.d), dtype=dt)
+            xp[:n] = x
+            pool[blk, :, h, :] = xp.reshape(nb, B, w.d)
+
+    # units write disjoint (block, head) slices of the pools
+    _pfill(fill, [(w, s, h) for s in range(w.S) for h in range(w.H)], workers)
     Q, bias = _queries_and_bias(w, workers)
     return dict(k_pool=k_pool, v_pool=v_pool, table=table, Q=Q, bias=bias,
                 n=np.array(w.n, dtype=np.int32), m=np.array(w.m, dtype=np.int32))
