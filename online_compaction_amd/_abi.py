@@ -63,11 +63,12 @@ _SIGS = {
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
-    """Load libkvc.so (built by online_compaction_amd.build); raises if it is not there."""
+    """Load libkvc.so (built by online_compaction_amd.build, or the file named by $KVC_LIB);
+    raises if it is not there."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    p = path or os.environ.get("KVC_LIB") or LIB_PATH
     if not os.path.exists(p):
         raise ImportError(f"libkvc.so not built at {p}: run `python -m online_compaction_amd.build`")
     lib = ctypes.CDLL(p)

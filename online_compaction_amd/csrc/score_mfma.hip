@@ -25,9 +25,17 @@ namespace kvc {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSub = 8;                 // 16-wide subtiles per wave held in registers
-constexpr int kPerWave = 16 * kSub;     // 128 keys (score) or rows (lse) per wave
-constexpr int kPerBlock = 4 * kPerWave; // 512 per workgroup
+constexpr int kSub = 8;                 // 16-wide subtiles per wave held in registers (LSE pass)
+constexpr int kPerWave = 16 * kSub;     // 128 rows per wave (LSE pass)
+constexpr int kPerBlock = 4 * kPerWave; // 512 per workgroup (LSE pass)
+#ifndef KVC_SCORE_KSUB
+#define KVC_SCORE_KSUB 8
+#endif
+#ifndef KVC_SCORE_OCC
+#define KVC_SCORE_OCC 2
+#endif
+constexpr int kScoreSub = KVC_SCORE_KSUB;           // key subtiles per wave (score pass)
+constexpr int kScoreKeys = 4 * 16 * kScoreSub;      // keys per workgroup (score pass)
 constexpr int kStage = 64;              // rows / keys per LDS stage
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
@@ -57,7 +65,7 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * 256 + ((ch
 // lse: natural-log LSE per proxy row, [S][H*G][q] == [unit][R].
 // ------------------------------------------------------------------------------------------------
 template <bool PAGED, bool BIAS>
-__global__ __launch_bounds__(kThreads, 2) void score_mfma(
+__global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, float* __restrict__ scores,
     int H, int R, int64_t n_max, float scale, SeqTable T) {
@@ -68,7 +76,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma(
   const int i = find_seq(T, t);
   const int n = T.n[i];
   const int s = T.first + i;
-  const int tiles = (n + kPerBlock - 1) / kPerBlock;
+  const int tiles = (n + kScoreKeys - 1) / kScoreKeys;
   const int local = t - T.start[i];
   const int h = local / tiles;
   const int kt = local - h * tiles;
@@ -78,11 +86,11 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma(
   const int32_t* trow = PAGED ? table + (int64_t)s * max_blocks : nullptr;
 
   // keys of this wave, held for the whole row sweep
-  bf16x8 kb[kSub][4];
-  float bb[kSub];
-  const int key0 = kt * kPerBlock + wave * kPerWave;
+  bf16x8 kb[kScoreSub][4];
+  float bb[kScoreSub];
+  const int key0 = kt * kScoreKeys + wave * (16 * kScoreSub);
 #pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
+  for (int sub = 0; sub < kScoreSub; ++sub) {
     const int key = key0 + sub * 16 + c16;
     if (key < n) {
       const u32x4* p = key_row<PAGED>(k, trow, H, h, n_max, unit, key);
@@ -125,9 +133,9 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma(
     if (tid < kStage) nbs[buf][tid] = prenb;
   };
 
-  float ssum[kSub];
+  float ssum[kScoreSub];
 #pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) ssum[sub] = 0.0f;
+  for (int sub = 0; sub < kScoreSub; ++sub) ssum[sub] = 0.0f;
 
   load_stage(0);
   store_stage(0);
@@ -142,15 +150,15 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(&qs[buf][swz(row, 4 * ks + g)]);
       const f32x4 nb4 = *reinterpret_cast<const f32x4*>(&nbs[buf][rt * 16 + 4 * g]);
-      f32x4 acc[kSub];
+      f32x4 acc[kScoreSub];
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) acc[sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      for (int sub = 0; sub < kScoreSub; ++sub) acc[sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int sub = 0; sub < kSub; ++sub) acc[sub] = mfma16(a[ks], kb[sub][ks], acc[sub]);
+        for (int sub = 0; sub < kScoreSub; ++sub) acc[sub] = mfma16(a[ks], kb[sub][ks], acc[sub]);
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
+      for (int sub = 0; sub < kScoreSub; ++sub) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           float x = __builtin_fmaf(acc[sub][e], a2, nb4[e]);
@@ -165,7 +173,7 @@ __global__ __launch_bounds__(kThreads, 2) void score_mfma(
 
   const float invR = 1.0f / (float)R;
 #pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
+  for (int sub = 0; sub < kScoreSub; ++sub) {
     float v = ssum[sub];
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
@@ -348,7 +356,7 @@ __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ pa
 // ------------------------------------------------------------------------------------------------
 // launchers
 // ------------------------------------------------------------------------------------------------
-int score_mfma_tiles(int n) { return (n + kPerBlock - 1) / kPerBlock; }
+int score_mfma_tiles(int n) { return (n + kScoreKeys - 1) / kScoreKeys; }
 int lse_mfma_row_blocks(int R) { return (R + kPerBlock - 1) / kPerBlock; }
 
 hipError_t launch_score_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
