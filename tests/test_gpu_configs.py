@@ -1,0 +1,235 @@
+"""GPU parity on the five named workloads at full size, in the launch configuration the benchmark
+times (every sequence/layer of the batch in one call per stage).
+
+The oracle recomputes every output of the smaller workloads; for the 36-layer trajectory and the
+64-session batch it recomputes sampled units in full (float64), and checks every unit through
+properties that hold at any size: scores in [0, 1] with 1/n <= sum_j s_j^2 <= 1, the kept list is
+exactly the top-m of the GPU's own scores, and compaction is bit-exact given the kept list.
+"""
+import time
+
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import oracle as O
+from tests.parity import (check_gather, check_kept_form, check_scores, check_selection_band,
+                          check_selection_exact, say)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _P():
+    from online_compaction_amd import path as P
+    return P
+
+
+def _workers():
+    return W.gen.default_workers()
+
+
+def _square_sum_bounds(s, n, tag):
+    ss = float(np.sum(np.asarray(s, dtype=np.float64) ** 2))
+    assert np.all(s >= 0) and np.all(s <= 1 + 1e-6), f"{tag}: score outside [0, 1]"
+    # with the LSE of the same n keys every proxy row's weights sum to 1
+    assert 1.0 / n * (1 - 1e-3) <= ss <= 1 + 1e-3, f"{tag}: sum of squared scores {ss} outside [1/n, 1]"
+
+
+def _full_contig(w, data, scores, kept, k_out, v_out):
+    worst = 0.0
+    for s in range(w.S):
+        for h in range(w.H):
+            n, m = w.n[s], w.m[s]
+            tag = f"{w.name} s={s} h={h}"
+            b = None if data["bias"] is None else data["bias"][s, :n]
+            ref = O.score_unit(O.unit_rows(data["Q"], s, h, w.G), data["K"][s, h, :n], w.dtype, w.logit_scale, b)
+            worst = max(worst, check_scores(scores[s, h, :n], ref, tag))
+            check_kept_form(kept[s, h], m, n, tag)
+            check_selection_exact(kept[s, h], scores[s, h, :n], m, tag)
+            check_selection_band(kept[s, h], ref, m, tag)
+            check_gather(data["K"][s, h, :n], kept[s, h], k_out[s, h], m, tag)
+            check_gather(data["V"][s, h, :n], kept[s, h], v_out[s, h], m, tag)
+    return worst
+
+
+@pytest.mark.parametrize("name", ["c1", "c2a", "c2b"])
+def test_small_workloads_full(name):
+    P = _P()
+    w = W.spec(name)
+    say(f"[case] {name}: S={w.S} H={w.H} R={w.R} n={w.n[0]} m={w.m[0]} {w.dtype}")
+    data = W.build_contiguous(w, _workers())
+    b = P.contiguous_batch(data["Q"], data["K"], data["V"], data["n"], data["m"], w.G, w.logit_scale)
+    o = P.allocate(b)
+    P.run(b, o)
+    torch.cuda.synchronize()
+    worst = _full_contig(w, data, P.host_array(o.scores), P.host_array(o.kept), P.host_array(o.k_out),
+                         P.host_array(o.v_out))
+    say(f"[ok] {name}: worst score rel err {worst:.3g}")
+
+
+def test_c4_paged_action_queries_all_budgets():
+    """1 layer, 8 KV heads, n = 33000, 1320 action-token proxy rows, +0.5 bias on the last 25%;
+    budgets m_k = min(30000, floor(512 * 1.75^k)), k = 0..6, each compacted in place."""
+    P = _P()
+    w0 = W.spec("c4", 0)
+    say(f"[case] c4: H={w0.H} R={w0.R} n={w0.n[0]} paged B={w0.block_size}, budgets k=0..6")
+    data = W.build_paged(w0, _workers())
+    b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], data["n"], data["m"], w0.G,
+                      w0.logit_scale, w0.block_size, n_max=w0.n_max, bias=data["bias"])
+    o = P.allocate(b)
+    P.run_score(b, o)
+    torch.cuda.synchronize()
+    scores = P.host_array(o.scores)
+    n = w0.n[0]
+    refs = {}
+    t0 = time.time()
+    for h in range(w0.H):
+        keys = O.paged_unit_keys(data["k_pool"], data["table"][0], n, h, w0.block_size)
+        refs[h] = O.score_unit(O.unit_rows(data["Q"], 0, h, w0.G), keys, w0.dtype, w0.logit_scale,
+                               data["bias"][0, :n])
+        check_scores(scores[0, h, :n], refs[h], f"c4 h={h}")
+    say(f"[ok] c4 scores match ({time.time() - t0:.1f} s of oracle)")
+    pristine = (b.k_pool.clone(), b.v_pool.clone(), b.table.clone())
+    for k in range(7):
+        w = W.spec("c4", k)
+        m = w.m[0]
+        b.k_pool.copy_(pristine[0])
+        b.v_pool.copy_(pristine[1])
+        b.table.copy_(pristine[2])
+        b.m = np.array([m], dtype=np.int32)
+        b.m_max = m
+        o.kept = torch.full((1, w.H, m), -1, dtype=torch.int32, device="cuda")
+        o.freed.fill_(-1)
+        P.run_select(b, o)
+        P.run_compact(b, o)
+        torch.cuda.synchronize()
+        kept = P.host_array(o.kept)
+        for h in range(w.H):
+            check_kept_form(kept[0, h], m, n, f"c4k{k} h={h}")
+            check_selection_exact(kept[0, h], scores[0, h, :n], m, f"c4k{k} h={h}")
+            check_selection_band(kept[0, h], refs[h], m, f"c4k{k} h={h}")
+        # stage-wise: the oracle's plan applied to the GPU's kept sets
+        kp = data["k_pool"].copy()
+        vp = data["v_pool"].copy()
+        table = data["table"].copy()
+        plans = [O.paged_plan(n, m, w.block_size, kept[0, h]) for h in range(w.H)]
+        for h in range(w.H):
+            O.apply_paged_copy(kp, vp, table[0], h, plans[h])
+        new, freed = O.table_update(table[0], n, m, w.block_size)
+        assert np.array_equal(P.host_array(b.k_pool), kp) and np.array_equal(P.host_array(b.v_pool), vp)
+        assert np.array_equal(P.host_array(b.table)[0], new)
+        F = len(freed)
+        assert o.freed_counts[0] == F == -(-n // 16) - -(-m // 16)
+        assert np.array_equal(P.host_array(o.freed)[0, :F], freed)
+        moved = sum(len(p.src) for p in plans)
+        say(f"[ok] c4k{k}: m={m}, freed {F} blocks, {moved} rows moved over {w.H} heads")
+
+
+def test_c3_full_trajectory_36_layers():
+    """36 layers x 8 KV heads, n = 33000, R = 4096, supplied float32 LSE, m = 6600, one call per
+    stage over every layer. Oracle on two sampled units; properties and compaction on all 288."""
+    import online_compaction_amd as oc
+    P = _P()
+    w = W.spec("c3")
+    t0 = time.time()
+    data = W.build_contiguous(w, _workers())
+    say(f"[case] c3 inputs in {time.time() - t0:.1f} s")
+    b = P.contiguous_batch(data["Q"], data["K"], data["V"], data["n"], data["m"], w.G, w.logit_scale)
+    # supplied LSE: the GPU's own LSE pass for every unit, then the oracle's for the sampled ones
+    lse = torch.empty((w.S, w.H * w.G, w.q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, oc.kvc_lse_workspace_size(b.shape, b.kview())), dtype=torch.uint8, device="cuda")
+    oc.kvc_lse(b.shape, b.q, b.kview(), None, lse, ws)
+    torch.cuda.synchronize()
+    gpu_lse = lse.cpu().numpy()
+    sampled = [(0, 0), (35, 7)]
+    ref_lse = {}
+    for s, h in sampled:
+        L = O.lse_unit(O.unit_rows(data["Q"], s, h, w.G), data["K"][s, h], w.dtype, w.logit_scale)
+        got = gpu_lse[s, h * w.G:(h + 1) * w.G].reshape(-1)
+        np.testing.assert_allclose(got, L, rtol=2e-6, atol=2e-6)
+        ref_lse[(s, h)] = L.astype(np.float32)
+        gpu_lse[s, h * w.G:(h + 1) * w.G] = ref_lse[(s, h)].reshape(w.G, w.q)
+    say(f"[ok] c3 LSE pass matches the oracle on {sampled}")
+    b.lse = P.device_tensor(gpu_lse)
+    o = P.allocate(b)
+    P.run(b, o)
+    torch.cuda.synchronize()
+    scores, kept = P.host_array(o.scores), P.host_array(o.kept)
+    k_out, v_out = P.host_array(o.k_out), P.host_array(o.v_out)
+    n, m = w.n[0], w.m[0]
+    for s, h in sampled:
+        tag = f"c3 s={s} h={h}"
+        ref = O.score_unit(O.unit_rows(data["Q"], s, h, w.G), data["K"][s, h], w.dtype, w.logit_scale, None,
+                           ref_lse[(s, h)].astype(np.float64))
+        worst = check_scores(scores[s, h, :n], ref, tag)
+        swaps = check_selection_band(kept[s, h], ref, m, tag)
+        say(f"[ok] {tag}: worst score rel err {worst:.3g}, tie-band swaps {swaps}")
+    for s in range(w.S):
+        for h in range(w.H):
+            tag = f"c3 s={s} h={h}"
+            _square_sum_bounds(scores[s, h, :n], n, tag)
+            check_kept_form(kept[s, h], m, n, tag)
+            check_selection_exact(kept[s, h], scores[s, h, :n], m, tag)
+        K_s, V_s = data["K"][s], data["V"][s]
+        idx = kept[s].astype(np.int64)
+        assert np.array_equal(k_out[s], np.take_along_axis(K_s, idx[:, :, None], axis=1)), f"c3 K layer {s}"
+        assert np.array_equal(v_out[s], np.take_along_axis(V_s, idx[:, :, None], axis=1)), f"c3 V layer {s}"
+    say("[ok] c3: all 288 units pass the property and compaction checks")
+
+
+def test_c5_variable_length_sessions():
+    """64 sessions, n ~ U[8192, 131072], 4 KV heads x 8 query heads, q = 256, paged with a
+    permuted block table, ratio 0.2; one call per stage for the whole batch. Oracle in full on
+    the shortest session and one head of the longest; compaction stage-wise on every session."""
+    P = _P()
+    w = W.spec("c5")
+    t0 = time.time()
+    data = W.build_paged(w, _workers())
+    say(f"[case] c5 inputs in {time.time() - t0:.1f} s: {data['k_pool'].shape[0]} blocks")
+    b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], data["n"], data["m"], w.G,
+                      w.logit_scale, w.block_size, n_max=w.n_max)
+    o = P.allocate(b)
+    P.run(b, o)
+    torch.cuda.synchronize()
+    scores, kept = P.host_array(o.scores), P.host_array(o.kept)
+    say("[ok] c5 GPU pass done")
+    lens = np.array(w.n)
+    short, long_ = int(lens.argmin()), int(lens.argmax())
+    for s, heads in ((short, range(w.H)), (long_, [0])):
+        n, m = w.n[s], w.m[s]
+        for h in heads:
+            tag = f"c5 s={s} h={h} n={n}"
+            keys = O.paged_unit_keys(data["k_pool"], data["table"][s], n, h, w.block_size)
+            ref = O.score_unit(O.unit_rows(data["Q"], s, h, w.G), keys, w.dtype, w.logit_scale)
+            worst = check_scores(scores[s, h, :n], ref, tag)
+            check_selection_band(kept[s, h], ref, m, tag)
+            say(f"[ok] {tag}: worst score rel err {worst:.3g}")
+    for s in range(w.S):
+        n, m = w.n[s], w.m[s]
+        for h in range(w.H):
+            tag = f"c5 s={s} h={h}"
+            _square_sum_bounds(scores[s, h, :n], n, tag)
+            check_kept_form(kept[s, h], m, n, tag)
+            check_selection_exact(kept[s, h], scores[s, h, :n], m, tag)
+    say("[ok] c5 score properties and selection on all 256 units")
+    # stage-wise compaction of every session
+    kp, vp, table = data["k_pool"], data["v_pool"], data["table"].copy()
+    freed = {}
+    moved = 0
+    for s in range(w.S):
+        n, m = w.n[s], w.m[s]
+        plans = [O.paged_plan(n, m, w.block_size, kept[s, h, :m]) for h in range(w.H)]
+        for h in range(w.H):
+            O.apply_paged_copy(kp, vp, table[s], h, plans[h])
+            moved += len(plans[h].src)
+        table[s], freed[s] = O.table_update(table[s], n, m, w.block_size)
+    say(f"[ok] c5 oracle compaction applied ({moved} rows moved)")
+    assert np.array_equal(P.host_array(b.k_pool), kp), "c5 K pool"
+    assert np.array_equal(P.host_array(b.v_pool), vp), "c5 V pool"
+    assert np.array_equal(P.host_array(b.table), table), "c5 block table"
+    fr = P.host_array(o.freed)
+    for s in range(w.S):
+        F = len(freed[s])
+        assert o.freed_counts[s] == F and np.array_equal(fr[s, :F], freed[s]), f"c5 freed list {s}"
+    say("[ok] c5 pools, tables and freed lists are bit-exact")
