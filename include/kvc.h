@@ -53,27 +53,35 @@ typedef enum {
 
 typedef enum { KVC_F32 = 0, KVC_BF16 = 1 } kvc_dtype;
 
-/* Problem shape (host memory). */
+/* Problem shape (host memory).
+ * The n_s scored keys of sequence s are the cache positions [start_s, start_s + n_s), where
+ * start_s = seq_starts[s] (0 when seq_starts is NULL). A nonzero start scores, selects and
+ * compacts one segment of a longer cache -- e.g. one agent turn, with proxy queries taken from the
+ * turns that followed it ("Practical Online KV Cache Compaction for LLM Agents", delayed
+ * future-turn queries). Per-key arrays (bias, scores, kept) are indexed relative to the segment. */
 typedef struct {
-  int32_t num_seqs;        /* S >= 1                                                         */
-  int32_t num_kv_heads;    /* H >= 1                                                         */
-  int32_t group;           /* G >= 1 query heads per KV head                                 */
-  int32_t num_queries;     /* q >= 1 proxy queries per query head                            */
-  int32_t head_dim;        /* d; this build supports 128 only (else KVC_ERR_UNSUPPORTED)     */
-  int32_t n_max;           /* token stride of contiguous K/V, of bias and of scores; >= n_s  */
-  const int32_t* seq_lens; /* host [S]: n_s >= 1 keys in sequence s                          */
-  float scale;             /* logit scale c (1/sqrt(d) in the usual attention)               */
+  int32_t num_seqs;          /* S >= 1                                                         */
+  int32_t num_kv_heads;      /* H >= 1                                                         */
+  int32_t group;             /* G >= 1 query heads per KV head                                 */
+  int32_t num_queries;       /* q >= 1 proxy queries per query head                            */
+  int32_t head_dim;          /* d; this build supports 128 only (else KVC_ERR_UNSUPPORTED)     */
+  int32_t n_max;             /* token stride of contiguous K/V, bias and scores;
+                                start_s + n_s <= n_max for contiguous K/V, n_s <= n_max always */
+  const int32_t* seq_lens;   /* host [S]: n_s >= 1 keys scored in sequence s                   */
+  float scale;               /* logit scale c (1/sqrt(d) in the usual attention)               */
+  const int32_t* seq_starts; /* host [S]: start_s >= 0, or NULL for all zero; paged caches
+                                need start_s to be a multiple of the block size               */
 } kvc_shape;
 
 /* How keys are addressed. Contiguous: data is [S][H][n_max][d]. Paged (vLLM-style pool):
- * data is [num_blocks][block_size][H][d] and position j of sequence s lives in physical block
- * block_table[s * max_blocks + j / block_size], slot j % block_size. */
+ * data is [num_blocks][block_size][H][d] and cache position p of sequence s lives in physical
+ * block block_table[s * max_blocks + p / block_size], slot p % block_size. */
 typedef struct {
   const void* data;            /* device                                                  */
   kvc_dtype dtype;             /* element type of K (and of the queries)                  */
   int32_t block_size;          /* 0 = contiguous; else B (this build: 16)                 */
   const int32_t* block_table;  /* device [S][max_blocks] (paged only, else NULL)          */
-  int32_t max_blocks;          /* row stride of block_table; ceil(n_s / B) <= max_blocks  */
+  int32_t max_blocks;          /* row stride of block_table; ceil((start_s + n_s) / B) <= max_blocks */
 } kvc_kv_view;
 
 /* ---------------------------------------------------------------------------------------------
@@ -82,7 +90,7 @@ typedef struct {
  * that have it skip this call.
  *   q       device [S][H*G][q][d], dtype of K
  *   k       key view
- *   bias    device [S][n_max] float32 additive logit bias, or NULL
+ *   bias    device [S][n_max] float32 additive logit bias (segment-relative), or NULL
  *   lse_out device out [S][H*G][q] float32, natural log
  *   ws      device workspace of at least kvc_lse_workspace_size(shape, k) bytes (any alignment
  *           of 256 bytes or more); its contents are scratch
@@ -100,7 +108,7 @@ kvc_status kvc_lse(const kvc_shape* shape, const void* q, const kvc_kv_view* k, 
  *           used as given, e.g. one covering more keys makes the weights sum to less than 1.
  *           It must not lie more than ~5 below the exact value (the weights' squares are
  *           accumulated with a 2^100 offset and would overflow float32).
- *   scores  device out [S][H][n_max] float32; entries j >= n_s are not written.
+ *   scores  device out [S][H][n_max] float32, segment-relative; entries j >= n_s not written.
  * Accuracy: within 1e-3 relative of the float64 definition for every score >= 1e-30
  * (squared weights below 2^-226 are flushed to zero). Deterministic.
  * ------------------------------------------------------------------------------------------- */
@@ -122,7 +130,9 @@ kvc_status kvc_select_topm(const kvc_shape* shape, const float* scores, const in
 
 /* ---------------------------------------------------------------------------------------------
  * kvc_compact_contig -- order-preserving gather of the kept rows ([TE] keep the original K, V):
- * k_out[s][h][r] = k[s][h][kept[s][h][r]] for r < m_s, and the same for V, bit for bit.
+ * k_out[s][h][r] = k[s][h][start_s + kept[s][h][r]] for r < m_s, and the same for V, bit for bit.
+ * For a segment (start_s > 0) this is the compacted segment; the caller splices it between the
+ * untouched prefix and suffix.
  *   k, v          device [S][H][n_max][d] of dtype
  *   kept          device [S][H][m_max] int32, strictly ascending, < n_s (as from select)
  *   k_out, v_out  device out [S][H][m_max][d]; rows r >= m_s are not written
@@ -133,25 +143,34 @@ kvc_status kvc_compact_contig(const kvc_shape* shape, kvc_dtype dtype, const voi
 
 /* ---------------------------------------------------------------------------------------------
  * kvc_compact_paged -- in-place conflict-free compaction of a paged pool ([ACT] slot plan).
- * Per sequence: N = ceil(n_s/B), X = ceil(m_s/B), window W = [(N-X)B, (N-X)B + m_s). Per head:
- * sources = kept positions outside W, holes = positions of W not kept (both ascending); the
- * i-th source's K and V rows are copied to the i-th hole, all pairs in one parallel pass (a
- * source is never a hole, so no slot is both read and written). Kept positions inside W stay
- * where they are, so the compacted order is not the original order. Afterwards:
- *   block_table[s][0..X)  = old block_table[s][N-X..N)   (new length m_s)
- *   block_table[s][X..N)  = -1; entries >= N untouched
- *   freed_blocks[s][0..N-X) = old block_table[s][0..N-X) (logical order); rest untouched
- *   freed_counts[s] (host, written during the call) = N - X = ceil(n_s/B) - ceil(m_s/B)
+ * Per sequence, with a = start_s (a multiple of B), n = n_s, L = cache_lens[s] (the sequence's
+ * total length; a + n when cache_lens is NULL): N = ceil(n/B), X = ceil(m_s/B), F = N - X,
+ * window W = [a + F*B, a + F*B + m_s). Per head: sources = kept positions outside W, holes =
+ * positions of W not kept (both ascending, all relative positions offset by a); the i-th
+ * source's K and V rows are copied to the i-th hole, all pairs in one parallel pass (a source is
+ * never a hole, so no slot is both read and written). Kept positions inside W stay where they
+ * are, so the compacted order is not the original order. Afterwards, with b = a/B and
+ * NT = ceil(L/B) table entries in use:
+ *   freed_blocks[s][0..F)      = old block_table[s][b..b+F) (logical order); rest untouched
+ *   block_table[s][b..NT-F)    = old block_table[s][b+F..NT)  (the window, then any later blocks)
+ *   block_table[s][NT-F..NT)   = -1; entries outside [b, NT) untouched
+ *   freed_counts[s] (host, written during the call) = F = ceil(n/B) - ceil(m_s/B)
+ * The sequence's new length is a + m_s if the segment ends it (a + n = L), else L - F*B.
+ * Positions after the segment keep their bytes and only
+ * change block-table entries, which is why a segment followed by more tokens (a + n < L) must
+ * have n and m_s multiples of B (otherwise the window's last block would hold a hole).
  * Source slots keep their bytes (copy, not move).
- *   k_pool, v_pool  device [num_blocks][B][H][d] of dtype, modified in place
- *   block_table     device in/out [S][max_blocks] int32 (valid, distinct ids for j < n_s)
- *   kept            device [S][H][m_max] int32, strictly ascending, < n_s
+ *   k_pool, v_pool  device [num_blocks][B][H][d] of dtype, modified in place (distinct buffers)
+ *   block_table     device in/out [S][max_blocks] int32 (valid, distinct ids for p < L)
+ *   kept            device [S][H][m_max] int32, strictly ascending, < n_s (segment-relative)
  *   m               host [S]
+ *   cache_lens      host [S] total length L >= start_s + n_s of each sequence, or NULL
  * ------------------------------------------------------------------------------------------- */
 kvc_status kvc_compact_paged(const kvc_shape* shape, kvc_dtype dtype, void* k_pool, void* v_pool,
                              int32_t block_size, int32_t* block_table, int32_t max_blocks,
                              const int32_t* kept, const int32_t* m, int32_t m_max,
-                             int32_t* freed_blocks, int32_t* freed_counts, void* stream);
+                             const int32_t* cache_lens, int32_t* freed_blocks, int32_t* freed_counts,
+                             void* stream);
 
 /* Static text for a status code; never NULL. */
 const char* kvc_status_string(kvc_status status);

@@ -29,7 +29,8 @@ class KvcError(RuntimeError):
 class _Shape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("num_queries", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_max", ctypes.c_int32),
-                ("seq_lens", ctypes.POINTER(ctypes.c_int32)), ("scale", ctypes.c_float)]
+                ("seq_lens", ctypes.POINTER(ctypes.c_int32)), ("scale", ctypes.c_float),
+                ("seq_starts", ctypes.POINTER(ctypes.c_int32))]
 
 
 class _KView(ctypes.Structure):
@@ -54,7 +55,8 @@ _SIGS = {
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_compact_paged": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
-                                         ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p,
                                          ctypes.POINTER(ctypes.c_int32), ctypes.c_void_p]),
     "kvc_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "kvc_last_error": (ctypes.c_char_p, []),
@@ -89,14 +91,20 @@ class Shape:
     num_queries: int
     head_dim: int
     n_max: int
-    seq_lens: object  # host ints [S]
+    seq_lens: object  # host ints [S]: keys scored per sequence
     scale: float
+    seq_starts: object = None  # host ints [S]: cache position of each sequence's first scored key
 
     def c(self):
         lens = np.ascontiguousarray(np.asarray(self.seq_lens, dtype=np.int32))
+        starts = None
+        sp = None
+        if self.seq_starts is not None:
+            starts = np.ascontiguousarray(np.asarray(self.seq_starts, dtype=np.int32))
+            sp = starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         sh = _Shape(self.num_seqs, self.num_kv_heads, self.group, self.num_queries, self.head_dim, self.n_max,
-                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(self.scale))
-        return sh, lens  # keep `lens` alive while `sh` is used
+                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(self.scale), sp)
+        return sh, (lens, starts)  # keep the arrays alive while `sh` is used
 
 
 @dataclass
@@ -225,7 +233,7 @@ def kvc_compact_contig(shape: Shape, dtype: int, k, v, kept, m, m_max: int, k_ou
 
 
 def kvc_compact_paged(shape: Shape, dtype: int, k_pool, v_pool, block_size: int, block_table, max_blocks: int,
-                      kept, m, m_max: int, freed_blocks, stream=None) -> np.ndarray:
+                      kept, m, m_max: int, freed_blocks, cache_lens=None, stream=None) -> np.ndarray:
     """Returns freed_counts (host int32 [S])."""
     S, H = shape.num_seqs, shape.num_kv_heads
     _need(block_table, S * max_blocks * 4, "block_table")
@@ -233,9 +241,10 @@ def kvc_compact_paged(shape: Shape, dtype: int, k_pool, v_pool, block_size: int,
     _need(kept, S * H * m_max * 4, "kept")
     sh, _keep = shape.c()
     marr, mp = _host_i32(m)
+    carr, cp = (None, None) if cache_lens is None else _host_i32(cache_lens)
     counts = np.zeros(S, dtype=np.int32)
     _check(load().kvc_compact_paged(ctypes.byref(sh), int(dtype), _ptr(k_pool), _ptr(v_pool), int(block_size),
-                                    _ptr(block_table), int(max_blocks), _ptr(kept), mp, int(m_max),
+                                    _ptr(block_table), int(max_blocks), _ptr(kept), mp, int(m_max), cp,
                                     _ptr(freed_blocks), counts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
                                     _stream(stream)), "kvc_compact_paged")
     return counts

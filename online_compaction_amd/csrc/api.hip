@@ -73,6 +73,8 @@ kvc_status ok() {
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+int seq_start(const kvc_shape* sh, int s) { return sh->seq_starts ? sh->seq_starts[s] : 0; }
+
 kvc_status check_shape(const kvc_shape* sh) {
   if (!sh) return fail(KVC_ERR_INVALID_ARGUMENT, "shape is NULL");
   if (sh->num_seqs < 1 || sh->num_kv_heads < 1 || sh->group < 1 || sh->num_queries < 1)
@@ -87,6 +89,20 @@ kvc_status check_shape(const kvc_shape* sh) {
     const int n = sh->seq_lens[s];
     if (n < 1 || n > sh->n_max)
       return fail(KVC_ERR_INVALID_ARGUMENT, "seq_lens[%d] = %d outside [1, n_max = %d]", s, n, sh->n_max);
+    const int a = seq_start(sh, s);
+    if (a < 0 || (int64_t)a + n > kMaxLen)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "seq_starts[%d] = %d out of range", s, a);
+  }
+  return KVC_OK;
+}
+
+// Contiguous K/V rows of a segment must lie inside the n_max-row stride.
+kvc_status check_contig_extent(const kvc_shape* sh, const char* what) {
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    const int64_t end = (int64_t)seq_start(sh, s) + sh->seq_lens[s];
+    if (end > sh->n_max)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "%s: sequence %d ends at cache row %lld > n_max %d", what, s,
+                  (long long)end, sh->n_max);
   }
   return KVC_OK;
 }
@@ -103,10 +119,14 @@ kvc_status check_paging(const kvc_shape* sh, int32_t block_size, const int32_t* 
   if (!table) return fail(KVC_ERR_INVALID_ARGUMENT, "%s: block_table is NULL", what);
   if (max_blocks < 1) return fail(KVC_ERR_INVALID_ARGUMENT, "%s: max_blocks must be >= 1", what);
   for (int s = 0; s < sh->num_seqs; ++s) {
-    const int nb = (sh->seq_lens[s] + block_size - 1) / block_size;
+    const int a = seq_start(sh, s);
+    if (a % block_size)
+      return fail(KVC_ERR_INVALID_ARGUMENT, "%s: seq_starts[%d] = %d is not a multiple of the block size", what, s,
+                  a);
+    const int64_t nb = ((int64_t)a + sh->seq_lens[s] + block_size - 1) / block_size;
     if (nb > max_blocks)
-      return fail(KVC_ERR_INVALID_ARGUMENT, "%s: sequence %d needs %d blocks > max_blocks %d", what, s, nb,
-                  max_blocks);
+      return fail(KVC_ERR_INVALID_ARGUMENT, "%s: sequence %d needs %lld blocks > max_blocks %d", what, s,
+                  (long long)nb, max_blocks);
   }
   return KVC_OK;
 }
@@ -115,7 +135,7 @@ kvc_status check_view(const kvc_shape* sh, const kvc_kv_view* kv) {
   if (!kv) return fail(KVC_ERR_INVALID_ARGUMENT, "key view is NULL");
   if (!kv->data) return fail(KVC_ERR_INVALID_ARGUMENT, "key data is NULL");
   if (kvc_status st = check_dtype(kv->dtype)) return st;
-  if (kv->block_size == 0) return KVC_OK;
+  if (kv->block_size == 0) return check_contig_extent(sh, "keys");
   return check_paging(sh, kv->block_size, kv->block_table, kv->max_blocks, "keys");
 }
 
@@ -158,18 +178,22 @@ size_t lse_bytes(const kvc_shape* sh) {
 // Run `body(T)` for consecutive slices of at most kChunkSeqs sequences; `items(s)` is the number
 // of work items (workgroups) of sequence s and `offset(s)` a kernel-specific per-sequence value.
 template <class Items, class Offset, class Body>
-hipError_t for_each_chunk(const kvc_shape* sh, const int32_t* m, Items&& items, Offset&& offset, Body&& body) {
+hipError_t for_each_chunk(const kvc_shape* sh, const int32_t* m, Items&& items, Offset&& offset, Body&& body,
+                          const int32_t* cache_lens = nullptr) {
   for (int s0 = 0; s0 < sh->num_seqs; s0 += kChunkSeqs) {
     SeqTable T{};
     T.count = std::min(kChunkSeqs, sh->num_seqs - s0);
     T.first = s0;
     int64_t total = 0;
     for (int i = 0; i < T.count; ++i) {
+      const int s = s0 + i;
       T.start[i] = (int32_t)total;
-      T.n[i] = sh->seq_lens[s0 + i];
-      T.m[i] = m ? m[s0 + i] : 0;
-      T.off[i] = offset(s0 + i);
-      total += items(s0 + i);
+      T.n[i] = sh->seq_lens[s];
+      T.m[i] = m ? m[s] : 0;
+      T.kofs[i] = seq_start(sh, s);
+      T.clen[i] = cache_lens ? cache_lens[s] : T.kofs[i] + T.n[i];
+      T.off[i] = offset(s);
+      total += items(s);
     }
     if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     T.start[T.count] = (int32_t)total;
@@ -332,6 +356,7 @@ kvc_status kvc_compact_contig(const kvc_shape* sh, kvc_dtype dtype, const void* 
   if (kvc_status st = check_shape(sh)) return st;
   if (kvc_status st = check_dtype(dtype)) return st;
   if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (kvc_status st = check_contig_extent(sh, "compact_contig")) return st;
   if (!k || !v || !kept || !k_out || !v_out)
     return fail(KVC_ERR_INVALID_ARGUMENT, "k, v, kept, k_out and v_out must be non-NULL");
   const hipError_t err = for_each_chunk(
@@ -345,11 +370,24 @@ kvc_status kvc_compact_contig(const kvc_shape* sh, kvc_dtype dtype, const void* 
 
 kvc_status kvc_compact_paged(const kvc_shape* sh, kvc_dtype dtype, void* k_pool, void* v_pool, int32_t block_size,
                              int32_t* block_table, int32_t max_blocks, const int32_t* kept, const int32_t* m,
-                             int32_t m_max, int32_t* freed_blocks, int32_t* freed_counts, void* stream) {
+                             int32_t m_max, const int32_t* cache_lens, int32_t* freed_blocks, int32_t* freed_counts,
+                             void* stream) {
   if (kvc_status st = check_shape(sh)) return st;
   if (kvc_status st = check_dtype(dtype)) return st;
   if (kvc_status st = check_budgets(sh, m, m_max)) return st;
   if (kvc_status st = check_paging(sh, block_size, block_table, max_blocks, "pool")) return st;
+  if (cache_lens) {
+    for (int s = 0; s < sh->num_seqs; ++s) {
+      const int a = seq_start(sh, s), n = sh->seq_lens[s], L = cache_lens[s];
+      if (L < a + n || L > kMaxLen || ((int64_t)L + block_size - 1) / block_size > max_blocks)
+        return fail(KVC_ERR_INVALID_ARGUMENT, "cache_lens[%d] = %d inconsistent with segment [%d, %d)", s, L, a,
+                    a + n);
+      if (a + n < L && (n % block_size || m[s] % block_size))
+        return fail(KVC_ERR_INVALID_ARGUMENT,
+                    "sequence %d: a segment followed by more tokens needs n (%d) and m (%d) to be multiples of %d",
+                    s, n, m[s], block_size);
+    }
+  }
   if (!k_pool || !v_pool || !kept || !freed_blocks || !freed_counts)
     return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool, v_pool, kept, freed_blocks and freed_counts must be non-NULL");
   if (k_pool == v_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool and v_pool must be distinct");
@@ -360,9 +398,10 @@ kvc_status kvc_compact_paged(const kvc_shape* sh, kvc_dtype dtype, void* k_pool,
                                  m_max, block_size, T, st);
       });
   if (err != hipSuccess) return hip_fail(err, "paged copy kernel");
-  err = for_each_chunk(sh, m, [](int) { return 1; }, no_offset, [&](const SeqTable& T) {
-    return launch_table_update(block_table, max_blocks, freed_blocks, block_size, T, st);
-  });
+  err = for_each_chunk(
+      sh, m, [](int) { return 1; }, no_offset,
+      [&](const SeqTable& T) { return launch_table_update(block_table, max_blocks, freed_blocks, block_size, T, st); },
+      cache_lens);
   if (err != hipSuccess) return hip_fail(err, "block table kernel");
   for (int s = 0; s < sh->num_seqs; ++s)
     freed_counts[s] = (sh->seq_lens[s] + block_size - 1) / block_size - (m[s] + block_size - 1) / block_size;

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void compact_contig(const u32x4* __restri
   constexpr int kRows = kRowsPerIter * kIters;  // 64 bf16 rows or 32 float32 rows
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
-  const int m = T.m[i], n = T.n[i];
+  const int m = T.m[i], n = T.n[i], kofs = T.kofs[i];
   const int s = T.first + i;
   const int tiles = (m + kRows - 1) / kRows;
   const int local = t - T.start[i];
@@ -63,8 +63,8 @@ __global__ __launch_bounds__(kThreads) void compact_contig(const u32x4* __restri
     if (r < m) {
       const int j = kept[unit * m_max + r];
       if ((unsigned)j < (unsigned)n) {  // kept comes from select; a bad index is skipped, not followed
-        kx[it] = k[(unit * n_max + j) * CH + c];
-        vx[it] = v[(unit * n_max + j) * CH + c];
+        kx[it] = k[(unit * n_max + kofs + j) * CH + c];
+        vx[it] = v[(unit * n_max + kofs + j) * CH + c];
       }
     }
   }
@@ -98,7 +98,8 @@ __global__ __launch_bounds__(kThreads) void paged_copy(u32x4* __restrict__ kp, u
   const int32_t* ku = kept + unit * m_max;
   const int32_t* trow = table + (int64_t)s * max_blocks;
   const int N = (n + B - 1) / B, X = (m + B - 1) / B;
-  const int start = (N - X) * B;
+  const int start = (N - X) * B;  // window start, relative to the segment
+  const int ko = T.kofs[i];       // the segment's first cache position (a multiple of B)
 
   if (threadIdx.x == 0) {
     const int a = lower_bound_i32(ku, m, start);
@@ -121,9 +122,10 @@ __global__ __launch_bounds__(kThreads) void paged_copy(u32x4* __restrict__ kp, u
       }
       const int dst = start + p + lo;
       const bool ok = (unsigned)src < (unsigned)n && dst < N * B;  // holds for any strictly ascending kept
-      const int32_t bs = ok ? trow[src / B] : -1, bd = ok ? trow[dst / B] : -1;
-      src_row[threadIdx.x] = (bs >= 0 && bd >= 0) ? ((int64_t)bs * B + src % B) * H + h : -1;
-      dst_row[threadIdx.x] = (bs >= 0 && bd >= 0) ? ((int64_t)bd * B + dst % B) * H + h : -1;
+      const int ps = ko + src, pd = ko + dst;                       // cache positions
+      const int32_t bs = ok ? trow[ps / B] : -1, bd = ok ? trow[pd / B] : -1;
+      src_row[threadIdx.x] = (bs >= 0 && bd >= 0) ? ((int64_t)bs * B + ps % B) * H + h : -1;
+      dst_row[threadIdx.x] = (bs >= 0 && bd >= 0) ? ((int64_t)bd * B + pd % B) * H + h : -1;
     } else {
       src_row[threadIdx.x] = -1;
       dst_row[threadIdx.x] = -1;
@@ -142,27 +144,31 @@ __global__ __launch_bounds__(kThreads) void paged_copy(u32x4* __restrict__ kp, u
   }
 }
 
-// One workgroup per sequence: freed = old[0, N-X); table[0, X) = old[N-X, N); table[X, N) = -1.
+// One workgroup per sequence, with b = segment start block, F = N - X freed blocks and NT blocks
+// in use: freed = old[b, b+F); table[b, NT-F) = old[b+F, NT); table[NT-F, NT) = -1.
 __global__ __launch_bounds__(1024) void table_update(int32_t* __restrict__ table, int max_blocks,
                                                      int32_t* __restrict__ freed, int B, SeqTable T) {
   const int i = blockIdx.x;
   const int s = T.first + i;
   const int n = T.n[i], m = T.m[i];
   const int N = (n + B - 1) / B, X = (m + B - 1) / B, F = N - X;
+  const int b = T.kofs[i] / B;
+  const int NT = (T.clen[i] + B - 1) / B;
   int32_t* tr = table + (int64_t)s * max_blocks;
   int32_t* fr = freed + (int64_t)s * max_blocks;
-  for (int j = threadIdx.x; j < F; j += blockDim.x) fr[j] = tr[j];
+  for (int j = threadIdx.x; j < F; j += blockDim.x) fr[j] = tr[b + j];
   __syncthreads();
-  // shift left by F one block-wide slice at a time: a slice reads [c0 + F, c0 + F + 1024), which
-  // no earlier slice has written (they wrote [0, c0))
-  for (int c0 = 0; c0 < X; c0 += blockDim.x) {
+  // shift [b+F, NT) left by F one block-wide slice at a time: a slice reads
+  // [b + c0 + F, b + c0 + F + 1024), which no earlier slice has written (they wrote [b, b + c0))
+  const int len = NT - b - F;
+  for (int c0 = 0; c0 < len; c0 += blockDim.x) {
     const int j = c0 + threadIdx.x;
-    const int32_t val = j < X ? tr[j + F] : 0;
+    const int32_t val = j < len ? tr[b + j + F] : 0;
     __syncthreads();
-    if (j < X) tr[j] = val;
+    if (j < len) tr[b + j] = val;
     __syncthreads();
   }
-  for (int j = X + threadIdx.x; j < N; j += blockDim.x) tr[j] = -1;
+  for (int j = NT - F + threadIdx.x; j < NT; j += blockDim.x) tr[j] = -1;
 }
 
 int contig_tiles(int m, bool f32) {

@@ -28,12 +28,15 @@ struct SeqTable {
   int32_t count;                  // sequences in this launch
   int32_t first;                  // global index of sequence 0 of this launch
   int32_t total;                  // work items in this launch (grid size)
-  int32_t per_head;               // unused by some kernels
+  int32_t pad;
   int32_t start[kChunkSeqs + 1];
-  int32_t n[kChunkSeqs];
-  int32_t m[kChunkSeqs];
+  int32_t n[kChunkSeqs];          // keys scored (segment length)
+  int32_t m[kChunkSeqs];          // kept positions
+  int32_t kofs[kChunkSeqs];       // cache position of the segment's first key
+  int32_t clen[kChunkSeqs];       // total cache length (paged compaction)
   int64_t off[kChunkSeqs];        // kernel-specific per-sequence offset (workspace slots)
 };
+static_assert(sizeof(SeqTable) <= 3800, "SeqTable must fit the kernel-argument segment");
 
 // Map a dispatch-ordered block index to a logical work index so that logically consecutive
 // work items run on the same XCD (blocks are dispatched round-robin over the 8 XCDs, each with

@@ -44,15 +44,15 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Pointer to the 256-byte stored row of key `key` of unit (s, h).
+// Pointer to the 256-byte stored row at cache position `pos` of unit (s, h).
 template <bool PAGED>
 __device__ __forceinline__ const u32x4* key_row(const uint16_t* __restrict__ k, const int32_t* __restrict__ trow,
-                                                int H, int h, int64_t n_max, int64_t unit, int key) {
+                                                int H, int h, int64_t n_max, int64_t unit, int pos) {
   if constexpr (PAGED) {
-    const int64_t blk = trow[key >> 4];
-    return reinterpret_cast<const u32x4*>(k + ((blk * 16 + (key & 15)) * H + h) * kHeadDim);
+    const int64_t blk = trow[pos >> 4];
+    return reinterpret_cast<const u32x4*>(k + ((blk * 16 + (pos & 15)) * H + h) * kHeadDim);
   } else {
-    return reinterpret_cast<const u32x4*>(k + (unit * n_max + key) * kHeadDim);
+    return reinterpret_cast<const u32x4*>(k + (unit * n_max + pos) * kHeadDim);
   }
 }
 
@@ -76,6 +76,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   const int i = find_seq(T, t);
   const int n = T.n[i];
   const int s = T.first + i;
+  const int ko = T.kofs[i];
   const int tiles = (n + kScoreKeys - 1) / kScoreKeys;
   const int local = t - T.start[i];
   const int h = local / tiles;
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   for (int sub = 0; sub < kScoreSub; ++sub) {
     const int key = key0 + sub * 16 + c16;
     if (key < n) {
-      const u32x4* p = key_row<PAGED>(k, trow, H, h, n_max, unit, key);
+      const u32x4* p = key_row<PAGED>(k, trow, H, h, n_max, unit, ko + key);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kb[sub][ks] = as_bf16x8(p[4 * ks + g]);
       if constexpr (BIAS) bb[sub] = 2.0f * kLog2e * bias[(int64_t)s * n_max + key];
@@ -201,6 +202,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   const int i = find_seq(T, t);
   const int n = T.n[i];
   const int s = T.first + i;
+  const int ko = T.kofs[i];
   const int nkc = (n + kchunk - 1) / kchunk;
   const int nrb = (R + kPerBlock - 1) / kPerBlock;
   int local = t - T.start[i];
@@ -243,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     for (int j = 0; j < 4; ++j) {
       const int id = tid + kThreads * j, row = id >> 4, c = id & 15;
       const int key = k0 + row;
-      pre[j] = key < kend ? key_row<PAGED>(k, trow, H, h, n_max, unit, key)[c] : u32x4{0u, 0u, 0u, 0u};
+      pre[j] = key < kend ? key_row<PAGED>(k, trow, H, h, n_max, unit, ko + key)[c] : u32x4{0u, 0u, 0u, 0u};
     }
     if (tid < kStage) {
       const int key = k0 + tid;

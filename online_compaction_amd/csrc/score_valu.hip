@@ -19,12 +19,12 @@ constexpr int kRowsStage = 32;  // proxy rows per LDS stage (32 x 512 B = 16 KB)
 
 template <bool F32, bool PAGED>
 __device__ __forceinline__ void load_key_f32(const void* __restrict__ kbase, const int32_t* __restrict__ trow, int H,
-                                             int h, int64_t n_max, int64_t unit, int key, float (&kr)[kHeadDim]) {
+                                             int h, int64_t n_max, int64_t unit, int pos, float (&kr)[kHeadDim]) {
   if constexpr (F32) {
     const float* k = static_cast<const float*>(kbase);
     const float* p;
-    if constexpr (PAGED) p = k + (((int64_t)trow[key >> 4] * 16 + (key & 15)) * H + h) * kHeadDim;
-    else p = k + (unit * n_max + key) * kHeadDim;
+    if constexpr (PAGED) p = k + (((int64_t)trow[pos >> 4] * 16 + (pos & 15)) * H + h) * kHeadDim;
+    else p = k + (unit * n_max + pos) * kHeadDim;
     const float4* p4 = reinterpret_cast<const float4*>(p);
 #pragma unroll
     for (int c = 0; c < kHeadDim / 4; ++c) {
@@ -34,8 +34,8 @@ __device__ __forceinline__ void load_key_f32(const void* __restrict__ kbase, con
   } else {
     const uint16_t* k = static_cast<const uint16_t*>(kbase);
     const uint16_t* p;
-    if constexpr (PAGED) p = k + (((int64_t)trow[key >> 4] * 16 + (key & 15)) * H + h) * kHeadDim;
-    else p = k + (unit * n_max + key) * kHeadDim;
+    if constexpr (PAGED) p = k + (((int64_t)trow[pos >> 4] * 16 + (pos & 15)) * H + h) * kHeadDim;
+    else p = k + (unit * n_max + pos) * kHeadDim;
     const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int c = 0; c < kHeadDim / 8; ++c) {
@@ -105,7 +105,9 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
   const bool valid = key < n;
 
   float kr[kHeadDim];
-  if (valid) load_key_f32<F32, PAGED>(k, PAGED ? table + (int64_t)s * max_blocks : nullptr, H, h, n_max, unit, key, kr);
+  if (valid)
+    load_key_f32<F32, PAGED>(k, PAGED ? table + (int64_t)s * max_blocks : nullptr, H, h, n_max, unit, T.kofs[i] + key,
+                             kr);
   else
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) kr[e] = 0.f;
@@ -156,7 +158,9 @@ __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __rest
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   float kr[kHeadDim];
-  if (valid) load_key_f32<F32, PAGED>(k, PAGED ? table + (int64_t)s * max_blocks : nullptr, H, h, n_max, unit, key, kr);
+  if (valid)
+    load_key_f32<F32, PAGED>(k, PAGED ? table + (int64_t)s * max_blocks : nullptr, H, h, n_max, unit, T.kofs[i] + key,
+                             kr);
   else
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) kr[e] = 0.f;

@@ -46,6 +46,7 @@ class Batch:
     max_blocks: int = 0
     bias: torch.Tensor = None
     lse: torch.Tensor = None          # supplied LSE [S][H*G][q] or None
+    cache_lens: np.ndarray = None     # paged: total length of each sequence (segment compaction)
 
     @property
     def paged(self) -> bool:
@@ -61,10 +62,12 @@ def _dtype_of(arr: np.ndarray) -> int:
     return A.KVC_BF16 if arr.dtype == np.uint16 else A.KVC_F32
 
 
-def contiguous_batch(Q, K, V, n, m, group: int, scale: float, bias=None, lse=None, device="cuda") -> Batch:
+def contiguous_batch(Q, K, V, n, m, group: int, scale: float, bias=None, lse=None, starts=None,
+                     device="cuda") -> Batch:
+    """Score/select/gather n[s] keys of each sequence, starting at cache row starts[s] (default 0)."""
     S, H, n_max, d = K.shape
     q = Q.shape[2]
-    shape = A.Shape(S, H, group, q, d, n_max, np.asarray(n, dtype=np.int32), scale)
+    shape = A.Shape(S, H, group, q, d, n_max, np.asarray(n, dtype=np.int32), scale, starts)
     m = np.asarray(m, dtype=np.int32)
     return Batch(shape, _dtype_of(K), device_tensor(Q, device), m, max(1, int(m.max())),
                  k=device_tensor(K, device), v=device_tensor(V, device),
@@ -73,20 +76,23 @@ def contiguous_batch(Q, K, V, n, m, group: int, scale: float, bias=None, lse=Non
 
 
 def paged_batch(Q, k_pool, v_pool, table, n, m, group: int, scale: float, block_size: int, n_max=None, bias=None,
-                lse=None, device="cuda") -> Batch:
+                lse=None, starts=None, cache_lens=None, device="cuda") -> Batch:
+    """Paged pool; n[s] keys scored from logical position starts[s] (default 0) of a sequence whose
+    total length is cache_lens[s] (default starts[s] + n[s])."""
     S, max_blocks = table.shape
     H, d = k_pool.shape[2], k_pool.shape[3]
     q = Q.shape[2]
     n = np.asarray(n, dtype=np.int32)
     n_max = int(n_max if n_max is not None else (bias.shape[1] if bias is not None else n.max()))
-    shape = A.Shape(S, H, group, q, d, n_max, n, scale)
+    shape = A.Shape(S, H, group, q, d, n_max, n, scale, starts)
     m = np.asarray(m, dtype=np.int32)
     return Batch(shape, _dtype_of(k_pool), device_tensor(Q, device), m, max(1, int(m.max())),
                  k_pool=device_tensor(k_pool, device), v_pool=device_tensor(v_pool, device),
                  table=device_tensor(np.asarray(table, dtype=np.int32), device), block_size=block_size,
                  max_blocks=max_blocks,
                  bias=None if bias is None else device_tensor(np.asarray(bias, dtype=np.float32), device),
-                 lse=None if lse is None else device_tensor(np.asarray(lse, dtype=np.float32), device))
+                 lse=None if lse is None else device_tensor(np.asarray(lse, dtype=np.float32), device),
+                 cache_lens=None if cache_lens is None else np.asarray(cache_lens, dtype=np.int32))
 
 
 @dataclass
@@ -128,7 +134,7 @@ def run_select(b: Batch, o: Outputs, stream=None) -> None:
 def run_compact(b: Batch, o: Outputs, stream=None) -> None:
     if b.paged:
         o.freed_counts = A.kvc_compact_paged(b.shape, b.dtype, b.k_pool, b.v_pool, b.block_size, b.table,
-                                             b.max_blocks, o.kept, b.m, b.m_max, o.freed, stream)
+                                             b.max_blocks, o.kept, b.m, b.m_max, o.freed, b.cache_lens, stream)
     else:
         A.kvc_compact_contig(b.shape, b.dtype, b.k, b.v, o.kept, b.m, b.m_max, o.k_out, o.v_out, stream)
 

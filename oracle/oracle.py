@@ -153,14 +153,16 @@ def paged_plan(n: int, m: int, B: int, kept) -> PagedPlan:
 
 
 def apply_paged_copy(k_pool: np.ndarray, v_pool: np.ndarray, table_row: np.ndarray, h: int,
-                     plan: PagedPlan) -> None:
+                     plan: PagedPlan, offset: int = 0) -> None:
     """Copy K and V rows of head h from each source slot to its paired hole, in place.
 
-    Pools are [num_blocks][B][H][d]; table_row maps logical block -> physical block. Sources
-    are never holes and holes are never read, so the order of the copies does not matter.
+    Pools are [num_blocks][B][H][d]; table_row maps logical block -> physical block; plan
+    positions are relative to a segment that starts at cache position `offset`. Sources are never
+    holes and holes are never read, so the order of the copies does not matter.
     """
     B = plan.B
     for a, b in zip(plan.src, plan.dst):
+        a, b = a + offset, b + offset
         pa, sa = int(table_row[a // B]), a % B
         pb, sb = int(table_row[b // B]), b % B
         k_pool[pb, sb, h, :] = k_pool[pa, sa, h, :]
@@ -177,6 +179,27 @@ def table_update(table_row: np.ndarray, n: int, m: int, B: int) -> tuple[np.ndar
     new[X:N] = -1
     freed = old[:N - X].copy()
     return new, freed
+
+
+def table_update_segment(table_row: np.ndarray, start: int, n: int, cache_len: int, m: int,
+                         B: int) -> tuple[np.ndarray, np.ndarray]:
+    """Block table after compacting the segment [start, start + n) of a sequence of cache_len
+    tokens: the segment's first N - X logical blocks are freed and every later block slides down
+    by that many entries (the kept window, then the rest of the sequence); the vacated tail
+    becomes -1. With start = 0 and cache_len = n this is `table_update`.
+    """
+    if start % B:
+        raise ValueError("a paged segment starts on a block boundary")
+    N = -(-n // B)
+    X = -(-m // B)
+    F = N - X
+    b = start // B
+    NT = -(-cache_len // B)
+    old = list(int(x) for x in table_row)
+    freed = old[b:b + F]
+    kept_blocks = old[:b] + old[b + F:NT]
+    new = np.array(kept_blocks + [-1] * F + old[NT:], dtype=np.int32)
+    return new, np.array(freed, dtype=np.int32)
 
 
 # ----------------------------------------------------------------------------- whole batches

@@ -111,11 +111,50 @@ def test_select_and_compact_validation(lib):
                                   None) == A.KVC_ERR_INVALID_ARGUMENT
     counts = (ctypes.c_int32 * 2)(-7, -7)
     # same pool for K and V, and an unsupported page size: rejected, counts untouched
-    assert lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE, 16, FAKE, 4096, FAKE, m_ok, 6600, FAKE,
-                                 counts, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE, 16, FAKE, 4096, FAKE, m_ok, 6600, None,
+                                 FAKE, counts, None) == A.KVC_ERR_INVALID_ARGUMENT
     assert lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE + 64, 8, FAKE, 4096, FAKE, m_ok, 6600,
-                                 FAKE, counts, None) == A.KVC_ERR_UNSUPPORTED
+                                 None, FAKE, counts, None) == A.KVC_ERR_UNSUPPORTED
     assert list(counts) == [-7, -7]
+
+
+def test_segment_validation(lib):
+    """Segments: paged starts must be block-aligned; a segment followed by more tokens needs
+    block-multiple lengths and budgets; contiguous segments must fit the row stride."""
+    counts = (ctypes.c_int32 * 1)(-7)
+    # paged segment start not a multiple of 16
+    sh, keep = _shape(S=1, n=(160,), n_max=160).c()
+    sh.seq_starts = (ctypes.c_int32 * 1)(8)
+    m = (ctypes.c_int32 * 1)(32)
+    st = lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE + 64, 16, FAKE, 100, FAKE, m, 32, None, FAKE,
+                               counts, None)
+    assert st == A.KVC_ERR_INVALID_ARGUMENT and b"multiple of the block size" in lib.kvc_last_error()
+    # followed by more tokens: m must be a multiple of 16
+    sh.seq_starts = (ctypes.c_int32 * 1)(32)
+    clen = (ctypes.c_int32 * 1)(400)
+    m_bad = (ctypes.c_int32 * 1)(33)
+    st = lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE + 64, 16, FAKE, 100, FAKE, m_bad, 33, clen,
+                               FAKE, counts, None)
+    assert st == A.KVC_ERR_INVALID_ARGUMENT and b"multiples of 16" in lib.kvc_last_error()
+    # cache length shorter than the segment's end
+    clen_bad = (ctypes.c_int32 * 1)(100)
+    st = lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE + 64, 16, FAKE, 100, FAKE, m, 32, clen_bad,
+                               FAKE, counts, None)
+    assert st == A.KVC_ERR_INVALID_ARGUMENT
+    assert counts[0] == -7
+    # contiguous segment running past n_max
+    sh2, keep2 = _shape(S=1, n=(100,), n_max=120).c()
+    sh2.seq_starts = (ctypes.c_int32 * 1)(30)
+    kv = A.KView(FAKE, A.KVC_BF16).c()
+    st = lib.kvc_score(ctypes.byref(sh2), FAKE, ctypes.byref(kv), FAKE, None, FAKE, None, 0, None)
+    assert st == A.KVC_ERR_INVALID_ARGUMENT and b"n_max" in lib.kvc_last_error()
+    m1 = (ctypes.c_int32 * 1)(20)
+    st = lib.kvc_compact_contig(ctypes.byref(sh2), A.KVC_BF16, FAKE, FAKE, FAKE, m1, 20, FAKE, FAKE, None)
+    assert st == A.KVC_ERR_INVALID_ARGUMENT
+    # a negative start
+    sh2.seq_starts = (ctypes.c_int32 * 1)(-1)
+    st = lib.kvc_score(ctypes.byref(sh2), FAKE, ctypes.byref(kv), FAKE, None, FAKE, None, 0, None)
+    assert st == A.KVC_ERR_INVALID_ARGUMENT
 
 
 def test_binding_refuses_host_tensors():

@@ -307,3 +307,53 @@ def test_paged_rejects_bad_kept():
         O.paged_plan(10, 3, 4, [1, 1, 2])
     with pytest.raises(ValueError):
         O.paged_plan(10, 3, 4, [1, 2, 10])
+
+
+# ------------------------------------------------------------------- segments (delayed turns)
+
+@pytest.mark.parametrize("ex", _load("segment_examples.json")["examples"], ids=lambda e: e["name"])
+def test_segment_worked_examples(ex):
+    B, a, n, L, m = ex["B"], ex["start"], ex["n"], ex["cache_len"], ex["m"]
+    plan = O.paged_plan(n, m, B, ex["kept"])
+    assert [a + plan.start, a + plan.start + m] == ex["window"]
+    assert [a + x for x in plan.src] == ex["src_abs"] and [a + x for x in plan.dst] == ex["dst_abs"]
+    new, freed = O.table_update_segment(np.array(ex["table"], dtype=np.int32), a, n, L, m, B)
+    assert new.tolist() == ex["new_table"] and freed.tolist() == ex["freed"]
+    new_len = a + m if a + n == L else L - plan.freed_count * B
+    assert new_len == ex["new_len"]
+
+
+def test_segment_update_reduces_to_whole_sequence():
+    t = np.array([3, 1, 4, 0, 2, -1], dtype=np.int32)
+    for n, m in ((17, 5), (16, 16), (20, 0), (9, 9)):
+        a1, f1 = O.table_update(t, n, m, 4)
+        a2, f2 = O.table_update_segment(t, 0, n, n, m, 4)
+        assert a1.tolist() == a2.tolist() and f1.tolist() == f2.tolist()
+
+
+@settings(max_examples=150, deadline=None)
+@given(st.sampled_from([1, 2, 4, 8]), st.integers(0, 5), st.integers(1, 6), st.integers(0, 20), st.data())
+def test_segment_compaction_keeps_prefix_kept_suffix(B, pre_blocks, seg_blocks, suffix, data):
+    """Compacting a block-aligned middle segment: the prefix is untouched, the segment's first m
+    slots hold exactly the kept tokens, and the suffix follows in order right after them."""
+    a = pre_blocks * B
+    n = seg_blocks * B if suffix else data.draw(st.integers(1, seg_blocks * B))
+    L = a + n + suffix
+    m = B * data.draw(st.integers(0, n // B)) if suffix else data.draw(st.integers(0, n))
+    kept = sorted(data.draw(st.lists(st.integers(0, n - 1), min_size=m, max_size=m, unique=True)))
+    NT = -(-L // B)
+    rng = np.random.default_rng(B * 1000 + a + n)
+    table = rng.permutation(NT + 2)[:NT].astype(np.int32)
+    pool = np.full((NT + 2, B, 1, 1), -9, dtype=np.int64)
+    for p in range(L):
+        pool[table[p // B], p % B, 0, 0] = p
+    vpool = pool.copy()
+    plan = O.paged_plan(n, m, B, kept)
+    O.apply_paged_copy(pool, vpool, table, 0, plan, offset=a)
+    new, freed = O.table_update_segment(table, a, n, L, m, B)
+    new_len = a + m if not suffix else L - plan.freed_count * B
+    read = [int(pool[new[p // B], p % B, 0, 0]) for p in range(new_len)]
+    assert read[:a] == list(range(a))
+    assert sorted(read[a:a + m]) == [a + j for j in kept]
+    assert read[a + m:] == list(range(a + n, L))
+    assert len(freed) == plan.freed_count and set(freed.tolist()).isdisjoint(new[: -(-new_len // B)].tolist())
