@@ -39,23 +39,32 @@ def describe(w) -> str:
     lay = "paged B=%d" % w.block_size if w.paged else "contiguous"
     lse = "supplied LSE" if w.lse_supplied else "computed LSE"
     n = f"n={w.n[0]}" if len(set(w.n)) == 1 else f"n={min(w.n)}..{max(w.n)}"
+    if w.seg_len:
+        n += f", segment [{w.seg_start}, {w.seg_start + w.seg_len})"
     return (f"{w.name}: {w.S} seqs x {w.H} KV heads, G={w.G}, q={w.q}, R={w.R}, {n}, d={w.d}, {w.dtype}, "
             f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}")
 
 
 def trajectory_tokens(w) -> int:
     """Token positions compacted per step: the 36 sequences of the default workload are layers of
-    one trajectory, so it counts 33 000; elsewhere sequences are distinct."""
+    one trajectory, so it counts 33 000 (the segment workload counts its turn once); elsewhere
+    sequences are distinct."""
+    if w.seg_len:
+        return w.seg_len
     if w.name == "c3":
         return w.n[0]
     return int(sum(w.n))
+
+
+def scored_lens(w):
+    return [w.seg_len] * w.S if w.seg_len else list(w.n)
 
 
 def algorithmic_bytes(w, moved_rows=None) -> dict:
     """Bytes the method must move per step (reads + writes), per stage."""
     el = 2 if w.dtype == "bf16" else 4
     row = w.d * el
-    entries = sum(w.n) * w.H
+    entries = sum(scored_lens(w)) * w.H
     kept = sum(w.m) * w.H
     rows_q = w.S * w.H * w.R
     score = entries * row + rows_q * row + entries * 4 + (rows_q * 4 if w.lse_supplied else 0)
@@ -72,7 +81,7 @@ def algorithmic_bytes(w, moved_rows=None) -> dict:
 
 def score_flops(w) -> float:
     passes = 1 if w.lse_supplied else 2
-    return float(passes) * 2.0 * w.R * w.d * sum(w.n) * w.H
+    return float(passes) * 2.0 * w.R * w.d * sum(scored_lens(w)) * w.H
 
 
 # ---------------------------------------------------------------------------------- CPU baseline
@@ -83,6 +92,8 @@ def _oracle_unit(args):
     from workloads import unit_keys, unit_queries, unit_values
     K = unit_keys(w, s, h)
     V = unit_values(w, s, h)
+    if w.seg_len:  # only the turn is scored and compacted
+        K, V = K[w.seg_start:w.seg_start + w.seg_len], V[w.seg_start:w.seg_start + w.seg_len]
     Qr = unit_queries(w, s, h)
     lse_rows = None
     if w.lse_supplied:  # the supplied input, prepared outside the timed region
@@ -197,7 +208,12 @@ def main():
     from online_compaction_amd import path as P
     A.load()  # fails loudly when libkvc.so is missing
 
-    if w.paged:
+    if w.paged and w.seg_len:
+        b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], [w.seg_len] * w.S, data["m"],
+                          w.G, w.logit_scale, w.block_size, n_max=w.seg_len, starts=[w.seg_start] * w.S,
+                          cache_lens=data["n"])
+        pristine = (b.k_pool.clone(), b.v_pool.clone(), b.table.clone())
+    elif w.paged:
         b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], data["n"], data["m"], w.G,
                           w.logit_scale, w.block_size, n_max=w.n_max, bias=data["bias"])
         pristine = (b.k_pool.clone(), b.v_pool.clone(), b.table.clone())
@@ -280,7 +296,7 @@ def main():
         kept = P.host_array(o.kept)
         moved = 0
         for s in range(w.S):
-            n, m = w.n[s], w.m[s]
+            n, m = (w.seg_len or w.n[s]), w.m[s]
             start = (-(-n // w.block_size) - -(-m // w.block_size)) * w.block_size
             for h in range(w.H):
                 k = kept[s, h, :m]
@@ -308,8 +324,8 @@ def main():
         "config": {
             "workload": describe(w),
             "tokens_per_step": tokens,
-            "kv_entries_per_step": int(sum(w.n) * w.H),
-            "entries_per_s": sum(w.n) * w.H / step_s,
+            "kv_entries_per_step": int(sum(scored_lens(w)) * w.H),
+            "entries_per_s": sum(scored_lens(w)) * w.H / step_s,
             "stage_ms": {"score": avg[0], "select": avg[1], "compact": avg[2]},
             "hbm_algorithmic_bytes_per_step": ab["total"],
             "hbm_algorithmic_gbps": ab["total"] / step_s / 1e9,

@@ -91,6 +91,8 @@ class Workload:
     lse_supplied: bool = False
     bias_tail: float = 0.0
     scale: float = 0.0     # 0 -> 1/sqrt(d)
+    seg_start: int = 0     # > 0 or seg_len > 0: compact only this segment (one agent turn)
+    seg_len: int = 0
 
     @property
     def R(self) -> int:
@@ -136,6 +138,15 @@ def spec(name: str, k: int | None = None) -> Workload:
         n = 33000
         return Workload(f"c4k{kk}", 4, 1, 8, 4, 330, 128, (n,), (c4_budget(kk),), "bf16", "mixture", "action",
                         paged=True, block_size=16, table="identity", max_blocks=-(-n // 16), bias_tail=0.5)
+    if name == "turn":
+        # one 4096-token turn in the middle of a 33000-token trajectory held in 36 layers' paged
+        # caches, scored with the 512 queries per query head of the turn that followed it; the
+        # keep budget is round(0.2 * 4096) rounded up to whole 16-token blocks
+        n, a, L = 33000, 16000, 4096
+        m = -(-ratio_budget(L) // 16) * 16
+        return Workload("turn", 6, 36, 8, 4, 512, 128, (n,) * 36, (m,) * 36, "bf16", "mixture", "cluster",
+                        paged=True, block_size=16, table="permuted", max_blocks=-(-n // 16), seg_start=a,
+                        seg_len=L)
     if name == "c5":
         n = _c5_lengths()
         return Workload("c5", 5, 64, 4, 8, 256, 128, n, tuple(ratio_budget(x) for x in n), "bf16", "mixture",
