@@ -28,7 +28,16 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
-SCORE_SRC = os.path.join(ROOT, "online_compaction_amd", "csrc", "score_mfma.hip")
+# the score kernel's source: its own file and the headers it includes
+SCORE_SRCS = [os.path.join(ROOT, "online_compaction_amd", "csrc", f)
+              for f in ("score_mfma.hip", "mfma_common.h", "kvc_internal.h")]
+
+
+def score_source_sha256() -> str:
+    h = hashlib.sha256()
+    for f in SCORE_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def log(*a):
@@ -164,7 +173,7 @@ def traffic_from_profile(launch_s: float):
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    src = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+    src = score_source_sha256()
     if kv.get("source_sha256") != src:
         return None
     try:

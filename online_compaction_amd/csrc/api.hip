@@ -147,12 +147,12 @@ bool use_mfma(const kvc_shape* sh, const kvc_kv_view* kv) {
 int mfma_kchunk(const kvc_shape* sh) {
   const int R = sh->group * sh->num_queries;
   const int64_t rb = lse_mfma_row_blocks(R);
-  for (int kc : {4096, 2048, 1024}) {
+  for (int kc : {kLseMaxChunk, kLseMaxChunk / 2, kLseMaxChunk / 4}) {
     int64_t wg = 0;
     for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
     if (wg >= 2048) return kc;
   }
-  return 512;
+  return kLseMaxChunk / 8;
 }
 
 int lse_kchunk(const kvc_shape* sh, const kvc_kv_view* kv) {

@@ -10,6 +10,8 @@ namespace kvc {
 
 constexpr int kHeadDim = 128;
 constexpr int kChunkSeqs = 128;     // sequences described per launch (kernel-argument table)
+// longest key chunk one LSE-pass workgroup may cover (the host picks 4096, 2048, 1024 or 512)
+constexpr int kLseMaxChunk = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Squared weights are accumulated as exp2(2*log2(alpha) + kSqOffset) so that alpha down to

@@ -1,0 +1,309 @@
+// Per-proxy-row log-sum-exp on MFMA (bf16 operands, float32 accumulate) for gfx950.
+//
+// LSE_r = ln sum_j exp(l_rj) over the same keys the score pass weighs (ActKV page, paged-memory
+// paragraph: the weights are recovered from the LSE; an engine gets it from its attention
+// kernel, here it is also computed). Mirror image of score_mfma: lse_partials_mfma reduces over
+// KEYS for every proxy row; the WG keeps 512 proxy rows in registers (MFMA B operand) and
+// streams 64-key stages of K through LDS (A operand) by LDS-DMA, two stages in flight; online
+// sum in the log2 domain against a lazily moved reference exponent; one (reference, sum)
+// partial per row and key chunk goes to the workspace, and lse_combine merges the chunks.
+#include "mfma_common.h"
+
+namespace kvc {
+
+using namespace mfma;
+
+namespace {
+
+constexpr int kSub = 8;                 // 16-wide subtiles per wave held in registers
+constexpr int kPerWave = 16 * kSub;     // 128 rows per wave
+constexpr int kPerBlock = 4 * kPerWave; // 512 per workgroup
+constexpr int kLseBufs = 3;             // LDS stage buffers (two loads in flight)
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// Per proxy row, partial (reference, sum) of 2^(log2e * l_rj) over one key chunk, with the
+// reference exponent moved only when a tile's sum would leave the float range (see below).
+// Work item = (sequence, KV head, key chunk kc, 512-row block rb), rb fastest so the blocks
+// sharing a key chunk run together on one XCD.
+// partials: float2 [T.off[i] + (h * nkc + kc) * R + row]
+// ------------------------------------------------------------------------------------------------
+template <bool PAGED, bool BIAS>
+__global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
+    int max_blocks, const float* __restrict__ bias, float2* __restrict__ partials, int H, int R,
+    int64_t n_max, float scale, int kchunk, SeqTable T) {
+  __shared__ __attribute__((aligned(16))) uint8_t ks_[kLseBufs][kStage * 256];
+  __shared__ __attribute__((aligned(16))) float kts[BIAS ? kLseBufs : 1][kStage];
+  __shared__ int32_t blks[PAGED ? kLseMaxChunk / 16 + 1 : 1];
+
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = find_seq(T, t);
+  const int n = T.n[i];
+  const int s = T.first + i;
+  const int ko = T.kofs[i];
+  const int nkc = (n + kchunk - 1) / kchunk;
+  const int nrb = (R + kPerBlock - 1) / kPerBlock;
+  int local = t - T.start[i];
+  const int h = local / (nkc * nrb);
+  local -= h * nkc * nrb;
+  const int kc = local / nrb;
+  const int rb = local - kc * nrb;
+  const int64_t unit = (int64_t)s * H + h;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+
+  const int kbeg = kc * kchunk;
+  const int kend = min(n, kbeg + kchunk);
+  const int nst = (kend - kbeg + kStage - 1) / kStage;
+  const float c2 = kLog2e * scale;
+
+  // paged: the chunk's block-table entries (at most kchunk / 16 + 1 <= kLseMaxChunk / 16 + 1,
+  // the host never picks a longer chunk) are read once, so the streamed loads depend on LDS only
+  const int blk0 = (ko + kbeg) >> 4;
+  if constexpr (PAGED) {
+    const int32_t* trow = table + (int64_t)s * max_blocks;
+    const int nb = ((ko + kend - 1) >> 4) - blk0 + 1;
+    for (int b = tid; b < nb; b += kThreads) blks[b] = trow[blk0 + b];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this loop stays pending below
+    __syncthreads();
+  }
+  auto key_ptr = [&](int key) -> const u32x4* {
+    const int pos = ko + key;
+    if constexpr (PAGED) {
+      const int64_t blk = blks[(pos >> 4) - blk0];
+      return reinterpret_cast<const u32x4*>(k + ((blk * 16 + (pos & 15)) * H + h) * kHeadDim);
+    } else {
+      return reinterpret_cast<const u32x4*>(k + (unit * n_max + pos) * kHeadDim);
+    }
+  };
+
+  // proxy rows of this wave, held for the whole key sweep
+  const uint16_t* qu = q + unit * (int64_t)R * kHeadDim;
+  const int row0 = rb * kPerBlock + wave * kPerWave;
+  bf16x8 qb[kSub][4];
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    const int r = row0 + sub * 16 + c16;
+    if (r < R) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(qu + (int64_t)r * kHeadDim);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qb[sub][kk] = as_bf16x8(p[4 * kk + g]);
+    } else {
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) qb[sub][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+
+  // A stage (64 keys) goes global -> LDS without passing through registers: each wave issues 4
+  // 16-byte-per-lane LDS-DMA loads (4 key rows each, the lane's chunk chosen so the rows land
+  // XOR-swizzled) plus, with a bias, one 4-byte load of its 16 keys' bias. Keys past the chunk
+  // load the chunk's last row (finite bytes, masked in the epilogue).
+  auto issue = [&](int st) {
+    const int k0 = kbeg + st * kStage;
+    const int b = st % kLseBufs;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = (wave * 4 + j) * 4 + (lane >> 4);
+      const int key = min(k0 + row, kend - 1);
+      dma16(key_ptr(key) + ((lane & 15) ^ (row & 15)), &ks_[b][(wave * 4 + j) * 1024]);
+    }
+    if constexpr (BIAS) {
+      if (lane < 16) dma4(bias + (int64_t)s * n_max + min(k0 + wave * 16 + lane, kend - 1), &kts[b][wave * 16]);
+    }
+  };
+
+  // Per row: a reference exponent mref (a logit in log2 units seen earlier in the chunk, or -1e30
+  // before the first) and the running sum of 2^(x - mref). A stage first runs the cheap form (one
+  // FMA, one exp2 and one add per logit against the current mref) into stage sums; if any lane's
+  // stage sum leaves [0, 2^64] (a logit rose more than about 60 above its mref, which includes the
+  // first stage) the whole wave discards them and redoes the stage exactly, moving mref to every
+  // new maximum. Terms never exceed 2^64 and the largest one seen is at least 1, so the dominant
+  // terms neither overflow nor underflow.
+  float mref[kSub], ssum[kSub];
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    mref[sub] = -1.0e30f;
+    ssum[sub] = 0.0f;
+  }
+  constexpr float kLazyLimit = 18446744073709551616.0f;  // 2^64
+
+  auto tile_acc = [&](int buf, int kt, f32x4 (&acc)[kSub]) {
+    const int row = kt * 16 + c16;
+    bf16x8 a[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(&ks_[buf][swz(row, 4 * kk + g)]);
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) acc[sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) acc[sub] = mfma16(a[kk], qb[sub][kk], acc[sub]);
+  };
+  // per-key term of the lane's 4 keys in tile kt (log2 units): the bias, -inf past the chunk
+  auto key_term = [&](int buf, int k0, int kt) {
+    f32x4 t4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (BIAS) {
+      t4 = *reinterpret_cast<const f32x4*>(&kts[buf][kt * 16 + 4 * g]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t4[j] *= kLog2e;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (k0 + kt * 16 + 4 * g + j >= kend) t4[j] = -INFINITY;
+    return t4;
+  };
+  auto stage = [&](int buf, int k0, auto masked) {
+    constexpr bool MASK = decltype(masked)::value;
+    float sst[kSub];
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) sst[sub] = 0.0f;
+#pragma unroll 1
+    for (int kt = 0; kt < kStage / 16; ++kt) {
+      f32x4 kt4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      if constexpr (MASK) kt4 = key_term(buf, k0, kt);
+      f32x4 acc[kSub];
+      tile_acc(buf, kt, acc);
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = MASK ? __builtin_fmaf(acc[sub][j], c2, kt4[j]) - mref[sub]
+                               : __builtin_fmaf(acc[sub][j], c2, -mref[sub]);
+          sst[sub] += __builtin_amdgcn_exp2f(x);
+        }
+      }
+    }
+    float mx = sst[0];
+#pragma unroll
+    for (int sub = 1; sub < kSub; ++sub) mx = fmaxf(mx, sst[sub]);
+    if (__builtin_amdgcn_ballot_w64(!(mx <= kLazyLimit)) == 0) {
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) ssum[sub] += sst[sub];
+      return;
+    }
+    // rare, wave-uniform: exact redo with the reference moved to every new maximum
+#pragma unroll 1
+    for (int kt = 0; kt < kStage / 16; ++kt) {
+      const f32x4 kt4 = key_term(buf, k0, kt);
+      f32x4 acc[kSub];
+      tile_acc(buf, kt, acc);
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(acc[sub][j], c2, kt4[j]);
+        const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        if (m4 > mref[sub]) {
+          ssum[sub] *= __builtin_amdgcn_exp2f(mref[sub] - m4);
+          mref[sub] = m4;
+        }
+        const float mr = mref[sub];
+        ssum[sub] += (__builtin_amdgcn_exp2f(x[0] - mr) + __builtin_amdgcn_exp2f(x[1] - mr)) +
+                     (__builtin_amdgcn_exp2f(x[2] - mr) + __builtin_amdgcn_exp2f(x[3] - mr));
+      }
+    }
+  };
+
+  // kLseBufs - 1 stages in flight. At stage st a wave waits for its own loads of st (those of the
+  // later stages already issued may stay outstanding), the barrier then makes every wave's loads
+  // visible and guarantees that nobody still reads the buffer the next issue overwrites.
+  constexpr int kLoadsPerStage = BIAS ? 5 : 4;
+  static_assert(kLseBufs == 3, "the wait counts below assume two stages in flight");
+  // the stationary rows have landed before any stage load is issued, so inside the loop the
+  // compiler has no register load left to wait for (its own waits would be vmcnt(0))
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  issue(0);
+  if (nst > 1) issue(1);
+  for (int st = 0; st < nst; ++st) {
+    if (st + 1 < nst) {
+      vm_wait_barrier<kLoadsPerStage>();
+    } else {
+      vm_wait_barrier<0>();
+    }
+    if (st + 2 < nst) issue(st + 2);
+    const int k0 = kbeg + st * kStage;
+    // the bias and the keys past the chunk enter through the per-key term; other stages skip it
+    if (BIAS || k0 + kStage > kend) {
+      stage(st % kLseBufs, k0, std::true_type{});
+    } else {
+      stage(st % kLseBufs, k0, std::false_type{});
+    }
+  }
+
+  const int64_t pbase = T.off[i] + ((int64_t)h * nkc + kc) * R;
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+    float m1 = mref[sub], s1 = ssum[sub];
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const float m2 = __shfl_xor(m1, off), s2 = __shfl_xor(s1, off);
+      const float mm = fmaxf(m1, m2);
+      s1 = s1 * __builtin_amdgcn_exp2f(m1 - mm) + s2 * __builtin_amdgcn_exp2f(m2 - mm);
+      m1 = mm;
+    }
+    const int r = row0 + sub * 16 + c16;
+    if (g == 0 && r < R) partials[pbase + r] = make_float2(m1, s1);
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Combine the per-chunk partials of every proxy row into its natural-log LSE.
+// Work item = (sequence, KV head, 256-row block); partial chunk count per unit = nchunk(n).
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ partials, float* __restrict__ lse_out,
+                                                   int H, int R, int kchunk, SeqTable T) {
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int n = T.n[i];
+  const int s = T.first + i;
+  const int nkc = (n + kchunk - 1) / kchunk;
+  const int nrb = (R + 255) / 256;
+  const int local = t - T.start[i];
+  const int h = local / nrb;
+  const int r = (local - h * nrb) * 256 + threadIdx.x;
+  if (r >= R) return;
+  const float2* p = partials + T.off[i] + (int64_t)h * nkc * R + r;
+  float mm = -INFINITY;
+  for (int c = 0; c < nkc; ++c) mm = fmaxf(mm, p[(int64_t)c * R].x);
+  float sum = 0.0f;
+  for (int c = 0; c < nkc; ++c) {
+    const float2 v = p[(int64_t)c * R];
+    sum += v.y * __builtin_amdgcn_exp2f(v.x - mm);
+  }
+  lse_out[((int64_t)s * H + h) * R + r] = (mm + __builtin_log2f(sum)) * kLn2;
+}
+
+// ------------------------------------------------------------------------------------------------
+// launchers
+// ------------------------------------------------------------------------------------------------
+int lse_mfma_row_blocks(int R) { return (R + kPerBlock - 1) / kPerBlock; }
+
+hipError_t launch_lse_partials_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+                                    int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
+                                    float scale, int kchunk, const SeqTable& T, hipStream_t st) {
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kk = static_cast<const uint16_t*>(k);
+  dim3 grid(T.total), block(kThreads);
+  if (paged) {
+    if (has_bias)
+      lse_partials_mfma<true, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
+    else
+      lse_partials_mfma<true, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
+  } else {
+    if (has_bias)
+      lse_partials_mfma<false, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
+    else
+      lse_partials_mfma<false, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int R, int kchunk, const SeqTable& T,
+                              hipStream_t st) {
+  lse_combine<<<dim3(T.total), dim3(256), 0, st>>>(partials, lse_out, H, R, kchunk, T);
+  return hipGetLastError();
+}
+
+}  // namespace kvc

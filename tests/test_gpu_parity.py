@@ -215,6 +215,52 @@ def test_lse_entry_point():
         say(f"[ok] lse {w.name}: max abs err {np.abs(got - ref).max():.3g}")
 
 
+def _wide_range_inputs(seed, n, q, rising):
+    """One unit whose logits span hundreds of nats: the first coordinate of key j follows a
+    staircase (each 256-key step adds 400, so the running maximum jumps by ~35 nats per step when
+    the query's first coordinate is positive and falls when it is negative) with isolated spikes;
+    the other coordinates are small noise. bf16 bit patterns, [1][1][n][128] / [1][1][q][128]."""
+    rng = np.random.default_rng(seed)
+    d = 128
+    K = rng.standard_normal((n, d)).astype(np.float32) * 0.5
+    step = (np.arange(n) // 256).astype(np.float32)
+    K[:, 0] = (-2000.0 + 400.0 * step) if rising else (2000.0 - 400.0 * step)
+    spikes = rng.choice(n, size=max(1, n // 500), replace=False)
+    K[spikes, 0] += 3000.0
+    Q = rng.standard_normal((q, d)).astype(np.float32) * 0.5
+    Q[:, 0] = rng.choice([-3.0, -1.0, 0.0, 0.5, 1.0, 3.0], size=q)
+    return W.f32_to_bf16_bits(Q)[None, None], W.f32_to_bf16_bits(K)[None, None]
+
+
+@pytest.mark.parametrize("rising", [True, False])
+def test_lse_and_scores_wide_logit_ranges(rising):
+    """Logits from about -700 to +1100 nats with jumps far beyond the float32 exponent range
+    between tiles, chunks and rows: the LSE pass must follow every rise of the maximum."""
+    import online_compaction_amd as oc
+    P = _P()
+    n, q = 5000, 48
+    Q, K = _wide_range_inputs(201 if rising else 202, n, q, rising)
+    V = np.zeros_like(K)
+    scale = 1.0 / np.sqrt(128.0)
+    say(f"[case] wide logit ranges, rising={rising}: n={n} rows={q}")
+    b = P.contiguous_batch(Q, K, V, [n], [n // 5], 1, scale)
+    out = torch.zeros((1, 1, q), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, oc.kvc_lse_workspace_size(b.shape, b.kview())), dtype=torch.uint8, device="cuda")
+    oc.kvc_lse(b.shape, b.q, b.kview(), None, out, ws)
+    o = P.allocate(b)
+    P.run(b, o)
+    torch.cuda.synchronize()
+    rows = O.unit_rows(Q, 0, 0, 1)
+    ref_lse = O.lse_unit(rows, K[0, 0], "bf16", scale)
+    got = out.cpu().numpy().reshape(-1)
+    np.testing.assert_allclose(got, ref_lse, rtol=2e-6, atol=2e-5)
+    ref = O.score_unit(rows, K[0, 0], "bf16", scale)
+    worst = check_scores(P.host_array(o.scores)[0, 0, :n], ref, "wide range")
+    check_selection_band(P.host_array(o.kept)[0, 0], ref, n // 5, "wide range")
+    say(f"[ok] wide logit ranges: LSE span {ref_lse.min():.0f}..{ref_lse.max():.0f}, "
+        f"max LSE err {np.abs(got - ref_lse).max():.3g}, worst score rel err {worst:.3g}")
+
+
 # ------------------------------------------------------------------------------------- paged
 
 def test_paged_bf16_mfma_permuted():
