@@ -27,12 +27,19 @@ Readings where the pages leave a step open (each is listed with its reason in th
     positions outside W, holes are positions of W that are not kept, both ascending, the i-th
     source fills the i-th hole. The new block table is old[N-X .. N), entries X .. N-1 become
     -1, and old[0 .. N-X) are freed, i.e. ceil(n/B) - ceil(m/B) blocks.
+  * ActKV retention ([ACT], paragraph on action-critical entries and LRFU): the attention that
+    the action tokens pay an entry is their mean weight on it; "within the top 90 %" is read as
+    the shortest run of entries, in descending attention order (ties to the lower position),
+    that holds 90 % of the total attention, the sums taken on the float32 masses quantised to
+    multiples of 2^-32 (so that the membership decision is exact on both sides); LRFU's value
+    decays by 2^-lambda per policy step and a hit adds 1.
 
 Every function below has pins in the CPU test suite (worked examples, closed forms, brute
 force and invariants); none is "parity unpinned".
 """
 from __future__ import annotations
 
+import math
 from dataclasses import dataclass
 
 import numpy as np
@@ -200,6 +207,88 @@ def table_update_segment(table_row: np.ndarray, start: int, n: int, cache_len: i
     kept_blocks = old[:b] + old[b + F:NT]
     new = np.array(kept_blocks + [-1] * F + old[NT:], dtype=np.int32)
     return new, np.array(freed, dtype=np.int32)
+
+
+# ----------------------------------------------------------------------------- ActKV retention
+
+def attention_mass(Q: np.ndarray, K: np.ndarray, scale: float, lse_rows: np.ndarray | None = None,
+                   bias: np.ndarray | None = None, row_chunk: int = 256) -> np.ndarray:
+    """Attention the proxy rows pay each key, averaged over the rows ([ACT]: for every entry,
+    the attention scores of all action tokens on it): mass_j = (1/R) * sum_r alpha_rj, with
+    alpha_rj = exp(l_rj - LSE_r) as in the score."""
+    R, n = Q.shape[0], K.shape[0]
+    if lse_rows is None:
+        lse_rows = lse(Q, K, scale, bias, row_chunk)
+    lse_rows = np.asarray(lse_rows, dtype=np.float64)
+    acc = np.zeros(n, dtype=np.float64)
+    for r0 in range(0, R, row_chunk):
+        L = logits(Q[r0:r0 + row_chunk], K, scale, bias)
+        acc += np.exp(L - lse_rows[r0:r0 + row_chunk, None]).sum(axis=0)
+    return acc / R
+
+
+MASS_QUANTUM = 2 ** 32   # a mass of 1 is this many integer units
+MASS_CAP = 2 ** 40       # per-entry cap of the integer mass (masses above 256)
+
+
+def quantised_mass(mass_f32) -> list:
+    """Integer mass of each float32 value: min(floor(mass * 2^32), 2^40), as Python ints."""
+    return [min(math.floor(float(x) * MASS_QUANTUM), MASS_CAP) for x in np.asarray(mass_f32, dtype=np.float32)]
+
+
+def action_critical(mass_f32, top_p: float) -> np.ndarray:
+    """Action-critical entries of one unit ([ACT]: entries within the top 90 % of the action
+    attention). Walk the entries in descending float32 mass, ties to the lower position, and
+    take them until their integer masses add up to at least ceil(top_p * U), U the total
+    integer mass (nothing when U = 0). Returns a boolean mask over the entries."""
+    v = np.asarray(mass_f32, dtype=np.float32)
+    n = v.shape[0]
+    u = quantised_mass(v)
+    total = sum(u)
+    hit = np.zeros(n, dtype=bool)
+    if total == 0:
+        return hit
+    target = math.ceil(float(top_p) * float(total))
+    order = np.lexsort((np.arange(n), -v.astype(np.float64)))  # mass desc, then position asc
+    acc = 0
+    for j in order:
+        hit[j] = True
+        acc += u[j]
+        if acc >= target:
+            break
+    return hit
+
+
+def lrfu_step(state: np.ndarray, hit: np.ndarray, decay: float) -> np.ndarray:
+    """One LRFU step ([ACT]: LRFU whose hit signal is "hit by action attention"): every
+    entry's combined recency-frequency value is multiplied by decay = 2^-lambda and a hit adds 1."""
+    return float(decay) * np.asarray(state, dtype=np.float64) + np.asarray(hit, dtype=np.float64)
+
+
+def lrfu_crf(hit_steps, now: int, lam: float) -> float:
+    """LRFU's combined recency-frequency value at step `now` of an entry hit at the given steps:
+    the sum over hits of (1/2)^(lam * (now - t))."""
+    return float(sum(0.5 ** (lam * (now - t)) for t in hit_steps))
+
+
+def side_order(n: int, m: int, B: int, kept) -> list:
+    """Old position of the entry found at each new position 0..m-1 after compaction: the kept
+    list itself for contiguous compaction (B = 0); for the paged slot plan, window slot start + p
+    keeps its own entry when kept, else holds the source paired with that hole."""
+    kept = [int(j) for j in kept]
+    if B == 0:
+        return kept
+    plan = paged_plan(n, m, B, kept)
+    filled = dict(zip(plan.dst, plan.src))
+    return [filled.get(w, w) for w in range(plan.start, plan.start + m)]
+
+
+def mass_unit(Qs, Ks, dtype, scale, bias=None, lse_rows=None):
+    """Attention mass of one unit from stored rows/keys (widened exactly to float64)."""
+    Qd = widen(Qs, dtype)
+    Kd = widen(Ks, dtype)
+    b = None if bias is None else np.asarray(bias, dtype=np.float64)
+    return attention_mass(Qd, Kd, scale, lse_rows=lse_rows, bias=b)
 
 
 # ----------------------------------------------------------------------------- whole batches
