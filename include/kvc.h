@@ -12,6 +12,8 @@
  *         attention; eviction holes are closed by a conflict-free slot plan (tail X logical blocks
  *         are the target region, kept entries outside it are paired one-to-one with holes inside
  *         it, all pairs are copied in one parallel pass) and the emptied blocks are returned.
+ *         Paragraph on the eviction policy: action-critical entries (the top 90 % of the action
+ *         tokens' attention) feed an LRFU ranking with decay lambda = 0.5.
  *
  * Conventions shared by every entry point
  *   unit        one (sequence s, KV head h). A "sequence" may also be one layer of a trajectory or
@@ -117,6 +119,19 @@ kvc_status kvc_score(const kvc_shape* shape, const void* q, const kvc_kv_view* k
                      const float* bias, float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * kvc_attention_mass -- mean attention weight of every key over the proxy rows,
+ * mass_j = (1/R) sum_r exp(l_rj - LSE_r). This is the per-entry tally of the attention that the
+ * action tokens pay an entry, which ActKV's retention policy thresholds ([ACT], paragraph on
+ * action-critical entries). Same arguments, workspace, LSE rules and determinism as kvc_score;
+ * mass sums to 1 over the n_s keys when the LSE is computed (or exact).
+ *   mass    device out [S][H][n_max] float32, segment-relative; entries j >= n_s not written.
+ * Accuracy: within 1e-3 relative of the float64 definition for every mass >= 1e-30 (weights
+ * below 2^-126 relative to the 2^100 offset are flushed to zero).
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_attention_mass(const kvc_shape* shape, const void* q, const kvc_kv_view* k, const float* lse,
+                              const float* bias, float* mass, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * kvc_select_topm -- per unit, the m_s positions with the largest scores, ties to the lower
  * position, written in ascending position order ([TE] top-m).
  *   scores  device [S][H][n_max] float32, non-negative and finite
@@ -171,6 +186,42 @@ kvc_status kvc_compact_paged(const kvc_shape* shape, kvc_dtype dtype, void* k_po
                              const int32_t* kept, const int32_t* m, int32_t m_max,
                              const int32_t* cache_lens, int32_t* freed_blocks, int32_t* freed_counts,
                              void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_lrfu_update -- one step of ActKV's retention state ([ACT], paragraph on action-critical
+ * entries: the attention of all action tokens on each entry is tallied, entries within the top
+ * 90 % are action-critical, and LRFU -- with "hit by action attention" as its hit signal and a
+ * decay of lambda = 0.5 -- ranks the entries). Per unit:
+ *   critical set  the shortest run of entries in descending mass order (ties to the lower
+ *                 position) whose integer masses u_j = min(floor(mass_j * 2^32), 2^40) add up to
+ *                 at least ceil(top_p * U), U = sum_j u_j computed exactly (empty when U = 0);
+ *   state_j       = fmaf(decay, state_j, critical ? 1 : 0) for every j < n_s.
+ * Exact: the same float32 masses always give the same critical set, whatever the summation order.
+ *   mass    device [S][H][n_max] float32, non-negative (e.g. from kvc_attention_mass),
+ *           segment-relative
+ *   top_p   in (0, 1] (0.9 for ActKV); decay in [0, 1] (2^-lambda per step; 2^-0.5 for ActKV)
+ *   state   device in/out [S][H][n_max] float32, segment-relative; entries j >= n_s untouched
+ *   counts  device out [S][H] int32, the size of each unit's critical set, or NULL
+ * Retention then keeps the m_s entries with the largest state: kvc_select_topm(state), the
+ * compaction of K/V, and kvc_compact_side to carry the state along.
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_lrfu_update(const kvc_shape* shape, const float* mass, double top_p, float decay, float* state,
+                           int32_t* counts, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_compact_side -- carries a per-entry float32 side array (such as the LRFU state) through a
+ * compaction, so that it stays aligned with the compacted K/V:
+ *   dst[s][h][p] = src[s][h][start_s + old(p)] for p < m_s,
+ * where old(p) = kept[p] for contiguous compaction (block_size = 0) and, for the paged slot plan
+ * of kvc_compact_paged with block size B (block_size = B), the position whose K/V occupies window
+ * slot p afterwards: a kept position inside the window stays, a hole receives its paired source.
+ *   kept    device [S][H][m_max] int32, strictly ascending, < n_s (as from select)
+ *   m       host [S]; m_max >= max m_s
+ *   src     device [S][H][n_max] float32; dst device out [S][H][m_max] float32 (distinct from src;
+ *           rows p >= m_s not written)
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_compact_side(const kvc_shape* shape, int32_t block_size, const int32_t* kept, const int32_t* m,
+                            int32_t m_max, const float* src, float* dst, void* stream);
 
 /* Static text for a status code; never NULL. */
 const char* kvc_status_string(kvc_status status);

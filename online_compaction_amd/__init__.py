@@ -9,9 +9,12 @@ from ._abi import (  # noqa: F401
     KvcError,
     KView,
     Shape,
+    kvc_attention_mass,
     kvc_compact_contig,
     kvc_compact_paged,
+    kvc_compact_side,
     kvc_lse,
+    kvc_lrfu_update,
     kvc_lse_workspace_size,
     kvc_score,
     kvc_score_workspace_size,

@@ -48,6 +48,14 @@ _SIGS = {
     "kvc_score": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView), ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p]),
+    "kvc_attention_mass": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p]),
+    "kvc_lrfu_update": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_double, ctypes.c_float,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "kvc_compact_side": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_select_topm": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_compact_contig": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
@@ -207,6 +215,41 @@ def kvc_score(shape: Shape, q, k: KView, lse, bias, scores, ws=None, stream=None
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().kvc_score(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), _ptr(lse), _ptr(bias), _ptr(scores),
                             _ptr(ws), ws_bytes, _stream(stream)), "kvc_score")
+
+
+def kvc_attention_mass(shape: Shape, q, k: KView, lse, bias, mass, ws=None, stream=None) -> None:
+    S, H, HG, R = shape.num_seqs, shape.num_kv_heads, shape.num_kv_heads * shape.group, shape.num_queries
+    _need(q, S * HG * R * shape.head_dim * _elt(k.dtype), "q")
+    _check_kview(shape, k)
+    _need(lse, S * HG * R * 4, "lse")
+    _need(bias, S * shape.n_max * 4, "bias")
+    _need(mass, S * H * shape.n_max * 4, "mass")
+    sh, _keep = shape.c()
+    kv = k.c()
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().kvc_attention_mass(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), _ptr(lse), _ptr(bias),
+                                     _ptr(mass), _ptr(ws), ws_bytes, _stream(stream)), "kvc_attention_mass")
+
+
+def kvc_lrfu_update(shape: Shape, mass, top_p: float, decay: float, state, counts=None, stream=None) -> None:
+    S, H = shape.num_seqs, shape.num_kv_heads
+    _need(mass, S * H * shape.n_max * 4, "mass")
+    _need(state, S * H * shape.n_max * 4, "state")
+    _need(counts, S * H * 4, "counts")
+    sh, _keep = shape.c()
+    _check(load().kvc_lrfu_update(ctypes.byref(sh), _ptr(mass), float(top_p), float(decay), _ptr(state),
+                                  _ptr(counts), _stream(stream)), "kvc_lrfu_update")
+
+
+def kvc_compact_side(shape: Shape, block_size: int, kept, m, m_max: int, src, dst, stream=None) -> None:
+    S, H = shape.num_seqs, shape.num_kv_heads
+    _need(kept, S * H * m_max * 4, "kept")
+    _need(src, S * H * shape.n_max * 4, "src")
+    _need(dst, S * H * m_max * 4, "dst")
+    sh, _keep = shape.c()
+    marr, mp = _host_i32(m)
+    _check(load().kvc_compact_side(ctypes.byref(sh), int(block_size), _ptr(kept), mp, int(m_max), _ptr(src),
+                                   _ptr(dst), _stream(stream)), "kvc_compact_side")
 
 
 def kvc_select_topm(shape: Shape, scores, m, m_max: int, kept, stream=None) -> None:

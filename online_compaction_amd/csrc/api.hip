@@ -12,7 +12,7 @@
 #include "kvc_internal.h"
 
 namespace kvc {
-// kernel launchers (score_mfma.hip, score_valu.hip, select.hip, compact.hip)
+// kernel launchers (score_mfma.hip, lse_mfma.hip, score_valu.hip, select.hip, retain.hip, compact.hip)
 int score_mfma_tiles(int n);
 int lse_mfma_row_blocks(int R);
 int score_valu_tiles(int n);
@@ -20,7 +20,7 @@ int contig_tiles(int m, bool f32);
 int paged_tiles(int m);
 hipError_t launch_score_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
+                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st);
 hipError_t launch_lse_partials_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
                                     int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
                                     float scale, int kchunk, const SeqTable& T, hipStream_t st);
@@ -28,12 +28,17 @@ hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int
                               hipStream_t st);
 hipError_t launch_score_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
+                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st);
 hipError_t launch_lse_partials_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k,
                                     const int32_t* table, int max_blocks, const float* bias, float2* partials, int H,
                                     int R, int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
 hipError_t launch_select(const float* scores, int32_t* kept, int H, int64_t n_max, int m_max, const SeqTable& T,
                          hipStream_t st);
+hipError_t launch_lrfu_update(const float* mass, float* state, int32_t* counts, int H, int64_t n_max, double top_p,
+                              float decay, const SeqTable& T, hipStream_t st);
+int side_tiles(int m);
+hipError_t launch_compact_side(const float* src, float* dst, const int32_t* kept, int H, int64_t n_max, int m_max,
+                               int B, const SeqTable& T, hipStream_t st);
 hipError_t launch_compact_contig(bool f32, const void* k, const void* v, const int32_t* kept, void* ko, void* vo, int H,
                                  int64_t n_max, int m_max, const SeqTable& T, hipStream_t st);
 hipError_t launch_paged_copy(bool f32, void* kp, void* vp, const int32_t* table, int max_blocks, const int32_t* kept,
@@ -290,11 +295,14 @@ size_t kvc_score_workspace_size(const kvc_shape* sh, const kvc_kv_view* k, int l
   return partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
 }
 
-kvc_status kvc_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse, const float* bias,
-                     float* scores, void* ws, size_t ws_bytes, void* stream) {
+// Per-key reduction over the proxy rows of alpha^pw: pw = 2 gives the TE score (after the square
+// root), pw = 1 the attention mass.
+static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse,
+                            const float* bias, float* out, void* ws, size_t ws_bytes, void* stream, int pw,
+                            const char* what) {
   if (kvc_status st = check_shape(sh)) return st;
   if (kvc_status st = check_view(sh, k)) return st;
-  if (!q || !scores) return fail(KVC_ERR_INVALID_ARGUMENT, "q and scores must be non-NULL");
+  if (!q || !out) return fail(KVC_ERR_INVALID_ARGUMENT, "q and %s must be non-NULL", what);
   if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int R = sh->group * sh->num_queries;
@@ -303,7 +311,7 @@ kvc_status kvc_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, c
     const size_t pb = partials_bytes(sh, lse_kchunk(sh, k));
     const size_t need = pb + lse_bytes(sh);
     if (!ws || ws_bytes < need)
-      return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "score needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+      return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "%s needs %zu workspace bytes, got %zu", what, need, ws ? ws_bytes : 0);
     float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pb);
     if (kvc_status s2 = run_lse(sh, q, k, bias, lse_ws, ws, st)) return s2;
     lse_rows = lse_ws;
@@ -317,12 +325,22 @@ kvc_status kvc_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, c
       no_offset, [&](const SeqTable& T) {
         if (mf)
           return launch_score_mfma(paged, bias != nullptr, q, k->data, k->block_table, k->max_blocks, lse_rows, bias,
-                                   scores, H, R, sh->n_max, sh->scale, T, st);
+                                   out, H, R, sh->n_max, sh->scale, pw, T, st);
         return launch_score_valu(k->dtype == KVC_F32, paged, bias != nullptr, q, k->data, k->block_table,
-                                 k->max_blocks, lse_rows, bias, scores, H, R, sh->n_max, sh->scale, T, st);
+                                 k->max_blocks, lse_rows, bias, out, H, R, sh->n_max, sh->scale, pw, T, st);
       });
   if (e != hipSuccess) return hip_fail(e, "score kernel");
   return ok();
+}
+
+kvc_status kvc_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse, const float* bias,
+                     float* scores, void* ws, size_t ws_bytes, void* stream) {
+  return run_score(sh, q, k, lse, bias, scores, ws, ws_bytes, stream, 2, "scores");
+}
+
+kvc_status kvc_attention_mass(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse,
+                              const float* bias, float* mass, void* ws, size_t ws_bytes, void* stream) {
+  return run_score(sh, q, k, lse, bias, mass, ws, ws_bytes, stream, 1, "mass");
 }
 
 static kvc_status check_budgets(const kvc_shape* sh, const int32_t* m, int32_t m_max) {
@@ -348,6 +366,39 @@ kvc_status kvc_select_topm(const kvc_shape* sh, const float* scores, const int32
         return launch_select(scores, kept, sh->num_kv_heads, sh->n_max, m_max, T, static_cast<hipStream_t>(stream));
       });
   if (err != hipSuccess) return hip_fail(err, "select kernel");
+  return ok();
+}
+
+kvc_status kvc_lrfu_update(const kvc_shape* sh, const float* mass, double top_p, float decay, float* state,
+                           int32_t* counts, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (!mass || !state) return fail(KVC_ERR_INVALID_ARGUMENT, "mass and state must be non-NULL");
+  if (!(top_p > 0.0 && top_p <= 1.0)) return fail(KVC_ERR_INVALID_ARGUMENT, "top_p = %g outside (0, 1]", top_p);
+  if (!(decay >= 0.0f && decay <= 1.0f)) return fail(KVC_ERR_INVALID_ARGUMENT, "decay = %g outside [0, 1]", decay);
+  const hipError_t err = for_each_chunk(
+      sh, nullptr, [&](int) { return sh->num_kv_heads; }, no_offset, [&](const SeqTable& T) {
+        return launch_lrfu_update(mass, state, counts, sh->num_kv_heads, sh->n_max, top_p, decay, T,
+                                  static_cast<hipStream_t>(stream));
+      });
+  if (err != hipSuccess) return hip_fail(err, "lrfu kernel");
+  return ok();
+}
+
+kvc_status kvc_compact_side(const kvc_shape* sh, int32_t block_size, const int32_t* kept, const int32_t* m,
+                            int32_t m_max, const float* src, float* dst, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (kvc_status st = check_contig_extent(sh, "compact_side")) return st;
+  if (block_size < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "block_size = %d < 0", block_size);
+  if (!kept || !src || !dst) return fail(KVC_ERR_INVALID_ARGUMENT, "kept, src and dst must be non-NULL");
+  if (static_cast<const void*>(src) == static_cast<const void*>(dst))
+    return fail(KVC_ERR_INVALID_ARGUMENT, "src and dst must be distinct buffers");
+  const hipError_t err = for_each_chunk(
+      sh, m, [&](int s) { return sh->num_kv_heads * side_tiles(m[s]); }, no_offset, [&](const SeqTable& T) {
+        return launch_compact_side(src, dst, kept, sh->num_kv_heads, sh->n_max, m_max, block_size, T,
+                                   static_cast<hipStream_t>(stream));
+      });
+  if (err != hipSuccess) return hip_fail(err, "side-array compaction kernel");
   return ok();
 }
 

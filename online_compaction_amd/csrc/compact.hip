@@ -171,6 +171,59 @@ __global__ __launch_bounds__(1024) void table_update(int32_t* __restrict__ table
   for (int j = NT - F + threadIdx.x; j < NT; j += blockDim.x) tr[j] = -1;
 }
 
+// ------------------------------------------------------------------------------------------------
+// Per-entry float32 side array (e.g. LRFU state) carried through a compaction: new position p of
+// a unit receives the entry of old position old(p): kept[p] for contiguous compaction (B = 0);
+// for the paged slot plan, window slot start + p keeps its own entry when kept, else holds the
+// source paired with that hole (the i-th hole gets the i-th kept position outside the window).
+// Work item = (sequence, KV head, 256 new positions). src [S][H][n_max] (read at the segment's
+// first position + old), dst [S][H][m_max].
+// ------------------------------------------------------------------------------------------------
+constexpr int kSideTile = 256;
+
+__global__ __launch_bounds__(kSideTile) void compact_side(const float* __restrict__ src, float* __restrict__ dst,
+                                                          const int32_t* __restrict__ kept, int H, int64_t n_max,
+                                                          int m_max, int B, SeqTable T) {
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int n = T.n[i], m = T.m[i];
+  const int s = T.first + i;
+  const int tiles = (m + kSideTile - 1) / kSideTile;
+  const int local = t - T.start[i];
+  const int h = local / tiles;
+  const int p = (local - h * tiles) * kSideTile + threadIdx.x;
+  if (p >= m) return;
+  const int64_t unit = (int64_t)s * H + h;
+  const int32_t* ku = kept + unit * m_max;
+  int old;
+  if (B == 0) {
+    old = ku[p];
+  } else {
+    const int start = ((n + B - 1) / B - (m + B - 1) / B) * B;
+    const int w = start + p;
+    const int lo = lower_bound_i32(ku, m, w);
+    if (lo < m && ku[lo] == w) {
+      old = w;
+    } else {
+      const int a = lower_bound_i32(ku, m, start);      // kept before the window
+      const int e = lower_bound_i32(ku, m, start + m);  // first kept past the window
+      const int hole = (w - start) - (lo - a);          // rank of w among the holes
+      const int q = hole < a ? hole : e + (hole - a);
+      old = (unsigned)q < (unsigned)m ? ku[q] : -1;
+    }
+  }
+  if ((unsigned)old >= (unsigned)n) return;  // only for a kept list that breaks the contract
+  dst[unit * m_max + p] = src[unit * n_max + T.kofs[i] + old];
+}
+
+int side_tiles(int m) { return (m + kSideTile - 1) / kSideTile; }
+
+hipError_t launch_compact_side(const float* src, float* dst, const int32_t* kept, int H, int64_t n_max, int m_max,
+                               int B, const SeqTable& T, hipStream_t st) {
+  compact_side<<<dim3(T.total), dim3(kSideTile), 0, st>>>(src, dst, kept, H, n_max, m_max, B, T);
+  return hipGetLastError();
+}
+
 int contig_tiles(int m, bool f32) {
   const int rows = f32 ? 32 : 64;
   return (m + rows - 1) / rows;

@@ -18,6 +18,8 @@ constexpr float kLn2 = 0.6931471805599453f;
 // 2^-113 survives float32's normal range; the offset is removed after the square root.
 constexpr float kSqOffset = 100.0f;
 constexpr float kSqUnscale = 8.8817841970012523e-16f;  // 2^-50
+// Attention mass (plain weights) uses the same offset: exp2(log2(alpha) + kSqOffset), unscaled by 2^-100.
+constexpr float kMassUnscale = 7.8886090522101181e-31f;  // 2^-100
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));

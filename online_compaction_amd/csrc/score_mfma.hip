@@ -34,12 +34,14 @@ constexpr int kBufs = 3;                            // LDS stage buffers (two lo
 // ------------------------------------------------------------------------------------------------
 // Scores. Work item = (sequence, KV head, 512-key tile).
 // lse: natural-log LSE per proxy row, [S][H*G][q] == [unit][R].
+// pw = 2: s_j = sqrt((1/R) sum_r alpha_rj^2) (the TE score); pw = 1: (1/R) sum_r alpha_rj, the
+// mean attention weight the proxy rows give key j (the per-entry action-attention tally of ActKV).
 // ------------------------------------------------------------------------------------------------
 template <bool PAGED, bool BIAS>
 __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, float* __restrict__ scores,
-    int H, int R, int64_t n_max, float scale, SeqTable T) {
+    int H, int R, int64_t n_max, float scale, int pw, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[kBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float lss[kBufs][kStage];
 
@@ -57,6 +59,8 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   const int g = lane >> 4, c16 = lane & 15;
   const int32_t* trow = PAGED ? table + (int64_t)s * max_blocks : nullptr;
 
+  // pw = 2: squared weights (the score); pw = 1: the weights themselves (attention mass)
+  const float pl2 = (float)pw * kLog2e;
   // keys of this wave, held for the whole row sweep
   bf16x8 kb[kScoreSub][4];
   float bb[kScoreSub];
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
       const u32x4* p = key_row<PAGED>(k, trow, H, h, n_max, unit, ko + key);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kb[sub][ks] = as_bf16x8(p[4 * ks + g]);
-      if constexpr (BIAS) bb[sub] = 2.0f * kLog2e * bias[(int64_t)s * n_max + key];
+      if constexpr (BIAS) bb[sub] = pl2 * bias[(int64_t)s * n_max + key];
     } else {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kb[sub][ks] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
@@ -78,7 +82,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
 
   const uint16_t* qu = q + unit * (int64_t)R * kHeadDim;
   const float* lu = lse + unit * (int64_t)R;
-  const float a2 = 2.0f * kLog2e * scale;
+  const float a2 = pl2 * scale;
   const int nst = (R + kStage - 1) / kStage;
 
   // A stage (64 proxy rows) goes global -> LDS without passing through registers: each wave
@@ -113,7 +117,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
       f32x4 nb4 = *reinterpret_cast<const f32x4*>(&lss[buf][rt * 16 + 4 * g]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        nb4[e] = __builtin_fmaf(nb4[e], -2.0f * kLog2e, kSqOffset);
+        nb4[e] = __builtin_fmaf(nb4[e], -pl2, kSqOffset);
         if constexpr (MASK)
           if (r0 + rt * 16 + 4 * g + e >= R) nb4[e] = -INFINITY;
       }
@@ -166,7 +170,8 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     v += __shfl_xor(v, 16);
     v += __shfl_xor(v, 32);
     const int key = key0 + sub * 16 + c16;
-    if (g == 0 && key < n) scores[unit * n_max + key] = __builtin_sqrtf(v * invR) * kSqUnscale;
+    if (g == 0 && key < n)
+      scores[unit * n_max + key] = pw == 2 ? __builtin_sqrtf(v * invR) * kSqUnscale : v * invR * kMassUnscale;
   }
 }
 
@@ -177,20 +182,20 @@ int score_mfma_tiles(int n) { return (n + kScoreKeys - 1) / kScoreKeys; }
 
 hipError_t launch_score_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, const SeqTable& T, hipStream_t st) {
+                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
   if (paged) {
     if (has_bias)
-      score_mfma<true, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, T);
+      score_mfma<true, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
     else
-      score_mfma<true, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, T);
+      score_mfma<true, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
   } else {
     if (has_bias)
-      score_mfma<false, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, T);
+      score_mfma<false, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
     else
-      score_mfma<false, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, T);
+      score_mfma<false, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
   }
   return hipGetLastError();
 }

@@ -8,7 +8,8 @@
 // address, a broadcast), and each logit is a 128-term FMA chain.
 //   pass 1 (lse_partials_valu): per proxy row, (max, sum) of 2^(log2e * logit) over the
 //           block's 256 keys -> workspace partials, combined by lse_combine.
-//   pass 2 (score_valu): per key, sum over rows of exp2(2 log2(alpha) + 100) -> score.
+//   pass 2 (score_valu): per key, sum over rows of exp2(2 log2(alpha) + 100) -> score, or of
+//           exp2(log2(alpha) + 100) -> attention mass.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -90,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
                                                        const int32_t* __restrict__ table, int max_blocks,
                                                        const float* __restrict__ lse, const float* __restrict__ bias,
                                                        float* __restrict__ scores, int H, int R, int64_t n_max,
-                                                       float scale, SeqTable T) {
+                                                       float scale, int pw, SeqTable T) {
   __shared__ __attribute__((aligned(16))) float qs[kRowsStage][kHeadDim];
   __shared__ float nbs[kRowsStage];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -111,17 +112,19 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
   else
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) kr[e] = 0.f;
+  // pw = 2: squared weights (the score); pw = 1: the weights themselves (attention mass)
+  const float pl2 = (float)pw * kLog2e;
   float bb = 0.f;
-  if constexpr (BIAS) bb = valid ? 2.0f * kLog2e * bias[(int64_t)s * n_max + key] : 0.f;
+  if constexpr (BIAS) bb = valid ? pl2 * bias[(int64_t)s * n_max + key] : 0.f;
 
-  const float a2 = 2.0f * kLog2e * scale;
+  const float a2 = pl2 * scale;
   float acc = 0.f;
   for (int r0 = 0; r0 < R; r0 += kRowsStage) {
     __syncthreads();
     stage_rows<F32>(q, unit, R, r0, qs);
     if (threadIdx.x < kRowsStage) {
       const int r = r0 + threadIdx.x;
-      nbs[threadIdx.x] = r < R ? kSqOffset - 2.0f * kLog2e * lse[unit * R + r] : -INFINITY;
+      nbs[threadIdx.x] = r < R ? kSqOffset - pl2 * lse[unit * R + r] : -INFINITY;
     }
     __syncthreads();
     const int rows = min(kRowsStage, R - r0);
@@ -131,7 +134,9 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
       acc += __builtin_amdgcn_exp2f(x);
     }
   }
-  if (valid) scores[unit * n_max + key] = __builtin_sqrtf(acc / (float)R) * kSqUnscale;
+  if (valid)
+    scores[unit * n_max + key] =
+        pw == 2 ? __builtin_sqrtf(acc / (float)R) * kSqUnscale : acc / (float)R * kMassUnscale;
 }
 
 // Work item = (sequence, KV head, 256-key tile); partial chunk = the tile.
@@ -221,9 +226,9 @@ int score_valu_tiles(int n) { return (n + kThreads - 1) / kThreads; }
 
 hipError_t launch_score_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, const SeqTable& T, hipStream_t st) {
+                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(kThreads);
-  KVC_VALU_DISPATCH(score_valu, q, k, table, max_blocks, lse, bias, scores, H, R, n_max, scale, T);
+  KVC_VALU_DISPATCH(score_valu, q, k, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
   return hipGetLastError();
 }
 

@@ -7,7 +7,7 @@
 // the number `need` of positions equal to T that must be kept. One ordered sweep then keeps
 // every position above T and the first `need` positions equal to T, compacting them in index
 // order with block-wide prefix sums.
-#include "kvc_internal.h"
+#include "block_scan.h"
 
 namespace kvc {
 
@@ -17,32 +17,6 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBins = 2048;
 constexpr int kItems = 4;  // consecutive positions per thread in the ordered sweep
 
-// Exclusive prefix sum over the block in thread order; `total` gets the block sum.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t& total, uint32_t* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t w = lane < kWaves ? wsum[lane] : 0u;
-#pragma unroll
-    for (int off = 1; off < kWaves; off <<= 1) {
-      const uint32_t y = __shfl_up(w, off);
-      if (lane >= off) w += y;
-    }
-    if (lane < kWaves) wsum[lane] = w;
-  }
-  __syncthreads();
-  const uint32_t before = wave > 0 ? wsum[wave - 1] : 0u;
-  total = wsum[kWaves - 1];
-  __syncthreads();
-  return before + x - v;
-}
 }  // namespace
 
 // Work item = (sequence, KV head).
@@ -84,7 +58,7 @@ __global__ __launch_bounds__(kThreads) void select_topm(const float* __restrict_
     const int b0 = 2 * (kThreads - 1 - tid);
     const uint32_t h0 = hist[b0], h1 = hist[b0 + 1];
     uint32_t tot;
-    const uint32_t above = block_excl_scan(h0 + h1, tot, wsum);  // candidates in bins >= b0 + 2
+    const uint32_t above = block_excl_scan<kWaves>(h0 + h1, tot, wsum);  // candidates in bins >= b0 + 2
     const uint32_t ge1 = above + h1;                               // ... in bins >= b0 + 1
     const uint32_t ge0 = ge1 + h0;                                 // ... in bins >= b0
     if (tid == 0) {
@@ -125,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void select_topm(const float* __restrict_
       eqc += eq[e];
     }
     uint32_t eq_tot;
-    uint32_t rank = eq_seen + block_excl_scan(eqc, eq_tot, wsum);
+    uint32_t rank = eq_seen + block_excl_scan<kWaves>(eqc, eq_tot, wsum);
     bool take[kItems];
     uint32_t tc = 0;
 #pragma unroll
@@ -135,7 +109,7 @@ __global__ __launch_bounds__(kThreads) void select_topm(const float* __restrict_
       tc += take[e];
     }
     uint32_t tk_tot;
-    uint32_t pos = base + block_excl_scan(tc, tk_tot, wsum);
+    uint32_t pos = base + block_excl_scan<kWaves>(tc, tk_tot, wsum);
 #pragma unroll
     for (int e = 0; e < kItems; ++e)
       if (take[e]) {

@@ -176,3 +176,24 @@ def test_binding_refuses_short_buffers():
     with pytest.raises(ValueError):
         A._need(Fake(), 41, "x")
     A._need(Fake(), 40, "x")
+
+
+def test_retention_validation(lib):
+    """Attention mass, LRFU update and side-array compaction reject bad arguments up front."""
+    sh, keep = _shape().c()
+    kv = A.KView(FAKE, A.KVC_BF16).c()
+    assert lib.kvc_attention_mass(ctypes.byref(sh), FAKE, ctypes.byref(kv), FAKE, None, None, None, 0,
+                                  None) == A.KVC_ERR_INVALID_ARGUMENT
+    st = lib.kvc_attention_mass(ctypes.byref(sh), FAKE, ctypes.byref(kv), None, None, FAKE, FAKE, 16, None)
+    assert st == A.KVC_ERR_WORKSPACE_TOO_SMALL and b"mass needs" in lib.kvc_last_error()
+    for top_p, decay in ((0.0, 0.5), (1.5, 0.5), (float("nan"), 0.5), (0.9, -0.1), (0.9, 1.5), (0.9, float("nan"))):
+        st = lib.kvc_lrfu_update(ctypes.byref(sh), FAKE, top_p, decay, FAKE, None, None)
+        assert st == A.KVC_ERR_INVALID_ARGUMENT, (top_p, decay)
+    assert lib.kvc_lrfu_update(ctypes.byref(sh), None, 0.9, 0.7, FAKE, None, None) == A.KVC_ERR_INVALID_ARGUMENT
+    m_ok = (ctypes.c_int32 * 2)(6600, 4000)
+    assert lib.kvc_compact_side(ctypes.byref(sh), 16, FAKE, m_ok, 6600, FAKE, FAKE, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert b"distinct" in lib.kvc_last_error()
+    assert lib.kvc_compact_side(ctypes.byref(sh), -1, FAKE, m_ok, 6600, FAKE, FAKE + 64, None) == \
+        A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_compact_side(ctypes.byref(sh), 0, FAKE, m_ok, 100, FAKE, FAKE + 64, None) == \
+        A.KVC_ERR_INVALID_ARGUMENT
