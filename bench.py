@@ -50,8 +50,10 @@ def describe(w) -> str:
     n = f"n={w.n[0]}" if len(set(w.n)) == 1 else f"n={min(w.n)}..{max(w.n)}"
     if w.seg_len:
         n += f", segment [{w.seg_start}, {w.seg_start + w.seg_len})"
+    pol = (", scored by attention mass, kept by LRFU state (ActKV: 90 % action-critical, lambda 0.5)"
+           if w.name == "actkv" else "")
     return (f"{w.name}: {w.S} seqs x {w.H} KV heads, G={w.G}, q={w.q}, R={w.R}, {n}, d={w.d}, {w.dtype}, "
-            f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}")
+            f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}{pol}")
 
 
 def trajectory_tokens(w) -> int:
@@ -80,11 +82,16 @@ def algorithmic_bytes(w, moved_rows=None) -> dict:
     if not w.lse_supplied:
         score += entries * row + rows_q * row  # LSE pass reads K and Q once more
     select = entries * 4 + kept * 4
+    if w.name == "actkv":
+        select += entries * 12  # LRFU step: mass read, state read and written
+        kept_side = kept * 8    # the state carried through compaction (read + write)
+    else:
+        kept_side = 0
     if w.paged:
         moved = kept if moved_rows is None else moved_rows
-        compact = kept * 4 + moved * 2 * row * 2
+        compact = kept * 4 + moved * 2 * row * 2 + kept_side
     else:
-        compact = kept * 4 + kept * 2 * row * 2
+        compact = kept * 4 + kept * 2 * row * 2 + kept_side
     return dict(score=score, select=select, compact=compact, total=score + select + compact)
 
 
@@ -108,8 +115,14 @@ def _oracle_unit(args):
     if w.lse_supplied:  # the supplied input, prepared outside the timed region
         lse_rows = O.lse_unit(Qr, K, w.dtype, w.logit_scale, bias_row).astype(np.float32).astype(np.float64)
     t0 = time.perf_counter()
-    sc = O.score_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
-    kept = O.select_topm(sc, w.m[s])
+    if w.name == "actkv":  # attention mass -> action-critical set -> LRFU step -> top-m of the state
+        mass = O.mass_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
+        hit = O.action_critical(mass.astype(np.float32), 0.9)
+        st0 = np.random.default_rng([4096, s, h]).random(K.shape[0]) * 3.41
+        kept = O.select_topm(O.lrfu_step(st0, hit, 2.0 ** -0.5), w.m[s])
+    else:
+        sc = O.score_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
+        kept = O.select_topm(sc, w.m[s])
     O.gather(K, kept)
     O.gather(V, kept)
     return time.perf_counter() - t0
@@ -238,6 +251,15 @@ def main():
         b.lse = lse
         del ws
     o = P.allocate(b)
+    retention = None
+    if w.name == "actkv":  # a warm LRFU state: seeded values in [0, 1 / (1 - 2^-0.5))
+        st0 = np.random.default_rng(4096).random((w.S, w.H, w.n_max)).astype(np.float32) * 3.41
+        retention = P.allocate_retention(b, st0)
+        pristine = pristine + (retention.state.clone(),)
+        stages = (lambda: P.run_retention_score(b, o, retention), lambda: P.run_retention_select(b, o, retention),
+                  lambda: P.run_retention_compact(b, o, retention))
+    else:
+        stages = (lambda: P.run_score(b, o), lambda: P.run_select(b, o), lambda: P.run_compact(b, o))
     torch.cuda.synchronize()
     log("[bench] inputs resident on the GPU")
 
@@ -253,28 +275,35 @@ def main():
             b.k_pool.copy_(pristine[0])
             b.v_pool.copy_(pristine[1])
             b.table.copy_(pristine[2])
+            if retention is not None:
+                retention.state.copy_(pristine[3])
 
     for _ in range(args.warmup):
         restore()
-        P.run(b, o)
+        for run_stage in stages:
+            run_stage()
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
 
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     stage_ms = np.zeros((args.steps, 3))
+    host_ms = np.zeros((args.steps, 3))  # time the host spends enqueueing each stage
+
+    def timed_step(i):
+        e = ev[i]
+        e[0].record()
+        for k in range(3):
+            h0 = time.perf_counter()
+            stages[k]()
+            host_ms[i, k] = (time.perf_counter() - h0) * 1e3
+            e[k + 1].record()
+
     wall = 0.0
     if pristine is None:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(args.steps):
-            e = ev[i]
-            e[0].record()
-            P.run_score(b, o)
-            e[1].record()
-            P.run_select(b, o)
-            e[2].record()
-            P.run_compact(b, o)
-            e[3].record()
+            timed_step(i)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
     else:  # paged: restore the pristine pool before each step, outside the timed region
@@ -282,14 +311,7 @@ def main():
             restore()
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            e = ev[i]
-            e[0].record()
-            P.run_score(b, o)
-            e[1].record()
-            P.run_select(b, o)
-            e[2].record()
-            P.run_compact(b, o)
-            e[3].record()
+            timed_step(i)
             torch.cuda.synchronize()
             wall += time.perf_counter() - t0
     for i in range(args.steps):
@@ -297,8 +319,9 @@ def main():
         stage_ms[i] = [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
     ms_step = wall * 1e3 / args.steps
     avg = stage_ms.mean(axis=0)
+    havg = host_ms.mean(axis=0)
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (score {avg[0]:.3f}, select {avg[1]:.3f}, "
-        f"compact {avg[2]:.3f} ms)")
+        f"compact {avg[2]:.3f} ms; host enqueue {havg[0]:.3f} / {havg[1]:.3f} / {havg[2]:.3f} ms)")
 
     moved = None
     if w.paged:
@@ -343,7 +366,7 @@ def main():
             "mfma_util": achieved_tf / MFMA_BF16_PEAK_TFLOPS,
         },
         "roofline": {
-            "kernel": "score_mfma (kvc_score)",
+            "kernel": "score_mfma (kvc_attention_mass)" if w.name == "actkv" else "score_mfma (kvc_score)",
             "bound": "mfma",
             "achieved": achieved_tf,
             "peak": MFMA_BF16_PEAK_TFLOPS,

@@ -144,3 +144,43 @@ def run(b: Batch, o: Outputs, stream=None) -> None:
     run_score(b, o, stream)
     run_select(b, o, stream)
     run_compact(b, o, stream)
+
+
+# ------------------------------------------------------------------------ ActKV retention stages
+
+@dataclass
+class Retention:
+    """Per-entry LRFU state of a batch and the buffers of one retention step."""
+    state: torch.Tensor        # float32 [S][H][n_max]
+    mass: torch.Tensor         # float32 [S][H][n_max]
+    side: torch.Tensor         # float32 [S][H][m_max], the state carried through compaction
+    counts: torch.Tensor       # int32 [S][H], critical-set sizes
+    top_p: float = 0.9
+    decay: float = 2.0 ** -0.5
+
+
+def allocate_retention(b: Batch, state=None) -> Retention:
+    sh = b.shape
+    dev = b.q.device
+    full = (sh.num_seqs, sh.num_kv_heads, sh.n_max)
+    st = torch.zeros(full, dtype=torch.float32, device=dev) if state is None else device_tensor(state, dev)
+    return Retention(st, torch.zeros(full, dtype=torch.float32, device=dev),
+                     torch.zeros((sh.num_seqs, sh.num_kv_heads, b.m_max), dtype=torch.float32, device=dev),
+                     torch.zeros((sh.num_seqs, sh.num_kv_heads), dtype=torch.int32, device=dev))
+
+
+def run_retention_score(b: Batch, o: Outputs, r: Retention, stream=None) -> None:
+    """The attention the proxy (action) rows pay each entry."""
+    A.kvc_attention_mass(b.shape, b.q, b.kview(), b.lse, b.bias, r.mass, o.ws, stream)
+
+
+def run_retention_select(b: Batch, o: Outputs, r: Retention, stream=None) -> None:
+    """Action-critical set + LRFU step, then the budget's largest LRFU values."""
+    A.kvc_lrfu_update(b.shape, r.mass, r.top_p, r.decay, r.state, r.counts, stream)
+    A.kvc_select_topm(b.shape, r.state, b.m, b.m_max, o.kept, stream)
+
+
+def run_retention_compact(b: Batch, o: Outputs, r: Retention, stream=None) -> None:
+    """K/V compaction, with the LRFU state carried along into r.side."""
+    run_compact(b, o, stream)
+    A.kvc_compact_side(b.shape, b.block_size if b.paged else 0, o.kept, b.m, b.m_max, r.state, r.side, stream)

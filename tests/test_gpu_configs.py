@@ -280,3 +280,51 @@ def test_turn_segment_36_layers():
     assert np.array_equal(P.host_array(b.k_pool), kp), "turn K pool"
     assert np.array_equal(P.host_array(b.v_pool), vp), "turn V pool"
     say("[ok] turn: 288 units pass; pools, tables and freed lists bit-exact on all 36 layers")
+
+
+def test_actkv_retention_step_full():
+    """ActKV's retention step on the action-token trajectory (8 KV heads, n = 33000, 1320 action
+    rows, +0.5 bias on the last 25 %), budget 14706, from the benchmark's warm LRFU state:
+    mass against the oracle on every head, the critical sets exact, the LRFU state, the kept set
+    (exactly the top-m of the GPU's own state), the paged compaction and the carried state."""
+    P = _P()
+    w = W.spec("actkv")
+    data = W.build_paged(w, _workers())
+    n, m, B = w.n[0], w.m[0], w.block_size
+    b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], data["n"], data["m"], w.G,
+                      w.logit_scale, B, n_max=w.n_max, bias=data["bias"])
+    st0 = np.random.default_rng(4096).random((w.S, w.H, w.n_max)).astype(np.float32) * 3.41
+    o = P.allocate(b)
+    r = P.allocate_retention(b, st0)
+    P.run_retention_score(b, o, r)
+    torch.cuda.synchronize()
+    mass = P.host_array(r.mass)
+    P.run_retention_select(b, o, r)
+    torch.cuda.synchronize()
+    state = P.host_array(r.state)
+    P.run_retention_compact(b, o, r)
+    torch.cuda.synchronize()
+    kept, side, crit = P.host_array(o.kept), P.host_array(r.side), P.host_array(r.counts)
+    kp, vp, table = data["k_pool"], data["v_pool"], data["table"].copy()
+    plans = []
+    for h in range(w.H):
+        tag = f"actkv h={h}"
+        keys = O.paged_unit_keys(kp, table[0], n, h, B)
+        ref = O.mass_unit(O.unit_rows(data["Q"], 0, h, w.G), keys, w.dtype, w.logit_scale, data["bias"][0, :n])
+        worst = check_scores(mass[0, h, :n], ref, tag)
+        hit = O.action_critical(mass[0, h, :n], 0.9)
+        assert crit[0, h] == hit.sum()
+        np.testing.assert_allclose(state[0, h, :n], O.lrfu_step(st0[0, h, :n], hit, 2.0 ** -0.5), rtol=2e-7)
+        check_kept_form(kept[0, h], m, n, tag)
+        check_selection_exact(kept[0, h], state[0, h, :n], m, tag)
+        plans.append(O.paged_plan(n, m, B, kept[0, h, :m]))
+        order = np.array(O.side_order(n, m, B, kept[0, h, :m]), dtype=np.int64)
+        assert np.array_equal(side[0, h, :m], state[0, h, order]), f"{tag}: carried state"
+        say(f"[ok] {tag}: mass worst rel err {worst:.3g}, critical {int(hit.sum())} entries")
+    for h in range(w.H):
+        O.apply_paged_copy(kp, vp, table[0], h, plans[h])
+    new, freed = O.table_update(table[0], n, m, B)
+    assert np.array_equal(P.host_array(b.table)[0], new)
+    assert np.array_equal(P.host_array(o.freed)[0, :len(freed)], freed)
+    assert np.array_equal(P.host_array(b.k_pool), kp) and np.array_equal(P.host_array(b.v_pool), vp)
+    say("[ok] actkv: pools, table and freed list bit-exact")

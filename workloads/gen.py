@@ -138,6 +138,12 @@ def spec(name: str, k: int | None = None) -> Workload:
         n = 33000
         return Workload(f"c4k{kk}", 4, 1, 8, 4, 330, 128, (n,), (c4_budget(kk),), "bf16", "mixture", "action",
                         paged=True, block_size=16, table="identity", max_blocks=-(-n // 16), bias_tail=0.5)
+    if name == "actkv":
+        # ActKV's retention step on the action-token trajectory: the inputs of "c4" (same seed),
+        # budget 14706 (six ratchet expansions); scored by attention mass, kept by LRFU state
+        n = 33000
+        return Workload("actkv", 4, 1, 8, 4, 330, 128, (n,), (c4_budget(6),), "bf16", "mixture", "action",
+                        paged=True, block_size=16, table="identity", max_blocks=-(-n // 16), bias_tail=0.5)
     if name == "turn":
         # one 4096-token turn in the middle of a 33000-token trajectory held in 36 layers' paged
         # caches, scored with the 512 queries per query head of the turn that followed it; the
