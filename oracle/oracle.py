@@ -33,6 +33,11 @@ Readings where the pages leave a step open (each is listed with its reason in th
     that holds 90 % of the total attention, the sums taken on the float32 masses quantised to
     multiples of 2^-32 (so that the membership decision is exact on both sides); LRFU's value
     decays by 2^-lambda per policy step and a hit adds 1.
+  * Layout-preserving eviction ([IKV] "IntentKV" page, layout-preserving eviction): evicted
+    positions are redirected to one reserved dead slot in a per-position slot map; the page's
+    constant sentinel key cannot cancel every query's attention (a query whose components sum
+    below zero favours it), so the dead slot is read as a logit mask: a position mapped to it
+    takes no part in the softmax and its own score is 0.
 
 Every function below has pins in the CPU test suite (worked examples, closed forms, brute
 force and invariants); none is "parity unpinned".
@@ -289,6 +294,38 @@ def mass_unit(Qs, Ks, dtype, scale, bias=None, lse_rows=None):
     Kd = widen(Ks, dtype)
     b = None if bias is None else np.asarray(bias, dtype=np.float64)
     return attention_mass(Qd, Kd, scale, lse_rows=lse_rows, bias=b)
+
+
+# ----------------------------------------------------------------------------- layout-preserving eviction
+
+def evict_redirect(slot_row, kept, n: int, dead: int) -> np.ndarray:
+    """[IKV] sentinel dead slot: every position of [0, n) that is not kept is redirected to the
+    dead slot; kept positions and positions past n keep their slots."""
+    out = np.array(slot_row, dtype=np.int64, copy=True)
+    keep = set(int(j) for j in kept)
+    for p in range(n):
+        if p not in keep:
+            out[p] = dead
+    return out
+
+
+def slot_unit_keys(pool, slot_row, n: int, h: int):
+    """Stored keys [n][d] of head h read through a per-position slot map (pool [slots][H][d])."""
+    return pool[np.asarray(slot_row[:n], dtype=np.int64), h, :]
+
+
+def score_unit_live(Qs, Ks, live, dtype, scale, bias=None, lse_rows=None, power: int = 2):
+    """TE score (power 2) or attention mass (power 1) of one unit when only the `live` positions
+    take part in the softmax (the logit-mask reading of the dead slot); dead positions score 0."""
+    live = np.asarray(live, dtype=bool)
+    out = np.zeros(live.shape[0], dtype=np.float64)
+    if not live.any():
+        return out
+    Kl = np.asarray(Ks)[live]
+    b = None if bias is None else np.asarray(bias)[live]
+    f = score_unit if power == 2 else mass_unit
+    out[live] = f(Qs, Kl, dtype, scale, b, lse_rows)
+    return out
 
 
 # ----------------------------------------------------------------------------- whole batches
