@@ -14,6 +14,8 @@
  *         it, all pairs are copied in one parallel pass) and the emptied blocks are returned.
  *         Paragraph on the eviction policy: action-critical entries (the top 90 % of the action
  *         tokens' attention) feed an LRFU ranking with decay lambda = 0.5.
+ *   [IKV] "IntentKV: Cross-Turn Intent-Aware KV Cache Pruning for Agent Inference" (gist.science),
+ *         layout-preserving eviction: evicted positions are redirected to a sentinel dead slot.
  *
  * Conventions shared by every entry point
  *   unit        one (sequence s, KV head h). A "sequence" may also be one layer of a trajectory or
@@ -77,13 +79,23 @@ typedef struct {
 
 /* How keys are addressed. Contiguous: data is [S][H][n_max][d]. Paged (vLLM-style pool):
  * data is [num_blocks][block_size][H][d] and cache position p of sequence s lives in physical
- * block block_table[s * max_blocks + p / block_size], slot p % block_size. */
+ * block block_table[s * max_blocks + p / block_size], slot p % block_size. Slot map
+ * (layout-preserving eviction, [IKV]): data is a slot pool [num_slots][H][d] -- a paged pool is
+ * one, with slot = block * B + offset -- and position p of unit (s, h) lives in slot
+ * slot_map[(s * H + h) * n_max + p], row head h. A position whose slot is dead_slot has been
+ * evicted without moving anything: it takes no part in any softmax (its logit is -inf, the
+ * reading of the page's sentinel key as a logit mask) and its score or mass is 0. The dead
+ * slot's row must hold finite values (e.g. the page's constants); a unit with no live key
+ * gets LSE -inf. */
 typedef struct {
   const void* data;            /* device                                                  */
   kvc_dtype dtype;             /* element type of K (and of the queries)                  */
-  int32_t block_size;          /* 0 = contiguous; else B (this build: 16)                 */
+  int32_t block_size;          /* 0 = contiguous; else B (this build: 16); ignored with a slot map */
   const int32_t* block_table;  /* device [S][max_blocks] (paged only, else NULL)          */
   int32_t max_blocks;          /* row stride of block_table; ceil((start_s + n_s) / B) <= max_blocks */
+  const int32_t* slot_map;     /* device [S][H][n_max] int32 slots, or NULL (then block_size decides);
+                                  start_s + n_s <= n_max                                   */
+  int32_t dead_slot;           /* with slot_map: the sentinel dead slot, or -1 for none   */
 } kvc_kv_view;
 
 /* ---------------------------------------------------------------------------------------------
@@ -186,6 +198,21 @@ kvc_status kvc_compact_paged(const kvc_shape* shape, kvc_dtype dtype, void* k_po
                              const int32_t* kept, const int32_t* m, int32_t m_max,
                              const int32_t* cache_lens, int32_t* freed_blocks, int32_t* freed_counts,
                              void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * kvc_evict_redirect -- layout-preserving eviction ([IKV], IntentKV page, layout-preserving
+ * eviction: an evicted position's slot-map entry is redirected to a reserved sentinel dead slot
+ * instead of compacting). For every unit and every scored position j < n_s that is not in
+ * kept[s][h][0..m_s):  slot_map[(s * H + h) * n_max + start_s + j] = dead_slot. Kept positions,
+ * positions outside the segment and every K/V row stay where they are, so prefix identity and
+ * RoPE phases are preserved; scoring through the map (kvc_kv_view.slot_map) then masks them.
+ *   kept       device [S][H][m_max] int32, strictly ascending, < n_s (as from select)
+ *   m          host [S]; m_max >= max m_s
+ *   slot_map   device in/out [S][H][n_max] int32
+ *   dead_slot  >= 0
+ * ------------------------------------------------------------------------------------------- */
+kvc_status kvc_evict_redirect(const kvc_shape* shape, const int32_t* kept, const int32_t* m, int32_t m_max,
+                              int32_t* slot_map, int32_t dead_slot, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * kvc_lrfu_update -- one step of ActKV's retention state ([ACT], paragraph on action-critical

@@ -13,6 +13,7 @@ from ._abi import (  # noqa: F401
     kvc_compact_contig,
     kvc_compact_paged,
     kvc_compact_side,
+    kvc_evict_redirect,
     kvc_lse,
     kvc_lrfu_update,
     kvc_lse_workspace_size,

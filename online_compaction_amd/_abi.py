@@ -35,7 +35,8 @@ class _Shape(ctypes.Structure):
 
 class _KView(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int), ("block_size", ctypes.c_int32),
-                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32)]
+                ("block_table", ctypes.c_void_p), ("max_blocks", ctypes.c_int32), ("slot_map", ctypes.c_void_p),
+                ("dead_slot", ctypes.c_int32)]
 
 
 _lib = None
@@ -51,6 +52,8 @@ _SIGS = {
     "kvc_attention_mass": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView),
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]),
+    "kvc_evict_redirect": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "kvc_lrfu_update": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_double, ctypes.c_float,
                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_compact_side": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_int32, ctypes.c_void_p,
@@ -122,10 +125,12 @@ class KView:
     block_size: int = 0
     block_table: object = None  # device int32 tensor [S][max_blocks] (paged)
     max_blocks: int = 0
+    slot_map: object = None     # device int32 tensor [S][H][n_max] (slot pool [slots][H][d])
+    dead_slot: int = -1
 
     def c(self):
         return _KView(_ptr(self.data), int(self.dtype), int(self.block_size), _ptr(self.block_table),
-                      int(self.max_blocks))
+                      int(self.max_blocks), _ptr(self.slot_map), int(self.dead_slot))
 
 
 def _ptr(t):
@@ -172,7 +177,9 @@ def _elt(dtype: int) -> int:
 
 def _check_kview(shape: Shape, kv: KView):
     S, H, d = shape.num_seqs, shape.num_kv_heads, shape.head_dim
-    if kv.block_size == 0:
+    if kv.slot_map is not None:
+        _need(kv.slot_map, S * H * shape.n_max * 4, "slot_map")
+    elif kv.block_size == 0:
         _need(kv.data, S * H * shape.n_max * d * _elt(kv.dtype), "k")
     else:
         _need(kv.block_table, S * kv.max_blocks * 4, "block_table")
@@ -229,6 +236,16 @@ def kvc_attention_mass(shape: Shape, q, k: KView, lse, bias, mass, ws=None, stre
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().kvc_attention_mass(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), _ptr(lse), _ptr(bias),
                                      _ptr(mass), _ptr(ws), ws_bytes, _stream(stream)), "kvc_attention_mass")
+
+
+def kvc_evict_redirect(shape: Shape, kept, m, m_max: int, slot_map, dead_slot: int, stream=None) -> None:
+    S, H = shape.num_seqs, shape.num_kv_heads
+    _need(kept, S * H * m_max * 4, "kept")
+    _need(slot_map, S * H * shape.n_max * 4, "slot_map")
+    sh, _keep = shape.c()
+    marr, mp = _host_i32(m)
+    _check(load().kvc_evict_redirect(ctypes.byref(sh), _ptr(kept), mp, int(m_max), _ptr(slot_map), int(dead_slot),
+                                     _stream(stream)), "kvc_evict_redirect")
 
 
 def kvc_lrfu_update(shape: Shape, mass, top_p: float, decay: float, state, counts=None, stream=None) -> None:

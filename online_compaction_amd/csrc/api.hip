@@ -18,20 +18,23 @@ int lse_mfma_row_blocks(int R);
 int score_valu_tiles(int n);
 int contig_tiles(int m, bool f32);
 int paged_tiles(int m);
-hipError_t launch_score_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+hipError_t launch_score_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st);
-hipError_t launch_lse_partials_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st);
+hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                                     int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
-                                    float scale, int kchunk, const SeqTable& T, hipStream_t st);
+                                    float scale, int kchunk, int dead, const SeqTable& T, hipStream_t st);
 hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int R, int kchunk, const SeqTable& T,
                               hipStream_t st);
-hipError_t launch_score_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+hipError_t launch_score_valu(bool f32, int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st);
-hipError_t launch_lse_partials_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k,
+                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st);
+hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const void* q, const void* k,
                                     const int32_t* table, int max_blocks, const float* bias, float2* partials, int H,
-                                    int R, int64_t n_max, float scale, const SeqTable& T, hipStream_t st);
+                                    int R, int64_t n_max, float scale, int dead, const SeqTable& T, hipStream_t st);
+hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
+                                 const SeqTable& T, hipStream_t st);
+int redirect_tiles(int n);
 hipError_t launch_select(const float* scores, int32_t* kept, int H, int64_t n_max, int m_max, const SeqTable& T,
                          hipStream_t st);
 hipError_t launch_lrfu_update(const float* mass, float* state, int32_t* counts, int H, int64_t n_max, double top_p,
@@ -53,7 +56,7 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kVersion = 100;          // 0.1.0
+constexpr int kVersion = 200;          // 0.2.0: slot-map key views, retention entry points
 constexpr int kBlockSize = 16;         // the one page size this build supports
 constexpr int kMfmaMinRows = 16;       // bf16 units with fewer proxy rows use the VALU path
 constexpr int64_t kMaxRows = 1 << 24;  // proxy rows per unit
@@ -140,9 +143,17 @@ kvc_status check_view(const kvc_shape* sh, const kvc_kv_view* kv) {
   if (!kv) return fail(KVC_ERR_INVALID_ARGUMENT, "key view is NULL");
   if (!kv->data) return fail(KVC_ERR_INVALID_ARGUMENT, "key data is NULL");
   if (kvc_status st = check_dtype(kv->dtype)) return st;
+  if (kv->slot_map) {
+    if (kv->dead_slot < -1) return fail(KVC_ERR_INVALID_ARGUMENT, "dead_slot = %d < -1", kv->dead_slot);
+    return check_contig_extent(sh, "slot map");
+  }
   if (kv->block_size == 0) return check_contig_extent(sh, "keys");
   return check_paging(sh, kv->block_size, kv->block_table, kv->max_blocks, "keys");
 }
+
+// Kernel-side addressing of a validated view, and the index table it reads.
+int layout_of(const kvc_kv_view* kv) { return kv->slot_map ? kSlots : (kv->block_size ? kPaged : kContig); }
+const int32_t* index_of(const kvc_kv_view* kv) { return kv->slot_map ? kv->slot_map : kv->block_table; }
 
 bool use_mfma(const kvc_shape* sh, const kvc_kv_view* kv) {
   return kv->dtype == KVC_BF16 && sh->group * sh->num_queries >= kMfmaMinRows;
@@ -223,7 +234,8 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
   const int H = sh->num_kv_heads;
   const int R = sh->group * sh->num_queries;
   const bool mf = use_mfma(sh, kv);
-  const bool paged = kv->block_size != 0;
+  const int layout = layout_of(kv);
+  const int32_t* index = index_of(kv);
   const bool has_bias = bias != nullptr;
   const int kc = lse_kchunk(sh, kv);
   std::vector<int64_t> off(sh->num_seqs);
@@ -239,10 +251,10 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
       sh, nullptr, [&](int s) { return H * rb * ((sh->seq_lens[s] + kc - 1) / kc); }, offset,
       [&](const SeqTable& T) {
         if (mf)
-          return launch_lse_partials_mfma(paged, has_bias, q, kv->data, kv->block_table, kv->max_blocks, bias, parts,
-                                          H, R, sh->n_max, sh->scale, kc, T, st);
-        return launch_lse_partials_valu(kv->dtype == KVC_F32, paged, has_bias, q, kv->data, kv->block_table,
-                                        kv->max_blocks, bias, parts, H, R, sh->n_max, sh->scale, T, st);
+          return launch_lse_partials_mfma(layout, has_bias, q, kv->data, index, kv->max_blocks, bias, parts, H, R,
+                                          sh->n_max, sh->scale, kc, kv->dead_slot, T, st);
+        return launch_lse_partials_valu(kv->dtype == KVC_F32, layout, has_bias, q, kv->data, index, kv->max_blocks,
+                                        bias, parts, H, R, sh->n_max, sh->scale, kv->dead_slot, T, st);
       });
   if (e != hipSuccess) return hip_fail(e, "lse partial kernel");
   e = for_each_chunk(
@@ -317,17 +329,18 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
     lse_rows = lse_ws;
   }
   const bool mf = use_mfma(sh, k);
-  const bool paged = k->block_size != 0;
+  const int layout = layout_of(k);
+  const int32_t* index = index_of(k);
   const int H = sh->num_kv_heads;
   const hipError_t e = for_each_chunk(
       sh, nullptr,
       [&](int s) { return H * (mf ? score_mfma_tiles(sh->seq_lens[s]) : score_valu_tiles(sh->seq_lens[s])); },
       no_offset, [&](const SeqTable& T) {
         if (mf)
-          return launch_score_mfma(paged, bias != nullptr, q, k->data, k->block_table, k->max_blocks, lse_rows, bias,
-                                   out, H, R, sh->n_max, sh->scale, pw, T, st);
-        return launch_score_valu(k->dtype == KVC_F32, paged, bias != nullptr, q, k->data, k->block_table,
-                                 k->max_blocks, lse_rows, bias, out, H, R, sh->n_max, sh->scale, pw, T, st);
+          return launch_score_mfma(layout, bias != nullptr, q, k->data, index, k->max_blocks, lse_rows, bias, out, H,
+                                   R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
+        return launch_score_valu(k->dtype == KVC_F32, layout, bias != nullptr, q, k->data, index, k->max_blocks,
+                                 lse_rows, bias, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
       });
   if (e != hipSuccess) return hip_fail(e, "score kernel");
   return ok();
@@ -399,6 +412,23 @@ kvc_status kvc_compact_side(const kvc_shape* sh, int32_t block_size, const int32
                                    static_cast<hipStream_t>(stream));
       });
   if (err != hipSuccess) return hip_fail(err, "side-array compaction kernel");
+  return ok();
+}
+
+kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const int32_t* m, int32_t m_max,
+                              int32_t* slot_map, int32_t dead_slot, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (kvc_status st = check_contig_extent(sh, "slot map")) return st;
+  if (!kept || !slot_map) return fail(KVC_ERR_INVALID_ARGUMENT, "kept and slot_map must be non-NULL");
+  if (dead_slot < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "dead_slot = %d < 0", dead_slot);
+  const hipError_t err = for_each_chunk(
+      sh, m, [&](int s) { return sh->num_kv_heads * redirect_tiles(sh->seq_lens[s]); }, no_offset,
+      [&](const SeqTable& T) {
+        return launch_evict_redirect(slot_map, kept, sh->num_kv_heads, sh->n_max, m_max, dead_slot, T,
+                                     static_cast<hipStream_t>(stream));
+      });
+  if (err != hipSuccess) return hip_fail(err, "redirect kernel");
   return ok();
 }
 

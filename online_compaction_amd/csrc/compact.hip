@@ -224,6 +224,41 @@ hipError_t launch_compact_side(const float* src, float* dst, const int32_t* kept
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------------
+// Layout-preserving eviction ("IntentKV" page, layout-preserving eviction): the slot-map entry of
+// every scored position that is not kept is redirected to the dead slot; nothing moves.
+// Work item = (sequence, KV head, 256 positions). slot_map [S][H][n_max], positions taken from
+// the segment start.
+// ------------------------------------------------------------------------------------------------
+constexpr int kRedirectTile = 256;
+
+__global__ __launch_bounds__(kRedirectTile) void evict_redirect(int32_t* __restrict__ slot_map,
+                                                                const int32_t* __restrict__ kept, int H,
+                                                                int64_t n_max, int m_max, int dead, SeqTable T) {
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int n = T.n[i], m = T.m[i];
+  const int s = T.first + i;
+  const int tiles = (n + kRedirectTile - 1) / kRedirectTile;
+  const int local = t - T.start[i];
+  const int h = local / tiles;
+  const int p = (local - h * tiles) * kRedirectTile + threadIdx.x;
+  if (p >= n) return;
+  const int64_t unit = (int64_t)s * H + h;
+  const int32_t* ku = kept + unit * m_max;
+  const int lo = lower_bound_i32(ku, m, p);
+  if (lo < m && ku[lo] == p) return;
+  slot_map[unit * n_max + T.kofs[i] + p] = dead;
+}
+
+int redirect_tiles(int n) { return (n + kRedirectTile - 1) / kRedirectTile; }
+
+hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
+                                 const SeqTable& T, hipStream_t st) {
+  evict_redirect<<<dim3(T.total), dim3(kRedirectTile), 0, st>>>(slot_map, kept, H, n_max, m_max, dead, T);
+  return hipGetLastError();
+}
+
 int contig_tiles(int m, bool f32) {
   const int rows = f32 ? 32 : 64;
   return (m + rows - 1) / rows;

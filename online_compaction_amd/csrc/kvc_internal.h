@@ -10,6 +10,10 @@ namespace kvc {
 
 constexpr int kHeadDim = 128;
 constexpr int kChunkSeqs = 128;     // sequences described per launch (kernel-argument table)
+// How keys are addressed: contiguous [S][H][n_max][d]; paged pool through a per-sequence block
+// table; slot pool [slots][H][d] through a per-(sequence, head) slot map with a dead slot.
+enum : int { kContig = 0, kPaged = 1, kSlots = 2 };
+
 // longest key chunk one LSE-pass workgroup may cover (the host picks 4096, 2048, 1024 or 512)
 constexpr int kLseMaxChunk = 4096;
 constexpr float kLog2e = 1.4426950408889634f;

@@ -29,14 +29,16 @@ constexpr int kLseBufs = 3;             // LDS stage buffers (two loads in fligh
 // sharing a key chunk run together on one XCD.
 // partials: float2 [T.off[i] + (h * nkc + kc) * R + row]
 // ------------------------------------------------------------------------------------------------
-template <bool PAGED, bool BIAS>
+template <int LAYOUT, bool BIAS>
 __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ bias, float2* __restrict__ partials, int H, int R,
-    int64_t n_max, float scale, int kchunk, SeqTable T) {
+    int64_t n_max, float scale, int kchunk, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t ks_[kLseBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float kts[BIAS ? kLseBufs : 1][kStage];
-  __shared__ int32_t blks[PAGED ? kLseMaxChunk / 16 + 1 : 1];
+  // the chunk's block-table entries (paged) or slots (slot map)
+  __shared__ __attribute__((aligned(16)))
+  int32_t idx[LAYOUT == kPaged ? kLseMaxChunk / 16 + 1 : (LAYOUT == kSlots ? kLseMaxChunk : 1)];
 
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
@@ -60,20 +62,28 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   const float c2 = kLog2e * scale;
 
   // paged: the chunk's block-table entries (at most kchunk / 16 + 1 <= kLseMaxChunk / 16 + 1,
-  // the host never picks a longer chunk) are read once, so the streamed loads depend on LDS only
+  // the host never picks a longer chunk); slot map: the chunk's slots (at most kLseMaxChunk).
+  // Read once, so the streamed loads (and the dead-slot mask) depend on LDS only.
   const int blk0 = (ko + kbeg) >> 4;
-  if constexpr (PAGED) {
+  if constexpr (LAYOUT == kPaged) {
     const int32_t* trow = table + (int64_t)s * max_blocks;
     const int nb = ((ko + kend - 1) >> 4) - blk0 + 1;
-    for (int b = tid; b < nb; b += kThreads) blks[b] = trow[blk0 + b];
+    for (int b = tid; b < nb; b += kThreads) idx[b] = trow[blk0 + b];
+  } else if constexpr (LAYOUT == kSlots) {
+    const int32_t* srow = table + unit * n_max + ko;  // the unit's slot-map row, segment start
+    for (int j = tid; j < kend - kbeg; j += kThreads) idx[j] = srow[kbeg + j];
+  }
+  if constexpr (LAYOUT != kContig) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): nothing of this loop stays pending below
     __syncthreads();
   }
   auto key_ptr = [&](int key) -> const u32x4* {
     const int pos = ko + key;
-    if constexpr (PAGED) {
-      const int64_t blk = blks[(pos >> 4) - blk0];
+    if constexpr (LAYOUT == kPaged) {
+      const int64_t blk = idx[(pos >> 4) - blk0];
       return reinterpret_cast<const u32x4*>(k + ((blk * 16 + (pos & 15)) * H + h) * kHeadDim);
+    } else if constexpr (LAYOUT == kSlots) {
+      return reinterpret_cast<const u32x4*>(k + ((int64_t)idx[key - kbeg] * H + h) * kHeadDim);
     } else {
       return reinterpret_cast<const u32x4*>(k + (unit * n_max + pos) * kHeadDim);
     }
@@ -142,6 +152,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       for (int sub = 0; sub < kSub; ++sub) acc[sub] = mfma16(a[kk], qb[sub][kk], acc[sub]);
   };
   // per-key term of the lane's 4 keys in tile kt (log2 units): the bias, -inf past the chunk
+  // and for keys in the dead slot
   auto key_term = [&](int buf, int k0, int kt) {
     f32x4 t4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (BIAS) {
@@ -150,8 +161,12 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       for (int j = 0; j < 4; ++j) t4[j] *= kLog2e;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (k0 + kt * 16 + 4 * g + j >= kend) t4[j] = -INFINITY;
+    for (int j = 0; j < 4; ++j) {
+      const int key = k0 + kt * 16 + 4 * g + j;
+      if (key >= kend) t4[j] = -INFINITY;
+      if constexpr (LAYOUT == kSlots)
+        if (key < kend && idx[key - kbeg] == dead) t4[j] = -INFINITY;
+    }
     return t4;
   };
   auto stage = [&](int buf, int k0, auto masked) {
@@ -224,8 +239,9 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     }
     if (st + 2 < nst) issue(st + 2);
     const int k0 = kbeg + st * kStage;
-    // the bias and the keys past the chunk enter through the per-key term; other stages skip it
-    if (BIAS || k0 + kStage > kend) {
+    // the bias, dead slots and the keys past the chunk enter through the per-key term; other
+    // stages skip it
+    if (BIAS || LAYOUT == kSlots || k0 + kStage > kend) {
       stage(st % kLseBufs, k0, std::true_type{});
     } else {
       stage(st % kLseBufs, k0, std::false_type{});
@@ -270,7 +286,7 @@ __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ pa
   float sum = 0.0f;
   for (int c = 0; c < nkc; ++c) {
     const float2 v = p[(int64_t)c * R];
-    sum += v.y * __builtin_amdgcn_exp2f(v.x - mm);
+    if (v.y > 0.0f) sum += v.y * __builtin_amdgcn_exp2f(v.x - mm);  // a chunk without live keys adds nothing
   }
   lse_out[((int64_t)s * H + h) * R + r] = (mm + __builtin_log2f(sum)) * kLn2;
 }
@@ -280,23 +296,23 @@ __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ pa
 // ------------------------------------------------------------------------------------------------
 int lse_mfma_row_blocks(int R) { return (R + kPerBlock - 1) / kPerBlock; }
 
-hipError_t launch_lse_partials_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                                     int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
-                                    float scale, int kchunk, const SeqTable& T, hipStream_t st) {
+                                    float scale, int kchunk, int dead, const SeqTable& T, hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
-  if (paged) {
-    if (has_bias)
-      lse_partials_mfma<true, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
-    else
-      lse_partials_mfma<true, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
+#define KVC_LSE_LAUNCH(L, B)                                                                               \
+  lse_partials_mfma<L, B><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, \
+                                                  kchunk, dead, T)
+  if (layout == kPaged) {
+    if (has_bias) KVC_LSE_LAUNCH(kPaged, true); else KVC_LSE_LAUNCH(kPaged, false);
+  } else if (layout == kSlots) {
+    if (has_bias) KVC_LSE_LAUNCH(kSlots, true); else KVC_LSE_LAUNCH(kSlots, false);
   } else {
-    if (has_bias)
-      lse_partials_mfma<false, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
-    else
-      lse_partials_mfma<false, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, kchunk, T);
+    if (has_bias) KVC_LSE_LAUNCH(kContig, true); else KVC_LSE_LAUNCH(kContig, false);
   }
+#undef KVC_LSE_LAUNCH
   return hipGetLastError();
 }
 

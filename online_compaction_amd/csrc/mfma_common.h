@@ -22,13 +22,16 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 
-// Pointer to the 256-byte stored row at cache position `pos` of unit (s, h).
-template <bool PAGED>
-__device__ __forceinline__ const u32x4* key_row(const uint16_t* __restrict__ k, const int32_t* __restrict__ trow,
+// Pointer to the 256-byte stored row of key position `pos` of unit (s, h). `map` is the
+// sequence's block table (kPaged) or the unit's slot-map row (kSlots); unused when contiguous.
+template <int LAYOUT>
+__device__ __forceinline__ const u32x4* key_row(const uint16_t* __restrict__ k, const int32_t* __restrict__ map,
                                                 int H, int h, int64_t n_max, int64_t unit, int pos) {
-  if constexpr (PAGED) {
-    const int64_t blk = trow[pos >> 4];
+  if constexpr (LAYOUT == kPaged) {
+    const int64_t blk = map[pos >> 4];
     return reinterpret_cast<const u32x4*>(k + ((blk * 16 + (pos & 15)) * H + h) * kHeadDim);
+  } else if constexpr (LAYOUT == kSlots) {
+    return reinterpret_cast<const u32x4*>(k + ((int64_t)map[pos] * H + h) * kHeadDim);
   } else {
     return reinterpret_cast<const u32x4*>(k + (unit * n_max + pos) * kHeadDim);
   }

@@ -37,11 +37,11 @@ constexpr int kBufs = 3;                            // LDS stage buffers (two lo
 // pw = 2: s_j = sqrt((1/R) sum_r alpha_rj^2) (the TE score); pw = 1: (1/R) sum_r alpha_rj, the
 // mean attention weight the proxy rows give key j (the per-entry action-attention tally of ActKV).
 // ------------------------------------------------------------------------------------------------
-template <bool PAGED, bool BIAS>
+template <int LAYOUT, bool BIAS>
 __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, float* __restrict__ scores,
-    int H, int R, int64_t n_max, float scale, int pw, SeqTable T) {
+    int H, int R, int64_t n_max, float scale, int pw, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[kBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float lss[kBufs][kStage];
 
@@ -57,19 +57,28 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   const int64_t unit = (int64_t)s * H + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int32_t* trow = PAGED ? table + (int64_t)s * max_blocks : nullptr;
+  // block-table row of the sequence, or slot-map row of the unit ([S][H][n_max])
+  const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
+                                        : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
 
   // pw = 2: squared weights (the score); pw = 1: the weights themselves (attention mass)
   const float pl2 = (float)pw * kLog2e;
   // keys of this wave, held for the whole row sweep
   bf16x8 kb[kScoreSub][4];
   float bb[kScoreSub];
+  uint32_t deadmask = 0;  // slot map: subtiles whose key sits in the dead slot (scored 0)
   const int key0 = kt * kScoreKeys + wave * (16 * kScoreSub);
 #pragma unroll
   for (int sub = 0; sub < kScoreSub; ++sub) {
     const int key = key0 + sub * 16 + c16;
-    if (key < n) {
-      const u32x4* p = key_row<PAGED>(k, trow, H, h, n_max, unit, ko + key);
+    bool live = key < n;
+    if constexpr (LAYOUT == kSlots)
+      if (live && map[ko + key] == dead) {
+        live = false;
+        deadmask |= 1u << sub;
+      }
+    if (live) {
+      const u32x4* p = key_row<LAYOUT>(k, map, H, h, n_max, unit, ko + key);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kb[sub][ks] = as_bf16x8(p[4 * ks + g]);
       if constexpr (BIAS) bb[sub] = pl2 * bias[(int64_t)s * n_max + key];
@@ -171,7 +180,8 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     v += __shfl_xor(v, 32);
     const int key = key0 + sub * 16 + c16;
     if (g == 0 && key < n)
-      scores[unit * n_max + key] = pw == 2 ? __builtin_sqrtf(v * invR) * kSqUnscale : v * invR * kMassUnscale;
+      scores[unit * n_max + key] = (deadmask >> sub) & 1u ? 0.0f
+                                   : pw == 2 ? __builtin_sqrtf(v * invR) * kSqUnscale : v * invR * kMassUnscale;
   }
 }
 
@@ -180,23 +190,23 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
 // ------------------------------------------------------------------------------------------------
 int score_mfma_tiles(int n) { return (n + kScoreKeys - 1) / kScoreKeys; }
 
-hipError_t launch_score_mfma(bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+hipError_t launch_score_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st) {
+                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
-  if (paged) {
-    if (has_bias)
-      score_mfma<true, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
-    else
-      score_mfma<true, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
+#define KVC_SCORE_LAUNCH(L, B)                                                                             \
+  score_mfma<L, B><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, \
+                                           dead, T)
+  if (layout == kPaged) {
+    if (has_bias) KVC_SCORE_LAUNCH(kPaged, true); else KVC_SCORE_LAUNCH(kPaged, false);
+  } else if (layout == kSlots) {
+    if (has_bias) KVC_SCORE_LAUNCH(kSlots, true); else KVC_SCORE_LAUNCH(kSlots, false);
   } else {
-    if (has_bias)
-      score_mfma<false, true><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
-    else
-      score_mfma<false, false><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
+    if (has_bias) KVC_SCORE_LAUNCH(kContig, true); else KVC_SCORE_LAUNCH(kContig, false);
   }
+#undef KVC_SCORE_LAUNCH
   return hipGetLastError();
 }
 

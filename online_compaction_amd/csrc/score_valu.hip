@@ -18,14 +18,22 @@ namespace {
 constexpr int kThreads = 256;   // keys per block
 constexpr int kRowsStage = 32;  // proxy rows per LDS stage (32 x 512 B = 16 KB)
 
-template <bool F32, bool PAGED>
-__device__ __forceinline__ void load_key_f32(const void* __restrict__ kbase, const int32_t* __restrict__ trow, int H,
+// Stored row of key position `pos` of unit (s, h), widened to float32. `map` is the sequence's
+// block table (kPaged) or the unit's slot-map row (kSlots).
+template <int LAYOUT>
+__device__ __forceinline__ int64_t key_row_index(const int32_t* __restrict__ map, int H, int h, int64_t n_max,
+                                                 int64_t unit, int pos) {
+  if constexpr (LAYOUT == kPaged) return ((int64_t)map[pos >> 4] * 16 + (pos & 15)) * H + h;
+  else if constexpr (LAYOUT == kSlots) return (int64_t)map[pos] * H + h;
+  else return unit * n_max + pos;
+}
+
+template <bool F32, int LAYOUT>
+__device__ __forceinline__ void load_key_f32(const void* __restrict__ kbase, const int32_t* __restrict__ map, int H,
                                              int h, int64_t n_max, int64_t unit, int pos, float (&kr)[kHeadDim]) {
+  const int64_t row = key_row_index<LAYOUT>(map, H, h, n_max, unit, pos);
   if constexpr (F32) {
-    const float* k = static_cast<const float*>(kbase);
-    const float* p;
-    if constexpr (PAGED) p = k + (((int64_t)trow[pos >> 4] * 16 + (pos & 15)) * H + h) * kHeadDim;
-    else p = k + (unit * n_max + pos) * kHeadDim;
+    const float* p = static_cast<const float*>(kbase) + row * kHeadDim;
     const float4* p4 = reinterpret_cast<const float4*>(p);
 #pragma unroll
     for (int c = 0; c < kHeadDim / 4; ++c) {
@@ -33,10 +41,7 @@ __device__ __forceinline__ void load_key_f32(const void* __restrict__ kbase, con
       kr[4 * c] = v.x; kr[4 * c + 1] = v.y; kr[4 * c + 2] = v.z; kr[4 * c + 3] = v.w;
     }
   } else {
-    const uint16_t* k = static_cast<const uint16_t*>(kbase);
-    const uint16_t* p;
-    if constexpr (PAGED) p = k + (((int64_t)trow[pos >> 4] * 16 + (pos & 15)) * H + h) * kHeadDim;
-    else p = k + (unit * n_max + pos) * kHeadDim;
+    const uint16_t* p = static_cast<const uint16_t*>(kbase) + row * kHeadDim;
     const u32x4* p4 = reinterpret_cast<const u32x4*>(p);
 #pragma unroll
     for (int c = 0; c < kHeadDim / 8; ++c) {
@@ -86,12 +91,12 @@ __device__ __forceinline__ float dot_row(const float (&kr)[kHeadDim], const floa
 }  // namespace
 
 // Work item = (sequence, KV head, 256-key tile).
-template <bool F32, bool PAGED, bool BIAS>
+template <bool F32, int LAYOUT, bool BIAS>
 __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ q, const void* __restrict__ k,
                                                        const int32_t* __restrict__ table, int max_blocks,
                                                        const float* __restrict__ lse, const float* __restrict__ bias,
                                                        float* __restrict__ scores, int H, int R, int64_t n_max,
-                                                       float scale, int pw, SeqTable T) {
+                                                       float scale, int pw, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) float qs[kRowsStage][kHeadDim];
   __shared__ float nbs[kRowsStage];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -103,12 +108,15 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
   const int h = local / tiles;
   const int key = (local - h * tiles) * kThreads + threadIdx.x;
   const int64_t unit = (int64_t)s * H + h;
-  const bool valid = key < n;
+  const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
+                                        : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
+  const bool inrange = key < n;
+  const bool isdead = LAYOUT == kSlots && inrange && map[T.kofs[i] + key] == dead;  // scored 0
+  const bool valid = inrange && !isdead;
 
   float kr[kHeadDim];
   if (valid)
-    load_key_f32<F32, PAGED>(k, PAGED ? table + (int64_t)s * max_blocks : nullptr, H, h, n_max, unit, T.kofs[i] + key,
-                             kr);
+    load_key_f32<F32, LAYOUT>(k, map, H, h, n_max, unit, T.kofs[i] + key, kr);
   else
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) kr[e] = 0.f;
@@ -134,19 +142,19 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
       acc += __builtin_amdgcn_exp2f(x);
     }
   }
-  if (valid)
-    scores[unit * n_max + key] =
-        pw == 2 ? __builtin_sqrtf(acc / (float)R) * kSqUnscale : acc / (float)R * kMassUnscale;
+  if (inrange)
+    scores[unit * n_max + key] = isdead ? 0.0f
+                                 : pw == 2 ? __builtin_sqrtf(acc / (float)R) * kSqUnscale : acc / (float)R * kMassUnscale;
 }
 
 // Work item = (sequence, KV head, 256-key tile); partial chunk = the tile.
 // partials: float2 [T.off[i] + (h * ntiles + tile) * R + row]
-template <bool F32, bool PAGED, bool BIAS>
+template <bool F32, int LAYOUT, bool BIAS>
 __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __restrict__ q, const void* __restrict__ k,
                                                               const int32_t* __restrict__ table, int max_blocks,
                                                               const float* __restrict__ bias,
                                                               float2* __restrict__ partials, int H, int R,
-                                                              int64_t n_max, float scale, SeqTable T) {
+                                                              int64_t n_max, float scale, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) float qs[kRowsStage][kHeadDim];
   __shared__ float2 wred[kThreads / 64][kRowsStage];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -159,13 +167,15 @@ __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __rest
   const int tile = local - h * tiles;
   const int key = tile * kThreads + threadIdx.x;
   const int64_t unit = (int64_t)s * H + h;
-  const bool valid = key < n;
+  const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
+                                        : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
+  // keys in the dead slot take no part in the softmax, like keys past n
+  const bool valid = key < n && !(LAYOUT == kSlots && map[T.kofs[i] + key] == dead);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 
   float kr[kHeadDim];
   if (valid)
-    load_key_f32<F32, PAGED>(k, PAGED ? table + (int64_t)s * max_blocks : nullptr, H, h, n_max, unit, T.kofs[i] + key,
-                             kr);
+    load_key_f32<F32, LAYOUT>(k, map, H, h, n_max, unit, T.kofs[i] + key, kr);
   else
 #pragma unroll
     for (int e = 0; e < kHeadDim; ++e) kr[e] = 0.f;
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __rest
       float mx = x;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-      // every wave holds at least one valid key unless the whole wave is past n
+      // every wave holds at least one valid key unless the whole wave is past n (or dead)
       float e = (mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x - mx);
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) e += __shfl_xor(e, off);
@@ -209,34 +219,38 @@ __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __rest
 
 int score_valu_tiles(int n) { return (n + kThreads - 1) / kThreads; }
 
+#define KVC_VALU_DISPATCH_L(KERNEL, F, ...)                                                         \
+  do {                                                                                            \
+    if (layout == kPaged) {                                                                       \
+      if (has_bias) KERNEL<F, kPaged, true><<<grid, block, 0, st>>>(__VA_ARGS__);                 \
+      else KERNEL<F, kPaged, false><<<grid, block, 0, st>>>(__VA_ARGS__);                         \
+    } else if (layout == kSlots) {                                                                \
+      if (has_bias) KERNEL<F, kSlots, true><<<grid, block, 0, st>>>(__VA_ARGS__);                 \
+      else KERNEL<F, kSlots, false><<<grid, block, 0, st>>>(__VA_ARGS__);                         \
+    } else {                                                                                      \
+      if (has_bias) KERNEL<F, kContig, true><<<grid, block, 0, st>>>(__VA_ARGS__);                \
+      else KERNEL<F, kContig, false><<<grid, block, 0, st>>>(__VA_ARGS__);                        \
+    }                                                                                             \
+  } while (0)
 #define KVC_VALU_DISPATCH(KERNEL, ...)                                                            \
   do {                                                                                          \
-    if (f32) {                                                                                  \
-      if (paged) { if (has_bias) KERNEL<true, true, true><<<grid, block, 0, st>>>(__VA_ARGS__);  \
-                   else KERNEL<true, true, false><<<grid, block, 0, st>>>(__VA_ARGS__); }       \
-      else { if (has_bias) KERNEL<true, false, true><<<grid, block, 0, st>>>(__VA_ARGS__);       \
-             else KERNEL<true, false, false><<<grid, block, 0, st>>>(__VA_ARGS__); }            \
-    } else {                                                                                    \
-      if (paged) { if (has_bias) KERNEL<false, true, true><<<grid, block, 0, st>>>(__VA_ARGS__); \
-                   else KERNEL<false, true, false><<<grid, block, 0, st>>>(__VA_ARGS__); }      \
-      else { if (has_bias) KERNEL<false, false, true><<<grid, block, 0, st>>>(__VA_ARGS__);      \
-             else KERNEL<false, false, false><<<grid, block, 0, st>>>(__VA_ARGS__); }           \
-    }                                                                                           \
+    if (f32) KVC_VALU_DISPATCH_L(KERNEL, true, __VA_ARGS__);                                    \
+    else KVC_VALU_DISPATCH_L(KERNEL, false, __VA_ARGS__);                                       \
   } while (0)
 
-hipError_t launch_score_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k, const int32_t* table,
+hipError_t launch_score_valu(bool f32, int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, const SeqTable& T, hipStream_t st) {
+                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(kThreads);
-  KVC_VALU_DISPATCH(score_valu, q, k, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, T);
+  KVC_VALU_DISPATCH(score_valu, q, k, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, dead, T);
   return hipGetLastError();
 }
 
-hipError_t launch_lse_partials_valu(bool f32, bool paged, bool has_bias, const void* q, const void* k,
+hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const void* q, const void* k,
                                     const int32_t* table, int max_blocks, const float* bias, float2* partials, int H,
-                                    int R, int64_t n_max, float scale, const SeqTable& T, hipStream_t st) {
+                                    int R, int64_t n_max, float scale, int dead, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(kThreads);
-  KVC_VALU_DISPATCH(lse_partials_valu, q, k, table, max_blocks, bias, partials, H, R, n_max, scale, T);
+  KVC_VALU_DISPATCH(lse_partials_valu, q, k, table, max_blocks, bias, partials, H, R, n_max, scale, dead, T);
   return hipGetLastError();
 }
 

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert oc.kvc_version() == 100
+    assert oc.kvc_version() == 200
     assert oc.kvc_status_string(0) == "ok"
     assert oc.kvc_status_string(3) == "workspace too small"
     assert oc.kvc_status_string(99) == "unknown status"
@@ -197,3 +197,22 @@ def test_retention_validation(lib):
         A.KVC_ERR_INVALID_ARGUMENT
     assert lib.kvc_compact_side(ctypes.byref(sh), 0, FAKE, m_ok, 100, FAKE, FAKE + 64, None) == \
         A.KVC_ERR_INVALID_ARGUMENT
+
+
+def test_slot_map_validation(lib):
+    """Slot-map key views and the dead-slot redirect reject bad arguments up front."""
+    sh, keep = _shape().c()
+    bad_dead = A.KView(FAKE, A.KVC_BF16, 0, None, 0, FAKE, -2).c()
+    assert lib.kvc_score(ctypes.byref(sh), FAKE, ctypes.byref(bad_dead), FAKE, None, FAKE, None, 0, None) == \
+        A.KVC_ERR_INVALID_ARGUMENT
+    ok_view = A.KView(FAKE, A.KVC_BF16, 0, None, 0, FAKE, 7).c()
+    assert oc.kvc_score_workspace_size(_shape(), A.KView(FAKE, A.KVC_BF16, 0, None, 0, FAKE, 7), True) == 0
+    sh2, keep2 = _shape(S=1, n=(100,), n_max=120).c()
+    sh2.seq_starts = (ctypes.c_int32 * 1)(30)
+    assert lib.kvc_score(ctypes.byref(sh2), FAKE, ctypes.byref(ok_view), FAKE, None, FAKE, None, 0, None) == \
+        A.KVC_ERR_INVALID_ARGUMENT  # the slot map row is n_max long
+    m_ok = (ctypes.c_int32 * 2)(6600, 4000)
+    m_bad = (ctypes.c_int32 * 2)(40000, 4000)
+    assert lib.kvc_evict_redirect(ctypes.byref(sh), FAKE, m_ok, 6600, None, 5, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_evict_redirect(ctypes.byref(sh), FAKE, m_ok, 6600, FAKE, -1, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert lib.kvc_evict_redirect(ctypes.byref(sh), FAKE, m_bad, 40000, FAKE, 5, None) == A.KVC_ERR_INVALID_ARGUMENT
