@@ -12,6 +12,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -51,7 +52,9 @@ def describe(w) -> str:
     if w.seg_len:
         n += f", segment [{w.seg_start}, {w.seg_start + w.seg_len})"
     pol = (", scored by attention mass, kept by LRFU state (ActKV: 90 % action-critical, lambda 0.5)"
-           if w.name == "actkv" else "")
+           if w.name == "actkv" else
+           ", read through a slot map; evicted positions redirected to a dead slot (no data moved)"
+           if w.name == "sentinel" else "")
     return (f"{w.name}: {w.S} seqs x {w.H} KV heads, G={w.G}, q={w.q}, R={w.R}, {n}, d={w.d}, {w.dtype}, "
             f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}{pol}")
 
@@ -82,6 +85,10 @@ def algorithmic_bytes(w, moved_rows=None) -> dict:
     if not w.lse_supplied:
         score += entries * row + rows_q * row  # LSE pass reads K and Q once more
     select = entries * 4 + kept * 4
+    if w.name == "sentinel":  # slot map read by both passes; redirect writes the evicted entries
+        score += entries * 4 * 2
+        return dict(score=score, select=select, compact=kept * 4 + (entries - kept) * 4,
+                    total=score + select + kept * 4 + (entries - kept) * 4)
     if w.name == "actkv":
         select += entries * 12  # LRFU step: mass read, state read and written
         kept_side = kept * 8    # the state carried through compaction (read + write)
@@ -123,8 +130,11 @@ def _oracle_unit(args):
     else:
         sc = O.score_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
         kept = O.select_topm(sc, w.m[s])
-    O.gather(K, kept)
-    O.gather(V, kept)
+    if w.name == "sentinel":  # layout-preserving: redirect the evicted positions, move nothing
+        O.evict_redirect(np.arange(K.shape[0]), kept, K.shape[0], K.shape[0])
+    else:
+        O.gather(K, kept)
+        O.gather(V, kept)
     return time.perf_counter() - t0
 
 
@@ -224,6 +234,10 @@ def main():
     if not args.no_cpu:
         cpu = cpu_baseline(w, args.cpu_seconds)
         log(f"[cpu] oracle baseline {cpu['value']:.4g} tokens/s on {cpu['cores']} cores")
+        # let the worker processes' exit (and the release of their memory) finish before the
+        # GPU is timed: right after a many-core CPU leg some host calls were seen to stall
+        gc.collect()
+        time.sleep(2.0)
 
     import torch
     from online_compaction_amd import _abi as A
@@ -252,13 +266,31 @@ def main():
         del ws
     o = P.allocate(b)
     retention = None
+    if w.name == "sentinel":  # slot pool = the paged pool + one sentinel block; slot map from the table
+        nb = b.k_pool.shape[0]
+        sent = torch.full((1,) + tuple(b.k_pool.shape[1:]), -1.0e4, dtype=b.k_pool.dtype, device="cuda")
+        spool = torch.cat([b.k_pool, sent]).reshape(-1, w.H, w.d)
+        dead = nb * w.block_size
+        pos = torch.arange(w.n_max, device="cuda")
+        base = (b.table[0, (pos // w.block_size).clamp(max=b.max_blocks - 1)].long() * w.block_size
+                + pos % w.block_size).to(torch.int32)
+        smap = base.expand(w.S, w.H, w.n_max).contiguous()
+        pristine = (smap.clone(),)
+        sview = A.KView(spool, b.dtype, 0, None, 0, smap, dead)
+
+        def sentinel_score():
+            A.kvc_score(b.shape, b.q, sview, None, b.bias, o.scores, o.ws)
+
+        def sentinel_redirect():
+            A.kvc_evict_redirect(b.shape, o.kept, b.m, b.m_max, smap, dead)
+        stages = (sentinel_score, lambda: P.run_select(b, o), sentinel_redirect)
     if w.name == "actkv":  # a warm LRFU state: seeded values in [0, 1 / (1 - 2^-0.5))
         st0 = np.random.default_rng(4096).random((w.S, w.H, w.n_max)).astype(np.float32) * 3.41
         retention = P.allocate_retention(b, st0)
         pristine = pristine + (retention.state.clone(),)
         stages = (lambda: P.run_retention_score(b, o, retention), lambda: P.run_retention_select(b, o, retention),
                   lambda: P.run_retention_compact(b, o, retention))
-    else:
+    elif w.name != "sentinel":
         stages = (lambda: P.run_score(b, o), lambda: P.run_select(b, o), lambda: P.run_compact(b, o))
     torch.cuda.synchronize()
     log("[bench] inputs resident on the GPU")
@@ -271,7 +303,9 @@ def main():
         log(f"[bench] calibration copy of {args.calib_copy_mib} MiB done")
 
     def restore():
-        if pristine is not None:
+        if w.name == "sentinel":
+            smap.copy_(pristine[0])
+        elif pristine is not None:
             b.k_pool.copy_(pristine[0])
             b.v_pool.copy_(pristine[1])
             b.table.copy_(pristine[2])
@@ -324,7 +358,7 @@ def main():
         f"compact {avg[2]:.3f} ms; host enqueue {havg[0]:.3f} / {havg[1]:.3f} / {havg[2]:.3f} ms)")
 
     moved = None
-    if w.paged:
+    if w.paged and w.name != "sentinel":
         kept = P.host_array(o.kept)
         moved = 0
         for s in range(w.S):

@@ -328,3 +328,51 @@ def test_actkv_retention_step_full():
     assert np.array_equal(P.host_array(o.freed)[0, :len(freed)], freed)
     assert np.array_equal(P.host_array(b.k_pool), kp) and np.array_equal(P.host_array(b.v_pool), vp)
     say("[ok] actkv: pools, table and freed list bit-exact")
+
+
+def test_sentinel_layout_preserving_full():
+    """The action-token trajectory read through a slot map: scores equal the paged path's bit
+    for bit (same kernels, other addressing); the redirect leaves exactly the kept positions
+    live; rescoring through the redirected map matches the oracle over the kept positions."""
+    import online_compaction_amd as oc
+    P = _P()
+    w = W.spec("sentinel")
+    data = W.build_paged(w, _workers())
+    n, m, B = w.n[0], w.m[0], w.block_size
+    b = P.paged_batch(data["Q"], data["k_pool"], data["v_pool"], data["table"], data["n"], data["m"], w.G,
+                      w.logit_scale, B, n_max=w.n_max, bias=data["bias"])
+    o = P.allocate(b)
+    P.run_score(b, o)
+    torch.cuda.synchronize()
+    paged_scores = P.host_array(o.scores)
+    nb = b.k_pool.shape[0]
+    spool = torch.cat([b.k_pool, torch.full((1,) + tuple(b.k_pool.shape[1:]), -1.0e4, dtype=b.k_pool.dtype,
+                                            device="cuda")]).reshape(-1, w.H, w.d)
+    dead = nb * B
+    pos = np.arange(w.n_max)
+    base = (data["table"][0][np.minimum(pos // B, w.max_blocks - 1)].astype(np.int64) * B + pos % B).astype(np.int32)
+    smap = np.ascontiguousarray(np.broadcast_to(base, (w.S, w.H, w.n_max)))
+    dmap = P.device_tensor(smap)
+    view = oc.KView(spool, oc.KVC_BF16, 0, None, 0, dmap, dead)
+    scores = torch.zeros_like(o.scores)
+    oc.kvc_score(b.shape, b.q, view, None, b.bias, scores, o.ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(P.host_array(scores), paged_scores), "slot-map scores differ from the paged path"
+    P.run_select(b, o)
+    oc.kvc_evict_redirect(b.shape, o.kept, b.m, b.m_max, dmap, dead)
+    oc.kvc_score(b.shape, b.q, view, None, b.bias, scores, o.ws)
+    torch.cuda.synchronize()
+    kept, mp, sc2 = P.host_array(o.kept), P.host_array(dmap), P.host_array(scores)
+    for h in range(w.H):
+        live = np.zeros(n, dtype=bool)
+        live[kept[0, h, :m]] = True
+        want = O.evict_redirect(smap[0, h], kept[0, h, :m], n, dead)
+        assert np.array_equal(mp[0, h], want), f"redirected map h={h}"
+        assert np.all(sc2[0, h, :n][~live] == 0)
+    for h in (0, 7):
+        live = np.zeros(n, dtype=bool)
+        live[kept[0, h, :m]] = True
+        ref = O.score_unit_live(O.unit_rows(data["Q"], 0, h, w.G), O.slot_unit_keys(P.host_array(spool), smap[0, h], n, h),
+                                live, w.dtype, w.logit_scale, data["bias"][0, :n])
+        worst = check_scores(sc2[0, h, :n], ref, f"sentinel rescore h={h}")
+        say(f"[ok] sentinel h={h}: rescore worst rel err {worst:.3g}")

@@ -144,6 +144,13 @@ def spec(name: str, k: int | None = None) -> Workload:
         n = 33000
         return Workload("actkv", 4, 1, 8, 4, 330, 128, (n,), (c4_budget(6),), "bf16", "mixture", "action",
                         paged=True, block_size=16, table="identity", max_blocks=-(-n // 16), bias_tail=0.5)
+    if name == "sentinel":
+        # layout-preserving eviction on the action-token trajectory: the inputs of "c4" (same
+        # seed), read through a per-(layer, head) slot map; the evicted positions of budget 14706
+        # are redirected to a dead slot instead of being compacted
+        n = 33000
+        return Workload("sentinel", 4, 1, 8, 4, 330, 128, (n,), (c4_budget(6),), "bf16", "mixture", "action",
+                        paged=True, block_size=16, table="identity", max_blocks=-(-n // 16), bias_tail=0.5)
     if name == "turn":
         # one 4096-token turn in the middle of a 33000-token trajectory held in 36 layers' paged
         # caches, scored with the 512 queries per query head of the turn that followed it; the
