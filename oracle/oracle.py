@@ -33,6 +33,14 @@ Readings where the pages leave a step open (each is listed with its reason in th
     that holds 90 % of the total attention, the sums taken on the float32 masses quantised to
     multiples of 2^-32 (so that the membership decision is exact on both sides); LRFU's value
     decays by 2^-lambda per policy step and a hit adds 1.
+  * Attention Matching ([TE], design-space section, the AM equations): after the top-m keys
+    K_C are chosen, beta minimises || exp(Q K_C^T + beta) 1 - exp(Q K^T) 1 ||^2 and V_C
+    minimises || A_hat(Q; K_C, beta, V_C) - A(Q; K, V) ||_F^2. The pages name no optimiser;
+    read here as: logits carry the scale c like every other logit, w = exp(beta) >= 0 is fitted
+    by multiplicative non-negative least-squares updates from w = 1 (beta = 0, plain eviction),
+    the exponentials of a unit taken relative to its largest LSE (a common factor that does not
+    move the minimiser); V_C by Landweber iterations from the kept keys' original values with
+    step 1 / (largest column sum of the compacted attention), a fixed number of each.
   * Layout-preserving eviction ([IKV] "IntentKV" page, layout-preserving eviction): evicted
     positions are redirected to one reserved dead slot in a per-position slot map; the page's
     constant sentinel key cannot cancel every query's attention (a query whose components sum
@@ -326,6 +334,64 @@ def score_unit_live(Qs, Ks, live, dtype, scale, bias=None, lse_rows=None, power:
     f = score_unit if power == 2 else mass_unit
     out[live] = f(Qs, Kl, dtype, scale, b, lse_rows)
     return out
+
+
+# ----------------------------------------------------------------------------- Attention Matching
+
+def am_targets(Q, K, V, scale, lse_rows=None):
+    """What AM matches ([TE] AM equations): the partition function of every proxy row over all n
+    keys, relative to the unit's largest LSE, z_i = exp(LSE_i - M), and the attention output
+    Y = softmax(c Q K^T) V. Returns (z, Y, M, LSE)."""
+    if lse_rows is None:
+        lse_rows = lse(Q, K, scale)
+    lse_rows = np.asarray(lse_rows, dtype=np.float64)
+    M = float(lse_rows.max())
+    P = np.exp(logits(Q, K, scale) - lse_rows[:, None])
+    return np.exp(lse_rows - M), P @ np.asarray(V, dtype=np.float64), M, lse_rows
+
+
+def am_design(Q, KC, scale, M):
+    """E_ij = exp(c q_i . k_Cj - M): the kept keys' unnormalised weights, on the same scale as z."""
+    return np.exp(logits(Q, KC, scale) - M)
+
+
+def am_fit_beta(E, z, iters: int):
+    """Non-negative least squares for w = exp(beta) in || E w - z ||^2 by multiplicative updates
+    w <- w * (E^T z) / (E^T E w), from w = 1 (beta = 0). A zero denominator leaves w_j at 0."""
+    E = np.asarray(E, dtype=np.float64)
+    b = E.T @ z
+    w = np.ones(E.shape[1])
+    for _ in range(iters):
+        g = E.T @ (E @ w)
+        w = np.where(g > 0, w * b / np.where(g > 0, g, 1.0), 0.0)
+    return w
+
+
+def am_fit_values(E, w, Y, V0, iters: int):
+    """Least squares for V_C in || P V_C - Y ||_F^2, P the compacted attention (rows of E w-weighted
+    and normalised), by Landweber iterations V <- V - eta P^T (P V - Y) from V_0 (the kept keys'
+    values), eta = 1 / max_j sum_i P_ij (then eta ||P||_2^2 <= 1, so the iteration is stable)."""
+    Ew = np.asarray(E, dtype=np.float64) * np.asarray(w, dtype=np.float64)[None, :]
+    rs = Ew.sum(axis=1)
+    P = np.where(rs[:, None] > 0, Ew / np.where(rs > 0, rs, 1.0)[:, None], 0.0)
+    cmax = P.sum(axis=0).max()
+    eta = 1.0 / cmax if cmax > 0 else 0.0
+    Vc = np.asarray(V0, dtype=np.float64).copy()
+    for _ in range(iters):
+        Vc = Vc - eta * (P.T @ (P @ Vc - Y))
+    return Vc
+
+
+def am_unit(Qs, Ks, Vs, kept, dtype, scale, iters_beta: int, iters_v: int, lse_rows=None):
+    """Attention Matching of one unit from stored rows/keys/values: returns (beta, V_C)."""
+    Q, K, V = widen(Qs, dtype), widen(Ks, dtype), widen(Vs, dtype)
+    kept = np.asarray(kept, dtype=np.int64)
+    z, Y, M, _ = am_targets(Q, K, V, scale, lse_rows)
+    E = am_design(Q, K[kept], scale, M)
+    w = am_fit_beta(E, z, iters_beta)
+    with np.errstate(divide="ignore"):
+        beta = np.log(w)
+    return beta, am_fit_values(E, w, Y, V[kept], iters_v)
 
 
 # ----------------------------------------------------------------------------- whole batches
