@@ -215,6 +215,39 @@ kvc_status kvc_evict_redirect(const kvc_shape* shape, const int32_t* kept, const
                               int32_t* slot_map, int32_t dead_slot, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * kvc_am_fit -- Attention Matching on top of a Token Eviction selection ([TE], design-space
+ * section, the AM equations): for the kept keys K_C of every unit, an additive logit bias beta
+ * with  min || exp(Q K_C^T + beta) 1_m - exp(Q K^T) 1_n ||^2  and compact values V_C with
+ * min || softmax(Q K_C^T + beta) V_C - softmax(Q K^T) V ||_F^2  (logits carry `scale`, no bias).
+ * The pages name no optimiser; this library uses, with w = exp(beta):
+ *   beta: iters_beta multiplicative non-negative least-squares updates
+ *         w <- w * (E^T z) / (E^T E w) from w = 1 (beta = 0, plain eviction), where
+ *         E_ij = exp(l_ij) over the kept keys and z_i = exp(LSE_i); internally both carry
+ *         their own constant factor (E its largest kept logit, z its largest LSE, moved to within
+ *         80 of the former) so float32 holds them -- the updates are scale-equivariant, so the
+ *         iterates are unchanged; w_j = 0 gives beta_j = -inf;
+ *   V_C:  iters_v Landweber steps V <- V - eta P^T (P V - Y) from the kept keys' stored values,
+ *         P = the compacted attention softmax(Q K_C^T + beta), Y = softmax(Q K^T) V, and
+ *         eta = 1 / max_j sum_i P_ij (stable: eta ||P||_2^2 <= 1).
+ * Everything is float32 on the GPU (the QK^T products on bf16 MFMA with float32 accumulation).
+ *   q          device [S][H*G][q][d] bf16;  G * q >= 16 (else KVC_ERR_UNSUPPORTED)
+ *   k, v       key and value views, bf16, both contiguous or both paged (no slot maps)
+ *   lse        device [S][H*G][q] LSE over the n_s keys, or NULL to compute it (in ws)
+ *   kept       device [S][H][m_max] int32, strictly ascending, < n_s (as from select)
+ *   m, m_max   host budgets [S] and the row stride of kept / beta / v_c
+ *   beta       device out [S][H][m_max] float32 (natural-log bias per kept key)
+ *   v_c        device out [S][H][m_max][d] float32
+ *   ws         device workspace of kvc_am_workspace_size(shape, k, v, m, lse != NULL) bytes:
+ *              about 4 * H * R * (m_s + n_s + 2d) bytes per sequence (the kept and the full
+ *              exponentials are materialised)
+ * ------------------------------------------------------------------------------------------- */
+size_t kvc_am_workspace_size(const kvc_shape* shape, const kvc_kv_view* k, const kvc_kv_view* v, const int32_t* m,
+                             int lse_supplied);
+kvc_status kvc_am_fit(const kvc_shape* shape, const void* q, const kvc_kv_view* k, const kvc_kv_view* v,
+                      const float* lse, const int32_t* kept, const int32_t* m, int32_t m_max, int32_t iters_beta,
+                      int32_t iters_v, float* beta, float* v_c, void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * kvc_lrfu_update -- one step of ActKV's retention state ([ACT], paragraph on action-critical
  * entries: the attention of all action tokens on each entry is tallied, entries within the top
  * 90 % are action-critical, and LRFU -- with "hit by action attention" as its hit signal and a

@@ -9,6 +9,8 @@ from ._abi import (  # noqa: F401
     KvcError,
     KView,
     Shape,
+    kvc_am_fit,
+    kvc_am_workspace_size,
     kvc_attention_mass,
     kvc_compact_contig,
     kvc_compact_paged,

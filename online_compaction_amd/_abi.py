@@ -52,6 +52,13 @@ _SIGS = {
     "kvc_attention_mass": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView),
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]),
+    "kvc_am_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(_Shape), ctypes.POINTER(_KView), ctypes.POINTER(_KView),
+                                                ctypes.POINTER(ctypes.c_int32), ctypes.c_int]),
+    "kvc_am_fit": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView),
+                                  ctypes.POINTER(_KView), ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]),
     "kvc_evict_redirect": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32),
                                           ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p]),
     "kvc_lrfu_update": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.c_double, ctypes.c_float,
@@ -236,6 +243,33 @@ def kvc_attention_mass(shape: Shape, q, k: KView, lse, bias, mass, ws=None, stre
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().kvc_attention_mass(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), _ptr(lse), _ptr(bias),
                                      _ptr(mass), _ptr(ws), ws_bytes, _stream(stream)), "kvc_attention_mass")
+
+
+def kvc_am_workspace_size(shape: Shape, k: KView, v: KView, m, lse_supplied: bool) -> int:
+    sh, _keep = shape.c()
+    kv, vv = k.c(), v.c()
+    marr, mp = _host_i32(m)
+    return int(load().kvc_am_workspace_size(ctypes.byref(sh), ctypes.byref(kv), ctypes.byref(vv), mp,
+                                            int(bool(lse_supplied))))
+
+
+def kvc_am_fit(shape: Shape, q, k: KView, v: KView, lse, kept, m, m_max: int, iters_beta: int, iters_v: int,
+               beta, v_c, ws, stream=None) -> None:
+    S, H, HG, R = shape.num_seqs, shape.num_kv_heads, shape.num_kv_heads * shape.group, shape.num_queries
+    _need(q, S * HG * R * shape.head_dim * 2, "q")
+    _check_kview(shape, k)
+    _check_kview(shape, v)
+    _need(lse, S * HG * R * 4, "lse")
+    _need(kept, S * H * m_max * 4, "kept")
+    _need(beta, S * H * m_max * 4, "beta")
+    _need(v_c, S * H * m_max * shape.head_dim * 4, "v_c")
+    sh, _keep = shape.c()
+    kv, vv = k.c(), v.c()
+    marr, mp = _host_i32(m)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load().kvc_am_fit(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), ctypes.byref(vv), _ptr(lse), _ptr(kept),
+                             mp, int(m_max), int(iters_beta), int(iters_v), _ptr(beta), _ptr(v_c), _ptr(ws),
+                             ws_bytes, _stream(stream)), "kvc_am_fit")
 
 
 def kvc_evict_redirect(shape: Shape, kept, m, m_max: int, slot_map, dead_slot: int, stream=None) -> None:

@@ -12,7 +12,7 @@
 #include "kvc_internal.h"
 
 namespace kvc {
-// kernel launchers (score_mfma.hip, lse_mfma.hip, score_valu.hip, select.hip, retain.hip, compact.hip)
+// kernel launchers (score_mfma.hip, lse_mfma.hip, score_valu.hip, select.hip, retain.hip, compact.hip, am.hip)
 int score_mfma_tiles(int n);
 int lse_mfma_row_blocks(int R);
 int score_valu_tiles(int n);
@@ -35,6 +35,30 @@ hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const v
 hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
                                  const SeqTable& T, hipStream_t st);
 int redirect_tiles(int n);
+int am_exp_items(int R, int cols);
+int am_scale_items(int R, int m);
+hipError_t launch_am_stats(const float* lse, float* ws, int H, int R, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_scale(float* ws, int H, int R, const SeqTable& T, hipStream_t st);
+int am_row_items(int R);
+int am_dot_row_items(int R);
+int am_col_items(int m);
+int am_key_tiles(int m);
+hipError_t launch_am_exp(int layout, bool all, const void* q, const void* k, const int32_t* table, int max_blocks,
+                         const int32_t* kept, int m_max, const float* lse, float* ws, int H, int R, int64_t n_max,
+                         float scale, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_rows_dot(const float* w, float* ws, int H, int R, int m_max, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_cols_dot(int mode, float* w, const float* lse, float* ws, int H, int R, int m_max,
+                              const SeqTable& T, hipStream_t st);
+hipError_t launch_am_eta(float* ws, int H, int R, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_rows_mm(int layout, int src, const void* v, const int32_t* table, int max_blocks, const float* w,
+                             const float* vc, float* ws, int H, int R, int64_t n_max, int m_max, const SeqTable& T,
+                             hipStream_t st);
+hipError_t launch_am_cols_mm(const float* w, float* vc, float* ws, int H, int R, int m_max, const SeqTable& T,
+                             hipStream_t st);
+hipError_t launch_am_init(int layout, const void* v, const int32_t* table, int max_blocks, const int32_t* kept,
+                          float* w, float* vc, const float* ws, int H, int R, int64_t n_max, int m_max,
+                          const SeqTable& T, hipStream_t st);
+hipError_t launch_am_finish(float* w, const float* ws, int H, int R, int m_max, const SeqTable& T, hipStream_t st);
 hipError_t launch_select(const float* scores, int32_t* kept, int H, int64_t n_max, int m_max, const SeqTable& T,
                          hipStream_t st);
 hipError_t launch_lrfu_update(const float* mass, float* state, int32_t* counts, int H, int64_t n_max, double top_p,
@@ -429,6 +453,114 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
                                      static_cast<hipStream_t>(stream));
       });
   if (err != hipSuccess) return hip_fail(err, "redirect kernel");
+  return ok();
+}
+
+// ------------------------------------------------------------------------------------------------
+// Attention Matching
+// ------------------------------------------------------------------------------------------------
+static int64_t am_seq_floats(const kvc_shape* sh, int s, const int32_t* m) {
+  const int64_t H = sh->num_kv_heads, R = (int64_t)sh->group * sh->num_queries;
+  return H * (R * ((int64_t)m[s] + sh->seq_lens[s] + 2 * kHeadDim + 1) + m[s] + 4);
+}
+
+static size_t am_bytes(const kvc_shape* sh, const int32_t* m) {
+  int64_t f = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(sh, s, m);
+  return ((size_t)f * sizeof(float) + 255) & ~size_t(255);
+}
+
+static kvc_status check_am(const kvc_shape* sh, const kvc_kv_view* k, const kvc_kv_view* v) {
+  if (kvc_status st = check_view(sh, k)) return st;
+  if (kvc_status st = check_view(sh, v)) return st;
+  if (k->slot_map || v->slot_map) return fail(KVC_ERR_UNSUPPORTED, "attention matching: slot-map views");
+  if (k->dtype != KVC_BF16 || v->dtype != KVC_BF16) return fail(KVC_ERR_UNSUPPORTED, "attention matching: bf16 only");
+  if (!use_mfma(sh, k))
+    return fail(KVC_ERR_UNSUPPORTED, "attention matching needs G * q >= %d proxy rows", kMfmaMinRows);
+  if (k->block_size != v->block_size) return fail(KVC_ERR_INVALID_ARGUMENT, "K and V views differ in layout");
+  return KVC_OK;
+}
+
+size_t kvc_am_workspace_size(const kvc_shape* sh, const kvc_kv_view* k, const kvc_kv_view* v, const int32_t* m,
+                             int lse_supplied) {
+  if (check_shape(sh) != KVC_OK || check_am(sh, k, v) != KVC_OK || !m) return 0;
+  for (int s = 0; s < sh->num_seqs; ++s)
+    if (m[s] < 0 || m[s] > sh->seq_lens[s]) return 0;
+  const size_t lse_part = lse_supplied ? 0 : partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  return lse_part + am_bytes(sh, m);
+}
+
+kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const kvc_kv_view* v,
+                      const float* lse, const int32_t* kept, const int32_t* m, int32_t m_max, int32_t iters_beta,
+                      int32_t iters_v, float* beta, float* v_c, void* ws, size_t ws_bytes, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_am(sh, k, v)) return st;
+  if (kvc_status st = check_budgets(sh, m, m_max)) return st;
+  if (!q || !kept || !beta || !v_c) return fail(KVC_ERR_INVALID_ARGUMENT, "q, kept, beta and v_c must be non-NULL");
+  if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
+  if (iters_beta < 0 || iters_beta > 100000 || iters_v < 0 || iters_v > 100000)
+    return fail(KVC_ERR_INVALID_ARGUMENT, "iteration counts must lie in [0, 100000]");
+  const size_t lse_part = lse ? 0 : partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  const size_t need = lse_part + am_bytes(sh, m);
+  if (!ws || ws_bytes < need)
+    return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "attention matching needs %zu workspace bytes, got %zu", need,
+                ws ? ws_bytes : 0);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const float* lse_rows = lse;
+  if (!lse) {
+    float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + partials_bytes(sh, lse_kchunk(sh, k)));
+    if (kvc_status s2 = run_lse(sh, q, k, nullptr, lse_ws, ws, st)) return s2;
+    lse_rows = lse_ws;
+  }
+  float* amws = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_part);
+  std::vector<int64_t> off(sh->num_seqs);
+  int64_t acc = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    off[s] = acc;
+    acc += am_seq_floats(sh, s, m);
+  }
+  auto offset = [&](int s) -> int64_t { return off[s]; };
+  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
+  const int layout = layout_of(k);
+  const int64_t nm = sh->n_max;
+  auto run = [&](auto&& items, auto&& body) -> hipError_t { return for_each_chunk(sh, m, items, offset, body); };
+  auto cols = [&](int s) { return H * am_col_items(m[s]); };
+#define KVC_AM_STEP(ITEMS, CALL)                                          \
+  do {                                                                    \
+    const hipError_t e_ = run(ITEMS, [&](const SeqTable& T) { return CALL; }); \
+    if (e_ != hipSuccess) return hip_fail(e_, "attention matching kernel");  \
+  } while (0)
+  auto units = [&](int) { return H; };
+  KVC_AM_STEP(units, launch_am_stats(lse_rows, amws, H, R, T, st));
+  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, m[s]); },
+              launch_am_exp(layout, false, q, k->data, k->block_table, k->max_blocks, kept, m_max, lse_rows, amws, H,
+                            R, nm, sh->scale, T, st));
+  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, sh->seq_lens[s]); },
+              launch_am_exp(layout, true, q, k->data, k->block_table, k->max_blocks, kept, m_max, lse_rows, amws, H,
+                            R, nm, sh->scale, T, st));
+  KVC_AM_STEP([&](int s) { return H * am_scale_items(R, m[s]); }, launch_am_scale(amws, H, R, T, st));
+  KVC_AM_STEP(cols, launch_am_cols_dot(0, beta, lse_rows, amws, H, R, m_max, T, st));
+  KVC_AM_STEP(cols, launch_am_init(layout, v->data, v->block_table, v->max_blocks, kept, beta, v_c, amws, H, R, nm,
+                                   m_max, T, st));
+  auto rows = [&](int) { return H * am_dot_row_items(R); };
+  for (int it = 0; it < iters_beta; ++it) {
+    KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, H, R, m_max, T, st));
+    KVC_AM_STEP(cols, launch_am_cols_dot(1, beta, lse_rows, amws, H, R, m_max, T, st));
+  }
+  KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, H, R, m_max, T, st));
+  KVC_AM_STEP(cols, launch_am_cols_dot(2, beta, lse_rows, amws, H, R, m_max, T, st));
+  KVC_AM_STEP(units, launch_am_eta(amws, H, R, T, st));
+  auto rtiles = [&](int) { return H * am_row_items(R); };
+  KVC_AM_STEP(rtiles, launch_am_rows_mm(layout, 0, v->data, v->block_table, v->max_blocks, beta, v_c, amws, H, R, nm,
+                                        m_max, T, st));
+  auto ktiles = [&](int s) { return H * am_key_tiles(m[s]); };
+  for (int it = 0; it < iters_v; ++it) {
+    KVC_AM_STEP(rtiles, launch_am_rows_mm(layout, 1, v->data, v->block_table, v->max_blocks, beta, v_c, amws, H, R,
+                                          nm, m_max, T, st));
+    KVC_AM_STEP(ktiles, launch_am_cols_mm(beta, v_c, amws, H, R, m_max, T, st));
+  }
+  KVC_AM_STEP(cols, launch_am_finish(beta, amws, H, R, m_max, T, st));
+#undef KVC_AM_STEP
   return ok();
 }
 

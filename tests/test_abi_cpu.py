@@ -216,3 +216,27 @@ def test_slot_map_validation(lib):
     assert lib.kvc_evict_redirect(ctypes.byref(sh), FAKE, m_ok, 6600, None, 5, None) == A.KVC_ERR_INVALID_ARGUMENT
     assert lib.kvc_evict_redirect(ctypes.byref(sh), FAKE, m_ok, 6600, FAKE, -1, None) == A.KVC_ERR_INVALID_ARGUMENT
     assert lib.kvc_evict_redirect(ctypes.byref(sh), FAKE, m_bad, 40000, FAKE, 5, None) == A.KVC_ERR_INVALID_ARGUMENT
+
+
+def test_attention_matching_validation(lib):
+    """kvc_am_fit rejects unsupported views, budgets and iteration counts up front."""
+    sh = _shape()
+    kv = A.KView(FAKE, A.KVC_BF16)
+    m = [6600, 4000]
+    assert oc.kvc_am_workspace_size(sh, kv, kv, m, True) > 4 * 8 * 4096 * (6600 + 33000)
+    assert oc.kvc_am_workspace_size(sh, kv, kv, m, False) > oc.kvc_am_workspace_size(sh, kv, kv, m, True)
+    assert oc.kvc_am_workspace_size(sh, A.KView(FAKE, A.KVC_F32), kv, m, True) == 0
+    assert oc.kvc_am_workspace_size(_shape(G=1, q=8), kv, kv, m, True) == 0  # too few rows for MFMA
+    s, keep = sh.c()
+    k_, v_ = kv.c(), kv.c()
+    mp = (ctypes.c_int32 * 2)(6600, 4000)
+    f = lib.kvc_am_fit
+    assert f(ctypes.byref(s), FAKE, ctypes.byref(k_), ctypes.byref(v_), FAKE, FAKE, mp, 6600, -1, 5, FAKE, FAKE, FAKE,
+             1 << 40, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(s), FAKE, ctypes.byref(k_), ctypes.byref(v_), FAKE, FAKE, mp, 6600, 5, 5, None, FAKE, FAKE,
+             1 << 40, None) == A.KVC_ERR_INVALID_ARGUMENT
+    assert f(ctypes.byref(s), FAKE, ctypes.byref(k_), ctypes.byref(v_), FAKE, FAKE, mp, 6600, 5, 5, FAKE, FAKE, FAKE,
+             16, None) == A.KVC_ERR_WORKSPACE_TOO_SMALL
+    sl = A.KView(FAKE, A.KVC_BF16, 0, None, 0, FAKE, 3).c()
+    assert f(ctypes.byref(s), FAKE, ctypes.byref(sl), ctypes.byref(v_), FAKE, FAKE, mp, 6600, 5, 5, FAKE, FAKE, FAKE,
+             1 << 40, None) == A.KVC_ERR_UNSUPPORTED

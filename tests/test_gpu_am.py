@@ -1,0 +1,152 @@
+"""GPU parity of Attention Matching (beta by multiplicative NNLS updates, V_C by Landweber steps)
+against the float64 oracle running the same iterations."""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import oracle as O
+from tests.parity import say
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _P():
+    from online_compaction_amd import path as P
+    return P
+
+
+def _run(w, data, kept, m, iters_beta, iters_v, lse=None):
+    P = _P()
+    import online_compaction_amd as oc
+    if w.paged:
+        kv = oc.KView(P.device_tensor(data["k_pool"]), oc.KVC_BF16, w.block_size, P.device_tensor(data["table"]),
+                      w.max_blocks)
+        vv = oc.KView(P.device_tensor(data["v_pool"]), oc.KVC_BF16, w.block_size, kv.block_table, w.max_blocks)
+    else:
+        kv = oc.KView(P.device_tensor(data["K"]), oc.KVC_BF16)
+        vv = oc.KView(P.device_tensor(data["V"]), oc.KVC_BF16)
+    shape = oc.Shape(w.S, w.H, w.G, w.q, w.d, w.n_max, np.array(w.n, dtype=np.int32), w.logit_scale)
+    m_max = int(max(m))
+    beta = torch.full((w.S, w.H, m_max), 7.0, dtype=torch.float32, device="cuda")
+    vc = torch.full((w.S, w.H, m_max, w.d), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, oc.kvc_am_workspace_size(shape, kv, vv, m, lse is not None)), dtype=torch.uint8,
+                     device="cuda")
+    dl = None if lse is None else P.device_tensor(lse)
+    oc.kvc_am_fit(shape, P.device_tensor(data["Q"]), kv, vv, dl, P.device_tensor(kept), m, m_max, iters_beta, iters_v,
+                  beta, vc, ws)
+    torch.cuda.synchronize()
+    return beta.cpu().numpy(), vc.cpu().numpy()
+
+
+def _keys_values(w, data, s, h):
+    n = w.n[s]
+    if w.paged:
+        return (O.paged_unit_keys(data["k_pool"], data["table"][s], n, h, w.block_size),
+                O.paged_unit_keys(data["v_pool"], data["table"][s], n, h, w.block_size))
+    return data["K"][s, h, :n], data["V"][s, h, :n]
+
+
+def _rownorm(E, w):
+    Ew = E * w[None, :]
+    rs = Ew.sum(axis=1)
+    return np.where(rs[:, None] > 0, Ew / np.where(rs > 0, rs, 1.0)[:, None], 0.0)
+
+
+def _check(w, data, kept, m, beta, vc, iters_beta, iters_v, lse=None, tag=""):
+    """AM's parameters are only determined where the proxy rows see them: a key that only rows
+    with a negligible partition function attend to can take almost any bias. Parity is therefore
+    checked on what the fit determines -- the objective, the fitted partition functions and the
+    compacted attention output of the rows that carry weight, and beta / V_C of the keys with
+    real support -- each against the oracle running the same iterations in float64 (within
+    2e-3), and every finite bias within 1e-2 (the float32 iterations drift a little along the
+    fit's poorly determined directions)."""
+    worst = {"obj": 0.0, "fit": 0.0, "out": 0.0, "beta": 0.0, "vc": 0.0}
+    for s in range(w.S):
+        for h in range(w.H):
+            t = f"{tag} s={s} h={h}"
+            K, V = _keys_values(w, data, s, h)
+            rows = O.unit_rows(data["Q"], s, h, w.G)
+            lr = None if lse is None else lse[s, h * w.G:(h + 1) * w.G].reshape(-1).astype(np.float64)
+            k_s = kept[s, h, :m[s]]
+            rb, rv = O.am_unit(rows, K, V, k_s, w.dtype, w.logit_scale, iters_beta, iters_v, lr)
+            gb, gv = beta[s, h, :m[s]].astype(np.float64), vc[s, h, :m[s]].astype(np.float64)
+            assert np.all(np.isfinite(gv)) and not np.any(np.isnan(gb)), f"{t}: non-finite output"
+            Q64, K64, V64 = O.widen(rows, w.dtype), O.widen(K, w.dtype), O.widen(V, w.dtype)
+            z, Y, M, _ = O.am_targets(Q64, K64, V64, w.logit_scale, lr)
+            E = O.am_design(Q64, K64[k_s], w.logit_scale, M)
+            wg, wr = np.exp(gb), np.exp(rb)
+            og, orf = np.linalg.norm(E @ wg - z), np.linalg.norm(E @ wr - z)
+            d_obj = abs(og - orf) / max(orf, 1e-300)
+            assert d_obj <= 1e-3 or abs(og - orf) <= 2e-5 * np.linalg.norm(z), f"{t}: objective {og:.6g} vs {orf:.6g}"
+            heavy = z >= 1e-3 * z.max()
+            fit_g, fit_r = (E @ wg)[heavy] / z[heavy], (E @ wr)[heavy] / z[heavy]
+            d_fit = float(np.max(np.abs(fit_g - fit_r)))
+            assert d_fit <= 2e-3, f"{t}: fitted partition functions differ by {d_fit:.3g}"
+            Pg, Pr = _rownorm(E, wg), _rownorm(E, wr)
+            outg, outr = Pg @ gv, Pr @ rv
+            d_out = float(np.max(np.abs(outg[heavy] - outr[heavy]) / (1.0 + np.abs(outr[heavy]))))
+            assert d_out <= 2e-3, f"{t}: compacted attention outputs differ by {d_out:.3g}"
+            supp_b = (E.T @ z) >= 1e-2 * (E.T @ z).max()
+            d_beta = float(np.max(np.abs(gb[supp_b] - rb[supp_b]))) if supp_b.any() else 0.0
+            assert d_beta <= 2e-3, f"{t}: beta of supported keys differs by {d_beta:.3g}"
+            supp_v = Pr[heavy].sum(axis=0) >= 1e-2 * Pr[heavy].sum(axis=0).max()
+            d_vc = float(np.max(np.abs(gv[supp_v] - rv[supp_v]) / (1.0 + np.abs(rv[supp_v])))) if supp_v.any() else 0.0
+            assert d_vc <= 2e-3, f"{t}: V_C of supported keys differs by {d_vc:.3g}"
+            fin = np.isfinite(rb)
+            d_all = float(np.max(np.abs(gb[fin] - rb[fin]))) if fin.any() else 0.0
+            assert np.array_equal(np.isfinite(gb), fin) and d_all <= 1e-2, f"{t}: beta differs by {d_all:.3g}"
+            assert og <= np.linalg.norm(E @ np.ones_like(wr) - z) * (1 + 1e-6) + 2e-5 * np.linalg.norm(z), \
+                f"{t}: the fit made things worse"
+            for key, val in (("obj", d_obj), ("fit", d_fit), ("out", d_out), ("beta", d_beta), ("vc", d_vc)):
+                worst[key] = max(worst[key], val)
+            assert np.all(beta[s, h, m[s]:] == 7.0) and np.all(vc[s, h, m[s]:] == 7.0), "rows past m_s untouched"
+    say(f"[ok] am {tag}: worst " + ", ".join(f"{k} {v:.3g}" for k, v in worst.items()))
+
+
+def _kept(rng, w, m):
+    kept = np.zeros((w.S, w.H, max(m)), dtype=np.int32)
+    for s in range(w.S):
+        for h in range(w.H):
+            kept[s, h, :m[s]] = np.sort(rng.choice(w.n[s], size=m[s], replace=False))
+    return kept
+
+
+@pytest.mark.parametrize("layout", ["contiguous", "paged"])
+def test_am_small_matches_oracle(layout):
+    w = W.custom(f"am_{layout}", 170, S=2, H=2, G=4, q=8, n=(300, 129), dtype="bf16", keys="mixture",
+                 queries="cluster", paged=layout == "paged", table="permuted", block_size=16)
+    data = W.build_paged(w) if w.paged else W.build_contiguous(w)
+    m = [60, 40]
+    kept = _kept(np.random.default_rng(3), w, m)
+    say(f"[case] am {layout}: n={list(w.n)} m={m} R={w.R}")
+    beta, vc = _run(w, data, kept, m, 8, 8)
+    _check(w, data, kept, m, beta, vc, 8, 8, tag=layout)
+
+
+def test_am_zero_iterations_is_plain_eviction():
+    w = W.custom("am_zero", 171, S=1, H=2, G=4, q=4, n=(200,), dtype="bf16", keys="mixture", queries="cluster")
+    data = W.build_contiguous(w)
+    m = [50]
+    kept = _kept(np.random.default_rng(4), w, m)
+    beta, vc = _run(w, data, kept, m, 0, 0)
+    # w = 1 is held as exp(ME - Mz) in scaled units: beta = 0 up to one float32 exp/log round trip
+    assert np.all(np.abs(beta[:, :, :50]) <= 1e-4)
+    for h in range(w.H):
+        assert np.array_equal(vc[0, h, :50], W.bf16_bits_to_f32(data["V"][0, h, kept[0, h, :50]]))
+
+
+def test_am_supplied_lse_and_many_tiles():
+    """2048 proxy rows (32 row tiles), 4096 keys, 819 kept (13 key tiles), 16 + 16 iterations,
+    LSE supplied by the oracle."""
+    w = W.custom("am_big", 172, S=1, H=2, G=4, q=512, n=(4096,), dtype="bf16", keys="mixture", queries="cluster")
+    data = W.build_contiguous(w)
+    m = [819]
+    kept = _kept(np.random.default_rng(5), w, m)
+    lse = np.zeros((w.S, w.H * w.G, w.q), dtype=np.float32)
+    for h in range(w.H):
+        L = O.lse_unit(O.unit_rows(data["Q"], 0, h, w.G), data["K"][0, h, :w.n[0]], w.dtype, w.logit_scale)
+        lse[0, h * w.G:(h + 1) * w.G] = L.astype(np.float32).reshape(w.G, w.q)
+    say(f"[case] am big: R={w.R} n={w.n[0]} m={m[0]}")
+    beta, vc = _run(w, data, kept, m, 16, 16, lse)
+    _check(w, data, kept, m, beta, vc, 16, 16, lse, tag="big")
