@@ -28,6 +28,7 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
 # the score kernel's source: its own file and the headers it includes
 SCORE_SRCS = [os.path.join(ROOT, "online_compaction_amd", "csrc", f)
@@ -54,7 +55,8 @@ def describe(w) -> str:
     pol = (", scored by attention mass, kept by LRFU state (ActKV: 90 % action-critical, lambda 0.5)"
            if w.name == "actkv" else
            ", read through a slot map; evicted positions redirected to a dead slot (no data moved)"
-           if w.name == "sentinel" else "")
+           if w.name == "sentinel" else
+           ", then beta and V_C fitted for the kept keys by Attention Matching" if w.name == "am" else "")
     return (f"{w.name}: {w.S} seqs x {w.H} KV heads, G={w.G}, q={w.q}, R={w.R}, {n}, d={w.d}, {w.dtype}, "
             f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}{pol}")
 
@@ -99,7 +101,11 @@ def algorithmic_bytes(w, moved_rows=None) -> dict:
         compact = kept * 4 + moved * 2 * row * 2 + kept_side
     else:
         compact = kept * 4 + kept * 2 * row * 2 + kept_side
-    return dict(score=score, select=select, compact=compact, total=score + select + compact)
+    out = dict(score=score, select=select, compact=compact, total=score + select + compact)
+    if w.name == "am":  # the fit reads Q, every key and value, the kept indices; writes beta and V_C
+        out["am_fit"] = rows_q * row + entries * 2 * row + kept * 4 + kept * 4 * (1 + w.d)
+        out["total"] += out["am_fit"]
+    return out
 
 
 def score_flops(w) -> float:
@@ -107,10 +113,23 @@ def score_flops(w) -> float:
     return float(passes) * 2.0 * w.R * w.d * sum(scored_lens(w)) * w.H
 
 
+def am_flops(w, iters_beta: int, iters_v: int) -> dict:
+    """Multiply-add work of one Attention Matching fit, split by the MFMA type that does it:
+    bf16 for the logits (kept keys; every key, twice when the LSE is computed), float32 for
+    Y = P V and the Landweber steps (two R x m x d products each); the bias updates are
+    matrix-vector products (counted with the float32 work)."""
+    bf16 = f32 = 0.0
+    for s in range(w.S):
+        n, m, R, d = w.n[s], w.m[s], w.R, w.d
+        bf16 += 2.0 * R * d * (m + n * (1 if w.lse_supplied else 2))
+        f32 += 2.0 * R * n * d + iters_v * 4.0 * R * m * d + (iters_beta + 1) * 4.0 * R * m
+    return {"bf16": bf16 * w.H, "f32": f32 * w.H}
+
+
 # ---------------------------------------------------------------------------------- CPU baseline
 
 def _oracle_unit(args):
-    w, s, h, bias_row = args
+    w, s, h, bias_row, am_iters = args
     from oracle import oracle as O
     from workloads import unit_keys, unit_queries, unit_values
     K = unit_keys(w, s, h)
@@ -130,6 +149,8 @@ def _oracle_unit(args):
     else:
         sc = O.score_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
         kept = O.select_topm(sc, w.m[s])
+    if w.name == "am":  # Attention Matching fit of the kept keys (K_C is their gather)
+        O.am_unit(Qr, K, V, kept, w.dtype, w.logit_scale, am_iters[0], am_iters[1], lse_rows)
     if w.name == "sentinel":  # layout-preserving: redirect the evicted positions, move nothing
         O.evict_redirect(np.arange(K.shape[0]), kept, K.shape[0], K.shape[0])
     else:
@@ -138,7 +159,19 @@ def _oracle_unit(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline(w, budget_s: float) -> dict:
+def _oracle_steps(w, am_iters) -> str:
+    lse = "supplied LSE" if w.lse_supplied else "computed LSE"
+    if w.name == "actkv":
+        return f"attention mass ({lse}) + action-critical set + LRFU step + top-m + gather"
+    if w.name == "sentinel":
+        return f"score ({lse}) + top-m + dead-slot redirect"
+    if w.name == "am":
+        return (f"score ({lse}) + top-m + gather + Attention Matching ({am_iters[0]} bias updates, "
+                f"{am_iters[1]} value steps)")
+    return f"score ({lse}) + top-m + gather"
+
+
+def cpu_baseline(w, budget_s: float, am_iters=(0, 0)) -> dict:
     from concurrent.futures import ProcessPoolExecutor
     import multiprocessing as mp
     try:
@@ -151,7 +184,7 @@ def cpu_baseline(w, budget_s: float) -> dict:
     ctx = mp.get_context("fork")
     if threadpool_limits:
         threadpool_limits(1)
-    t_first = _oracle_unit((w, 0, 0, W.bias_row(w, 0)))
+    t_first = _oracle_unit((w, 0, 0, W.bias_row(w, 0), am_iters))
     per_wave = max(1, int(budget_s / max(t_first, 1e-3)))
     rng = np.random.default_rng(0)
     if len(units) > 1:
@@ -163,7 +196,7 @@ def cpu_baseline(w, budget_s: float) -> dict:
     log(f"[cpu] oracle: first unit {t_first:.2f} s; timing {count} more units on {cores} processes")
     t0 = time.perf_counter()
     with ProcessPoolExecutor(max_workers=cores, mp_context=ctx) as ex:
-        busy = list(ex.map(_oracle_unit, [(w, s, h, W.bias_row(w, s)) for s, h in pick]))
+        busy = list(ex.map(_oracle_unit, [(w, s, h, W.bias_row(w, s), am_iters) for s, h in pick]))
     wall = time.perf_counter() - t0
     # units of one workload cost about the same, so a step takes units / count times the sample
     step_s = wall * len(units) / count
@@ -177,8 +210,8 @@ def cpu_baseline(w, budget_s: float) -> dict:
     except OSError:
         pass
     return {"value": trajectory_tokens(w) / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{count} of {len(units)} (layer, KV head) units, float64 NumPy oracle score (supplied "
-                       f"LSE) + top-m + gather, one unit per process with 1 BLAS thread; "
+            "sample": (f"{count} of {len(units)} (sequence or layer, KV head) units, float64 NumPy oracle "
+                       f"{_oracle_steps(w, am_iters)}, one unit per process with 1 BLAS thread; "
                        f"wall {wall:.1f} s (busy {sum(busy):.1f} s) scaled by {len(units)}/{count}"),
             "cpu_model": model}
 
@@ -214,6 +247,8 @@ def main():
     ap.add_argument("--k", type=int, default=6, help="budget index for the paged action-token workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="approximate CPU baseline budget")
+    ap.add_argument("--am-iters", type=int, nargs=2, default=(32, 32), metavar=("BETA", "V"),
+                    help="Attention Matching: multiplicative bias updates and Landweber value steps")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -232,7 +267,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, args.cpu_seconds)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.am_iters)
         log(f"[cpu] oracle baseline {cpu['value']:.4g} tokens/s on {cpu['cores']} cores")
         # let the worker processes' exit (and the release of their memory) finish before the
         # GPU is timed: right after a many-core CPU leg some host calls were seen to stall
@@ -292,6 +327,13 @@ def main():
                   lambda: P.run_retention_compact(b, o, retention))
     elif w.name != "sentinel":
         stages = (lambda: P.run_score(b, o), lambda: P.run_select(b, o), lambda: P.run_compact(b, o))
+    names = ("score", "select", "redirect" if w.name == "sentinel" else "compact")
+    matching = None
+    if w.name == "am":  # the fit reads the pool before a paged compaction would rewrite it
+        matching = P.allocate_matching(b, *args.am_iters)
+        stages = stages[:2] + (lambda: P.run_matching(b, o, matching),) + stages[2:]
+        names = ("score", "select", "am_fit", "compact")
+    ns = len(stages)
     torch.cuda.synchronize()
     log("[bench] inputs resident on the GPU")
 
@@ -319,14 +361,14 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    stage_ms = np.zeros((args.steps, 3))
-    host_ms = np.zeros((args.steps, 3))  # time the host spends enqueueing each stage
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(ns + 1)] for _ in range(args.steps)]
+    stage_ms = np.zeros((args.steps, ns))
+    host_ms = np.zeros((args.steps, ns))  # time the host spends enqueueing each stage
 
     def timed_step(i):
         e = ev[i]
         e[0].record()
-        for k in range(3):
+        for k in range(ns):
             h0 = time.perf_counter()
             stages[k]()
             host_ms[i, k] = (time.perf_counter() - h0) * 1e3
@@ -350,12 +392,14 @@ def main():
             wall += time.perf_counter() - t0
     for i in range(args.steps):
         e = ev[i]
-        stage_ms[i] = [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+        stage_ms[i] = [e[k].elapsed_time(e[k + 1]) for k in range(ns)]
     ms_step = wall * 1e3 / args.steps
     avg = stage_ms.mean(axis=0)
     havg = host_ms.mean(axis=0)
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (score {avg[0]:.3f}, select {avg[1]:.3f}, "
-        f"compact {avg[2]:.3f} ms; host enqueue {havg[0]:.3f} / {havg[1]:.3f} / {havg[2]:.3f} ms)")
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step ("
+        + ", ".join(f"{nm} {t:.3f}" for nm, t in zip(names, avg)) + " ms; host enqueue "
+        + " / ".join(f"{t:.3f}" for t in havg) + " ms)")
+    st = dict(zip(names, avg))
 
     moved = None
     if w.paged and w.name != "sentinel":
@@ -374,6 +418,26 @@ def main():
     achieved_tf = flops / score_s / 1e12
     step_s = ms_step * 1e-3
     traffic = traffic_from_profile(score_s) if (w.name == "c3") else None
+    roof = {
+        "kernel": "score_mfma (kvc_attention_mass)" if w.name == "actkv" else "score_mfma (kvc_score)",
+        "bound": "mfma",
+        "achieved": achieved_tf,
+        "peak": MFMA_BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": achieved_tf / MFMA_BF16_PEAK_TFLOPS,
+        "traffic": traffic,
+        "flops_per_launch": flops,
+        "launch_ms": avg[0],
+    }
+    if w.name == "am":  # the fit dominates: its kernels against the mixed bf16 / float32 MFMA peak
+        af = am_flops(w, *args.am_iters)
+        fit_s = st["am_fit"] * 1e-3
+        at_peak = af["bf16"] / (MFMA_BF16_PEAK_TFLOPS * 1e12) + af["f32"] / (MFMA_F32_PEAK_TFLOPS * 1e12)
+        tot = af["bf16"] + af["f32"]
+        roof = {"kernel": "kvc_am_fit (all of its kernels)", "bound": "mfma", "achieved": tot / fit_s / 1e12,
+                "peak": tot / at_peak / 1e12, "unit": "TFLOP/s", "frac": at_peak / fit_s, "traffic": None,
+                "flops_per_launch": af, "launch_ms": st["am_fit"],
+                "iters": {"beta": args.am_iters[0], "v": args.am_iters[1]}}
     line = {
         "metric": "compacted KV tokens/sec (score+select+compact) and % of peak HBM GB/s, 1 GPU",
         "value": tokens / step_s,
@@ -392,24 +456,14 @@ def main():
             "tokens_per_step": tokens,
             "kv_entries_per_step": int(sum(scored_lens(w)) * w.H),
             "entries_per_s": sum(scored_lens(w)) * w.H / step_s,
-            "stage_ms": {"score": avg[0], "select": avg[1], "compact": avg[2]},
+            "stage_ms": st,
             "hbm_algorithmic_bytes_per_step": ab["total"],
             "hbm_algorithmic_gbps": ab["total"] / step_s / 1e9,
             "hbm_frac_of_peak": ab["total"] / step_s / 1e9 / HBM_PEAK_GBPS,
-            "select_compact_hbm_gbps": (ab["select"] + ab["compact"]) / ((avg[1] + avg[2]) * 1e-3) / 1e9,
+            "select_compact_hbm_gbps": (ab["select"] + ab["compact"]) / ((st["select"] + st[names[-1]]) * 1e-3) / 1e9,
             "mfma_util": achieved_tf / MFMA_BF16_PEAK_TFLOPS,
         },
-        "roofline": {
-            "kernel": "score_mfma (kvc_attention_mass)" if w.name == "actkv" else "score_mfma (kvc_score)",
-            "bound": "mfma",
-            "achieved": achieved_tf,
-            "peak": MFMA_BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": achieved_tf / MFMA_BF16_PEAK_TFLOPS,
-            "traffic": traffic,
-            "flops_per_launch": flops,
-            "launch_ms": avg[0],
-        },
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -4,48 +4,69 @@
 // and compact values V_C with
 //   min_V_C || A_hat(Q; K_C, beta, V_C) - A(Q; K, V) ||_F^2.
 // With w = exp(beta) the first is non-negative least squares in w; the second, with
-// P = diag(1 / (E w)) E diag(w) the compacted attention, is least squares in V_C.
+// P_C = diag(1 / (E w)) E diag(w) the compacted attention, is least squares in V_C.
 //
 // Per unit the kernels materialise E_ij = exp(c q_i . k_Cj - ME) (ME the largest kept logit) and,
 // for the target A(Q; K, V) = P_full V, P_full_ij = exp(c q_i . k_j - LSE_i) over all n keys, then
 // iterate:
 //   beta: w' <- w' * (E^T z) / (E^T E w') (multiplicative NNLS updates), z_i = exp(LSE_i - Mz);
-//   V_C:  V <- V - eta P^T (P V - Y) from the kept keys' values (Landweber), eta = 1 / max_j sum_i P_ij.
+//   V_C:  V <- V - eta P_C^T (P_C V - Y) from the kept keys' values (Landweber),
+//         eta = 1 / max_j sum_i (P_C)_ij.
 // E and z carry separate factors so that neither underflows in float32 (Mz = the largest LSE,
 // lowered to ME + 80 if the kept logits lie far below it). The updates are scale-equivariant:
 // with w' = exp(ME - Mz) w they are the updates of w = exp(beta) from w = 1 on the unscaled
-// exponentials, so w' starts at exp(ME - Mz) and beta = log w' - (ME - Mz).
+// exponentials, so w' starts at exp(ME - Mz) and beta = log w' - (ME - Mz). Once beta is fixed,
+// E is overwritten in place by P_C, which the value iterations then multiply from both sides.
 // The QK^T products use v_mfma_f32_16x16x32_bf16 on the stored bf16 rows; the solver products
-// use v_mfma_f32_16x16x4_f32 (float32 throughout); the vector products are plain VALU.
+// use v_mfma_f32_16x16x4_f32 (float32 throughout); the vector products are plain VALU. Every
+// reduction has a fixed order (split sums land in partial buffers that one pass adds up in
+// order), so a fit is reproducible bit for bit.
 //
-// Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], n = T.n[i]):
-//   E [H][R][m] | P [H][R][n] | Y [H][R][128] | Tm [H][R][128] | u [H][R] | b [H][m] |
+// Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], n = T.n[i],
+// ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 the split counts of the two value
+// products; every array starts on a 256-byte boundary):
+//   E [H][R][ldm] | P [H][R][n] | Y [H][R][128] | Z [H][R][128] | Zp [S1 > 1 ? S1 : 0][H][R][128] |
+//   Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] | u [H][R] | b [H][ldm] |
 //   Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H]
+// Columns m .. ldm-1 of E hold zeros (logit -inf), so tiles never need a column bound on E.
 #include "mfma_common.h"
 
 namespace kvc {
 
 using namespace mfma;
 
+struct AmCfg {
+  int H, R, m_max, S1, S2;
+};
+
 namespace {
 
 constexpr int kD = kHeadDim;
+constexpr int kRowChunk = 64;  // rows per partial column sum
+
+__host__ __device__ constexpr int64_t pad64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
 struct AmWs {
-  float *E, *P, *Y, *Tm, *u, *b, *M, *eta, *ME;
+  float *E, *P, *Y, *Z, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
   uint32_t* mekey;
+  int ldm;
 };
 
-__device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, int H, int R) {
-  const int64_t m = T.m[i], n = T.n[i];
+__device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const AmCfg& C) {
+  const int64_t m = T.m[i], n = T.n[i], H = C.H, R = C.R;
+  const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
   AmWs w;
+  w.ldm = (int)ldm;
   w.E = ws + T.off[i];
-  w.P = w.E + (int64_t)H * R * m;
-  w.Y = w.P + (int64_t)H * R * n;
-  w.Tm = w.Y + (int64_t)H * R * kD;
-  w.u = w.Tm + (int64_t)H * R * kD;
-  w.b = w.u + (int64_t)H * R;
-  w.M = w.b + (int64_t)H * m;
+  w.P = w.E + pad64(H * R * ldm);
+  w.Y = w.P + pad64(H * R * n);
+  w.Z = w.Y + pad64(H * R * kD);
+  w.Zp = w.Z + pad64(H * R * kD);
+  w.Up = w.Zp + (C.S1 > 1 ? C.S1 : 0) * pad64(H * R * kD);
+  w.part = w.Up + (C.S2 > 1 ? C.S2 : 0) * pad64(H * ldm * kD);
+  w.u = w.part + pad64(H * nr * ldm);
+  w.b = w.u + pad64(H * R);
+  w.M = w.b + pad64(H * ldm);
   w.eta = w.M + H;
   w.ME = w.eta + H;
   w.mekey = reinterpret_cast<uint32_t*>(w.ME + H);
@@ -67,22 +88,35 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 }  // namespace
 
+// Floats of one sequence's workspace (the layout above).
+int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2) {
+  const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
+  const int64_t rk = pad64((int64_t)H * R * kD);
+  return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * R * n) + 2 * rk + (S1 > 1 ? S1 : 0) * rk +
+         (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) + pad64((int64_t)H * R) +
+         pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H);
+}
+
 // ------------------------------------------------------------------------------------------------
-// Logit tiles of 64 rows x 64 keys: into E the raw kept logits c q_i . k_Cj (ALL = false; their
-// maximum goes to an atomic per unit, and am_scale turns them into exponentials), into P the
-// weights exp(c q_i . k_j - LSE_i) over every key (ALL = true). Work item = (seq, head, row tile,
-// key tile), key tile fastest. Both operands come straight from global memory (L2-resident).
+// Logit tiles of 64 rows x 64 keys: into E the raw kept logits c q_i . k_Cj (ALL = false; -inf in
+// the padding columns; their maximum goes to an atomic per unit, and am_scale turns them into
+// exponentials), into P the weights exp(c q_i . k_j - LSE_i) over every key (ALL = true). Work
+// item = (seq, head, row tile, key tile), key tile fastest. Both operands come straight from
+// global memory (L2-resident).
 // ------------------------------------------------------------------------------------------------
 template <int LAYOUT, bool ALL>
 __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const int32_t* __restrict__ table, int max_blocks,
-                                                   const int32_t* __restrict__ kept, int m_max,
-                                                   const float* __restrict__ lse, float* __restrict__ ws, int H,
-                                                   int R, int64_t n_max, float scale, SeqTable T) {
+                                                   const int32_t* __restrict__ kept, const float* __restrict__ lse,
+                                                   float* __restrict__ ws, int64_t n_max, float scale, AmCfg C,
+                                                   SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int n = T.n[i], m = T.m[i];
+  const int H = C.H, R = C.R;
+  AmWs W = am_ws(ws, T, i, C);
   const int cols = ALL ? n : m;
+  const int ld = ALL ? n : W.ldm;
   const int s = T.first + i;
   const int rt_n = (R + 63) / 64, ct_n = (cols + 63) / 64;
   int local = t - T.start[i];
@@ -91,7 +125,6 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
   const int rt = local / ct_n, ct = local - rt * ct_n;
   const int64_t unit = (int64_t)s * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  AmWs W = am_ws(ws, T, i, H, R);
   const float* lu = lse + unit * R;
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
@@ -101,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
   const uint16_t* qrow = q + (unit * R + min(row, R - 1)) * (int64_t)kD;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8(reinterpret_cast<const u32x4*>(qrow)[4 * ks + g]);
-  float* out = (ALL ? W.P : W.E) + ((int64_t)h * R) * cols;
-  const int32_t* ku = kept + unit * m_max;
+  float* out = (ALL ? W.P : W.E) + ((int64_t)h * R) * ld;
+  const int32_t* ku = kept + unit * C.m_max;
   float lmax = -INFINITY;
 #pragma unroll 1
   for (int sub = 0; sub < 4; ++sub) {
@@ -115,13 +148,15 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int orow = rt * 64 + wave * 16 + 4 * g + e;
-      if (orow < R && col < cols) {
+      if (orow < R && col < ld) {
         const float l = acc[e] * scale;
         if constexpr (ALL) {
-          out[(int64_t)orow * cols + col] = __builtin_amdgcn_exp2f((l - lu[orow]) * kLog2e);
-        } else {
-          out[(int64_t)orow * cols + col] = l;
+          out[(int64_t)orow * ld + col] = __builtin_amdgcn_exp2f((l - lu[orow]) * kLog2e);
+        } else if (col < m) {
+          out[(int64_t)orow * ld + col] = l;
           lmax = fmaxf(lmax, l);
+        } else {
+          out[(int64_t)orow * ld + col] = -INFINITY;
         }
       }
     }
@@ -134,15 +169,15 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
 }
 
 // Per unit, before am_exp: Mz = max_i LSE_i, and the kept-logit maximum reset. Work item = (seq, head).
-__global__ __launch_bounds__(64) void am_stats(const float* __restrict__ lse, float* __restrict__ ws, int H, int R,
+__global__ __launch_bounds__(64) void am_stats(const float* __restrict__ lse, float* __restrict__ ws, AmCfg C,
                                                SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int s = T.first + i, h = t - T.start[i];
-  AmWs W = am_ws(ws, T, i, H, R);
-  const float* lu = lse + ((int64_t)s * H + h) * R;
+  AmWs W = am_ws(ws, T, i, C);
+  const float* lu = lse + ((int64_t)s * C.H + h) * C.R;
   float mx = -INFINITY;
-  for (int r = threadIdx.x; r < R; r += 64) mx = fmaxf(mx, lu[r]);
+  for (int r = threadIdx.x; r < C.R; r += 64) mx = fmaxf(mx, lu[r]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if (threadIdx.x == 0) {
@@ -153,16 +188,15 @@ __global__ __launch_bounds__(64) void am_stats(const float* __restrict__ lse, fl
 
 // E <- exp(E - ME), ME the unit's largest kept logit; Mz lowered to ME + 80 when the kept keys
 // lie far below the largest LSE (so that exp(ME - Mz), the start of w', stays in range).
-// Work item = (seq, head, 256 x 16 elements).
-__global__ __launch_bounds__(256) void am_scale(float* __restrict__ ws, int H, int R, SeqTable T) {
+// Work item = (seq, head, 4096 elements).
+__global__ __launch_bounds__(256) void am_scale(float* __restrict__ ws, AmCfg C, SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
-  const int m = T.m[i];
-  const int64_t per = (int64_t)R * m;
+  AmWs W = am_ws(ws, T, i, C);
+  const int64_t per = (int64_t)C.R * W.ldm;
   const int nb = (int)((per + 4095) / 4096);
   const int local = t - T.start[i];
   const int h = local / nb, blk = local - h * nb;
-  AmWs W = am_ws(ws, T, i, H, R);
   const float me = key_float(W.mekey[h]);
   if (blk == 0 && threadIdx.x == 0) {
     W.ME[h] = me;
@@ -176,20 +210,21 @@ __global__ __launch_bounds__(256) void am_scale(float* __restrict__ ws, int H, i
 // ------------------------------------------------------------------------------------------------
 // u = E w per row (one wave per row). Work item = (seq, head, 4 rows).
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void am_rows_dot(const float* __restrict__ w_all, float* __restrict__ ws, int H,
-                                                   int R, int m_max, SeqTable T) {
+__global__ __launch_bounds__(256) void am_rows_dot(const float* __restrict__ w_all, float* __restrict__ ws, AmCfg C,
+                                                   SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
+  const int R = C.R;
   const int rb = (R + 3) / 4;
   const int local = t - T.start[i];
   const int h = local / rb;
   const int r = (local - h * rb) * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (r >= R) return;
-  AmWs W = am_ws(ws, T, i, H, R);
-  const float* e = W.E + ((int64_t)h * R + r) * m;
-  const float* w = w_all + ((int64_t)s * H + h) * m_max;
+  AmWs W = am_ws(ws, T, i, C);
+  const float* e = W.E + ((int64_t)h * R + r) * W.ldm;
+  const float* w = w_all + ((int64_t)s * C.H + h) * C.m_max;
   float acc = 0.0f;
   for (int j = lane; j < m; j += 64) acc = __builtin_fmaf(e[j], w[j], acc);
 #pragma unroll
@@ -198,53 +233,88 @@ __global__ __launch_bounds__(256) void am_rows_dot(const float* __restrict__ w_a
 }
 
 // ------------------------------------------------------------------------------------------------
-// Column products g_j = sum_i E_ij r_i (one thread per column, rows in order), with
-//   MODE 0: r_i = exp(LSE_i - M)       -> b_j = g_j                      (E^T z, once)
-//   MODE 1: r_i = u_i = (E w)_i        -> w_j <- w_j b_j / g_j, 0 if g_j = 0  (one NNLS step)
-//   MODE 2: r_i = 1 / u_i              -> b_j = w_j g_j (column sums of P, for the step size)
-// Work item = (seq, head, 256 columns).
+// Column products g_j = sum_i E_ij r_i in two passes: partial sums over chunks of 64 rows (one
+// thread per column, rows in order), then the chunks added in order per column. With
+//   MODE 0: r_i = exp(LSE_i - M)       -> b_j = g_j                          (E^T z, once)
+//   MODE 1: r_i = u_i = (E w)_i        -> w_j <- w_j b_j / g_j, 0 if g_j = 0 (one NNLS step)
+//   MODE 2: r_i = 1 / u_i              -> E_ij <- E_ij w_j / u_i in place (E becomes P_C) and
+//                                         b_j = sum_i (P_C)_ij (column sums, for the step size)
+// Partial work item = (seq, head, 256 columns, 64-row chunk); final = (seq, head, 256 columns).
 // ------------------------------------------------------------------------------------------------
 template <int MODE>
-__global__ __launch_bounds__(256) void am_cols_dot(float* __restrict__ w_all, const float* __restrict__ lse,
-                                                   float* __restrict__ ws, int H, int R, int m_max, SeqTable T) {
+__global__ __launch_bounds__(256) void am_cols_part(const float* __restrict__ w_all, const float* __restrict__ lse,
+                                                    float* __restrict__ ws, AmCfg C, SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
-  const int cb = (m + 255) / 256;
-  const int local = t - T.start[i];
-  const int h = local / cb;
-  const int j = (local - h * cb) * 256 + threadIdx.x;
-  if (j >= m) return;
-  const int64_t unit = (int64_t)s * H + h;
-  AmWs W = am_ws(ws, T, i, H, R);
-  const float* e = W.E + (int64_t)h * R * m + j;
+  const int R = C.R;
+  AmWs W = am_ws(ws, T, i, C);
+  const int ldm = W.ldm;
+  const int cb_n = (ldm + 255) / 256, nr = (R + kRowChunk - 1) / kRowChunk;
+  int local = t - T.start[i];
+  const int rc = local % nr;
+  local /= nr;
+  const int cb = local % cb_n, h = local / cb_n;
+  const int j = cb * 256 + threadIdx.x;
+  if (j >= ldm) return;
+  const int64_t unit = (int64_t)s * C.H + h;
+  float* e = W.E + (int64_t)h * R * ldm + j;
   const float* u = W.u + (int64_t)h * R;
   const float* lu = lse + unit * R;
   const float M = W.M[h];
+  const float wj = (MODE == 2 && j < m) ? w_all[unit * C.m_max + j] : 0.0f;
+  const int r0 = rc * kRowChunk, r1 = min(R, r0 + kRowChunk);
   float acc = 0.0f;
-  for (int r = 0; r < R; ++r) {
-    float rv;
-    if constexpr (MODE == 0) rv = __builtin_amdgcn_exp2f((lu[r] - M) * kLog2e);
-    else if constexpr (MODE == 1) rv = u[r];
-    else rv = u[r] > 0.0f ? 1.0f / u[r] : 0.0f;
-    acc = __builtin_fmaf(e[(int64_t)r * m], rv, acc);
+  for (int r = r0; r < r1; ++r) {
+    const float x = e[(int64_t)r * ldm];
+    if constexpr (MODE == 0) {
+      acc = __builtin_fmaf(x, __builtin_amdgcn_exp2f((lu[r] - M) * kLog2e), acc);
+    } else if constexpr (MODE == 1) {
+      acc = __builtin_fmaf(x, u[r], acc);
+    } else {
+      const float pc = u[r] > 0.0f ? x * wj / u[r] : 0.0f;
+      if (j < m) e[(int64_t)r * ldm] = pc;
+      acc += pc;
+    }
   }
-  float* w = w_all + unit * m_max;
-  if constexpr (MODE == 0) W.b[(int64_t)h * m + j] = acc;
-  else if constexpr (MODE == 1) w[j] = acc > 0.0f ? w[j] * W.b[(int64_t)h * m + j] / acc : 0.0f;
-  else W.b[(int64_t)h * m + j] = w[j] * acc;
+  W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
 }
 
-// eta = 1 / max_j (column sums of P) per unit (0 when every column is empty). Work item = (seq, head).
-__global__ __launch_bounds__(256) void am_eta(float* __restrict__ ws, int H, int R, SeqTable T) {
+template <int MODE>
+__global__ __launch_bounds__(256) void am_cols_fin(float* __restrict__ w_all, float* __restrict__ ws, AmCfg C,
+                                                   SeqTable T) {
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int m = T.m[i], s = T.first + i;
+  AmWs W = am_ws(ws, T, i, C);
+  const int ldm = W.ldm;
+  const int cb_n = (m + 255) / 256, nr = (C.R + kRowChunk - 1) / kRowChunk;
+  const int local = t - T.start[i];
+  const int h = local / cb_n;
+  const int j = (local - h * cb_n) * 256 + threadIdx.x;
+  if (j >= m) return;
+  const float* p = W.part + (int64_t)h * nr * ldm + j;
+  float g = 0.0f;
+  for (int rc = 0; rc < nr; ++rc) g += p[(int64_t)rc * ldm];
+  float* b = W.b + (int64_t)h * ldm + j;
+  if constexpr (MODE == 1) {
+    float* w = w_all + ((int64_t)s * C.H + h) * C.m_max + j;
+    *w = g > 0.0f ? *w * *b / g : 0.0f;
+  } else {
+    *b = g;
+  }
+}
+
+// eta = 1 / max_j (column sums of P_C) per unit (0 when every column is empty). Work item = (seq, head).
+__global__ __launch_bounds__(256) void am_eta(float* __restrict__ ws, AmCfg C, SeqTable T) {
   __shared__ float red[4];
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int m = T.m[i];
   const int h = t - T.start[i];
-  AmWs W = am_ws(ws, T, i, H, R);
+  AmWs W = am_ws(ws, T, i, C);
   float mx = 0.0f;
-  for (int j = threadIdx.x; j < m; j += 256) mx = fmaxf(mx, W.b[(int64_t)h * m + j]);
+  for (int j = threadIdx.x; j < m; j += 256) mx = fmaxf(mx, W.b[(int64_t)h * W.ldm + j]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
@@ -256,62 +326,50 @@ __global__ __launch_bounds__(256) void am_eta(float* __restrict__ ws, int H, int
 }
 
 // ------------------------------------------------------------------------------------------------
-// Row products out_i = sum_j A_ij B_j (128-wide rows), float32 MFMA, 64 rows x 128 per workgroup:
-//   SRC 0: A = P (all n keys), B_j = V row of key j (bf16, through the view) -> Y
-//   SRC 1: A = E (kept keys),  B_j = w_j * Vc_j (float32)                   -> Tm
-// Work item = (seq, head, 64-row tile). LDS stages 16 columns of A and B at a time.
+// Target Y = P V (all n keys, V rows bf16 through the view), float32 MFMA, 64 rows x 128 per
+// workgroup. Work item = (seq, head, 64-row tile). LDS stages 16 columns of P and V at a time.
 // ------------------------------------------------------------------------------------------------
-template <int LAYOUT, int SRC>
-__global__ __launch_bounds__(256) void am_rows_mm(const uint16_t* __restrict__ v, const int32_t* __restrict__ table,
-                                                  int max_blocks, const float* __restrict__ w_all,
-                                                  const float* __restrict__ vc_all, float* __restrict__ ws, int H,
-                                                  int R, int64_t n_max, int m_max, SeqTable T) {
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void am_target(const uint16_t* __restrict__ v, const int32_t* __restrict__ table,
+                                                 int max_blocks, float* __restrict__ ws, int64_t n_max, AmCfg C,
+                                                 SeqTable T) {
   __shared__ float As[64][17];
   __shared__ float Bs[16][kD];
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
-  const int n = T.n[i], m = T.m[i], s = T.first + i;
-  const int cols = SRC == 0 ? n : m;
+  const int n = T.n[i], s = T.first + i;
+  const int H = C.H, R = C.R;
   const int rt_n = (R + 63) / 64;
   const int local = t - T.start[i];
   const int h = local / rt_n, rt = local - h * rt_n;
   const int64_t unit = (int64_t)s * H + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  AmWs W = am_ws(ws, T, i, H, R);
-  const float* A = (SRC == 0 ? W.P : W.E) + (int64_t)h * R * cols;
+  AmWs W = am_ws(ws, T, i, C);
+  const float* A = W.P + (int64_t)h * R * n;
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
-  const float* w = w_all + unit * m_max;
-  const float* vc = vc_all + unit * m_max * (int64_t)kD;
 
   f32x4 acc[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll 1
-  for (int c0 = 0; c0 < cols; c0 += 16) {
-    // stage A[64 rows][16 cols] and B[16 cols][128]
+  for (int c0 = 0; c0 < n; c0 += 16) {
     for (int x = tid; x < 64 * 16; x += 256) {
       const int rr = x >> 4, cc = x & 15;
       const int r = rt * 64 + rr, c = c0 + cc;
-      As[rr][cc] = (r < R && c < cols) ? A[(int64_t)r * cols + c] : 0.0f;
+      As[rr][cc] = (r < R && c < n) ? A[(int64_t)r * n + c] : 0.0f;
     }
     for (int x = tid; x < 16 * (kD / 8); x += 256) {
       const int cc = x / (kD / 8), ch = x % (kD / 8);  // 8 elements per item
       const int c = c0 + cc;
       float vals[8];
-      if (c < cols) {
-        if constexpr (SRC == 0) {
-          const u32x4 raw = key_row<LAYOUT>(v, map, H, h, n_max, unit, T.kofs[i] + c)[ch];
-          const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+      if (c < n) {
+        const u32x4 raw = key_row<LAYOUT>(v, map, H, h, n_max, unit, T.kofs[i] + c)[ch];
+        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            vals[2 * e] = bf16_lo(wd[e]);
-            vals[2 * e + 1] = bf16_hi(wd[e]);
-          }
-        } else {
-          const float wj = w[c];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) vals[e] = wj * vc[(int64_t)c * kD + ch * 8 + e];
+        for (int e = 0; e < 4; ++e) {
+          vals[2 * e] = bf16_lo(wd[e]);
+          vals[2 * e + 1] = bf16_hi(wd[e]);
         }
       } else {
 #pragma unroll
@@ -329,7 +387,7 @@ __global__ __launch_bounds__(256) void am_rows_mm(const uint16_t* __restrict__ v
     }
     __syncthreads();
   }
-  float* out = (SRC == 0 ? W.Y : W.Tm) + (int64_t)h * R * kD;
+  float* out = W.Y + (int64_t)h * R * kD;
 #pragma unroll
   for (int b = 0; b < 8; ++b)
 #pragma unroll
@@ -340,67 +398,191 @@ __global__ __launch_bounds__(256) void am_rows_mm(const uint16_t* __restrict__ v
 }
 
 // ------------------------------------------------------------------------------------------------
-// One Landweber step for 64 kept keys: with Z_i = Tm_i / u_i - Y_i (the residual of P Vc),
-// U_j = sum_i (E_ij / u_i) Z_i, then Vc_j -= eta w_j U_j (P^T = diag(w) E^T diag(1/u)).
-// float32 MFMA on LDS-staged E^T and Z. Work item = (seq, head, 64-key tile).
+// The two products of a Landweber step, float32 MFMA, one 64 x 128 output tile per workgroup
+// (each wave 16 x 128, eight 16 x 16 accumulators), the contraction in stages of 32 through
+// double-buffered LDS with the next stage's global loads in flight during the current stage's
+// MFMAs, and split over S workgroups whose partial tiles a second pass adds in order:
+//   KIND 0: Z = P_C Vc - Y          (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
+//   KIND 1: Vc -= eta P_C^T Z        (columns of P_C, contraction over rows)    -> Vc, or partials Up
+// Within a stage, MFMA step e takes contraction index 4e + g from lane group g on both operands.
+// LDS row pitches (36, 80 and 144 floats) put the 64 lanes of every operand read on distinct
+// banks and keep 16-byte stores aligned.
+// Work item = (seq, head, output tile, split), split fastest.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void am_cols_mm(const float* __restrict__ w_all, float* __restrict__ vc_all,
-                                                  float* __restrict__ ws, int H, int R, int m_max, SeqTable T) {
-  __shared__ float Ats[64][17];
-  __shared__ float Zs[16][kD];
-  const int t = blockIdx.x;
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
+                                                  SeqTable T) {
+  constexpr int LA = KIND == 0 ? 36 : 80;
+  constexpr int ASZ = KIND == 0 ? 64 * 36 : 32 * 80;
+  constexpr int LB = 144;
+  __shared__ __attribute__((aligned(16))) float As[2][ASZ];
+  __shared__ __attribute__((aligned(16))) float Bs[2][32 * LB];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
-  const int kt_n = (m + 63) / 64;
-  const int local = t - T.start[i];
-  const int h = local / kt_n, kt = local - h * kt_n;
-  const int64_t unit = (int64_t)s * H + h;
+  const int R = C.R;
+  AmWs W = am_ws(ws, T, i, C);
+  const int ldm = W.ldm;
+  const int S = KIND == 0 ? C.S1 : C.S2;
+  const int tiles = KIND == 0 ? (R + 63) / 64 : ldm / 64;
+  int local = t - T.start[i];
+  const int sp = local % S;
+  local /= S;
+  const int tile = local % tiles, h = local / tiles;
+  const int64_t unit = (int64_t)s * C.H + h;
+  const float* PC = W.E + (int64_t)h * R * ldm;
+  const float* vc = vc_all + unit * C.m_max * (int64_t)kD;
+  const float* Zh = W.Z + (int64_t)h * R * kD;
+  const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
+  const int per = (nst + S - 1) / S;
+  const int st0 = sp * per, st1 = min(nst, st0 + per);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  AmWs W = am_ws(ws, T, i, H, R);
-  const float* E = W.E + (int64_t)h * R * m;
-  const float* Y = W.Y + (int64_t)h * R * kD;
-  const float* Tm = W.Tm + (int64_t)h * R * kD;
-  const float* u = W.u + (int64_t)h * R;
+
+  float4 ra[2], rb[4];
+  auto load = [&](int stg) {
+    const int k0 = stg * 32;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = tid + 256 * c;
+      if constexpr (KIND == 0) {  // A = P_C[64 rows][32 keys]
+        const int row = idx >> 3, c4 = idx & 7, r = tile * 64 + row;
+        ra[c] = r < R ? *reinterpret_cast<const float4*>(PC + (int64_t)r * ldm + k0 + 4 * c4)
+                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      } else {  // A^T = P_C[32 rows][64 keys]
+        const int row = idx >> 4, c4 = idx & 15, r = k0 + row;
+        ra[c] = r < R ? *reinterpret_cast<const float4*>(PC + (int64_t)r * ldm + tile * 64 + 4 * c4)
+                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = tid + 256 * c;
+      const int row = idx >> 5, c4 = idx & 31, kk = k0 + row;
+      if constexpr (KIND == 0)  // B = Vc[32 keys][128]
+        rb[c] = kk < m ? *reinterpret_cast<const float4*>(vc + (int64_t)kk * kD + 4 * c4)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      else  // B = Z[32 rows][128]
+        rb[c] = kk < R ? *reinterpret_cast<const float4*>(Zh + (int64_t)kk * kD + 4 * c4)
+                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int idx = tid + 256 * c;
+      const int off = KIND == 0 ? (idx >> 3) * LA + 4 * (idx & 7) : (idx >> 4) * LA + 4 * (idx & 15);
+      *reinterpret_cast<float4*>(&As[buf][off]) = ra[c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int idx = tid + 256 * c;
+      *reinterpret_cast<float4*>(&Bs[buf][(idx >> 5) * LB + 4 * (idx & 31)]) = rb[c];
+    }
+  };
 
   f32x4 acc[8];
 #pragma unroll
   for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (st0 < st1) {
+    load(st0);
+    store(0);
+    __syncthreads();
 #pragma unroll 1
-  for (int r0 = 0; r0 < R; r0 += 16) {
-    for (int x = tid; x < 16 * 64; x += 256) {  // E[16 rows][64 keys] / u_row -> transposed
-      const int rr = x >> 6, jj = x & 63;
-      const int r = r0 + rr, j = kt * 64 + jj;
-      Ats[jj][rr] = (r < R && j < m && u[r] > 0.0f) ? E[(int64_t)r * m + j] / u[r] : 0.0f;
-    }
-    for (int x = tid; x < 16 * kD; x += 256) {
-      const int rr = x / kD, dd = x % kD;
-      const int r = r0 + rr;
-      float z = 0.0f;
-      if (r < R) {
-        const float ur = u[r];
-        z = ur > 0.0f ? Tm[(int64_t)r * kD + dd] / ur - Y[(int64_t)r * kD + dd] : 0.0f;
+    for (int stg = st0; stg < st1; ++stg) {
+      const int buf = (stg - st0) & 1;
+      const bool more = stg + 1 < st1;
+      if (more) load(stg + 1);
+      const float* as = As[buf];
+      const float* bs = Bs[buf];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = 4 * e + g;
+        const float a = KIND == 0 ? as[(16 * wave + c16) * LA + kk] : as[kk * LA + 16 * wave + c16];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[b] = mfma_f32(a, bs[kk * LB + 16 * b + c16], acc[b]);
       }
-      Zs[rr][dd] = z;
+      if (more) store(buf ^ 1);
+      __syncthreads();
     }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float a = Ats[wave * 16 + c16][kk * 4 + g];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) acc[b] = mfma_f32(a, Zs[kk * 4 + g][b * 16 + c16], acc[b]);
-    }
-    __syncthreads();
   }
-  const float eta = W.eta[h];
-  const float* w = w_all + unit * m_max;
-  float* vc = vc_all + unit * m_max * (int64_t)kD;
+
+  if constexpr (KIND == 0) {
+    const int64_t hofs = (int64_t)h * R * kD;
+    float* out = (S == 1 ? W.Z : W.Zp + (int64_t)sp * pad64((int64_t)C.H * R * kD)) + hofs;
+    const float* y = W.Y + hofs;
 #pragma unroll
-  for (int b = 0; b < 8; ++b)
+    for (int b = 0; b < 8; ++b)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int j = kt * 64 + wave * 16 + 4 * g + e;
-      if (j < m) vc[(int64_t)j * kD + b * 16 + c16] -= eta * w[j] * acc[b][e];
+      for (int e = 0; e < 4; ++e) {
+        const int r = tile * 64 + 16 * wave + 4 * g + e;
+        const int64_t o = (int64_t)r * kD + 16 * b + c16;
+        if (r < R) out[o] = S == 1 ? acc[b][e] - y[o] : acc[b][e];
+      }
+  } else {
+    const float eta = W.eta[h];
+    float* vcw = vc_all + unit * C.m_max * (int64_t)kD;
+    float* up = W.Up + (int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD;
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = tile * 64 + 16 * wave + 4 * g + e;
+        const int64_t o = (int64_t)j * kD + 16 * b + c16;
+        if (S == 1) {
+          if (j < m) vcw[o] -= eta * acc[b][e];
+        } else {
+          up[o] = acc[b][e];
+        }
+      }
+  }
+}
+
+// Split sums, in split order: Z = sum_s Zp[s] - Y (KIND 0, work item = (seq, head, 64 rows)) and
+// Vc_j -= eta sum_s Up[s]_j (KIND 1, work item = (seq, head, 64 kept keys)).
+template <int KIND>
+__global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
+                                                    SeqTable T) {
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int m = T.m[i], s = T.first + i;
+  const int R = C.R;
+  AmWs W = am_ws(ws, T, i, C);
+  const int ldm = W.ldm;
+  const int nb = KIND == 0 ? (R + 63) / 64 : ldm / 64;
+  const int local = t - T.start[i];
+  const int h = local / nb, blk = local - h * nb;
+  const int lim = KIND == 0 ? R : m;
+  const int S = KIND == 0 ? C.S1 : C.S2;
+  const int64_t unit = (int64_t)s * C.H + h;
+  const int64_t stride = KIND == 0 ? pad64((int64_t)C.H * R * kD) : pad64((int64_t)C.H * ldm * kD);
+  const float* src = (KIND == 0 ? W.Zp + (int64_t)h * R * kD : W.Up + (int64_t)h * ldm * kD);
+  for (int x = threadIdx.x; x < 64 * (kD / 4); x += 256) {
+    const int row = blk * 64 + (x >> 5), c4 = x & 31;
+    if (row >= lim) continue;
+    const int64_t o = (int64_t)row * kD + 4 * c4;
+    float4 a = *reinterpret_cast<const float4*>(src + o);
+    for (int sp = 1; sp < S; ++sp) {
+      const float4 p = *reinterpret_cast<const float4*>(src + sp * stride + o);
+      a.x += p.x;
+      a.y += p.y;
+      a.z += p.z;
+      a.w += p.w;
     }
+    if constexpr (KIND == 0) {
+      const float4 y = *reinterpret_cast<const float4*>(W.Y + (int64_t)h * R * kD + o);
+      *reinterpret_cast<float4*>(W.Z + (int64_t)h * R * kD + o) =
+          make_float4(a.x - y.x, a.y - y.y, a.z - y.z, a.w - y.w);
+    } else {
+      const float f = W.eta[h];
+      float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
+      float4 v = *d;
+      v.x -= f * a.x;
+      v.y -= f * a.y;
+      v.z -= f * a.z;
+      v.w -= f * a.w;
+      *d = v;
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -411,8 +593,8 @@ __global__ __launch_bounds__(256) void am_cols_mm(const float* __restrict__ w_al
 template <int LAYOUT>
 __global__ __launch_bounds__(256) void am_init(const uint16_t* __restrict__ v, const int32_t* __restrict__ table,
                                                int max_blocks, const int32_t* __restrict__ kept, float* __restrict__ w_all,
-                                               float* __restrict__ vc_all, const float* __restrict__ ws, int H, int R,
-                                               int64_t n_max, int m_max, SeqTable T) {
+                                               float* __restrict__ vc_all, const float* __restrict__ ws, int64_t n_max,
+                                               AmCfg C, SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int m = T.m[i], n = T.n[i], s = T.first + i;
@@ -421,14 +603,14 @@ __global__ __launch_bounds__(256) void am_init(const uint16_t* __restrict__ v, c
   const int h = local / cb;
   const int j = (local - h * cb) * 256 + threadIdx.x;
   if (j >= m) return;
-  const int64_t unit = (int64_t)s * H + h;
+  const int64_t unit = (int64_t)s * C.H + h;
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
-  AmWs W = am_ws(const_cast<float*>(ws), T, i, H, R);
-  w_all[unit * m_max + j] = __builtin_amdgcn_exp2f((W.ME[h] - W.M[h]) * kLog2e);  // w = 1 in scaled units
-  const int key = min(max(kept[unit * m_max + j], 0), n - 1);
-  const u32x4* row = key_row<LAYOUT>(v, map, H, h, n_max, unit, T.kofs[i] + key);
-  float* dst = vc_all + (unit * m_max + j) * (int64_t)kD;
+  AmWs W = am_ws(const_cast<float*>(ws), T, i, C);
+  w_all[unit * C.m_max + j] = __builtin_amdgcn_exp2f((W.ME[h] - W.M[h]) * kLog2e);  // w = 1 in scaled units
+  const int key = min(max(kept[unit * C.m_max + j], 0), n - 1);
+  const u32x4* row = key_row<LAYOUT>(v, map, C.H, h, n_max, unit, T.kofs[i] + key);
+  float* dst = vc_all + (unit * C.m_max + j) * (int64_t)kD;
 #pragma unroll 4
   for (int ch = 0; ch < kD / 8; ++ch) {
     const u32x4 raw = row[ch];
@@ -441,8 +623,8 @@ __global__ __launch_bounds__(256) void am_init(const uint16_t* __restrict__ v, c
   }
 }
 
-__global__ __launch_bounds__(256) void am_finish(float* __restrict__ w_all, const float* __restrict__ ws, int H,
-                                                 int R, int m_max, SeqTable T) {
+__global__ __launch_bounds__(256) void am_finish(float* __restrict__ w_all, const float* __restrict__ ws, AmCfg C,
+                                                 SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
@@ -451,8 +633,8 @@ __global__ __launch_bounds__(256) void am_finish(float* __restrict__ w_all, cons
   const int h = local / cb;
   const int j = (local - h * cb) * 256 + threadIdx.x;
   if (j >= m) return;
-  AmWs W = am_ws(const_cast<float*>(ws), T, i, H, R);
-  float* w = w_all + ((int64_t)s * H + h) * m_max + j;
+  AmWs W = am_ws(const_cast<float*>(ws), T, i, C);
+  float* w = w_all + ((int64_t)s * C.H + h) * C.m_max + j;
   *w = *w > 0.0f ? __logf(*w) - (W.ME[h] - W.M[h]) : -INFINITY;
 }
 
@@ -467,82 +649,97 @@ __global__ __launch_bounds__(256) void am_finish(float* __restrict__ w_all, cons
   } while (0)
 #define KVC_COMMA ,
 
+// Work items per head of each kernel.
 int am_exp_items(int R, int cols) { return ((R + 63) / 64) * ((cols + 63) / 64); }
-int am_scale_items(int R, int m) { return (int)(((int64_t)R * m + 4095) / 4096); }
-int am_row_items(int R) { return (R + 63) / 64; }
+int am_scale_items(int R, int m) { return (int)(((int64_t)R * pad64(m) + 4095) / 4096); }
+int am_row_tiles(int R) { return (R + 63) / 64; }
 int am_dot_row_items(int R) { return (R + 3) / 4; }
 int am_col_items(int m) { return (m + 255) / 256; }
-int am_key_tiles(int m) { return (m + 63) / 64; }
+int am_col_part_items(int R, int m) { return (int)((pad64(m) + 255) / 256) * ((R + kRowChunk - 1) / kRowChunk); }
+int am_key_tiles(int m) { return (int)(pad64(m) / 64); }
+int am_stages_rows(int m) { return (int)(pad64(m) / 32); }
+int am_stages_cols(int R) { return (R + 31) / 32; }
 
 hipError_t launch_am_exp(int layout, bool all, const void* q, const void* k, const int32_t* table, int max_blocks,
-                         const int32_t* kept, int m_max, const float* lse, float* ws, int H, int R, int64_t n_max,
-                         float scale, const SeqTable& T, hipStream_t st) {
+                         const int32_t* kept, const float* lse, float* ws, int64_t n_max, float scale, const AmCfg& C,
+                         const SeqTable& T, hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
-  if (all) KVC_AM_LAYOUT(am_exp, KVC_COMMA true, qq, kk, table, max_blocks, kept, m_max, lse, ws, H, R, n_max, scale, T);
-  else KVC_AM_LAYOUT(am_exp, KVC_COMMA false, qq, kk, table, max_blocks, kept, m_max, lse, ws, H, R, n_max, scale, T);
+  if (all) KVC_AM_LAYOUT(am_exp, KVC_COMMA true, qq, kk, table, max_blocks, kept, lse, ws, n_max, scale, C, T);
+  else KVC_AM_LAYOUT(am_exp, KVC_COMMA false, qq, kk, table, max_blocks, kept, lse, ws, n_max, scale, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_stats(const float* lse, float* ws, int H, int R, const SeqTable& T, hipStream_t st) {
-  am_stats<<<dim3(T.total), dim3(64), 0, st>>>(lse, ws, H, R, T);
+hipError_t launch_am_stats(const float* lse, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_stats<<<dim3(T.total), dim3(64), 0, st>>>(lse, ws, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_scale(float* ws, int H, int R, const SeqTable& T, hipStream_t st) {
-  am_scale<<<dim3(T.total), dim3(256), 0, st>>>(ws, H, R, T);
+hipError_t launch_am_scale(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_scale<<<dim3(T.total), dim3(256), 0, st>>>(ws, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_rows_dot(const float* w, float* ws, int H, int R, int m_max, const SeqTable& T, hipStream_t st) {
-  am_rows_dot<<<dim3(T.total), dim3(256), 0, st>>>(w, ws, H, R, m_max, T);
+hipError_t launch_am_rows_dot(const float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_rows_dot<<<dim3(T.total), dim3(256), 0, st>>>(w, ws, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_cols_dot(int mode, float* w, const float* lse, float* ws, int H, int R, int m_max,
-                              const SeqTable& T, hipStream_t st) {
+hipError_t launch_am_cols_part(int mode, const float* w, const float* lse, float* ws, const AmCfg& C,
+                               const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(256);
-  if (mode == 0) am_cols_dot<0><<<grid, block, 0, st>>>(w, lse, ws, H, R, m_max, T);
-  else if (mode == 1) am_cols_dot<1><<<grid, block, 0, st>>>(w, lse, ws, H, R, m_max, T);
-  else am_cols_dot<2><<<grid, block, 0, st>>>(w, lse, ws, H, R, m_max, T);
+  if (mode == 0) am_cols_part<0><<<grid, block, 0, st>>>(w, lse, ws, C, T);
+  else if (mode == 1) am_cols_part<1><<<grid, block, 0, st>>>(w, lse, ws, C, T);
+  else am_cols_part<2><<<grid, block, 0, st>>>(w, lse, ws, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_eta(float* ws, int H, int R, const SeqTable& T, hipStream_t st) {
-  am_eta<<<dim3(T.total), dim3(256), 0, st>>>(ws, H, R, T);
+hipError_t launch_am_cols_fin(int mode, float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  dim3 grid(T.total), block(256);
+  if (mode == 1) am_cols_fin<1><<<grid, block, 0, st>>>(w, ws, C, T);
+  else am_cols_fin<0><<<grid, block, 0, st>>>(w, ws, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_rows_mm(int layout, int src, const void* v, const int32_t* table, int max_blocks, const float* w,
-                             const float* vc, float* ws, int H, int R, int64_t n_max, int m_max, const SeqTable& T,
-                             hipStream_t st) {
+hipError_t launch_am_eta(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_eta<<<dim3(T.total), dim3(256), 0, st>>>(ws, C, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_am_target(int layout, const void* v, const int32_t* table, int max_blocks, float* ws,
+                            int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   const auto* vv = static_cast<const uint16_t*>(v);
   dim3 grid(T.total), block(256);
-  if (src == 0)
-    KVC_AM_LAYOUT(am_rows_mm, KVC_COMMA 0, vv, table, max_blocks, w, vc, ws, H, R, n_max, m_max, T);
-  else
-    am_rows_mm<kContig, 1><<<grid, block, 0, st>>>(vv, table, max_blocks, w, vc, ws, H, R, n_max, m_max, T);
+  KVC_AM_LAYOUT(am_target, , vv, table, max_blocks, ws, n_max, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_cols_mm(const float* w, float* vc, float* ws, int H, int R, int m_max, const SeqTable& T,
-                             hipStream_t st) {
-  am_cols_mm<<<dim3(T.total), dim3(256), 0, st>>>(w, vc, ws, H, R, m_max, T);
+hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  dim3 grid(T.total), block(256);
+  if (kind == 0) am_gemm<0><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else am_gemm<1><<<grid, block, 0, st>>>(vc, ws, C, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_am_split_sum(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  dim3 grid(T.total), block(256);
+  if (kind == 0) am_split_sum<0><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else am_split_sum<1><<<grid, block, 0, st>>>(vc, ws, C, T);
   return hipGetLastError();
 }
 
 hipError_t launch_am_init(int layout, const void* v, const int32_t* table, int max_blocks, const int32_t* kept,
-                          float* w, float* vc, const float* ws, int H, int R, int64_t n_max, int m_max,
-                          const SeqTable& T, hipStream_t st) {
+                          float* w, float* vc, const float* ws, int64_t n_max, const AmCfg& C, const SeqTable& T,
+                          hipStream_t st) {
   const auto* vv = static_cast<const uint16_t*>(v);
   dim3 grid(T.total), block(256);
-  KVC_AM_LAYOUT(am_init, , vv, table, max_blocks, kept, w, vc, ws, H, R, n_max, m_max, T);
+  KVC_AM_LAYOUT(am_init, , vv, table, max_blocks, kept, w, vc, ws, n_max, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_finish(float* w, const float* ws, int H, int R, int m_max, const SeqTable& T, hipStream_t st) {
-  am_finish<<<dim3(T.total), dim3(256), 0, st>>>(w, ws, H, R, m_max, T);
+hipError_t launch_am_finish(float* w, const float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_finish<<<dim3(T.total), dim3(256), 0, st>>>(w, ws, C, T);
   return hipGetLastError();
 }
 

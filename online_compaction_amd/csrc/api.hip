@@ -35,30 +35,37 @@ hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const v
 hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
                                  const SeqTable& T, hipStream_t st);
 int redirect_tiles(int n);
+struct AmCfg {
+  int H, R, m_max, S1, S2;
+};
+int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2);
 int am_exp_items(int R, int cols);
 int am_scale_items(int R, int m);
-hipError_t launch_am_stats(const float* lse, float* ws, int H, int R, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_scale(float* ws, int H, int R, const SeqTable& T, hipStream_t st);
-int am_row_items(int R);
+int am_row_tiles(int R);
 int am_dot_row_items(int R);
 int am_col_items(int m);
+int am_col_part_items(int R, int m);
 int am_key_tiles(int m);
+int am_stages_rows(int m);
+int am_stages_cols(int R);
+hipError_t launch_am_stats(const float* lse, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_scale(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_exp(int layout, bool all, const void* q, const void* k, const int32_t* table, int max_blocks,
-                         const int32_t* kept, int m_max, const float* lse, float* ws, int H, int R, int64_t n_max,
-                         float scale, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_rows_dot(const float* w, float* ws, int H, int R, int m_max, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_cols_dot(int mode, float* w, const float* lse, float* ws, int H, int R, int m_max,
-                              const SeqTable& T, hipStream_t st);
-hipError_t launch_am_eta(float* ws, int H, int R, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_rows_mm(int layout, int src, const void* v, const int32_t* table, int max_blocks, const float* w,
-                             const float* vc, float* ws, int H, int R, int64_t n_max, int m_max, const SeqTable& T,
-                             hipStream_t st);
-hipError_t launch_am_cols_mm(const float* w, float* vc, float* ws, int H, int R, int m_max, const SeqTable& T,
-                             hipStream_t st);
+                         const int32_t* kept, const float* lse, float* ws, int64_t n_max, float scale, const AmCfg& C,
+                         const SeqTable& T, hipStream_t st);
+hipError_t launch_am_rows_dot(const float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_cols_part(int mode, const float* w, const float* lse, float* ws, const AmCfg& C,
+                               const SeqTable& T, hipStream_t st);
+hipError_t launch_am_cols_fin(int mode, float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_eta(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_target(int layout, const void* v, const int32_t* table, int max_blocks, float* ws,
+                            int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_split_sum(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_init(int layout, const void* v, const int32_t* table, int max_blocks, const int32_t* kept,
-                          float* w, float* vc, const float* ws, int H, int R, int64_t n_max, int m_max,
-                          const SeqTable& T, hipStream_t st);
-hipError_t launch_am_finish(float* w, const float* ws, int H, int R, int m_max, const SeqTable& T, hipStream_t st);
+                          float* w, float* vc, const float* ws, int64_t n_max, const AmCfg& C, const SeqTable& T,
+                          hipStream_t st);
+hipError_t launch_am_finish(float* w, const float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_select(const float* scores, int32_t* kept, int H, int64_t n_max, int m_max, const SeqTable& T,
                          hipStream_t st);
 hipError_t launch_lrfu_update(const float* mass, float* state, int32_t* counts, int H, int64_t n_max, double top_p,
@@ -459,14 +466,36 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
 // ------------------------------------------------------------------------------------------------
 // Attention Matching
 // ------------------------------------------------------------------------------------------------
-static int64_t am_seq_floats(const kvc_shape* sh, int s, const int32_t* m) {
-  const int64_t H = sh->num_kv_heads, R = (int64_t)sh->group * sh->num_queries;
-  return H * (R * ((int64_t)m[s] + sh->seq_lens[s] + 2 * kHeadDim + 1) + m[s] + 4);
+// Split counts of the two value products: enough workgroups for about four per CU over the
+// batch (at most 8 splits, at least 4 stages of 32 per split). A function of the shape alone, so
+// that the workspace size and the fit agree.
+static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2) {
+  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
+  int64_t t1 = 0, t2 = 0;
+  int st1 = INT32_MAX, st2 = am_stages_cols(R);
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    if (m[s] == 0) continue;
+    t1 += (int64_t)H * am_row_tiles(R);
+    t2 += (int64_t)H * am_key_tiles(m[s]);
+    st1 = std::min(st1, am_stages_rows(m[s]));
+  }
+  auto pick = [](int64_t tiles, int stages) {
+    if (tiles == 0) return 1;
+    int64_t sp = (1024 + tiles - 1) / tiles;
+    sp = std::min<int64_t>(sp, 8);
+    sp = std::min<int64_t>(sp, std::max(1, stages / 4));
+    return (int)std::max<int64_t>(sp, 1);
+  };
+  *S1 = pick(t1, st1);
+  *S2 = pick(t2, st2);
 }
 
 static size_t am_bytes(const kvc_shape* sh, const int32_t* m) {
+  int S1, S2;
+  am_splits(sh, m, &S1, &S2);
+  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
   int64_t f = 0;
-  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(sh, s, m);
+  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(H, R, sh->seq_lens[s], m[s], S1, S2);
   return ((size_t)f * sizeof(float) + 255) & ~size_t(255);
 }
 
@@ -513,53 +542,61 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
     lse_rows = lse_ws;
   }
   float* amws = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_part);
+  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
+  AmCfg C{H, R, m_max, 1, 1};
+  am_splits(sh, m, &C.S1, &C.S2);
   std::vector<int64_t> off(sh->num_seqs);
   int64_t acc = 0;
   for (int s = 0; s < sh->num_seqs; ++s) {
     off[s] = acc;
-    acc += am_seq_floats(sh, s, m);
+    acc += am_seq_floats(H, R, sh->seq_lens[s], m[s], C.S1, C.S2);
   }
   auto offset = [&](int s) -> int64_t { return off[s]; };
-  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
   const int layout = layout_of(k);
   const int64_t nm = sh->n_max;
   auto run = [&](auto&& items, auto&& body) -> hipError_t { return for_each_chunk(sh, m, items, offset, body); };
-  auto cols = [&](int s) { return H * am_col_items(m[s]); };
-#define KVC_AM_STEP(ITEMS, CALL)                                          \
-  do {                                                                    \
-    const hipError_t e_ = run(ITEMS, [&](const SeqTable& T) { return CALL; }); \
-    if (e_ != hipSuccess) return hip_fail(e_, "attention matching kernel");  \
+  // a sequence with m = 0 has nothing to fit: every per-sequence kernel gets no work items for it
+  auto per = [&](auto&& f) { return [&, f](int s) -> int { return m[s] ? f(s) : 0; }; };
+#define KVC_AM_STEP(ITEMS, CALL)                                              \
+  do {                                                                        \
+    const hipError_t e_ = run(per(ITEMS), [&](const SeqTable& T) { return CALL; }); \
+    if (e_ != hipSuccess) return hip_fail(e_, "attention matching kernel");      \
   } while (0)
   auto units = [&](int) { return H; };
-  KVC_AM_STEP(units, launch_am_stats(lse_rows, amws, H, R, T, st));
-  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, m[s]); },
-              launch_am_exp(layout, false, q, k->data, k->block_table, k->max_blocks, kept, m_max, lse_rows, amws, H,
-                            R, nm, sh->scale, T, st));
-  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, sh->seq_lens[s]); },
-              launch_am_exp(layout, true, q, k->data, k->block_table, k->max_blocks, kept, m_max, lse_rows, amws, H,
-                            R, nm, sh->scale, T, st));
-  KVC_AM_STEP([&](int s) { return H * am_scale_items(R, m[s]); }, launch_am_scale(amws, H, R, T, st));
-  KVC_AM_STEP(cols, launch_am_cols_dot(0, beta, lse_rows, amws, H, R, m_max, T, st));
-  KVC_AM_STEP(cols, launch_am_init(layout, v->data, v->block_table, v->max_blocks, kept, beta, v_c, amws, H, R, nm,
-                                   m_max, T, st));
+  auto cols = [&](int s) { return H * am_col_items(m[s]); };
+  auto cparts = [&](int s) { return H * am_col_part_items(R, m[s]); };
   auto rows = [&](int) { return H * am_dot_row_items(R); };
-  for (int it = 0; it < iters_beta; ++it) {
-    KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, H, R, m_max, T, st));
-    KVC_AM_STEP(cols, launch_am_cols_dot(1, beta, lse_rows, amws, H, R, m_max, T, st));
-  }
-  KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, H, R, m_max, T, st));
-  KVC_AM_STEP(cols, launch_am_cols_dot(2, beta, lse_rows, amws, H, R, m_max, T, st));
-  KVC_AM_STEP(units, launch_am_eta(amws, H, R, T, st));
-  auto rtiles = [&](int) { return H * am_row_items(R); };
-  KVC_AM_STEP(rtiles, launch_am_rows_mm(layout, 0, v->data, v->block_table, v->max_blocks, beta, v_c, amws, H, R, nm,
-                                        m_max, T, st));
+  auto rtiles = [&](int) { return H * am_row_tiles(R); };
   auto ktiles = [&](int s) { return H * am_key_tiles(m[s]); };
-  for (int it = 0; it < iters_v; ++it) {
-    KVC_AM_STEP(rtiles, launch_am_rows_mm(layout, 1, v->data, v->block_table, v->max_blocks, beta, v_c, amws, H, R,
-                                          nm, m_max, T, st));
-    KVC_AM_STEP(ktiles, launch_am_cols_mm(beta, v_c, amws, H, R, m_max, T, st));
+  KVC_AM_STEP(units, launch_am_stats(lse_rows, amws, C, T, st));
+  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, m[s]); },
+              launch_am_exp(layout, false, q, k->data, k->block_table, k->max_blocks, kept, lse_rows, amws, nm,
+                            sh->scale, C, T, st));
+  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, sh->seq_lens[s]); },
+              launch_am_exp(layout, true, q, k->data, k->block_table, k->max_blocks, kept, lse_rows, amws, nm,
+                            sh->scale, C, T, st));
+  KVC_AM_STEP([&](int s) { return H * am_scale_items(R, m[s]); }, launch_am_scale(amws, C, T, st));
+  KVC_AM_STEP(cparts, launch_am_cols_part(0, beta, lse_rows, amws, C, T, st));
+  KVC_AM_STEP(cols, launch_am_cols_fin(0, beta, amws, C, T, st));
+  KVC_AM_STEP(cols, launch_am_init(layout, v->data, v->block_table, v->max_blocks, kept, beta, v_c, amws, nm, C, T,
+                                   st));
+  for (int it = 0; it < iters_beta; ++it) {
+    KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, C, T, st));
+    KVC_AM_STEP(cparts, launch_am_cols_part(1, beta, lse_rows, amws, C, T, st));
+    KVC_AM_STEP(cols, launch_am_cols_fin(1, beta, amws, C, T, st));
   }
-  KVC_AM_STEP(cols, launch_am_finish(beta, amws, H, R, m_max, T, st));
+  KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, C, T, st));
+  KVC_AM_STEP(cparts, launch_am_cols_part(2, beta, lse_rows, amws, C, T, st));  // E becomes P_C
+  KVC_AM_STEP(cols, launch_am_cols_fin(2, beta, amws, C, T, st));
+  KVC_AM_STEP(units, launch_am_eta(amws, C, T, st));
+  KVC_AM_STEP(rtiles, launch_am_target(layout, v->data, v->block_table, v->max_blocks, amws, nm, C, T, st));
+  for (int it = 0; it < iters_v; ++it) {
+    KVC_AM_STEP([&](int s) { return rtiles(s) * C.S1; }, launch_am_gemm(0, v_c, amws, C, T, st));
+    if (C.S1 > 1) KVC_AM_STEP(rtiles, launch_am_split_sum(0, v_c, amws, C, T, st));
+    KVC_AM_STEP([&](int s) { return ktiles(s) * C.S2; }, launch_am_gemm(1, v_c, amws, C, T, st));
+    if (C.S2 > 1) KVC_AM_STEP(ktiles, launch_am_split_sum(1, v_c, amws, C, T, st));
+  }
+  KVC_AM_STEP(cols, launch_am_finish(beta, amws, C, T, st));
 #undef KVC_AM_STEP
   return ok();
 }

@@ -1,4 +1,4 @@
-// Shared pieces of the MFMA scoring kernels for gfx950 (score_mfma.hip, lse_mfma.hip).
+// Shared pieces of the MFMA kernels for gfx950 (score_mfma.hip, lse_mfma.hip, am.hip).
 //
 // The d = 128 contraction is 4 k-steps of v_mfma_f32_16x16x32_bf16. Within a k-step, lane
 // group g = lane / 16 supplies d-chunk 4*kstep + g (8 bf16 = 16 bytes) of its row, the same
@@ -72,6 +72,7 @@ __device__ __forceinline__ void vm_wait_barrier() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else if constexpr (N == 5) asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   else static_assert(N == 0, "unsupported count");
 }
 

@@ -184,3 +184,38 @@ def run_retention_compact(b: Batch, o: Outputs, r: Retention, stream=None) -> No
     """K/V compaction, with the LRFU state carried along into r.side."""
     run_compact(b, o, stream)
     A.kvc_compact_side(b.shape, b.block_size if b.paged else 0, o.kept, b.m, b.m_max, r.state, r.side, stream)
+
+
+# ------------------------------------------------------------------------ Attention Matching stage
+
+@dataclass
+class Matching:
+    """Attention Matching outputs of a batch (bias beta and compact values V_C per kept key) and
+    the fit's workspace; K_C is the kept keys, gathered by the compaction stage."""
+    beta: torch.Tensor         # float32 [S][H][m_max]
+    v_c: torch.Tensor          # float32 [S][H][m_max][d]
+    ws: torch.Tensor
+    iters_beta: int
+    iters_v: int
+
+
+def _value_view(b: Batch) -> A.KView:
+    if b.paged:
+        return A.KView(b.v_pool, b.dtype, b.block_size, b.table, b.max_blocks)
+    return A.KView(b.v, b.dtype)
+
+
+def allocate_matching(b: Batch, iters_beta: int, iters_v: int) -> Matching:
+    sh = b.shape
+    dev = b.q.device
+    wsb = A.kvc_am_workspace_size(sh, b.kview(), _value_view(b), b.m, b.lse is not None)
+    return Matching(torch.zeros((sh.num_seqs, sh.num_kv_heads, b.m_max), dtype=torch.float32, device=dev),
+                    torch.zeros((sh.num_seqs, sh.num_kv_heads, b.m_max, sh.head_dim), dtype=torch.float32,
+                                device=dev),
+                    torch.empty(max(256, wsb), dtype=torch.uint8, device=dev), iters_beta, iters_v)
+
+
+def run_matching(b: Batch, o: Outputs, am: Matching, stream=None) -> None:
+    """Fit beta and V_C for the kept keys o.kept (before a paged compaction rewrites the pool)."""
+    A.kvc_am_fit(b.shape, b.q, b.kview(), _value_view(b), b.lse, o.kept, b.m, b.m_max, am.iters_beta, am.iters_v,
+                 am.beta, am.v_c, am.ws, stream)

@@ -81,3 +81,56 @@ def oracle_lse_units(w, data_Q, keys_of, units, bias_of=None) -> dict:
         b = None if bias_of is None else bias_of(s)
         out[(s, h)] = O.lse_unit(rows, keys_of(s, h), w.dtype, w.logit_scale, b)
     return out
+
+
+def _am_rownorm(E, w):
+    Ew = E * w[None, :]
+    rs = Ew.sum(axis=1)
+    return np.where(rs[:, None] > 0, Ew / np.where(rs > 0, rs, 1.0)[:, None], 0.0)
+
+
+def check_am_unit(rows, K, V, lse_rows, kept, beta_row, vc_rows, dtype, scale, iters_beta, iters_v,
+                  what: str = "") -> dict:
+    """One unit's Attention Matching outputs (beta_row [m_max], vc_rows [m_max][d]; the first
+    m = len(kept) filled, the rest holding the sentinel 7.0) against the oracle running the same
+    iterations in float64.
+
+    AM's parameters are only determined where the proxy rows see them: a key that only rows
+    with a negligible partition function attend to can take almost any bias. Parity is therefore
+    checked on what the fit determines -- the objective, the fitted partition functions and the
+    compacted attention output of the rows that carry weight, and beta / V_C of the keys with
+    real support -- each against the oracle within 2e-3, and every finite bias within 1e-2 (the
+    float32 iterations drift a little along the fit's poorly determined directions)."""
+    m = len(kept)
+    rb, rv = O.am_unit(rows, K, V, kept, dtype, scale, iters_beta, iters_v, lse_rows)
+    gb, gv = beta_row[:m].astype(np.float64), vc_rows[:m].astype(np.float64)
+    t = what
+    assert np.all(np.isfinite(gv)) and not np.any(np.isnan(gb)), f"{t}: non-finite output"
+    Q64, K64, V64 = O.widen(rows, dtype), O.widen(K, dtype), O.widen(V, dtype)
+    z, Y, M, _ = O.am_targets(Q64, K64, V64, scale, lse_rows)
+    E = O.am_design(Q64, K64[kept], scale, M)
+    wg, wr = np.exp(gb), np.exp(rb)
+    og, orf = np.linalg.norm(E @ wg - z), np.linalg.norm(E @ wr - z)
+    d_obj = abs(og - orf) / max(orf, 1e-300)
+    assert d_obj <= 1e-3 or abs(og - orf) <= 2e-5 * np.linalg.norm(z), f"{t}: objective {og:.6g} vs {orf:.6g}"
+    heavy = z >= 1e-3 * z.max()
+    fit_g, fit_r = (E @ wg)[heavy] / z[heavy], (E @ wr)[heavy] / z[heavy]
+    d_fit = float(np.max(np.abs(fit_g - fit_r)))
+    assert d_fit <= 2e-3, f"{t}: fitted partition functions differ by {d_fit:.3g}"
+    Pg, Pr = _am_rownorm(E, wg), _am_rownorm(E, wr)
+    outg, outr = Pg @ gv, Pr @ rv
+    d_out = float(np.max(np.abs(outg[heavy] - outr[heavy]) / (1.0 + np.abs(outr[heavy]))))
+    assert d_out <= 2e-3, f"{t}: compacted attention outputs differ by {d_out:.3g}"
+    supp_b = (E.T @ z) >= 1e-2 * (E.T @ z).max()
+    d_beta = float(np.max(np.abs(gb[supp_b] - rb[supp_b]))) if supp_b.any() else 0.0
+    assert d_beta <= 2e-3, f"{t}: beta of supported keys differs by {d_beta:.3g}"
+    supp_v = Pr[heavy].sum(axis=0) >= 1e-2 * Pr[heavy].sum(axis=0).max()
+    d_vc = float(np.max(np.abs(gv[supp_v] - rv[supp_v]) / (1.0 + np.abs(rv[supp_v])))) if supp_v.any() else 0.0
+    assert d_vc <= 2e-3, f"{t}: V_C of supported keys differs by {d_vc:.3g}"
+    fin = np.isfinite(rb)
+    d_all = float(np.max(np.abs(gb[fin] - rb[fin]))) if fin.any() else 0.0
+    assert np.array_equal(np.isfinite(gb), fin) and d_all <= 1e-2, f"{t}: beta differs by {d_all:.3g}"
+    assert og <= np.linalg.norm(E @ np.ones_like(wr) - z) * (1 + 1e-6) + 2e-5 * np.linalg.norm(z), \
+        f"{t}: the fit made things worse"
+    assert np.all(beta_row[m:] == 7.0) and np.all(vc_rows[m:] == 7.0), f"{t}: rows past m touched"
+    return {"obj": d_obj, "fit": d_fit, "out": d_out, "beta": d_beta, "vc": d_vc}

@@ -124,7 +124,7 @@ def _c5_lengths() -> tuple:
 
 
 def spec(name: str, k: int | None = None) -> Workload:
-    """The five named workloads (c4 takes the expansion count k = 0..6)."""
+    """The named workloads (c4 takes the expansion count k = 0..6)."""
     if name == "c1":
         return Workload("c1", 1, 1, 1, 1, 32, 128, (4096,), (819,), "f32", "normal", "normal")
     if name in ("c2a", "c2b"):
@@ -151,6 +151,10 @@ def spec(name: str, k: int | None = None) -> Workload:
         n = 33000
         return Workload("sentinel", 4, 1, 8, 4, 330, 128, (n,), (c4_budget(6),), "bf16", "mixture", "action",
                         paged=True, block_size=16, table="identity", max_blocks=-(-n // 16), bias_tail=0.5)
+    if name == "am":
+        # Attention Matching on the cluster-query snapshot: the inputs of "c2b" (same seed); the
+        # top-m keys by Token Eviction score, then beta and V_C fitted for them
+        return Workload("am", 2, 1, 8, 4, 512, 128, (16384,), (ratio_budget(16384),), "bf16", "mixture", "cluster")
     if name == "turn":
         # one 4096-token turn in the middle of a 33000-token trajectory held in 36 layers' paged
         # caches, scored with the 512 queries per query head of the turn that followed it; the
