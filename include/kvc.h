@@ -238,8 +238,9 @@ kvc_status kvc_evict_redirect(const kvc_shape* shape, const int32_t* kept, const
  *   beta       device out [S][H][m_max] float32 (natural-log bias per kept key)
  *   v_c        device out [S][H][m_max][d] float32
  *   ws         device workspace of kvc_am_workspace_size(shape, k, v, m, lse != NULL) bytes:
- *              about 4 * H * R * (m_s + n_s + 2d) bytes per sequence (the kept and the full
- *              exponentials are materialised)
+ *              at most about 4 * H * (R * (m_s + n_s + 10 d) + 8 m_s d) bytes per sequence (the
+ *              kept and the full exponentials are materialised, plus up to 8 split partial
+ *              sums of each value product)
  * ------------------------------------------------------------------------------------------- */
 size_t kvc_am_workspace_size(const kvc_shape* shape, const kvc_kv_view* k, const kvc_kv_view* v, const int32_t* m,
                              int lse_supplied);
