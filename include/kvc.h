@@ -146,7 +146,8 @@ kvc_status kvc_attention_mass(const kvc_shape* shape, const void* q, const kvc_k
 /* ---------------------------------------------------------------------------------------------
  * kvc_select_topm -- per unit, the m_s positions with the largest scores, ties to the lower
  * position, written in ascending position order ([TE] top-m).
- *   scores  device [S][H][n_max] float32, non-negative and finite
+ *   scores  device [S][H][n_max] float32, non-negative (sign bit clear, so +0.0 and not -0.0)
+ *           and finite
  *   m       host [S]: 0 <= m_s <= n_s
  *   m_max   row stride of kept, >= max m_s
  *   kept    device out [S][H][m_max] int32; entries r >= m_s are not written

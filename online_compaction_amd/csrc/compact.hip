@@ -54,26 +54,27 @@ __global__ __launch_bounds__(kThreads) void compact_contig(const u32x4* __restri
   const int64_t unit = (int64_t)s * H + h;
   const int c = threadIdx.x % CH;
   const int rr = threadIdx.x / CH;
+  // Every load is unconditional (indices clamped into the row, addresses into the unit), so
+  // the kept indices, then all K and V chunks, are in flight together; rows past m are not
+  // stored and a kept index outside [0, n) is not followed (it comes from select; such a row
+  // is written as zeros).
+  int j[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) j[it] = kept[unit * m_max + min(r0 + it * kRowsPerIter + rr, m - 1)];
   u32x4 kx[kIters], vx[kIters];
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
-    const int r = r0 + it * kRowsPerIter + rr;
-    kx[it] = u32x4{0u, 0u, 0u, 0u};
-    vx[it] = kx[it];
-    if (r < m) {
-      const int j = kept[unit * m_max + r];
-      if ((unsigned)j < (unsigned)n) {  // kept comes from select; a bad index is skipped, not followed
-        kx[it] = k[(unit * n_max + kofs + j) * CH + c];
-        vx[it] = v[(unit * n_max + kofs + j) * CH + c];
-      }
-    }
+    const int jj = (unsigned)j[it] < (unsigned)n ? j[it] : 0;
+    kx[it] = k[(unit * n_max + kofs + jj) * CH + c];
+    vx[it] = v[(unit * n_max + kofs + jj) * CH + c];
   }
 #pragma unroll
   for (int it = 0; it < kIters; ++it) {
     const int r = r0 + it * kRowsPerIter + rr;
     if (r < m) {
-      ko[(unit * m_max + r) * CH + c] = kx[it];
-      vo[(unit * m_max + r) * CH + c] = vx[it];
+      const bool ok = (unsigned)j[it] < (unsigned)n;
+      ko[(unit * m_max + r) * CH + c] = ok ? kx[it] : u32x4{0u, 0u, 0u, 0u};
+      vo[(unit * m_max + r) * CH + c] = ok ? vx[it] : u32x4{0u, 0u, 0u, 0u};
     }
   }
 }
@@ -134,13 +135,27 @@ __global__ __launch_bounds__(kThreads) void paged_copy(u32x4* __restrict__ kp, u
   __syncthreads();
   const int np = min(kRowsPerBlock, npairs - p0);
   constexpr int kRowsPerIter = kThreads / CH;
+  constexpr int kIters = kRowsPerBlock / kRowsPerIter;
   const int c = threadIdx.x % CH;
-  for (int r = threadIdx.x / CH; r < np; r += kRowsPerIter) {
-    if (src_row[r] < 0) continue;
-    const u32x4 kx = kp[src_row[r] * CH + c];
-    const u32x4 vx = vp[src_row[r] * CH + c];
-    kp[dst_row[r] * CH + c] = kx;
-    vp[dst_row[r] * CH + c] = vx;
+  // Sources are kept positions and destinations are holes, so no row of the launch is both
+  // read and written: all of the tile's loads go first (unconditional; an unused slot reads
+  // pool row 0), then the stores.
+  u32x4 kx[kIters], vx[kIters];
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int r = threadIdx.x / CH + it * kRowsPerIter;
+    const int64_t sr = r < np ? src_row[r] : -1;
+    const int64_t row = sr < 0 ? 0 : sr;
+    kx[it] = kp[row * CH + c];
+    vx[it] = vp[row * CH + c];
+  }
+#pragma unroll
+  for (int it = 0; it < kIters; ++it) {
+    const int r = threadIdx.x / CH + it * kRowsPerIter;
+    if (r < np && src_row[r] >= 0) {
+      kp[dst_row[r] * CH + c] = kx[it];
+      vp[dst_row[r] * CH + c] = vx[it];
+    }
   }
 }
 

@@ -13,4 +13,5 @@ from .gen import (  # noqa: F401
     f32_to_bf16_bits,
     bf16_bits_to_f32,
     c4_budget,
+    score_rows,
 )

@@ -371,3 +371,29 @@ def build_paged(w: Workload, workers: int = 1) -> dict:
     Q, bias = _queries_and_bias(w, workers)
     return dict(k_pool=k_pool, v_pool=v_pool, table=table, Q=Q, bias=bias,
                 n=np.array(w.n, dtype=np.int32), m=np.array(w.m, dtype=np.int32))
+
+
+def score_rows(seed: int, lens, kind: str, n_max: int | None = None) -> np.ndarray:
+    """Synthetic non-negative float32 score rows [len(lens)][n_max] for exercising selection on
+    its own (zeros past each length). kind: "uniform" (U[0, 1)), "levels" (8 distinct values,
+    heavy ties), "zeros" (70 % exact zeros, the rest U[0, 1)), "tiny" (subnormal and normal
+    values spanning 2^-149 .. 1), "narrow" (all within one binade, [0.5, 0.5 + 2^-12))."""
+    n_max = int(n_max or max(lens))
+    out = np.zeros((len(lens), n_max), dtype=np.float32)
+    for s, n in enumerate(lens):
+        rng = _rng(900, s, seed, 50)
+        if kind == "uniform":
+            x = rng.random(n, dtype=np.float32)
+        elif kind == "levels":
+            x = rng.integers(0, 8, n).astype(np.float32) / 8.0
+        elif kind == "zeros":
+            x = np.where(rng.random(n) < 0.7, 0.0, rng.random(n)).astype(np.float32)
+        elif kind == "tiny":
+            bits = rng.integers(1, 0x3F800000, n, dtype=np.uint32)
+            x = bits.view(np.float32)
+        elif kind == "narrow":
+            x = (0.5 + rng.random(n) * 2.0 ** -12).astype(np.float32)
+        else:
+            raise ValueError(kind)
+        out[s, :n] = x
+    return out
