@@ -6,9 +6,9 @@
 // With w = exp(beta) the first is non-negative least squares in w; the second, with
 // P_C = diag(1 / (E w)) E diag(w) the compacted attention, is least squares in V_C.
 //
-// Per unit the kernels materialise E_ij = exp(c q_i . k_Cj - ME) (ME the largest kept logit) and,
-// for the target A(Q; K, V) = P_full V, P_full_ij = exp(c q_i . k_j - LSE_i) over all n keys, then
-// iterate:
+// Per unit the kernels materialise E_ij = exp(c q_i . k_Cj - ME) (ME the largest kept logit) and
+// the target A(Q; K, V) = P_full V, P_full_ij = exp(c q_i . k_j - LSE_i) over all n keys (P_full
+// itself only one 64-key chunk at a time, in registers and LDS), then iterate:
 //   beta: w' <- w' * (E^T z) / (E^T E w') (multiplicative NNLS updates), z_i = exp(LSE_i - Mz);
 //   V_C:  V <- V - eta P_C^T (P_C V - Y) from the kept keys' values (Landweber),
 //         eta = 1 / max_j sum_i (P_C)_ij.
@@ -25,7 +25,7 @@
 // Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], n = T.n[i],
 // ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 the split counts of the two value
 // products; every array starts on a 256-byte boundary):
-//   E [H][R][ldm] | P [H][R][n] | Y [H][R][128] | Z [H][R][128] | Zp [S1 > 1 ? S1 : 0][H][R][128] |
+//   E [H][R][ldm] | Y [H][R][128] | Z [H][R][128] | Zp [S1 > 1 ? S1 : 0][H][R][128] |
 //   Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] | u [H][R] | b [H][ldm] |
 //   Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H]
 // Columns m .. ldm-1 of E hold zeros (logit -inf), so tiles never need a column bound on E.
@@ -47,19 +47,18 @@ constexpr int kRowChunk = 64;  // rows per partial column sum
 __host__ __device__ constexpr int64_t pad64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
 struct AmWs {
-  float *E, *P, *Y, *Z, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
+  float *E, *Y, *Z, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
   uint32_t* mekey;
   int ldm;
 };
 
 __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const AmCfg& C) {
-  const int64_t m = T.m[i], n = T.n[i], H = C.H, R = C.R;
+  const int64_t m = T.m[i], H = C.H, R = C.R;
   const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
   AmWs w;
   w.ldm = (int)ldm;
   w.E = ws + T.off[i];
-  w.P = w.E + pad64(H * R * ldm);
-  w.Y = w.P + pad64(H * R * n);
+  w.Y = w.E + pad64(H * R * ldm);
   w.Z = w.Y + pad64(H * R * kD);
   w.Zp = w.Z + pad64(H * R * kD);
   w.Up = w.Zp + (C.S1 > 1 ? C.S1 : 0) * pad64(H * R * kD);
@@ -92,40 +91,36 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2) {
   const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
   const int64_t rk = pad64((int64_t)H * R * kD);
-  return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * R * n) + 2 * rk + (S1 > 1 ? S1 : 0) * rk +
+  return pad64((int64_t)H * R * ldm) + 2 * rk + (S1 > 1 ? S1 : 0) * rk +
          (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) + pad64((int64_t)H * R) +
          pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H);
 }
 
 // ------------------------------------------------------------------------------------------------
-// Logit tiles of 64 rows x 64 keys: into E the raw kept logits c q_i . k_Cj (ALL = false; -inf in
-// the padding columns; their maximum goes to an atomic per unit, and am_scale turns them into
-// exponentials), into P the weights exp(c q_i . k_j - LSE_i) over every key (ALL = true). Work
-// item = (seq, head, row tile, key tile), key tile fastest. Both operands come straight from
-// global memory (L2-resident).
+// Kept-logit tiles of 64 rows x 64 kept keys into E: the raw logits c q_i . k_Cj, -inf in the
+// padding columns; their maximum goes to an atomic per unit, and am_scale turns them into
+// exponentials. Work item = (seq, head, row tile, key tile), key tile fastest. Both operands
+// come straight from global memory (L2-resident).
 // ------------------------------------------------------------------------------------------------
-template <int LAYOUT, bool ALL>
+template <int LAYOUT>
 __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                    const int32_t* __restrict__ table, int max_blocks,
-                                                   const int32_t* __restrict__ kept, const float* __restrict__ lse,
-                                                   float* __restrict__ ws, int64_t n_max, float scale, AmCfg C,
-                                                   SeqTable T) {
+                                                   const int32_t* __restrict__ kept, float* __restrict__ ws,
+                                                   int64_t n_max, float scale, AmCfg C, SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int n = T.n[i], m = T.m[i];
   const int H = C.H, R = C.R;
   AmWs W = am_ws(ws, T, i, C);
-  const int cols = ALL ? n : m;
-  const int ld = ALL ? n : W.ldm;
+  const int ld = W.ldm;
   const int s = T.first + i;
-  const int rt_n = (R + 63) / 64, ct_n = (cols + 63) / 64;
+  const int rt_n = (R + 63) / 64, ct_n = (m + 63) / 64;
   int local = t - T.start[i];
   const int h = local / (rt_n * ct_n);
   local -= h * rt_n * ct_n;
   const int rt = local / ct_n, ct = local - rt * ct_n;
   const int64_t unit = (int64_t)s * H + h;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  const float* lu = lse + unit * R;
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
 
@@ -134,13 +129,13 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
   const uint16_t* qrow = q + (unit * R + min(row, R - 1)) * (int64_t)kD;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8(reinterpret_cast<const u32x4*>(qrow)[4 * ks + g]);
-  float* out = (ALL ? W.P : W.E) + ((int64_t)h * R) * ld;
+  float* out = W.E + ((int64_t)h * R) * ld;
   const int32_t* ku = kept + unit * C.m_max;
   float lmax = -INFINITY;
 #pragma unroll 1
   for (int sub = 0; sub < 4; ++sub) {
     const int col = ct * 64 + sub * 16 + c16;  // B operand key of this lane
-    const int key = ALL ? min(col, n - 1) : min(max(ku[min(col, m - 1)], 0), n - 1);
+    const int key = min(max(ku[min(col, m - 1)], 0), n - 1);
     const u32x4* kr = key_row<LAYOUT>(k, map, H, h, n_max, unit, T.kofs[i] + key);
     f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -150,9 +145,7 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
       const int orow = rt * 64 + wave * 16 + 4 * g + e;
       if (orow < R && col < ld) {
         const float l = acc[e] * scale;
-        if constexpr (ALL) {
-          out[(int64_t)orow * ld + col] = __builtin_amdgcn_exp2f((l - lu[orow]) * kLog2e);
-        } else if (col < m) {
+        if (col < m) {
           out[(int64_t)orow * ld + col] = l;
           lmax = fmaxf(lmax, l);
         } else {
@@ -161,10 +154,17 @@ __global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ 
       }
     }
   }
-  if constexpr (!ALL) {
+  // one atomic per workgroup at most: the four wave maxima meet in LDS, and the unit's running
+  // maximum is read first (it only grows, so a stale read costs at most a redundant atomic)
+  __shared__ float wmax[4];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
-    if (lane == 0 && lmax > -INFINITY) atomicMax(W.mekey + h, float_key(lmax));
+  for (int o = 32; o >= 1; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
+  if (lane == 0) wmax[wave] = lmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float bm = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const uint32_t key = float_key(bm);
+    if (bm > -INFINITY && key > __atomic_load_n(W.mekey + h, __ATOMIC_RELAXED)) atomicMax(W.mekey + h, key);
   }
 }
 
@@ -326,16 +326,34 @@ __global__ __launch_bounds__(256) void am_eta(float* __restrict__ ws, AmCfg C, S
 }
 
 // ------------------------------------------------------------------------------------------------
-// Target Y = P V (all n keys, V rows bf16 through the view), float32 MFMA, 64 rows x 128 per
-// workgroup. Work item = (seq, head, 64-row tile). LDS stages 16 columns of P and V at a time.
+// Target Y = P V with P_ij = exp(c q_i . k_j - LSE_i) over all n keys, without materialising P
+// (the weights of one 64-key chunk exist only in registers and a per-wave LDS tile).
+// Work item = (seq, head, 64-row tile), 8 waves: wave w owns rows 16 (w % 4) .. + 15 of the tile
+// and output columns 64 (w / 4) .. + 63 (the two halves recompute the same weights, which cost
+// 1/16 of the float32 product). Per 64-key chunk, staged through double-buffered LDS (keys as
+// bf16 rows, chunk c of row r at c ^ (r & 15); values widened to float32 rows):
+//   S = Q K^T     16 v_mfma_f32_16x16x32_bf16 (the wave's query rows stay in registers),
+//   P = exp2(S c log2(e) - LSE log2(e)), 0 for keys past n, through LDS into the A layout,
+//   Y += P V      64 v_mfma_f32_16x16x4_f32.
 // ------------------------------------------------------------------------------------------------
+namespace {
+constexpr int kTgtThreads = 512;
+constexpr int kVPitch = 132;  // float32 value row pitch in LDS
+constexpr int kPPitch = 68;   // per-wave weight tile pitch
+}  // namespace
+
 template <int LAYOUT>
-__global__ __launch_bounds__(256) void am_target(const uint16_t* __restrict__ v, const int32_t* __restrict__ table,
-                                                 int max_blocks, float* __restrict__ ws, int64_t n_max, AmCfg C,
-                                                 SeqTable T) {
-  __shared__ float As[64][17];
-  __shared__ float Bs[16][kD];
-  const int t = blockIdx.x;
+__global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __restrict__ q,
+                                                            const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v,
+                                                            const int32_t* __restrict__ table, int max_blocks,
+                                                            const int32_t* __restrict__ vtable, int vmax_blocks,
+                                                            const float* __restrict__ lse, float* __restrict__ ws,
+                                                            int64_t n_max, float scale, AmCfg C, SeqTable T) {
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][64 * 256];
+  __shared__ __attribute__((aligned(16))) float Vs[2][64 * kVPitch];
+  __shared__ __attribute__((aligned(16))) float Ps[8][16 * kPPitch];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int n = T.n[i], s = T.first + i;
   const int H = C.H, R = C.R;
@@ -344,79 +362,137 @@ __global__ __launch_bounds__(256) void am_target(const uint16_t* __restrict__ v,
   const int h = local / rt_n, rt = local - h * rt_n;
   const int64_t unit = (int64_t)s * H + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int rw = wave & 3, dh = wave >> 2;
   AmWs W = am_ws(ws, T, i, C);
-  const float* A = W.P + (int64_t)h * R * n;
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
+  const int32_t* vmap = LAYOUT == kPaged ? vtable + (int64_t)s * vmax_blocks
+                                         : (LAYOUT == kSlots ? vtable + unit * n_max : nullptr);
+  const int kofs = T.kofs[i];
 
-  f32x4 acc[8];
+  // query rows of this wave (A operand of S), and the LSE of the lane's four output rows
+  bf16x8 qa[4];
+  {
+    const int row = min(rt * 64 + 16 * rw + c16, R - 1);
+    const u32x4* qr = reinterpret_cast<const u32x4*>(q + (unit * R + row) * (int64_t)kD);
 #pragma unroll
-  for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8(qr[4 * ks + g]);
+  }
+  float lb[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) lb[e] = lse[unit * R + min(rt * 64 + 16 * rw + 4 * g + e, R - 1)] * kLog2e;
+  const float cl = scale * kLog2e;
+
+  // chunk staging: thread tid moves 16-byte piece tid & 15 (and tid & 15 + 16 for the second
+  // half of the key row set) of key row tid >> 4 (0 .. 31) and of key row 32 + (tid >> 4)
+  u32x4 kr[2], vr[2];
+  auto load = [&](int c0) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int kk = c0 + x * 32 + (tid >> 4);
+      const int pos = kofs + min(kk, n - 1);
+      kr[x] = key_row<LAYOUT>(k, map, H, h, n_max, unit, pos)[tid & 15];
+      vr[x] = key_row<LAYOUT>(v, vmap, H, h, n_max, unit, pos)[tid & 15];
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+      const int key = x * 32 + (tid >> 4), ch = tid & 15;
+      *reinterpret_cast<u32x4*>(&Ks[buf][swz(key, ch)]) = kr[x];
+      const uint32_t wd[4] = {vr[x].x, vr[x].y, vr[x].z, vr[x].w};
+      float4* vd = reinterpret_cast<float4*>(&Vs[buf][key * kVPitch + 8 * ch]);
+      vd[0] = make_float4(bf16_lo(wd[0]), bf16_hi(wd[0]), bf16_lo(wd[1]), bf16_hi(wd[1]));
+      vd[1] = make_float4(bf16_lo(wd[2]), bf16_hi(wd[2]), bf16_lo(wd[3]), bf16_hi(wd[3]));
+    }
+  };
+
+  f32x4 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  float* pw = Ps[wave];
+  const int nch = (n + 63) / 64;
+  load(0);
+  store(0);
+  __syncthreads();
 #pragma unroll 1
-  for (int c0 = 0; c0 < n; c0 += 16) {
-    for (int x = tid; x < 64 * 16; x += 256) {
-      const int rr = x >> 4, cc = x & 15;
-      const int r = rt * 64 + rr, c = c0 + cc;
-      As[rr][cc] = (r < R && c < n) ? A[(int64_t)r * n + c] : 0.0f;
+  for (int ch = 0; ch < nch; ++ch) {
+    const int buf = ch & 1;
+    const bool more = ch + 1 < nch;
+    if (more) load((ch + 1) * 64);
+    const uint8_t* kb = Ks[buf];
+    // S and the weights of 16 rows x 64 keys; lane (g, c16) holds rows 4g + e of key 16 sub + c16
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        sacc = mfma16(qa[ks], *reinterpret_cast<const bf16x8*>(&kb[swz(16 * sub + c16, 4 * ks + g)]), sacc);
+      const bool live = ch * 64 + 16 * sub + c16 < n;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        pw[(4 * g + e) * kPPitch + 16 * sub + c16] =
+            live ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], cl, -lb[e])) : 0.0f;
     }
-    for (int x = tid; x < 16 * (kD / 8); x += 256) {
-      const int cc = x / (kD / 8), ch = x % (kD / 8);  // 8 elements per item
-      const int c = c0 + cc;
-      float vals[8];
-      if (c < n) {
-        const u32x4 raw = key_row<LAYOUT>(v, map, H, h, n_max, unit, T.kofs[i] + c)[ch];
-        const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
+    // Y += P V over the 64 keys: step kk takes keys 4 kk + g (A from the weight tile, B from V)
+    const float* vb = Vs[buf];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vals[2 * e] = bf16_lo(wd[e]);
-          vals[2 * e + 1] = bf16_hi(wd[e]);
-        }
-      } else {
+    for (int kk = 0; kk < 16; ++kk) {
+      const float a = pw[c16 * kPPitch + 4 * kk + g];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vals[e] = 0.0f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) Bs[cc][ch * 8 + e] = vals[e];
+      for (int b = 0; b < 4; ++b) acc[b] = mfma_f32(a, vb[(4 * kk + g) * kVPitch + 64 * dh + 16 * b + c16], acc[b]);
     }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const float a = As[wave * 16 + c16][kk * 4 + g];
-#pragma unroll
-      for (int b = 0; b < 8; ++b) acc[b] = mfma_f32(a, Bs[kk * 4 + g][b * 16 + c16], acc[b]);
-    }
+    if (more) store(buf ^ 1);
     __syncthreads();
   }
   float* out = W.Y + (int64_t)h * R * kD;
 #pragma unroll
-  for (int b = 0; b < 8; ++b)
+  for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int r = rt * 64 + wave * 16 + 4 * g + e;
-      if (r < R) out[(int64_t)r * kD + b * 16 + c16] = acc[b][e];
+      const int r = rt * 64 + 16 * rw + 4 * g + e;
+      if (r < R) out[(int64_t)r * kD + 64 * dh + 16 * b + c16] = acc[b][e];
     }
 }
 
 // ------------------------------------------------------------------------------------------------
-// The two products of a Landweber step, float32 MFMA, one 64 x 128 output tile per workgroup
-// (each wave 16 x 128, eight 16 x 16 accumulators), the contraction in stages of 32 through
-// double-buffered LDS with the next stage's global loads in flight during the current stage's
-// MFMAs, and split over S workgroups whose partial tiles a second pass adds in order:
+// The two products of a Landweber step, one 64 x 128 output tile per workgroup (each wave 16 x
+// 128, eight 16 x 16 accumulators), the contraction in stages of 32 through double-buffered LDS
+// with the next stage's global loads in flight during the current stage's MFMAs, and split over
+// S workgroups whose partial tiles a second pass adds in order:
 //   KIND 0: Z = P_C Vc - Y          (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
 //   KIND 1: Vc -= eta P_C^T Z        (columns of P_C, contraction over rows)    -> Vc, or partials Up
-// Within a stage, MFMA step e takes contraction index 4e + g from lane group g on both operands.
-// LDS row pitches (36, 80 and 144 floats) put the 64 lanes of every operand read on distinct
-// banks and keep 16-byte stores aligned.
+// The float32 operands are split when they are staged: x = hi + lo with hi = bf16(x) and
+// lo = bf16(x - hi), and a product is taken as hi_a hi_b + hi_a lo_b + lo_a hi_b on
+// v_mfma_f32_16x16x32_bf16 with float32 accumulation (the dropped lo_a lo_b and the rounding of
+// lo leave a relative error near 2^-16 per product, against 2^-24 for float32 inputs, at a
+// third of the float32 MFMA's cycles per product).
+// LDS holds, per operand and half, rows of 32 contraction indices (bf16) at a pitch of 80 bytes,
+// so each MFMA operand read (16 bytes of 16 consecutive rows) is free of bank conflicts. Lane
+// group g of an MFMA supplies contraction indices 8g .. 8g + 7 on both operands.
 // Work item = (seq, head, output tile, split), split fastest.
 // ------------------------------------------------------------------------------------------------
+namespace {
+constexpr int kGPitch = 40;  // bf16 per LDS row: 32 contraction indices + 8 padding
+
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 b = (__bf16)x[e];
+    h[e] = b;
+    l[e] = (__bf16)(x[e] - (float)b);
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
+}  // namespace
+
 template <int KIND>
 __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
                                                   SeqTable T) {
-  constexpr int LA = KIND == 0 ? 36 : 80;
-  constexpr int ASZ = KIND == 0 ? 64 * 36 : 32 * 80;
-  constexpr int LB = 144;
-  __shared__ __attribute__((aligned(16))) float As[2][ASZ];
-  __shared__ __attribute__((aligned(16))) float Bs[2][32 * LB];
+  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][64 * kGPitch], Al[2][64 * kGPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Bh[2][128 * kGPitch], Bl[2][128 * kGPitch];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
@@ -438,45 +514,51 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   const int st0 = sp * per, st1 = min(nst, st0 + per);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
 
-  float4 ra[2], rb[4];
+  // staging assignment: A row ar (of 64), contraction indices 8 ac .. + 7; B column bd (of 128),
+  // contraction indices 16 bk .. + 15
+  const int ar = KIND == 0 ? tid >> 2 : tid & 63, ac = KIND == 0 ? tid & 3 : tid >> 6;
+  const int bd = tid & 127, bk = tid >> 7;
+  float ra[8], rb[16];
   auto load = [&](int stg) {
     const int k0 = stg * 32;
+    if constexpr (KIND == 0) {  // A = P_C[64 rows][32 keys], row-major in memory
+      const int r = tile * 64 + ar;
+      const float4* src = reinterpret_cast<const float4*>(PC + (int64_t)min(r, R - 1) * ldm + k0 + 8 * ac);
+      const float4 x0 = src[0], x1 = src[1];
+      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int idx = tid + 256 * c;
-      if constexpr (KIND == 0) {  // A = P_C[64 rows][32 keys]
-        const int row = idx >> 3, c4 = idx & 7, r = tile * 64 + row;
-        ra[c] = r < R ? *reinterpret_cast<const float4*>(PC + (int64_t)r * ldm + k0 + 4 * c4)
-                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      } else {  // A^T = P_C[32 rows][64 keys]
-        const int row = idx >> 4, c4 = idx & 15, r = k0 + row;
-        ra[c] = r < R ? *reinterpret_cast<const float4*>(PC + (int64_t)r * ldm + tile * 64 + 4 * c4)
-                      : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int e = 0; e < 8; ++e) ra[e] = r < R ? v[e] : 0.0f;
+    } else {  // A = P_C^T[64 keys][32 rows]: a column of P_C, one row per load (coalesced over keys)
+      const int j = tile * 64 + ar;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = k0 + 8 * ac + e;
+        const float x = PC[(int64_t)min(r, R - 1) * ldm + j];
+        ra[e] = r < R ? x : 0.0f;
       }
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + 256 * c;
-      const int row = idx >> 5, c4 = idx & 31, kk = k0 + row;
-      if constexpr (KIND == 0)  // B = Vc[32 keys][128]
-        rb[c] = kk < m ? *reinterpret_cast<const float4*>(vc + (int64_t)kk * kD + 4 * c4)
-                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-      else  // B = Z[32 rows][128]
-        rb[c] = kk < R ? *reinterpret_cast<const float4*>(Zh + (int64_t)kk * kD + 4 * c4)
-                       : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int e = 0; e < 16; ++e) {
+      const int kk = k0 + 16 * bk + e;
+      if constexpr (KIND == 0) {  // B = Vc[32 keys][128]
+        const float x = vc[(int64_t)min(kk, m - 1) * kD + bd];
+        rb[e] = kk < m ? x : 0.0f;
+      } else {  // B = Z[32 rows][128]
+        const float x = Zh[(int64_t)min(kk, R - 1) * kD + bd];
+        rb[e] = kk < R ? x : 0.0f;
+      }
     }
   };
   auto store = [&](int buf) {
+    u32x4 hi, lo;
+    split8(ra, hi, lo);
+    *reinterpret_cast<u32x4*>(&Ah[buf][ar * kGPitch + 8 * ac]) = hi;
+    *reinterpret_cast<u32x4*>(&Al[buf][ar * kGPitch + 8 * ac]) = lo;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int idx = tid + 256 * c;
-      const int off = KIND == 0 ? (idx >> 3) * LA + 4 * (idx & 7) : (idx >> 4) * LA + 4 * (idx & 15);
-      *reinterpret_cast<float4*>(&As[buf][off]) = ra[c];
-    }
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int idx = tid + 256 * c;
-      *reinterpret_cast<float4*>(&Bs[buf][(idx >> 5) * LB + 4 * (idx & 31)]) = rb[c];
+      split8(rb + 8 * c, hi, lo);
+      *reinterpret_cast<u32x4*>(&Bh[buf][bd * kGPitch + 16 * bk + 8 * c]) = hi;
+      *reinterpret_cast<u32x4*>(&Bl[buf][bd * kGPitch + 16 * bk + 8 * c]) = lo;
     }
   };
 
@@ -492,14 +574,17 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
       const int buf = (stg - st0) & 1;
       const bool more = stg + 1 < st1;
       if (more) load(stg + 1);
-      const float* as = As[buf];
-      const float* bs = Bs[buf];
+      const int ao = (16 * wave + c16) * kGPitch + 8 * g;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[buf][ao]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[buf][ao]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kk = 4 * e + g;
-        const float a = KIND == 0 ? as[(16 * wave + c16) * LA + kk] : as[kk * LA + 16 * wave + c16];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) acc[b] = mfma_f32(a, bs[kk * LB + 16 * b + c16], acc[b]);
+      for (int b = 0; b < 8; ++b) {
+        const int bo = (16 * b + c16) * kGPitch + 8 * g;
+        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[buf][bo]);
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[buf][bo]);
+        acc[b] = mfma16(ah, bh, acc[b]);
+        acc[b] = mfma16(ah, bl, acc[b]);
+        acc[b] = mfma16(al, bh, acc[b]);
       }
       if (more) store(buf ^ 1);
       __syncthreads();
@@ -660,14 +745,13 @@ int am_key_tiles(int m) { return (int)(pad64(m) / 64); }
 int am_stages_rows(int m) { return (int)(pad64(m) / 32); }
 int am_stages_cols(int R) { return (R + 31) / 32; }
 
-hipError_t launch_am_exp(int layout, bool all, const void* q, const void* k, const int32_t* table, int max_blocks,
-                         const int32_t* kept, const float* lse, float* ws, int64_t n_max, float scale, const AmCfg& C,
-                         const SeqTable& T, hipStream_t st) {
+hipError_t launch_am_exp(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
+                         const int32_t* kept, float* ws, int64_t n_max, float scale, const AmCfg& C, const SeqTable& T,
+                         hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
-  if (all) KVC_AM_LAYOUT(am_exp, KVC_COMMA true, qq, kk, table, max_blocks, kept, lse, ws, n_max, scale, C, T);
-  else KVC_AM_LAYOUT(am_exp, KVC_COMMA false, qq, kk, table, max_blocks, kept, lse, ws, n_max, scale, C, T);
+  KVC_AM_LAYOUT(am_exp, , qq, kk, table, max_blocks, kept, ws, n_max, scale, C, T);
   return hipGetLastError();
 }
 
@@ -707,11 +791,14 @@ hipError_t launch_am_eta(float* ws, const AmCfg& C, const SeqTable& T, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_am_target(int layout, const void* v, const int32_t* table, int max_blocks, float* ws,
-                            int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+hipError_t launch_am_target(int layout, const void* q, const void* k, const void* v, const int32_t* table,
+                            int max_blocks, const int32_t* vtable, int vmax_blocks, const float* lse, float* ws,
+                            int64_t n_max, float scale, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  const auto* qq = static_cast<const uint16_t*>(q);
+  const auto* kk = static_cast<const uint16_t*>(k);
   const auto* vv = static_cast<const uint16_t*>(v);
-  dim3 grid(T.total), block(256);
-  KVC_AM_LAYOUT(am_target, , vv, table, max_blocks, ws, n_max, C, T);
+  dim3 grid(T.total), block(kTgtThreads);
+  KVC_AM_LAYOUT(am_target, , qq, kk, vv, table, max_blocks, vtable, vmax_blocks, lse, ws, n_max, scale, C, T);
   return hipGetLastError();
 }
 

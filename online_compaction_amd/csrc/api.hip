@@ -50,16 +50,17 @@ int am_stages_rows(int m);
 int am_stages_cols(int R);
 hipError_t launch_am_stats(const float* lse, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_scale(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_exp(int layout, bool all, const void* q, const void* k, const int32_t* table, int max_blocks,
-                         const int32_t* kept, const float* lse, float* ws, int64_t n_max, float scale, const AmCfg& C,
-                         const SeqTable& T, hipStream_t st);
+hipError_t launch_am_exp(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
+                         const int32_t* kept, float* ws, int64_t n_max, float scale, const AmCfg& C, const SeqTable& T,
+                         hipStream_t st);
 hipError_t launch_am_rows_dot(const float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_cols_part(int mode, const float* w, const float* lse, float* ws, const AmCfg& C,
                                const SeqTable& T, hipStream_t st);
 hipError_t launch_am_cols_fin(int mode, float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_eta(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_target(int layout, const void* v, const int32_t* table, int max_blocks, float* ws,
-                            int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_target(int layout, const void* q, const void* k, const void* v, const int32_t* table,
+                            int max_blocks, const int32_t* vtable, int vmax_blocks, const float* lse, float* ws,
+                            int64_t n_max, float scale, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_split_sum(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_init(int layout, const void* v, const int32_t* table, int max_blocks, const int32_t* kept,
@@ -570,11 +571,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   auto ktiles = [&](int s) { return H * am_key_tiles(m[s]); };
   KVC_AM_STEP(units, launch_am_stats(lse_rows, amws, C, T, st));
   KVC_AM_STEP([&](int s) { return H * am_exp_items(R, m[s]); },
-              launch_am_exp(layout, false, q, k->data, k->block_table, k->max_blocks, kept, lse_rows, amws, nm,
-                            sh->scale, C, T, st));
-  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, sh->seq_lens[s]); },
-              launch_am_exp(layout, true, q, k->data, k->block_table, k->max_blocks, kept, lse_rows, amws, nm,
-                            sh->scale, C, T, st));
+              launch_am_exp(layout, q, k->data, k->block_table, k->max_blocks, kept, amws, nm, sh->scale, C, T, st));
   KVC_AM_STEP([&](int s) { return H * am_scale_items(R, m[s]); }, launch_am_scale(amws, C, T, st));
   KVC_AM_STEP(cparts, launch_am_cols_part(0, beta, lse_rows, amws, C, T, st));
   KVC_AM_STEP(cols, launch_am_cols_fin(0, beta, amws, C, T, st));
@@ -589,7 +586,8 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   KVC_AM_STEP(cparts, launch_am_cols_part(2, beta, lse_rows, amws, C, T, st));  // E becomes P_C
   KVC_AM_STEP(cols, launch_am_cols_fin(2, beta, amws, C, T, st));
   KVC_AM_STEP(units, launch_am_eta(amws, C, T, st));
-  KVC_AM_STEP(rtiles, launch_am_target(layout, v->data, v->block_table, v->max_blocks, amws, nm, C, T, st));
+  KVC_AM_STEP(rtiles, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
+                                       v->max_blocks, lse_rows, amws, nm, sh->scale, C, T, st));
   for (int it = 0; it < iters_v; ++it) {
     KVC_AM_STEP([&](int s) { return rtiles(s) * C.S1; }, launch_am_gemm(0, v_c, amws, C, T, st));
     if (C.S1 > 1) KVC_AM_STEP(rtiles, launch_am_split_sum(0, v_c, amws, C, T, st));

@@ -223,7 +223,10 @@ def test_attention_matching_validation(lib):
     sh = _shape()
     kv = A.KView(FAKE, A.KVC_BF16)
     m = [6600, 4000]
-    assert oc.kvc_am_workspace_size(sh, kv, kv, m, True) > 4 * 8 * 4096 * (6600 + 33000)
+    # the kept exponentials E are materialised ([H][R][m rounded up to 64] floats per sequence), the
+    # full attention weights are not
+    ws = oc.kvc_am_workspace_size(sh, kv, kv, m, True)
+    assert 4 * 8 * 4096 * (6656 + 4032) < ws < 4 * 8 * 4096 * (6600 + 33000)
     assert oc.kvc_am_workspace_size(sh, kv, kv, m, False) > oc.kvc_am_workspace_size(sh, kv, kv, m, True)
     assert oc.kvc_am_workspace_size(sh, A.KView(FAKE, A.KVC_F32), kv, m, True) == 0
     assert oc.kvc_am_workspace_size(_shape(G=1, q=8), kv, kv, m, True) == 0  # too few rows for MFMA
