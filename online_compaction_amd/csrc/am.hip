@@ -16,7 +16,8 @@
 // lowered to ME + 80 if the kept logits lie far below it). The updates are scale-equivariant:
 // with w' = exp(ME - Mz) w they are the updates of w = exp(beta) from w = 1 on the unscaled
 // exponentials, so w' starts at exp(ME - Mz) and beta = log w' - (ME - Mz). Once beta is fixed,
-// E is overwritten in place by P_C, which the value iterations then multiply from both sides.
+// E is overwritten in place by P_C and P_C^T is written beside it (PT), so both value products
+// read their left operand row by row.
 // The QK^T products use v_mfma_f32_16x16x32_bf16 on the stored bf16 rows; the solver products
 // use v_mfma_f32_16x16x4_f32 (float32 throughout); the vector products are plain VALU. Every
 // reduction has a fixed order (split sums land in partial buffers that one pass adds up in
@@ -25,7 +26,7 @@
 // Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], n = T.n[i],
 // ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 the split counts of the two value
 // products; every array starts on a 256-byte boundary):
-//   E [H][R][ldm] | Y [H][R][128] | Z [H][R][128] | Zp [S1 > 1 ? S1 : 0][H][R][128] |
+//   E [H][R][ldm] | PT [H][ldm][R] | Y [H][R][128] | Z [H][R][128] | Zp [S1 > 1 ? S1 : 0][H][R][128] |
 //   Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] | u [H][R] | b [H][ldm] |
 //   Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H]
 // Columns m .. ldm-1 of E hold zeros (logit -inf), so tiles never need a column bound on E.
@@ -47,7 +48,7 @@ constexpr int kRowChunk = 64;  // rows per partial column sum
 __host__ __device__ constexpr int64_t pad64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
 struct AmWs {
-  float *E, *Y, *Z, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
+  float *E, *PT, *Y, *Z, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
   uint32_t* mekey;
   int ldm;
 };
@@ -58,7 +59,8 @@ __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const
   AmWs w;
   w.ldm = (int)ldm;
   w.E = ws + T.off[i];
-  w.Y = w.E + pad64(H * R * ldm);
+  w.PT = w.E + pad64(H * R * ldm);
+  w.Y = w.PT + pad64(H * R * ldm);
   w.Z = w.Y + pad64(H * R * kD);
   w.Zp = w.Z + pad64(H * R * kD);
   w.Up = w.Zp + (C.S1 > 1 ? C.S1 : 0) * pad64(H * R * kD);
@@ -91,7 +93,7 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2) {
   const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
   const int64_t rk = pad64((int64_t)H * R * kD);
-  return pad64((int64_t)H * R * ldm) + 2 * rk + (S1 > 1 ? S1 : 0) * rk +
+  return 2 * pad64((int64_t)H * R * ldm) + 2 * rk + (S1 > 1 ? S1 : 0) * rk +
          (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) + pad64((int64_t)H * R) +
          pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H);
 }
@@ -237,8 +239,9 @@ __global__ __launch_bounds__(256) void am_rows_dot(const float* __restrict__ w_a
 // thread per column, rows in order), then the chunks added in order per column. With
 //   MODE 0: r_i = exp(LSE_i - M)       -> b_j = g_j                          (E^T z, once)
 //   MODE 1: r_i = u_i = (E w)_i        -> w_j <- w_j b_j / g_j, 0 if g_j = 0 (one NNLS step)
-//   MODE 2: r_i = 1 / u_i              -> E_ij <- E_ij w_j / u_i in place (E becomes P_C) and
-//                                         b_j = sum_i (P_C)_ij (column sums, for the step size)
+//   MODE 2: r_i = 1 / u_i              -> E_ij <- E_ij w_j / u_i in place (E becomes P_C),
+//                                         b_j = sum_i (P_C)_ij (column sums, for the step size),
+//                                         and P_C^T written to PT
 // Partial work item = (seq, head, 256 columns, 64-row chunk); final = (seq, head, 256 columns).
 // ------------------------------------------------------------------------------------------------
 template <int MODE>
@@ -256,28 +259,47 @@ __global__ __launch_bounds__(256) void am_cols_part(const float* __restrict__ w_
   local /= nr;
   const int cb = local % cb_n, h = local / cb_n;
   const int j = cb * 256 + threadIdx.x;
-  if (j >= ldm) return;
   const int64_t unit = (int64_t)s * C.H + h;
-  float* e = W.E + (int64_t)h * R * ldm + j;
-  const float* u = W.u + (int64_t)h * R;
-  const float* lu = lse + unit * R;
-  const float M = W.M[h];
-  const float wj = (MODE == 2 && j < m) ? w_all[unit * C.m_max + j] : 0.0f;
   const int r0 = rc * kRowChunk, r1 = min(R, r0 + kRowChunk);
-  float acc = 0.0f;
-  for (int r = r0; r < r1; ++r) {
-    const float x = e[(int64_t)r * ldm];
-    if constexpr (MODE == 0) {
-      acc = __builtin_fmaf(x, __builtin_amdgcn_exp2f((lu[r] - M) * kLog2e), acc);
-    } else if constexpr (MODE == 1) {
-      acc = __builtin_fmaf(x, u[r], acc);
-    } else {
-      const float pc = u[r] > 0.0f ? x * wj / u[r] : 0.0f;
-      if (j < m) e[(int64_t)r * ldm] = pc;
-      acc += pc;
+  if constexpr (MODE == 2) {
+    // P_C in place of E, its column sums, and P_C^T (row j of PT holds column j): the chunk's
+    // 64 x 256 block of P_C is staged in LDS (row pitch 257: a column read is conflict-free),
+    // then each wave writes 64 PT rows, 64 consecutive floats each.
+    __shared__ float tile[kRowChunk][257];
+    float acc = 0.0f;
+    if (j < ldm) {
+      float* e = W.E + (int64_t)h * R * ldm + j;
+      const float* u = W.u + (int64_t)h * R;
+      const float wj = j < m ? w_all[unit * C.m_max + j] : 0.0f;
+      for (int r = r0; r < r1; ++r) {
+        const float x = e[(int64_t)r * ldm];
+        const float pc = u[r] > 0.0f ? x * wj / u[r] : 0.0f;
+        if (j < m) e[(int64_t)r * ldm] = pc;
+        tile[r - r0][threadIdx.x] = pc;
+        acc += pc;
+      }
+      W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
     }
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int c = wave; c < 256; c += 4) {
+      const int jj = cb * 256 + c;
+      if (jj < ldm && r0 + lane < r1) W.PT[((int64_t)h * ldm + jj) * R + r0 + lane] = tile[lane][c];
+    }
+  } else {
+    if (j >= ldm) return;
+    const float* e = W.E + (int64_t)h * R * ldm + j;
+    const float* u = W.u + (int64_t)h * R;
+    const float* lu = lse + unit * R;
+    const float M = W.M[h];
+    float acc = 0.0f;
+    for (int r = r0; r < r1; ++r) {
+      const float x = e[(int64_t)r * ldm];
+      if constexpr (MODE == 0) acc = __builtin_fmaf(x, __builtin_amdgcn_exp2f((lu[r] - M) * kLog2e), acc);
+      else acc = __builtin_fmaf(x, u[r], acc);
+    }
+    W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
   }
-  W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
 }
 
 template <int MODE>
@@ -456,10 +478,10 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 }
 
 // ------------------------------------------------------------------------------------------------
-// The two products of a Landweber step, one 64 x 128 output tile per workgroup (each wave 16 x
-// 128, eight 16 x 16 accumulators), the contraction in stages of 32 through double-buffered LDS
-// with the next stage's global loads in flight during the current stage's MFMAs, and split over
-// S workgroups whose partial tiles a second pass adds in order:
+// The two products of a Landweber step, one 128 x 128 output tile per workgroup (four waves in a
+// 2 x 2 grid, each 64 x 64: sixteen 16 x 16 accumulators), the contraction in stages of 32
+// through double-buffered LDS with the next stage's global loads in flight during the current
+// stage's MFMAs, and split over S workgroups whose partial tiles a second pass adds in order:
 //   KIND 0: Z = P_C Vc - Y          (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
 //   KIND 1: Vc -= eta P_C^T Z        (columns of P_C, contraction over rows)    -> Vc, or partials Up
 // The float32 operands are split when they are staged: x = hi + lo with hi = bf16(x) and
@@ -467,13 +489,14 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation (the dropped lo_a lo_b and the rounding of
 // lo leave a relative error near 2^-16 per product, against 2^-24 for float32 inputs, at a
 // third of the float32 MFMA's cycles per product).
-// LDS holds, per operand and half, rows of 32 contraction indices (bf16) at a pitch of 80 bytes,
-// so each MFMA operand read (16 bytes of 16 consecutive rows) is free of bank conflicts. Lane
-// group g of an MFMA supplies contraction indices 8g .. 8g + 7 on both operands.
+// LDS holds, per operand and half, 128 rows of 32 contraction indices (bf16, 64 bytes per row);
+// 16-byte chunk c of row r sits at chunk position c ^ ((r >> 1) & 3), so each MFMA operand read
+// (chunk g of 16 consecutive rows) is free of bank conflicts. Lane group g of an MFMA supplies
+// contraction indices 8g .. 8g + 7 on both operands.
 // Work item = (seq, head, output tile, split), split fastest.
 // ------------------------------------------------------------------------------------------------
 namespace {
-constexpr int kGPitch = 40;  // bf16 per LDS row: 32 contraction indices + 8 padding
+constexpr int kGTile = 128;
 
 __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   bf16x8 h, l;
@@ -486,13 +509,15 @@ __device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
   hi = __builtin_bit_cast(u32x4, h);
   lo = __builtin_bit_cast(u32x4, l);
 }
+
+__device__ __forceinline__ int gswz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 }  // namespace
 
 template <int KIND>
 __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
                                                   SeqTable T) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ah[2][64 * kGPitch], Al[2][64 * kGPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Bh[2][128 * kGPitch], Bl[2][128 * kGPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t Ah[2][kGTile * 64], Al[2][kGTile * 64];
+  __shared__ __attribute__((aligned(16))) uint8_t Bh[2][kGTile * 64], Bl[2][kGTile * 64];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
@@ -500,41 +525,61 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   AmWs W = am_ws(ws, T, i, C);
   const int ldm = W.ldm;
   const int S = KIND == 0 ? C.S1 : C.S2;
-  const int tiles = KIND == 0 ? (R + 63) / 64 : ldm / 64;
+  const int rows = KIND == 0 ? R : ldm;  // output rows
+  const int tiles = (rows + kGTile - 1) / kGTile;
   int local = t - T.start[i];
   const int sp = local % S;
   local /= S;
   const int tile = local % tiles, h = local / tiles;
   const int64_t unit = (int64_t)s * C.H + h;
   const float* PC = W.E + (int64_t)h * R * ldm;
+  const float* PTh = W.PT + (int64_t)h * ldm * R;
   const float* vc = vc_all + unit * C.m_max * (int64_t)kD;
   const float* Zh = W.Z + (int64_t)h * R * kD;
   const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
   const int per = (nst + S - 1) / S;
   const int st0 = sp * per, st1 = min(nst, st0 + per);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int wr = wave >> 1, wc = wave & 1;
 
-  // staging assignment: A row ar (of 64), contraction indices 8 ac .. + 7; B column bd (of 128),
-  // contraction indices 16 bk .. + 15
-  const int ar = KIND == 0 ? tid >> 2 : tid & 63, ac = KIND == 0 ? tid & 3 : tid >> 6;
+  // staging: A row ar of the tile, contraction indices 16 ak .. + 15; B column bd, indices
+  // 16 bk .. + 15 (chunks 2 ak, 2 ak + 1 and 2 bk, 2 bk + 1)
+  const int ar = tid >> 1, ak = tid & 1;
   const int bd = tid & 127, bk = tid >> 7;
-  float ra[8], rb[16];
+  float ra[16], rb[16];
   auto load = [&](int stg) {
     const int k0 = stg * 32;
-    if constexpr (KIND == 0) {  // A = P_C[64 rows][32 keys], row-major in memory
-      const int r = tile * 64 + ar;
-      const float4* src = reinterpret_cast<const float4*>(PC + (int64_t)min(r, R - 1) * ldm + k0 + 8 * ac);
-      const float4 x0 = src[0], x1 = src[1];
-      const float v[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if constexpr (KIND == 0) {  // A = P_C[128 rows][32 keys], row-major in memory
+      const int r = tile * kGTile + ar;
+      const float4* src = reinterpret_cast<const float4*>(PC + (int64_t)min(r, R - 1) * ldm + k0 + 16 * ak);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ra[e] = r < R ? v[e] : 0.0f;
-    } else {  // A = P_C^T[64 keys][32 rows]: a column of P_C, one row per load (coalesced over keys)
-      const int j = tile * 64 + ar;
+      for (int c = 0; c < 4; ++c) {
+        const float4 x = src[c];
+        ra[4 * c] = r < R ? x.x : 0.0f;
+        ra[4 * c + 1] = r < R ? x.y : 0.0f;
+        ra[4 * c + 2] = r < R ? x.z : 0.0f;
+        ra[4 * c + 3] = r < R ? x.w : 0.0f;
+      }
+    } else {  // A = P_C^T[128 keys][32 rows], row-major in PT
+      const int j = tile * kGTile + ar;
+      const int r0 = k0 + 16 * ak;
+      const float* src = PTh + (int64_t)min(j, ldm - 1) * R;
+      if (r0 + 16 <= R && (R & 3) == 0) {  // whole, 16-byte aligned row segment
+        const float4* s4 = reinterpret_cast<const float4*>(src + r0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = k0 + 8 * ac + e;
-        const float x = PC[(int64_t)min(r, R - 1) * ldm + j];
-        ra[e] = r < R ? x : 0.0f;
+        for (int c = 0; c < 4; ++c) {
+          const float4 x = s4[c];
+          ra[4 * c] = j < ldm ? x.x : 0.0f;
+          ra[4 * c + 1] = j < ldm ? x.y : 0.0f;
+          ra[4 * c + 2] = j < ldm ? x.z : 0.0f;
+          ra[4 * c + 3] = j < ldm ? x.w : 0.0f;
+        }
+      } else {  // the last, partial stage of rows (or rows of a length not a multiple of 4)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float x = src[min(r0 + e, R - 1)];
+          ra[e] = (r0 + e < R && j < ldm) ? x : 0.0f;
+        }
       }
     }
 #pragma unroll
@@ -551,20 +596,22 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   };
   auto store = [&](int buf) {
     u32x4 hi, lo;
-    split8(ra, hi, lo);
-    *reinterpret_cast<u32x4*>(&Ah[buf][ar * kGPitch + 8 * ac]) = hi;
-    *reinterpret_cast<u32x4*>(&Al[buf][ar * kGPitch + 8 * ac]) = lo;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      split8(ra + 8 * c, hi, lo);
+      *reinterpret_cast<u32x4*>(&Ah[buf][gswz(ar, 2 * ak + c)]) = hi;
+      *reinterpret_cast<u32x4*>(&Al[buf][gswz(ar, 2 * ak + c)]) = lo;
       split8(rb + 8 * c, hi, lo);
-      *reinterpret_cast<u32x4*>(&Bh[buf][bd * kGPitch + 16 * bk + 8 * c]) = hi;
-      *reinterpret_cast<u32x4*>(&Bl[buf][bd * kGPitch + 16 * bk + 8 * c]) = lo;
+      *reinterpret_cast<u32x4*>(&Bh[buf][gswz(bd, 2 * bk + c)]) = hi;
+      *reinterpret_cast<u32x4*>(&Bl[buf][gswz(bd, 2 * bk + c)]) = lo;
     }
   };
 
-  f32x4 acc[8];
+  f32x4 acc[4][4];
 #pragma unroll
-  for (int b = 0; b < 8; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (st0 < st1) {
     load(st0);
     store(0);
@@ -574,53 +621,57 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
       const int buf = (stg - st0) & 1;
       const bool more = stg + 1 < st1;
       if (more) load(stg + 1);
-      const int ao = (16 * wave + c16) * kGPitch + 8 * g;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[buf][ao]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[buf][ao]);
+      bf16x8 bh[4], bl[4];
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int bo = (16 * b + c16) * kGPitch + 8 * g;
-        const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[buf][bo]);
-        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[buf][bo]);
-        acc[b] = mfma16(ah, bh, acc[b]);
-        acc[b] = mfma16(ah, bl, acc[b]);
-        acc[b] = mfma16(al, bh, acc[b]);
+      for (int b = 0; b < 4; ++b) {
+        const int o = gswz(64 * wc + 16 * b + c16, g);
+        bh[b] = *reinterpret_cast<const bf16x8*>(&Bh[buf][o]);
+        bl[b] = *reinterpret_cast<const bf16x8*>(&Bl[buf][o]);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int o = gswz(64 * wr + 16 * a + c16, g);
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[buf][o]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[buf][o]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          acc[a][b] = mfma16(ah, bh[b], acc[a][b]);
+          acc[a][b] = mfma16(ah, bl[b], acc[a][b]);
+          acc[a][b] = mfma16(al, bh[b], acc[a][b]);
+        }
       }
       if (more) store(buf ^ 1);
       __syncthreads();
     }
   }
 
-  if constexpr (KIND == 0) {
-    const int64_t hofs = (int64_t)h * R * kD;
-    float* out = (S == 1 ? W.Z : W.Zp + (int64_t)sp * pad64((int64_t)C.H * R * kD)) + hofs;
-    const float* y = W.Y + hofs;
 #pragma unroll
-    for (int b = 0; b < 8; ++b)
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = tile * 64 + 16 * wave + 4 * g + e;
-        const int64_t o = (int64_t)r * kD + 16 * b + c16;
-        if (r < R) out[o] = S == 1 ? acc[b][e] - y[o] : acc[b][e];
-      }
-  } else {
-    const float eta = W.eta[h];
-    float* vcw = vc_all + unit * C.m_max * (int64_t)kD;
-    float* up = W.Up + (int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD;
-#pragma unroll
-    for (int b = 0; b < 8; ++b)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = tile * 64 + 16 * wave + 4 * g + e;
-        const int64_t o = (int64_t)j * kD + 16 * b + c16;
-        if (S == 1) {
-          if (j < m) vcw[o] -= eta * acc[b][e];
+        const int r = tile * kGTile + 64 * wr + 16 * a + 4 * g + e;
+        const int col = 64 * wc + 16 * b + c16;
+        if constexpr (KIND == 0) {
+          const int64_t o = (int64_t)h * R * kD + (int64_t)r * kD + col;
+          if (r < R) {
+            if (S == 1) W.Z[o] = acc[a][b][e] - W.Y[o];
+            else W.Zp[(int64_t)sp * pad64((int64_t)C.H * R * kD) + o] = acc[a][b][e];
+          }
         } else {
-          up[o] = acc[b][e];
+          const int64_t o = (int64_t)r * kD + col;
+          if (S == 1) {
+            if (r < m) vc_all[unit * C.m_max * (int64_t)kD + o] -= W.eta[h] * acc[a][b][e];
+          } else if (r < ldm) {
+            W.Up[(int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD + o] = acc[a][b][e];
+          }
         }
       }
-  }
 }
+
+// Output tiles of the Landweber products: KIND 0 over the R rows, KIND 1 over the ldm kept keys.
+int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 
 // Split sums, in split order: Z = sum_s Zp[s] - Y (KIND 0, work item = (seq, head, 64 rows)) and
 // Vc_j -= eta sum_s Up[s]_j (KIND 1, work item = (seq, head, 64 kept keys)).

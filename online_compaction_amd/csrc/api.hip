@@ -46,6 +46,7 @@ int am_dot_row_items(int R);
 int am_col_items(int m);
 int am_col_part_items(int R, int m);
 int am_key_tiles(int m);
+int am_gemm_tiles(int rows);
 int am_stages_rows(int m);
 int am_stages_cols(int R);
 hipError_t launch_am_stats(const float* lse, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
@@ -467,25 +468,32 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
 // ------------------------------------------------------------------------------------------------
 // Attention Matching
 // ------------------------------------------------------------------------------------------------
-// Split counts of the two value products: enough workgroups for about four per CU over the
-// batch (at most 8 splits, at least 4 stages of 32 per split). A function of the shape alone, so
-// that the workspace size and the fit agree.
+// Split counts of the two value products (at most 8 splits, at least 4 stages of 32 per split).
+// A function of the shape alone, so that the workspace size and the fit agree.
 static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2) {
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
   int64_t t1 = 0, t2 = 0;
   int st1 = INT32_MAX, st2 = am_stages_cols(R);
   for (int s = 0; s < sh->num_seqs; ++s) {
     if (m[s] == 0) continue;
-    t1 += (int64_t)H * am_row_tiles(R);
-    t2 += (int64_t)H * am_key_tiles(m[s]);
+    t1 += (int64_t)H * am_gemm_tiles(R);
+    t2 += (int64_t)H * am_gemm_tiles((m[s] + 63) / 64 * 64);
     st1 = std::min(st1, am_stages_rows(m[s]));
   }
+  // the split count that needs the fewest rounds of workgroups (two per CU) times stages per
+  // split, fewer splits on a tie
   auto pick = [](int64_t tiles, int stages) {
     if (tiles == 0) return 1;
-    int64_t sp = (1024 + tiles - 1) / tiles;
-    sp = std::min<int64_t>(sp, 8);
-    sp = std::min<int64_t>(sp, std::max(1, stages / 4));
-    return (int)std::max<int64_t>(sp, 1);
+    int best = 1;
+    int64_t best_cost = INT64_MAX;
+    for (int sp = 1; sp <= 8 && sp <= std::max(1, stages / 4); ++sp) {
+      const int64_t rounds = (tiles * sp + 511) / 512, per = (stages + sp - 1) / sp;
+      if (rounds * per < best_cost) {
+        best_cost = rounds * per;
+        best = sp;
+      }
+    }
+    return best;
   };
   *S1 = pick(t1, st1);
   *S2 = pick(t2, st2);
@@ -589,9 +597,10 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   KVC_AM_STEP(rtiles, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
                                        v->max_blocks, lse_rows, amws, nm, sh->scale, C, T, st));
   for (int it = 0; it < iters_v; ++it) {
-    KVC_AM_STEP([&](int s) { return rtiles(s) * C.S1; }, launch_am_gemm(0, v_c, amws, C, T, st));
+    KVC_AM_STEP([&](int) { return H * am_gemm_tiles(R) * C.S1; }, launch_am_gemm(0, v_c, amws, C, T, st));
     if (C.S1 > 1) KVC_AM_STEP(rtiles, launch_am_split_sum(0, v_c, amws, C, T, st));
-    KVC_AM_STEP([&](int s) { return ktiles(s) * C.S2; }, launch_am_gemm(1, v_c, amws, C, T, st));
+    KVC_AM_STEP([&](int s) { return H * am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; },
+                launch_am_gemm(1, v_c, amws, C, T, st));
     if (C.S2 > 1) KVC_AM_STEP(ktiles, launch_am_split_sum(1, v_c, amws, C, T, st));
   }
   KVC_AM_STEP(cols, launch_am_finish(beta, amws, C, T, st));
