@@ -230,7 +230,10 @@ kvc_status kvc_evict_redirect(const kvc_shape* shape, const int32_t* kept, const
  *   V_C:  iters_v Landweber steps V <- V - eta P^T (P V - Y) from the kept keys' stored values,
  *         P = the compacted attention softmax(Q K_C^T + beta), Y = softmax(Q K^T) V, and
  *         eta = 1 / max_j sum_i P_ij (stable: eta ||P||_2^2 <= 1).
- * Everything is float32 on the GPU (the QK^T products on bf16 MFMA with float32 accumulation).
+ * Arithmetic on the GPU: the QK^T products on bf16 MFMA with float32 accumulation; every other
+ * quantity float32, with the two matrix products of the value fit (and P V of the target) taken as
+ * bf16 MFMA products of float32 operands split into two bf16 halves each (hi = bf16(x),
+ * lo = bf16(x - hi); hi hi + hi lo + lo hi, relative error near 2^-16 per product).
  *   q          device [S][H*G][q][d] bf16;  G * q >= 16 (else KVC_ERR_UNSUPPORTED)
  *   k, v       key and value views, bf16, both contiguous or both paged (no slot maps)
  *   lse        device [S][H*G][q] LSE over the n_s keys, or NULL to compute it (in ws)
@@ -239,9 +242,9 @@ kvc_status kvc_evict_redirect(const kvc_shape* shape, const int32_t* kept, const
  *   beta       device out [S][H][m_max] float32 (natural-log bias per kept key)
  *   v_c        device out [S][H][m_max][d] float32
  *   ws         device workspace of kvc_am_workspace_size(shape, k, v, m, lse != NULL) bytes:
- *              at most about 4 * H * (R * (m_s + n_s + 10 d) + 8 m_s d) bytes per sequence (the
- *              kept and the full exponentials are materialised, plus up to 8 split partial
- *              sums of each value product)
+ *              at most about 4 * H * (R * (2 m_s + 10 d) + 8 m_s d) bytes per sequence (the kept
+ *              exponentials and their transpose are materialised, plus up to 8 split partial
+ *              sums of each value product; the attention over all n_s keys is not stored)
  * ------------------------------------------------------------------------------------------- */
 size_t kvc_am_workspace_size(const kvc_shape* shape, const kvc_kv_view* k, const kvc_kv_view* v, const int32_t* m,
                              int lse_supplied);

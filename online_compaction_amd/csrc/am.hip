@@ -351,17 +351,30 @@ __global__ __launch_bounds__(256) void am_eta(float* __restrict__ ws, AmCfg C, S
 // Target Y = P V with P_ij = exp(c q_i . k_j - LSE_i) over all n keys, without materialising P
 // (the weights of one 64-key chunk exist only in registers and a per-wave LDS tile).
 // Work item = (seq, head, 64-row tile), 8 waves: wave w owns rows 16 (w % 4) .. + 15 of the tile
-// and output columns 64 (w / 4) .. + 63 (the two halves recompute the same weights, which cost
-// 1/16 of the float32 product). Per 64-key chunk, staged through double-buffered LDS (keys as
-// bf16 rows, chunk c of row r at c ^ (r & 15); values widened to float32 rows):
+// and output columns 64 (w / 4) .. + 63 (the two halves recompute the same weights, a small
+// part of the work). Per 64-key chunk, staged through double-buffered LDS (keys as bf16 rows,
+// chunk c of row r at c ^ (r & 15); values transposed, one bf16 row of 64 keys per column):
 //   S = Q K^T     16 v_mfma_f32_16x16x32_bf16 (the wave's query rows stay in registers),
 //   P = exp2(S c log2(e) - LSE log2(e)), 0 for keys past n, through LDS into the A layout,
-//   Y += P V      64 v_mfma_f32_16x16x4_f32.
+//   Y += P V      P split as hi + lo (bf16 each; V is bf16 already, so the two products
+//                 P_hi V + P_lo V carry P to a relative 2^-16), 16 v_mfma_f32_16x16x32_bf16.
 // ------------------------------------------------------------------------------------------------
 namespace {
 constexpr int kTgtThreads = 512;
-constexpr int kVPitch = 132;  // float32 value row pitch in LDS
-constexpr int kPPitch = 68;   // per-wave weight tile pitch
+constexpr int kVtPitch = 72;  // bf16 per transposed value row (64 keys + 8 padding)
+constexpr int kPPitch = 68;   // per-wave weight tile pitch (float32)
+
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 b = (__bf16)x[e];
+    h[e] = b;
+    l[e] = (__bf16)(x[e] - (float)b);
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
 }  // namespace
 
 template <int LAYOUT>
@@ -373,7 +386,7 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
                                                             const float* __restrict__ lse, float* __restrict__ ws,
                                                             int64_t n_max, float scale, AmCfg C, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][64 * 256];
-  __shared__ __attribute__((aligned(16))) float Vs[2][64 * kVPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kD * kVtPitch];
   __shared__ __attribute__((aligned(16))) float Ps[8][16 * kPPitch];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
@@ -405,8 +418,7 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
   for (int e = 0; e < 4; ++e) lb[e] = lse[unit * R + min(rt * 64 + 16 * rw + 4 * g + e, R - 1)] * kLog2e;
   const float cl = scale * kLog2e;
 
-  // chunk staging: thread tid moves 16-byte piece tid & 15 (and tid & 15 + 16 for the second
-  // half of the key row set) of key row tid >> 4 (0 .. 31) and of key row 32 + (tid >> 4)
+  // chunk staging: thread tid moves 16-byte piece tid & 15 of key rows tid >> 4 and 32 + (tid >> 4)
   u32x4 kr[2], vr[2];
   auto load = [&](int c0) {
 #pragma unroll
@@ -423,9 +435,11 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
       const int key = x * 32 + (tid >> 4), ch = tid & 15;
       *reinterpret_cast<u32x4*>(&Ks[buf][swz(key, ch)]) = kr[x];
       const uint32_t wd[4] = {vr[x].x, vr[x].y, vr[x].z, vr[x].w};
-      float4* vd = reinterpret_cast<float4*>(&Vs[buf][key * kVPitch + 8 * ch]);
-      vd[0] = make_float4(bf16_lo(wd[0]), bf16_hi(wd[0]), bf16_lo(wd[1]), bf16_hi(wd[1]));
-      vd[1] = make_float4(bf16_lo(wd[2]), bf16_hi(wd[2]), bf16_lo(wd[3]), bf16_hi(wd[3]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {  // values d = 8 ch + 2 e, 8 ch + 2 e + 1 of this key
+        Vt[buf][(8 * ch + 2 * e) * kVtPitch + key] = (uint16_t)(wd[e] & 0xffffu);
+        Vt[buf][(8 * ch + 2 * e + 1) * kVtPitch + key] = (uint16_t)(wd[e] >> 16);
+      }
     }
   };
 
@@ -456,13 +470,21 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
         pw[(4 * g + e) * kPPitch + 16 * sub + c16] =
             live ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], cl, -lb[e])) : 0.0f;
     }
-    // Y += P V over the 64 keys: step kk takes keys 4 kk + g (A from the weight tile, B from V)
-    const float* vb = Vs[buf];
+    // Y += P V over the 64 keys in two steps of 32: lane group g takes keys 32 ks + 8 g .. + 7
+    const uint16_t* vb = Vt[buf];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      const float a = pw[c16 * kPPitch + 4 * kk + g];
+    for (int ks = 0; ks < 2; ++ks) {
+      const float4* pr = reinterpret_cast<const float4*>(&pw[c16 * kPPitch + 32 * ks + 8 * g]);
+      const float4 p0 = pr[0], p1 = pr[1];
+      const float px[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+      u32x4 ph, pl;
+      split8(px, ph, pl);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) acc[b] = mfma_f32(a, vb[(4 * kk + g) * kVPitch + 64 * dh + 16 * b + c16], acc[b]);
+      for (int b = 0; b < 4; ++b) {
+        const bf16x8 vb8 = *reinterpret_cast<const bf16x8*>(&vb[(64 * dh + 16 * b + c16) * kVtPitch + 32 * ks + 8 * g]);
+        acc[b] = mfma16(as_bf16x8(ph), vb8, acc[b]);
+        acc[b] = mfma16(as_bf16x8(pl), vb8, acc[b]);
+      }
     }
     if (more) store(buf ^ 1);
     __syncthreads();
@@ -497,18 +519,6 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 // ------------------------------------------------------------------------------------------------
 namespace {
 constexpr int kGTile = 128;
-
-__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
-  bf16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 b = (__bf16)x[e];
-    h[e] = b;
-    l[e] = (__bf16)(x[e] - (float)b);
-  }
-  hi = __builtin_bit_cast(u32x4, h);
-  lo = __builtin_bit_cast(u32x4, l);
-}
 
 __device__ __forceinline__ int gswz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
 }  // namespace
