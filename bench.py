@@ -242,6 +242,41 @@ def traffic_from_profile(launch_s: float):
         return None
 
 
+def measured_ceilings() -> dict:
+    """What the box reaches outside this library, for context beside the spec peaks: a plain
+    1 GiB device-to-device copy (torch; read + write bytes per second) and a square bf16 matrix
+    product of 8192 (torch.mm on contiguous operands, float32 accumulation). Timed after the
+    benchmark's own timed region, a few repetitions each."""
+    import torch
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_gbps"] = 2.0 * (1 << 30) * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16).contiguous()
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        c = torch.mm(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    out["bf16_matmul_tflops"] = 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -253,6 +288,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="approximate CPU baseline budget")
     ap.add_argument("--am-iters", type=int, nargs=2, default=(32, 32), metavar=("BETA", "V"),
                     help="Attention Matching: multiplicative bias updates and Landweber value steps")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the copy / matmul ceiling measurement after the timed region")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this size (HBM counter calibration)")
     args = ap.parse_args()
@@ -471,6 +508,11 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if not args.no_ceilings:
+        line["ceilings"] = measured_ceilings()
+        log(f"[bench] measured ceilings: device copy {line['ceilings']['copy_gbps']:.0f} GB/s, "
+            f"bf16 matmul {line['ceilings']['bf16_matmul_tflops']:.0f} TFLOP/s "
+            f"(spec {HBM_PEAK_GBPS:.0f} GB/s, {MFMA_BF16_PEAK_TFLOPS:.0f} TFLOP/s)")
     print(json.dumps(line), flush=True)
 
 

@@ -32,6 +32,168 @@ __device__ __forceinline__ u64 qmass(uint32_t bits) {
 }
 }  // namespace
 
+// Register-resident variant for n <= 1024 K: thread t holds the mass bits of positions
+// t + 1024 k (k < K), read once with all K loads in flight (clamped into the row, so every load
+// is in bounds; positions past n hold 0, which carries no mass and never reaches the
+// threshold, whose integer mass is positive). The passes run on registers; the state update
+// reads and writes the same positions. When the entries equal to T number at most `need` (the
+// count the last pass leaves in T's bin), all of them are hits and no ranking is needed;
+// otherwise the ties are ranked in position order from per-slice ballot counts.
+template <int K>
+__global__ __launch_bounds__(kThreads) void lrfu_update_reg(const float* __restrict__ mass, float* __restrict__ state,
+                                                            int32_t* __restrict__ counts, int H, int64_t n_max,
+                                                            double top_p, float decay, SeqTable T) {
+  __shared__ uint32_t hcnt[kBins];
+  __shared__ u64 hmass[kBins];
+  __shared__ uint32_t wsum[kWaves];
+  __shared__ u64 wsum64[kWaves];
+  __shared__ uint32_t sel_bin, sel_cnt, sel_eq;
+  __shared__ u64 sel_mass;
+  __shared__ uint32_t eqcnt[K * kWaves];
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int n = T.n[i];
+  const int s = T.first + i;
+  const int h = t - T.start[i];
+  const int64_t unit = (int64_t)s * H + h;
+  const uint32_t* mu = reinterpret_cast<const uint32_t*>(mass + unit * n_max);
+  float* su = state + unit * n_max;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // buffer loads: one scalar resource for the row, a 32-bit offset per lane
+  const __amdgpu_buffer_rsrc_t row = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint32_t*>(mu), (short)0,
+                                                                       n * 4, 0x00020000);
+  uint32_t u[K];
+#pragma unroll
+  for (int k = 0; k < K; ++k) {
+    const int j = tid + k * kThreads;
+    const uint32_t x = __builtin_amdgcn_raw_buffer_load_b32(row, min(j, n - 1) * 4, 0, 0);
+    u[k] = j < n ? x : 0u;
+  }
+  u64 part = 0;
+#pragma unroll
+  for (int k = 0; k < K; ++k) part += qmass(u[k]);
+#pragma unroll
+  for (int k = 0; k < K; ++k) asm volatile("" : "+v"(u[k]));
+  u64 total;
+  (void)block_excl_scan<kWaves>(part, total, wsum64);
+  const u64 target = total == 0 ? 0ull : (u64)ceil(top_p * (double)total);
+
+  uint32_t thr = 0xffffffffu;  // no entry compares above it
+  uint32_t need = 0, above = 0, ties = 0;
+  if (target > 0) {
+    uint32_t prefix = 0, pmask = 0;
+    u64 want = target;
+#pragma unroll 1
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
+      const uint32_t dmask = pass < 2 ? 0x7ffu : 0x3ffu;
+      for (int b = tid; b < kBins; b += kThreads) {
+        hcnt[b] = 0u;
+        hmass[b] = 0ull;
+      }
+      __syncthreads();
+      // opaque to the optimiser, so that the integer masses are formed per pass instead of being
+      // hoisted out of the pass loop (K 64-bit values would not fit the register budget)
+#pragma unroll
+      for (int k = 0; k < K; ++k) asm volatile("" : "+v"(u[k]));
+#pragma unroll
+      for (int k = 0; k < K; ++k)
+        if ((u[k] & pmask) == prefix && u[k] != 0u) {
+          const uint32_t b = (u[k] >> shift) & dmask;
+          atomicAdd(&hcnt[b], 1u);
+          atomicAdd(&hmass[b], qmass(u[k]));
+        }
+      __syncthreads();
+      const int b0 = 2 * (kThreads - 1 - tid);
+      const u64 m0 = hmass[b0], m1 = hmass[b0 + 1];
+      const uint32_t c0 = hcnt[b0], c1 = hcnt[b0 + 1];
+      u64 mtot;
+      uint32_t ctot;
+      const u64 above_m = block_excl_scan<kWaves>(m0 + m1, mtot, wsum64);
+      const uint32_t above_c = block_excl_scan<kWaves>(c0 + c1, ctot, wsum);
+      const u64 ge1 = above_m + m1, ge0 = ge1 + m0;
+      if (tid == 0) {
+        sel_bin = 0u;
+        sel_cnt = 0u;
+        sel_mass = 0ull;
+        sel_eq = 0u;
+      }
+      __syncthreads();
+      if (above_m < want && ge1 >= want) {
+        sel_bin = (uint32_t)(b0 + 1);
+        sel_mass = above_m;
+        sel_cnt = above_c;
+        sel_eq = c1;
+      } else if (ge1 < want && ge0 >= want) {
+        sel_bin = (uint32_t)b0;
+        sel_mass = ge1;
+        sel_cnt = above_c + c1;
+        sel_eq = c0;
+      }
+      __syncthreads();
+      want -= sel_mass;
+      above += sel_cnt;
+      ties = sel_eq;  // after the last pass: the entries whose bits equal T
+      prefix |= sel_bin << shift;
+      pmask |= dmask << shift;
+      __syncthreads();
+    }
+    thr = prefix;
+    const u64 uq = qmass(thr);
+    need = uq > 0 ? (uint32_t)((want + uq - 1) / uq) : 0u;
+  }
+
+  const bool ranked = target > 0 && ties > need;  // uniform
+#pragma unroll
+  for (int k = 0; k < K; ++k) asm volatile("" : "+v"(u[k]));
+  if (ranked) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const uint64_t be = __ballot(u[k] == thr);
+      if (lane == 0) eqcnt[k * kWaves + wave] = (uint32_t)__popcll(be);
+    }
+    __syncthreads();
+    uint32_t tot;
+    const uint32_t c = tid < K * kWaves ? eqcnt[tid] : 0u;
+    const uint32_t ex = block_excl_scan<kWaves>(c, tot, wsum);  // ties before each slice
+    if (tid < K * kWaves) eqcnt[tid] = ex;
+    __syncthreads();
+  }
+  // the state update, in groups of 12 positions per thread (loads of a group in flight together);
+  // its indices come from an opaque copy of the thread index, so that the clamped offsets of the
+  // first loads are not kept alive until here
+  int tix = tid;
+  asm volatile("" : "+v"(tix));
+  constexpr int kGroup = 12;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += kGroup) {
+    float st[kGroup];
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e)
+      if (k0 + e < K) st[e] = su[min(tix + (k0 + e) * kThreads, n - 1)];
+#pragma unroll
+    for (int e = 0; e < kGroup; ++e) {
+      const int k = k0 + e;
+      if (k >= K) break;
+      const int j = tix + k * kThreads;
+      bool hit = target > 0 && u[k] > thr;
+      if (target > 0 && u[k] == thr) {
+        if (!ranked) {
+          hit = true;
+        } else {
+          const uint64_t be = __ballot(true);  // lanes of this wave whose entry ties (inside the branch)
+          const uint32_t lb = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(be >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(be), 0u));
+          hit = eqcnt[k * kWaves + wave] + lb < need;
+        }
+      }
+      if (j < n) su[j] = __builtin_fmaf(decay, st[e], hit ? 1.0f : 0.0f);
+    }
+  }
+  if (tid == 0 && counts) counts[unit] = (int32_t)(above + need);
+}
+
 // Work item = (sequence, KV head). mass, state: [S][H][n_max] (segment-relative); counts: [S][H].
 __global__ __launch_bounds__(kThreads) void lrfu_update(const float* __restrict__ mass, float* __restrict__ state,
                                                         int32_t* __restrict__ counts, int H, int64_t n_max,
@@ -148,7 +310,15 @@ __global__ __launch_bounds__(kThreads) void lrfu_update(const float* __restrict_
 
 hipError_t launch_lrfu_update(const float* mass, float* state, int32_t* counts, int H, int64_t n_max, double top_p,
                               float decay, const SeqTable& T, hipStream_t st) {
-  lrfu_update<<<dim3(T.total), dim3(kThreads), 0, st>>>(mass, state, counts, H, n_max, top_p, decay, T);
+  int nl = 0;
+  for (int i = 0; i < T.count; ++i) nl = nl > T.n[i] ? nl : T.n[i];
+  const dim3 grid(T.total), block(kThreads);
+  if (nl <= 8 * kThreads) lrfu_update_reg<8><<<grid, block, 0, st>>>(mass, state, counts, H, n_max, top_p, decay, T);
+  else if (nl <= 16 * kThreads)
+    lrfu_update_reg<16><<<grid, block, 0, st>>>(mass, state, counts, H, n_max, top_p, decay, T);
+  else if (nl <= 36 * kThreads)
+    lrfu_update_reg<36><<<grid, block, 0, st>>>(mass, state, counts, H, n_max, top_p, decay, T);
+  else lrfu_update<<<grid, block, 0, st>>>(mass, state, counts, H, n_max, top_p, decay, T);
   return hipGetLastError();
 }
 

@@ -88,12 +88,19 @@ def _masses(rng, n, kind):
     return vals.astype(np.float32)
 
 
-@pytest.mark.parametrize("top_p", [0.9, 0.5, 1.0])
-def test_lrfu_update_critical_set_exact(top_p):
+# length sets whose longest sequence selects each kernel variant: 8, 16 and 36 positions per
+# thread held in registers, and the global-memory kernel past 36864
+LRFU_LENS = [(5000, 777, 3), (16000, 9000, 1), (33000, 20000, 64), (40000, 100, 5)]
+
+
+@pytest.mark.parametrize("top_p,lens", [(0.9, LRFU_LENS[0]), (0.5, LRFU_LENS[0]), (1.0, LRFU_LENS[0]),
+                                        (0.9, LRFU_LENS[1]), (0.5, LRFU_LENS[2]), (0.9, LRFU_LENS[2]),
+                                        (0.9, LRFU_LENS[3])])
+def test_lrfu_update_critical_set_exact(top_p, lens):
     oc = _oc()
-    rng = np.random.default_rng(int(top_p * 100))
-    S, H, n_max = 3, 3, 5000
-    lens = [5000, 777, 3]
+    rng = np.random.default_rng([int(top_p * 100), lens[0]])
+    lens = list(lens)
+    S, H, n_max = 3, 3, max(lens)
     kinds = [["ties", "uniform", "peaked"], ["zero", "ties", "peaked"], ["uniform", "ties", "zero"]]
     mass = np.zeros((S, H, n_max), dtype=np.float32)
     for s in range(S):
