@@ -46,6 +46,10 @@ Readings where the pages leave a step open (each is listed with its reason in th
     constant sentinel key cannot cancel every query's attention (a query whose components sum
     below zero favours it), so the dead slot is read as a logit mask: a position mapped to it
     takes no part in the softmax and its own score is 0.
+  * Causal proxy rows (optional; [ACT] tallies the attention that the action tokens pay the
+    entries, and an action token inside the trajectory attends only to what came before it):
+    row r sees the keys at positions j <= row_pos[r]; the softmax of a row runs over its
+    visible keys, masked weights are 0, and the mean over rows still divides by all R rows.
 
 Every function below has pins in the CPU test suite (worked examples, closed forms, brute
 force and invariants); none is "parity unpinned".
@@ -238,6 +242,44 @@ def attention_mass(Q: np.ndarray, K: np.ndarray, scale: float, lse_rows: np.ndar
         L = logits(Q[r0:r0 + row_chunk], K, scale, bias)
         acc += np.exp(L - lse_rows[r0:r0 + row_chunk, None]).sum(axis=0)
     return acc / R
+
+
+def causal_weights(Q: np.ndarray, K: np.ndarray, scale: float, row_pos, lse_rows=None,
+                   bias: np.ndarray | None = None, power: int = 2, row_chunk: int = 256):
+    """Scores (power 2) or attention masses (power 1) when proxy row r only sees the keys at
+    positions j <= row_pos[r] (a causal mask for in-trajectory action tokens, [ACT]: the
+    attention each action token actually paid). Per row the weights are the softmax over its
+    visible keys, alpha_rj = exp(l_rj - LSE_r) with LSE_r over the visible keys (or the supplied
+    value); masked weights are 0, and a row that sees no key contributes nothing. The mean over
+    rows still divides by all R rows. Returns (scores or masses, the LSE used per row)."""
+    R, n = Q.shape[0], K.shape[0]
+    pos = np.asarray(row_pos, dtype=np.int64)
+    j = np.arange(n)
+    lse_out = np.full(R, -np.inf, dtype=np.float64)
+    acc = np.zeros(n, dtype=np.float64)
+    for r0 in range(0, R, row_chunk):
+        r1 = min(R, r0 + row_chunk)
+        vis = j[None, :] <= pos[r0:r1, None]
+        L = np.where(vis, logits(Q[r0:r1], K, scale, bias), -np.inf)
+        if lse_rows is None:
+            for r in range(r1 - r0):
+                if vis[r].any():
+                    lv = L[r, vis[r]]
+                    mx = lv.max()
+                    lse_out[r0 + r] = mx + np.log(np.exp(lv - mx).sum())
+        else:
+            lse_out[r0:r1] = np.asarray(lse_rows, dtype=np.float64)[r0:r1]
+        with np.errstate(invalid="ignore"):
+            alpha = np.where(vis, np.exp(L - lse_out[r0:r1, None]), 0.0)
+        acc += (alpha ** power).sum(axis=0)
+    out = np.sqrt(acc / R) if power == 2 else acc / R
+    return out, lse_out
+
+
+def causal_unit(Qs, Ks, row_pos, dtype, scale, bias=None, lse_rows=None, power: int = 2):
+    """causal_weights of one unit from stored rows/keys (widened exactly to float64)."""
+    b = None if bias is None else np.asarray(bias, dtype=np.float64)
+    return causal_weights(widen(Qs, dtype), widen(Ks, dtype), scale, row_pos, lse_rows, b, power)
 
 
 MASS_QUANTUM = 2 ** 32   # a mass of 1 is this many integer units

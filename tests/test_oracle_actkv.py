@@ -155,3 +155,74 @@ def test_side_order_follows_the_paged_copy(n, B, data):
     found = [int(kp[w // B, w % B, 0, 0]) for w in range(plan.start, plan.start + m)]
     assert found == O.side_order(n, m, B, kept)
     assert sorted(found) == kept
+
+
+# ------------------------------------------------------------------------- causal proxy rows
+
+def test_causal_hand_worked_example():
+    """Keys (0, ln 2, ln 3), d = 1, scale 1, three rows q = 1 at positions 0, 1, 2: the rows'
+    weights are (1, 0, 0), (1/3, 2/3, 0), (1/6, 1/3, 1/2), so the squared scores are 41/108,
+    20/108, 9/108 and the masses 1/2, 1/3, 1/6."""
+    K = np.array([[0.0], [math.log(2.0)], [math.log(3.0)]])
+    Q = np.ones((3, 1))
+    pos = [0, 1, 2]
+    s, L = O.causal_weights(Q, K, 1.0, pos)
+    np.testing.assert_allclose(s ** 2, np.array([41, 20, 9]) / 108.0, rtol=1e-14)
+    np.testing.assert_allclose(L, [0.0, math.log(3.0), math.log(6.0)], rtol=1e-14, atol=1e-15)
+    mass, _ = O.causal_weights(Q, K, 1.0, pos, power=1)
+    np.testing.assert_allclose(mass, [1 / 2, 1 / 3, 1 / 6], rtol=1e-14)
+
+
+def _causal_problem(seed, R=9, n=17, d=5):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((R, d)), rng.standard_normal((n, d)), rng.integers(-2, n + 2, R), rng
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_causal_rows_are_softmax_over_their_prefix(seed):
+    """Brute force: each row's weights are scipy's softmax over the keys up to its position."""
+    Q, K, pos, rng = _causal_problem(seed)
+    bias = rng.standard_normal(K.shape[0])
+    R, n = Q.shape[0], K.shape[0]
+    for power in (1, 2):
+        got, _ = O.causal_weights(Q, K, 0.7, pos, bias=bias, power=power)
+        acc = np.zeros(n)
+        for r in range(R):
+            p = min(int(pos[r]), n - 1)
+            if p < 0:
+                continue
+            w = softmax(0.7 * (K[:p + 1] @ Q[r]) + bias[:p + 1])
+            acc[:p + 1] += w ** power
+        want = np.sqrt(acc / R) if power == 2 else acc / R
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-300)
+
+
+def test_causal_mask_that_hides_nothing_is_the_plain_score():
+    Q, K, _, _ = _causal_problem(7)
+    n = K.shape[0]
+    pos = np.full(Q.shape[0], n - 1)
+    s, L = O.causal_weights(Q, K, 0.3, pos)
+    np.testing.assert_allclose(s, O.te_scores(Q, K, 0.3), rtol=1e-13)
+    np.testing.assert_allclose(L, O.lse(Q, K, 0.3), rtol=1e-13)
+    mass, _ = O.causal_weights(Q, K, 0.3, pos + 5, power=1)
+    np.testing.assert_allclose(mass, O.attention_mass(Q, K, 0.3), rtol=1e-13)
+
+
+def test_a_row_that_sees_nothing_only_dilutes_the_mean():
+    """A row at position -1 sees no key: it adds nothing, but it counts in R."""
+    Q, K, pos, _ = _causal_problem(8)
+    pos = np.clip(pos, 0, None)
+    s, _ = O.causal_weights(Q, K, 0.5, pos)
+    Q2 = np.vstack([Q, np.ones((1, Q.shape[1]))])
+    s2, L2 = O.causal_weights(Q2, K, 0.5, np.concatenate([pos, [-1]]))
+    np.testing.assert_allclose(s2 ** 2, s ** 2 * Q.shape[0] / (Q.shape[0] + 1), rtol=1e-13)
+    assert L2[-1] == -np.inf
+
+
+def test_causal_supplied_lse_is_used_as_given():
+    """A supplied LSE larger by ln 2 halves every weight (quarters the squares)."""
+    Q, K, pos, _ = _causal_problem(9)
+    pos = np.clip(pos, 0, None)
+    s, L = O.causal_weights(Q, K, 0.5, pos)
+    s2, _ = O.causal_weights(Q, K, 0.5, pos, lse_rows=L + math.log(2.0))
+    np.testing.assert_allclose(s2, s / 2.0, rtol=1e-13)
