@@ -75,6 +75,15 @@ typedef struct {
   float scale;               /* logit scale c (1/sqrt(d) in the usual attention)               */
   const int32_t* seq_starts; /* host [S]: start_s >= 0, or NULL for all zero; paged caches
                                 need start_s to be a multiple of the block size               */
+  const int32_t* row_pos;    /* device [S][H*G][q] int32, or NULL: a causal mask on the proxy
+                                rows. Row r of unit (s, h) then sees only the keys j <= row_pos
+                                (j counted from the segment start, like the per-key arrays):
+                                its softmax, LSE and weights run over those keys alone, a row
+                                with row_pos < 0 sees none (LSE -inf, weights 0), and the mean
+                                over rows still divides by all R = G * q rows. This is how the
+                                in-trajectory action tokens of "ActKV" weigh the cache: each
+                                attends only to what preceded it. Read by kvc_lse, kvc_score and
+                                kvc_attention_mass; kvc_am_fit rejects it                    */
 } kvc_shape;
 
 /* How keys are addressed. Contiguous: data is [S][H][n_max][d]. Paged (vLLM-style pool):

@@ -30,7 +30,7 @@ class _Shape(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("group", ctypes.c_int32),
                 ("num_queries", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("n_max", ctypes.c_int32),
                 ("seq_lens", ctypes.POINTER(ctypes.c_int32)), ("scale", ctypes.c_float),
-                ("seq_starts", ctypes.POINTER(ctypes.c_int32))]
+                ("seq_starts", ctypes.POINTER(ctypes.c_int32)), ("row_pos", ctypes.c_void_p)]
 
 
 class _KView(ctypes.Structure):
@@ -112,6 +112,7 @@ class Shape:
     seq_lens: object  # host ints [S]: keys scored per sequence
     scale: float
     seq_starts: object = None  # host ints [S]: cache position of each sequence's first scored key
+    row_pos: object = None     # device int32 tensor [S][H*G][q]: causal mask, row sees keys j <= row_pos
 
     def c(self):
         lens = np.ascontiguousarray(np.asarray(self.seq_lens, dtype=np.int32))
@@ -120,8 +121,13 @@ class Shape:
         if self.seq_starts is not None:
             starts = np.ascontiguousarray(np.asarray(self.seq_starts, dtype=np.int32))
             sp = starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        if self.row_pos is not None and not isinstance(self.row_pos, int):
+            if str(self.row_pos.dtype) != "torch.int32":
+                raise ValueError(f"row_pos: int32 tensor required, got {self.row_pos.dtype}")
+            _need(self.row_pos, self.num_seqs * self.num_kv_heads * self.group * self.num_queries * 4, "row_pos")
         sh = _Shape(self.num_seqs, self.num_kv_heads, self.group, self.num_queries, self.head_dim, self.n_max,
-                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(self.scale), sp)
+                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(self.scale), sp,
+                    _ptr(self.row_pos))
         return sh, (lens, starts)  # keep the arrays alive while `sh` is used
 
 

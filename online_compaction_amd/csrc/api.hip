@@ -19,19 +19,23 @@ int score_valu_tiles(int n);
 int contig_tiles(int m, bool f32);
 int paged_tiles(int m);
 hipError_t launch_score_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                             int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st);
+                             int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
+                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
+                             hipStream_t st);
 hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                                    int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
-                                    float scale, int kchunk, int dead, const SeqTable& T, hipStream_t st);
+                                    int max_blocks, const float* bias, const int32_t* rpos, float2* partials, int H,
+                                    int R, int64_t n_max, float scale, int kchunk, int dead, const SeqTable& T,
+                                    hipStream_t st);
 hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int R, int kchunk, const SeqTable& T,
                               hipStream_t st);
 hipError_t launch_score_valu(bool f32, int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                             int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st);
+                             int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
+                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
+                             hipStream_t st);
 hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const void* q, const void* k,
-                                    const int32_t* table, int max_blocks, const float* bias, float2* partials, int H,
-                                    int R, int64_t n_max, float scale, int dead, const SeqTable& T, hipStream_t st);
+                                    const int32_t* table, int max_blocks, const float* bias, const int32_t* rpos,
+                                    float2* partials, int H, int R, int64_t n_max, float scale, int dead,
+                                    const SeqTable& T, hipStream_t st);
 hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
                                  const SeqTable& T, hipStream_t st);
 int redirect_tiles(int n);
@@ -89,7 +93,7 @@ namespace {
 
 thread_local std::string g_err;
 
-constexpr int kVersion = 200;          // 0.2.0: slot-map key views, retention entry points
+constexpr int kVersion = 300;          // 0.3.0: causal proxy rows (kvc_shape.row_pos)
 constexpr int kBlockSize = 16;         // the one page size this build supports
 constexpr int kMfmaMinRows = 16;       // bf16 units with fewer proxy rows use the VALU path
 constexpr int64_t kMaxRows = 1 << 24;  // proxy rows per unit
@@ -284,10 +288,10 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
       sh, nullptr, [&](int s) { return H * rb * ((sh->seq_lens[s] + kc - 1) / kc); }, offset,
       [&](const SeqTable& T) {
         if (mf)
-          return launch_lse_partials_mfma(layout, has_bias, q, kv->data, index, kv->max_blocks, bias, parts, H, R,
-                                          sh->n_max, sh->scale, kc, kv->dead_slot, T, st);
+          return launch_lse_partials_mfma(layout, has_bias, q, kv->data, index, kv->max_blocks, bias, sh->row_pos,
+                                          parts, H, R, sh->n_max, sh->scale, kc, kv->dead_slot, T, st);
         return launch_lse_partials_valu(kv->dtype == KVC_F32, layout, has_bias, q, kv->data, index, kv->max_blocks,
-                                        bias, parts, H, R, sh->n_max, sh->scale, kv->dead_slot, T, st);
+                                        bias, sh->row_pos, parts, H, R, sh->n_max, sh->scale, kv->dead_slot, T, st);
       });
   if (e != hipSuccess) return hip_fail(e, "lse partial kernel");
   e = for_each_chunk(
@@ -370,10 +374,11 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
       [&](int s) { return H * (mf ? score_mfma_tiles(sh->seq_lens[s]) : score_valu_tiles(sh->seq_lens[s])); },
       no_offset, [&](const SeqTable& T) {
         if (mf)
-          return launch_score_mfma(layout, bias != nullptr, q, k->data, index, k->max_blocks, lse_rows, bias, out, H,
-                                   R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
+          return launch_score_mfma(layout, bias != nullptr, q, k->data, index, k->max_blocks, lse_rows, bias,
+                                   sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
         return launch_score_valu(k->dtype == KVC_F32, layout, bias != nullptr, q, k->data, index, k->max_blocks,
-                                 lse_rows, bias, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
+                                 lse_rows, bias, sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T,
+                                 st);
       });
   if (e != hipSuccess) return hip_fail(e, "score kernel");
   return ok();
@@ -512,6 +517,7 @@ static kvc_status check_am(const kvc_shape* sh, const kvc_kv_view* k, const kvc_
   if (kvc_status st = check_view(sh, k)) return st;
   if (kvc_status st = check_view(sh, v)) return st;
   if (k->slot_map || v->slot_map) return fail(KVC_ERR_UNSUPPORTED, "attention matching: slot-map views");
+  if (sh->row_pos) return fail(KVC_ERR_UNSUPPORTED, "attention matching: causal proxy rows (row_pos)");
   if (k->dtype != KVC_BF16 || v->dtype != KVC_BF16) return fail(KVC_ERR_UNSUPPORTED, "attention matching: bf16 only");
   if (!use_mfma(sh, k))
     return fail(KVC_ERR_UNSUPPORTED, "attention matching needs G * q >= %d proxy rows", kMfmaMinRows);

@@ -7,6 +7,8 @@
 // streams 64-key stages of K through LDS (A operand) by LDS-DMA, two stages in flight; online
 // sum in the log2 domain against a lazily moved reference exponent; one (reference, sum)
 // partial per row and key chunk goes to the workspace, and lse_combine merges the chunks.
+#include <type_traits>
+
 #include "mfma_common.h"
 
 namespace kvc {
@@ -29,13 +31,19 @@ constexpr int kLseBufs = 3;             // LDS stage buffers (two loads in fligh
 // sharing a key chunk run together on one XCD.
 // partials: float2 [T.off[i] + (h * nkc + kc) * R + row]
 // ------------------------------------------------------------------------------------------------
-template <int LAYOUT, bool BIAS>
+// CAUSAL: proxy row r sees only the keys at positions j <= rpos[unit][r]; per stage, a wave whose
+// rows see none of the stage's keys skips it, one whose rows see all of them runs the plain
+// stage, and otherwise the logits are masked element by element.
+template <int LAYOUT, bool BIAS, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
-    int max_blocks, const float* __restrict__ bias, float2* __restrict__ partials, int H, int R,
-    int64_t n_max, float scale, int kchunk, int dead, SeqTable T) {
+    int max_blocks, const float* __restrict__ bias, const int32_t* __restrict__ rpos, float2* __restrict__ partials,
+    int H, int R, int64_t n_max, float scale, int kchunk, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t ks_[kLseBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float kts[BIAS ? kLseBufs : 1][kStage];
+  // causal: the positions of the workgroup's rows (read only by the stages that mask, so they
+  // cost no registers across the sweep)
+  __shared__ int32_t pls[CAUSAL ? kPerBlock : 1];
   // the chunk's block-table entries (paged) or slots (slot map)
   __shared__ __attribute__((aligned(16)))
   int32_t idx[LAYOUT == kPaged ? kLseMaxChunk / 16 + 1 : (LAYOUT == kSlots ? kLseMaxChunk : 1)];
@@ -105,6 +113,21 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       for (int kk = 0; kk < 4; ++kk) qb[sub][kk] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
   }
+  // causal: the wave's row positions go to LDS, with their range over the wave in registers
+  // (rows past R repeat the last row)
+  int wpmin = 0, wpmax = 0;
+  if constexpr (CAUSAL) {
+    int lo = INT32_MAX, hi = INT32_MIN;
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub) {
+      const int p = rpos[unit * (int64_t)R + min(row0 + sub * 16 + c16, R - 1)];
+      if (g == 0) pls[wave * kPerWave + sub * 16 + c16] = p;
+      lo = min(lo, p);
+      hi = max(hi, p);
+    }
+    wpmin = wave_min(lo);
+    wpmax = wave_max(hi);
+  }
 
   // A stage (64 keys) goes global -> LDS without passing through registers: each wave issues 4
   // 16-byte-per-lane LDS-DMA loads (4 key rows each, the lane's chunk chosen so the rows land
@@ -139,17 +162,19 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   }
   constexpr float kLazyLimit = 18446744073709551616.0f;  // 2^64
 
-  auto tile_acc = [&](int buf, int kt, f32x4 (&acc)[kSub]) {
+  // logits of tile kt for the subtiles s0 .. s0 + NS - 1
+  auto tile_acc = [&](int buf, int kt, int s0, auto& acc) {
+    constexpr int NS = std::extent<std::remove_reference_t<decltype(acc)>>::value;
     const int row = kt * 16 + c16;
     bf16x8 a[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) a[kk] = *reinterpret_cast<const bf16x8*>(&ks_[buf][swz(row, 4 * kk + g)]);
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) acc[sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int sub = 0; sub < NS; ++sub) acc[sub] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) acc[sub] = mfma16(a[kk], qb[sub][kk], acc[sub]);
+      for (int sub = 0; sub < NS; ++sub) acc[sub] = mfma16(a[kk], qb[s0 + sub][kk], acc[sub]);
   };
   // per-key term of the lane's 4 keys in tile kt (log2 units): the bias, -inf past the chunk
   // and for keys in the dead slot
@@ -169,8 +194,12 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     }
     return t4;
   };
-  auto stage = [&](int buf, int k0, auto masked) {
+  auto row_pos = [&](int sub) -> int { return pls[wave * kPerWave + sub * 16 + c16]; };
+  auto stage = [&](int buf, int k0, auto masked, auto causal) {
     constexpr bool MASK = decltype(masked)::value;
+    constexpr bool CM = decltype(causal)::value;  // mask element by element (rows near the keys)
+    // a masked tile is formed in halves, so that the row positions fit beside the accumulators
+    constexpr int NH = CM ? 2 : 1, NS = kSub / NH;
     float sst[kSub];
 #pragma unroll
     for (int sub = 0; sub < kSub; ++sub) sst[sub] = 0.0f;
@@ -178,15 +207,22 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     for (int kt = 0; kt < kStage / 16; ++kt) {
       f32x4 kt4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       if constexpr (MASK) kt4 = key_term(buf, k0, kt);
-      f32x4 acc[kSub];
-      tile_acc(buf, kt, acc);
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
+      for (int hh = 0; hh < NH; ++hh) {
+        f32x4 acc[NS];
+        tile_acc(buf, kt, hh * NS, acc);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x = MASK ? __builtin_fmaf(acc[sub][j], c2, kt4[j]) - mref[sub]
-                               : __builtin_fmaf(acc[sub][j], c2, -mref[sub]);
-          sst[sub] += __builtin_amdgcn_exp2f(x);
+        for (int s2 = 0; s2 < NS; ++s2) {
+          const int sub = hh * NS + s2;
+          // (CM) how far past the lane's first key of the tile the row still sees
+          const int lim = CM ? row_pos(sub) - (k0 + kt * 16 + 4 * g) : 0;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x = MASK ? __builtin_fmaf(acc[s2][j], c2, kt4[j]) - mref[sub]
+                           : __builtin_fmaf(acc[s2][j], c2, -mref[sub]);
+            if constexpr (CM) x = j > lim ? -INFINITY : x;
+            sst[sub] += __builtin_amdgcn_exp2f(x);
+          }
         }
       }
     }
@@ -202,13 +238,20 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
 #pragma unroll 1
     for (int kt = 0; kt < kStage / 16; ++kt) {
       const f32x4 kt4 = key_term(buf, k0, kt);
-      f32x4 acc[kSub];
-      tile_acc(buf, kt, acc);
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
+      for (int hh = 0; hh < NH; ++hh) {
+      f32x4 acc[NS];
+      tile_acc(buf, kt, hh * NS, acc);
+#pragma unroll
+      for (int s2 = 0; s2 < NS; ++s2) {
+        const int sub = hh * NS + s2;
+        const int lim = CM ? row_pos(sub) - (k0 + kt * 16 + 4 * g) : 0;
         float x[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = __builtin_fmaf(acc[sub][j], c2, kt4[j]);
+        for (int j = 0; j < 4; ++j) {
+          x[j] = __builtin_fmaf(acc[s2][j], c2, kt4[j]);
+          if constexpr (CM) x[j] = j > lim ? -INFINITY : x[j];
+        }
         const float m4 = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
         if (m4 > mref[sub]) {
           ssum[sub] *= __builtin_amdgcn_exp2f(mref[sub] - m4);
@@ -218,16 +261,18 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
         ssum[sub] += (__builtin_amdgcn_exp2f(x[0] - mr) + __builtin_amdgcn_exp2f(x[1] - mr)) +
                      (__builtin_amdgcn_exp2f(x[2] - mr) + __builtin_amdgcn_exp2f(x[3] - mr));
       }
+      }
     }
   };
 
   // kLseBufs - 1 stages in flight. At stage st a wave waits for its own loads of st (those of the
   // later stages already issued may stay outstanding), the barrier then makes every wave's loads
   // visible and guarantees that nobody still reads the buffer the next issue overwrites.
-  constexpr int kLoadsPerStage = BIAS ? 5 : 4;
+  constexpr int kLoadsPerStage = BIAS ? 5 : 4;  // (the causal positions are in registers)
   static_assert(kLseBufs == 3, "the wait counts below assume two stages in flight");
   // the stationary rows have landed before any stage load is issued, so inside the loop the
-  // compiler has no register load left to wait for (its own waits would be vmcnt(0))
+  // compiler has no register load left to wait for (its own waits would be vmcnt(0)); the
+  // first barrier below also publishes the causal positions
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   issue(0);
   if (nst > 1) issue(1);
@@ -239,12 +284,19 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     }
     if (st + 2 < nst) issue(st + 2);
     const int k0 = kbeg + st * kStage;
+    if constexpr (CAUSAL) {
+      if (wpmax < k0) continue;  // no row of the wave sees a key of this stage
+      if (wpmin < k0 + kStage - 1) {
+        stage(st % kLseBufs, k0, std::true_type{}, std::true_type{});
+        continue;
+      }
+    }
     // the bias, dead slots and the keys past the chunk enter through the per-key term; other
     // stages skip it
     if (BIAS || LAYOUT == kSlots || k0 + kStage > kend) {
-      stage(st % kLseBufs, k0, std::true_type{});
+      stage(st % kLseBufs, k0, std::true_type{}, std::false_type{});
     } else {
-      stage(st % kLseBufs, k0, std::false_type{});
+      stage(st % kLseBufs, k0, std::false_type{}, std::false_type{});
     }
   }
 
@@ -297,21 +349,28 @@ __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ pa
 int lse_mfma_row_blocks(int R) { return (R + kPerBlock - 1) / kPerBlock; }
 
 hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                                    int max_blocks, const float* bias, float2* partials, int H, int R, int64_t n_max,
-                                    float scale, int kchunk, int dead, const SeqTable& T, hipStream_t st) {
+                                    int max_blocks, const float* bias, const int32_t* rpos, float2* partials, int H,
+                                    int R, int64_t n_max, float scale, int kchunk, int dead, const SeqTable& T,
+                                    hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
-#define KVC_LSE_LAUNCH(L, B)                                                                               \
-  lse_partials_mfma<L, B><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, partials, H, R, n_max, scale, \
-                                                  kchunk, dead, T)
+#define KVC_LSE_LAUNCH(L, B, C)                                                                                  \
+  lse_partials_mfma<L, B, C><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, rpos, partials, H, R, n_max, \
+                                                     scale, kchunk, dead, T)
+#define KVC_LSE_LAUNCH_C(L, B)            \
+  do {                                   \
+    if (rpos) KVC_LSE_LAUNCH(L, B, true);  \
+    else KVC_LSE_LAUNCH(L, B, false);      \
+  } while (0)
   if (layout == kPaged) {
-    if (has_bias) KVC_LSE_LAUNCH(kPaged, true); else KVC_LSE_LAUNCH(kPaged, false);
+    if (has_bias) KVC_LSE_LAUNCH_C(kPaged, true); else KVC_LSE_LAUNCH_C(kPaged, false);
   } else if (layout == kSlots) {
-    if (has_bias) KVC_LSE_LAUNCH(kSlots, true); else KVC_LSE_LAUNCH(kSlots, false);
+    if (has_bias) KVC_LSE_LAUNCH_C(kSlots, true); else KVC_LSE_LAUNCH_C(kSlots, false);
   } else {
-    if (has_bias) KVC_LSE_LAUNCH(kContig, true); else KVC_LSE_LAUNCH(kContig, false);
+    if (has_bias) KVC_LSE_LAUNCH_C(kContig, true); else KVC_LSE_LAUNCH_C(kContig, false);
   }
+#undef KVC_LSE_LAUNCH_C
 #undef KVC_LSE_LAUNCH
   return hipGetLastError();
 }

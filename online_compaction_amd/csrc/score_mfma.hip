@@ -37,13 +37,18 @@ constexpr int kBufs = 3;                            // LDS stage buffers (two lo
 // pw = 2: s_j = sqrt((1/R) sum_r alpha_rj^2) (the TE score); pw = 1: (1/R) sum_r alpha_rj, the
 // mean attention weight the proxy rows give key j (the per-entry action-attention tally of ActKV).
 // ------------------------------------------------------------------------------------------------
-template <int LAYOUT, bool BIAS>
+// CAUSAL: proxy row r sees only the keys at positions j <= rpos[unit][r] (segment-relative);
+// the stage's row positions arrive with its rows, and per stage and wave the 128 keys are either
+// all visible to the stage's 64 rows (the plain epilogue), all hidden (the stage is skipped), or
+// masked element by element.
+template <int LAYOUT, bool BIAS, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
-    int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, float* __restrict__ scores,
-    int H, int R, int64_t n_max, float scale, int pw, int dead, SeqTable T) {
+    int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, const int32_t* __restrict__ rpos,
+    float* __restrict__ scores, int H, int R, int64_t n_max, float scale, int pw, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t qs[kBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float lss[kBufs][kStage];
+  __shared__ __attribute__((aligned(16))) int32_t pss[CAUSAL ? kBufs : 1][kStage];
 
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
@@ -109,14 +114,19 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
             &qs[b][(wave * 4 + j) * 1024]);
     }
     if (lane < 16) dma4(lu + min(r0 + wave * 16 + lane, R - 1), &lss[b][wave * 16]);
+    if constexpr (CAUSAL)
+      if (lane < 16)
+        dma4(reinterpret_cast<const float*>(rpos + unit * (int64_t)R + min(r0 + wave * 16 + lane, R - 1)),
+             &pss[b][wave * 16]);
   };
 
   float ssum[kScoreSub];
 #pragma unroll
   for (int sub = 0; sub < kScoreSub; ++sub) ssum[sub] = 0.0f;
 
-  auto stage = [&](int buf, int r0, auto masked) {
+  auto stage = [&](int buf, int r0, auto masked, auto causal) {
     constexpr bool MASK = decltype(masked)::value;
+    constexpr bool CM = decltype(causal)::value;  // mask element by element (rows near the keys)
 #pragma unroll 1
     for (int rt = 0; rt < kStage / 16; ++rt) {
       const int row = rt * 16 + c16;
@@ -124,6 +134,14 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(&qs[buf][swz(row, 4 * ks + g)]);
       f32x4 nb4 = *reinterpret_cast<const f32x4*>(&lss[buf][rt * 16 + 4 * g]);
+      int32_t p4[4] = {0, 0, 0, 0};
+      if constexpr (CM) {
+        const int4 pv = *reinterpret_cast<const int4*>(&pss[buf][rt * 16 + 4 * g]);
+        p4[0] = pv.x;
+        p4[1] = pv.y;
+        p4[2] = pv.z;
+        p4[3] = pv.w;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         nb4[e] = __builtin_fmaf(nb4[e], -pl2, kSqOffset);
@@ -143,6 +161,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
         for (int e = 0; e < 4; ++e) {
           float x = __builtin_fmaf(acc[sub][e], a2, nb4[e]);
           if constexpr (BIAS) x += bb[sub];
+          if constexpr (CM) x = key0 + sub * 16 + c16 > p4[e] ? -INFINITY : x;
           ssum[sub] += __builtin_amdgcn_exp2f(x);
         }
       }
@@ -154,21 +173,32 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   // The stationary keys have landed before the first issue, so the compiler has no register load
   // left to wait for inside the loop.
   static_assert(kBufs == 3, "the wait counts below assume two stages in flight");
+  constexpr int kLoadsPerStage = CAUSAL ? 6 : 5;
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   issue(0);
   if (nst > 1) issue(1);
   for (int st = 0; st < nst; ++st) {
     if (st + 1 < nst) {
-      vm_wait_barrier<5>();
+      vm_wait_barrier<kLoadsPerStage>();
     } else {
       vm_wait_barrier<0>();
     }
     if (st + 2 < nst) issue(st + 2);
     const int r0 = st * kStage;
-    if (r0 + kStage > R) {
-      stage(st % kBufs, r0, std::true_type{});
+    const int buf = st % kBufs;
+    int vis = 0;  // 0: every key of the wave visible to every row of the stage; 1: mixed; 2: none
+    if constexpr (CAUSAL) {
+      const int pr = pss[buf][lane];
+      const int pmin = wave_min(pr), pmax = wave_max(pr);
+      vis = pmax < key0 ? 2 : (pmin >= key0 + 16 * kScoreSub - 1 ? 0 : 1);
+    }
+    if (vis == 2) continue;
+    if (vis == 1) {
+      if constexpr (CAUSAL) stage(buf, r0, std::true_type{}, std::true_type{});
+    } else if (r0 + kStage > R) {
+      stage(buf, r0, std::true_type{}, std::false_type{});
     } else {
-      stage(st % kBufs, r0, std::false_type{});
+      stage(buf, r0, std::false_type{}, std::false_type{});
     }
   }
 
@@ -191,21 +221,28 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
 int score_mfma_tiles(int n) { return (n + kScoreKeys - 1) / kScoreKeys; }
 
 hipError_t launch_score_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                             int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st) {
+                             int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
+                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
+                             hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
-#define KVC_SCORE_LAUNCH(L, B)                                                                             \
-  score_mfma<L, B><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, \
-                                           dead, T)
+#define KVC_SCORE_LAUNCH(L, B, C)                                                                            \
+  score_mfma<L, B, C><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, \
+                                              scale, pw, dead, T)
+#define KVC_SCORE_LAUNCH_C(L, B)            \
+  do {                                     \
+    if (rpos) KVC_SCORE_LAUNCH(L, B, true);  \
+    else KVC_SCORE_LAUNCH(L, B, false);      \
+  } while (0)
   if (layout == kPaged) {
-    if (has_bias) KVC_SCORE_LAUNCH(kPaged, true); else KVC_SCORE_LAUNCH(kPaged, false);
+    if (has_bias) KVC_SCORE_LAUNCH_C(kPaged, true); else KVC_SCORE_LAUNCH_C(kPaged, false);
   } else if (layout == kSlots) {
-    if (has_bias) KVC_SCORE_LAUNCH(kSlots, true); else KVC_SCORE_LAUNCH(kSlots, false);
+    if (has_bias) KVC_SCORE_LAUNCH_C(kSlots, true); else KVC_SCORE_LAUNCH_C(kSlots, false);
   } else {
-    if (has_bias) KVC_SCORE_LAUNCH(kContig, true); else KVC_SCORE_LAUNCH(kContig, false);
+    if (has_bias) KVC_SCORE_LAUNCH_C(kContig, true); else KVC_SCORE_LAUNCH_C(kContig, false);
   }
+#undef KVC_SCORE_LAUNCH_C
 #undef KVC_SCORE_LAUNCH
   return hipGetLastError();
 }

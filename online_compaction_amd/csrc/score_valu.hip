@@ -10,6 +10,8 @@
 //           block's 256 keys -> workspace partials, combined by lse_combine.
 //   pass 2 (score_valu): per key, sum over rows of exp2(2 log2(alpha) + 100) -> score, or of
 //           exp2(log2(alpha) + 100) -> attention mass.
+#include <climits>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -95,10 +97,12 @@ template <bool F32, int LAYOUT, bool BIAS>
 __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ q, const void* __restrict__ k,
                                                        const int32_t* __restrict__ table, int max_blocks,
                                                        const float* __restrict__ lse, const float* __restrict__ bias,
-                                                       float* __restrict__ scores, int H, int R, int64_t n_max,
-                                                       float scale, int pw, int dead, SeqTable T) {
+                                                       const int32_t* __restrict__ rpos, float* __restrict__ scores,
+                                                       int H, int R, int64_t n_max, float scale, int pw, int dead,
+                                                       SeqTable T) {
   __shared__ __attribute__((aligned(16))) float qs[kRowsStage][kHeadDim];
   __shared__ float nbs[kRowsStage];
+  __shared__ int32_t pss[kRowsStage];  // causal: the rows' positions (INT32_MAX without a mask)
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int n = T.n[i];
@@ -133,12 +137,14 @@ __global__ __launch_bounds__(kThreads) void score_valu(const void* __restrict__ 
     if (threadIdx.x < kRowsStage) {
       const int r = r0 + threadIdx.x;
       nbs[threadIdx.x] = r < R ? kSqOffset - pl2 * lse[unit * R + r] : -INFINITY;
+      pss[threadIdx.x] = (rpos && r < R) ? rpos[unit * R + r] : INT32_MAX;
     }
     __syncthreads();
     const int rows = min(kRowsStage, R - r0);
     for (int rr = 0; rr < rows; ++rr) {
       float x = __builtin_fmaf(dot_row(kr, qs[rr]), a2, nbs[rr]);
       if constexpr (BIAS) x += bb;
+      if (key > pss[rr]) x = -INFINITY;  // causal: the row does not see this key
       acc += __builtin_amdgcn_exp2f(x);
     }
   }
@@ -153,10 +159,12 @@ template <bool F32, int LAYOUT, bool BIAS>
 __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __restrict__ q, const void* __restrict__ k,
                                                               const int32_t* __restrict__ table, int max_blocks,
                                                               const float* __restrict__ bias,
+                                                              const int32_t* __restrict__ rpos,
                                                               float2* __restrict__ partials, int H, int R,
                                                               int64_t n_max, float scale, int dead, SeqTable T) {
   __shared__ __attribute__((aligned(16))) float qs[kRowsStage][kHeadDim];
   __shared__ float2 wred[kThreads / 64][kRowsStage];
+  __shared__ int32_t pss[kRowsStage];  // causal: the rows' positions (INT32_MAX without a mask)
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int n = T.n[i];
@@ -187,10 +195,15 @@ __global__ __launch_bounds__(kThreads) void lse_partials_valu(const void* __rest
   for (int r0 = 0; r0 < R; r0 += kRowsStage) {
     __syncthreads();
     stage_rows<F32>(q, unit, R, r0, qs);
+    if (threadIdx.x < kRowsStage) {
+      const int r = r0 + threadIdx.x;
+      pss[threadIdx.x] = (rpos && r < R) ? rpos[unit * R + r] : INT32_MAX;
+    }
     __syncthreads();
     const int rows = min(kRowsStage, R - r0);
     for (int rr = 0; rr < rows; ++rr) {
-      const float x = __builtin_fmaf(dot_row(kr, qs[rr]), c2, kt);
+      float x = __builtin_fmaf(dot_row(kr, qs[rr]), c2, kt);
+      if (key > pss[rr]) x = -INFINITY;  // causal: the row does not see this key
       float mx = x;
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -239,18 +252,20 @@ int score_valu_tiles(int n) { return (n + kThreads - 1) / kThreads; }
   } while (0)
 
 hipError_t launch_score_valu(bool f32, int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                             int max_blocks, const float* lse, const float* bias, float* scores, int H, int R,
-                             int64_t n_max, float scale, int pw, int dead, const SeqTable& T, hipStream_t st) {
+                             int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
+                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
+                             hipStream_t st) {
   dim3 grid(T.total), block(kThreads);
-  KVC_VALU_DISPATCH(score_valu, q, k, table, max_blocks, lse, bias, scores, H, R, n_max, scale, pw, dead, T);
+  KVC_VALU_DISPATCH(score_valu, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead, T);
   return hipGetLastError();
 }
 
 hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const void* q, const void* k,
-                                    const int32_t* table, int max_blocks, const float* bias, float2* partials, int H,
-                                    int R, int64_t n_max, float scale, int dead, const SeqTable& T, hipStream_t st) {
+                                    const int32_t* table, int max_blocks, const float* bias, const int32_t* rpos,
+                                    float2* partials, int H, int R, int64_t n_max, float scale, int dead,
+                                    const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(kThreads);
-  KVC_VALU_DISPATCH(lse_partials_valu, q, k, table, max_blocks, bias, partials, H, R, n_max, scale, dead, T);
+  KVC_VALU_DISPATCH(lse_partials_valu, q, k, table, max_blocks, bias, rpos, partials, H, R, n_max, scale, dead, T);
   return hipGetLastError();
 }
 

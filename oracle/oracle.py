@@ -282,6 +282,24 @@ def causal_unit(Qs, Ks, row_pos, dtype, scale, bias=None, lse_rows=None, power: 
     return causal_weights(widen(Qs, dtype), widen(Ks, dtype), scale, row_pos, lse_rows, b, power)
 
 
+def causal_unit_live(Qs, Ks, live, row_pos, dtype, scale, bias=None, lse_rows=None, power: int = 2):
+    """causal_unit when only the `live` positions take part (the dead slot of [IKV]'s
+    layout-preserving eviction read as a logit mask, combined with causal [ACT] rows): row r sees
+    the live keys at positions j <= row_pos[r]. The live keys keep their order, so a row sees
+    the first (number of live positions <= row_pos[r]) of them; dead positions score 0.
+    Returns (scores or masses over all positions, the LSE used per row)."""
+    live = np.asarray(live, dtype=bool)
+    n = live.shape[0]
+    pos = np.asarray(row_pos, dtype=np.int64)
+    seen = np.concatenate([[0], np.cumsum(live)])           # live positions among the first i
+    vis_live = seen[np.clip(pos + 1, 0, n)] - 1             # last live index each row sees
+    out = np.zeros(n, dtype=np.float64)
+    b = None if bias is None else np.asarray(bias)[live]
+    sub, lse_out = causal_unit(Qs, np.asarray(Ks)[live], vis_live, dtype, scale, b, lse_rows, power)
+    out[live] = sub
+    return out, lse_out
+
+
 MASS_QUANTUM = 2 ** 32   # a mass of 1 is this many integer units
 MASS_CAP = 2 ** 40       # per-entry cap of the integer mass (masses above 256)
 

@@ -11,6 +11,7 @@ import sys
 
 import numpy as np
 
+import workloads as W
 from oracle import oracle as O
 
 SCORE_RTOL = 1e-3
@@ -134,3 +135,25 @@ def check_am_unit(rows, K, V, lse_rows, kept, beta_row, vc_rows, dtype, scale, i
         f"{t}: the fit made things worse"
     assert np.all(beta_row[m:] == 7.0) and np.all(vc_rows[m:] == 7.0), f"{t}: rows past m touched"
     return {"obj": d_obj, "fit": d_fit, "out": d_out, "beta": d_beta, "vc": d_vc}
+
+
+def slot_setup(w, data, dead_frac, rng):
+    """A slot pool from the paged pool plus one sentinel block (K = -1e4 as on the page, V = 0);
+    per-(sequence, head) slot maps from the block table, with a random share of positions
+    already redirected to the dead slot."""
+    nb, B, H, d = data["k_pool"].shape
+    sent = np.full((1, B, H, d), W.f32_to_bf16_bits(np.float32(-1.0e4)) if w.dtype == "bf16" else -1.0e4,
+                   dtype=data["k_pool"].dtype)
+    pool = np.concatenate([data["k_pool"], sent]).reshape(-1, H, d)
+    dead = nb * B
+    smap = np.zeros((w.S, H, w.n_max), dtype=np.int32)
+    live = np.zeros((w.S, H, w.n_max), dtype=bool)
+    for s in range(w.S):
+        n = w.n[s]
+        pos = np.arange(n)
+        base = data["table"][s][pos // B].astype(np.int64) * B + pos % B
+        for h in range(H):
+            lv = rng.random(n) >= dead_frac
+            smap[s, h, :n] = np.where(lv, base, dead)
+            live[s, h, :n] = lv
+    return pool, smap, live, dead

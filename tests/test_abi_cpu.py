@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert oc.kvc_version() == 200
+    assert oc.kvc_version() == 300
     assert oc.kvc_status_string(0) == "ok"
     assert oc.kvc_status_string(3) == "workspace too small"
     assert oc.kvc_status_string(99) == "unknown status"
@@ -243,3 +243,29 @@ def test_attention_matching_validation(lib):
     sl = A.KView(FAKE, A.KVC_BF16, 0, None, 0, FAKE, 3).c()
     assert f(ctypes.byref(s), FAKE, ctypes.byref(sl), ctypes.byref(v_), FAKE, FAKE, mp, 6600, 5, 5, FAKE, FAKE, FAKE,
              1 << 40, None) == A.KVC_ERR_UNSUPPORTED
+
+
+def test_causal_rows_validation(lib):
+    """A causal mask sizes no workspace differently, attention matching rejects it, and the
+    binding refuses a row_pos tensor that is not int32 or too short."""
+    torch = pytest.importorskip("torch")
+    kv = A.KView(FAKE, A.KVC_BF16)
+    sh = _shape()
+    cz = _shape()
+    cz.row_pos = FAKE
+    assert oc.kvc_score_workspace_size(cz, kv, False) == oc.kvc_score_workspace_size(sh, kv, False)
+    assert oc.kvc_lse_workspace_size(cz, kv) == oc.kvc_lse_workspace_size(sh, kv)
+    assert oc.kvc_am_workspace_size(cz, kv, kv, [6600, 4000], True) == 0
+    s, keep = cz.c()
+    k_, v_ = kv.c(), kv.c()
+    mp = (ctypes.c_int32 * 2)(6600, 4000)
+    assert lib.kvc_am_fit(ctypes.byref(s), FAKE, ctypes.byref(k_), ctypes.byref(v_), FAKE, FAKE, mp, 6600, 5, 5,
+                          FAKE, FAKE, FAKE, 1 << 40, None) == A.KVC_ERR_UNSUPPORTED
+    assert b"row_pos" in lib.kvc_last_error()
+    bad = _shape()
+    bad.row_pos = torch.zeros((2, 32, 1024), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        bad.c()
+    bad.row_pos = torch.zeros((2, 32, 1000), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        bad.c()

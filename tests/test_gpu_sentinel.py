@@ -5,7 +5,8 @@ import pytest
 
 import workloads as W
 from oracle import oracle as O
-from tests.parity import check_kept_form, check_scores, check_selection_band, check_selection_exact, say
+from tests.parity import (check_kept_form, check_scores, check_selection_band, check_selection_exact, say,
+                          slot_setup)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -21,28 +22,6 @@ def _oc():
     return oc
 
 
-def _slot_setup(w, data, dead_frac, rng):
-    """A slot pool from the paged pool plus one sentinel block (K = -1e4 as on the page, V = 0);
-    per-(sequence, head) slot maps from the block table, with a random share of positions
-    already redirected to the dead slot."""
-    nb, B, H, d = data["k_pool"].shape
-    sent = np.full((1, B, H, d), W.f32_to_bf16_bits(np.float32(-1.0e4)) if w.dtype == "bf16" else -1.0e4,
-                   dtype=data["k_pool"].dtype)
-    pool = np.concatenate([data["k_pool"], sent]).reshape(-1, H, d)
-    dead = nb * B
-    smap = np.zeros((w.S, H, w.n_max), dtype=np.int32)
-    live = np.zeros((w.S, H, w.n_max), dtype=bool)
-    for s in range(w.S):
-        n = w.n[s]
-        pos = np.arange(n)
-        base = data["table"][s][pos // B].astype(np.int64) * B + pos % B
-        for h in range(H):
-            lv = rng.random(n) >= dead_frac
-            smap[s, h, :n] = np.where(lv, base, dead)
-            live[s, h, :n] = lv
-    return pool, smap, live, dead
-
-
 @pytest.mark.parametrize("case", ["mfma_bf16", "valu_f32", "mfma_bias_all_dead_unit"])
 def test_scores_and_mass_through_slot_map(case):
     P, oc = _P(), _oc()
@@ -55,7 +34,7 @@ def test_scores_and_mass_through_slot_map(case):
                      bias_tail=0.5 if "bias" in case else 0.0)
     rng = np.random.default_rng(7)
     data = W.build_paged(w)
-    pool, smap, live, dead = _slot_setup(w, data, 0.45, rng)
+    pool, smap, live, dead = slot_setup(w, data, 0.45, rng)
     if "all_dead" in case:
         smap[1, 0, :w.n[1]] = dead
         live[1, 0, :] = False
@@ -125,7 +104,7 @@ def test_evict_then_rescore_end_to_end():
     w = W.custom("slot_e2e", 162, S=2, H=2, G=4, q=16, n=(3000, 1500), dtype="bf16", keys="mixture",
                  queries="cluster", paged=True, table="permuted", block_size=16)
     data = W.build_paged(w)
-    pool, smap, live, dead = _slot_setup(w, data, 0.0, np.random.default_rng(1))
+    pool, smap, live, dead = slot_setup(w, data, 0.0, np.random.default_rng(1))
     dq = P.device_tensor(data["Q"])
     dmap = P.device_tensor(smap)
     kv = oc.KView(P.device_tensor(pool), oc.KVC_BF16, 0, None, 0, dmap, dead)

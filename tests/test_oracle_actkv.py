@@ -226,3 +226,29 @@ def test_causal_supplied_lse_is_used_as_given():
     s, L = O.causal_weights(Q, K, 0.5, pos)
     s2, _ = O.causal_weights(Q, K, 0.5, pos, lse_rows=L + math.log(2.0))
     np.testing.assert_allclose(s2, s / 2.0, rtol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_causal_through_a_live_mask_is_brute_force_with_dead_logits(seed):
+    """Dead positions take no part: the same as giving them logit -inf by brute force (each row
+    a softmax over its visible live keys), and a dead position scores exactly 0."""
+    Q, K, pos, rng = _causal_problem(20 + seed, R=11, n=23)
+    Q, K = Q.astype(np.float32).astype(np.float64), K.astype(np.float32).astype(np.float64)  # stored as f32
+    n = K.shape[0]
+    live = rng.random(n) >= 0.4
+    live[0] = True  # every row that sees a key sees a live one (position >= 0 includes key 0)
+    bias = rng.standard_normal(n)
+    for power in (1, 2):
+        got, L = O.causal_unit_live(Q, K, live, pos, "f32", 0.6, bias=bias, power=power)
+        acc = np.zeros(n)
+        for r in range(Q.shape[0]):
+            p = min(int(pos[r]), n - 1)
+            if p < 0:
+                assert L[r] == -np.inf
+                continue
+            x = np.where(live[:p + 1], 0.6 * (K[:p + 1] @ Q[r]) + bias[:p + 1], -np.inf)
+            acc[:p + 1] += softmax(x) ** power
+            np.testing.assert_allclose(L[r], np.log(np.exp(x - x.max()).sum()) + x.max(), rtol=1e-13)
+        want = np.sqrt(acc / Q.shape[0]) if power == 2 else acc / Q.shape[0]
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-300)
+        assert np.all(got[~live] == 0.0)

@@ -14,4 +14,5 @@ from .gen import (  # noqa: F401
     bf16_bits_to_f32,
     c4_budget,
     score_rows,
+    row_positions,
 )

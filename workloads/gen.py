@@ -16,6 +16,8 @@ round-to-nearest-even to bfloat16 where the workload is bf16):
 * "cluster" queries (delayed future-turn proxies): z + 0.5 * mu_c, z ~ N(0, I), c uniform.
 * "action" queries: 10 non-overlapping spans of q/10 positions at seeded starts in
   [4, n - q/10]; the query for position p is z + 0.5 * mu_{c_p} (the cluster of key p).
+* causal row positions (row_positions): the action tokens' own positions, or seeded uniform
+  integers over [-2, n + 1].
 * values: N(0, 1) (they never influence scores, only the compacted bytes).
 * bias (1-layer paged trajectory): +b on the last floor(n/4) keys, 0 elsewhere.
 * paged pools: vLLM-style [num_blocks][B][H][d]; identity block table, or a seeded
@@ -35,7 +37,8 @@ import os
 import numpy as np
 
 # generator tags: one independent stream per kind of draw
-T_CLUSTERS, T_ASSIGN, T_KEYNOISE, T_VALUES, T_QUERIES, T_QCLUSTER, T_LENGTHS, T_PERM, T_SPANS, T_KEYS = range(10)
+(T_CLUSTERS, T_ASSIGN, T_KEYNOISE, T_VALUES, T_QUERIES, T_QCLUSTER, T_LENGTHS, T_PERM, T_SPANS, T_KEYS,
+ T_POSITIONS) = range(11)
 NUM_CLUSTERS = 64
 NUM_SINKS = 4
 SINK_GAIN = 8.0
@@ -228,6 +231,28 @@ def action_positions(w: Workload, s: int) -> np.ndarray:
         if np.all(np.diff(starts) >= L):
             break
     return np.concatenate([np.arange(a, a + L) for a in starts])
+
+
+def row_positions(w: Workload, kind: str = "action") -> np.ndarray:
+    """Causal positions of the proxy rows, int32 [S][H*G][q]: row r of a unit sees the keys at
+    segment positions j <= its entry. "action": each action-token query sits at its own position
+    in the trajectory (every query head of every KV head shares them); "spread": seeded uniform
+    over [-2, n + 1] per row (rows that see no key, rows that see every key, and all between);
+    "all": n - 1 (every row sees every key); "none": -1 (no row sees any key)."""
+    out = np.zeros((w.S, w.H * w.G, w.q), dtype=np.int32)
+    for s in range(w.S):
+        n = w.n[s]
+        if kind == "action":
+            out[s] = action_positions(w, s)[None, :]
+        elif kind == "spread":
+            out[s] = _rng(w.cfg_id, s, 0, T_POSITIONS).integers(-2, n + 1, size=(w.H * w.G, w.q), endpoint=True)
+        elif kind == "all":
+            out[s] = n - 1
+        elif kind == "none":
+            out[s] = -1
+        else:
+            raise ValueError(kind)
+    return out
 
 
 def unit_queries(w: Workload, s: int, h: int) -> np.ndarray:
