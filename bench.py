@@ -13,6 +13,7 @@ from __future__ import annotations
 
 import argparse
 import gc
+import dataclasses
 import hashlib
 import json
 import os
@@ -57,8 +58,9 @@ def describe(w) -> str:
            ", read through a slot map; evicted positions redirected to a dead slot (no data moved)"
            if w.name == "sentinel" else
            ", then beta and V_C fitted for the kept keys by Attention Matching" if w.name == "am" else "")
+    causal = ", causal action rows (each sees the keys up to its own position)" if w.causal else ""
     return (f"{w.name}: {w.S} seqs x {w.H} KV heads, G={w.G}, q={w.q}, R={w.R}, {n}, d={w.d}, {w.dtype}, "
-            f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}{pol}")
+            f"{lse}, m={w.m[0] if len(set(w.m)) == 1 else 'round(n/5)'}, {lay}{pol}{causal}")
 
 
 def trajectory_tokens(w) -> int:
@@ -109,7 +111,13 @@ def algorithmic_bytes(w, moved_rows=None) -> dict:
 
 
 def score_flops(w) -> float:
+    """QK^T multiply-adds the scores need: every logit (R x n per unit), or with causal rows only
+    the logits a row sees (min(position + 1, n) keys per row)."""
     passes = 1 if w.lse_supplied else 2
+    if w.causal:
+        rp = W.row_positions(w, "action").astype(np.int64)
+        seen = sum(int(np.clip(rp[s] + 1, 0, scored_lens(w)[s]).sum()) for s in range(w.S))
+        return float(passes) * 2.0 * w.d * seen
     return float(passes) * 2.0 * w.R * w.d * sum(scored_lens(w)) * w.H
 
 
@@ -144,12 +152,24 @@ def _oracle_unit(args):
     lse_rows = None
     if w.lse_supplied:  # the supplied input, prepared outside the timed region
         lse_rows = O.lse_unit(Qr, K, w.dtype, w.logit_scale, bias_row).astype(np.float32).astype(np.float64)
+    pos = None
+    if w.causal:
+        from workloads import row_positions
+        pos = row_positions(w, "action")[s, h * w.G:(h + 1) * w.G].reshape(-1)
     t0 = time.perf_counter()
-    if w.name == "actkv":  # attention mass -> action-critical set -> LRFU step -> top-m of the state
+    if w.name == "actkv" and w.causal:
+        mass, _ = O.causal_unit(Qr, K, pos, w.dtype, w.logit_scale, bias_row, lse_rows, power=1)
+        hit = O.action_critical(mass.astype(np.float32), 0.9)
+        st0 = np.random.default_rng([4096, s, h]).random(K.shape[0]) * 3.41
+        kept = O.select_topm(O.lrfu_step(st0, hit, 2.0 ** -0.5), w.m[s])
+    elif w.name == "actkv":  # attention mass -> action-critical set -> LRFU step -> top-m of the state
         mass = O.mass_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
         hit = O.action_critical(mass.astype(np.float32), 0.9)
         st0 = np.random.default_rng([4096, s, h]).random(K.shape[0]) * 3.41
         kept = O.select_topm(O.lrfu_step(st0, hit, 2.0 ** -0.5), w.m[s])
+    elif w.causal:
+        sc, _ = O.causal_unit(Qr, K, pos, w.dtype, w.logit_scale, bias_row, lse_rows)
+        kept = O.select_topm(sc, w.m[s])
     else:
         sc = O.score_unit(Qr, K, w.dtype, w.logit_scale, bias_row, lse_rows)
         kept = O.select_topm(sc, w.m[s])
@@ -164,7 +184,7 @@ def _oracle_unit(args):
 
 
 def _oracle_steps(w, am_iters) -> str:
-    lse = "supplied LSE" if w.lse_supplied else "computed LSE"
+    lse = ("supplied LSE" if w.lse_supplied else "computed LSE") + (", causal rows" if w.causal else "")
     if w.name == "actkv":
         return f"attention mass ({lse}) + action-critical set + LRFU step + top-m + gather"
     if w.name == "sentinel":
@@ -284,6 +304,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c3", help="c3 (default) or another named workload, for study")
     ap.add_argument("--k", type=int, default=6, help="budget index for the paged action-token workload")
+    ap.add_argument("--causal", action="store_true",
+                    help="action-token workloads (c4, actkv, sentinel): each proxy row sees only the keys "
+                         "up to its own position")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="approximate CPU baseline budget")
     ap.add_argument("--am-iters", type=int, nargs=2, default=(32, 32), metavar=("BETA", "V"),
@@ -300,6 +323,11 @@ def main():
         sys.exit(2)
 
     w = W.spec(args.workload, args.k) if args.workload == "c4" else W.spec(args.workload)
+    if args.causal:
+        if w.queries != "action":
+            print(f"--causal needs an action-token workload (c4, actkv, sentinel), not {w.name}", file=sys.stderr)
+            sys.exit(2)
+        w = dataclasses.replace(w, causal=True)
     log(f"[bench] workload {describe(w)}")
     t0 = time.perf_counter()
     workers = W.gen.default_workers()
@@ -334,6 +362,8 @@ def main():
                                bias=data["bias"])
         pristine = None
     del data
+    if w.causal:
+        b.shape.row_pos = P.device_tensor(W.row_positions(w, "action"))
     if w.lse_supplied:  # the harness computes the supplied LSE with the library's own LSE pass
         lse = torch.empty((w.S, w.H * w.G, w.q), dtype=torch.float32, device="cuda")
         ws = torch.empty(max(256, A.kvc_lse_workspace_size(b.shape, b.kview())), dtype=torch.uint8, device="cuda")

@@ -96,6 +96,7 @@ class Workload:
     scale: float = 0.0     # 0 -> 1/sqrt(d)
     seg_start: int = 0     # > 0 or seg_len > 0: compact only this segment (one agent turn)
     seg_len: int = 0
+    causal: bool = False   # action-query rows see only the keys up to their own positions
 
     @property
     def R(self) -> int:
