@@ -96,6 +96,9 @@ thread_local std::string g_err;
 constexpr int kVersion = 300;          // 0.3.0: causal proxy rows (kvc_shape.row_pos)
 constexpr int kBlockSize = 16;         // the one page size this build supports
 constexpr int kMfmaMinRows = 16;       // bf16 units with fewer proxy rows use the VALU path
+constexpr int kLseStage = 64;          // keys per stage of the MFMA LSE pass
+constexpr int64_t kLseSlots = 512;     // LSE workgroups resident at once on gfx950 (256 CUs x 2)
+constexpr int kLseChunkOverhead = 256; // per-workgroup start-up cost, in keys
 constexpr int64_t kMaxRows = 1 << 24;  // proxy rows per unit
 constexpr int kMaxLen = 1 << 28;       // keys per sequence
 constexpr size_t kAlign = 256;
@@ -196,16 +199,39 @@ bool use_mfma(const kvc_shape* sh, const kvc_kv_view* kv) {
   return kv->dtype == KVC_BF16 && sh->group * sh->num_queries >= kMfmaMinRows;
 }
 
-// Key-chunk length of the MFMA LSE pass: the longest chunk that still gives >= 2048 workgroups.
+// Key-chunk length of the MFMA LSE pass. kLseSlots workgroups (256 CUs, two resident each) run at
+// once and a workgroup takes time in proportion to its keys plus kLseChunkOverhead (the rows it
+// loads before its first key). With many workgroups the longest chunk is best (fewer partials,
+// less overhead, and the last partial round costs little). With few, the chunk splits the longest
+// sequence into equal parts (a multiple of the 64-key stage, at least 512 keys), choosing the
+// split that minimises rounds x (chunk + overhead); ties go to the longer chunk.
+int64_t lse_workgroups(const kvc_shape* sh, int64_t rb, int kc) {
+  int64_t wg = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
+  return wg;
+}
+
 int mfma_kchunk(const kvc_shape* sh) {
   const int R = sh->group * sh->num_queries;
   const int64_t rb = lse_mfma_row_blocks(R);
-  for (int kc : {kLseMaxChunk, kLseMaxChunk / 2, kLseMaxChunk / 4}) {
-    int64_t wg = 0;
-    for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
-    if (wg >= 2048) return kc;
+  if (lse_workgroups(sh, rb, kLseMaxChunk) >= 8 * kLseSlots) return kLseMaxChunk;
+  int longest = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) longest = std::max(longest, sh->seq_lens[s]);
+  int best = kLseMaxChunk;
+  int64_t best_cost = INT64_MAX;
+  for (int parts = 1;; ++parts) {
+    const int per = (longest + parts - 1) / parts;
+    const int kc = (per + kLseStage - 1) / kLseStage * kLseStage;
+    if (kc > kLseMaxChunk) continue;
+    if (kc < 512) break;
+    const int64_t rounds = (lse_workgroups(sh, rb, kc) + kLseSlots - 1) / kLseSlots;
+    const int64_t cost = rounds * (std::min(kc, longest) + kLseChunkOverhead);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = kc;
+    }
   }
-  return kLseMaxChunk / 8;
+  return best;
 }
 
 int lse_kchunk(const kvc_shape* sh, const kvc_kv_view* kv) {
