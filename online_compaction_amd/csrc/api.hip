@@ -13,12 +13,13 @@
 
 namespace kvc {
 // kernel launchers (score_mfma.hip, lse_mfma.hip, score_valu.hip, select.hip, retain.hip, compact.hip, am.hip)
-int score_mfma_tiles(int n);
+int score_mfma_tiles(int n, int ksub);
+bool score_mfma_ksub_ok(int ksub, int layout, bool has_bias, bool causal);
 int lse_mfma_row_blocks(int R);
 int score_valu_tiles(int n);
 int contig_tiles(int m, bool f32);
 int paged_tiles(int m);
-hipError_t launch_score_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
+hipError_t launch_score_mfma(int layout, bool has_bias, int ksub, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
                              int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
                              hipStream_t st);
@@ -97,7 +98,8 @@ constexpr int kVersion = 300;          // 0.3.0: causal proxy rows (kvc_shape.ro
 constexpr int kBlockSize = 16;         // the one page size this build supports
 constexpr int kMfmaMinRows = 16;       // bf16 units with fewer proxy rows use the VALU path
 constexpr int kLseStage = 64;          // keys per stage of the MFMA LSE pass
-constexpr int64_t kLseSlots = 512;     // LSE workgroups resident at once on gfx950 (256 CUs x 2)
+constexpr int64_t kCUs = 256;          // compute units of the MI355X
+constexpr int64_t kLseSlots = 2 * kCUs; // LSE workgroups resident at once (two per CU)
 constexpr int kLseChunkOverhead = 256; // per-workgroup start-up cost, in keys
 constexpr int64_t kMaxRows = 1 << 24;  // proxy rows per unit
 constexpr int kMaxLen = 1 << 28;       // keys per sequence
@@ -291,6 +293,33 @@ kvc_status hip_fail(hipError_t e, const char* what) {
   return fail(KVC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Key subtiles per wave of the MFMA score kernel (4, 8 or 9; 64 x that many keys per workgroup).
+// A workgroup streams every proxy row past its keys, so its time grows with its keys plus about
+// one subtile's worth of per-row work; a CU runs its share of the workgroups one after another
+// in effect, and one alone on a CU (nothing to interleave with) still takes about 0.7 of two.
+// 8 unless 4 (three resident per CU) or 9 (fewer, longer workgroups: fills the 512 resident
+// slots when 512-key tiles overshoot them slightly) is estimated at least 5 % faster.
+int score_ksub(const kvc_shape* sh, int layout, bool bias) {
+  auto cost = [&](int ks) -> double {
+    int64_t wg = 0;
+    for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * score_mfma_tiles(sh->seq_lens[s], ks);
+    const int64_t per_cu = (wg + kCUs - 1) / kCUs;
+    return (per_cu >= 2 ? (double)per_cu : 1.4) * (ks + 1);
+  };
+  const double base = cost(8);
+  int best = 8;
+  double best_cost = 0.95 * base;
+  for (int ks : {9, 4}) {
+    if (!score_mfma_ksub_ok(ks, layout, bias, sh->row_pos != nullptr)) continue;
+    const double c = cost(ks);
+    if (c < best_cost) {
+      best_cost = c;
+      best = ks;
+    }
+  }
+  return best;
+}
+
 // Internal LSE: per-chunk partials into ws_partials, then combined into lse_out.
 kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, const float* bias, float* lse_out,
                    void* ws_partials, hipStream_t st) {
@@ -395,12 +424,13 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
   const int layout = layout_of(k);
   const int32_t* index = index_of(k);
   const int H = sh->num_kv_heads;
+  const int ksub = mf ? score_ksub(sh, layout, bias != nullptr) : 0;
   const hipError_t e = for_each_chunk(
       sh, nullptr,
-      [&](int s) { return H * (mf ? score_mfma_tiles(sh->seq_lens[s]) : score_valu_tiles(sh->seq_lens[s])); },
+      [&](int s) { return H * (mf ? score_mfma_tiles(sh->seq_lens[s], ksub) : score_valu_tiles(sh->seq_lens[s])); },
       no_offset, [&](const SeqTable& T) {
         if (mf)
-          return launch_score_mfma(layout, bias != nullptr, q, k->data, index, k->max_blocks, lse_rows, bias,
+          return launch_score_mfma(layout, bias != nullptr, ksub, q, k->data, index, k->max_blocks, lse_rows, bias,
                                    sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
         return launch_score_valu(k->dtype == KVC_F32, layout, bias != nullptr, q, k->data, index, k->max_blocks,
                                  lse_rows, bias, sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T,

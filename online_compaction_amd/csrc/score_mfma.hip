@@ -19,20 +19,17 @@ using namespace mfma;
 
 namespace {
 
-#ifndef KVC_SCORE_KSUB
-#define KVC_SCORE_KSUB 8
-#endif
 #ifndef KVC_SCORE_OCC
 #define KVC_SCORE_OCC 2
 #endif
-constexpr int kScoreSub = KVC_SCORE_KSUB;           // key subtiles per wave
-constexpr int kScoreKeys = 4 * 16 * kScoreSub;      // keys per workgroup
-constexpr int kBufs = 3;                            // LDS stage buffers (two loads in flight)
+constexpr int kBufs = 3;  // LDS stage buffers (two loads in flight)
 
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------
-// Scores. Work item = (sequence, KV head, 512-key tile).
+// Scores. Work item = (sequence, KV head, key tile of 64 * KSUB keys): each of the 4 waves holds
+// KSUB 16-key subtiles (8 by default; 4 or 9 when that fills the GPU's resident workgroups better,
+// chosen by the host).
 // lse: natural-log LSE per proxy row, [S][H*G][q] == [unit][R].
 // pw = 2: s_j = sqrt((1/R) sum_r alpha_rj^2) (the TE score); pw = 1: (1/R) sum_r alpha_rj, the
 // mean attention weight the proxy rows give key j (the per-entry action-attention tally of ActKV).
@@ -41,11 +38,13 @@ constexpr int kBufs = 3;                            // LDS stage buffers (two lo
 // the stage's row positions arrive with its rows, and per stage and wave the 128 keys are either
 // all visible to the stage's 64 rows (the plain epilogue), all hidden (the stage is skipped), or
 // masked element by element.
-template <int LAYOUT, bool BIAS, bool CAUSAL>
+template <int LAYOUT, bool BIAS, bool CAUSAL, int KSUB>
 __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, const int32_t* __restrict__ rpos,
     float* __restrict__ scores, int H, int R, int64_t n_max, float scale, int pw, int dead, SeqTable T) {
+  constexpr int kScoreSub = KSUB;               // key subtiles per wave
+  constexpr int kScoreKeys = 4 * 16 * kScoreSub;  // keys per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t qs[kBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float lss[kBufs][kStage];
   __shared__ __attribute__((aligned(16))) int32_t pss[CAUSAL ? kBufs : 1][kStage];
@@ -218,32 +217,83 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
 // ------------------------------------------------------------------------------------------------
 // launcher
 // ------------------------------------------------------------------------------------------------
-int score_mfma_tiles(int n) { return (n + kScoreKeys - 1) / kScoreKeys; }
+int score_mfma_tiles(int n, int ksub) { return (n + 64 * ksub - 1) / (64 * ksub); }
 
-hipError_t launch_score_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
+bool score_mfma_ksub_ok(int ksub, int layout, bool has_bias, bool causal) {
+  if (ksub == 4 || ksub == 8) return true;
+  return ksub == 9 && !causal && !(layout == kSlots && has_bias);
+}
+
+namespace {
+
+template <int L, bool B, bool C, int KS>
+void launch_ks(dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const int32_t* table,
+               int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores, int H,
+               int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
+  score_mfma<L, B, C, KS><<<grid, dim3(kThreads), 0, st>>>(q, k, table, max_blocks, lse, bias, rpos, scores, H, R,
+                                                            n_max, scale, pw, dead, T);
+}
+
+template <int L, bool B, bool C>
+void launch_c(int ksub, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const int32_t* table,
+              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores, int H, int R,
+              int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
+  if (ksub == 4) {
+    launch_ks<L, B, C, 4>(grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead, T);
+  } else if (ksub == 9) {
+    if constexpr (!C && !(L == kSlots && B))
+      launch_ks<L, B, C, 9>(grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead,
+                            T);
+  } else {
+    launch_ks<L, B, C, 8>(grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead, T);
+  }
+}
+
+template <int L, bool B>
+void launch_b(int ksub, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const int32_t* table,
+              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores, int H, int R,
+              int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
+  if (rpos)
+    launch_c<L, B, true>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw,
+                         dead, T);
+  else
+    launch_c<L, B, false>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw,
+                          dead, T);
+}
+
+template <int L>
+void launch_l(bool has_bias, int ksub, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k,
+              const int32_t* table, int max_blocks, const float* lse, const float* bias, const int32_t* rpos,
+              float* scores, int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
+  if (has_bias)
+    launch_b<L, true>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead,
+                      T);
+  else
+    launch_b<L, false>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead,
+                       T);
+}
+
+}  // namespace
+
+hipError_t launch_score_mfma(int layout, bool has_bias, int ksub, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
                              int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
                              hipStream_t st) {
+  // 9 subtiles per wave fit the registers only without the causal mask and outside the biased
+  // slot-map variant (score_mfma_ksub_ok); the host asks for them only there
+  if (!score_mfma_ksub_ok(ksub, layout, has_bias, rpos != nullptr)) return hipErrorInvalidValue;
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
-  dim3 grid(T.total), block(kThreads);
-#define KVC_SCORE_LAUNCH(L, B, C)                                                                            \
-  score_mfma<L, B, C><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, \
-                                              scale, pw, dead, T)
-#define KVC_SCORE_LAUNCH_C(L, B)            \
-  do {                                     \
-    if (rpos) KVC_SCORE_LAUNCH(L, B, true);  \
-    else KVC_SCORE_LAUNCH(L, B, false);      \
-  } while (0)
-  if (layout == kPaged) {
-    if (has_bias) KVC_SCORE_LAUNCH_C(kPaged, true); else KVC_SCORE_LAUNCH_C(kPaged, false);
-  } else if (layout == kSlots) {
-    if (has_bias) KVC_SCORE_LAUNCH_C(kSlots, true); else KVC_SCORE_LAUNCH_C(kSlots, false);
-  } else {
-    if (has_bias) KVC_SCORE_LAUNCH_C(kContig, true); else KVC_SCORE_LAUNCH_C(kContig, false);
-  }
-#undef KVC_SCORE_LAUNCH_C
-#undef KVC_SCORE_LAUNCH
+  const dim3 grid(T.total);
+  if (layout == kPaged)
+    launch_l<kPaged>(has_bias, ksub, grid, st, qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale,
+                     pw, dead, T);
+  else if (layout == kSlots)
+    launch_l<kSlots>(has_bias, ksub, grid, st, qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale,
+                     pw, dead, T);
+  else
+    launch_l<kContig>(has_bias, ksub, grid, st, qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max,
+                      scale, pw, dead, T);
   return hipGetLastError();
 }
 

@@ -157,3 +157,21 @@ def slot_setup(w, data, dead_frac, rng):
             smap[s, h, :n] = np.where(lv, base, dead)
             live[s, h, :n] = lv
     return pool, smap, live, dead
+
+
+def score_key_subtiles(lens, H: int, causal: bool = False, slot_bias: bool = False) -> int:
+    """The keys per wave (in 16-key subtiles) that the library picks for the MFMA score kernel,
+    restated here so that a test can make sure it runs the variant it names: 8, unless 4 or 9 is
+    estimated at least 5 % faster (per CU, ceil(workgroups / 256) workgroups of (subtiles + 1)
+    units each, one alone counting 1.4; 9 never with causal rows or a biased slot map)."""
+    def cost(ks):
+        wg = sum(H * -(-n // (64 * ks)) for n in lens)
+        per = -(-wg // 256)
+        return (per if per >= 2 else 1.4) * (ks + 1)
+    best, best_cost = 8, 0.95 * cost(8)
+    for ks in (9, 4):
+        if ks == 9 and (causal or slot_bias):
+            continue
+        if cost(ks) < best_cost:
+            best, best_cost = ks, cost(ks)
+    return best

@@ -282,3 +282,25 @@ def test_paged_degenerate_budgets():
 def test_paged_supplied_lse():
     run_paged_case(W.custom("paged_lse", 123, S=2, H=2, G=4, q=12, n=(260, 1500), dtype="bf16", keys="mixture",
                             queries="cluster", paged=True, table="identity", block_size=16), supply_lse=True)
+
+
+@pytest.mark.parametrize("case", ["subtiles9_contig", "subtiles9_paged_bias", "subtiles8_contig"])
+def test_score_key_tile_variants(case):
+    """The score kernel holds 4, 8 or 9 key subtiles per wave, picked from the workgroup count.
+    Small cases run 4; these full-length trajectories with 16 proxy rows run the other two."""
+    from tests.parity import score_key_subtiles
+    if case == "subtiles9_contig":
+        w = W.custom("kt9c", 121, S=1, H=8, G=4, q=4, n=(33000,), dtype="bf16", keys="mixture", queries="cluster")
+    elif case == "subtiles9_paged_bias":
+        w = W.custom("kt9p", 122, S=1, H=8, G=4, q=4, n=(33000,), dtype="bf16", keys="mixture", queries="cluster",
+                     paged=True, table="permuted", block_size=16, bias_tail=0.5)
+    else:
+        w = W.custom("kt8c", 123, S=4, H=8, G=4, q=4, n=(33000,) * 4, dtype="bf16", keys="mixture",
+                     queries="cluster")
+    want = int(case[8])
+    assert score_key_subtiles(list(w.n), w.H) == want, "the case no longer selects the variant it names"
+    if w.paged:
+        run_paged_case(w)
+    else:
+        run_contig_case(w)
+
