@@ -533,31 +533,38 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
 // A function of the shape alone, so that the workspace size and the fit agree.
 static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2) {
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
-  int64_t t1 = 0, t2 = 0;
+  int64_t t1 = 0, t2 = 0, out1 = 0, out2 = 0;
   int st1 = INT32_MAX, st2 = am_stages_cols(R);
   for (int s = 0; s < sh->num_seqs; ++s) {
     if (m[s] == 0) continue;
     t1 += (int64_t)H * am_gemm_tiles(R);
     t2 += (int64_t)H * am_gemm_tiles((m[s] + 63) / 64 * 64);
+    out1 += (int64_t)H * R * 128;
+    out2 += (int64_t)H * ((m[s] + 63) / 64 * 64) * 128;
     st1 = std::min(st1, am_stages_rows(m[s]));
   }
-  // the split count that needs the fewest rounds of workgroups (two per CU) times stages per
-  // split, fewer splits on a tie
-  auto pick = [](int64_t tiles, int stages) {
+  // The split count that minimises rounds of workgroups (two per CU) x stages per split, plus
+  // the round trip of the partial products through memory: each split writes the whole output
+  // once and the split sum reads it back (8 bytes per output element), priced against a round
+  // of stages, in which the 512 resident workgroups read 16 KB of the left operand each.
+  // Fewer splits on a tie.
+  auto pick = [](int64_t tiles, int stages, int64_t out) {
     if (tiles == 0) return 1;
+    const double part = 8.0 * (double)out / (512.0 * 16384.0);
     int best = 1;
-    int64_t best_cost = INT64_MAX;
+    double best_cost = 1e300;
     for (int sp = 1; sp <= 8 && sp <= std::max(1, stages / 4); ++sp) {
       const int64_t rounds = (tiles * sp + 511) / 512, per = (stages + sp - 1) / sp;
-      if (rounds * per < best_cost) {
-        best_cost = rounds * per;
+      const double cost = (double)(rounds * per) + (sp > 1 ? sp * part : 0.0);
+      if (cost < best_cost) {
+        best_cost = cost;
         best = sp;
       }
     }
     return best;
   };
-  *S1 = pick(t1, st1);
-  *S2 = pick(t2, st2);
+  *S1 = pick(t1, st1, out1);
+  *S2 = pick(t2, st2, out2);
 }
 
 static size_t am_bytes(const kvc_shape* sh, const int32_t* m) {
