@@ -47,22 +47,57 @@ constexpr int kRowChunk = 64;  // rows per partial column sum
 
 __host__ __device__ constexpr int64_t pad64(int64_t x) { return (x + 63) & ~int64_t(63); }
 
+// E / P_C [H][R][ldm], PT [H][ldm][Rp], ZT [H][128][Rp] and VT [H][128][ldm] (Rp = R rounded up
+// to 64): P_C, PT, ZT and VT are held in the split layout below.
 struct AmWs {
-  float *E, *PT, *Y, *Z, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
+  float *E, *PT, *Y, *ZT, *VT, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
   uint32_t* mekey;
-  int ldm;
+  int ldm, Rp;
 };
+
+// The split layout of a float32 matrix row: each group of 8 consecutive elements keeps its 32
+// bytes, as the 8 bfloat16 high parts followed by the 8 bfloat16 low parts (hi = bf16(x),
+// lo = bf16(x - hi), so hi + lo carries x to a relative 2^-16). A matrix converts in place, and
+// the 16-byte halves load straight into the bf16 MFMA operand tiles of the split products.
+__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
+  bf16x8 h, l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 b = (__bf16)x[e];
+    h[e] = b;
+    l[e] = (__bf16)(x[e] - (float)b);
+  }
+  hi = __builtin_bit_cast(u32x4, h);
+  lo = __builtin_bit_cast(u32x4, l);
+}
+// group g of a split row (8 elements, 32 bytes) from 8 floats
+__device__ __forceinline__ void put_split8(float* row, int g, const float* x) {
+  u32x4 hi, lo;
+  split8(x, hi, lo);
+  u32x4* d = reinterpret_cast<u32x4*>(row + 8 * g);
+  d[0] = hi;
+  d[1] = lo;
+}
+// element k of a split row
+__device__ __forceinline__ void put_split1(float* row, int k, float x) {
+  uint16_t* d = reinterpret_cast<uint16_t*>(row + 8 * (k >> 3));
+  const __bf16 b = (__bf16)x;
+  d[k & 7] = __builtin_bit_cast(uint16_t, b);
+  d[8 + (k & 7)] = __builtin_bit_cast(uint16_t, (__bf16)(x - (float)b));
+}
 
 __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const AmCfg& C) {
   const int64_t m = T.m[i], H = C.H, R = C.R;
-  const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
+  const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk, Rp = pad64(R);
   AmWs w;
   w.ldm = (int)ldm;
+  w.Rp = (int)Rp;
   w.E = ws + T.off[i];
   w.PT = w.E + pad64(H * R * ldm);
-  w.Y = w.PT + pad64(H * R * ldm);
-  w.Z = w.Y + pad64(H * R * kD);
-  w.Zp = w.Z + pad64(H * R * kD);
+  w.Y = w.PT + pad64(H * ldm * Rp);
+  w.ZT = w.Y + pad64(H * R * kD);
+  w.VT = w.ZT + pad64(H * kD * Rp);
+  w.Zp = w.VT + pad64(H * kD * ldm);
   w.Up = w.Zp + (C.S1 > 1 ? C.S1 : 0) * pad64(H * R * kD);
   w.part = w.Up + (C.S2 > 1 ? C.S2 : 0) * pad64(H * ldm * kD);
   w.u = w.part + pad64(H * nr * ldm);
@@ -91,9 +126,10 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 // Floats of one sequence's workspace (the layout above).
 int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2) {
-  const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk;
+  const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk, Rp = pad64(R);
   const int64_t rk = pad64((int64_t)H * R * kD);
-  return 2 * pad64((int64_t)H * R * ldm) + 2 * rk + (S1 > 1 ? S1 : 0) * rk +
+  return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * ldm * Rp) + rk + pad64((int64_t)H * kD * Rp) +
+         pad64((int64_t)H * kD * ldm) + (S1 > 1 ? S1 : 0) * rk +
          (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) + pad64((int64_t)H * R) +
          pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H);
 }
@@ -262,29 +298,39 @@ __global__ __launch_bounds__(256) void am_cols_part(const float* __restrict__ w_
   const int64_t unit = (int64_t)s * C.H + h;
   const int r0 = rc * kRowChunk, r1 = min(R, r0 + kRowChunk);
   if constexpr (MODE == 2) {
-    // P_C in place of E, its column sums, and P_C^T (row j of PT holds column j): the chunk's
-    // 64 x 256 block of P_C is staged in LDS (row pitch 257: a column read is conflict-free),
-    // then each wave writes 64 PT rows, 64 consecutive floats each.
+    // P_C in place of E and P_C^T (row j of PT holds column j), both in the split layout, and
+    // the column sums of P_C. The chunk's 64 x 256 block of P_C is staged in LDS (row pitch 257:
+    // a column read is conflict-free); after the barrier every float of the block has been read,
+    // so the block is rewritten in place, 8 consecutive columns of a row per group, and PT gets
+    // 8 consecutive rows of a column per group (zeros for the rows past R up to Rp).
     __shared__ float tile[kRowChunk][257];
     float acc = 0.0f;
+    float* E = W.E + (int64_t)h * R * ldm;
     if (j < ldm) {
-      float* e = W.E + (int64_t)h * R * ldm + j;
       const float* u = W.u + (int64_t)h * R;
       const float wj = j < m ? w_all[unit * C.m_max + j] : 0.0f;
       for (int r = r0; r < r1; ++r) {
-        const float x = e[(int64_t)r * ldm];
+        const float x = E[(int64_t)r * ldm + j];
         const float pc = u[r] > 0.0f ? x * wj / u[r] : 0.0f;
-        if (j < m) e[(int64_t)r * ldm] = pc;
         tile[r - r0][threadIdx.x] = pc;
         acc += pc;
       }
       W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
     }
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    for (int c = wave; c < 256; c += 4) {
-      const int jj = cb * 256 + c;
-      if (jj < ldm && r0 + lane < r1) W.PT[((int64_t)h * ldm + jj) * R + r0 + lane] = tile[lane][c];
+    const int cols = min(256, ldm - cb * 256);  // a multiple of 64
+    for (int q = threadIdx.x; q < kRowChunk * 32; q += 256) {
+      const int rr = q >> 5, gq = q & 31;
+      if (r0 + rr < r1 && 8 * gq < cols) put_split8(E + (int64_t)(r0 + rr) * ldm + cb * 256, gq, &tile[rr][8 * gq]);
+    }
+    const int Rp = W.Rp;
+    for (int q = threadIdx.x; q < 256 * (kRowChunk / 8); q += 256) {
+      const int c = q >> 3, gq = q & 7;
+      if (c >= cols) continue;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = r0 + 8 * gq + e < r1 ? tile[8 * gq + e][c] : 0.0f;
+      put_split8(W.PT + ((int64_t)h * ldm + cb * 256 + c) * Rp + r0, gq, x);
     }
   } else {
     if (j >= ldm) return;
@@ -364,17 +410,6 @@ constexpr int kTgtThreads = 512;
 constexpr int kVtPitch = 72;  // bf16 per transposed value row (64 keys + 8 padding)
 constexpr int kPPitch = 68;   // per-wave weight tile pitch (float32)
 
-__device__ __forceinline__ void split8(const float* x, u32x4& hi, u32x4& lo) {
-  bf16x8 h, l;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const __bf16 b = (__bf16)x[e];
-    h[e] = b;
-    l[e] = (__bf16)(x[e] - (float)b);
-  }
-  hi = __builtin_bit_cast(u32x4, h);
-  lo = __builtin_bit_cast(u32x4, l);
-}
 }  // namespace
 
 template <int LAYOUT>
@@ -542,10 +577,10 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   local /= S;
   const int tile = local % tiles, h = local / tiles;
   const int64_t unit = (int64_t)s * C.H + h;
-  const float* PC = W.E + (int64_t)h * R * ldm;
-  const float* PTh = W.PT + (int64_t)h * ldm * R;
-  const float* vc = vc_all + unit * C.m_max * (int64_t)kD;
-  const float* Zh = W.Z + (int64_t)h * R * kD;
+  const float* PC = W.E + (int64_t)h * R * ldm;           // split rows of P_C
+  const float* PTh = W.PT + (int64_t)h * ldm * W.Rp;      // split rows of P_C^T
+  const float* VTh = W.VT + (int64_t)h * kD * ldm;        // split rows of Vc^T
+  const float* ZTh = W.ZT + (int64_t)h * kD * W.Rp;       // split rows of Z^T
   const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
   const int per = (nst + S - 1) / S;
   const int st0 = sp * per, st1 = min(nst, st0 + per);
@@ -553,67 +588,38 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   const int wr = wave >> 1, wc = wave & 1;
 
   // staging: A row ar of the tile, contraction indices 16 ak .. + 15; B column bd, indices
-  // 16 bk .. + 15 (chunks 2 ak, 2 ak + 1 and 2 bk, 2 bk + 1)
+  // 16 bk .. + 15 (chunks 2 ak, 2 ak + 1 and 2 bk, 2 bk + 1). Every operand is stored split, so
+  // a thread's 16 indices are 64 contiguous bytes: high parts of the first 8, their low parts,
+  // then the same for the next 8, copied to the high and low LDS tiles unchanged. The
+  // contraction never leaves the stored rows (ldm and Rp are multiples of 64).
   const int ar = tid >> 1, ak = tid & 1;
   const int bd = tid & 127, bk = tid >> 7;
-  float ra[16], rb[16];
+  const int arow = tile * kGTile + ar;                    // A row: output row of the tile
+  const bool alive = arow < (KIND == 0 ? R : ldm);
+  const u32x4* asrc = reinterpret_cast<const u32x4*>(
+      KIND == 0 ? PC + (int64_t)min(arow, R - 1) * ldm + 16 * ak : PTh + (int64_t)min(arow, ldm - 1) * W.Rp + 16 * ak);
+  const u32x4* bsrc = reinterpret_cast<const u32x4*>(KIND == 0 ? VTh + (int64_t)bd * ldm + 16 * bk
+                                                               : ZTh + (int64_t)bd * W.Rp + 16 * bk);
+  u32x4 ra[4], rb[4];
   auto load = [&](int stg) {
-    const int k0 = stg * 32;
-    if constexpr (KIND == 0) {  // A = P_C[128 rows][32 keys], row-major in memory
-      const int r = tile * kGTile + ar;
-      const float4* src = reinterpret_cast<const float4*>(PC + (int64_t)min(r, R - 1) * ldm + k0 + 16 * ak);
+    const int o = stg * 8;  // 32 indices = 8 u32x4 per row
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const float4 x = src[c];
-        ra[4 * c] = r < R ? x.x : 0.0f;
-        ra[4 * c + 1] = r < R ? x.y : 0.0f;
-        ra[4 * c + 2] = r < R ? x.z : 0.0f;
-        ra[4 * c + 3] = r < R ? x.w : 0.0f;
-      }
-    } else {  // A = P_C^T[128 keys][32 rows], row-major in PT
-      const int j = tile * kGTile + ar;
-      const int r0 = k0 + 16 * ak;
-      const float* src = PTh + (int64_t)min(j, ldm - 1) * R;
-      if (r0 + 16 <= R && (R & 3) == 0) {  // whole, 16-byte aligned row segment
-        const float4* s4 = reinterpret_cast<const float4*>(src + r0);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float4 x = s4[c];
-          ra[4 * c] = j < ldm ? x.x : 0.0f;
-          ra[4 * c + 1] = j < ldm ? x.y : 0.0f;
-          ra[4 * c + 2] = j < ldm ? x.z : 0.0f;
-          ra[4 * c + 3] = j < ldm ? x.w : 0.0f;
-        }
-      } else {  // the last, partial stage of rows (or rows of a length not a multiple of 4)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float x = src[min(r0 + e, R - 1)];
-          ra[e] = (r0 + e < R && j < ldm) ? x : 0.0f;
-        }
-      }
+    for (int c = 0; c < 4; ++c) {
+      ra[c] = asrc[o + c];
+      rb[c] = bsrc[o + c];
     }
+    if (!alive) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int kk = k0 + 16 * bk + e;
-      if constexpr (KIND == 0) {  // B = Vc[32 keys][128]
-        const float x = vc[(int64_t)min(kk, m - 1) * kD + bd];
-        rb[e] = kk < m ? x : 0.0f;
-      } else {  // B = Z[32 rows][128]
-        const float x = Zh[(int64_t)min(kk, R - 1) * kD + bd];
-        rb[e] = kk < R ? x : 0.0f;
-      }
+      for (int c = 0; c < 4; ++c) ra[c] = u32x4{0u, 0u, 0u, 0u};
     }
   };
   auto store = [&](int buf) {
-    u32x4 hi, lo;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      split8(ra + 8 * c, hi, lo);
-      *reinterpret_cast<u32x4*>(&Ah[buf][gswz(ar, 2 * ak + c)]) = hi;
-      *reinterpret_cast<u32x4*>(&Al[buf][gswz(ar, 2 * ak + c)]) = lo;
-      split8(rb + 8 * c, hi, lo);
-      *reinterpret_cast<u32x4*>(&Bh[buf][gswz(bd, 2 * bk + c)]) = hi;
-      *reinterpret_cast<u32x4*>(&Bl[buf][gswz(bd, 2 * bk + c)]) = lo;
+      *reinterpret_cast<u32x4*>(&Ah[buf][gswz(ar, 2 * ak + c)]) = ra[2 * c];
+      *reinterpret_cast<u32x4*>(&Al[buf][gswz(ar, 2 * ak + c)]) = ra[2 * c + 1];
+      *reinterpret_cast<u32x4*>(&Bh[buf][gswz(bd, 2 * bk + c)]) = rb[2 * c];
+      *reinterpret_cast<u32x4*>(&Bl[buf][gswz(bd, 2 * bk + c)]) = rb[2 * c + 1];
     }
   };
 
@@ -663,16 +669,25 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
       for (int e = 0; e < 4; ++e) {
         const int r = tile * kGTile + 64 * wr + 16 * a + 4 * g + e;
         const int col = 64 * wc + 16 * b + c16;
-        if constexpr (KIND == 0) {
+        if constexpr (KIND == 0) {  // Z = P_C Vc - Y, kept as split rows of Z^T (zeros past R)
           const int64_t o = (int64_t)h * R * kD + (int64_t)r * kD + col;
-          if (r < R) {
-            if (S == 1) W.Z[o] = acc[a][b][e] - W.Y[o];
-            else W.Zp[(int64_t)sp * pad64((int64_t)C.H * R * kD) + o] = acc[a][b][e];
+          if (S == 1) {
+            if (r < W.Rp) put_split1(W.ZT + ((int64_t)h * kD + col) * W.Rp, r, r < R ? acc[a][b][e] - W.Y[o] : 0.0f);
+          } else if (r < R) {
+            W.Zp[(int64_t)sp * pad64((int64_t)C.H * R * kD) + o] = acc[a][b][e];
           }
-        } else {
+        } else {  // Vc -= eta P_C^T Z, with its split rows of Vc^T (zeros past m)
           const int64_t o = (int64_t)r * kD + col;
           if (S == 1) {
-            if (r < m) vc_all[unit * C.m_max * (int64_t)kD + o] -= W.eta[h] * acc[a][b][e];
+            if (r < ldm) {
+              float v = 0.0f;
+              if (r < m) {
+                float* d = vc_all + unit * C.m_max * (int64_t)kD + o;
+                v = *d - W.eta[h] * acc[a][b][e];
+                *d = v;
+              }
+              put_split1(W.VT + ((int64_t)h * kD + col) * ldm, r, v);
+            }
           } else if (r < ldm) {
             W.Up[(int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD + o] = acc[a][b][e];
           }
@@ -684,10 +699,13 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
 int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 
 // Split sums, in split order: Z = sum_s Zp[s] - Y (KIND 0, work item = (seq, head, 64 rows)) and
-// Vc_j -= eta sum_s Up[s]_j (KIND 1, work item = (seq, head, 64 kept keys)).
+// Vc_j -= eta sum_s Up[s]_j (KIND 1, work item = (seq, head, 64 kept keys)). The block's results
+// (zeros past R, or past m) are staged in LDS and leave as split rows of Z^T or Vc^T, the form
+// the next product reads; Vc itself is also kept in float32.
 template <int KIND>
 __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
                                                     SeqTable T) {
+  __shared__ float tile[64][kD + 1];
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
@@ -704,30 +722,47 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
   const float* src = (KIND == 0 ? W.Zp + (int64_t)h * R * kD : W.Up + (int64_t)h * ldm * kD);
   for (int x = threadIdx.x; x < 64 * (kD / 4); x += 256) {
     const int row = blk * 64 + (x >> 5), c4 = x & 31;
-    if (row >= lim) continue;
-    const int64_t o = (int64_t)row * kD + 4 * c4;
-    float4 a = *reinterpret_cast<const float4*>(src + o);
-    for (int sp = 1; sp < S; ++sp) {
-      const float4 p = *reinterpret_cast<const float4*>(src + sp * stride + o);
-      a.x += p.x;
-      a.y += p.y;
-      a.z += p.z;
-      a.w += p.w;
+    float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (row < lim) {
+      const int64_t o = (int64_t)row * kD + 4 * c4;
+      float4 a = *reinterpret_cast<const float4*>(src + o);
+      for (int sp = 1; sp < S; ++sp) {
+        const float4 p = *reinterpret_cast<const float4*>(src + sp * stride + o);
+        a.x += p.x;
+        a.y += p.y;
+        a.z += p.z;
+        a.w += p.w;
+      }
+      if constexpr (KIND == 0) {
+        const float4 y = *reinterpret_cast<const float4*>(W.Y + (int64_t)h * R * kD + o);
+        val = make_float4(a.x - y.x, a.y - y.y, a.z - y.z, a.w - y.w);
+      } else {
+        const float f = W.eta[h];
+        float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
+        float4 v = *d;
+        v.x -= f * a.x;
+        v.y -= f * a.y;
+        v.z -= f * a.z;
+        v.w -= f * a.w;
+        *d = v;
+        val = v;
+      }
     }
-    if constexpr (KIND == 0) {
-      const float4 y = *reinterpret_cast<const float4*>(W.Y + (int64_t)h * R * kD + o);
-      *reinterpret_cast<float4*>(W.Z + (int64_t)h * R * kD + o) =
-          make_float4(a.x - y.x, a.y - y.y, a.z - y.z, a.w - y.w);
-    } else {
-      const float f = W.eta[h];
-      float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
-      float4 v = *d;
-      v.x -= f * a.x;
-      v.y -= f * a.y;
-      v.z -= f * a.z;
-      v.w -= f * a.w;
-      *d = v;
-    }
+    float* tr = &tile[x >> 5][4 * c4];
+    tr[0] = val.x;
+    tr[1] = val.y;
+    tr[2] = val.z;
+    tr[3] = val.w;
+  }
+  __syncthreads();
+  const int pitch = KIND == 0 ? W.Rp : ldm;
+  float* dst = (KIND == 0 ? W.ZT : W.VT) + (int64_t)h * kD * pitch + blk * 64;
+  for (int q = threadIdx.x; q < kD * 8; q += 256) {
+    const int d = q >> 3, gq = q & 7;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = tile[8 * gq + e][d];
+    put_split8(dst + (int64_t)d * pitch, gq, x);
   }
 }
 
@@ -748,11 +783,16 @@ __global__ __launch_bounds__(256) void am_init(const uint16_t* __restrict__ v, c
   const int local = t - T.start[i];
   const int h = local / cb;
   const int j = (local - h * cb) * 256 + threadIdx.x;
-  if (j >= m) return;
+  AmWs W = am_ws(const_cast<float*>(ws), T, i, C);
+  if (j >= W.ldm) return;
+  float* vt = W.VT + (int64_t)h * kD * W.ldm;  // split rows of Vc^T: column j of each
+  if (j >= m) {  // padding columns of Vc^T are zero
+    for (int d = 0; d < kD; ++d) put_split1(vt + (int64_t)d * W.ldm, j, 0.0f);
+    return;
+  }
   const int64_t unit = (int64_t)s * C.H + h;
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
-  AmWs W = am_ws(const_cast<float*>(ws), T, i, C);
   w_all[unit * C.m_max + j] = __builtin_amdgcn_exp2f((W.ME[h] - W.M[h]) * kLog2e);  // w = 1 in scaled units
   const int key = min(max(kept[unit * C.m_max + j], 0), n - 1);
   const u32x4* row = key_row<LAYOUT>(v, map, C.H, h, n_max, unit, T.kofs[i] + key);
@@ -763,8 +803,11 @@ __global__ __launch_bounds__(256) void am_init(const uint16_t* __restrict__ v, c
     const uint32_t wd[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      dst[ch * 8 + 2 * e] = bf16_lo(wd[e]);
-      dst[ch * 8 + 2 * e + 1] = bf16_hi(wd[e]);
+      const float lo = bf16_lo(wd[e]), hi = bf16_hi(wd[e]);
+      dst[ch * 8 + 2 * e] = lo;
+      dst[ch * 8 + 2 * e + 1] = hi;
+      put_split1(vt + (int64_t)(ch * 8 + 2 * e) * W.ldm, j, lo);
+      put_split1(vt + (int64_t)(ch * 8 + 2 * e + 1) * W.ldm, j, hi);
     }
   }
 }
