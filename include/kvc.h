@@ -251,7 +251,7 @@ kvc_status kvc_evict_redirect(const kvc_shape* shape, const int32_t* kept, const
  *   beta       device out [S][H][m_max] float32 (natural-log bias per kept key)
  *   v_c        device out [S][H][m_max][d] float32
  *   ws         device workspace of kvc_am_workspace_size(shape, k, v, m, lse != NULL) bytes:
- *              at most about 4 * H * (R * (2 m_s + 10 d) + 8 m_s d) bytes per sequence (the kept
+ *              at most about 4 * H * (R * (2 m_s + 10 d) + 9 m_s d) bytes per sequence (the kept
  *              exponentials and their transpose are materialised, plus up to 8 split partial
  *              sums of each value product; the attention over all n_s keys is not stored)
  * ------------------------------------------------------------------------------------------- */
