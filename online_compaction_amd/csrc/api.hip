@@ -21,12 +21,12 @@ int contig_tiles(int m, bool f32);
 int paged_tiles(int m);
 hipError_t launch_score_mfma(int layout, bool has_bias, int ksub, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
-                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
-                             hipStream_t st);
+                             int H, int R, int64_t n_max, float scale, int pw, int dead, const RowOrder& ord,
+                             const SeqTable& T, hipStream_t st);
 hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                                     int max_blocks, const float* bias, const int32_t* rpos, float2* partials, int H,
-                                    int R, int64_t n_max, float scale, int kchunk, int dead, const SeqTable& T,
-                                    hipStream_t st);
+                                    int R, int64_t n_max, float scale, int kchunk, int dead, const RowOrder& ord,
+                                    const SeqTable& T, hipStream_t st);
 hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int R, int kchunk, const SeqTable& T,
                               hipStream_t st);
 hipError_t launch_score_valu(bool f32, int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
@@ -320,6 +320,16 @@ int score_ksub(const kvc_shape* sh, int layout, bool bias) {
   return best;
 }
 
+// The order the MFMA kernels take the proxy rows in: query-major (the G query heads' rows of one
+// query position together) with causal rows, when 1 < G <= 256 (the multiply-high division is
+// exact there); the stored order otherwise.
+RowOrder row_order(const kvc_shape* sh) {
+  const int G = sh->group;
+  if (!sh->row_pos || G <= 1 || G > 256) return RowOrder{1, sh->num_queries, 0u};
+  const uint32_t magic = (uint32_t)(((uint64_t)1 << 32) / (uint64_t)G + 1);
+  return RowOrder{G, sh->num_queries, magic};
+}
+
 // Internal LSE: per-chunk partials into ws_partials, then combined into lse_out.
 kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, const float* bias, float* lse_out,
                    void* ws_partials, hipStream_t st) {
@@ -344,7 +354,8 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
       [&](const SeqTable& T) {
         if (mf)
           return launch_lse_partials_mfma(layout, has_bias, q, kv->data, index, kv->max_blocks, bias, sh->row_pos,
-                                          parts, H, R, sh->n_max, sh->scale, kc, kv->dead_slot, T, st);
+                                          parts, H, R, sh->n_max, sh->scale, kc, kv->dead_slot, row_order(sh), T,
+                                          st);
         return launch_lse_partials_valu(kv->dtype == KVC_F32, layout, has_bias, q, kv->data, index, kv->max_blocks,
                                         bias, sh->row_pos, parts, H, R, sh->n_max, sh->scale, kv->dead_slot, T, st);
       });
@@ -431,7 +442,8 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
       no_offset, [&](const SeqTable& T) {
         if (mf)
           return launch_score_mfma(layout, bias != nullptr, ksub, q, k->data, index, k->max_blocks, lse_rows, bias,
-                                   sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
+                                   sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, row_order(sh), T,
+                                   st);
         return launch_score_valu(k->dtype == KVC_F32, layout, bias != nullptr, q, k->data, index, k->max_blocks,
                                  lse_rows, bias, sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T,
                                  st);

@@ -46,6 +46,22 @@ struct SeqTable {
 };
 static_assert(sizeof(SeqTable) <= 3800, "SeqTable must fit the kernel-argument segment");
 
+// Order in which the MFMA kernels take a unit's proxy rows when the rows are causal. A unit's
+// R = G * q rows are stored head-major (row g * q + i is query i of query head g); with causal
+// rows the kernels group them query-major instead (work row rho is row (rho mod G) * q + rho / G),
+// so that the rows a wave holds together share query positions and more of its key stages are
+// wholly visible or wholly hidden. g = 1 keeps the stored order. rho / G is one multiply-high by
+// magic = ceil(2^32 / g), exact for rho * g < 2^32 (the host uses it for g <= 256 only).
+struct RowOrder {
+  int32_t g, q;
+  uint32_t magic;
+};
+__device__ __forceinline__ int row_of(const RowOrder& o, int rho) {
+  if (o.g == 1) return rho;
+  const int i = (int)__umulhi((uint32_t)rho, o.magic);
+  return (rho - i * o.g) * o.q + i;
+}
+
 // Map a dispatch-ordered block index to a logical work index so that logically consecutive
 // work items run on the same XCD (blocks are dispatched round-robin over the 8 XCDs, each with
 // its own L2): neighbours then share the operands they re-read.

@@ -38,7 +38,7 @@ template <int LAYOUT, bool BIAS, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ bias, const int32_t* __restrict__ rpos, float2* __restrict__ partials,
-    int H, int R, int64_t n_max, float scale, int kchunk, int dead, SeqTable T) {
+    int H, int R, int64_t n_max, float scale, int kchunk, int dead, RowOrder ord, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t ks_[kLseBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float kts[BIAS ? kLseBufs : 1][kStage];
   // causal: the positions of the workgroup's rows (read only by the stages that mask, so they
@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
 
   const int kbeg = kc * kchunk;
   const int kend = min(n, kbeg + kchunk);
-  const int nst = (kend - kbeg + kStage - 1) / kStage;
+  int nst = (kend - kbeg + kStage - 1) / kStage;
   const float c2 = kLog2e * scale;
 
   // paged: the chunk's block-table entries (at most kchunk / 16 + 1 <= kLseMaxChunk / 16 + 1,
@@ -105,7 +105,8 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   for (int sub = 0; sub < kSub; ++sub) {
     const int r = row0 + sub * 16 + c16;
     if (r < R) {
-      const u32x4* p = reinterpret_cast<const u32x4*>(qu + (int64_t)r * kHeadDim);
+      const int rr = CAUSAL ? row_of(ord, r) : r;  // stored row (causal rows are taken query-major)
+      const u32x4* p = reinterpret_cast<const u32x4*>(qu + (int64_t)rr * kHeadDim);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) qb[sub][kk] = as_bf16x8(p[4 * kk + g]);
     } else {
@@ -120,13 +121,19 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     int lo = INT32_MAX, hi = INT32_MIN;
 #pragma unroll
     for (int sub = 0; sub < kSub; ++sub) {
-      const int p = rpos[unit * (int64_t)R + min(row0 + sub * 16 + c16, R - 1)];
+      const int p = rpos[unit * (int64_t)R + row_of(ord, min(row0 + sub * 16 + c16, R - 1))];
       if (g == 0) pls[wave * kPerWave + sub * 16 + c16] = p;
       lo = min(lo, p);
       hi = max(hi, p);
     }
     wpmin = wave_min(lo);
     wpmax = wave_max(hi);
+    // the workgroup stops after the last stage that any of its rows sees (no loads past it)
+    __shared__ int wgmax[4];
+    if (lane == 0) wgmax[wave] = wpmax;
+    __syncthreads();
+    const int last = max(max(wgmax[0], wgmax[1]), max(wgmax[2], wgmax[3]));
+    nst = last < kbeg ? 0 : min(nst, (last - kbeg) / kStage + 1);
   }
 
   // A stage (64 keys) goes global -> LDS without passing through registers: each wave issues 4
@@ -274,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // compiler has no register load left to wait for (its own waits would be vmcnt(0)); the
   // first barrier below also publishes the causal positions
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  issue(0);
+  if (nst > 0) issue(0);  // (causal rows may leave a workgroup nothing to do)
   if (nst > 1) issue(1);
   for (int st = 0; st < nst; ++st) {
     if (st + 1 < nst) {
@@ -312,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       m1 = mm;
     }
     const int r = row0 + sub * 16 + c16;
-    if (g == 0 && r < R) partials[pbase + r] = make_float2(m1, s1);
+    if (g == 0 && r < R) partials[pbase + (CAUSAL ? row_of(ord, r) : r)] = make_float2(m1, s1);
   }
 }
 
@@ -350,14 +357,14 @@ int lse_mfma_row_blocks(int R) { return (R + kPerBlock - 1) / kPerBlock; }
 
 hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
                                     int max_blocks, const float* bias, const int32_t* rpos, float2* partials, int H,
-                                    int R, int64_t n_max, float scale, int kchunk, int dead, const SeqTable& T,
-                                    hipStream_t st) {
+                                    int R, int64_t n_max, float scale, int kchunk, int dead, const RowOrder& ord,
+                                    const SeqTable& T, hipStream_t st) {
   const auto* qq = static_cast<const uint16_t*>(q);
   const auto* kk = static_cast<const uint16_t*>(k);
   dim3 grid(T.total), block(kThreads);
 #define KVC_LSE_LAUNCH(L, B, C)                                                                                  \
   lse_partials_mfma<L, B, C><<<grid, block, 0, st>>>(qq, kk, table, max_blocks, bias, rpos, partials, H, R, n_max, \
-                                                     scale, kchunk, dead, T)
+                                                     scale, kchunk, dead, ord, T)
 #define KVC_LSE_LAUNCH_C(L, B)            \
   do {                                   \
     if (rpos) KVC_LSE_LAUNCH(L, B, true);  \

@@ -42,7 +42,7 @@ template <int LAYOUT, bool BIAS, bool CAUSAL, int KSUB>
 __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
     int max_blocks, const float* __restrict__ lse, const float* __restrict__ bias, const int32_t* __restrict__ rpos,
-    float* __restrict__ scores, int H, int R, int64_t n_max, float scale, int pw, int dead, SeqTable T) {
+    float* __restrict__ scores, int H, int R, int64_t n_max, float scale, int pw, int dead, RowOrder ord, SeqTable T) {
   constexpr int kScoreSub = KSUB;               // key subtiles per wave
   constexpr int kScoreKeys = 4 * 16 * kScoreSub;  // keys per workgroup
   __shared__ __attribute__((aligned(16))) uint8_t qs[kBufs][kStage * 256];
@@ -108,15 +108,20 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = (wave * 4 + j) * 4 + (lane >> 4);
-      const int r = min(r0 + row, R - 1);
+      int r = min(r0 + row, R - 1);
+      if constexpr (CAUSAL) r = row_of(ord, r);
       dma16(reinterpret_cast<const u32x4*>(qu + (int64_t)r * kHeadDim) + ((lane & 15) ^ (row & 15)),
             &qs[b][(wave * 4 + j) * 1024]);
     }
-    if (lane < 16) dma4(lu + min(r0 + wave * 16 + lane, R - 1), &lss[b][wave * 16]);
-    if constexpr (CAUSAL)
-      if (lane < 16)
-        dma4(reinterpret_cast<const float*>(rpos + unit * (int64_t)R + min(r0 + wave * 16 + lane, R - 1)),
-             &pss[b][wave * 16]);
+    if constexpr (CAUSAL) {
+      if (lane < 16) {
+        const int r = row_of(ord, min(r0 + wave * 16 + lane, R - 1));
+        dma4(lu + r, &lss[b][wave * 16]);
+        dma4(reinterpret_cast<const float*>(rpos + unit * (int64_t)R + r), &pss[b][wave * 16]);
+      }
+    } else {
+      if (lane < 16) dma4(lu + min(r0 + wave * 16 + lane, R - 1), &lss[b][wave * 16]);
+    }
   };
 
   float ssum[kScoreSub];
@@ -226,74 +231,67 @@ bool score_mfma_ksub_ok(int ksub, int layout, bool has_bias, bool causal) {
 
 namespace {
 
+// Everything a score launch passes through to the kernel, bundled for the dispatch below.
+struct ScoreArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* table;
+  int max_blocks;
+  const float* lse;
+  const float* bias;
+  const int32_t* rpos;
+  float* scores;
+  int H, R;
+  int64_t n_max;
+  float scale;
+  int pw, dead;
+  RowOrder ord;
+};
+
 template <int L, bool B, bool C, int KS>
-void launch_ks(dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const int32_t* table,
-               int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores, int H,
-               int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
-  score_mfma<L, B, C, KS><<<grid, dim3(kThreads), 0, st>>>(q, k, table, max_blocks, lse, bias, rpos, scores, H, R,
-                                                            n_max, scale, pw, dead, T);
+void launch_ks(dim3 grid, hipStream_t st, const ScoreArgs& a, const SeqTable& T) {
+  score_mfma<L, B, C, KS><<<grid, dim3(kThreads), 0, st>>>(a.q, a.k, a.table, a.max_blocks, a.lse, a.bias, a.rpos,
+                                                            a.scores, a.H, a.R, a.n_max, a.scale, a.pw, a.dead, a.ord,
+                                                            T);
 }
 
 template <int L, bool B, bool C>
-void launch_c(int ksub, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const int32_t* table,
-              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores, int H, int R,
-              int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
+void launch_c(int ksub, dim3 grid, hipStream_t st, const ScoreArgs& a, const SeqTable& T) {
   if (ksub == 4) {
-    launch_ks<L, B, C, 4>(grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead, T);
+    launch_ks<L, B, C, 4>(grid, st, a, T);
   } else if (ksub == 9) {
-    if constexpr (!C && !(L == kSlots && B))
-      launch_ks<L, B, C, 9>(grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead,
-                            T);
+    if constexpr (!C && !(L == kSlots && B)) launch_ks<L, B, C, 9>(grid, st, a, T);
   } else {
-    launch_ks<L, B, C, 8>(grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead, T);
+    launch_ks<L, B, C, 8>(grid, st, a, T);
   }
 }
 
-template <int L, bool B>
-void launch_b(int ksub, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k, const int32_t* table,
-              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores, int H, int R,
-              int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
-  if (rpos)
-    launch_c<L, B, true>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw,
-                         dead, T);
-  else
-    launch_c<L, B, false>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw,
-                          dead, T);
-}
-
 template <int L>
-void launch_l(bool has_bias, int ksub, dim3 grid, hipStream_t st, const uint16_t* q, const uint16_t* k,
-              const int32_t* table, int max_blocks, const float* lse, const float* bias, const int32_t* rpos,
-              float* scores, int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T) {
-  if (has_bias)
-    launch_b<L, true>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead,
-                      T);
-  else
-    launch_b<L, false>(ksub, grid, st, q, k, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale, pw, dead,
-                       T);
+void launch_l(bool has_bias, int ksub, dim3 grid, hipStream_t st, const ScoreArgs& a, const SeqTable& T) {
+  if (has_bias) {
+    if (a.rpos) launch_c<L, true, true>(ksub, grid, st, a, T);
+    else launch_c<L, true, false>(ksub, grid, st, a, T);
+  } else {
+    if (a.rpos) launch_c<L, false, true>(ksub, grid, st, a, T);
+    else launch_c<L, false, false>(ksub, grid, st, a, T);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_score_mfma(int layout, bool has_bias, int ksub, const void* q, const void* k, const int32_t* table,
                              int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
-                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
-                             hipStream_t st) {
+                             int H, int R, int64_t n_max, float scale, int pw, int dead, const RowOrder& ord,
+                             const SeqTable& T, hipStream_t st) {
   // 9 subtiles per wave fit the registers only without the causal mask and outside the biased
   // slot-map variant (score_mfma_ksub_ok); the host asks for them only there
   if (!score_mfma_ksub_ok(ksub, layout, has_bias, rpos != nullptr)) return hipErrorInvalidValue;
-  const auto* qq = static_cast<const uint16_t*>(q);
-  const auto* kk = static_cast<const uint16_t*>(k);
+  const ScoreArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), table, max_blocks, lse, bias,
+                    rpos, scores, H, R, n_max, scale, pw, dead, ord};
   const dim3 grid(T.total);
-  if (layout == kPaged)
-    launch_l<kPaged>(has_bias, ksub, grid, st, qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale,
-                     pw, dead, T);
-  else if (layout == kSlots)
-    launch_l<kSlots>(has_bias, ksub, grid, st, qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max, scale,
-                     pw, dead, T);
-  else
-    launch_l<kContig>(has_bias, ksub, grid, st, qq, kk, table, max_blocks, lse, bias, rpos, scores, H, R, n_max,
-                      scale, pw, dead, T);
+  if (layout == kPaged) launch_l<kPaged>(has_bias, ksub, grid, st, a, T);
+  else if (layout == kSlots) launch_l<kSlots>(has_bias, ksub, grid, st, a, T);
+  else launch_l<kContig>(has_bias, ksub, grid, st, a, T);
   return hipGetLastError();
 }
 
