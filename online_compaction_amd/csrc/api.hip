@@ -206,7 +206,8 @@ bool use_mfma(const kvc_shape* sh, const kvc_kv_view* kv) {
 // loads before its first key). With many workgroups the longest chunk is best (fewer partials,
 // less overhead, and the last partial round costs little). With few, the chunk splits the longest
 // sequence into equal parts (a multiple of the 64-key stage, at least 512 keys), choosing the
-// split that minimises rounds x (chunk + overhead); ties go to the longer chunk.
+// split that minimises rounds x (chunk + overhead); ties go to the longer chunk. (The partials,
+// and so the workspace, depend on the chunk: sizes come from the same shape, row_pos included.)
 int64_t lse_workgroups(const kvc_shape* sh, int64_t rb, int kc) {
   int64_t wg = 0;
   for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
@@ -217,6 +218,9 @@ int mfma_kchunk(const kvc_shape* sh) {
   const int R = sh->group * sh->num_queries;
   const int64_t rb = lse_mfma_row_blocks(R);
   if (lse_workgroups(sh, rb, kLseMaxChunk) >= 8 * kLseSlots) return kLseMaxChunk;
+  // causal rows: workgroups whose rows see few of their keys end early, so the shortest chunk
+  // lets the others spread over the freed slots
+  if (sh->row_pos) return 512;
   int longest = 0;
   for (int s = 0; s < sh->num_seqs; ++s) longest = std::max(longest, sh->seq_lens[s]);
   int best = kLseMaxChunk;
@@ -361,7 +365,7 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
       });
   if (e != hipSuccess) return hip_fail(e, "lse partial kernel");
   e = for_each_chunk(
-      sh, nullptr, [&](int) { return H * ((R + 255) / 256); }, offset,
+      sh, nullptr, [&](int) { return H * ((R + 63) / 64); }, offset,
       [&](const SeqTable& T) { return launch_lse_combine(parts, lse_out, H, R, kc, T, st); });
   if (e != hipSuccess) return hip_fail(e, "lse combine kernel");
   return KVC_OK;

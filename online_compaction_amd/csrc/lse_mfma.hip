@@ -325,7 +325,8 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
 
 // ------------------------------------------------------------------------------------------------
 // Combine the per-chunk partials of every proxy row into its natural-log LSE.
-// Work item = (sequence, KV head, 256-row block); partial chunk count per unit = nchunk(n).
+// Work item = (sequence, KV head, 64-row block): four lanes per row each merge every fourth
+// chunk's (reference, sum) online, then the four merge by two exchanges.
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ partials, float* __restrict__ lse_out,
                                                    int H, int R, int kchunk, SeqTable T) {
@@ -334,20 +335,36 @@ __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ pa
   const int n = T.n[i];
   const int s = T.first + i;
   const int nkc = (n + kchunk - 1) / kchunk;
-  const int nrb = (R + 255) / 256;
+  const int nrb = (R + 63) / 64;
   const int local = t - T.start[i];
   const int h = local / nrb;
-  const int r = (local - h * nrb) * 256 + threadIdx.x;
-  if (r >= R) return;
-  const float2* p = partials + T.off[i] + (int64_t)h * nkc * R + r;
-  float mm = -INFINITY;
-  for (int c = 0; c < nkc; ++c) mm = fmaxf(mm, p[(int64_t)c * R].x);
-  float sum = 0.0f;
-  for (int c = 0; c < nkc; ++c) {
-    const float2 v = p[(int64_t)c * R];
-    if (v.y > 0.0f) sum += v.y * __builtin_amdgcn_exp2f(v.x - mm);  // a chunk without live keys adds nothing
+  const int r = (local - h * nrb) * 64 + (threadIdx.x >> 2);
+  const int part = threadIdx.x & 3;
+  // (mm, sum): sum of 2^(x - mm) over the merged chunks with live keys; mm = -inf before any
+  float mm = -INFINITY, sum = 0.0f;
+  if (r < R) {
+    const float2* p = partials + T.off[i] + (int64_t)h * nkc * R + r;
+    for (int c = part; c < nkc; c += 4) {
+      const float2 v = p[(int64_t)c * R];
+      if (!(v.y > 0.0f)) continue;  // a chunk without live keys adds nothing
+      if (v.x > mm) {
+        sum = sum * __builtin_amdgcn_exp2f(mm - v.x) + v.y;
+        mm = v.x;
+      } else {
+        sum += v.y * __builtin_amdgcn_exp2f(v.x - mm);
+      }
+    }
   }
-  lse_out[((int64_t)s * H + h) * R + r] = (mm + __builtin_log2f(sum)) * kLn2;
+#pragma unroll
+  for (int off = 1; off <= 2; off <<= 1) {
+    const float m2 = __shfl_xor(mm, off), s2 = __shfl_xor(sum, off);
+    const float mx = fmaxf(mm, m2);
+    if (mx > -INFINITY) sum = (sum > 0.0f ? sum * __builtin_amdgcn_exp2f(mm - mx) : 0.0f) +
+                              (s2 > 0.0f ? s2 * __builtin_amdgcn_exp2f(m2 - mx) : 0.0f);
+    mm = mx;
+  }
+  if (part == 0 && r < R)
+    lse_out[((int64_t)s * H + h) * R + r] = sum > 0.0f ? (mm + __builtin_log2f(sum)) * kLn2 : -INFINITY;
 }
 
 // ------------------------------------------------------------------------------------------------

@@ -246,15 +246,17 @@ def test_attention_matching_validation(lib):
 
 
 def test_causal_rows_validation(lib):
-    """A causal mask sizes no workspace differently, attention matching rejects it, and the
-    binding refuses a row_pos tensor that is not int32 or too short."""
+    """A causal mask can only grow the workspace (its LSE pass may use shorter key chunks),
+    attention matching rejects it, and the binding refuses a row_pos tensor that is not int32 or
+    too short."""
     torch = pytest.importorskip("torch")
     kv = A.KView(FAKE, A.KVC_BF16)
     sh = _shape()
     cz = _shape()
     cz.row_pos = FAKE
-    assert oc.kvc_score_workspace_size(cz, kv, False) == oc.kvc_score_workspace_size(sh, kv, False)
-    assert oc.kvc_lse_workspace_size(cz, kv) == oc.kvc_lse_workspace_size(sh, kv)
+    assert oc.kvc_score_workspace_size(cz, kv, False) >= oc.kvc_score_workspace_size(sh, kv, False) > 0
+    assert oc.kvc_lse_workspace_size(cz, kv) >= oc.kvc_lse_workspace_size(sh, kv) > 0
+    assert oc.kvc_score_workspace_size(cz, kv, True) == 0
     assert oc.kvc_am_workspace_size(cz, kv, kv, [6600, 4000], True) == 0
     s, keep = cz.c()
     k_, v_ = kv.c(), kv.c()

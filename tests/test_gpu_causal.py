@@ -163,11 +163,10 @@ def test_causal_through_slot_map_with_dead_slots():
 
 @pytest.mark.parametrize("case", ["mfma_one_head", "mfma_action_bias", "mfma_paged", "valu_f32"])
 def test_mask_that_hides_nothing(case):
-    """row_pos >= n - 1 everywhere takes the unmasked stages only. With one query head per KV
-    head (and on the VALU path) the rows keep their order and every output equals the run
-    without a mask bit for bit; with several, the MFMA kernels take causal rows query-major, so
-    the scores and masses are the same sums in another order (equal to float32 rounding) and the
-    LSE of each row is the same."""
+    """row_pos >= n - 1 everywhere takes the unmasked code only. On the VALU path every output
+    equals the run without a mask bit for bit. The MFMA path takes causal rows query-major and
+    splits the LSE pass into shorter key chunks, so there the same sums come in another order:
+    equal to float32 rounding."""
     P, oc = _P(), _oc()
     if case == "mfma_one_head":
         w = W.custom("causal_g1", 178, S=2, H=2, G=1, q=40, n=(2100, 700), dtype="bf16", keys="mixture",
@@ -177,7 +176,7 @@ def test_mask_that_hides_nothing(case):
     data = W.build_paged(w) if w.paged else W.build_contiguous(w)
     b = _batch(w, data)
     base = _run_all(oc, b, w)
-    exact = w.G == 1 or w.dtype == "f32"
+    exact = w.dtype == "f32"
     for extra in (0, 7):
         b.shape.row_pos = P.device_tensor(W.row_positions(w, "all") + extra)
         got = _run_all(oc, b, w)
@@ -185,7 +184,8 @@ def test_mask_that_hides_nothing(case):
             if exact:
                 assert np.array_equal(x, y), f"{case} +{extra}: {what} differ from the unmasked run"
             else:
-                np.testing.assert_allclose(y, x, rtol=2e-6, atol=1e-30, err_msg=f"{case} +{extra}: {what}")
+                np.testing.assert_allclose(y, x, rtol=1e-5, atol=1e-30 if what != "lse" else 1e-5,
+                                           err_msg=f"{case} +{extra}: {what}")
     say(f"[ok] causal nothing hidden {case}")
 
 
