@@ -29,6 +29,7 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+F32_VALU_PEAK_TFLOPS = 157.3  # published vector float32 peak: 256 CUs x 128 FMA lanes (packed) x 2 x 2.4 GHz
 MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
 # the score kernel's source: its own file and the headers it includes
@@ -500,6 +501,15 @@ def main():
         "flops_per_launch": flops,
         "launch_ms": avg[0],
     }
+    if w.dtype == "f32":  # float32 scoring runs on the vector ALU (score_valu / lse_partials_valu)
+        roof.update({"kernel": "score_valu + lse_partials_valu (score stage)", "bound": "alu",
+                     "achieved": achieved_tf, "peak": F32_VALU_PEAK_TFLOPS,
+                     "frac": achieved_tf / F32_VALU_PEAK_TFLOPS})
+    elif w.R < 16:  # bf16 with few proxy rows: the VALU kernels, bound by reading K (twice)
+        gbps = ab["score"] / score_s / 1e9
+        roof.update({"kernel": "score_valu + lse_partials_valu (score stage)", "bound": "hbm", "achieved": gbps,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
+                     "bytes_per_launch": ab["score"]})
     if w.name == "am":  # the fit dominates: its kernels against the peak of the units they use
         af = am_flops(w, *args.am_iters)
         fit_s = st["am_fit"] * 1e-3
