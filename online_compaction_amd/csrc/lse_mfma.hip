@@ -344,16 +344,25 @@ __global__ __launch_bounds__(256) void lse_combine(const float2* __restrict__ pa
   float mm = -INFINITY, sum = 0.0f;
   if (r < R) {
     const float2* p = partials + T.off[i] + (int64_t)h * nkc * R + r;
-    for (int c = part; c < nkc; c += 4) {
-      const float2 v = p[(int64_t)c * R];
-      if (!(v.y > 0.0f)) continue;  // a chunk without live keys adds nothing
+    auto merge = [&](float2 v) {
+      if (!(v.y > 0.0f)) return;  // a chunk without live keys adds nothing
       if (v.x > mm) {
         sum = sum * __builtin_amdgcn_exp2f(mm - v.x) + v.y;
         mm = v.x;
       } else {
         sum += v.y * __builtin_amdgcn_exp2f(v.x - mm);
       }
+    };
+    int c = part;
+    for (; c + 12 < nkc; c += 16) {  // four loads in flight per lane
+      const float2 v0 = p[(int64_t)c * R], v1 = p[(int64_t)(c + 4) * R];
+      const float2 v2 = p[(int64_t)(c + 8) * R], v3 = p[(int64_t)(c + 12) * R];
+      merge(v0);
+      merge(v1);
+      merge(v2);
+      merge(v3);
     }
+    for (; c < nkc; c += 4) merge(p[(int64_t)c * R]);
   }
 #pragma unroll
   for (int off = 1; off <= 2; off <<= 1) {
