@@ -304,3 +304,21 @@ def test_score_key_tile_variants(case):
     else:
         run_contig_case(w)
 
+
+
+@pytest.mark.parametrize("path", ["mfma_contig", "valu_contig", "mfma_paged"])
+def test_more_sequences_than_one_launch_describes(path):
+    """300 ragged sequences: every entry point splits them over several launches (one launch's
+    argument table describes at most 128 sequences), with per-sequence offsets into the
+    workspace, the outputs and the paged pool carried across the launches."""
+    rng = np.random.default_rng(77)
+    lens = tuple(int(x) for x in rng.integers(1, 400, size=300))
+    if path == "valu_contig":
+        w = W.custom("many_valu", 124, S=300, H=2, G=1, q=3, n=lens)
+    else:
+        w = W.custom(f"many_{path}", 125, S=300, H=2, G=4, q=4, n=lens, dtype="bf16", keys="mixture",
+                     queries="cluster", paged=path == "mfma_paged", table="permuted", block_size=16)
+    if w.paged:
+        run_paged_case(w)
+    else:
+        run_contig_case(w)
