@@ -18,8 +18,9 @@
 // exponentials, so w' starts at exp(ME - Mz) and beta = log w' - (ME - Mz). Once beta is fixed,
 // E is overwritten in place by P_C and P_C^T is written beside it (PT), so both value products
 // read their left operand row by row.
-// The QK^T products use v_mfma_f32_16x16x32_bf16 on the stored bf16 rows; the solver products
-// use v_mfma_f32_16x16x4_f32 (float32 throughout); the vector products are plain VALU. Every
+// The QK^T products use v_mfma_f32_16x16x32_bf16 on the stored bf16 rows; the solver's matrix
+// products run on the same instruction with their float32 operands stored split into bf16 high
+// and low parts (three products each); the vector products are plain VALU. Every
 // reduction has a fixed order (split sums land in partial buffers that one pass adds up in
 // order), so a fit is reproducible bit for bit.
 //
@@ -116,10 +117,6 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 }
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
 }  // namespace
@@ -541,8 +538,8 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 // stage's MFMAs, and split over S workgroups whose partial tiles a second pass adds in order:
 //   KIND 0: Z = P_C Vc - Y          (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
 //   KIND 1: Vc -= eta P_C^T Z        (columns of P_C, contraction over rows)    -> Vc, or partials Up
-// The float32 operands are split when they are staged: x = hi + lo with hi = bf16(x) and
-// lo = bf16(x - hi), and a product is taken as hi_a hi_b + hi_a lo_b + lo_a hi_b on
+// The float32 operands are stored split (x = hi + lo with hi = bf16(x) and lo = bf16(x - hi),
+// the layout of put_split8), and a product is taken as hi_a hi_b + hi_a lo_b + lo_a hi_b on
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation (the dropped lo_a lo_b and the rounding of
 // lo leave a relative error near 2^-16 per product, against 2^-24 for float32 inputs, at a
 // third of the float32 MFMA's cycles per product).
