@@ -15,4 +15,5 @@ from .gen import (  # noqa: F401
     c4_budget,
     score_rows,
     row_positions,
+    device_normal_bf16,
 )

@@ -423,3 +423,20 @@ def score_rows(seed: int, lens, kind: str, n_max: int | None = None) -> np.ndarr
             raise ValueError(kind)
         out[s, :n] = x
     return out
+
+
+def device_normal_bf16(shape, seed: int, device="cuda", chunk_rows: int = 1 << 20):
+    """Standard normal values rounded to bfloat16 (round to nearest even), generated on the device
+    by torch's seeded generator: for inputs of several GiB that the host could not generate in a
+    test's time. Deterministic for a given seed, shape and device; the last axis is kept whole and
+    the leading axes are filled `chunk_rows` rows at a time to bound the float32 staging."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    flat = out.view(-1, shape[-1])
+    for r0 in range(0, flat.shape[0], chunk_rows):
+        r1 = min(r0 + chunk_rows, flat.shape[0])
+        flat[r0:r1] = torch.randn((r1 - r0, shape[-1]), generator=g, device=device, dtype=torch.float32)
+    return out
