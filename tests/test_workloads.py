@@ -91,3 +91,20 @@ def test_paged_layout_and_permuted_table():
 def test_c5_lengths_fixed_by_seed():
     assert W.spec("c5").n == W.spec("c5").n
     assert len(W.spec("c5").n) == 64
+
+
+def test_device_normal_generator_is_seeded():
+    """The on-device generator (used for multi-GiB inputs) is a function of its seed: the same
+    seed gives the same bfloat16 values, another seed other values, and the values are standard
+    normal rounded to bfloat16 (checked here on the CPU device)."""
+    torch = pytest.importorskip("torch")
+    a = W.device_normal_bf16((3, 1000, 128), seed=7, device="cpu")
+    b = W.device_normal_bf16((3, 1000, 128), seed=7, device="cpu")
+    c = W.device_normal_bf16((3, 1000, 128), seed=8, device="cpu")
+    assert a.dtype == torch.bfloat16 and a.shape == (3, 1000, 128)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a.view(torch.int16), c.view(torch.int16))
+    x = a.float()
+    assert abs(float(x.mean())) < 0.02 and abs(float(x.std()) - 1.0) < 0.02
+    # every value is a bfloat16 (the low 16 bits of its float32 pattern are zero)
+    assert int((x.view(torch.int32) & 0xFFFF).abs().sum()) == 0

@@ -428,8 +428,8 @@ def score_rows(seed: int, lens, kind: str, n_max: int | None = None) -> np.ndarr
 def device_normal_bf16(shape, seed: int, device="cuda", chunk_rows: int = 1 << 20):
     """Standard normal values rounded to bfloat16 (round to nearest even), generated on the device
     by torch's seeded generator: for inputs of several GiB that the host could not generate in a
-    test's time. Deterministic for a given seed, shape and device; the last axis is kept whole and
-    the leading axes are filled `chunk_rows` rows at a time to bound the float32 staging."""
+    test's time. The leading axes are filled `chunk_rows` rows at a time to bound the float32
+    staging; the values are fixed by the seed, the shape, `chunk_rows` and the device type."""
     import torch
 
     g = torch.Generator(device=device)
