@@ -29,7 +29,10 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-F32_VALU_PEAK_TFLOPS = 157.3  # published vector float32 peak: 256 CUs x 128 FMA lanes (packed) x 2 x 2.4 GHz
+# vector float32 peak without packed-FP32 instructions (the library is built with them turned
+# off): 256 CUs x 4 SIMDs x 16 lanes x 2 flop (one FMA) x 2.4 GHz = 78.6 TFLOP/s; the published
+# 157.3 TFLOP/s counts the packed (two-wide) FMA
+F32_VALU_PEAK_TFLOPS = 78.6
 MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
 # the score kernel's source: its own file and the headers it includes
@@ -196,7 +199,26 @@ def _oracle_steps(w, am_iters) -> str:
     return f"score ({lse}) + top-m + gather"
 
 
-def cpu_baseline(w, budget_s: float, am_iters=(0, 0)) -> dict:
+SINGLE_CORE_WORKLOADS = ("c1", "c2a", "c2b", "c4")
+
+
+def single_core_baseline() -> dict:
+    """The oracle on ONE core (one BLAS thread, this process) for the small named workloads: one
+    unit of each timed and scaled by the workload's unit count (its units cost the same), c4 at
+    its largest budget."""
+    from threadpoolctl import threadpool_limits
+    out = {}
+    for name in SINGLE_CORE_WORKLOADS:
+        w = W.spec(name, 6) if name == "c4" else W.spec(name)
+        with threadpool_limits(1):
+            t = _oracle_unit((w, 0, 0, W.bias_row(w, 0), (0, 0)))
+        units = w.S * w.H
+        out[name] = {"tokens_per_s": trajectory_tokens(w) / (t * units), "step_s": t * units,
+                     "sample": f"1 of {units} units timed ({t:.3f} s), scaled by {units}"}
+    return out
+
+
+def cpu_baseline(w, budget_s: float, am_iters=(0, 0), single_core: bool = False) -> dict:
     from concurrent.futures import ProcessPoolExecutor
     import multiprocessing as mp
     try:
@@ -234,11 +256,14 @@ def cpu_baseline(w, budget_s: float, am_iters=(0, 0)) -> dict:
                     break
     except OSError:
         pass
-    return {"value": trajectory_tokens(w) / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": (f"{count} of {len(units)} (sequence or layer, KV head) units, float64 NumPy oracle "
-                       f"{_oracle_steps(w, am_iters)}, one unit per process with 1 BLAS thread; "
-                       f"wall {wall:.1f} s (busy {sum(busy):.1f} s) scaled by {len(units)}/{count}"),
-            "cpu_model": model}
+    out = {"value": trajectory_tokens(w) / step_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": (f"{count} of {len(units)} (sequence or layer, KV head) units, float64 NumPy oracle "
+                      f"{_oracle_steps(w, am_iters)}, one unit per process with 1 BLAS thread; "
+                      f"wall {wall:.1f} s (busy {sum(busy):.1f} s) scaled by {len(units)}/{count}"),
+           "cpu_model": model}
+    if single_core:  # the same oracle on one core, for the small named workloads
+        out["single_core"] = single_core_baseline()
+    return out
 
 
 # ---------------------------------------------------------------------------------- roofline
@@ -337,8 +362,11 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(w, args.cpu_seconds, args.am_iters)
+        cpu = cpu_baseline(w, args.cpu_seconds, args.am_iters, single_core=(w.name == "c3"))
         log(f"[cpu] oracle baseline {cpu['value']:.4g} tokens/s on {cpu['cores']} cores")
+        if "single_core" in cpu:
+            log("[cpu] one core: " + ", ".join(f"{k} {v['tokens_per_s']:.4g} tokens/s"
+                                              for k, v in cpu["single_core"].items()))
         # let the worker processes' exit (and the release of their memory) finish before the
         # GPU is timed: right after a many-core CPU leg some host calls were seen to stall
         gc.collect()

@@ -1,7 +1,7 @@
 """ActKV's retention policy on top of the library: action-critical entries feed an LRFU state,
-retention keeps the entries with the largest state, and a confidence-driven ratchet sets the
-budget ("ActKV" analysis page on zhichai.net: the paragraph on the eviction policy and the
-paragraph on the adaptive budget).
+retention keeps the entries with the largest state, and a one-way ratchet sets the budget
+("ActKV" analysis page on zhichai.net: the paragraph on the eviction policy and the paragraph
+on the adaptive budget).
 
 Host policy only (which budget, when to evict); every step on the data runs in libkvc:
 kvc_attention_mass (the attention the action tokens pay each entry), kvc_lrfu_update (the
@@ -13,12 +13,9 @@ Readings of the page used here:
   * "within the top 90 %" is the shortest run of entries, in descending attention, that holds
     90 % of the total attention (the library takes this decision on exact integer masses);
   * LRFU's value decays by 2^-lambda per policy step and a hit adds 1 (lambda = 0.5);
-  * budget_k = min(30000, floor(512 * 1.75^k)) after k expansions; it never shrinks;
-  * token confidence is the mean negative log-probability of the 20 most likely next tokens, as
-    the page names it. That value is larger when the model is sure (the other candidates get
-    tiny probabilities), so a collapse of confidence is a dip: sliding-window minimum pooling
-    (window 64, stride 8) keeps the dips, and a negative least-squares slope of the pooled series
-    over the tokens of one policy step expands the budget once.
+  * budget_k = min(30000, floor(512 * 1.75^k)) after k expansions; it never shrinks. When to
+    expand is the model's signal (the page derives it from next-token confidence); the caller
+    passes that decision in.
 """
 from __future__ import annotations
 
@@ -31,54 +28,25 @@ import torch
 from . import _abi as A
 
 
-def token_confidence(top_logprobs) -> np.ndarray:
-    """Per generated token, the mean negative log-probability of its top-20 candidates
-    ([T][20] natural-log probabilities in, [T] out)."""
-    lp = np.asarray(top_logprobs, dtype=np.float64)
-    return -lp.mean(axis=-1)
-
-
-def min_pool(series, window: int = 64, stride: int = 8) -> np.ndarray:
-    """Minimum over every full window of `window` consecutive values, windows `stride` apart."""
-    x = np.asarray(series, dtype=np.float64)
-    if x.shape[0] < window:
-        return np.zeros(0)
-    starts = range(0, x.shape[0] - window + 1, stride)
-    return np.array([x[a:a + window].min() for a in starts])
-
-
-def ls_slope(y) -> float:
-    """Least-squares slope of y against 0, 1, 2, ... (0 for fewer than two points)."""
-    y = np.asarray(y, dtype=np.float64)
-    if y.shape[0] < 2:
-        return 0.0
-    x = np.arange(y.shape[0], dtype=np.float64)
-    xc = x - x.mean()
-    return float((xc * (y - y.mean())).sum() / (xc * xc).sum())
-
-
 @dataclass
 class BudgetRatchet:
-    """One-way budget: starts at `initial`, multiplied by `factor` (capped) whenever a policy
-    step's pooled confidence trends down; it never shrinks."""
+    """One-way budget: starts at `initial` and is multiplied by `factor` (capped) on each
+    expansion; it never shrinks."""
     initial: int = 512
     factor: float = 1.75
     cap: int = 30000
-    window: int = 64
-    stride: int = 8
     expansions: int = 0
 
     @property
     def budget(self) -> int:
         return min(self.cap, math.floor(self.initial * self.factor ** self.expansions))
 
-    def observe(self, confidences) -> bool:
-        """Confidences of the tokens generated in one policy step; True when the budget grew."""
-        slope = ls_slope(min_pool(confidences, self.window, self.stride))
-        if slope < 0 and self.budget < self.cap:
-            self.expansions += 1
-            return True
-        return False
+    def expand(self) -> bool:
+        """One expansion; False (and no change) once the cap is reached."""
+        if self.budget >= self.cap:
+            return False
+        self.expansions += 1
+        return True
 
 
 @dataclass
@@ -111,17 +79,17 @@ class ActKVRetention:
         return A.Shape(1, self.num_kv_heads, self.group, q, d, self.state.shape[2], np.array([n], dtype=np.int32),
                        self.scale)
 
-    def step(self, new_tokens: int, action_queries: torch.Tensor, confidences=None) -> dict:
+    def step(self, new_tokens: int, action_queries: torch.Tensor, expand: bool = False) -> dict:
         """One policy step: update() then evict()."""
-        out = self.update(new_tokens, action_queries, confidences)
+        out = self.update(new_tokens, action_queries, expand)
         out.update(self.evict())
         return out
 
-    def update(self, new_tokens: int, action_queries: torch.Tensor, confidences=None) -> dict:
+    def update(self, new_tokens: int, action_queries: torch.Tensor, expand: bool = False) -> dict:
         """The engine has written `new_tokens` more K/V rows at [length, length + new_tokens)
         and produced `action_queries` ([H*G][q][d], K's dtype) in this step. Update the LRFU
-        state with their attention over the whole cache and let the ratchet see the step's
-        token confidences (None: no decision this step)."""
+        state with their attention over the whole cache; `expand` (the model's signal that
+        confidence collapsed during the step) grows the budget once."""
         self.length += new_tokens
         n = self.length
         q, d = action_queries.shape[1], action_queries.shape[2]
@@ -133,7 +101,7 @@ class ActKVRetention:
         A.kvc_attention_mass(shape, action_queries.unsqueeze(0).contiguous(), kv, None, None, mass, ws)
         counts = torch.zeros((1, self.num_kv_heads), dtype=torch.int32, device=dev)
         A.kvc_lrfu_update(shape, mass, self.top_p, 2.0 ** -self.lam, self.state, counts)
-        grew = self.ratchet.observe(confidences) if confidences is not None else False
+        grew = self.ratchet.expand() if expand else False
         return {"n": n, "budget": self.ratchet.budget, "grew": grew, "mass": mass, "critical": counts}
 
     def evict(self) -> dict:

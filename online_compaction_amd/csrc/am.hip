@@ -836,13 +836,13 @@ __global__ __launch_bounds__(256) void am_finish(float* __restrict__ w_all, cons
 #define KVC_COMMA ,
 
 // Work items per head of each kernel.
-int am_exp_items(int R, int cols) { return ((R + 63) / 64) * ((cols + 63) / 64); }
-int am_scale_items(int R, int m) { return (int)(((int64_t)R * pad64(m) + 4095) / 4096); }
+int64_t am_exp_items(int R, int cols) { return (int64_t)((R + 63) / 64) * ((cols + 63) / 64); }
+int64_t am_scale_items(int R, int m) { return ((int64_t)R * pad64(m) + 4095) / 4096; }
 int am_row_tiles(int R) { return (R + 63) / 64; }
 int am_dot_row_items(int R) { return (R + 3) / 4; }
 int am_col_items(int m) { return (m + 255) / 256; }
-int am_col_part_items(int R, int m) { return (int)((pad64(m) + 255) / 256) * ((R + kRowChunk - 1) / kRowChunk); }
-int am_key_tiles(int m) { return (int)(pad64(m) / 64); }
+int64_t am_col_part_items(int R, int m) { return (int64_t)((pad64(m) + 255) / 256) * ((R + kRowChunk - 1) / kRowChunk); }
+int64_t am_key_tiles(int m) { return pad64(m) / 64; }
 int am_stages_rows(int m) { return (int)(pad64(m) / 32); }
 int am_stages_cols(int R) { return (R + 31) / 32; }
 

@@ -44,13 +44,13 @@ struct AmCfg {
   int H, R, m_max, S1, S2;
 };
 int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2);
-int am_exp_items(int R, int cols);
-int am_scale_items(int R, int m);
+int64_t am_exp_items(int R, int cols);
+int64_t am_scale_items(int R, int m);
 int am_row_tiles(int R);
 int am_dot_row_items(int R);
 int am_col_items(int m);
-int am_col_part_items(int R, int m);
-int am_key_tiles(int m);
+int64_t am_col_part_items(int R, int m);
+int64_t am_key_tiles(int m);
 int am_gemm_tiles(int rows);
 int am_stages_rows(int m);
 int am_stages_cols(int R);
@@ -262,6 +262,8 @@ size_t lse_bytes(const kvc_shape* sh) {
 
 // Run `body(T)` for consecutive slices of at most kChunkSeqs sequences; `items(s)` is the number
 // of work items (workgroups) of sequence s and `offset(s)` a kernel-specific per-sequence value.
+// Every entry point checks its launches' item counts with check_items before the first launch, so
+// the count test here never fires on a validated call.
 template <class Items, class Offset, class Body>
 hipError_t for_each_chunk(const kvc_shape* sh, const int32_t* m, Items&& items, Offset&& offset, Body&& body,
                           const int32_t* cache_lens = nullptr) {
@@ -278,9 +280,9 @@ hipError_t for_each_chunk(const kvc_shape* sh, const int32_t* m, Items&& items, 
       T.kofs[i] = seq_start(sh, s);
       T.clen[i] = cache_lens ? cache_lens[s] : T.kofs[i] + T.n[i];
       T.off[i] = offset(s);
-      total += items(s);
+      total += (int64_t)items(s);
+      if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     }
-    if (total > INT32_MAX) return hipErrorInvalidConfiguration;
     T.start[T.count] = (int32_t)total;
     T.total = (int32_t)total;
     if (total > 0) {
@@ -289,6 +291,25 @@ hipError_t for_each_chunk(const kvc_shape* sh, const int32_t* m, Items&& items, 
     }
   }
   return hipSuccess;
+}
+
+// Validation of one launch family: the work items of every slice of kChunkSeqs sequences, summed
+// in 64 bits, must fit the int32 grid and work-item indices.
+template <class Items>
+kvc_status check_items(const kvc_shape* sh, Items&& items, const char* what) {
+  for (int s0 = 0; s0 < sh->num_seqs; s0 += kChunkSeqs) {
+    int64_t total = 0;
+    for (int s = s0; s < std::min(sh->num_seqs, s0 + kChunkSeqs); ++s) {
+      const int64_t it = (int64_t)items(s);
+      if (it < 0 || it > INT32_MAX) return fail(KVC_ERR_UNSUPPORTED, "%s: sequence %d needs %lld work items", what, s,
+                                                (long long)it);
+      total += it;
+    }
+    if (total > INT32_MAX)
+      return fail(KVC_ERR_UNSUPPORTED, "%s: %lld work items in one launch of sequences %d.. exceed 2^31 - 1", what,
+                  (long long)total, s0);
+  }
+  return KVC_OK;
 }
 
 auto no_offset = [](int) -> int64_t { return 0; };
@@ -334,7 +355,27 @@ RowOrder row_order(const kvc_shape* sh) {
   return RowOrder{G, sh->num_queries, magic};
 }
 
-// Internal LSE: per-chunk partials into ws_partials, then combined into lse_out.
+// Work items of the LSE pass per sequence: the partial kernel's (key chunk x row block) workgroups
+// and the combine kernel's 64-row items.
+int64_t lse_partial_items(const kvc_shape* sh, const kvc_kv_view* kv, int s) {
+  const int R = sh->group * sh->num_queries;
+  const int kc = lse_kchunk(sh, kv);
+  const int64_t rb = use_mfma(sh, kv) ? lse_mfma_row_blocks(R) : 1;
+  return (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
+}
+
+int64_t lse_combine_items(const kvc_shape* sh) {
+  return (int64_t)sh->num_kv_heads * ((sh->group * sh->num_queries + 63) / 64);
+}
+
+kvc_status check_lse_work(const kvc_shape* sh, const kvc_kv_view* kv) {
+  if (kvc_status st = check_items(sh, [&](int s) { return lse_partial_items(sh, kv, s); }, "lse partial kernel"))
+    return st;
+  return check_items(sh, [&](int) { return lse_combine_items(sh); }, "lse combine kernel");
+}
+
+// Internal LSE: per-chunk partials into ws_partials, then combined into lse_out (the work was
+// checked by check_lse_work).
 kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, const float* bias, float* lse_out,
                    void* ws_partials, hipStream_t st) {
   const int H = sh->num_kv_heads;
@@ -351,10 +392,9 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
     acc += partial_slots(sh, s, kc);
   }
   auto* parts = static_cast<float2*>(ws_partials);
-  const int rb = mf ? lse_mfma_row_blocks(R) : 1;
   auto offset = [&](int s) -> int64_t { return off[s]; };
   hipError_t e = for_each_chunk(
-      sh, nullptr, [&](int s) { return H * rb * ((sh->seq_lens[s] + kc - 1) / kc); }, offset,
+      sh, nullptr, [&](int s) { return lse_partial_items(sh, kv, s); }, offset,
       [&](const SeqTable& T) {
         if (mf)
           return launch_lse_partials_mfma(layout, has_bias, q, kv->data, index, kv->max_blocks, bias, sh->row_pos,
@@ -365,7 +405,7 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
       });
   if (e != hipSuccess) return hip_fail(e, "lse partial kernel");
   e = for_each_chunk(
-      sh, nullptr, [&](int) { return H * ((R + 63) / 64); }, offset,
+      sh, nullptr, [&](int) { return lse_combine_items(sh); }, offset,
       [&](const SeqTable& T) { return launch_lse_combine(parts, lse_out, H, R, kc, T, st); });
   if (e != hipSuccess) return hip_fail(e, "lse combine kernel");
   return KVC_OK;
@@ -404,6 +444,7 @@ kvc_status kvc_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* k, con
   const size_t need = partials_bytes(sh, lse_kchunk(sh, k));
   if (!ws || ws_bytes < need)
     return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "lse needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
+  if (kvc_status st = check_lse_work(sh, k)) return st;
   if (kvc_status st = run_lse(sh, q, k, bias, lse_out, ws, static_cast<hipStream_t>(stream))) return st;
   return ok();
 }
@@ -425,25 +466,28 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
   if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int R = sh->group * sh->num_queries;
+  const bool mf = use_mfma(sh, k);
+  const int layout = layout_of(k);
+  const int32_t* index = index_of(k);
+  const int H = sh->num_kv_heads;
+  const int ksub = mf ? score_ksub(sh, layout, bias != nullptr) : 0;
+  auto items = [&](int s) -> int64_t {
+    return (int64_t)H * (mf ? score_mfma_tiles(sh->seq_lens[s], ksub) : score_valu_tiles(sh->seq_lens[s]));
+  };
+  if (kvc_status s2 = check_items(sh, items, "score kernel")) return s2;
   const float* lse_rows = lse;
   if (!lse) {
     const size_t pb = partials_bytes(sh, lse_kchunk(sh, k));
     const size_t need = pb + lse_bytes(sh);
     if (!ws || ws_bytes < need)
       return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "%s needs %zu workspace bytes, got %zu", what, need, ws ? ws_bytes : 0);
+    if (kvc_status s2 = check_lse_work(sh, k)) return s2;
     float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pb);
     if (kvc_status s2 = run_lse(sh, q, k, bias, lse_ws, ws, st)) return s2;
     lse_rows = lse_ws;
   }
-  const bool mf = use_mfma(sh, k);
-  const int layout = layout_of(k);
-  const int32_t* index = index_of(k);
-  const int H = sh->num_kv_heads;
-  const int ksub = mf ? score_ksub(sh, layout, bias != nullptr) : 0;
   const hipError_t e = for_each_chunk(
-      sh, nullptr,
-      [&](int s) { return H * (mf ? score_mfma_tiles(sh->seq_lens[s], ksub) : score_valu_tiles(sh->seq_lens[s])); },
-      no_offset, [&](const SeqTable& T) {
+      sh, nullptr, items, no_offset, [&](const SeqTable& T) {
         if (mf)
           return launch_score_mfma(layout, bias != nullptr, ksub, q, k->data, index, k->max_blocks, lse_rows, bias,
                                    sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, row_order(sh), T,
@@ -484,8 +528,10 @@ kvc_status kvc_select_topm(const kvc_shape* sh, const float* scores, const int32
   if (kvc_status st = check_shape(sh)) return st;
   if (kvc_status st = check_budgets(sh, m, m_max)) return st;
   if (!scores || !kept) return fail(KVC_ERR_INVALID_ARGUMENT, "scores and kept must be non-NULL");
+  auto items = [&](int) -> int64_t { return sh->num_kv_heads; };
+  if (kvc_status st = check_items(sh, items, "select kernel")) return st;
   const hipError_t err = for_each_chunk(
-      sh, m, [&](int) { return sh->num_kv_heads; }, no_offset, [&](const SeqTable& T) {
+      sh, m, items, no_offset, [&](const SeqTable& T) {
         return launch_select(scores, kept, sh->num_kv_heads, sh->n_max, m_max, T, static_cast<hipStream_t>(stream));
       });
   if (err != hipSuccess) return hip_fail(err, "select kernel");
@@ -498,8 +544,10 @@ kvc_status kvc_lrfu_update(const kvc_shape* sh, const float* mass, double top_p,
   if (!mass || !state) return fail(KVC_ERR_INVALID_ARGUMENT, "mass and state must be non-NULL");
   if (!(top_p > 0.0 && top_p <= 1.0)) return fail(KVC_ERR_INVALID_ARGUMENT, "top_p = %g outside (0, 1]", top_p);
   if (!(decay >= 0.0f && decay <= 1.0f)) return fail(KVC_ERR_INVALID_ARGUMENT, "decay = %g outside [0, 1]", decay);
+  auto items = [&](int) -> int64_t { return sh->num_kv_heads; };
+  if (kvc_status st = check_items(sh, items, "lrfu kernel")) return st;
   const hipError_t err = for_each_chunk(
-      sh, nullptr, [&](int) { return sh->num_kv_heads; }, no_offset, [&](const SeqTable& T) {
+      sh, nullptr, items, no_offset, [&](const SeqTable& T) {
         return launch_lrfu_update(mass, state, counts, sh->num_kv_heads, sh->n_max, top_p, decay, T,
                                   static_cast<hipStream_t>(stream));
       });
@@ -516,8 +564,10 @@ kvc_status kvc_compact_side(const kvc_shape* sh, int32_t block_size, const int32
   if (!kept || !src || !dst) return fail(KVC_ERR_INVALID_ARGUMENT, "kept, src and dst must be non-NULL");
   if (static_cast<const void*>(src) == static_cast<const void*>(dst))
     return fail(KVC_ERR_INVALID_ARGUMENT, "src and dst must be distinct buffers");
+  auto items = [&](int s) -> int64_t { return (int64_t)sh->num_kv_heads * side_tiles(m[s]); };
+  if (kvc_status st = check_items(sh, items, "side-array compaction kernel")) return st;
   const hipError_t err = for_each_chunk(
-      sh, m, [&](int s) { return sh->num_kv_heads * side_tiles(m[s]); }, no_offset, [&](const SeqTable& T) {
+      sh, m, items, no_offset, [&](const SeqTable& T) {
         return launch_compact_side(src, dst, kept, sh->num_kv_heads, sh->n_max, m_max, block_size, T,
                                    static_cast<hipStream_t>(stream));
       });
@@ -532,8 +582,10 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
   if (kvc_status st = check_contig_extent(sh, "slot map")) return st;
   if (!kept || !slot_map) return fail(KVC_ERR_INVALID_ARGUMENT, "kept and slot_map must be non-NULL");
   if (dead_slot < 0) return fail(KVC_ERR_INVALID_ARGUMENT, "dead_slot = %d < 0", dead_slot);
+  auto items = [&](int s) -> int64_t { return (int64_t)sh->num_kv_heads * redirect_tiles(sh->seq_lens[s]); };
+  if (kvc_status st = check_items(sh, items, "redirect kernel")) return st;
   const hipError_t err = for_each_chunk(
-      sh, m, [&](int s) { return sh->num_kv_heads * redirect_tiles(sh->seq_lens[s]); }, no_offset,
+      sh, m, items, no_offset,
       [&](const SeqTable& T) {
         return launch_evict_redirect(slot_map, kept, sh->num_kv_heads, sh->n_max, m_max, dead_slot, T,
                                      static_cast<hipStream_t>(stream));
@@ -629,6 +681,38 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
     return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "attention matching needs %zu workspace bytes, got %zu", need,
                 ws ? ws_bytes : 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
+  AmCfg C{H, R, m_max, 1, 1};
+  am_splits(sh, m, &C.S1, &C.S2);
+  // work items per sequence of every launch family; a sequence with m = 0 has nothing to fit and
+  // gets no work items
+  auto per = [&](auto&& f) { return [&, f](int s) -> int64_t { return m[s] ? (int64_t)H * f(s) : 0; }; };
+  auto units = per([](int) -> int64_t { return 1; });
+  auto exps = per([&](int s) { return am_exp_items(R, m[s]); });
+  auto scales = per([&](int s) { return am_scale_items(R, m[s]); });
+  auto cols = per([&](int s) -> int64_t { return am_col_items(m[s]); });
+  auto cparts = per([&](int s) { return am_col_part_items(R, m[s]); });
+  auto rows = per([&](int) -> int64_t { return am_dot_row_items(R); });
+  auto rtiles = per([&](int) -> int64_t { return am_row_tiles(R); });
+  auto ktiles = per([&](int s) { return am_key_tiles(m[s]); });
+  auto gemm0 = per([&](int) -> int64_t { return (int64_t)am_gemm_tiles(R) * C.S1; });
+  auto gemm1 = per([&](int s) -> int64_t { return (int64_t)am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; });
+  {
+    const char* what = "attention matching kernel";
+    kvc_status e = KVC_OK;
+    if (!e) e = check_items(sh, units, what);
+    if (!e) e = check_items(sh, exps, what);
+    if (!e) e = check_items(sh, scales, what);
+    if (!e) e = check_items(sh, cols, what);
+    if (!e) e = check_items(sh, cparts, what);
+    if (!e) e = check_items(sh, rows, what);
+    if (!e) e = check_items(sh, rtiles, what);
+    if (!e) e = check_items(sh, ktiles, what);
+    if (!e) e = check_items(sh, gemm0, what);
+    if (!e) e = check_items(sh, gemm1, what);
+    if (!e && !lse) e = check_lse_work(sh, k);
+    if (e) return e;
+  }
   const float* lse_rows = lse;
   if (!lse) {
     float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + partials_bytes(sh, lse_kchunk(sh, k)));
@@ -636,9 +720,6 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
     lse_rows = lse_ws;
   }
   float* amws = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_part);
-  const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
-  AmCfg C{H, R, m_max, 1, 1};
-  am_splits(sh, m, &C.S1, &C.S2);
   std::vector<int64_t> off(sh->num_seqs);
   int64_t acc = 0;
   for (int s = 0; s < sh->num_seqs; ++s) {
@@ -649,23 +730,15 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   const int layout = layout_of(k);
   const int64_t nm = sh->n_max;
   auto run = [&](auto&& items, auto&& body) -> hipError_t { return for_each_chunk(sh, m, items, offset, body); };
-  // a sequence with m = 0 has nothing to fit: every per-sequence kernel gets no work items for it
-  auto per = [&](auto&& f) { return [&, f](int s) -> int { return m[s] ? f(s) : 0; }; };
 #define KVC_AM_STEP(ITEMS, CALL)                                              \
   do {                                                                        \
-    const hipError_t e_ = run(per(ITEMS), [&](const SeqTable& T) { return CALL; }); \
+    const hipError_t e_ = run(ITEMS, [&](const SeqTable& T) { return CALL; }); \
     if (e_ != hipSuccess) return hip_fail(e_, "attention matching kernel");      \
   } while (0)
-  auto units = [&](int) { return H; };
-  auto cols = [&](int s) { return H * am_col_items(m[s]); };
-  auto cparts = [&](int s) { return H * am_col_part_items(R, m[s]); };
-  auto rows = [&](int) { return H * am_dot_row_items(R); };
-  auto rtiles = [&](int) { return H * am_row_tiles(R); };
-  auto ktiles = [&](int s) { return H * am_key_tiles(m[s]); };
   KVC_AM_STEP(units, launch_am_stats(lse_rows, amws, C, T, st));
-  KVC_AM_STEP([&](int s) { return H * am_exp_items(R, m[s]); },
+  KVC_AM_STEP(exps,
               launch_am_exp(layout, q, k->data, k->block_table, k->max_blocks, kept, amws, nm, sh->scale, C, T, st));
-  KVC_AM_STEP([&](int s) { return H * am_scale_items(R, m[s]); }, launch_am_scale(amws, C, T, st));
+  KVC_AM_STEP(scales, launch_am_scale(amws, C, T, st));
   KVC_AM_STEP(cparts, launch_am_cols_part(0, beta, lse_rows, amws, C, T, st));
   KVC_AM_STEP(cols, launch_am_cols_fin(0, beta, amws, C, T, st));
   KVC_AM_STEP(cols, launch_am_init(layout, v->data, v->block_table, v->max_blocks, kept, beta, v_c, amws, nm, C, T,
@@ -682,10 +755,9 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   KVC_AM_STEP(rtiles, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
                                        v->max_blocks, lse_rows, amws, nm, sh->scale, C, T, st));
   for (int it = 0; it < iters_v; ++it) {
-    KVC_AM_STEP([&](int) { return H * am_gemm_tiles(R) * C.S1; }, launch_am_gemm(0, v_c, amws, C, T, st));
+    KVC_AM_STEP(gemm0, launch_am_gemm(0, v_c, amws, C, T, st));
     if (C.S1 > 1) KVC_AM_STEP(rtiles, launch_am_split_sum(0, v_c, amws, C, T, st));
-    KVC_AM_STEP([&](int s) { return H * am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; },
-                launch_am_gemm(1, v_c, amws, C, T, st));
+    KVC_AM_STEP(gemm1, launch_am_gemm(1, v_c, amws, C, T, st));
     if (C.S2 > 1) KVC_AM_STEP(ktiles, launch_am_split_sum(1, v_c, amws, C, T, st));
   }
   KVC_AM_STEP(cols, launch_am_finish(beta, amws, C, T, st));
@@ -701,8 +773,10 @@ kvc_status kvc_compact_contig(const kvc_shape* sh, kvc_dtype dtype, const void* 
   if (kvc_status st = check_contig_extent(sh, "compact_contig")) return st;
   if (!k || !v || !kept || !k_out || !v_out)
     return fail(KVC_ERR_INVALID_ARGUMENT, "k, v, kept, k_out and v_out must be non-NULL");
+  auto items = [&](int s) -> int64_t { return (int64_t)sh->num_kv_heads * contig_tiles(m[s], dtype == KVC_F32); };
+  if (kvc_status st = check_items(sh, items, "contiguous compaction kernel")) return st;
   const hipError_t err = for_each_chunk(
-      sh, m, [&](int s) { return sh->num_kv_heads * contig_tiles(m[s], dtype == KVC_F32); }, no_offset, [&](const SeqTable& T) {
+      sh, m, items, no_offset, [&](const SeqTable& T) {
         return launch_compact_contig(dtype == KVC_F32, k, v, kept, k_out, v_out, sh->num_kv_heads, sh->n_max, m_max,
                                      T, static_cast<hipStream_t>(stream));
       });
@@ -734,8 +808,10 @@ kvc_status kvc_compact_paged(const kvc_shape* sh, kvc_dtype dtype, void* k_pool,
     return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool, v_pool, kept, freed_blocks and freed_counts must be non-NULL");
   if (k_pool == v_pool) return fail(KVC_ERR_INVALID_ARGUMENT, "k_pool and v_pool must be distinct");
   hipStream_t st = static_cast<hipStream_t>(stream);
+  auto items = [&](int s) -> int64_t { return (int64_t)sh->num_kv_heads * paged_tiles(m[s]); };
+  if (kvc_status s2 = check_items(sh, items, "paged copy kernel")) return s2;
   hipError_t err = for_each_chunk(
-      sh, m, [&](int s) { return sh->num_kv_heads * paged_tiles(m[s]); }, no_offset, [&](const SeqTable& T) {
+      sh, m, items, no_offset, [&](const SeqTable& T) {
         return launch_paged_copy(dtype == KVC_F32, k_pool, v_pool, block_table, max_blocks, kept, sh->num_kv_heads,
                                  m_max, block_size, T, st);
       });

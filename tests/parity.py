@@ -24,6 +24,79 @@ def say(*a):
     sys.stdout.flush()
 
 
+# ----------------------------------------------------------------------------- oracle process pool
+
+_JOB: dict = {}
+
+
+def _one_blas_thread():
+    try:
+        from threadpoolctl import threadpool_limits
+        threadpool_limits(1)
+    except ImportError:  # pragma: no cover
+        pass
+
+
+def _job_call(i):
+    return _JOB["fn"](*_JOB["items"][i])
+
+
+def shared_array(shape, dtype) -> np.ndarray:
+    """Zeroed array in an anonymous shared mapping: forked workers write into it in place."""
+    import mmap
+    count = int(np.prod(shape))
+    mm = mmap.mmap(-1, max(count * np.dtype(dtype).itemsize, 1))
+    return np.frombuffer(mm, dtype=dtype, count=count).reshape(shape)
+
+
+def pool_map(fn, items, workers: int | None = None) -> list:
+    """fn(*item) for every item, in forked worker processes with one BLAS thread each; results in
+    item order. fn may be a closure: it and the arrays it reads reach the workers through fork,
+    so only the item index and the (small) results are pickled. Outputs that are large go to
+    arrays from `shared_array`. An assertion in a worker is raised here."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    items = list(items)
+    workers = min(workers or W.gen.default_workers(), max(1, len(items)))
+    if workers <= 1:
+        return [fn(*it) for it in items]
+    _JOB.update(fn=fn, items=items)
+    try:
+        with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("fork"),
+                                 initializer=_one_blas_thread) as ex:
+            return list(ex.map(_job_call, range(len(items)), chunksize=1))
+    finally:
+        _JOB.clear()
+
+
+def check_unit_outputs(scores, kept, ref, m, what, gathers=()) -> tuple:
+    """Every check of one unit: scores against the oracle's, the kept list's form, selection
+    exact on the GPU's own scores and within the tie band of the oracle's, and bit-exact gathers
+    (pairs of (stored rows [n][d], compacted rows [m_max][d])). Returns (worst rel err, swaps)."""
+    n = ref.shape[0]
+    worst = check_scores(scores[:n], ref, what)
+    check_kept_form(kept, m, n, what)
+    check_selection_exact(kept, scores[:n], m, what)
+    swaps = check_selection_band(kept, ref, m, what)
+    for X, out in gathers:
+        check_gather(X, kept, out, m, what)
+    return worst, swaps
+
+
+def summarize_units(results: dict, name: str, group: str = "s") -> float:
+    """Log the worst score error (and tie-band swaps) of every unit, one line per sequence or
+    layer, and return the overall worst."""
+    by_s: dict = {}
+    for (s, h), (worst, swaps) in sorted(results.items()):
+        by_s.setdefault(s, []).append((h, worst, swaps))
+    for s, row in by_s.items():
+        say(f"  {name} {group}={s}: " + " ".join(f"h{h} {wv:.2e}/{sw}" for h, wv, sw in row))
+    overall = max(wv for wv, _ in results.values())
+    say(f"[ok] {name}: {len(results)} units against the oracle; worst score rel err {overall:.3g}; "
+        f"tie-band swaps {sum(sw for _, sw in results.values())}")
+    return overall
+
+
 def check_scores(got: np.ndarray, ref: np.ndarray, what: str = "") -> float:
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)

@@ -271,3 +271,30 @@ def test_causal_rows_validation(lib):
     bad.row_pos = torch.zeros((2, 32, 1000), dtype=torch.int32)
     with pytest.raises(ValueError):
         bad.c()
+
+
+def test_oversized_launches_rejected_before_any_launch(lib):
+    """Work-item counts are summed in 64 bits per launch slice (128 sequences) during validation:
+    a request whose later slice would exceed 2^31 - 1 work items fails as unsupported before the
+    first slice is launched, and a paged compaction then leaves its host outputs untouched."""
+    S, n = 130, 1 << 16
+    lens = np.full(S, n, dtype=np.int32)
+    sh, keep = A.Shape(S, 1 << 20, 1, 1, 128, n, lens, 0.088).c()
+    m = (ctypes.c_int32 * S)(*([0] * 128 + [n, n]))  # nothing to do in the first slice
+    counts = (ctypes.c_int32 * S)(*([-7] * S))
+    st = lib.kvc_compact_paged(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE + 64, 16, FAKE, n // 16, FAKE, m, n, None,
+                               FAKE, counts, None)
+    assert st == A.KVC_ERR_UNSUPPORTED, lib.kvc_last_error()
+    assert b"work items" in lib.kvc_last_error()
+    assert list(counts) == [-7] * S
+    st = lib.kvc_compact_contig(ctypes.byref(sh), A.KVC_BF16, FAKE, FAKE, FAKE, m, n, FAKE, FAKE, None)
+    assert st == A.KVC_ERR_UNSUPPORTED
+    # one work item per (sequence, head): 128 sequences x 2^25 heads
+    sh2, keep2 = A.Shape(128, 1 << 25, 1, 1, 128, 64, np.full(128, 64, dtype=np.int32), 0.088).c()
+    m2 = (ctypes.c_int32 * 128)(*([1] * 128))
+    assert lib.kvc_select_topm(ctypes.byref(sh2), FAKE, m2, 1, FAKE, None) == A.KVC_ERR_UNSUPPORTED
+    # the score kernel's key tiles are checked before the LSE pass would launch
+    kv = A.KView(FAKE, A.KVC_BF16).c()
+    sh3, keep3 = A.Shape(2, 1 << 24, 1, 16, 128, 1 << 16, np.full(2, 1 << 16, dtype=np.int32), 0.088).c()
+    st = lib.kvc_score(ctypes.byref(sh3), FAKE, ctypes.byref(kv), None, None, FAKE, FAKE, 1 << 62, None)
+    assert st == A.KVC_ERR_UNSUPPORTED, lib.kvc_last_error()

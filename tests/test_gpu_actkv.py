@@ -205,8 +205,7 @@ def test_actkv_policy_session_mirror():
                 p = int(rng.integers(max(0, L - 150), L))
                 qf[hq, r] += W.bf16_bits_to_f32(k_pool[table[0, p // B], p % B, hq // G])
         qb = W.f32_to_bf16_bits(qf)
-        conf = np.linspace(4.0, 2.0, 160) if t in (2, 5) else np.linspace(2.0, 4.0, 160)
-        out = pol.update(n_new, P.device_tensor(qb), conf)
+        out = pol.update(n_new, P.device_tensor(qb), expand=t in (2, 5))
         torch.cuda.synchronize()
         mass = P.host_array(out["mass"])[0]
         crit = P.host_array(out["critical"])[0]

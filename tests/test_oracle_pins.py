@@ -309,6 +309,37 @@ def test_paged_rejects_bad_kept():
         O.paged_plan(10, 3, 4, [1, 2, 10])
 
 
+@pytest.mark.parametrize("n,B,H", [(37, 16, 3), (48, 16, 2), (1, 16, 1), (13, 4, 4), (16, 1, 2)])
+def test_paged_unit_keys_reads_through_the_table(n, B, H):
+    """The paged reader returns, for every head, exactly the keys that were written slot by slot
+    at pool[table[p // B], p % B, h] for p < n -- through a permuted table with unused physical
+    blocks, spare table entries past ceil(n/B) and a ragged last block whose padding slots hold
+    other values -- and reads nothing else."""
+    d = 5
+    N = -(-n // B)
+    rng = np.random.default_rng(n * 100 + B * 10 + H)
+    nblocks = N + 4
+    table = np.full(N + 3, -1, dtype=np.int32)
+    table[:N] = rng.permutation(nblocks)[:N]
+    table[N] = int(np.setdiff1d(np.arange(nblocks), table[:N])[0])  # a spare entry past ceil(n/B)
+    pool = rng.integers(1000, 2000, (nblocks, B, H, d)).astype(np.int64)  # not a key anywhere
+    want = rng.integers(-999, 0, (H, n, d)).astype(np.int64)              # distinct range from the filler
+    for h in range(H):
+        for p in range(n):
+            pool[table[p // B], p % B, h, :] = want[h, p]
+    for h in range(H):
+        got = O.paged_unit_keys(pool, table, n, h, B)
+        assert got.shape == (n, d)
+        np.testing.assert_array_equal(got, want[h])
+    # a block id outside [0, ceil(n/B)) of the table never matters: scramble the spare and the pads
+    pool2 = pool.copy()
+    pool2[table[N]] = -5
+    for p in range(n, N * B):
+        pool2[table[p // B], p % B] = -6
+    for h in range(H):
+        np.testing.assert_array_equal(O.paged_unit_keys(pool2, table, n, h, B), want[h])
+
+
 # ------------------------------------------------------------------- segments (delayed turns)
 
 @pytest.mark.parametrize("ex", _load("segment_examples.json")["examples"], ids=lambda e: e["name"])
