@@ -140,6 +140,24 @@ kvc_status kvc_score(const kvc_shape* shape, const void* q, const kvc_kv_view* k
                      const float* bias, float* scores, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * kvc_score_noalloc -- kvc_score without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, results (bit for bit) and errors as kvc_score, minus ws / ws_bytes.
+ * When it computes the LSE (lse == NULL) its scratch -- what kvc_score_workspace_size(shape, k, 0)
+ * counts -- lives in a static device array of KVC_NOALLOC_SCRATCH_BYTES bytes that the library
+ * holds on every GPU it runs on until the process ends; a larger shape is rejected with
+ * KVC_ERR_UNSUPPORTED before anything is enqueued (supply the LSE, or call kvc_score with a
+ * workspace). The call allocates, frees and clears no memory; nothing in the scratch needs to start
+ * at zero (every byte read is first written by the same call). Every call on one GPU shares that
+ * GPU's array: calls whose device work overlaps on one GPU (other streams, other threads) race,
+ * so callers serialise them, e.g. on one stream. The first call on a device looks the array's
+ * address up (hipGetSymbolAddress) and keeps it for the process; the device is the stream's.
+ * ------------------------------------------------------------------------------------------- */
+#define KVC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kvc_status kvc_score_noalloc(const kvc_shape* shape, const void* q, const kvc_kv_view* k, const float* lse,
+                             const float* bias, float* scores, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * kvc_attention_mass -- mean attention weight of every key over the proxy rows,
  * mass_j = (1/R) sum_r exp(l_rj - LSE_r). This is the per-entry tally of the attention that the
  * action tokens pay an entry, which ActKV's retention policy thresholds ([ACT], paragraph on

@@ -20,6 +20,7 @@ from ._abi import (  # noqa: F401
     kvc_lrfu_update,
     kvc_lse_workspace_size,
     kvc_score,
+    kvc_score_noalloc,
     kvc_score_workspace_size,
     kvc_select_topm,
     kvc_status_string,

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkvc.so")
 
 KVC_OK, KVC_ERR_INVALID_ARGUMENT, KVC_ERR_UNSUPPORTED, KVC_ERR_WORKSPACE_TOO_SMALL, KVC_ERR_HIP = range(5)
 KVC_F32, KVC_BF16 = 0, 1
+KVC_NOALLOC_SCRATCH_BYTES = 64 << 20  # the static scratch of kvc_score_noalloc (kvc.h)
 
 
 class KvcError(RuntimeError):
@@ -49,6 +50,8 @@ _SIGS = {
     "kvc_score": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView), ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
                                  ctypes.c_void_p]),
+    "kvc_score_noalloc": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView),
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "kvc_attention_mass": (ctypes.c_int, [ctypes.POINTER(_Shape), ctypes.c_void_p, ctypes.POINTER(_KView),
                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p]),
@@ -235,6 +238,19 @@ def kvc_score(shape: Shape, q, k: KView, lse, bias, scores, ws=None, stream=None
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().kvc_score(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), _ptr(lse), _ptr(bias), _ptr(scores),
                             _ptr(ws), ws_bytes, _stream(stream)), "kvc_score")
+
+
+def kvc_score_noalloc(shape: Shape, q, k: KView, lse, bias, scores, stream=None) -> None:
+    S, H, HG, R = shape.num_seqs, shape.num_kv_heads, shape.num_kv_heads * shape.group, shape.num_queries
+    _need(q, S * HG * R * shape.head_dim * _elt(k.dtype), "q")
+    _check_kview(shape, k)
+    _need(lse, S * HG * R * 4, "lse")
+    _need(bias, S * shape.n_max * 4, "bias")
+    _need(scores, S * H * shape.n_max * 4, "scores")
+    sh, _keep = shape.c()
+    kv = k.c()
+    _check(load().kvc_score_noalloc(ctypes.byref(sh), _ptr(q), ctypes.byref(kv), _ptr(lse), _ptr(bias),
+                                    _ptr(scores), _stream(stream)), "kvc_score_noalloc")
 
 
 def kvc_attention_mass(shape: Shape, q, k: KView, lse, bias, mass, ws=None, stream=None) -> None:

@@ -6,6 +6,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -413,6 +414,49 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
 
 }  // namespace
 
+// ------------------------------------------------------------------------------------------------
+// Static scratch of kvc_score_noalloc: the LSE partials and the LSE of a score call that computes
+// its own LSE, in a device array of fixed size instead of a caller-provided workspace. Each GPU
+// holds its own copy for the life of the process. Host code never passes `scratch` itself to a
+// kernel (on the host it only names the variable): its device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and kept in g_scratch_ptr.
+// ------------------------------------------------------------------------------------------------
+static constexpr size_t kScratchBytes = KVC_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this process's scratch on the device that runs `stream`.
+kvc_status scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "device of the stream");
+  if (dev < 0 || dev >= kMaxDevices) return fail(KVC_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_fail(e2, "hipSetDevice");
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(KVC_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return KVC_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* kvc_status_string(kvc_status st) {
@@ -503,6 +547,22 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
 kvc_status kvc_score(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse, const float* bias,
                      float* scores, void* ws, size_t ws_bytes, void* stream) {
   return run_score(sh, q, k, lse, bias, scores, ws, ws_bytes, stream, 2, "scores");
+}
+
+kvc_status kvc_score_noalloc(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse,
+                             const float* bias, float* scores, void* stream) {
+  if (kvc_status st = check_shape(sh)) return st;
+  if (kvc_status st = check_view(sh, k)) return st;
+  if (lse) return run_score(sh, q, k, lse, bias, scores, nullptr, 0, stream, 2, "scores");
+  const size_t need = partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  if (need > kScratchBytes)
+    return fail(KVC_ERR_UNSUPPORTED,
+                "kvc_score_noalloc: computing the LSE of this shape needs %zu bytes of scratch; the static scratch "
+                "holds %zu (supply the LSE, or call kvc_score with a workspace)",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (kvc_status st = scratch_for_stream(static_cast<hipStream_t>(stream), &ws)) return st;
+  return run_score(sh, q, k, lse, bias, scores, ws, kScratchBytes, stream, 2, "scores");
 }
 
 kvc_status kvc_attention_mass(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* lse,

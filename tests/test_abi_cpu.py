@@ -298,3 +298,31 @@ def test_oversized_launches_rejected_before_any_launch(lib):
     sh3, keep3 = A.Shape(2, 1 << 24, 1, 16, 128, 1 << 16, np.full(2, 1 << 16, dtype=np.int32), 0.088).c()
     st = lib.kvc_score(ctypes.byref(sh3), FAKE, ctypes.byref(kv), None, None, FAKE, FAKE, 1 << 62, None)
     assert st == A.KVC_ERR_UNSUPPORTED, lib.kvc_last_error()
+
+
+def test_noalloc_scratch_limit_and_validation(lib):
+    """kvc_score_noalloc: the binding's scratch size is the header's; bad shapes are invalid
+    arguments; a shape whose computed LSE needs more scratch than the static array holds is
+    rejected as unsupported before any device call (the same shape the GPU test uses)."""
+    text = open(HEADER).read()
+    m = re.search(r"#define KVC_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == A.KVC_NOALLOC_SCRATCH_BYTES
+    kv = A.KView(FAKE, A.KVC_BF16).c()
+    sh, keep = _shape(d=64).c()
+    assert lib.kvc_score_noalloc(ctypes.byref(sh), FAKE, ctypes.byref(kv), None, None, FAKE, None) == \
+        A.KVC_ERR_UNSUPPORTED
+    sh, keep = _shape(n=(0, 5)).c()
+    assert lib.kvc_score_noalloc(ctypes.byref(sh), FAKE, ctypes.byref(kv), None, None, FAKE, None) == \
+        A.KVC_ERR_INVALID_ARGUMENT
+    S, H, G, q, n = 64, 4, 8, 256, 131072
+    shape = A.Shape(S, H, G, q, 128, n, np.full(S, n, dtype=np.int32), 0.088)
+    pv = A.KView(FAKE, A.KVC_BF16, 16, FAKE, n // 16)
+    assert oc.kvc_score_workspace_size(shape, pv, False) > A.KVC_NOALLOC_SCRATCH_BYTES
+    sh, keep = shape.c()
+    v = pv.c()
+    st = lib.kvc_score_noalloc(ctypes.byref(sh), FAKE, ctypes.byref(v), None, None, FAKE, None)
+    assert st == A.KVC_ERR_UNSUPPORTED and b"scratch" in lib.kvc_last_error()
+    # the action-token trajectory (8 heads x 1320 rows, 33000 keys) fits
+    small = A.Shape(1, 8, 4, 330, 128, 33000, np.array([33000], dtype=np.int32), 0.088)
+    assert 0 < oc.kvc_score_workspace_size(small, A.KView(FAKE, A.KVC_BF16, 16, FAKE, 2063), False) \
+        <= A.KVC_NOALLOC_SCRATCH_BYTES
