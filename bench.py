@@ -83,15 +83,16 @@ def scored_lens(w):
 
 
 def algorithmic_bytes(w, moved_rows=None) -> dict:
-    """Bytes the method must move per step (reads + writes), per stage."""
+    """Bytes the method must move per step (reads + writes), per stage: every key row and proxy row
+    once, the scores written, and a supplied LSE. (How often an implementation reads the keys is
+    not counted: the MFMA path reads them once for the LSE and once for the scores, the few-row
+    paths once plus R logits per key.)"""
     el = 2 if w.dtype == "bf16" else 4
     row = w.d * el
     entries = sum(scored_lens(w)) * w.H
     kept = sum(w.m) * w.H
     rows_q = w.S * w.H * w.R
     score = entries * row + rows_q * row + entries * 4 + (rows_q * 4 if w.lse_supplied else 0)
-    if not w.lse_supplied:
-        score += entries * row + rows_q * row  # LSE pass reads K and Q once more
     select = entries * 4 + kept * 4
     if w.name == "sentinel":  # slot map read by both passes; redirect writes the evicted entries
         score += entries * 4 * 2
@@ -529,13 +530,17 @@ def main():
         "flops_per_launch": flops,
         "launch_ms": avg[0],
     }
-    if w.dtype == "f32":  # float32 scoring runs on the vector ALU (score_valu / lse_partials_valu)
-        roof.update({"kernel": "score_valu + lse_partials_valu (score stage)", "bound": "alu",
+    few_kernels = ("valu_lse_pass + valu_score_cached" if w.R <= 32 else "valu_lse_pass + valu_score_keys")
+    if w.lse_supplied:
+        few_kernels = "valu_score_keys"
+    if w.dtype == "f32":  # float32 scoring runs on the vector ALU
+        roof.update({"kernel": few_kernels + " (score stage)", "bound": "alu",
                      "achieved": achieved_tf, "peak": F32_VALU_PEAK_TFLOPS,
                      "frac": achieved_tf / F32_VALU_PEAK_TFLOPS})
-    elif w.R < 16:  # bf16 with few proxy rows: the VALU kernels, bound by reading K (twice)
+    elif w.R < 16:  # bf16 with few proxy rows: one pass over K (few-row MFMA kernels), bound by reading it
         gbps = ab["score"] / score_s / 1e9
-        roof.update({"kernel": "score_valu + lse_partials_valu (score stage)", "bound": "hbm", "achieved": gbps,
+        small = "small_score_keys" if w.lse_supplied else "small_lse_pass + valu_score_cached"
+        roof.update({"kernel": small + " (score stage)", "bound": "hbm", "achieved": gbps,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                      "bytes_per_launch": ab["score"]})
     if w.name == "am":  # the fit dominates: its kernels against the peak of the units they use

@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libkvc.so")
-SOURCES = ["api.hip", "score_mfma.hip", "lse_mfma.hip", "score_valu.hip", "select.hip", "retain.hip", "compact.hip", "am.hip"]
+SOURCES = ["api.hip", "score_mfma.hip", "lse_mfma.hip", "score_valu.hip", "score_small.hip", "select.hip", "retain.hip", "compact.hip", "am.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 VALU instructions are kept out of the generated code.

@@ -17,7 +17,10 @@ namespace kvc {
 int score_mfma_tiles(int n, int ksub);
 bool score_mfma_ksub_ok(int ksub, int layout, bool has_bias, bool causal);
 int lse_mfma_row_blocks(int R);
-int score_valu_tiles(int n);
+int valu_row_block(int R);
+int valu_min_chunk_f32(int R);
+int small_chunk();
+int valu_cached_tiles(int n);
 int contig_tiles(int m, bool f32);
 int paged_tiles(int m);
 hipError_t launch_score_mfma(int layout, bool has_bias, int ksub, const void* q, const void* k, const int32_t* table,
@@ -30,13 +33,22 @@ hipError_t launch_lse_partials_mfma(int layout, bool has_bias, const void* q, co
                                     const SeqTable& T, hipStream_t st);
 hipError_t launch_lse_combine(const float2* partials, float* lse_out, int H, int R, int kchunk, const SeqTable& T,
                               hipStream_t st);
-hipError_t launch_score_valu(bool f32, int layout, bool has_bias, const void* q, const void* k, const int32_t* table,
-                             int max_blocks, const float* lse, const float* bias, const int32_t* rpos, float* scores,
-                             int H, int R, int64_t n_max, float scale, int pw, int dead, const SeqTable& T,
-                             hipStream_t st);
-hipError_t launch_lse_partials_valu(bool f32, int layout, bool has_bias, const void* q, const void* k,
-                                    const int32_t* table, int max_blocks, const float* bias, const int32_t* rpos,
-                                    float2* partials, int H, int R, int64_t n_max, float scale, int dead,
+// few proxy rows: float32 on the vector ALU (score_valu.hip), bf16 on MFMA (score_small.hip)
+hipError_t launch_valu_lse_pass(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
+                                const float* bias, const int32_t* rpos, float2* ws, bool cache, int H, int R,
+                                int64_t n_max, float scale, int kchunk, int dead, const SeqTable& T, hipStream_t st);
+hipError_t launch_valu_score_keys(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
+                                  const float* lse, const float2* ws, const float* bias, const int32_t* rpos,
+                                  float* out, int H, int R, int64_t n_max, float scale, int pw, int lse_kchunk,
+                                  int chunk, int dead, const SeqTable& T, hipStream_t st);
+hipError_t launch_small_lse_pass(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
+                                 const float* bias, const int32_t* rpos, float2* ws, bool cache, int H, int R,
+                                 int64_t n_max, float scale, int dead, const SeqTable& T, hipStream_t st);
+hipError_t launch_small_score_keys(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
+                                   const float* lse, const float2* ws, const float* bias, const int32_t* rpos,
+                                   float* out, int H, int R, int64_t n_max, float scale, int pw, int dead,
+                                   const SeqTable& T, hipStream_t st);
+hipError_t launch_valu_score_cached(const float2* ws, float* out, int H, int R, int64_t n_max, int kchunk, int pw,
                                     const SeqTable& T, hipStream_t st);
 hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
                                  const SeqTable& T, hipStream_t st);
@@ -241,19 +253,51 @@ int mfma_kchunk(const kvc_shape* sh) {
   return best;
 }
 
+// Keys per workgroup of a few-row pass. bf16 (MFMA): the kernels' fixed chunk. float32: a power
+// of two, at least the kernels' shortest chunk (whole rounds of their key-row prefetch ring) and
+// at most kValuMaxChunk; the longest that still gives every CU four workgroups (`per` = workgroups
+// per key chunk: the row blocks of the LSE pass, 1 for the score pass), else the shortest.
+int valu_chunk(const kvc_shape* sh, const kvc_kv_view* kv, int per) {
+  if (kv->dtype != KVC_F32) return small_chunk();
+  const int lo = valu_min_chunk_f32(sh->group * sh->num_queries);
+  for (int c = kValuMaxChunk; c > lo; c >>= 1) {
+    int64_t wg = 0;
+    for (int s = 0; s < sh->num_seqs; ++s) wg += (int64_t)sh->num_kv_heads * per * ((sh->seq_lens[s] + c - 1) / c);
+    if (wg >= 4 * kCUs) return c;
+  }
+  return lo;
+}
+
+// Row blocks of the few-row LSE pass: float32 takes the rows in blocks (of valu_row_block), the
+// bf16 MFMA pass all of them (fewer than 16) at once.
+int valu_row_blocks(const kvc_shape* sh, const kvc_kv_view* kv) {
+  const int R = sh->group * sh->num_queries;
+  if (kv->dtype != KVC_F32) return 1;
+  const int rb = valu_row_block(R);
+  return (R + rb - 1) / rb;
+}
+
 int lse_kchunk(const kvc_shape* sh, const kvc_kv_view* kv) {
-  return use_mfma(sh, kv) ? mfma_kchunk(sh) : 256;  // VALU: a chunk is one 256-key tile
+  return use_mfma(sh, kv) ? mfma_kchunk(sh) : valu_chunk(sh, kv, valu_row_blocks(sh, kv));
 }
 
-// float2 partial slots of sequence s in the LSE workspace
-int64_t partial_slots(const kvc_shape* sh, int s, int kchunk) {
-  const int64_t R = (int64_t)sh->group * sh->num_queries;
-  return (int64_t)sh->num_kv_heads * ((sh->seq_lens[s] + kchunk - 1) / kchunk) * R;
+// A VALU score call that computes its LSE keeps the logits of its LSE pass when there are few rows.
+bool valu_cache(const kvc_shape* sh, const kvc_kv_view* kv) {
+  return !use_mfma(sh, kv) && sh->group * sh->num_queries <= kValuMaxCacheRows;
 }
 
-size_t partials_bytes(const kvc_shape* sh, int kchunk) {
+// float2 slots of sequence s in the LSE pass's workspace region: the chunk partials (MFMA), or the
+// VALU region (partials, then the cached logits when `for_score` and the rows are few).
+int64_t lse_region_slots(const kvc_shape* sh, const kvc_kv_view* kv, int s, int kchunk, bool for_score) {
+  const int R = sh->group * sh->num_queries;
+  if (use_mfma(sh, kv)) return (int64_t)sh->num_kv_heads * ((sh->seq_lens[s] + kchunk - 1) / kchunk) * R;
+  return valu_region_float2(sh->num_kv_heads, R, sh->seq_lens[s], kchunk, for_score && valu_cache(sh, kv));
+}
+
+size_t lse_region_bytes(const kvc_shape* sh, const kvc_kv_view* kv, bool for_score) {
+  const int kc = lse_kchunk(sh, kv);
   int64_t slots = 0;
-  for (int s = 0; s < sh->num_seqs; ++s) slots += partial_slots(sh, s, kchunk);
+  for (int s = 0; s < sh->num_seqs; ++s) slots += lse_region_slots(sh, kv, s, kc, for_score);
   return align_up((size_t)slots * sizeof(float2));
 }
 
@@ -361,7 +405,7 @@ RowOrder row_order(const kvc_shape* sh) {
 int64_t lse_partial_items(const kvc_shape* sh, const kvc_kv_view* kv, int s) {
   const int R = sh->group * sh->num_queries;
   const int kc = lse_kchunk(sh, kv);
-  const int64_t rb = use_mfma(sh, kv) ? lse_mfma_row_blocks(R) : 1;
+  const int64_t rb = use_mfma(sh, kv) ? lse_mfma_row_blocks(R) : valu_row_blocks(sh, kv);
   return (int64_t)sh->num_kv_heads * rb * ((sh->seq_lens[s] + kc - 1) / kc);
 }
 
@@ -375,10 +419,24 @@ kvc_status check_lse_work(const kvc_shape* sh, const kvc_kv_view* kv) {
   return check_items(sh, [&](int) { return lse_combine_items(sh); }, "lse combine kernel");
 }
 
-// Internal LSE: per-chunk partials into ws_partials, then combined into lse_out (the work was
-// checked by check_lse_work).
+// Per-sequence offsets (float2 units) of the LSE pass's regions in the workspace.
+std::vector<int64_t> lse_region_offsets(const kvc_shape* sh, const kvc_kv_view* kv, bool for_score) {
+  const int kc = lse_kchunk(sh, kv);
+  std::vector<int64_t> off(sh->num_seqs);
+  int64_t acc = 0;
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    off[s] = acc;
+    acc += lse_region_slots(sh, kv, s, kc, for_score);
+  }
+  return off;
+}
+
+// The LSE pass: per-chunk partials (and, for a VALU score call with few rows, the cached logits)
+// into the workspace regions at ws_partials. Unless `for_score` is a VALU call (whose score kernel
+// merges the partials itself), the partials are then combined into lse_out. The work was checked
+// by check_lse_work.
 kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, const float* bias, float* lse_out,
-                   void* ws_partials, hipStream_t st) {
+                   void* ws_partials, hipStream_t st, bool for_score = false) {
   const int H = sh->num_kv_heads;
   const int R = sh->group * sh->num_queries;
   const bool mf = use_mfma(sh, kv);
@@ -386,12 +444,7 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
   const int32_t* index = index_of(kv);
   const bool has_bias = bias != nullptr;
   const int kc = lse_kchunk(sh, kv);
-  std::vector<int64_t> off(sh->num_seqs);
-  int64_t acc = 0;
-  for (int s = 0; s < sh->num_seqs; ++s) {
-    off[s] = acc;
-    acc += partial_slots(sh, s, kc);
-  }
+  const std::vector<int64_t> off = lse_region_offsets(sh, kv, for_score);
   auto* parts = static_cast<float2*>(ws_partials);
   auto offset = [&](int s) -> int64_t { return off[s]; };
   hipError_t e = for_each_chunk(
@@ -401,10 +454,15 @@ kvc_status run_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* kv, co
           return launch_lse_partials_mfma(layout, has_bias, q, kv->data, index, kv->max_blocks, bias, sh->row_pos,
                                           parts, H, R, sh->n_max, sh->scale, kc, kv->dead_slot, row_order(sh), T,
                                           st);
-        return launch_lse_partials_valu(kv->dtype == KVC_F32, layout, has_bias, q, kv->data, index, kv->max_blocks,
-                                        bias, sh->row_pos, parts, H, R, sh->n_max, sh->scale, kv->dead_slot, T, st);
+        const bool cache = for_score && valu_cache(sh, kv);
+        if (kv->dtype == KVC_F32)
+          return launch_valu_lse_pass(layout, q, kv->data, index, kv->max_blocks, bias, sh->row_pos, parts, cache, H, R,
+                                      sh->n_max, sh->scale, kc, kv->dead_slot, T, st);
+        return launch_small_lse_pass(layout, q, kv->data, index, kv->max_blocks, bias, sh->row_pos, parts, cache, H, R,
+                                     sh->n_max, sh->scale, kv->dead_slot, T, st);
       });
   if (e != hipSuccess) return hip_fail(e, "lse partial kernel");
+  if (for_score && !mf) return KVC_OK;
   e = for_each_chunk(
       sh, nullptr, [&](int) { return lse_combine_items(sh); }, offset,
       [&](const SeqTable& T) { return launch_lse_combine(parts, lse_out, H, R, kc, T, st); });
@@ -476,7 +534,7 @@ int kvc_version(void) { return kVersion; }
 
 size_t kvc_lse_workspace_size(const kvc_shape* sh, const kvc_kv_view* k) {
   if (check_shape(sh) != KVC_OK || check_view(sh, k) != KVC_OK) return 0;
-  return partials_bytes(sh, lse_kchunk(sh, k));
+  return lse_region_bytes(sh, k, false);
 }
 
 kvc_status kvc_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* k, const float* bias, float* lse_out,
@@ -485,7 +543,7 @@ kvc_status kvc_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* k, con
   if (kvc_status st = check_view(sh, k)) return st;
   if (!q || !lse_out) return fail(KVC_ERR_INVALID_ARGUMENT, "q and lse_out must be non-NULL");
   if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
-  const size_t need = partials_bytes(sh, lse_kchunk(sh, k));
+  const size_t need = lse_region_bytes(sh, k, false);
   if (!ws || ws_bytes < need)
     return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "lse needs %zu workspace bytes, got %zu", need, ws ? ws_bytes : 0);
   if (kvc_status st = check_lse_work(sh, k)) return st;
@@ -496,7 +554,7 @@ kvc_status kvc_lse(const kvc_shape* sh, const void* q, const kvc_kv_view* k, con
 size_t kvc_score_workspace_size(const kvc_shape* sh, const kvc_kv_view* k, int lse_supplied) {
   if (check_shape(sh) != KVC_OK || check_view(sh, k) != KVC_OK) return 0;
   if (lse_supplied) return 0;
-  return partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  return lse_region_bytes(sh, k, true) + lse_bytes(sh);
 }
 
 // Per-key reduction over the proxy rows of alpha^pw: pw = 2 gives the TE score (after the square
@@ -514,31 +572,45 @@ static kvc_status run_score(const kvc_shape* sh, const void* q, const kvc_kv_vie
   const int layout = layout_of(k);
   const int32_t* index = index_of(k);
   const int H = sh->num_kv_heads;
+  const bool f32 = k->dtype == KVC_F32;
+  // MFMA: LSE pass + combine (when not supplied), then the score kernel over key tiles. VALU: the
+  // LSE pass (logits cached when the rows are few), then the score kernel -- from the cached
+  // logits, or from the keys again -- merging the partials itself.
+  const bool cached = !lse && valu_cache(sh, k);
   const int ksub = mf ? score_ksub(sh, layout, bias != nullptr) : 0;
+  const int vchunk = mf ? 0 : valu_chunk(sh, k, 1);
   auto items = [&](int s) -> int64_t {
-    return (int64_t)H * (mf ? score_mfma_tiles(sh->seq_lens[s], ksub) : score_valu_tiles(sh->seq_lens[s]));
+    const int n = sh->seq_lens[s];
+    return (int64_t)H * (mf ? score_mfma_tiles(n, ksub) : cached ? valu_cached_tiles(n) : (n + vchunk - 1) / vchunk);
   };
   if (kvc_status s2 = check_items(sh, items, "score kernel")) return s2;
   const float* lse_rows = lse;
+  const size_t rb_bytes = lse ? 0 : lse_region_bytes(sh, k, true);
   if (!lse) {
-    const size_t pb = partials_bytes(sh, lse_kchunk(sh, k));
-    const size_t need = pb + lse_bytes(sh);
+    const size_t need = rb_bytes + lse_bytes(sh);
     if (!ws || ws_bytes < need)
       return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "%s needs %zu workspace bytes, got %zu", what, need, ws ? ws_bytes : 0);
     if (kvc_status s2 = check_lse_work(sh, k)) return s2;
-    float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + pb);
-    if (kvc_status s2 = run_lse(sh, q, k, bias, lse_ws, ws, st)) return s2;
-    lse_rows = lse_ws;
+    float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + rb_bytes);
+    if (kvc_status s2 = run_lse(sh, q, k, bias, lse_ws, ws, st, true)) return s2;
+    lse_rows = mf ? lse_ws : nullptr;  // VALU: merged from the partials by the score kernel
   }
+  const float2* regions = static_cast<const float2*>(ws);
+  const std::vector<int64_t> off = (!lse && !mf) ? lse_region_offsets(sh, k, true) : std::vector<int64_t>();
+  auto offset = [&](int s) -> int64_t { return off.empty() ? 0 : off[s]; };
+  const int lkc = (!lse && !mf) ? lse_kchunk(sh, k) : 0;
   const hipError_t e = for_each_chunk(
-      sh, nullptr, items, no_offset, [&](const SeqTable& T) {
+      sh, nullptr, items, offset, [&](const SeqTable& T) {
         if (mf)
           return launch_score_mfma(layout, bias != nullptr, ksub, q, k->data, index, k->max_blocks, lse_rows, bias,
                                    sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, row_order(sh), T,
                                    st);
-        return launch_score_valu(k->dtype == KVC_F32, layout, bias != nullptr, q, k->data, index, k->max_blocks,
-                                 lse_rows, bias, sh->row_pos, out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T,
-                                 st);
+        if (cached) return launch_valu_score_cached(regions, out, H, R, sh->n_max, lkc, pw, T, st);
+        if (f32)
+          return launch_valu_score_keys(layout, q, k->data, index, k->max_blocks, lse_rows, regions, bias, sh->row_pos,
+                                        out, H, R, sh->n_max, sh->scale, pw, lkc, vchunk, k->dead_slot, T, st);
+        return launch_small_score_keys(layout, q, k->data, index, k->max_blocks, lse_rows, regions, bias, sh->row_pos,
+                                       out, H, R, sh->n_max, sh->scale, pw, k->dead_slot, T, st);
       });
   if (e != hipSuccess) return hip_fail(e, "score kernel");
   return ok();
@@ -554,7 +626,7 @@ kvc_status kvc_score_noalloc(const kvc_shape* sh, const void* q, const kvc_kv_vi
   if (kvc_status st = check_shape(sh)) return st;
   if (kvc_status st = check_view(sh, k)) return st;
   if (lse) return run_score(sh, q, k, lse, bias, scores, nullptr, 0, stream, 2, "scores");
-  const size_t need = partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  const size_t need = lse_region_bytes(sh, k, true) + lse_bytes(sh);
   if (need > kScratchBytes)
     return fail(KVC_ERR_UNSUPPORTED,
                 "kvc_score_noalloc: computing the LSE of this shape needs %zu bytes of scratch; the static scratch "
@@ -721,7 +793,7 @@ size_t kvc_am_workspace_size(const kvc_shape* sh, const kvc_kv_view* k, const kv
   if (check_shape(sh) != KVC_OK || check_am(sh, k, v) != KVC_OK || !m) return 0;
   for (int s = 0; s < sh->num_seqs; ++s)
     if (m[s] < 0 || m[s] > sh->seq_lens[s]) return 0;
-  const size_t lse_part = lse_supplied ? 0 : partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  const size_t lse_part = lse_supplied ? 0 : lse_region_bytes(sh, k, false) + lse_bytes(sh);
   return lse_part + am_bytes(sh, m);
 }
 
@@ -735,7 +807,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   if (!isfinite(sh->scale)) return fail(KVC_ERR_INVALID_ARGUMENT, "scale must be finite");
   if (iters_beta < 0 || iters_beta > 100000 || iters_v < 0 || iters_v > 100000)
     return fail(KVC_ERR_INVALID_ARGUMENT, "iteration counts must lie in [0, 100000]");
-  const size_t lse_part = lse ? 0 : partials_bytes(sh, lse_kchunk(sh, k)) + lse_bytes(sh);
+  const size_t lse_part = lse ? 0 : lse_region_bytes(sh, k, false) + lse_bytes(sh);
   const size_t need = lse_part + am_bytes(sh, m);
   if (!ws || ws_bytes < need)
     return fail(KVC_ERR_WORKSPACE_TOO_SMALL, "attention matching needs %zu workspace bytes, got %zu", need,
@@ -775,7 +847,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   }
   const float* lse_rows = lse;
   if (!lse) {
-    float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + partials_bytes(sh, lse_kchunk(sh, k)));
+    float* lse_ws = reinterpret_cast<float*>(static_cast<char*>(ws) + lse_region_bytes(sh, k, false));
     if (kvc_status s2 = run_lse(sh, q, k, nullptr, lse_ws, ws, st)) return s2;
     lse_rows = lse_ws;
   }

@@ -16,6 +16,10 @@ enum : int { kContig = 0, kPaged = 1, kSlots = 2 };
 
 // longest key chunk one LSE-pass workgroup may cover (the host picks 4096, 2048, 1024 or 512)
 constexpr int kLseMaxChunk = 4096;
+// VALU scoring: longest key chunk of one workgroup, and the most proxy rows whose logits are cached
+// (R floats per key, written by the LSE pass and read by the score pass instead of the key rows)
+constexpr int kValuMaxChunk = 1024;
+constexpr int kValuMaxCacheRows = 32;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // Squared weights are accumulated as exp2(2*log2(alpha) + kSqOffset) so that alpha down to
@@ -45,6 +49,20 @@ struct SeqTable {
   int64_t off[kChunkSeqs];        // kernel-specific per-sequence offset (workspace slots)
 };
 static_assert(sizeof(SeqTable) <= 3800, "SeqTable must fit the kernel-argument segment");
+
+// Workspace region of one sequence for the few-row LSE pass, in float2 units (16-byte
+// multiples): the chunk partials [H][nkc][R] (float2 (max, sum)), nkc = ceil(n/kchunk), then,
+// when the logits are cached, [H][R][nkc * kchunk] float32 logits (whole chunks, so the pass stores
+// every lane's logit without a bounds test).
+__host__ __device__ inline int64_t valu_partials_float2(int H, int R, int n, int kchunk) {
+  const int64_t p = (int64_t)H * ((n + kchunk - 1) / kchunk) * R;
+  return (p + 1) & ~(int64_t)1;
+}
+__host__ __device__ inline int64_t valu_region_float2(int H, int R, int n, int kchunk, bool cache) {
+  const int64_t npad = (int64_t)((n + kchunk - 1) / kchunk) * kchunk;
+  const int64_t lg = cache ? (((int64_t)H * R * npad + 3) & ~(int64_t)3) / 2 : 0;
+  return valu_partials_float2(H, R, n, kchunk) + lg;
+}
 
 // Order in which the MFMA kernels take a unit's proxy rows when the rows are causal. A unit's
 // R = G * q rows are stored head-major (row g * q + i is query i of query head g); with causal

@@ -57,10 +57,13 @@ def test_workspace_sizes():
     assert full > lse_only > 0 and full % 256 == 0
     # computed LSE needs one float per proxy row on top of the partials
     assert full - lse_only >= 2 * 8 * 4 * 1024 * 4
-    # VALU path (float32) uses 256-key chunks
+    # VALU path (float32, 32 rows in two blocks of 16): one partial per row and 64-key chunk (the
+    # shortest chunk, since even it gives fewer than 4 workgroups per CU)
     kvf = A.KView(FAKE, A.KVC_F32)
     shf = _shape(S=1, H=1, G=1, q=32, n=(4096,), n_max=4096)
-    assert oc.kvc_lse_workspace_size(shf, kvf) == 16 * 32 * 8
+    assert oc.kvc_lse_workspace_size(shf, kvf) == 64 * 32 * 8
+    # a score call that computes its LSE also keeps the 32 logits of every key, and the LSE itself
+    assert oc.kvc_score_workspace_size(shf, kvf, False) == 64 * 32 * 8 + 4096 * 32 * 4 + 256
     # invalid shapes size to 0
     assert oc.kvc_lse_workspace_size(_shape(d=64), kv) == 0
 
