@@ -35,6 +35,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 F32_VALU_PEAK_TFLOPS = 78.6
 MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_counters.txt")
 # the score kernel's source: its own file and the headers it includes
 SCORE_SRCS = [os.path.join(ROOT, "online_compaction_amd", "csrc", f)
               for f in ("score_mfma.hip", "mfma_common.h", "kvc_internal.h")]
@@ -269,22 +270,45 @@ def cpu_baseline(w, budget_s: float, am_iters=(0, 0), single_core: bool = False)
 
 # ---------------------------------------------------------------------------------- roofline
 
-def traffic_from_profile(launch_s: float):
-    """HBM bytes per launch of the score kernel from the committed PMC summary, or None if the
-    summary is missing or the kernel source changed since the counters were taken."""
-    if not os.path.exists(TRAFFIC_FILE):
+def _profile_fields(path: str, check_source: bool = True):
+    """The key = value lines of a committed PMC summary, or None if it is missing or (unless
+    check_source is False) the score kernel's source changed since its counters were taken."""
+    if not os.path.exists(path):
         return None
     kv = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if "=" in line and not line.startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    src = score_source_sha256()
-    if kv.get("source_sha256") != src:
+    if check_source and kv.get("source_sha256") != score_source_sha256():
+        return None
+    return kv
+
+
+def traffic_from_profile():
+    """HBM bytes per launch of the score kernel from the committed PMC summary, or None."""
+    kv = _profile_fields(TRAFFIC_FILE)
+    try:
+        return float(kv["hbm_bytes_per_launch"]) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def serialized_bound_from_profile(launch_ms: float, check_source: bool = True):
+    """The score kernel's serialized MFMA + VALU bound from its committed pipe counters: the
+    QK^T FLOP at the bf16 spec rate plus every VALU instruction it issues at 4 cycles per wave
+    at 2.4 GHz, none of it overlapped, beside the busy fractions the counters read. `frac` is
+    that bound over the measured launch (1.0 = the kernel runs no slower than its two pipes
+    back to back). None if the summary is missing or stale."""
+    kv = _profile_fields(COUNTERS_FILE, check_source)
+    if not kv:
         return None
     try:
-        return float(kv["hbm_bytes_per_launch"])
+        b = float(kv["serialized_bound_ms"])
+        return {"ms": b, "mfma_ms": float(kv["mfma_only_ms"]), "valu_ms": float(kv["valu_only_ms"]),
+                "frac": b / launch_ms, "mfma_busy": float(kv["mfma_busy"]),
+                "valu_busy": float(kv["valu_busy"]), "mfma_valu_coexec": float(kv["coexec"])}
     except (KeyError, ValueError):
         return None
 
@@ -518,7 +542,7 @@ def main():
     score_s = avg[0] * 1e-3
     achieved_tf = flops / score_s / 1e12
     step_s = ms_step * 1e-3
-    traffic = traffic_from_profile(score_s) if (w.name == "c3") else None
+    traffic = traffic_from_profile() if (w.name == "c3") else None
     roof = {
         "kernel": "score_mfma (kvc_attention_mass)" if w.name == "actkv" else "score_mfma (kvc_score)",
         "bound": "mfma",
@@ -530,6 +554,8 @@ def main():
         "flops_per_launch": flops,
         "launch_ms": avg[0],
     }
+    if w.name == "c3":
+        roof["serialized_bound"] = serialized_bound_from_profile(avg[0])
     few_kernels = ("valu_lse_pass + valu_score_cached" if w.R <= 32 else "valu_lse_pass + valu_score_keys")
     if w.lse_supplied:
         few_kernels = "valu_score_keys"

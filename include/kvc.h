@@ -31,7 +31,9 @@
  * freed_counts, written) synchronously during the call. The library never allocates or frees
  * memory, keeps no pointer after returning, holds no state between calls and never
  * synchronises the stream: device work is enqueued on `stream` (a hipStream_t, NULL = the
- * default stream) and runs asynchronously. All functions are thread-safe.
+ * default stream) and runs asynchronously. All functions are thread-safe. One exception:
+ * kvc_score_noalloc keeps its scratch in a static device array per GPU (below), whose address
+ * the library looks up once per device and keeps; calls of it that overlap on one GPU race.
  *
  * Errors: arguments are validated before anything is enqueued; on an error nothing is launched
  * and no output is touched. Inputs must be finite (unchecked). kvc_last_error() returns a
