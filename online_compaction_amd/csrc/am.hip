@@ -6,40 +6,44 @@
 // With w = exp(beta) the first is non-negative least squares in w; the second, with
 // P_C = diag(1 / (E w)) E diag(w) the compacted attention, is least squares in V_C.
 //
-// Per unit the kernels materialise E_ij = exp(c q_i . k_Cj - ME) (ME the largest kept logit) and
-// the target A(Q; K, V) = P_full V, P_full_ij = exp(c q_i . k_j - LSE_i) over all n keys (P_full
-// itself only one 64-key chunk at a time, in registers and LDS), then iterate:
+// Per unit, with E_ij = exp(c q_i . k_Cj - ME) (ME the largest kept logit) and the target
+// A(Q; K, V) = P_full V, P_full_ij = exp(c q_i . k_j - LSE_i) over all n keys:
 //   beta: w' <- w' * (E^T z) / (E^T E w') (multiplicative NNLS updates), z_i = exp(LSE_i - Mz);
 //   V_C:  V <- V - eta P_C^T (P_C V - Y) from the kept keys' values (Landweber),
 //         eta = 1 / max_j sum_i (P_C)_ij.
-// E and z carry separate factors so that neither underflows in float32 (Mz = the largest LSE,
-// lowered to ME + 80 if the kept logits lie far below it). The updates are scale-equivariant:
-// with w' = exp(ME - Mz) w they are the updates of w = exp(beta) from w = 1 on the unscaled
-// exponentials, so w' starts at exp(ME - Mz) and beta = log w' - (ME - Mz). Once beta is fixed,
-// E is overwritten in place by P_C and P_C^T is written beside it (PT), so both value products
-// read their left operand row by row.
+// E is never stored: every pass that needs it re-forms its tiles from the bf16 rows of Q and of
+// the gathered kept keys on the MFMA units (am_bias), which costs less than reading 4 bytes per
+// entry back from memory; P_full exists only one 64-key chunk at a time (am_target). P_C and
+// P_C^T are written once, as split rows, when beta is fixed. The Landweber steps run as the
+// equivalent iteration of the residual on the smaller side of P_C with its Gram matrix (am_gram,
+// then one product per step). E and z carry separate factors so that neither underflows in
+// float32 (Mz = the largest LSE, lowered to ME + 80 if the kept logits lie far below it). The
+// updates are scale-equivariant: with w' = exp(ME - Mz) w they are the updates of w = exp(beta)
+// from w = 1 on the unscaled exponentials, so w' starts at exp(ME - Mz) and
+// beta = log w' - (ME - Mz).
 // The QK^T products use v_mfma_f32_16x16x32_bf16 on the stored bf16 rows; the solver's matrix
 // products run on the same instruction with their float32 operands stored split into bf16 high
-// and low parts (three products each); the vector products are plain VALU. Every
-// reduction has a fixed order (split sums land in partial buffers that one pass adds up in
-// order), so a fit is reproducible bit for bit.
+// and low parts (three products each). Every reduction has a fixed order (partial sums land in
+// buffers that one pass adds up in order), so a fit is reproducible bit for bit.
 //
-// Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], n = T.n[i],
-// ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 the split counts of the two value
-// products; every array starts on a 256-byte boundary):
-//   E [H][R][ldm] | PT [H][ldm][R] | Y [H][R][128] | Z [H][R][128] | Zp [S1 > 1 ? S1 : 0][H][R][128] |
-//   Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] | u [H][R] | b [H][ldm] |
-//   Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H]
-// Columns m .. ldm-1 of E hold zeros (logit -inf), so tiles never need a column bound on E.
+// Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], Rp = R and
+// ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 / S3 the split counts of the value
+// products, Np the padded rows of the iteration's side (Rp or ldm); every array starts on a
+// 256-byte boundary):
+//   P [H][R][ldm] | PT [H][ldm][Rp] | Y [H][R][128] | ZT [H][128][Rp] | VT [H][128][ldm] |
+//   Zp [S1 > 1 ? S1 : 0][H][R][128] | Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] |
+//   b [H][ldm] | Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H] | Mg [H][Np][Np] |
+//   X, Sx [H][Np][128] | XT1 [H][128][Np] | Xp [S3 > 1 ? S3 : 0][H][Np][128] |
+//   KC [H][ldk][128] bf16 (ldk = m rounded up to 256)
+// Columns m .. ldm-1 of P_C hold zeros, so tiles never need a column bound on it.
+#include <type_traits>
+
+#include "am_cfg.h"
 #include "mfma_common.h"
 
 namespace kvc {
 
 using namespace mfma;
-
-struct AmCfg {
-  int H, R, m_max, S1, S2;
-};
 
 namespace {
 
@@ -47,14 +51,27 @@ constexpr int kD = kHeadDim;
 constexpr int kRowChunk = 64;  // rows per partial column sum
 
 __host__ __device__ constexpr int64_t pad64(int64_t x) { return (x + 63) & ~int64_t(63); }
+__host__ __device__ constexpr int64_t pad256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // E / P_C [H][R][ldm], PT [H][ldm][Rp], ZT [H][128][Rp] and VT [H][128][ldm] (Rp = R rounded up
-// to 64): P_C, PT, ZT and VT are held in the split layout below.
+// to 64): P_C, PT, ZT and VT are held in the split layout below. The value iteration's side
+// (am_rows_side) has N rows (R, or m) padded to Np (Rp, or ldm): its Gram matrix Mg [H][Np][Np]
+// (split), the iterate X and its running sum Sx [H][Np][128] (float32), and a second buffer XT1
+// [H][128][Np] (split) for the iterate's transpose, which alternates with ZT (rows side) or VT
+// (keys side) from step to step so that no product rewrites the operand it reads.
 struct AmWs {
-  float *E, *PT, *Y, *ZT, *VT, *Zp, *Up, *part, *u, *b, *M, *eta, *ME;
+  float *P, *PT, *Y, *ZT, *VT, *Zp, *Up, *part, *b, *M, *eta, *ME;
+  float *Mg, *X, *Sx, *XT1, *Xp;
+  uint16_t* KC;  // the kept keys' rows, gathered: [H][ldk][128] bf16 (ldk = m rounded up to 256), zero rows from m
   uint32_t* mekey;
-  int ldm, Rp;
+  int ldm, Rp, N, Np, ldk;
+  bool rside;
 };
+// the iterate's transpose: buffer 0 (ZT or VT) or XT1 (by value, so that the workspace
+// description stays in registers)
+__device__ __forceinline__ float* am_xt(float* xt1, float* zt, float* vt, bool rside, int sel) {
+  return sel ? xt1 : (rside ? zt : vt);
+}
 
 // The split layout of a float32 matrix row: each group of 8 consecutive elements keeps its 32
 // bytes, as the 8 bfloat16 high parts followed by the 8 bfloat16 low parts (hi = bf16(x),
@@ -93,20 +110,30 @@ __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const
   AmWs w;
   w.ldm = (int)ldm;
   w.Rp = (int)Rp;
-  w.E = ws + T.off[i];
-  w.PT = w.E + pad64(H * R * ldm);
+  w.rside = am_rows_side((int)R, (int)m);
+  w.N = w.rside ? (int)R : (int)m;
+  w.Np = w.rside ? (int)Rp : (int)ldm;
+  const int64_t Np = w.Np;
+  w.P = ws + T.off[i];
+  w.PT = w.P + pad64(H * R * ldm);
   w.Y = w.PT + pad64(H * ldm * Rp);
   w.ZT = w.Y + pad64(H * R * kD);
   w.VT = w.ZT + pad64(H * kD * Rp);
   w.Zp = w.VT + pad64(H * kD * ldm);
   w.Up = w.Zp + (C.S1 > 1 ? C.S1 : 0) * pad64(H * R * kD);
   w.part = w.Up + (C.S2 > 1 ? C.S2 : 0) * pad64(H * ldm * kD);
-  w.u = w.part + pad64(H * nr * ldm);
-  w.b = w.u + pad64(H * R);
+  w.b = w.part + pad64(H * nr * ldm);
   w.M = w.b + pad64(H * ldm);
   w.eta = w.M + H;
   w.ME = w.eta + H;
   w.mekey = reinterpret_cast<uint32_t*>(w.ME + H);
+  w.Mg = w.M + pad64(4 * H);
+  w.X = w.Mg + pad64(H * Np * Np);
+  w.Sx = w.X + pad64(H * Np * kD);
+  w.XT1 = w.Sx + pad64(H * Np * kD);
+  w.Xp = w.XT1 + pad64(H * kD * Np);
+  w.ldk = (int)pad256(m);
+  w.KC = reinterpret_cast<uint16_t*>(w.Xp + (C.S3 > 1 ? C.S3 : 0) * pad64(H * Np * kD));
   return w;
 }
 
@@ -122,88 +149,19 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }  // namespace
 
 // Floats of one sequence's workspace (the layout above).
-int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2) {
+int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int S3) {
+  (void)n;
   const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk, Rp = pad64(R);
-  const int64_t rk = pad64((int64_t)H * R * kD);
+  const int64_t Np = am_rows_side(R, m) ? Rp : ldm;
+  const int64_t rk = pad64((int64_t)H * R * kD), xk = pad64((int64_t)H * Np * kD);
   return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * ldm * Rp) + rk + pad64((int64_t)H * kD * Rp) +
          pad64((int64_t)H * kD * ldm) + (S1 > 1 ? S1 : 0) * rk +
-         (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) + pad64((int64_t)H * R) +
-         pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H);
+         (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) +
+         pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H) + pad64((int64_t)H * Np * Np) + 3 * xk +
+         (S3 > 1 ? S3 : 0) * xk + pad64((int64_t)H * pad256(m) * (kD / 2));
 }
 
-// ------------------------------------------------------------------------------------------------
-// Kept-logit tiles of 64 rows x 64 kept keys into E: the raw logits c q_i . k_Cj, -inf in the
-// padding columns; their maximum goes to an atomic per unit, and am_scale turns them into
-// exponentials. Work item = (seq, head, row tile, key tile), key tile fastest. Both operands
-// come straight from global memory (L2-resident).
-// ------------------------------------------------------------------------------------------------
-template <int LAYOUT>
-__global__ __launch_bounds__(kThreads) void am_exp(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                   const int32_t* __restrict__ table, int max_blocks,
-                                                   const int32_t* __restrict__ kept, float* __restrict__ ws,
-                                                   int64_t n_max, float scale, AmCfg C, SeqTable T) {
-  const int t = blockIdx.x;
-  const int i = find_seq(T, t);
-  const int n = T.n[i], m = T.m[i];
-  const int H = C.H, R = C.R;
-  AmWs W = am_ws(ws, T, i, C);
-  const int ld = W.ldm;
-  const int s = T.first + i;
-  const int rt_n = (R + 63) / 64, ct_n = (m + 63) / 64;
-  int local = t - T.start[i];
-  const int h = local / (rt_n * ct_n);
-  local -= h * rt_n * ct_n;
-  const int rt = local / ct_n, ct = local - rt * ct_n;
-  const int64_t unit = (int64_t)s * H + h;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
-  const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
-                                        : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
-
-  const int row = rt * 64 + wave * 16 + c16;  // A operand row of this lane
-  bf16x8 qa[4];
-  const uint16_t* qrow = q + (unit * R + min(row, R - 1)) * (int64_t)kD;
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8(reinterpret_cast<const u32x4*>(qrow)[4 * ks + g]);
-  float* out = W.E + ((int64_t)h * R) * ld;
-  const int32_t* ku = kept + unit * C.m_max;
-  float lmax = -INFINITY;
-#pragma unroll 1
-  for (int sub = 0; sub < 4; ++sub) {
-    const int col = ct * 64 + sub * 16 + c16;  // B operand key of this lane
-    const int key = min(max(ku[min(col, m - 1)], 0), n - 1);
-    const u32x4* kr = key_row<LAYOUT>(k, map, H, h, n_max, unit, T.kofs[i] + key);
-    f32x4 acc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], as_bf16x8(kr[4 * ks + g]), acc);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int orow = rt * 64 + wave * 16 + 4 * g + e;
-      if (orow < R && col < ld) {
-        const float l = acc[e] * scale;
-        if (col < m) {
-          out[(int64_t)orow * ld + col] = l;
-          lmax = fmaxf(lmax, l);
-        } else {
-          out[(int64_t)orow * ld + col] = -INFINITY;
-        }
-      }
-    }
-  }
-  // one atomic per workgroup at most: the four wave maxima meet in LDS, and the unit's running
-  // maximum is read first (it only grows, so a stale read costs at most a redundant atomic)
-  __shared__ float wmax[4];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
-  if (lane == 0) wmax[wave] = lmax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float bm = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const uint32_t key = float_key(bm);
-    if (bm > -INFINITY && key > __atomic_load_n(W.mekey + h, __ATOMIC_RELAXED)) atomicMax(W.mekey + h, key);
-  }
-}
-
-// Per unit, before am_exp: Mz = max_i LSE_i, and the kept-logit maximum reset. Work item = (seq, head).
+// Per unit, first: Mz = max_i LSE_i, and the kept-logit maximum reset. Work item = (seq, head).
 __global__ __launch_bounds__(64) void am_stats(const float* __restrict__ lse, float* __restrict__ ws, AmCfg C,
                                                SeqTable T) {
   const int t = blockIdx.x;
@@ -221,130 +179,27 @@ __global__ __launch_bounds__(64) void am_stats(const float* __restrict__ lse, fl
   }
 }
 
-// E <- exp(E - ME), ME the unit's largest kept logit; Mz lowered to ME + 80 when the kept keys
-// lie far below the largest LSE (so that exp(ME - Mz), the start of w', stays in range).
-// Work item = (seq, head, 4096 elements).
-__global__ __launch_bounds__(256) void am_scale(float* __restrict__ ws, AmCfg C, SeqTable T) {
+// Per unit, after the kept-logit maximum: ME, and Mz lowered to ME + 80 when the kept keys lie
+// far below the largest LSE (so that exp(ME - Mz), the start of w', stays in range).
+// Work item = (seq, head).
+__global__ __launch_bounds__(64) void am_me(float* __restrict__ ws, AmCfg C, SeqTable T) {
   const int t = blockIdx.x;
   const int i = find_seq(T, t);
+  const int h = t - T.start[i];
   AmWs W = am_ws(ws, T, i, C);
-  const int64_t per = (int64_t)C.R * W.ldm;
-  const int nb = (int)((per + 4095) / 4096);
-  const int local = t - T.start[i];
-  const int h = local / nb, blk = local - h * nb;
-  const float me = key_float(W.mekey[h]);
-  if (blk == 0 && threadIdx.x == 0) {
+  if (threadIdx.x == 0) {
+    const float me = key_float(W.mekey[h]);
     W.ME[h] = me;
     W.M[h] = fminf(W.M[h], me + 80.0f);
   }
-  float* e = W.E + (int64_t)h * per;
-  for (int64_t x = (int64_t)blk * 4096 + threadIdx.x; x < min(per, (int64_t)(blk + 1) * 4096); x += 256)
-    e[x] = __builtin_amdgcn_exp2f((e[x] - me) * kLog2e);
 }
 
 // ------------------------------------------------------------------------------------------------
-// u = E w per row (one wave per row). Work item = (seq, head, 4 rows).
+// Column sums g_j = sum_i part_ij over the 64-row tiles, in tile order, then per kept key:
+//   MODE 0: b_j = g_j (E^T z once; or the column sums of P_C, for the step size)
+//   MODE 1: w_j <- w_j b_j / g_j, 0 if g_j = 0 (one NNLS step)
+// Work item = (seq, head, 256 kept keys).
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void am_rows_dot(const float* __restrict__ w_all, float* __restrict__ ws, AmCfg C,
-                                                   SeqTable T) {
-  const int t = blockIdx.x;
-  const int i = find_seq(T, t);
-  const int m = T.m[i], s = T.first + i;
-  const int R = C.R;
-  const int rb = (R + 3) / 4;
-  const int local = t - T.start[i];
-  const int h = local / rb;
-  const int r = (local - h * rb) * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (r >= R) return;
-  AmWs W = am_ws(ws, T, i, C);
-  const float* e = W.E + ((int64_t)h * R + r) * W.ldm;
-  const float* w = w_all + ((int64_t)s * C.H + h) * C.m_max;
-  float acc = 0.0f;
-  for (int j = lane; j < m; j += 64) acc = __builtin_fmaf(e[j], w[j], acc);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
-  if (lane == 0) W.u[(int64_t)h * R + r] = acc;
-}
-
-// ------------------------------------------------------------------------------------------------
-// Column products g_j = sum_i E_ij r_i in two passes: partial sums over chunks of 64 rows (one
-// thread per column, rows in order), then the chunks added in order per column. With
-//   MODE 0: r_i = exp(LSE_i - M)       -> b_j = g_j                          (E^T z, once)
-//   MODE 1: r_i = u_i = (E w)_i        -> w_j <- w_j b_j / g_j, 0 if g_j = 0 (one NNLS step)
-//   MODE 2: r_i = 1 / u_i              -> E_ij <- E_ij w_j / u_i in place (E becomes P_C),
-//                                         b_j = sum_i (P_C)_ij (column sums, for the step size),
-//                                         and P_C^T written to PT
-// Partial work item = (seq, head, 256 columns, 64-row chunk); final = (seq, head, 256 columns).
-// ------------------------------------------------------------------------------------------------
-template <int MODE>
-__global__ __launch_bounds__(256) void am_cols_part(const float* __restrict__ w_all, const float* __restrict__ lse,
-                                                    float* __restrict__ ws, AmCfg C, SeqTable T) {
-  const int t = blockIdx.x;
-  const int i = find_seq(T, t);
-  const int m = T.m[i], s = T.first + i;
-  const int R = C.R;
-  AmWs W = am_ws(ws, T, i, C);
-  const int ldm = W.ldm;
-  const int cb_n = (ldm + 255) / 256, nr = (R + kRowChunk - 1) / kRowChunk;
-  int local = t - T.start[i];
-  const int rc = local % nr;
-  local /= nr;
-  const int cb = local % cb_n, h = local / cb_n;
-  const int j = cb * 256 + threadIdx.x;
-  const int64_t unit = (int64_t)s * C.H + h;
-  const int r0 = rc * kRowChunk, r1 = min(R, r0 + kRowChunk);
-  if constexpr (MODE == 2) {
-    // P_C in place of E and P_C^T (row j of PT holds column j), both in the split layout, and
-    // the column sums of P_C. The chunk's 64 x 256 block of P_C is staged in LDS (row pitch 257:
-    // a column read is conflict-free); after the barrier every float of the block has been read,
-    // so the block is rewritten in place, 8 consecutive columns of a row per group, and PT gets
-    // 8 consecutive rows of a column per group (zeros for the rows past R up to Rp).
-    __shared__ float tile[kRowChunk][257];
-    float acc = 0.0f;
-    float* E = W.E + (int64_t)h * R * ldm;
-    if (j < ldm) {
-      const float* u = W.u + (int64_t)h * R;
-      const float wj = j < m ? w_all[unit * C.m_max + j] : 0.0f;
-      for (int r = r0; r < r1; ++r) {
-        const float x = E[(int64_t)r * ldm + j];
-        const float pc = u[r] > 0.0f ? x * wj / u[r] : 0.0f;
-        tile[r - r0][threadIdx.x] = pc;
-        acc += pc;
-      }
-      W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
-    }
-    __syncthreads();
-    const int cols = min(256, ldm - cb * 256);  // a multiple of 64
-    for (int q = threadIdx.x; q < kRowChunk * 32; q += 256) {
-      const int rr = q >> 5, gq = q & 31;
-      if (r0 + rr < r1 && 8 * gq < cols) put_split8(E + (int64_t)(r0 + rr) * ldm + cb * 256, gq, &tile[rr][8 * gq]);
-    }
-    const int Rp = W.Rp;
-    for (int q = threadIdx.x; q < 256 * (kRowChunk / 8); q += 256) {
-      const int c = q >> 3, gq = q & 7;
-      if (c >= cols) continue;
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = r0 + 8 * gq + e < r1 ? tile[8 * gq + e][c] : 0.0f;
-      put_split8(W.PT + ((int64_t)h * ldm + cb * 256 + c) * Rp + r0, gq, x);
-    }
-  } else {
-    if (j >= ldm) return;
-    const float* e = W.E + (int64_t)h * R * ldm + j;
-    const float* u = W.u + (int64_t)h * R;
-    const float* lu = lse + unit * R;
-    const float M = W.M[h];
-    float acc = 0.0f;
-    for (int r = r0; r < r1; ++r) {
-      const float x = e[(int64_t)r * ldm];
-      if constexpr (MODE == 0) acc = __builtin_fmaf(x, __builtin_amdgcn_exp2f((lu[r] - M) * kLog2e), acc);
-      else acc = __builtin_fmaf(x, u[r], acc);
-    }
-    W.part[((int64_t)h * nr + rc) * ldm + j] = acc;
-  }
-}
-
 template <int MODE>
 __global__ __launch_bounds__(256) void am_cols_fin(float* __restrict__ w_all, float* __restrict__ ws, AmCfg C,
                                                    SeqTable T) {
@@ -360,7 +215,15 @@ __global__ __launch_bounds__(256) void am_cols_fin(float* __restrict__ w_all, fl
   if (j >= m) return;
   const float* p = W.part + (int64_t)h * nr * ldm + j;
   float g = 0.0f;
-  for (int rc = 0; rc < nr; ++rc) g += p[(int64_t)rc * ldm];
+  int rc = 0;
+  for (; rc + 8 <= nr; rc += 8) {  // eight loads in flight, added in order
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = p[(int64_t)(rc + k) * ldm];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g += x[k];
+  }
+  for (; rc < nr; ++rc) g += p[(int64_t)rc * ldm];
   float* b = W.b + (int64_t)h * ldm + j;
   if constexpr (MODE == 1) {
     float* w = w_all + ((int64_t)s * C.H + h) * C.m_max + j;
@@ -387,6 +250,416 @@ __global__ __launch_bounds__(256) void am_eta(float* __restrict__ ws, AmCfg C, S
   if (threadIdx.x == 0) {
     const float c = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     W.eta[h] = c > 0.0f ? 1.0f / c : 0.0f;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// The kept keys' rows gathered into KC (zero rows from m up to ldk), the operand from which the
+// bias updates re-form E. Work item = (seq, head, 64 rows of KC).
+// ------------------------------------------------------------------------------------------------
+template <int LAYOUT>
+__global__ __launch_bounds__(256) void am_gather(const uint16_t* __restrict__ k, const int32_t* __restrict__ table,
+                                                 int max_blocks, const int32_t* __restrict__ kept,
+                                                 float* __restrict__ ws, int64_t n_max, AmCfg C, SeqTable T) {
+  const int t = blockIdx.x;
+  const int i = find_seq(T, t);
+  const int m = T.m[i], n = T.n[i], s = T.first + i;
+  AmWs W = am_ws(ws, T, i, C);
+  const int nb = W.ldk / 64;
+  const int local = t - T.start[i];
+  const int h = local / nb, blk = local - h * nb;
+  const int64_t unit = (int64_t)s * C.H + h;
+  const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
+                                        : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
+  u32x4* dst = reinterpret_cast<u32x4*>(W.KC + ((int64_t)h * W.ldk + blk * 64) * kD);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int q = x * 256 + threadIdx.x, j = blk * 64 + (q >> 4), ch = q & 15;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (j < m) {
+      const int key = min(max(kept[unit * C.m_max + j], 0), n - 1);
+      v = key_row<LAYOUT>(k, map, C.H, h, n_max, unit, T.kofs[i] + key)[ch];
+    }
+    dst[q] = v;
+  }
+}
+
+// ------------------------------------------------------------------------------------------------
+// Everything the fit needs from E_ij = exp(c q_i . k_Cj - ME), re-formed on the MFMA units from the
+// bf16 rows of Q and KC instead of kept in memory, per 64-row tile:
+//   MODE 3: the kept logits' maximum ME (one atomic per workgroup)
+//   MODE 0: b_j = sum_i E_ij z_i, z_i = exp(LSE_i - Mz)               (column partials)
+//   MODE 1: u_i = sum_j E_ij w_j, then the column partials of E^T u      (one NNLS update)
+//   MODE 2: u_i as in MODE 1, then P_C = E_ij w_j / u_i written as split rows of P_C and of
+//           P_C^T (zeros past R and past m), with the column partials of P_C
+// Column partials land one per 64-row tile and kept key, the layout am_cols_fin reads (it adds
+// them in order and applies the update).
+// Work item = (seq, head, 64-row tile); eight waves, two per SIMD: wave w holds rows
+// 32 (w & 1) .. + 31 of the tile (two 16-row fragments of Q in registers) and takes key tiles
+// 4 st + (w >> 1) of KC. Each step stages four consecutive 64-key tiles (64 KB, rows swizzled as in
+// the score kernels) and their w through double-buffered LDS. Per 16-key slice a B fragment
+// serves both row fragments. The row sums meet across the four key quarters in LDS, in order; a
+// key's column partial is reduced over the wave's lane groups, then over the two waves of its
+// quarter through LDS (even wave first).
+// ------------------------------------------------------------------------------------------------
+namespace {
+constexpr int kBiasThreads = 512;
+constexpr int kBiasStep = 256;  // kept keys per step (KC rows are padded to a multiple)
+}  // namespace
+
+template <int MODE>
+__global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restrict__ q,
+                                                        const float* __restrict__ w_all,
+                                                        const float* __restrict__ lse, float* __restrict__ ws,
+                                                        float scale, AmCfg C, SeqTable T) {
+  constexpr bool kW = MODE == 1 || MODE == 2;  // the pass needs w
+  __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBiasStep * 256];
+  __shared__ float ws_l[2][kBiasStep];
+  __shared__ float rsum[4][64];          // row sums of the four key quarters
+  __shared__ float xpart[2][kBiasStep];  // column partials of the odd waves, per step parity
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = find_seq(T, t);
+  const int m = T.m[i], s = T.first + i;
+  const int H = C.H, R = C.R;
+  const int rt_n = (R + 63) / 64;
+  const int local = t - T.start[i];
+  const int h = local / rt_n, rt = local - h * rt_n;
+  const int64_t unit = (int64_t)s * H + h;
+  AmWs W = am_ws(ws, T, i, C);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int rb = 32 * (wave & 1), kq = wave >> 1;
+  const float cl = scale * kLog2e, mb = MODE == 3 ? 0.0f : W.ME[h] * kLog2e;
+  const float* wu = w_all + unit * C.m_max;
+  const u32x4* kc = reinterpret_cast<const u32x4*>(W.KC + (int64_t)h * W.ldk * kD);
+  const int nsteps = W.ldk / kBiasStep;
+
+  bf16x8 qa[2][4];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg) {
+    const int row = min(rt * 64 + rb + 16 * rg + c16, R - 1);
+    const u32x4* qr = reinterpret_cast<const u32x4*>(q + (unit * R + row) * (int64_t)kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qa[rg][ks] = as_bf16x8(qr[4 * ks + g]);
+  }
+
+  // staging of step st: key rows 256 st .. + 255, 8 pieces of 16 bytes per thread
+  u32x4 kr[8];
+  float wr = 0.0f;
+  auto load = [&](int st) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) kr[x] = kc[(int64_t)st * kBiasStep * 16 + x * kBiasThreads + tid];
+    if (kW && tid < kBiasStep) {
+      const int j = st * kBiasStep + tid;
+      wr = j < m ? wu[j] : 0.0f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int q16 = x * kBiasThreads + tid;
+      *reinterpret_cast<u32x4*>(&Ks[buf][swz(q16 >> 4, q16 & 15)]) = kr[x];
+    }
+    if (kW && tid < kBiasStep) ws_l[buf][tid] = wr;
+  };
+  // The kept-logit MFMAs of a step (this wave's 32 rows x its 64-key tile of buffer buf;
+  // acc[sub][rg] holds rows rb + 16 rg + 4 g + x, key 256 st + 64 kq + 16 sub + c16, and wv[sub]
+  // that key's w). The update passes are software-pipelined: a step's MFMAs run while the
+  // previous step's exponentials and sums are formed from registers, so the two waves of a SIMD,
+  // which the step barrier keeps in phase, still overlap their MFMAs with vector work.
+  auto mma = [&](int buf, f32x4 (&acc)[4][2], float (&wv)[4]) {
+    const uint8_t* kb = Ks[buf];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) acc[sub][0] = acc[sub][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&kb[swz(64 * kq + 16 * sub + c16, 4 * ks + g)]);
+        acc[sub][0] = mfma16(qa[0][ks], b, acc[sub][0]);
+        acc[sub][1] = mfma16(qa[1][ks], b, acc[sub][1]);
+      }
+    if constexpr (kW) {
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) wv[sub] = ws_l[buf][64 * kq + 16 * sub + c16];
+    }
+  };
+  // E = exp(c q.k - ME) of a step's accumulators, 0 past m when the step reaches it
+  auto expo = [&](int st, const f32x4 (&acc)[4][2], float (&e)[4][2][4]) {
+    const bool tail = (st + 1) * kBiasStep > m;
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      const bool live = st * kBiasStep + 64 * kq + 16 * sub + c16 < m;
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[sub][rg][x], cl, -mb));
+          e[sub][rg][x] = (tail && !live) ? 0.0f : v;
+        }
+    }
+  };
+  auto interleave = [] {
+    // one MFMA, then three vector instructions, for the 32 MFMAs of a step
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+    }
+  };
+  // column partial over the lane's 8 rows of each slice (weights rw), reduced over the four lane
+  // groups (rows 4g ..): lane group g ends with slice sub = g, i.e. key 64 kq + 16 g + c16 of the
+  // step, summed over the wave's 32 rows
+  auto colsum = [&](const float (&e)[4][2][4], const float (&rw)[2][4]) {
+    float gp[4];
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) {
+      float a = 0.0f;
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) a = __builtin_fmaf(e[sub][rg][x], rw[rg][x], a);
+      gp[sub] = a;
+    }
+    const bool hi32 = g >= 2;
+    const float s0 = hi32 ? gp[0] : gp[2], s1 = hi32 ? gp[1] : gp[3];
+    const float r0 = __shfl_xor(s0, 32), r1 = __shfl_xor(s1, 32);
+    const float k0 = (hi32 ? gp[2] : gp[0]) + r0, k1 = (hi32 ? gp[3] : gp[1]) + r1;
+    const bool odd = g & 1;
+    const float rcv = __shfl_xor(odd ? k0 : k1, 16);
+    return (odd ? k1 : k0) + rcv;
+  };
+  float* part = W.part + ((int64_t)h * rt_n + rt) * W.ldm;
+  f32x4 acc0[4][2], acc1[4][2];
+  float wv0[4], wv1[4];
+
+  if constexpr (MODE == 3) {
+    // the largest kept logit c q_i . k_Cj over the tile's rows and the live keys
+    float lmax = -INFINITY;
+    load(0);
+    store(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int st = 0; st < nsteps; ++st) {
+      const bool more = st + 1 < nsteps;
+      if (more) load(st + 1);
+      mma(st & 1, acc0, wv0);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        const bool live = st * kBiasStep + 64 * kq + 16 * sub + c16 < m;
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int x = 0; x < 4; ++x)
+            if (live) lmax = fmaxf(lmax, acc0[sub][rg][x] * scale);
+      }
+      if (more) store((st + 1) & 1);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
+    if (lane == 0) xpart[0][wave] = lmax;
+    __syncthreads();
+    if (tid == 0) {
+      float bm = xpart[0][0];
+      for (int x = 1; x < kBiasThreads / 64; ++x) bm = fmaxf(bm, xpart[0][x]);
+      const uint32_t key = float_key(bm);
+      if (bm > -INFINITY && key > __atomic_load_n(W.mekey + h, __ATOMIC_RELAXED)) atomicMax(W.mekey + h, key);
+    }
+    return;
+  }
+
+  float rv[2][4];  // the row weights of the lane's rows for the column pass
+  if constexpr (kW) {
+    // pass A: u_i = sum_j E_ij w_j
+    float up[2][4] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    auto post = [&](int st, const f32x4 (&acc)[4][2], const float (&wv)[4]) {
+      float e[4][2][4];
+      expo(st, acc, e);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) up[rg][x] = __builtin_fmaf(e[sub][rg][x], wv[sub], up[rg][x]);
+    };
+    // step st: loads of st + 1 in flight, MFMAs of st, sums of st - 1, then st + 1 staged
+    auto step = [&](int st, f32x4 (&cur)[4][2], float (&wc)[4], f32x4 (&prev)[4][2], float (&wp)[4]) {
+      const bool more = st + 1 < nsteps;
+      if (more) load(st + 1);
+      mma(st & 1, cur, wc);
+      if (st > 0) {
+        post(st - 1, prev, wp);
+        interleave();
+      }
+      if (more) store((st + 1) & 1);
+      __syncthreads();
+    };
+    load(0);
+    store(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int st = 0; st < nsteps; st += 2) {
+      step(st, acc0, wv0, acc1, wv1);
+      if (st + 1 < nsteps) step(st + 1, acc1, wv1, acc0, wv0);
+    }
+    if (nsteps & 1) post(nsteps - 1, acc0, wv0);
+    else post(nsteps - 1, acc1, wv1);
+    // reduce over the 16 keys of each lane row (c16), then add the four key quarters in order
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        float v = up[rg][x];
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o);
+        up[rg][x] = v;
+      }
+    if (c16 == 0) {
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) rsum[kq][rb + 16 * rg + 4 * g + x] = up[rg][x];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = rb + 16 * rg + 4 * g + x;
+        const float u = ((rsum[0][r] + rsum[1][r]) + rsum[2][r]) + rsum[3][r];
+        // MODE 1 weighs the column pass by u; MODE 2 forms P_C = E w / u
+        rv[rg][x] = rt * 64 + r < R ? (MODE == 1 ? u : (u > 0.0f ? 1.0f / u : 0.0f)) : 0.0f;
+      }
+  } else {
+    const float* lu = lse + unit * R;
+    const float Mz = W.M[h];
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int r = rt * 64 + rb + 16 * rg + 4 * g + x;
+        rv[rg][x] = r < R ? __builtin_amdgcn_exp2f((lu[r] - Mz) * kLog2e) : 0.0f;
+      }
+  }
+
+  if constexpr (MODE == 2) {
+    // pass C, one step at a time: P_C of the tile's 64 rows x 256 keys, its column partials, then
+    // the tile through LDS (in place of the step's keys once every wave has used them; row r at
+    // float r * 256 + (key ^ 16 ((r >> 2) & 3)), so the lane groups' rows spread over the banks)
+    // and out as split rows of P_C (8 keys per group) and of P_C^T (8 rows per group)
+    float* Pu = W.P + (int64_t)h * R * W.ldm;
+    float* PTu = W.PT + (int64_t)h * W.ldm * W.Rp;
+    load(0);
+    store(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int st = 0; st < nsteps; ++st) {
+      const int buf = st & 1;
+      const bool more = st + 1 < nsteps;
+      if (more) load(st + 1);
+      mma(buf, acc0, wv0);
+      float e[4][2][4];
+      expo(st, acc0, e);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) e[sub][rg][x] = e[sub][rg][x] * wv0[sub] * rv[rg][x];
+      const float ones[2][4] = {{1.0f, 1.0f, 1.0f, 1.0f}, {1.0f, 1.0f, 1.0f, 1.0f}};
+      const float gsum = colsum(e, ones);
+      if (wave & 1) xpart[buf][64 * kq + lane] = gsum;
+      __syncthreads();  // every wave is done with the step's keys
+      if (!(wave & 1)) {
+        const int j = st * kBiasStep + 64 * kq + lane;
+        if (j < W.ldm) part[j] = gsum + xpart[buf][64 * kq + lane];
+      }
+      float* pl = reinterpret_cast<float*>(Ks[buf]);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub)
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int r = rb + 16 * rg + 4 * g + x, key = 64 * kq + 16 * sub + c16;
+            pl[r * kBiasStep + (key ^ (16 * ((r >> 2) & 3)))] = e[sub][rg][x];
+          }
+      __syncthreads();
+      for (int qq = tid; qq < 64 * (kBiasStep / 8); qq += kBiasThreads) {  // rows of P_C
+        const int r = qq >> 5, gq = qq & 31;
+        const int row = rt * 64 + r, col = st * kBiasStep + 8 * gq;
+        if (row < R && col < W.ldm) {
+          float x[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = pl[r * kBiasStep + ((8 * gq + k) ^ (16 * ((r >> 2) & 3)))];
+          put_split8(Pu + (int64_t)row * W.ldm + st * kBiasStep, gq, x);
+        }
+      }
+      for (int qq = tid; qq < kBiasStep * 8; qq += kBiasThreads) {  // rows of P_C^T
+        const int c = qq >> 3, gq = qq & 7;
+        const int key = st * kBiasStep + c;
+        if (key < W.ldm) {
+          float x[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int r = 8 * gq + k;
+            x[k] = pl[r * kBiasStep + (c ^ (16 * ((r >> 2) & 3)))];
+          }
+          put_split8(PTu + (int64_t)key * W.Rp + rt * 64, gq, x);
+        }
+      }
+      __syncthreads();  // the tile is out before the buffer is staged again
+      if (more) store(buf ^ 1);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // pass B: column partials sum_i E_ij r_i over the tile's 64 rows. A step's partial (lane
+  // (g, c16): the wave's 32 rows at key 256 st + 64 kq + 16 g + c16) is formed in the next step;
+  // the odd waves leave theirs in LDS, and after that step's barrier the even waves add them
+  // (even first) and write the tile's partial.
+  auto column = [&](int st, const f32x4 (&acc)[4][2]) {
+    float e[4][2][4];
+    expo(st, acc, e);
+    return colsum(e, rv);
+  };
+  float gkeep = 0.0f;  // an even wave's own partial of the previous step
+  auto flush = [&](int st) {  // the tile's partial of step st (even waves, after the barrier)
+    if (!(wave & 1)) {
+      const int j = st * kBiasStep + 64 * kq + lane;
+      if (j < W.ldm) part[j] = gkeep + xpart[st & 1][64 * kq + lane];
+    }
+  };
+  auto stepB = [&](int st, f32x4 (&cur)[4][2], float (&wc)[4], f32x4 (&prev)[4][2]) {
+    const bool more = st + 1 < nsteps;
+    if (more) load(st + 1);
+    mma(st & 1, cur, wc);
+    if (st > 1) flush(st - 2);
+    if (st > 0) {
+      const float gs = column(st - 1, prev);
+      interleave();
+      if (wave & 1) xpart[(st - 1) & 1][64 * kq + lane] = gs;
+      else gkeep = gs;
+    }
+    if (more) store((st + 1) & 1);
+    __syncthreads();
+  };
+  load(0);
+  store(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int st = 0; st < nsteps; st += 2) {
+    stepB(st, acc0, wv0, acc1);
+    if (st + 1 < nsteps) stepB(st + 1, acc1, wv1, acc0);
+  }
+  if (nsteps > 1) flush(nsteps - 2);
+  {
+    const float gs = (nsteps & 1) ? column(nsteps - 1, acc0) : column(nsteps - 1, acc1);
+    if (wave & 1) xpart[(nsteps - 1) & 1][64 * kq + lane] = gs;
+    else gkeep = gs;
+    __syncthreads();
+    flush(nsteps - 1);
   }
 }
 
@@ -532,12 +805,10 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 }
 
 // ------------------------------------------------------------------------------------------------
-// The two products of a Landweber step, one 128 x 128 output tile per workgroup (four waves in a
-// 2 x 2 grid, each 64 x 64: sixteen 16 x 16 accumulators), the contraction in stages of 32
-// through double-buffered LDS with the next stage's global loads in flight during the current
-// stage's MFMAs, and split over S workgroups whose partial tiles a second pass adds in order:
-//   KIND 0: Z = P_C Vc - Y          (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
-//   KIND 1: Vc -= eta P_C^T Z        (columns of P_C, contraction over rows)    -> Vc, or partials Up
+// The value fit's matrix products, one 128 x 128 output tile per workgroup (four waves in a 2 x 2
+// grid, each 64 x 64: sixteen 16 x 16 accumulators), the contraction in stages of 32 through
+// double-buffered LDS with the next stage's global loads in flight during the current stage's
+// MFMAs. Both operands are read by rows along the contraction: out = A B^T.
 // The float32 operands are stored split (x = hi + lo with hi = bf16(x) and lo = bf16(x - hi),
 // the layout of put_split8), and a product is taken as hi_a hi_b + hi_a lo_b + lo_a hi_b on
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation (the dropped lo_a lo_b and the rounding of
@@ -547,56 +818,32 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 // 16-byte chunk c of row r sits at chunk position c ^ ((r >> 1) & 3), so each MFMA operand read
 // (chunk g of 16 consecutive rows) is free of bank conflicts. Lane group g of an MFMA supplies
 // contraction indices 8g .. 8g + 7 on both operands.
-// Work item = (seq, head, output tile, split), split fastest.
 // ------------------------------------------------------------------------------------------------
 namespace {
 constexpr int kGTile = 128;
+constexpr int kGLds = 4 * 2 * kGTile * 64;  // bytes: hi and lo of both operands, double-buffered
 
 __device__ __forceinline__ int gswz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
-}  // namespace
 
-template <int KIND>
-__global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
-                                                  SeqTable T) {
-  __shared__ __attribute__((aligned(16))) uint8_t Ah[2][kGTile * 64], Al[2][kGTile * 64];
-  __shared__ __attribute__((aligned(16))) uint8_t Bh[2][kGTile * 64], Bl[2][kGTile * 64];
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
-  const int i = find_seq(T, t);
-  const int m = T.m[i], s = T.first + i;
-  const int R = C.R;
-  AmWs W = am_ws(ws, T, i, C);
-  const int ldm = W.ldm;
-  const int S = KIND == 0 ? C.S1 : C.S2;
-  const int rows = KIND == 0 ? R : ldm;  // output rows
-  const int tiles = (rows + kGTile - 1) / kGTile;
-  int local = t - T.start[i];
-  const int sp = local % S;
-  local /= S;
-  const int tile = local % tiles, h = local / tiles;
-  const int64_t unit = (int64_t)s * C.H + h;
-  const float* PC = W.E + (int64_t)h * R * ldm;           // split rows of P_C
-  const float* PTh = W.PT + (int64_t)h * ldm * W.Rp;      // split rows of P_C^T
-  const float* VTh = W.VT + (int64_t)h * kD * ldm;        // split rows of Vc^T
-  const float* ZTh = W.ZT + (int64_t)h * kD * W.Rp;       // split rows of Z^T
-  const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
-  const int per = (nst + S - 1) / S;
-  const int st0 = sp * per, st1 = min(nst, st0 + per);
+// acc += A B^T over contraction stages st0 .. st1 - 1 (32 indices each) of one 128 x 128 tile.
+// arow / brow: the split rows of A and B that this thread stages (row tid >> 1 of A, indices
+// 16 (tid & 1) .. + 15 of each stage; row tid & 127 of B, indices 16 (tid >> 7) .. + 15); a row
+// that is not alive is staged as zeros. Every operand is stored split, so a thread's 16 indices
+// are 64 contiguous bytes: high parts of the first 8, their low parts, then the same for the
+// next 8, copied to the high and low LDS tiles unchanged.
+__device__ __forceinline__ void tile_mma(const float* arow, bool alive_a, const float* brow, bool alive_b, int st0,
+                                         int st1, f32x4 (&acc)[4][4], uint8_t* sm) {
+  uint8_t* Ah = sm;
+  uint8_t* Al = sm + 2 * kGTile * 64;
+  uint8_t* Bh = sm + 4 * kGTile * 64;
+  uint8_t* Bl = sm + 6 * kGTile * 64;
+  constexpr int kBuf = kGTile * 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int wr = wave >> 1, wc = wave & 1;
-
-  // staging: A row ar of the tile, contraction indices 16 ak .. + 15; B column bd, indices
-  // 16 bk .. + 15 (chunks 2 ak, 2 ak + 1 and 2 bk, 2 bk + 1). Every operand is stored split, so
-  // a thread's 16 indices are 64 contiguous bytes: high parts of the first 8, their low parts,
-  // then the same for the next 8, copied to the high and low LDS tiles unchanged. The
-  // contraction never leaves the stored rows (ldm and Rp are multiples of 64).
   const int ar = tid >> 1, ak = tid & 1;
   const int bd = tid & 127, bk = tid >> 7;
-  const int arow = tile * kGTile + ar;                    // A row: output row of the tile
-  const bool alive = arow < (KIND == 0 ? R : ldm);
-  const u32x4* asrc = reinterpret_cast<const u32x4*>(
-      KIND == 0 ? PC + (int64_t)min(arow, R - 1) * ldm + 16 * ak : PTh + (int64_t)min(arow, ldm - 1) * W.Rp + 16 * ak);
-  const u32x4* bsrc = reinterpret_cast<const u32x4*>(KIND == 0 ? VTh + (int64_t)bd * ldm + 16 * bk
-                                                               : ZTh + (int64_t)bd * W.Rp + 16 * bk);
+  const u32x4* asrc = reinterpret_cast<const u32x4*>(arow + 16 * ak);
+  const u32x4* bsrc = reinterpret_cast<const u32x4*>(brow + 16 * bk);
   u32x4 ra[4], rb[4];
   auto load = [&](int stg) {
     const int o = stg * 8;  // 32 indices = 8 u32x4 per row
@@ -605,59 +852,110 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
       ra[c] = asrc[o + c];
       rb[c] = bsrc[o + c];
     }
-    if (!alive) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) ra[c] = u32x4{0u, 0u, 0u, 0u};
-    }
   };
   auto store = [&](int buf) {
+    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      *reinterpret_cast<u32x4*>(&Ah[buf][gswz(ar, 2 * ak + c)]) = ra[2 * c];
-      *reinterpret_cast<u32x4*>(&Al[buf][gswz(ar, 2 * ak + c)]) = ra[2 * c + 1];
-      *reinterpret_cast<u32x4*>(&Bh[buf][gswz(bd, 2 * bk + c)]) = rb[2 * c];
-      *reinterpret_cast<u32x4*>(&Bl[buf][gswz(bd, 2 * bk + c)]) = rb[2 * c + 1];
+      *reinterpret_cast<u32x4*>(&Ah[buf * kBuf + gswz(ar, 2 * ak + c)]) = alive_a ? ra[2 * c] : z;
+      *reinterpret_cast<u32x4*>(&Al[buf * kBuf + gswz(ar, 2 * ak + c)]) = alive_a ? ra[2 * c + 1] : z;
+      *reinterpret_cast<u32x4*>(&Bh[buf * kBuf + gswz(bd, 2 * bk + c)]) = alive_b ? rb[2 * c] : z;
+      *reinterpret_cast<u32x4*>(&Bl[buf * kBuf + gswz(bd, 2 * bk + c)]) = alive_b ? rb[2 * c + 1] : z;
     }
   };
+  if (st0 >= st1) return;
+  load(st0);
+  store(0);
+  __syncthreads();
+#pragma unroll 1
+  for (int stg = st0; stg < st1; ++stg) {
+    const int buf = (stg - st0) & 1;
+    const bool more = stg + 1 < st1;
+    if (more) load(stg + 1);
+    bf16x8 bh[4], bl[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int o = buf * kBuf + gswz(64 * wc + 16 * b + c16, g);
+      bh[b] = *reinterpret_cast<const bf16x8*>(&Bh[o]);
+      bl[b] = *reinterpret_cast<const bf16x8*>(&Bl[o]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int o = buf * kBuf + gswz(64 * wr + 16 * a + c16, g);
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[o]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[o]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        acc[a][b] = mfma16(ah, bh[b], acc[a][b]);
+        acc[a][b] = mfma16(ah, bl[b], acc[a][b]);
+        acc[a][b] = mfma16(al, bh[b], acc[a][b]);
+      }
+    }
+    if (more) store(buf ^ 1);
+    __syncthreads();
+  }
+}
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------
+// The products of the value fit, split over S workgroups along the contraction whose partial
+// tiles a second pass (am_split_sum) adds in order:
+//   KIND 0: Z = P_C V0 - Y           (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
+//           (rows side: also the iterate X = Z and its sum Sx = Z)
+//   KIND 1: P_C^T T                  (columns of P_C, contraction over rows; T = Z, or the sum of
+//           the iterates when C.xsel = 1)                                      -> or partials Up
+//           mode 0: Vc -= eta P_C^T T (the last product of the rows side, or the only step)
+//           mode 1: X = Sx = P_C^T Z  (the first iterate of the keys side)
+//   KIND 2: one step of the iteration X <- X - eta Mg X, Sx += X           -> or partials Xp
+//           mode 0: the new iterate's transpose goes to the other buffer for the next step
+//           mode 1 (last step): rows side, Sx's transpose goes there for KIND 1;
+//                   keys side, Vc -= eta Sx
+// Work item = (seq, head, output tile, split), split fastest.
+// ------------------------------------------------------------------------------------------------
+template <int KIND>
+__global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
+                                                  SeqTable T) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kGLds];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = find_seq(T, t);
+  const int m = T.m[i], s = T.first + i;
+  const int R = C.R;
+  AmWs W = am_ws(ws, T, i, C);
+  const int ldm = W.ldm, Np = W.Np;
+  const int S = KIND == 0 ? C.S1 : (KIND == 1 ? C.S2 : C.S3);
+  const int rows = KIND == 0 ? R : (KIND == 1 ? ldm : Np);  // output rows
+  const int tiles = (rows + kGTile - 1) / kGTile;
+  int local = t - T.start[i];
+  const int sp = local % S;
+  local /= S;
+  const int tile = local % tiles, h = local / tiles;
+  const int64_t unit = (int64_t)s * C.H + h;
+  // A rows (pitch apitch) and B rows (the 128 columns of the right operand, pitch bpitch)
+  const int apitch = KIND == 0 ? ldm : (KIND == 1 ? W.Rp : Np);
+  const float* A = KIND == 0 ? W.P + (int64_t)h * R * ldm
+                             : (KIND == 1 ? W.PT + (int64_t)h * ldm * W.Rp : W.Mg + (int64_t)h * Np * Np);
+  const float* B = KIND == 0 ? W.VT + (int64_t)h * kD * ldm
+                             : (KIND == 1 ? (C.xsel ? W.XT1 : W.ZT) + (int64_t)h * kD * W.Rp
+                                          : am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel) + (int64_t)h * kD * Np);
+  const int bpitch = apitch;
+  const int nst = KIND == 0 ? ldm / 32 : (KIND == 1 ? (R + 31) / 32 : Np / 32);
+  const int per = (nst + S - 1) / S;
+  const int st0 = sp * per, st1 = min(nst, st0 + per);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int arow = tile * kGTile + (tid >> 1);
+  const int alim = KIND == 0 ? R : (KIND == 1 ? ldm : Np);
 
   f32x4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  if (st0 < st1) {
-    load(st0);
-    store(0);
-    __syncthreads();
-#pragma unroll 1
-    for (int stg = st0; stg < st1; ++stg) {
-      const int buf = (stg - st0) & 1;
-      const bool more = stg + 1 < st1;
-      if (more) load(stg + 1);
-      bf16x8 bh[4], bl[4];
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int o = gswz(64 * wc + 16 * b + c16, g);
-        bh[b] = *reinterpret_cast<const bf16x8*>(&Bh[buf][o]);
-        bl[b] = *reinterpret_cast<const bf16x8*>(&Bl[buf][o]);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int o = gswz(64 * wr + 16 * a + c16, g);
-        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[buf][o]);
-        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[buf][o]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          acc[a][b] = mfma16(ah, bh[b], acc[a][b]);
-          acc[a][b] = mfma16(ah, bl[b], acc[a][b]);
-          acc[a][b] = mfma16(al, bh[b], acc[a][b]);
-        }
-      }
-      if (more) store(buf ^ 1);
-      __syncthreads();
-    }
-  }
+  tile_mma(A + (int64_t)min(arow, alim - 1) * apitch, arow < alim, B + (int64_t)(tid & 127) * bpitch, true, st0, st1,
+           acc, sm);
 
+  const float eta = W.eta[h];
+  const int64_t xk = pad64((int64_t)C.H * Np * kD);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -666,39 +964,154 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
       for (int e = 0; e < 4; ++e) {
         const int r = tile * kGTile + 64 * wr + 16 * a + 4 * g + e;
         const int col = 64 * wc + 16 * b + c16;
-        if constexpr (KIND == 0) {  // Z = P_C Vc - Y, kept as split rows of Z^T (zeros past R)
+        const float v = acc[a][b][e];
+        if constexpr (KIND == 0) {  // Z = P_C V0 - Y, kept as split rows of Z^T (zeros past R)
           const int64_t o = (int64_t)h * R * kD + (int64_t)r * kD + col;
           if (S == 1) {
-            if (r < W.Rp) put_split1(W.ZT + ((int64_t)h * kD + col) * W.Rp, r, r < R ? acc[a][b][e] - W.Y[o] : 0.0f);
+            if (r < W.Rp) {
+              const float z = r < R ? v - W.Y[o] : 0.0f;
+              put_split1(W.ZT + ((int64_t)h * kD + col) * W.Rp, r, z);
+              if (W.rside && r < R) {
+                const int64_t ox = ((int64_t)h * Np + r) * kD + col;
+                W.X[ox] = z;
+                W.Sx[ox] = z;
+              }
+            }
           } else if (r < R) {
-            W.Zp[(int64_t)sp * pad64((int64_t)C.H * R * kD) + o] = acc[a][b][e];
+            W.Zp[(int64_t)sp * pad64((int64_t)C.H * R * kD) + o] = v;
           }
-        } else {  // Vc -= eta P_C^T Z, with its split rows of Vc^T (zeros past m)
+        } else if constexpr (KIND == 1) {
           const int64_t o = (int64_t)r * kD + col;
           if (S == 1) {
             if (r < ldm) {
-              float v = 0.0f;
-              if (r < m) {
-                float* d = vc_all + unit * C.m_max * (int64_t)kD + o;
-                v = *d - W.eta[h] * acc[a][b][e];
-                *d = v;
+              if (C.mode == 0) {  // Vc -= eta P_C^T T, with its split rows of Vc^T (zeros past m)
+                float x = 0.0f;
+                if (r < m) {
+                  float* d = vc_all + unit * C.m_max * (int64_t)kD + o;
+                  x = *d - eta * v;
+                  *d = x;
+                }
+                put_split1(W.VT + ((int64_t)h * kD + col) * ldm, r, x);
+              } else {  // the keys side's first iterate
+                const float x = r < m ? v : 0.0f;
+                const int64_t ox = ((int64_t)h * Np + r) * kD + col;
+                W.X[ox] = x;
+                W.Sx[ox] = x;
+                put_split1(W.VT + ((int64_t)h * kD + col) * ldm, r, x);
               }
-              put_split1(W.VT + ((int64_t)h * kD + col) * ldm, r, v);
             }
           } else if (r < ldm) {
-            W.Up[(int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD + o] = acc[a][b][e];
+            W.Up[(int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD + o] = v;
+          }
+        } else {  // one step of the iteration
+          if (S == 1) {
+            if (r < Np) {
+              const int64_t ox = ((int64_t)h * Np + r) * kD + col;
+              float xn = 0.0f, sum = 0.0f;
+              if (r < W.N) {
+                xn = W.X[ox] - eta * v;
+                sum = W.Sx[ox] + xn;
+                W.X[ox] = xn;
+                W.Sx[ox] = sum;
+              }
+              if (C.mode == 1 && !W.rside) {
+                if (r < m) vc_all[unit * C.m_max * (int64_t)kD + (int64_t)r * kD + col] -= eta * sum;
+              } else {
+                put_split1(am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel ^ 1) + ((int64_t)h * kD + col) * Np, r, C.mode == 1 ? sum : xn);
+              }
+            }
+          } else if (r < Np) {
+            W.Xp[(int64_t)sp * xk + ((int64_t)h * Np + r) * kD + col] = v;
           }
         }
       }
 }
 
-// Output tiles of the Landweber products: KIND 0 over the R rows, KIND 1 over the ldm kept keys.
+// Output tiles of the products: KIND 0 over the R rows, KIND 1 over the ldm kept keys, KIND 2
+// over the Np rows of the iteration's side.
 int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 
-// Split sums, in split order: Z = sum_s Zp[s] - Y (KIND 0, work item = (seq, head, 64 rows)) and
-// Vc_j -= eta sum_s Up[s]_j (KIND 1, work item = (seq, head, 64 kept keys)). The block's results
-// (zeros past R, or past m) are staged in LDS and leave as split rows of Z^T or Vc^T, the form
-// the next product reads; Vc itself is also kept in float32.
+// ------------------------------------------------------------------------------------------------
+// The Gram matrix of the iteration's side, Mg = X X^T with X = P_C (rows side: Np = Rp rows,
+// contraction over the kept keys) or X = P_C^T (keys side: Np = ldm rows, contraction over the
+// proxy rows), stored as split rows [Np][Np]. Mg is symmetric: a workgroup forms the tile (a, b)
+// with a <= b and writes it and, off the diagonal, its transpose, both through LDS (the tile in
+// float32, pitch 129) as split rows. Rows and columns of X past its live rows are zero, so are
+// those of Mg. Work item = (seq, head, tile pair), pairs a-major.
+// ------------------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void am_gram(float* __restrict__ ws, AmCfg C, SeqTable T) {
+  constexpr int kPitch = kGTile + 1;
+  __shared__ __attribute__((aligned(16))) float tl[kGTile * kPitch];
+  static_assert(sizeof(float) * kGTile * kPitch >= kGLds, "the product stages live in the tile's LDS");
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = find_seq(T, t);
+  const int R = C.R;
+  AmWs W = am_ws(ws, T, i, C);
+  const int ldm = W.ldm, Np = W.Np;
+  const int nt = (Np + kGTile - 1) / kGTile, pairs = nt * (nt + 1) / 2;
+  const int local = t - T.start[i];
+  const int h = local / pairs;
+  int p = local - h * pairs, a = 0;
+  while (p >= nt - a) {
+    p -= nt - a;
+    ++a;
+  }
+  const int b = a + p;
+  const float* X = W.rside ? W.P + (int64_t)h * R * ldm : W.PT + (int64_t)h * ldm * W.Rp;
+  const int pitch = W.rside ? ldm : W.Rp;
+  const int xrows = W.rside ? R : ldm;
+  const int nst = W.rside ? ldm / 32 : (R + 31) / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int ra = a * kGTile + (tid >> 1), rb = b * kGTile + (tid & 127);
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  tile_mma(X + (int64_t)min(ra, xrows - 1) * pitch, ra < xrows, X + (int64_t)min(rb, xrows - 1) * pitch, rb < xrows,
+           0, nst, acc, reinterpret_cast<uint8_t*>(tl));
+  __syncthreads();  // the stages are done with the LDS
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tl[(64 * wr + 16 * x + 4 * g + e) * kPitch + 64 * wc + 16 * y + c16] = acc[x][y][e];
+  __syncthreads();
+  float* Mh = W.Mg + (int64_t)h * Np * Np;
+  for (int q = tid; q < kGTile * (kGTile / 8); q += 256) {
+    const int r = q >> 4, gq = q & 15;
+    if (a * kGTile + r < Np && b * kGTile + 8 * gq < Np)
+      put_split8(Mh + (int64_t)(a * kGTile + r) * Np + b * kGTile, gq, &tl[r * kPitch + 8 * gq]);
+  }
+  if (a != b) {
+    for (int q = tid; q < kGTile * (kGTile / 8); q += 256) {
+      const int c = q >> 4, gq = q & 15;
+      if (b * kGTile + c >= Np || a * kGTile + 8 * gq >= Np) continue;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = tl[(8 * gq + e) * kPitch + c];
+      put_split8(Mh + (int64_t)(b * kGTile + c) * Np + a * kGTile, gq, x);
+    }
+  }
+}
+
+// Tile pairs of the Gram matrix of an Np-row side.
+int64_t am_gram_items(int Np) {
+  const int64_t nt = (Np + kGTile - 1) / kGTile;
+  return nt * (nt + 1) / 2;
+}
+
+// Split sums, in split order, then the product's epilogue (as in am_gemm with one split):
+//   KIND 0: Z = sum_s Zp[s] - Y                       work item = (seq, head, 64 rows)
+//   KIND 1: mode 0: Vc_j -= eta sum_s Up[s]_j; mode 1: X = Sx = sum_s Up[s]
+//                                                     work item = (seq, head, 64 kept keys)
+//   KIND 2: X <- X - eta sum_s Xp[s], Sx += X, then as am_gemm's KIND 2
+//                                                     work item = (seq, head, 64 rows of the side)
+// The block's results (zeros past the live rows) are staged in LDS and leave as split rows of
+// the transpose, the form the next product reads; Vc and the iterates are also kept in float32.
 template <int KIND>
 __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
                                                     SeqTable T) {
@@ -708,15 +1121,20 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
   const int m = T.m[i], s = T.first + i;
   const int R = C.R;
   AmWs W = am_ws(ws, T, i, C);
-  const int ldm = W.ldm;
-  const int nb = KIND == 0 ? (R + 63) / 64 : ldm / 64;
+  const int ldm = W.ldm, Np = W.Np;
+  const int nb = KIND == 0 ? (R + 63) / 64 : (KIND == 1 ? ldm / 64 : Np / 64);
   const int local = t - T.start[i];
   const int h = local / nb, blk = local - h * nb;
-  const int lim = KIND == 0 ? R : m;
-  const int S = KIND == 0 ? C.S1 : C.S2;
+  const int lim = KIND == 0 ? R : (KIND == 1 ? m : W.N);
+  const int S = KIND == 0 ? C.S1 : (KIND == 1 ? C.S2 : C.S3);
   const int64_t unit = (int64_t)s * C.H + h;
-  const int64_t stride = KIND == 0 ? pad64((int64_t)C.H * R * kD) : pad64((int64_t)C.H * ldm * kD);
-  const float* src = (KIND == 0 ? W.Zp + (int64_t)h * R * kD : W.Up + (int64_t)h * ldm * kD);
+  const int64_t stride = KIND == 0 ? pad64((int64_t)C.H * R * kD)
+                                   : (KIND == 1 ? pad64((int64_t)C.H * ldm * kD) : pad64((int64_t)C.H * Np * kD));
+  const float* src = KIND == 0 ? W.Zp + (int64_t)h * R * kD
+                               : (KIND == 1 ? W.Up + (int64_t)h * ldm * kD : W.Xp + (int64_t)h * Np * kD);
+  const float eta = W.eta[h];
+  // keys side, last step: Vc takes the sum and no transpose is written
+  const bool to_vc = KIND == 2 && C.mode == 1 && !W.rside;
   for (int x = threadIdx.x; x < 64 * (kD / 4); x += 256) {
     const int row = blk * 64 + (x >> 5), c4 = x & 31;
     float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -730,19 +1148,53 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
         a.z += p.z;
         a.w += p.w;
       }
+      const int64_t ox = ((int64_t)h * Np + row) * kD + 4 * c4;
       if constexpr (KIND == 0) {
         const float4 y = *reinterpret_cast<const float4*>(W.Y + (int64_t)h * R * kD + o);
         val = make_float4(a.x - y.x, a.y - y.y, a.z - y.z, a.w - y.w);
+        if (W.rside) {
+          *reinterpret_cast<float4*>(W.X + ox) = val;
+          *reinterpret_cast<float4*>(W.Sx + ox) = val;
+        }
+      } else if constexpr (KIND == 1) {
+        if (C.mode == 0) {
+          float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
+          float4 v = *d;
+          v.x -= eta * a.x;
+          v.y -= eta * a.y;
+          v.z -= eta * a.z;
+          v.w -= eta * a.w;
+          *d = v;
+          val = v;
+        } else {
+          val = a;
+          *reinterpret_cast<float4*>(W.X + ox) = val;
+          *reinterpret_cast<float4*>(W.Sx + ox) = val;
+        }
       } else {
-        const float f = W.eta[h];
-        float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
-        float4 v = *d;
-        v.x -= f * a.x;
-        v.y -= f * a.y;
-        v.z -= f * a.z;
-        v.w -= f * a.w;
-        *d = v;
-        val = v;
+        float4* xp = reinterpret_cast<float4*>(W.X + ox);
+        float4* sp4 = reinterpret_cast<float4*>(W.Sx + ox);
+        float4 xn = *xp, sum = *sp4;
+        xn.x -= eta * a.x;
+        xn.y -= eta * a.y;
+        xn.z -= eta * a.z;
+        xn.w -= eta * a.w;
+        sum.x += xn.x;
+        sum.y += xn.y;
+        sum.z += xn.z;
+        sum.w += xn.w;
+        *xp = xn;
+        *sp4 = sum;
+        val = C.mode == 1 ? sum : xn;
+        if (to_vc) {
+          float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
+          float4 v = *d;
+          v.x -= eta * sum.x;
+          v.y -= eta * sum.y;
+          v.z -= eta * sum.z;
+          v.w -= eta * sum.w;
+          *d = v;
+        }
       }
     }
     float* tr = &tile[x >> 5][4 * c4];
@@ -751,9 +1203,11 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
     tr[2] = val.z;
     tr[3] = val.w;
   }
+  if (to_vc) return;  // uniform across the block
   __syncthreads();
-  const int pitch = KIND == 0 ? W.Rp : ldm;
-  float* dst = (KIND == 0 ? W.ZT : W.VT) + (int64_t)h * kD * pitch + blk * 64;
+  const int pitch = KIND == 0 ? W.Rp : (KIND == 1 ? ldm : Np);
+  float* base = KIND == 0 ? W.ZT : (KIND == 1 ? W.VT : am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel ^ 1));
+  float* dst = base + (int64_t)h * kD * pitch + blk * 64;
   for (int q = threadIdx.x; q < kD * 8; q += 256) {
     const int d = q >> 3, gq = q & 7;
     float x[8];
@@ -836,47 +1290,19 @@ __global__ __launch_bounds__(256) void am_finish(float* __restrict__ w_all, cons
 #define KVC_COMMA ,
 
 // Work items per head of each kernel.
-int64_t am_exp_items(int R, int cols) { return (int64_t)((R + 63) / 64) * ((cols + 63) / 64); }
-int64_t am_scale_items(int R, int m) { return ((int64_t)R * pad64(m) + 4095) / 4096; }
 int am_row_tiles(int R) { return (R + 63) / 64; }
-int am_dot_row_items(int R) { return (R + 3) / 4; }
 int am_col_items(int m) { return (m + 255) / 256; }
-int64_t am_col_part_items(int R, int m) { return (int64_t)((pad64(m) + 255) / 256) * ((R + kRowChunk - 1) / kRowChunk); }
 int64_t am_key_tiles(int m) { return pad64(m) / 64; }
 int am_stages_rows(int m) { return (int)(pad64(m) / 32); }
 int am_stages_cols(int R) { return (R + 31) / 32; }
-
-hipError_t launch_am_exp(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
-                         const int32_t* kept, float* ws, int64_t n_max, float scale, const AmCfg& C, const SeqTable& T,
-                         hipStream_t st) {
-  const auto* qq = static_cast<const uint16_t*>(q);
-  const auto* kk = static_cast<const uint16_t*>(k);
-  dim3 grid(T.total), block(kThreads);
-  KVC_AM_LAYOUT(am_exp, , qq, kk, table, max_blocks, kept, ws, n_max, scale, C, T);
-  return hipGetLastError();
-}
 
 hipError_t launch_am_stats(const float* lse, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   am_stats<<<dim3(T.total), dim3(64), 0, st>>>(lse, ws, C, T);
   return hipGetLastError();
 }
 
-hipError_t launch_am_scale(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
-  am_scale<<<dim3(T.total), dim3(256), 0, st>>>(ws, C, T);
-  return hipGetLastError();
-}
-
-hipError_t launch_am_rows_dot(const float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
-  am_rows_dot<<<dim3(T.total), dim3(256), 0, st>>>(w, ws, C, T);
-  return hipGetLastError();
-}
-
-hipError_t launch_am_cols_part(int mode, const float* w, const float* lse, float* ws, const AmCfg& C,
-                               const SeqTable& T, hipStream_t st) {
-  dim3 grid(T.total), block(256);
-  if (mode == 0) am_cols_part<0><<<grid, block, 0, st>>>(w, lse, ws, C, T);
-  else if (mode == 1) am_cols_part<1><<<grid, block, 0, st>>>(w, lse, ws, C, T);
-  else am_cols_part<2><<<grid, block, 0, st>>>(w, lse, ws, C, T);
+hipError_t launch_am_me(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_me<<<dim3(T.total), dim3(64), 0, st>>>(ws, C, T);
   return hipGetLastError();
 }
 
@@ -906,14 +1332,21 @@ hipError_t launch_am_target(int layout, const void* q, const void* k, const void
 hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(256);
   if (kind == 0) am_gemm<0><<<grid, block, 0, st>>>(vc, ws, C, T);
-  else am_gemm<1><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else if (kind == 1) am_gemm<1><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else am_gemm<2><<<grid, block, 0, st>>>(vc, ws, C, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_am_gram(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_gram<<<dim3(T.total), dim3(256), 0, st>>>(ws, C, T);
   return hipGetLastError();
 }
 
 hipError_t launch_am_split_sum(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(256);
   if (kind == 0) am_split_sum<0><<<grid, block, 0, st>>>(vc, ws, C, T);
-  else am_split_sum<1><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else if (kind == 1) am_split_sum<1><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else am_split_sum<2><<<grid, block, 0, st>>>(vc, ws, C, T);
   return hipGetLastError();
 }
 
@@ -925,6 +1358,28 @@ hipError_t launch_am_init(int layout, const void* v, const int32_t* table, int m
   KVC_AM_LAYOUT(am_init, , vv, table, max_blocks, kept, w, vc, ws, n_max, C, T);
   return hipGetLastError();
 }
+
+hipError_t launch_am_gather(int layout, const void* k, const int32_t* table, int max_blocks, const int32_t* kept,
+                            float* ws, int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  const auto* kk = static_cast<const uint16_t*>(k);
+  dim3 grid(T.total), block(256);
+  KVC_AM_LAYOUT(am_gather, , kk, table, max_blocks, kept, ws, n_max, C, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_am_bias(int mode, const void* q, const float* w, const float* lse, float* ws, float scale,
+                          const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  const auto* qq = static_cast<const uint16_t*>(q);
+  dim3 grid(T.total), block(256);
+  block = dim3(kBiasThreads);
+  if (mode == 0) am_bias<0><<<grid, block, 0, st>>>(qq, w, lse, ws, scale, C, T);
+  else if (mode == 1) am_bias<1><<<grid, block, 0, st>>>(qq, w, lse, ws, scale, C, T);
+  else if (mode == 2) am_bias<2><<<grid, block, 0, st>>>(qq, w, lse, ws, scale, C, T);
+  else am_bias<3><<<grid, block, 0, st>>>(qq, w, lse, ws, scale, C, T);
+  return hipGetLastError();
+}
+
+int64_t am_gather_items(int m) { return pad256(m) / 64; }
 
 hipError_t launch_am_finish(float* w, const float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   am_finish<<<dim3(T.total), dim3(256), 0, st>>>(w, ws, C, T);

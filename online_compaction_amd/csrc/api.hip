@@ -10,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "am_cfg.h"
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -53,34 +54,28 @@ hipError_t launch_valu_score_cached(const float2* ws, float* out, int H, int R, 
 hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
                                  const SeqTable& T, hipStream_t st);
 int redirect_tiles(int n);
-struct AmCfg {
-  int H, R, m_max, S1, S2;
-};
-int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2);
-int64_t am_exp_items(int R, int cols);
-int64_t am_scale_items(int R, int m);
+int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int S3);
 int am_row_tiles(int R);
-int am_dot_row_items(int R);
 int am_col_items(int m);
-int64_t am_col_part_items(int R, int m);
 int64_t am_key_tiles(int m);
 int am_gemm_tiles(int rows);
 int am_stages_rows(int m);
 int am_stages_cols(int R);
 hipError_t launch_am_stats(const float* lse, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_scale(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_exp(int layout, const void* q, const void* k, const int32_t* table, int max_blocks,
-                         const int32_t* kept, float* ws, int64_t n_max, float scale, const AmCfg& C, const SeqTable& T,
-                         hipStream_t st);
-hipError_t launch_am_rows_dot(const float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
-hipError_t launch_am_cols_part(int mode, const float* w, const float* lse, float* ws, const AmCfg& C,
-                               const SeqTable& T, hipStream_t st);
+hipError_t launch_am_me(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_cols_fin(int mode, float* w, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_eta(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_target(int layout, const void* q, const void* k, const void* v, const int32_t* table,
                             int max_blocks, const int32_t* vtable, int vmax_blocks, const float* lse, float* ws,
                             int64_t n_max, float scale, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_gram(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_gather(int layout, const void* k, const int32_t* table, int max_blocks, const int32_t* kept,
+                            float* ws, int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_bias(int mode, const void* q, const float* w, const float* lse, float* ws, float scale,
+                          const AmCfg& C, const SeqTable& T, hipStream_t st);
+int64_t am_gather_items(int m);
+int64_t am_gram_items(int Np);
 hipError_t launch_am_split_sum(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_init(int layout, const void* v, const int32_t* table, int max_blocks, const int32_t* kept,
                           float* w, float* vc, const float* ws, int64_t n_max, const AmCfg& C, const SeqTable& T,
@@ -729,19 +724,25 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
 // ------------------------------------------------------------------------------------------------
 // Attention Matching
 // ------------------------------------------------------------------------------------------------
-// Split counts of the two value products (at most 8 splits, at least 4 stages of 32 per split).
-// A function of the shape alone, so that the workspace size and the fit agree.
-static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2) {
+// Split counts of the three value products (at most 8 splits, at least 4 stages of 32 per
+// split). A function of the shape alone, so that the workspace size and the fit agree.
+static int am_side_rows_padded(int R, int m) { return am_rows_side(R, m) ? (R + 63) / 64 * 64 : (m + 63) / 64 * 64; }
+
+static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2, int* S3) {
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
-  int64_t t1 = 0, t2 = 0, out1 = 0, out2 = 0;
-  int st1 = INT32_MAX, st2 = am_stages_cols(R);
+  int64_t t1 = 0, t2 = 0, t3 = 0, out1 = 0, out2 = 0, out3 = 0;
+  int st1 = INT32_MAX, st2 = am_stages_cols(R), st3 = INT32_MAX;
   for (int s = 0; s < sh->num_seqs; ++s) {
     if (m[s] == 0) continue;
+    const int ldm = (m[s] + 63) / 64 * 64, Np = am_side_rows_padded(R, m[s]);
     t1 += (int64_t)H * am_gemm_tiles(R);
-    t2 += (int64_t)H * am_gemm_tiles((m[s] + 63) / 64 * 64);
+    t2 += (int64_t)H * am_gemm_tiles(ldm);
+    t3 += (int64_t)H * am_gemm_tiles(Np);
     out1 += (int64_t)H * R * 128;
-    out2 += (int64_t)H * ((m[s] + 63) / 64 * 64) * 128;
+    out2 += (int64_t)H * ldm * 128;
+    out3 += (int64_t)H * Np * 128;
     st1 = std::min(st1, am_stages_rows(m[s]));
+    st3 = std::min(st3, Np / 32);
   }
   // The split count that minimises rounds of workgroups (two per CU) x stages per split, plus
   // the round trip of the partial products through memory: each split writes the whole output
@@ -765,14 +766,15 @@ static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2) {
   };
   *S1 = pick(t1, st1, out1);
   *S2 = pick(t2, st2, out2);
+  *S3 = pick(t3, st3, out3);
 }
 
 static size_t am_bytes(const kvc_shape* sh, const int32_t* m) {
-  int S1, S2;
-  am_splits(sh, m, &S1, &S2);
+  int S1, S2, S3;
+  am_splits(sh, m, &S1, &S2, &S3);
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
   int64_t f = 0;
-  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(H, R, sh->seq_lens[s], m[s], S1, S2);
+  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(H, R, sh->seq_lens[s], m[s], S1, S2, S3);
   return ((size_t)f * sizeof(float) + 255) & ~size_t(255);
 }
 
@@ -814,34 +816,42 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
                 ws ? ws_bytes : 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
-  AmCfg C{H, R, m_max, 1, 1};
-  am_splits(sh, m, &C.S1, &C.S2);
+  AmCfg C{H, R, m_max, 1, 1, 1, 0, 0};
+  am_splits(sh, m, &C.S1, &C.S2, &C.S3);
   // work items per sequence of every launch family; a sequence with m = 0 has nothing to fit and
   // gets no work items
   auto per = [&](auto&& f) { return [&, f](int s) -> int64_t { return m[s] ? (int64_t)H * f(s) : 0; }; };
   auto units = per([](int) -> int64_t { return 1; });
-  auto exps = per([&](int s) { return am_exp_items(R, m[s]); });
-  auto scales = per([&](int s) { return am_scale_items(R, m[s]); });
   auto cols = per([&](int s) -> int64_t { return am_col_items(m[s]); });
-  auto cparts = per([&](int s) { return am_col_part_items(R, m[s]); });
-  auto rows = per([&](int) -> int64_t { return am_dot_row_items(R); });
   auto rtiles = per([&](int) -> int64_t { return am_row_tiles(R); });
   auto ktiles = per([&](int s) { return am_key_tiles(m[s]); });
   auto gemm0 = per([&](int) -> int64_t { return (int64_t)am_gemm_tiles(R) * C.S1; });
   auto gemm1 = per([&](int s) -> int64_t { return (int64_t)am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; });
+  // the value iteration (am_rows_side): Gram tile pairs, step tiles and their split sums, and the
+  // launches that only one side's sequences take part in
+  auto side = [&](int s) { return am_rows_side(R, m[s]); };
+  auto gram = per([&](int s) { return am_gram_items(am_side_rows_padded(R, m[s])); });
+  auto gathers = per([&](int s) { return am_gather_items(m[s]); });
+  auto gemm2 = per([&](int s) -> int64_t { return (int64_t)am_gemm_tiles(am_side_rows_padded(R, m[s])) * C.S3; });
+  auto sum2 = per([&](int s) -> int64_t { return am_side_rows_padded(R, m[s]) / 64; });
+  auto ktile_items = [&](int s) -> int64_t { return (int64_t)am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; };
+  auto gemm1_rows = per([&](int s) -> int64_t { return side(s) ? ktile_items(s) : 0; });
+  auto gemm1_keys = per([&](int s) -> int64_t { return side(s) ? 0 : ktile_items(s); });
+  auto ktiles_rows = per([&](int s) -> int64_t { return side(s) ? am_key_tiles(m[s]) : 0; });
+  auto ktiles_keys = per([&](int s) -> int64_t { return side(s) ? 0 : am_key_tiles(m[s]); });
   {
     const char* what = "attention matching kernel";
     kvc_status e = KVC_OK;
     if (!e) e = check_items(sh, units, what);
-    if (!e) e = check_items(sh, exps, what);
-    if (!e) e = check_items(sh, scales, what);
     if (!e) e = check_items(sh, cols, what);
-    if (!e) e = check_items(sh, cparts, what);
-    if (!e) e = check_items(sh, rows, what);
     if (!e) e = check_items(sh, rtiles, what);
     if (!e) e = check_items(sh, ktiles, what);
     if (!e) e = check_items(sh, gemm0, what);
     if (!e) e = check_items(sh, gemm1, what);
+    if (!e) e = check_items(sh, gram, what);
+    if (!e) e = check_items(sh, gathers, what);
+    if (!e) e = check_items(sh, gemm2, what);
+    if (!e) e = check_items(sh, sum2, what);
     if (!e && !lse) e = check_lse_work(sh, k);
     if (e) return e;
   }
@@ -856,7 +866,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   int64_t acc = 0;
   for (int s = 0; s < sh->num_seqs; ++s) {
     off[s] = acc;
-    acc += am_seq_floats(H, R, sh->seq_lens[s], m[s], C.S1, C.S2);
+    acc += am_seq_floats(H, R, sh->seq_lens[s], m[s], C.S1, C.S2, C.S3);
   }
   auto offset = [&](int s) -> int64_t { return off[s]; };
   const int layout = layout_of(k);
@@ -868,29 +878,53 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
     if (e_ != hipSuccess) return hip_fail(e_, "attention matching kernel");      \
   } while (0)
   KVC_AM_STEP(units, launch_am_stats(lse_rows, amws, C, T, st));
-  KVC_AM_STEP(exps,
-              launch_am_exp(layout, q, k->data, k->block_table, k->max_blocks, kept, amws, nm, sh->scale, C, T, st));
-  KVC_AM_STEP(scales, launch_am_scale(amws, C, T, st));
-  KVC_AM_STEP(cparts, launch_am_cols_part(0, beta, lse_rows, amws, C, T, st));
+  KVC_AM_STEP(gathers,
+              launch_am_gather(layout, k->data, k->block_table, k->max_blocks, kept, amws, nm, C, T, st));
+  KVC_AM_STEP(rtiles, launch_am_bias(3, q, beta, lse_rows, amws, sh->scale, C, T, st));  // ME
+  KVC_AM_STEP(units, launch_am_me(amws, C, T, st));
+  KVC_AM_STEP(rtiles, launch_am_bias(0, q, beta, lse_rows, amws, sh->scale, C, T, st));  // E^T z
   KVC_AM_STEP(cols, launch_am_cols_fin(0, beta, amws, C, T, st));
   KVC_AM_STEP(cols, launch_am_init(layout, v->data, v->block_table, v->max_blocks, kept, beta, v_c, amws, nm, C, T,
                                    st));
   for (int it = 0; it < iters_beta; ++it) {
-    KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, C, T, st));
-    KVC_AM_STEP(cparts, launch_am_cols_part(1, beta, lse_rows, amws, C, T, st));
+    KVC_AM_STEP(rtiles, launch_am_bias(1, q, beta, lse_rows, amws, sh->scale, C, T, st));
     KVC_AM_STEP(cols, launch_am_cols_fin(1, beta, amws, C, T, st));
   }
-  KVC_AM_STEP(rows, launch_am_rows_dot(beta, amws, C, T, st));
-  KVC_AM_STEP(cparts, launch_am_cols_part(2, beta, lse_rows, amws, C, T, st));  // E becomes P_C
-  KVC_AM_STEP(cols, launch_am_cols_fin(2, beta, amws, C, T, st));
+  KVC_AM_STEP(rtiles, launch_am_bias(2, q, beta, lse_rows, amws, sh->scale, C, T, st));  // P_C, P_C^T
+  KVC_AM_STEP(cols, launch_am_cols_fin(0, beta, amws, C, T, st));                       // column sums
   KVC_AM_STEP(units, launch_am_eta(amws, C, T, st));
-  KVC_AM_STEP(rtiles, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
-                                       v->max_blocks, lse_rows, amws, nm, sh->scale, C, T, st));
-  for (int it = 0; it < iters_v; ++it) {
+  // Values: k = iters_v Landweber steps V <- V - eta P_C^T (P_C V - Y), run as the iteration of
+  // the residual on the smaller side of P_C (exact rewriting of the same steps): with
+  // Z_0 = P_C V_0 - Y,
+  //   rows side:  Z_{t+1} = Z_t - eta (P_C P_C^T) Z_t,          V_k = V_0 - eta P_C^T sum_{t<k} Z_t
+  //   keys side:  r_0 = P_C^T Z_0, r_{t+1} = r_t - eta (P_C^T P_C) r_t,   V_k = V_0 - eta sum_{t<k} r_t
+  // (one step, k = 1, is the direct product for both).
+  if (iters_v > 0) {
+    KVC_AM_STEP(rtiles, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
+                                         v->max_blocks, lse_rows, amws, nm, sh->scale, C, T, st));
+    C.mode = 0;
+    C.xsel = 0;
     KVC_AM_STEP(gemm0, launch_am_gemm(0, v_c, amws, C, T, st));
     if (C.S1 > 1) KVC_AM_STEP(rtiles, launch_am_split_sum(0, v_c, amws, C, T, st));
-    KVC_AM_STEP(gemm1, launch_am_gemm(1, v_c, amws, C, T, st));
-    if (C.S2 > 1) KVC_AM_STEP(ktiles, launch_am_split_sum(1, v_c, amws, C, T, st));
+    if (iters_v == 1) {
+      KVC_AM_STEP(gemm1, launch_am_gemm(1, v_c, amws, C, T, st));
+      if (C.S2 > 1) KVC_AM_STEP(ktiles, launch_am_split_sum(1, v_c, amws, C, T, st));
+    } else {
+      C.mode = 1;  // keys side: the first iterate r_0
+      KVC_AM_STEP(gemm1_keys, launch_am_gemm(1, v_c, amws, C, T, st));
+      if (C.S2 > 1) KVC_AM_STEP(ktiles_keys, launch_am_split_sum(1, v_c, amws, C, T, st));
+      KVC_AM_STEP(gram, launch_am_gram(amws, C, T, st));
+      for (int it = 1; it < iters_v; ++it) {
+        C.xsel = (it - 1) & 1;
+        C.mode = it == iters_v - 1;
+        KVC_AM_STEP(gemm2, launch_am_gemm(2, v_c, amws, C, T, st));
+        if (C.S3 > 1) KVC_AM_STEP(sum2, launch_am_split_sum(2, v_c, amws, C, T, st));
+      }
+      C.mode = 0;  // rows side: V_k = V_0 - eta P_C^T (sum of the iterates), read from where the last step put it
+      C.xsel = (iters_v - 1) & 1;
+      KVC_AM_STEP(gemm1_rows, launch_am_gemm(1, v_c, amws, C, T, st));
+      if (C.S2 > 1) KVC_AM_STEP(ktiles_rows, launch_am_split_sum(1, v_c, amws, C, T, st));
+    }
   }
   KVC_AM_STEP(cols, launch_am_finish(beta, amws, C, T, st));
 #undef KVC_AM_STEP

@@ -108,3 +108,18 @@ def test_am_supplied_lse_and_many_tiles():
     say(f"[case] am big: R={w.R} n={w.n[0]} m={m[0]}")
     beta, vc = _run(w, data, kept, m, 16, 16, lse)
     _check(w, data, kept, m, beta, vc, 16, 16, lse, tag="big")
+
+
+@pytest.mark.parametrize("iters_v", [1, 2, 3, 9])
+def test_am_value_iteration_on_either_side(iters_v):
+    """The value steps run on the smaller side of P_C: 128 proxy rows against 60 kept keys (the
+    keys side) and 200 kept keys (the rows side) in one call; one step is the direct product,
+    two or more go through the Gram matrix, an odd and an even count end in either buffer."""
+    w = W.custom("am_sides", 173, S=2, H=2, G=4, q=32, n=(400, 257), dtype="bf16", keys="mixture",
+                 queries="cluster")
+    data = W.build_contiguous(w)
+    m = [60, 200]
+    kept = _kept(np.random.default_rng(6 + iters_v), w, m)
+    say(f"[case] am sides: R={w.R} n={list(w.n)} m={m} iterations 4 + {iters_v}")
+    beta, vc = _run(w, data, kept, m, 4, iters_v)
+    _check(w, data, kept, m, beta, vc, 4, iters_v, tag=f"sides v{iters_v}")
