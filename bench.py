@@ -33,7 +33,6 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 # off): 256 CUs x 4 SIMDs x 16 lanes x 2 flop (one FMA) x 2.4 GHz = 78.6 TFLOP/s; the published
 # 157.3 TFLOP/s counts the packed (two-wide) FMA
 F32_VALU_PEAK_TFLOPS = 78.6
-MFMA_F32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_traffic.txt")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "score_mfma_c3_counters.txt")
 # the score kernel's source: its own file and the headers it includes
@@ -127,21 +126,48 @@ def score_flops(w) -> float:
     return float(passes) * 2.0 * w.R * w.d * sum(scored_lens(w)) * w.H
 
 
-def am_flops(w, iters_beta: int, iters_v: int) -> dict:
-    """Multiply-add work of one Attention Matching fit, by the units that do it: bf16 MFMA for the
-    logits (kept keys; every key, twice when the LSE is computed); the target Y = P V as two
-    bf16 products ("split2": P split into two bf16 halves, V exact in bf16); the Landweber steps
-    (two R x m x d products each) as three bf16 products of split float32 operands ("split3");
-    and VALU for the bias updates (matrix-vector products, priced at the float32 rate). Split
-    work is counted once in the totals and priced at two or three bf16 products."""
-    bf16 = f32 = split2 = split3 = 0.0
+def am_work(w, iters_beta: int, iters_v: int) -> dict:
+    """The work one Attention Matching fit does, by the units that do it, and the time it takes
+    at their peaks (the bound the fit is priced against):
+      bf16     MFMA FLOP on stored bf16 rows: every pass that re-forms E_ij = exp(c q_i.k_Cj - ME)
+               (the kept-logit maximum, E^T z, two per bias update, two for P_C) and the target's
+               logits over all n keys (twice when the fit computes the LSE itself);
+      split2   the target Y = P V, as two bf16 products (P split into halves, V exact);
+      split3   the value products on split float32 operands, three bf16 products each:
+               Z_0 = P_C V_0, the last P_C^T product, the symmetric Gram matrix of the smaller side
+               (N (N + 1) L FLOP) and one N x N x d product per further step;
+      exp      the exponentials of every re-formed E entry and of the target's weights, at the
+               transcendental rate (a quarter of the FMA rate);
+      valu     the float32 FMAs beside them (logit scaling and the row / column sums);
+      step_hbm the Gram matrix read once per step (float32 split, 4 bytes per entry), which bounds
+               those products instead of their MFMA work."""
+    bf16 = split2 = split3 = exps = valu = step_s_mfma = step_bytes = 0.0
     for s in range(w.S):
         n, m, R, d = w.n[s], w.m[s], w.R, w.d
-        bf16 += 2.0 * R * d * (m + n * (1 if w.lse_supplied else 2))
+        passes = 2 * iters_beta + 5
+        bf16 += 2.0 * R * d * (passes * m + n * (1 if w.lse_supplied else 2))
+        exps += (passes - 1) * R * m + R * n
+        valu += 4.0 * passes * R * m
         split2 += 2.0 * R * n * d
-        split3 += iters_v * 4.0 * R * m * d
-        f32 += (iters_beta + 1) * 4.0 * R * m
-    return {"bf16": bf16 * w.H, "split2": split2 * w.H, "split3": split3 * w.H, "f32": f32 * w.H}
+        if iters_v > 0:
+            rows_side = -(-R // 64) * 64 <= -(-m // 64) * 64
+            N, L = (R, m) if rows_side else (m, R)
+            split3 += 2 * 2.0 * R * m * d
+            if iters_v > 1:
+                split3 += N * (N + 1) * L
+                step = 2.0 * N * N * d * (iters_v - 1)
+                split3 += step
+                step_s_mfma += 3.0 * step / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                step_bytes += 4.0 * N * N * (iters_v - 1)
+    H = w.H
+    out = {"bf16": bf16 * H, "split2": split2 * H, "split3": split3 * H, "exp": exps * H, "valu": valu * H}
+    step_s_mfma *= H
+    step_s_hbm = step_bytes * H / (HBM_PEAK_GBPS * 1e9)
+    out["bound_s"] = ((out["bf16"] + 2.0 * out["split2"] + 3.0 * out["split3"]) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+                      - step_s_mfma + max(step_s_mfma, step_s_hbm)
+                      + out["exp"] / (F32_VALU_PEAK_TFLOPS * 1e12 / 8.0)
+                      + out["valu"] / (F32_VALU_PEAK_TFLOPS * 1e12))
+    return out
 
 
 # ---------------------------------------------------------------------------------- CPU baseline
@@ -570,14 +596,12 @@ def main():
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": gbps / HBM_PEAK_GBPS,
                      "bytes_per_launch": ab["score"]})
     if w.name == "am":  # the fit dominates: its kernels against the peak of the units they use
-        af = am_flops(w, *args.am_iters)
+        af = am_work(w, *args.am_iters)
         fit_s = st["am_fit"] * 1e-3
-        at_peak = ((af["bf16"] + 2.0 * af["split2"] + 3.0 * af["split3"]) / (MFMA_BF16_PEAK_TFLOPS * 1e12)
-                   + af["f32"] / (MFMA_F32_PEAK_TFLOPS * 1e12))
-        tot = af["bf16"] + af["split2"] + af["split3"] + af["f32"]
+        tot = af["bf16"] + af["split2"] + af["split3"] + af["valu"]
         roof = {"kernel": "kvc_am_fit (all of its kernels)", "bound": "mfma", "achieved": tot / fit_s / 1e12,
-                "peak": tot / at_peak / 1e12, "unit": "TFLOP/s", "frac": at_peak / fit_s, "traffic": None,
-                "flops_per_launch": af, "launch_ms": st["am_fit"],
+                "peak": tot / af["bound_s"] / 1e12, "unit": "TFLOP/s", "frac": af["bound_s"] / fit_s,
+                "traffic": None, "work_per_launch": af, "launch_ms": st["am_fit"],
                 "iters": {"beta": args.am_iters[0], "v": args.am_iters[1]}}
     line = {
         "metric": "compacted KV tokens/sec (score+select+compact) and % of peak HBM GB/s, 1 GPU",

@@ -27,13 +27,14 @@
 // buffers that one pass adds up in order), so a fit is reproducible bit for bit.
 //
 // Workspace of sequence i (floats, from T.off[i]; H heads, R rows, m = T.m[i], Rp = R and
-// ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 / S3 the split counts of the value
-// products, Np the padded rows of the iteration's side (Rp or ldm); every array starts on a
-// 256-byte boundary):
-//   P [H][R][ldm] | PT [H][ldm][Rp] | Y [H][R][128] | ZT [H][128][Rp] | VT [H][128][ldm] |
+// ldm = m rounded up to 64, NR = ceil(R / 64), S1 / S2 the split counts of the two P_C products,
+// St that of the target's keys,
+// Np the padded rows of the iteration's side (Rp or ldm); every array starts on a 256-byte
+// boundary):
+//   P [H][R][ldm] | PT [H][ldm][Rp] | Y [St][H][R][128] | ZT [H][128][Rp] | VT [H][128][ldm] |
 //   Zp [S1 > 1 ? S1 : 0][H][R][128] | Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] |
 //   b [H][ldm] | Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H] | Mg [H][Np][Np] |
-//   X, Sx [H][Np][128] | XT1 [H][128][Np] | Xp [S3 > 1 ? S3 : 0][H][Np][128] |
+//   X, Sx [H][Np][128] | XT1 [H][128][Np] |
 //   KC [H][ldk][128] bf16 (ldk = m rounded up to 256)
 // Columns m .. ldm-1 of P_C hold zeros, so tiles never need a column bound on it.
 #include <type_traits>
@@ -61,7 +62,7 @@ __host__ __device__ constexpr int64_t pad256(int64_t x) { return (x + 255) & ~in
 // (keys side) from step to step so that no product rewrites the operand it reads.
 struct AmWs {
   float *P, *PT, *Y, *ZT, *VT, *Zp, *Up, *part, *b, *M, *eta, *ME;
-  float *Mg, *X, *Sx, *XT1, *Xp;
+  float *Mg, *X, *Sx, *XT1;
   uint16_t* KC;  // the kept keys' rows, gathered: [H][ldk][128] bf16 (ldk = m rounded up to 256), zero rows from m
   uint32_t* mekey;
   int ldm, Rp, N, Np, ldk;
@@ -117,7 +118,7 @@ __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const
   w.P = ws + T.off[i];
   w.PT = w.P + pad64(H * R * ldm);
   w.Y = w.PT + pad64(H * ldm * Rp);
-  w.ZT = w.Y + pad64(H * R * kD);
+  w.ZT = w.Y + C.St * pad64(H * R * kD);
   w.VT = w.ZT + pad64(H * kD * Rp);
   w.Zp = w.VT + pad64(H * kD * ldm);
   w.Up = w.Zp + (C.S1 > 1 ? C.S1 : 0) * pad64(H * R * kD);
@@ -131,9 +132,8 @@ __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const
   w.X = w.Mg + pad64(H * Np * Np);
   w.Sx = w.X + pad64(H * Np * kD);
   w.XT1 = w.Sx + pad64(H * Np * kD);
-  w.Xp = w.XT1 + pad64(H * kD * Np);
   w.ldk = (int)pad256(m);
-  w.KC = reinterpret_cast<uint16_t*>(w.Xp + (C.S3 > 1 ? C.S3 : 0) * pad64(H * Np * kD));
+  w.KC = reinterpret_cast<uint16_t*>(w.XT1 + pad64(H * kD * Np));
   return w;
 }
 
@@ -149,16 +149,15 @@ __device__ __forceinline__ float key_float(uint32_t k) {
 }  // namespace
 
 // Floats of one sequence's workspace (the layout above).
-int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int S3) {
+int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int St) {
   (void)n;
   const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk, Rp = pad64(R);
   const int64_t Np = am_rows_side(R, m) ? Rp : ldm;
   const int64_t rk = pad64((int64_t)H * R * kD), xk = pad64((int64_t)H * Np * kD);
-  return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * ldm * Rp) + rk + pad64((int64_t)H * kD * Rp) +
+  return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * ldm * Rp) + St * rk + pad64((int64_t)H * kD * Rp) +
          pad64((int64_t)H * kD * ldm) + (S1 > 1 ? S1 : 0) * rk +
          (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) +
-         pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H) + pad64((int64_t)H * Np * Np) + 3 * xk +
-         (S3 > 1 ? S3 : 0) * xk + pad64((int64_t)H * pad256(m) * (kD / 2));
+         pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H) + pad64((int64_t)H * Np * Np) + 3 * xk + pad64((int64_t)H * pad256(m) * (kD / 2));
 }
 
 // Per unit, first: Mz = max_i LSE_i, and the kept-logit maximum reset. Work item = (seq, head).
@@ -665,21 +664,39 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
 
 // ------------------------------------------------------------------------------------------------
 // Target Y = P V with P_ij = exp(c q_i . k_j - LSE_i) over all n keys, without materialising P
-// (the weights of one 64-key chunk exist only in registers and a per-wave LDS tile).
-// Work item = (seq, head, 64-row tile), 8 waves: wave w owns rows 16 (w % 4) .. + 15 of the tile
-// and output columns 64 (w / 4) .. + 63 (the two halves recompute the same weights, a small
-// part of the work). Per 64-key chunk, staged through double-buffered LDS (keys as bf16 rows,
-// chunk c of row r at c ^ (r & 15); values transposed, one bf16 row of 64 keys per column):
-//   S = Q K^T     16 v_mfma_f32_16x16x32_bf16 (the wave's query rows stay in registers),
-//   P = exp2(S c log2(e) - LSE log2(e)), 0 for keys past n, through LDS into the A layout,
+// (the weights of one 64-key chunk exist only in registers).
+// Work item = (seq, head, 256-row block, key split): the keys are split C.St ways (contiguous
+// runs of 64-key chunks) into partial targets Y_t that the first value product adds in order;
+// a workgroup re-reads only its share of K and V, and there are C.St times as many of them.
+// Eight waves: wave w owns rows 32 w .. + 31 of the block (two 16-row fragments) and all 128
+// output columns. Per 64-key chunk, staged through double-buffered LDS (key and value rows alike
+// as bf16 rows, chunk c of row r at c ^ (r & 15)):
+//   S^T = K Q^T   per row fragment 16 v_mfma_f32_16x16x32_bf16 (the fragment's query rows stay in
+//                 registers as the B operand; a key fragment read serves both row fragments), so
+//                 lane (g, c16) holds row c16's logits of keys 16 sub + 4 g + x;
+//   P = exp2(S c log2(e) - LSE log2(e)), 0 for keys past n: the lane's eight weights of keys
+//                 32 s + {4 g .. 4 g + 3, 16 + 4 g .. 16 + 4 g + 3} are directly its A operand
+//                 of k-step s of the next product, with the contraction taken in that key order;
 //   Y += P V      P split as hi + lo (bf16 each; V is bf16 already, so the two products
-//                 P_hi V + P_lo V carry P to a relative 2^-16), 16 v_mfma_f32_16x16x32_bf16.
+//                 P_hi V + P_lo V carry P to a relative 2^-16), V's B operand read in the same
+//                 key order by ds_read_b64_tr_b16 (a transposing LDS read: within 16 lanes, lane
+//                 l's element x comes from the 8 bytes lane 4 x + l / 4 addresses, element l % 4,
+//                 so lanes addressing 4 consecutive values of 4 keys receive one value column
+//                 each) and used by both row fragments.
 // ------------------------------------------------------------------------------------------------
 namespace {
 constexpr int kTgtThreads = 512;
-constexpr int kVtPitch = 72;  // bf16 per transposed value row (64 keys + 8 padding)
-constexpr int kPPitch = 68;   // per-wave weight tile pitch (float32)
+constexpr int kTgtRows = 256;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
 
+// four consecutive bf16 values of one value column (keys k0 .. k0 + 3) for each lane of a
+// 16-lane group: lane j addresses key k0 + j / 4, columns col0 + 4 (j % 4) .. + 3
+__device__ __forceinline__ v4i16 tr_read(const uint8_t* rows, int k0, int col0, int j) {
+  const int key = k0 + (j >> 2), col = col0 + 4 * (j & 3);
+  const uint8_t* p = rows + swz(key, col >> 3) + 8 * ((col >> 2) & 1);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(__attribute__((address_space(3))) const void*)p);
+}
 }  // namespace
 
 template <int LAYOUT>
@@ -691,39 +708,42 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
                                                             const float* __restrict__ lse, float* __restrict__ ws,
                                                             int64_t n_max, float scale, AmCfg C, SeqTable T) {
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][64 * 256];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][kD * kVtPitch];
-  __shared__ __attribute__((aligned(16))) float Ps[8][16 * kPPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t Vs[2][64 * 256];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int n = T.n[i], s = T.first + i;
   const int H = C.H, R = C.R;
-  const int rt_n = (R + 63) / 64;
-  const int local = t - T.start[i];
-  const int h = local / rt_n, rt = local - h * rt_n;
+  const int rb_n = (R + kTgtRows - 1) / kTgtRows;
+  int local = t - T.start[i];
+  const int sp = local % C.St;
+  local /= C.St;
+  const int h = local / rb_n, rb = local - h * rb_n;
   const int64_t unit = (int64_t)s * H + h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int rw = wave & 3, dh = wave >> 2;
   AmWs W = am_ws(ws, T, i, C);
   const int32_t* map = LAYOUT == kPaged ? table + (int64_t)s * max_blocks
                                         : (LAYOUT == kSlots ? table + unit * n_max : nullptr);
   const int32_t* vmap = LAYOUT == kPaged ? vtable + (int64_t)s * vmax_blocks
                                          : (LAYOUT == kSlots ? vtable + unit * n_max : nullptr);
   const int kofs = T.kofs[i];
+  const int nch_all = (n + 63) / 64, per = (nch_all + C.St - 1) / C.St;
+  const int ch0 = sp * per, ch1 = min(nch_all, ch0 + per);
 
-  // query rows of this wave (A operand of S), and the LSE of the lane's four output rows
-  bf16x8 qa[4];
-  {
-    const int row = min(rt * 64 + 16 * rw + c16, R - 1);
-    const u32x4* qr = reinterpret_cast<const u32x4*>(q + (unit * R + row) * (int64_t)kD);
+  // query row c16 of each row fragment (B operand of S^T) and its LSE
+  bf16x8 qb[2][4];
+  float lb[2];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qa[ks] = as_bf16x8(qr[4 * ks + g]);
+  for (int rf = 0; rf < 2; ++rf) {
+    const int qrow = min(rb * kTgtRows + 32 * wave + 16 * rf + c16, R - 1);
+    const u32x4* qr = reinterpret_cast<const u32x4*>(q + (unit * R + qrow) * (int64_t)kD);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qb[rf][ks] = as_bf16x8(qr[4 * ks + g]);
+    lb[rf] = lse[unit * R + qrow] * kLog2e;
   }
-  float lb[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) lb[e] = lse[unit * R + min(rt * 64 + 16 * rw + 4 * g + e, R - 1)] * kLog2e;
   const float cl = scale * kLog2e;
 
-  // chunk staging: thread tid moves 16-byte piece tid & 15 of key rows tid >> 4 and 32 + (tid >> 4)
+  // chunk staging: thread tid moves 16-byte piece tid & 15 of key and value rows tid >> 4 and
+  // 32 + (tid >> 4)
   u32x4 kr[2], vr[2];
   auto load = [&](int c0) {
 #pragma unroll
@@ -739,70 +759,86 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
     for (int x = 0; x < 2; ++x) {
       const int key = x * 32 + (tid >> 4), ch = tid & 15;
       *reinterpret_cast<u32x4*>(&Ks[buf][swz(key, ch)]) = kr[x];
-      const uint32_t wd[4] = {vr[x].x, vr[x].y, vr[x].z, vr[x].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {  // values d = 8 ch + 2 e, 8 ch + 2 e + 1 of this key
-        Vt[buf][(8 * ch + 2 * e) * kVtPitch + key] = (uint16_t)(wd[e] & 0xffffu);
-        Vt[buf][(8 * ch + 2 * e + 1) * kVtPitch + key] = (uint16_t)(wd[e] >> 16);
-      }
+      *reinterpret_cast<u32x4*>(&Vs[buf][swz(key, ch)]) = vr[x];
     }
   };
 
-  f32x4 acc[4];
+  f32x4 acc[2][8];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  float* pw = Ps[wave];
-  const int nch = (n + 63) / 64;
-  load(0);
-  store(0);
-  __syncthreads();
+  for (int rf = 0; rf < 2; ++rf)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[rf][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (ch0 < ch1) {
+    load(ch0 * 64);
+    store(0);
+    __syncthreads();
+  }
 #pragma unroll 1
-  for (int ch = 0; ch < nch; ++ch) {
-    const int buf = ch & 1;
-    const bool more = ch + 1 < nch;
+  for (int ch = ch0; ch < ch1; ++ch) {
+    const int buf = (ch - ch0) & 1;
+    const bool more = ch + 1 < ch1;
     if (more) load((ch + 1) * 64);
     const uint8_t* kb = Ks[buf];
-    // S and the weights of 16 rows x 64 keys; lane (g, c16) holds rows 4g + e of key 16 sub + c16
+    const uint8_t* vb = Vs[buf];
+    // S^T and the weights: pw[rf][sub][x] is row c16's weight of key 64 ch + 16 sub + 4 g + x
+    float pw[2][4][4];
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      f32x4 sacc = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      f32x4 sacc[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        sacc = mfma16(qa[ks], *reinterpret_cast<const bf16x8*>(&kb[swz(16 * sub + c16, 4 * ks + g)]), sacc);
-      const bool live = ch * 64 + 16 * sub + c16 < n;
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&kb[swz(16 * sub + c16, 4 * ks + g)]);
+        sacc[0] = mfma16(ka, qb[0][ks], sacc[0]);
+        sacc[1] = mfma16(ka, qb[1][ks], sacc[1]);
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pw[(4 * g + e) * kPPitch + 16 * sub + c16] =
-            live ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[e], cl, -lb[e])) : 0.0f;
+      for (int x = 0; x < 4; ++x) {
+        const bool live = ch * 64 + 16 * sub + 4 * g + x < n;
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf)
+          pw[rf][sub][x] = live ? __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[rf][x], cl, -lb[rf])) : 0.0f;
+      }
     }
-    // Y += P V over the 64 keys in two steps of 32: lane group g takes keys 32 ks + 8 g .. + 7
-    const uint16_t* vb = Vt[buf];
+    // Y += P V over the 64 keys in two k-steps of 32 (keys 32 s + 4 g + x and 32 s + 16 + 4 g + x)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const float4* pr = reinterpret_cast<const float4*>(&pw[c16 * kPPitch + 32 * ks + 8 * g]);
-      const float4 p0 = pr[0], p1 = pr[1];
-      const float px[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
-      u32x4 ph, pl;
-      split8(px, ph, pl);
+      u32x4 ph[2], pl[2];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const bf16x8 vb8 = *reinterpret_cast<const bf16x8*>(&vb[(64 * dh + 16 * b + c16) * kVtPitch + 32 * ks + 8 * g]);
-        acc[b] = mfma16(as_bf16x8(ph), vb8, acc[b]);
-        acc[b] = mfma16(as_bf16x8(pl), vb8, acc[b]);
+      for (int rf = 0; rf < 2; ++rf) {
+        const float px[8] = {pw[rf][2 * ks][0],     pw[rf][2 * ks][1],     pw[rf][2 * ks][2],
+                             pw[rf][2 * ks][3],     pw[rf][2 * ks + 1][0], pw[rf][2 * ks + 1][1],
+                             pw[rf][2 * ks + 1][2], pw[rf][2 * ks + 1][3]};
+        split8(px, ph[rf], pl[rf]);
+      }
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const v4i16 v0 = tr_read(vb, 32 * ks + 4 * g, 16 * b, c16);
+        const v4i16 v1 = tr_read(vb, 32 * ks + 16 + 4 * g, 16 * b, c16);
+        const bf16x8 vv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int rf = 0; rf < 2; ++rf) {
+          acc[rf][b] = mfma16(as_bf16x8(ph[rf]), vv, acc[rf][b]);
+          acc[rf][b] = mfma16(as_bf16x8(pl[rf]), vv, acc[rf][b]);
+        }
       }
     }
     if (more) store(buf ^ 1);
     __syncthreads();
   }
-  float* out = W.Y + (int64_t)h * R * kD;
+  float* out = W.Y + sp * pad64((int64_t)H * R * kD) + (int64_t)h * R * kD;
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int rf = 0; rf < 2; ++rf)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = rt * 64 + 16 * rw + 4 * g + e;
-      if (r < R) out[(int64_t)r * kD + 64 * dh + 16 * b + c16] = acc[b][e];
-    }
+    for (int b = 0; b < 8; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = rb * kTgtRows + 32 * wave + 16 * rf + 4 * g + e;
+        if (r < R) out[(int64_t)r * kD + 16 * b + c16] = acc[rf][b][e];
+      }
 }
+
+// Row blocks of the target kernel.
+int am_target_blocks(int R) { return (R + kTgtRows - 1) / kTgtRows; }
 
 // ------------------------------------------------------------------------------------------------
 // The value fit's matrix products, one 128 x 128 output tile per workgroup (four waves in a 2 x 2
@@ -898,7 +934,7 @@ __device__ __forceinline__ void tile_mma(const float* arow, bool alive_a, const 
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------
-// The products of the value fit, split over S workgroups along the contraction whose partial
+// The P_C products of the value fit, split over S workgroups along the contraction whose partial
 // tiles a second pass (am_split_sum) adds in order:
 //   KIND 0: Z = P_C V0 - Y           (rows of P_C, contraction over kept keys)  -> Z, or partials Zp
 //           (rows side: also the iterate X = Z and its sum Sx = Z)
@@ -906,10 +942,6 @@ __device__ __forceinline__ void tile_mma(const float* arow, bool alive_a, const 
 //           the iterates when C.xsel = 1)                                      -> or partials Up
 //           mode 0: Vc -= eta P_C^T T (the last product of the rows side, or the only step)
 //           mode 1: X = Sx = P_C^T Z  (the first iterate of the keys side)
-//   KIND 2: one step of the iteration X <- X - eta Mg X, Sx += X           -> or partials Xp
-//           mode 0: the new iterate's transpose goes to the other buffer for the next step
-//           mode 1 (last step): rows side, Sx's transpose goes there for KIND 1;
-//                   keys side, Vc -= eta Sx
 // Work item = (seq, head, output tile, split), split fastest.
 // ------------------------------------------------------------------------------------------------
 template <int KIND>
@@ -922,8 +954,8 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   const int R = C.R;
   AmWs W = am_ws(ws, T, i, C);
   const int ldm = W.ldm, Np = W.Np;
-  const int S = KIND == 0 ? C.S1 : (KIND == 1 ? C.S2 : C.S3);
-  const int rows = KIND == 0 ? R : (KIND == 1 ? ldm : Np);  // output rows
+  const int S = KIND == 0 ? C.S1 : C.S2;
+  const int rows = KIND == 0 ? R : ldm;  // output rows
   const int tiles = (rows + kGTile - 1) / kGTile;
   int local = t - T.start[i];
   const int sp = local % S;
@@ -931,20 +963,17 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   const int tile = local % tiles, h = local / tiles;
   const int64_t unit = (int64_t)s * C.H + h;
   // A rows (pitch apitch) and B rows (the 128 columns of the right operand, pitch bpitch)
-  const int apitch = KIND == 0 ? ldm : (KIND == 1 ? W.Rp : Np);
-  const float* A = KIND == 0 ? W.P + (int64_t)h * R * ldm
-                             : (KIND == 1 ? W.PT + (int64_t)h * ldm * W.Rp : W.Mg + (int64_t)h * Np * Np);
-  const float* B = KIND == 0 ? W.VT + (int64_t)h * kD * ldm
-                             : (KIND == 1 ? (C.xsel ? W.XT1 : W.ZT) + (int64_t)h * kD * W.Rp
-                                          : am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel) + (int64_t)h * kD * Np);
+  const int apitch = KIND == 0 ? ldm : W.Rp;
+  const float* A = KIND == 0 ? W.P + (int64_t)h * R * ldm : W.PT + (int64_t)h * ldm * W.Rp;
+  const float* B = KIND == 0 ? W.VT + (int64_t)h * kD * ldm : (C.xsel ? W.XT1 : W.ZT) + (int64_t)h * kD * W.Rp;
   const int bpitch = apitch;
-  const int nst = KIND == 0 ? ldm / 32 : (KIND == 1 ? (R + 31) / 32 : Np / 32);
+  const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
   const int per = (nst + S - 1) / S;
   const int st0 = sp * per, st1 = min(nst, st0 + per);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int wr = wave >> 1, wc = wave & 1;
   const int arow = tile * kGTile + (tid >> 1);
-  const int alim = KIND == 0 ? R : (KIND == 1 ? ldm : Np);
+  const int alim = KIND == 0 ? R : ldm;
 
   f32x4 acc[4][4];
 #pragma unroll
@@ -955,7 +984,6 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
            acc, sm);
 
   const float eta = W.eta[h];
-  const int64_t xk = pad64((int64_t)C.H * Np * kD);
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -969,7 +997,12 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
           const int64_t o = (int64_t)h * R * kD + (int64_t)r * kD + col;
           if (S == 1) {
             if (r < W.Rp) {
-              const float z = r < R ? v - W.Y[o] : 0.0f;
+              float y = 0.0f;
+              if (r < R) {
+                y = W.Y[o];
+                for (int tp = 1; tp < C.St; ++tp) y += W.Y[tp * pad64((int64_t)C.H * R * kD) + o];
+              }
+              const float z = r < R ? v - y : 0.0f;
               put_split1(W.ZT + ((int64_t)h * kD + col) * W.Rp, r, z);
               if (W.rside && r < R) {
                 const int64_t ox = ((int64_t)h * Np + r) * kD + col;
@@ -980,7 +1013,7 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
           } else if (r < R) {
             W.Zp[(int64_t)sp * pad64((int64_t)C.H * R * kD) + o] = v;
           }
-        } else if constexpr (KIND == 1) {
+        } else {
           const int64_t o = (int64_t)r * kD + col;
           if (S == 1) {
             if (r < ldm) {
@@ -1003,29 +1036,160 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
           } else if (r < ldm) {
             W.Up[(int64_t)sp * pad64((int64_t)C.H * ldm * kD) + (int64_t)h * ldm * kD + o] = v;
           }
-        } else {  // one step of the iteration
-          if (S == 1) {
-            if (r < Np) {
-              const int64_t ox = ((int64_t)h * Np + r) * kD + col;
-              float xn = 0.0f, sum = 0.0f;
-              if (r < W.N) {
-                xn = W.X[ox] - eta * v;
-                sum = W.Sx[ox] + xn;
-                W.X[ox] = xn;
-                W.Sx[ox] = sum;
-              }
-              if (C.mode == 1 && !W.rside) {
-                if (r < m) vc_all[unit * C.m_max * (int64_t)kD + (int64_t)r * kD + col] -= eta * sum;
-              } else {
-                put_split1(am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel ^ 1) + ((int64_t)h * kD + col) * Np, r, C.mode == 1 ? sum : xn);
-              }
-            }
-          } else if (r < Np) {
-            W.Xp[(int64_t)sp * xk + ((int64_t)h * Np + r) * kD + col] = v;
-          }
         }
       }
 }
+
+// ------------------------------------------------------------------------------------------------
+// One step of the value iteration, X <- X - eta Mg X and Sx += X (the rows of the iteration's
+// side), with its epilogue fused: no split of the contraction, so no partial products. The
+// product is bound by reading Mg (4 bytes per entry, once per step); its right operand, the
+// iterate's transpose (split rows [128][Np]), is shared by all row tiles of a unit and read from
+// L2. One 64 x 128 output tile per workgroup of eight waves (wave w: rows 16 (w & 3) .. + 15,
+// columns 64 (w >> 2) .. + 63: four 16 x 16 accumulators), operands split as in am_gemm (three
+// bf16 products). The contraction runs in stages of 32 through a ring of kStepRing LDS slots
+// filled by LDS-DMA (global_load_lds_dwordx4, three per wave per stage) kStepRing - 2 stages
+// ahead (deep enough that the bytes in flight cover the memory latency at full rate): a
+// stage is 64 rows of Mg and the 128 rows of the transpose, 128 bytes per row (the 32 indices'
+// split groups: high half, low half), 16-byte chunk c of row r at position c ^ ((r >> 1) & 7),
+// so the 16 rows an MFMA operand reads hit distinct banks (the DMA lands each wave's 1 KB
+// contiguously, so the source address of a lane carries the permutation). Past the last stage
+// the ring is refilled with the last stage again (never read), which keeps three loads per wave
+// per stage and so the fixed wait counts exact.
+//   mode 0: the new iterate's transpose goes to the other buffer for the next step
+//   mode 1 (last step): rows side, Sx's transpose goes there for the last P_C^T product;
+//           keys side, Vc -= eta Sx
+// The tile leaves through LDS: X and Sx as float32 rows, the transpose as split rows.
+// Work item = (seq, head, 64-row tile of the side).
+// ------------------------------------------------------------------------------------------------
+namespace {
+constexpr int kStepRows = 64;
+constexpr int kStepThreads = 512;
+constexpr int kStepRing = 6;
+constexpr int kStepA = kStepRows * 128, kStepB = kGTile * 128, kStepSlot = kStepA + kStepB;
+__device__ __forceinline__ int sswz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }
+// Mg is stored as the step kernel reads it: per 64-row block and 32-column stage an 8 KB block of
+// 64 rows x 128 bytes (the four 8-column groups, high half then low half), 16-byte chunk c of
+// row r at position c ^ ((r >> 1) & 7); a stage of a row block is one contiguous read.
+__device__ __forceinline__ void mg_put8(float* mh, int Np, int r, int c, const float* x) {
+  u32x4 hi, lo;
+  split8(x, hi, lo);
+  const int row = r & (kStepRows - 1), grp = (c & 31) >> 3, sw = (row >> 1) & 7;
+  uint8_t* blk = reinterpret_cast<uint8_t*>(mh) + (((int64_t)(r / kStepRows) * (Np / 32) + (c >> 5)) << 13) + row * 128;
+  *reinterpret_cast<u32x4*>(blk + (((2 * grp) ^ sw) << 4)) = hi;
+  *reinterpret_cast<u32x4*>(blk + (((2 * grp + 1) ^ sw) << 4)) = lo;
+}
+// at most 12 of this wave's loads outstanding (the four later stages of the ring), then a barrier
+__device__ __forceinline__ void step_wait_barrier() {
+  static_assert(3 * (kStepRing - 2) == 12, "the wait count follows the ring depth");
+  asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+}  // namespace
+
+__global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
+                                                        SeqTable T) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kStepRing * kStepSlot];
+  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = find_seq(T, t);
+  const int m = T.m[i], s = T.first + i;
+  AmWs W = am_ws(ws, T, i, C);
+  const int Np = W.Np;
+  const int nb = Np / kStepRows;
+  const int local = t - T.start[i];
+  const int h = local / nb, blk = local - h * nb;
+  const int64_t unit = (int64_t)s * C.H + h;
+  const float* A = W.Mg + ((int64_t)h * Np + blk * kStepRows) * Np;  // the row block's stages, 8 KB each
+  const float* B = am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel) + (int64_t)h * kD * Np;
+  const int nst = Np / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int wr = wave & 3, wc = wave >> 2;
+  // this lane's DMA sources: the three 1 KB pieces (8 rows x 128 bytes) of a stage that wave w
+  // lands are pieces 3 w .. 3 w + 2 of the 24 (8 of A, then 16 of B); lane L lands row L / 8 of
+  // its piece at position L % 8. A is stored in that order already (a stage is 8 KB further on);
+  // for B the lane reads chunk (L % 8) ^ ((row >> 1) & 7) of its row (a stage is 32 floats on).
+  const u32x4* src[3];
+  int sstep[3];  // u32x4 per stage
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const int piece = 3 * wave + x;
+    if (piece < 8) {
+      src[x] = reinterpret_cast<const u32x4*>(A) + piece * 64 + lane;
+      sstep[x] = 512;
+    } else {
+      const int row = 8 * (piece - 8) + (lane >> 3);
+      src[x] = reinterpret_cast<const u32x4*>(B + (int64_t)row * Np) + ((lane & 7) ^ ((row >> 1) & 7));
+      sstep[x] = 8;
+    }
+  }
+  auto issue = [&](int stg) {
+    const int st = min(stg, nst - 1);
+    uint8_t* slot = sm + (stg % kStepRing) * kStepSlot;
+#pragma unroll
+    for (int x = 0; x < 3; ++x) dma16(src[x] + st * sstep[x], slot + (3 * wave + x) * 1024);
+  };
+  f32x4 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int stg = 0; stg < kStepRing - 1; ++stg) issue(stg);
+#pragma unroll 1
+  for (int stg = 0; stg < nst; ++stg) {
+    // this stage's loads are in: at most the later stages' loads (three each) are outstanding;
+    // the barrier also retires every wave's reads of the slot refilled next
+    step_wait_barrier();
+    issue(stg + kStepRing - 1);
+    const uint8_t* slot = sm + (stg % kStepRing) * kStepSlot;
+    const int ra = 16 * wr + c16;
+    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
+    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int rbw = 64 * wc + 16 * b + c16;
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g)]);
+      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g + 1)]);
+      acc[b] = mfma16(ah, bh, acc[b]);
+      acc[b] = mfma16(ah, bl, acc[b]);
+      acc[b] = mfma16(al, bh, acc[b]);
+    }
+  }
+  vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
+
+  // epilogue through LDS: the tile's new iterate in float32 rows of 128 (pitch 129)
+  float* tl = reinterpret_cast<float*>(sm);
+  static_assert(sizeof(sm) >= sizeof(float) * kStepRows * (kD + 1), "the epilogue tile fits the ring");
+  const float eta = W.eta[h];
+  const bool to_vc = C.mode == 1 && !W.rside;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rl = 16 * wr + 4 * g + e, r = blk * kStepRows + rl, col = 64 * wc + 16 * b + c16;
+      float out = 0.0f;
+      if (r < W.N) {
+        const int64_t ox = ((int64_t)h * Np + r) * kD + col;
+        const float xn = W.X[ox] - eta * acc[b][e];
+        const float sum = W.Sx[ox] + xn;
+        W.X[ox] = xn;
+        W.Sx[ox] = sum;
+        out = C.mode == 1 ? sum : xn;
+        if (to_vc && r < m) vc_all[unit * C.m_max * (int64_t)kD + (int64_t)r * kD + col] -= eta * sum;
+      }
+      tl[rl * (kD + 1) + col] = out;
+    }
+  if (to_vc) return;  // uniform across the block
+  __syncthreads();
+  float* dst = am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel ^ 1) + (int64_t)h * kD * Np + blk * kStepRows;
+  for (int qq = tid; qq < kD * (kStepRows / 8); qq += kStepThreads) {
+    const int d = qq >> 3, gq = qq & 7;
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = tl[(8 * gq + e) * (kD + 1) + d];
+    put_split8(dst + (int64_t)d * Np, gq, x);
+  }
+}
+
+// 64-row tiles of a step on an Np-row side.
+int64_t am_step_items(int Np) { return Np / kStepRows; }
 
 // Output tiles of the products: KIND 0 over the R rows, KIND 1 over the ldm kept keys, KIND 2
 // over the Np rows of the iteration's side.
@@ -1036,7 +1200,7 @@ int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 // contraction over the kept keys) or X = P_C^T (keys side: Np = ldm rows, contraction over the
 // proxy rows), stored as split rows [Np][Np]. Mg is symmetric: a workgroup forms the tile (a, b)
 // with a <= b and writes it and, off the diagonal, its transpose, both through LDS (the tile in
-// float32, pitch 129) as split rows. Rows and columns of X past its live rows are zero, so are
+// float32, pitch 129), in the blocked layout the step kernel reads (mg_put8). Rows and columns of X past its live rows are zero, so are
 // those of Mg. Work item = (seq, head, tile pair), pairs a-major.
 // ------------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(256, 2) void am_gram(float* __restrict__ ws, AmCfg C, SeqTable T) {
@@ -1084,7 +1248,7 @@ __global__ __launch_bounds__(256, 2) void am_gram(float* __restrict__ ws, AmCfg 
   for (int q = tid; q < kGTile * (kGTile / 8); q += 256) {
     const int r = q >> 4, gq = q & 15;
     if (a * kGTile + r < Np && b * kGTile + 8 * gq < Np)
-      put_split8(Mh + (int64_t)(a * kGTile + r) * Np + b * kGTile, gq, &tl[r * kPitch + 8 * gq]);
+      mg_put8(Mh, Np, a * kGTile + r, b * kGTile + 8 * gq, &tl[r * kPitch + 8 * gq]);
   }
   if (a != b) {
     for (int q = tid; q < kGTile * (kGTile / 8); q += 256) {
@@ -1093,7 +1257,7 @@ __global__ __launch_bounds__(256, 2) void am_gram(float* __restrict__ ws, AmCfg 
       float x[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[e] = tl[(8 * gq + e) * kPitch + c];
-      put_split8(Mh + (int64_t)(b * kGTile + c) * Np + a * kGTile, gq, x);
+      mg_put8(Mh, Np, b * kGTile + c, a * kGTile + 8 * gq, x);
     }
   }
 }
@@ -1108,8 +1272,6 @@ int64_t am_gram_items(int Np) {
 //   KIND 0: Z = sum_s Zp[s] - Y                       work item = (seq, head, 64 rows)
 //   KIND 1: mode 0: Vc_j -= eta sum_s Up[s]_j; mode 1: X = Sx = sum_s Up[s]
 //                                                     work item = (seq, head, 64 kept keys)
-//   KIND 2: X <- X - eta sum_s Xp[s], Sx += X, then as am_gemm's KIND 2
-//                                                     work item = (seq, head, 64 rows of the side)
 // The block's results (zeros past the live rows) are staged in LDS and leave as split rows of
 // the transpose, the form the next product reads; Vc and the iterates are also kept in float32.
 template <int KIND>
@@ -1122,19 +1284,15 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
   const int R = C.R;
   AmWs W = am_ws(ws, T, i, C);
   const int ldm = W.ldm, Np = W.Np;
-  const int nb = KIND == 0 ? (R + 63) / 64 : (KIND == 1 ? ldm / 64 : Np / 64);
+  const int nb = KIND == 0 ? (R + 63) / 64 : ldm / 64;
   const int local = t - T.start[i];
   const int h = local / nb, blk = local - h * nb;
-  const int lim = KIND == 0 ? R : (KIND == 1 ? m : W.N);
-  const int S = KIND == 0 ? C.S1 : (KIND == 1 ? C.S2 : C.S3);
+  const int lim = KIND == 0 ? R : m;
+  const int S = KIND == 0 ? C.S1 : C.S2;
   const int64_t unit = (int64_t)s * C.H + h;
-  const int64_t stride = KIND == 0 ? pad64((int64_t)C.H * R * kD)
-                                   : (KIND == 1 ? pad64((int64_t)C.H * ldm * kD) : pad64((int64_t)C.H * Np * kD));
-  const float* src = KIND == 0 ? W.Zp + (int64_t)h * R * kD
-                               : (KIND == 1 ? W.Up + (int64_t)h * ldm * kD : W.Xp + (int64_t)h * Np * kD);
+  const int64_t stride = KIND == 0 ? pad64((int64_t)C.H * R * kD) : pad64((int64_t)C.H * ldm * kD);
+  const float* src = KIND == 0 ? W.Zp + (int64_t)h * R * kD : W.Up + (int64_t)h * ldm * kD;
   const float eta = W.eta[h];
-  // keys side, last step: Vc takes the sum and no transpose is written
-  const bool to_vc = KIND == 2 && C.mode == 1 && !W.rside;
   for (int x = threadIdx.x; x < 64 * (kD / 4); x += 256) {
     const int row = blk * 64 + (x >> 5), c4 = x & 31;
     float4 val = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
@@ -1150,13 +1308,20 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
       }
       const int64_t ox = ((int64_t)h * Np + row) * kD + 4 * c4;
       if constexpr (KIND == 0) {
-        const float4 y = *reinterpret_cast<const float4*>(W.Y + (int64_t)h * R * kD + o);
+        float4 y = *reinterpret_cast<const float4*>(W.Y + (int64_t)h * R * kD + o);
+        for (int tp = 1; tp < C.St; ++tp) {  // the target's key splits, in order
+          const float4 yp = *reinterpret_cast<const float4*>(W.Y + tp * stride + (int64_t)h * R * kD + o);
+          y.x += yp.x;
+          y.y += yp.y;
+          y.z += yp.z;
+          y.w += yp.w;
+        }
         val = make_float4(a.x - y.x, a.y - y.y, a.z - y.z, a.w - y.w);
         if (W.rside) {
           *reinterpret_cast<float4*>(W.X + ox) = val;
           *reinterpret_cast<float4*>(W.Sx + ox) = val;
         }
-      } else if constexpr (KIND == 1) {
+      } else {
         if (C.mode == 0) {
           float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
           float4 v = *d;
@@ -1171,30 +1336,6 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
           *reinterpret_cast<float4*>(W.X + ox) = val;
           *reinterpret_cast<float4*>(W.Sx + ox) = val;
         }
-      } else {
-        float4* xp = reinterpret_cast<float4*>(W.X + ox);
-        float4* sp4 = reinterpret_cast<float4*>(W.Sx + ox);
-        float4 xn = *xp, sum = *sp4;
-        xn.x -= eta * a.x;
-        xn.y -= eta * a.y;
-        xn.z -= eta * a.z;
-        xn.w -= eta * a.w;
-        sum.x += xn.x;
-        sum.y += xn.y;
-        sum.z += xn.z;
-        sum.w += xn.w;
-        *xp = xn;
-        *sp4 = sum;
-        val = C.mode == 1 ? sum : xn;
-        if (to_vc) {
-          float4* d = reinterpret_cast<float4*>(vc_all + unit * C.m_max * (int64_t)kD + o);
-          float4 v = *d;
-          v.x -= eta * sum.x;
-          v.y -= eta * sum.y;
-          v.z -= eta * sum.z;
-          v.w -= eta * sum.w;
-          *d = v;
-        }
       }
     }
     float* tr = &tile[x >> 5][4 * c4];
@@ -1203,10 +1344,9 @@ __global__ __launch_bounds__(256) void am_split_sum(float* __restrict__ vc_all, 
     tr[2] = val.z;
     tr[3] = val.w;
   }
-  if (to_vc) return;  // uniform across the block
   __syncthreads();
-  const int pitch = KIND == 0 ? W.Rp : (KIND == 1 ? ldm : Np);
-  float* base = KIND == 0 ? W.ZT : (KIND == 1 ? W.VT : am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel ^ 1));
+  const int pitch = KIND == 0 ? W.Rp : ldm;
+  float* base = KIND == 0 ? W.ZT : W.VT;
   float* dst = base + (int64_t)h * kD * pitch + blk * 64;
   for (int q = threadIdx.x; q < kD * 8; q += 256) {
     const int d = q >> 3, gq = q & 7;
@@ -1332,8 +1472,12 @@ hipError_t launch_am_target(int layout, const void* q, const void* k, const void
 hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(256);
   if (kind == 0) am_gemm<0><<<grid, block, 0, st>>>(vc, ws, C, T);
-  else if (kind == 1) am_gemm<1><<<grid, block, 0, st>>>(vc, ws, C, T);
-  else am_gemm<2><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else am_gemm<1><<<grid, block, 0, st>>>(vc, ws, C, T);
+  return hipGetLastError();
+}
+
+hipError_t launch_am_step(float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
+  am_step<<<dim3(T.total), dim3(kStepThreads), 0, st>>>(vc, ws, C, T);
   return hipGetLastError();
 }
 
@@ -1345,8 +1489,7 @@ hipError_t launch_am_gram(float* ws, const AmCfg& C, const SeqTable& T, hipStrea
 hipError_t launch_am_split_sum(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
   dim3 grid(T.total), block(256);
   if (kind == 0) am_split_sum<0><<<grid, block, 0, st>>>(vc, ws, C, T);
-  else if (kind == 1) am_split_sum<1><<<grid, block, 0, st>>>(vc, ws, C, T);
-  else am_split_sum<2><<<grid, block, 0, st>>>(vc, ws, C, T);
+  else am_split_sum<1><<<grid, block, 0, st>>>(vc, ws, C, T);
   return hipGetLastError();
 }
 

@@ -54,7 +54,8 @@ hipError_t launch_valu_score_cached(const float2* ws, float* out, int H, int R, 
 hipError_t launch_evict_redirect(int32_t* slot_map, const int32_t* kept, int H, int64_t n_max, int m_max, int dead,
                                  const SeqTable& T, hipStream_t st);
 int redirect_tiles(int n);
-int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int S3);
+int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int St);
+int am_target_blocks(int R);
 int am_row_tiles(int R);
 int am_col_items(int m);
 int64_t am_key_tiles(int m);
@@ -70,6 +71,8 @@ hipError_t launch_am_target(int layout, const void* q, const void* k, const void
                             int64_t n_max, float scale, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_gram(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+hipError_t launch_am_step(float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st);
+int64_t am_step_items(int Np);
 hipError_t launch_am_gather(int layout, const void* k, const int32_t* table, int max_blocks, const int32_t* kept,
                             float* ws, int64_t n_max, const AmCfg& C, const SeqTable& T, hipStream_t st);
 hipError_t launch_am_bias(int mode, const void* q, const float* w, const float* lse, float* ws, float scale,
@@ -724,25 +727,21 @@ kvc_status kvc_evict_redirect(const kvc_shape* sh, const int32_t* kept, const in
 // ------------------------------------------------------------------------------------------------
 // Attention Matching
 // ------------------------------------------------------------------------------------------------
-// Split counts of the three value products (at most 8 splits, at least 4 stages of 32 per
-// split). A function of the shape alone, so that the workspace size and the fit agree.
+// Split counts of the two P_C products (at most 8 splits, at least 4 stages of 32 per split). A function of the shape alone, so that the workspace size and the fit agree.
 static int am_side_rows_padded(int R, int m) { return am_rows_side(R, m) ? (R + 63) / 64 * 64 : (m + 63) / 64 * 64; }
 
-static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2, int* S3) {
+static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2, int* St) {
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
-  int64_t t1 = 0, t2 = 0, t3 = 0, out1 = 0, out2 = 0, out3 = 0;
-  int st1 = INT32_MAX, st2 = am_stages_cols(R), st3 = INT32_MAX;
+  int64_t t1 = 0, t2 = 0, out1 = 0, out2 = 0;
+  int st1 = INT32_MAX, st2 = am_stages_cols(R);
   for (int s = 0; s < sh->num_seqs; ++s) {
     if (m[s] == 0) continue;
-    const int ldm = (m[s] + 63) / 64 * 64, Np = am_side_rows_padded(R, m[s]);
+    const int ldm = (m[s] + 63) / 64 * 64;
     t1 += (int64_t)H * am_gemm_tiles(R);
     t2 += (int64_t)H * am_gemm_tiles(ldm);
-    t3 += (int64_t)H * am_gemm_tiles(Np);
     out1 += (int64_t)H * R * 128;
     out2 += (int64_t)H * ldm * 128;
-    out3 += (int64_t)H * Np * 128;
     st1 = std::min(st1, am_stages_rows(m[s]));
-    st3 = std::min(st3, Np / 32);
   }
   // The split count that minimises rounds of workgroups (two per CU) x stages per split, plus
   // the round trip of the partial products through memory: each split writes the whole output
@@ -766,15 +765,26 @@ static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2, i
   };
   *S1 = pick(t1, st1, out1);
   *S2 = pick(t2, st2, out2);
-  *S3 = pick(t3, st3, out3);
+  // the target's key splits: enough workgroups for every CU (one each), at least four 64-key
+  // chunks per split
+  int64_t tt = 0;
+  int chunks = INT32_MAX;
+  for (int s = 0; s < sh->num_seqs; ++s) {
+    if (m[s] == 0) continue;
+    tt += (int64_t)H * am_target_blocks(R);
+    chunks = std::min(chunks, (sh->seq_lens[s] + 63) / 64);
+  }
+  int sp = 1;
+  while (sp < 8 && tt * sp < 256 && chunks / (2 * sp) >= 4) sp *= 2;
+  *St = sp;
 }
 
 static size_t am_bytes(const kvc_shape* sh, const int32_t* m) {
-  int S1, S2, S3;
-  am_splits(sh, m, &S1, &S2, &S3);
+  int S1, S2, St;
+  am_splits(sh, m, &S1, &S2, &St);
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
   int64_t f = 0;
-  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(H, R, sh->seq_lens[s], m[s], S1, S2, S3);
+  for (int s = 0; s < sh->num_seqs; ++s) f += am_seq_floats(H, R, sh->seq_lens[s], m[s], S1, S2, St);
   return ((size_t)f * sizeof(float) + 255) & ~size_t(255);
 }
 
@@ -817,13 +827,14 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int H = sh->num_kv_heads, R = sh->group * sh->num_queries;
   AmCfg C{H, R, m_max, 1, 1, 1, 0, 0};
-  am_splits(sh, m, &C.S1, &C.S2, &C.S3);
+  am_splits(sh, m, &C.S1, &C.S2, &C.St);
   // work items per sequence of every launch family; a sequence with m = 0 has nothing to fit and
   // gets no work items
   auto per = [&](auto&& f) { return [&, f](int s) -> int64_t { return m[s] ? (int64_t)H * f(s) : 0; }; };
   auto units = per([](int) -> int64_t { return 1; });
   auto cols = per([&](int s) -> int64_t { return am_col_items(m[s]); });
   auto rtiles = per([&](int) -> int64_t { return am_row_tiles(R); });
+  auto tblocks = per([&](int) -> int64_t { return (int64_t)am_target_blocks(R) * C.St; });
   auto ktiles = per([&](int s) { return am_key_tiles(m[s]); });
   auto gemm0 = per([&](int) -> int64_t { return (int64_t)am_gemm_tiles(R) * C.S1; });
   auto gemm1 = per([&](int s) -> int64_t { return (int64_t)am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; });
@@ -832,8 +843,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   auto side = [&](int s) { return am_rows_side(R, m[s]); };
   auto gram = per([&](int s) { return am_gram_items(am_side_rows_padded(R, m[s])); });
   auto gathers = per([&](int s) { return am_gather_items(m[s]); });
-  auto gemm2 = per([&](int s) -> int64_t { return (int64_t)am_gemm_tiles(am_side_rows_padded(R, m[s])) * C.S3; });
-  auto sum2 = per([&](int s) -> int64_t { return am_side_rows_padded(R, m[s]) / 64; });
+  auto steps = per([&](int s) { return am_step_items(am_side_rows_padded(R, m[s])); });
   auto ktile_items = [&](int s) -> int64_t { return (int64_t)am_gemm_tiles((m[s] + 63) / 64 * 64) * C.S2; };
   auto gemm1_rows = per([&](int s) -> int64_t { return side(s) ? ktile_items(s) : 0; });
   auto gemm1_keys = per([&](int s) -> int64_t { return side(s) ? 0 : ktile_items(s); });
@@ -845,13 +855,13 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
     if (!e) e = check_items(sh, units, what);
     if (!e) e = check_items(sh, cols, what);
     if (!e) e = check_items(sh, rtiles, what);
+    if (!e) e = check_items(sh, tblocks, what);
     if (!e) e = check_items(sh, ktiles, what);
     if (!e) e = check_items(sh, gemm0, what);
     if (!e) e = check_items(sh, gemm1, what);
     if (!e) e = check_items(sh, gram, what);
     if (!e) e = check_items(sh, gathers, what);
-    if (!e) e = check_items(sh, gemm2, what);
-    if (!e) e = check_items(sh, sum2, what);
+    if (!e) e = check_items(sh, steps, what);
     if (!e && !lse) e = check_lse_work(sh, k);
     if (e) return e;
   }
@@ -866,7 +876,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   int64_t acc = 0;
   for (int s = 0; s < sh->num_seqs; ++s) {
     off[s] = acc;
-    acc += am_seq_floats(H, R, sh->seq_lens[s], m[s], C.S1, C.S2, C.S3);
+    acc += am_seq_floats(H, R, sh->seq_lens[s], m[s], C.S1, C.S2, C.St);
   }
   auto offset = [&](int s) -> int64_t { return off[s]; };
   const int layout = layout_of(k);
@@ -900,7 +910,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
   //   keys side:  r_0 = P_C^T Z_0, r_{t+1} = r_t - eta (P_C^T P_C) r_t,   V_k = V_0 - eta sum_{t<k} r_t
   // (one step, k = 1, is the direct product for both).
   if (iters_v > 0) {
-    KVC_AM_STEP(rtiles, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
+    KVC_AM_STEP(tblocks, launch_am_target(layout, q, k->data, v->data, k->block_table, k->max_blocks, v->block_table,
                                          v->max_blocks, lse_rows, amws, nm, sh->scale, C, T, st));
     C.mode = 0;
     C.xsel = 0;
@@ -917,8 +927,7 @@ kvc_status kvc_am_fit(const kvc_shape* sh, const void* q, const kvc_kv_view* k, 
       for (int it = 1; it < iters_v; ++it) {
         C.xsel = (it - 1) & 1;
         C.mode = it == iters_v - 1;
-        KVC_AM_STEP(gemm2, launch_am_gemm(2, v_c, amws, C, T, st));
-        if (C.S3 > 1) KVC_AM_STEP(sum2, launch_am_split_sum(2, v_c, amws, C, T, st));
+        KVC_AM_STEP(steps, launch_am_step(v_c, amws, C, T, st));
       }
       C.mode = 0;  // rows side: V_k = V_0 - eta P_C^T (sum of the iterates), read from where the last step put it
       C.xsel = (iters_v - 1) & 1;
