@@ -1,10 +1,11 @@
 """Properties of the generated gfx950 device code that the kernels rely on but no GPU run can
-show: the LDS-DMA loads of the MFMA scoring passes (many rows and few rows) set M0 themselves in
-inline assembly, which is only sound while no compiler-generated instruction reads or writes M0
-in those kernels; their stage loops wait for the loads they need only (a compiler-placed vmcnt(0)
-inside the loop would also wait for the loads meant to stay in flight); and the few-row kernels,
-which count their LDS-DMA loads in fixed waits, issue no other vector-memory access between the
-first of those loads and the last wait."""
+show: the LDS-DMA loads of the MFMA scoring passes (many rows and few rows) and of the Attention
+Matching value step set M0 themselves in inline assembly, which is only sound while no
+compiler-generated instruction reads or writes M0 in those kernels; their stage loops wait for the
+loads they need only (a compiler-placed vmcnt(0) inside the loop would also wait for the loads
+meant to stay in flight); and the kernels that count their LDS-DMA loads in fixed waits (the
+few-row kernels, the value step) issue no other vector-memory access between the first of those
+loads and the last wait."""
 import os
 import re
 import subprocess
@@ -48,10 +49,15 @@ def small_asm():
     return _device_asm("score_small.hip")
 
 
-def test_m0_only_feeds_lds_dma(lse_asm, score_asm, small_asm):
+@pytest.fixture(scope="module")
+def am_asm():
+    return _device_asm("am.hip")
+
+
+def test_m0_only_feeds_lds_dma(lse_asm, score_asm, small_asm, am_asm):
     seen = 0
     for name, lines in list(_functions(lse_asm, "_ZN3kvc")) + list(_functions(score_asm, "_ZN3kvc")) + \
-            list(_functions(small_asm, "_ZN3kvc")):
+            list(_functions(small_asm, "_ZN3kvc")) + list(_functions(am_asm, "_ZN3kvc")):
         code = [l.strip() for l in lines if l.strip() and not l.strip().startswith((";", "."))]
         for i, l in enumerate(code):
             if re.search(r"\bm0\b", l):
@@ -153,3 +159,30 @@ def test_few_row_kernels_issue_only_their_dma_loads_before_the_last_wait(small_a
             assert code[i16 + 1] == "s_barrier"
             assert len([t for t in code[:i16] if t.startswith("global_load_lds_")]) == 19
     assert kernels == 6
+
+
+def test_value_step_issues_only_its_dma_loads_in_the_ring(am_asm):
+    """The value step's ring waits with a fixed count (three loads per wave per stage): between
+    its first LDS-DMA load and the wait for all of them, every vector-memory instruction on a
+    path is one of those loads, and the stage wait is vmcnt(12) followed by the barrier."""
+    (name, lines), = list(_functions(am_asm, "_ZN3kvc7am_step"))
+    blocks, succ = _blocks(lines)
+    body = dict(blocks)
+    first_b = next(lab for lab, b in blocks if any(t.startswith("global_load_lds_") for t in b))
+    last_b = next(lab for lab, b in blocks if any(t.startswith("s_waitcnt vmcnt(0) lgkmcnt(0)") for t in b)
+                  and lab in _reach(first_b, succ))
+    fwd = _reach(first_b, succ)
+    window = [lab for lab, _ in blocks if lab in fwd and last_b in _reach(lab, succ)]
+    code = []
+    for lab in window:
+        b = body[lab]
+        if lab == first_b:
+            b = b[next(i for i, t in enumerate(b) if t.startswith("global_load_lds_")):]
+        if lab == last_b:
+            b = b[:next(i for i, t in enumerate(b) if t.startswith("s_waitcnt vmcnt(0) lgkmcnt(0)"))]
+        code += b
+    other = [t for t in code if re.match(r"(global|buffer|flat|scratch)_", t) and not t.startswith("global_load_lds_")]
+    assert not other, f"{name}: other vector-memory accesses among the counted loads: {other[:3]}"
+    assert all(t.startswith("global_load_lds_dwordx4") for t in code if t.startswith("global_load_lds_"))
+    i12 = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(12)"))
+    assert code[i12 + 1] == "s_barrier"
