@@ -140,15 +140,38 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // 16-byte-per-lane LDS-DMA loads (4 key rows each, the lane's chunk chosen so the rows land
   // XOR-swizzled) plus, with a bias, one 4-byte load of its 16 keys' bias. Keys past the chunk
   // load the chunk's last row (finite bytes, masked in the epilogue).
+  // paged, a full stage: lane row j's key is 64 st further on, so its block-table slot moves by 4
+  // per stage and its place inside the block (and so its offset past the block's start) stays
+  int slot0[4], loff[4];
+  if constexpr (LAYOUT == kPaged) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = (wave * 4 + j) * 4 + (lane >> 4), pos = ko + kbeg + row;
+      slot0[j] = (pos >> 4) - blk0;
+      loff[j] = ((pos & 15) * H + h) * (kHeadDim / 8) + ((lane & 15) ^ (row & 15));
+    }
+  }
   auto issue = [&](int st) {
     const int k0 = kbeg + st * kStage;
     const int b = st % kLseBufs;
+    // the four sources first (their table entries are LDS reads that then complete together),
+    // then the four loads
+    const u32x4* src[4];
+    if (LAYOUT == kPaged && k0 + kStage <= kend) {
+      const u32x4* pool = reinterpret_cast<const u32x4*>(k);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = (wave * 4 + j) * 4 + (lane >> 4);
-      const int key = min(k0 + row, kend - 1);
-      dma16(key_ptr(key) + ((lane & 15) ^ (row & 15)), &ks_[b][(wave * 4 + j) * 1024]);
+      for (int j = 0; j < 4; ++j)
+        src[j] = pool + (int64_t)idx[slot0[j] + 4 * st] * (16 * H * (kHeadDim / 8)) + loff[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = (wave * 4 + j) * 4 + (lane >> 4);
+        const int key = min(k0 + row, kend - 1);
+        src[j] = key_ptr(key) + ((lane & 15) ^ (row & 15));
+      }
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(src[j], &ks_[b][(wave * 4 + j) * 1024]);
     if constexpr (BIAS) {
       if (lane < 16) dma4(bias + (int64_t)s * n_max + min(k0 + wave * 16 + lane, kend - 1), &kts[b][wave * 16]);
     }
@@ -157,9 +180,9 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // Per row: a reference exponent mref (a logit in log2 units seen earlier in the chunk, or -1e30
   // before the first) and the running sum of 2^(x - mref). A stage first runs the cheap form (one
   // FMA, one exp2 and one add per logit against the current mref) into stage sums; if any lane's
-  // stage sum leaves [0, 2^64] (a logit rose more than about 60 above its mref, which includes the
-  // first stage) the whole wave discards them and redoes the stage exactly, moving mref to every
-  // new maximum. Terms never exceed 2^64 and the largest one seen is at least 1, so the dominant
+  // stage sum leaves [0, 2^64] (a logit rose more than about 60 above its mref) the whole wave
+  // discards them and redoes the stage exactly, moving mref to every new maximum. The wave's
+  // first stage, which has no reference yet, takes the exact form directly. Terms never exceed 2^64 and the largest one seen is at least 1, so the dominant
   // terms neither overflow nor underflow.
   float mref[kSub], ssum[kSub];
 #pragma unroll
@@ -202,46 +225,53 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     return t4;
   };
   auto row_pos = [&](int sub) -> int { return pls[wave * kPerWave + sub * 16 + c16]; };
+  // The wave's first stage has no reference yet and runs the exact form at once.
+  bool fresh = true;
   auto stage = [&](int buf, int k0, auto masked, auto causal) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr bool CM = decltype(causal)::value;  // mask element by element (rows near the keys)
     // a masked tile is formed in halves, so that the row positions fit beside the accumulators
     constexpr int NH = CM ? 2 : 1, NS = kSub / NH;
-    float sst[kSub];
+    const bool exact = fresh;
+    fresh = false;
+    if (!exact) {
+      float sst[kSub];
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub) sst[sub] = 0.0f;
+      for (int sub = 0; sub < kSub; ++sub) sst[sub] = 0.0f;
 #pragma unroll 1
-    for (int kt = 0; kt < kStage / 16; ++kt) {
-      f32x4 kt4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      if constexpr (MASK) kt4 = key_term(buf, k0, kt);
+      for (int kt = 0; kt < kStage / 16; ++kt) {
+        f32x4 kt4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (MASK) kt4 = key_term(buf, k0, kt);
 #pragma unroll
-      for (int hh = 0; hh < NH; ++hh) {
-        f32x4 acc[NS];
-        tile_acc(buf, kt, hh * NS, acc);
+        for (int hh = 0; hh < NH; ++hh) {
+          f32x4 acc[NS];
+          tile_acc(buf, kt, hh * NS, acc);
 #pragma unroll
-        for (int s2 = 0; s2 < NS; ++s2) {
-          const int sub = hh * NS + s2;
-          // (CM) how far past the lane's first key of the tile the row still sees
-          const int lim = CM ? row_pos(sub) - (k0 + kt * 16 + 4 * g) : 0;
+          for (int s2 = 0; s2 < NS; ++s2) {
+            const int sub = hh * NS + s2;
+            // (CM) how far past the lane's first key of the tile the row still sees
+            const int lim = CM ? row_pos(sub) - (k0 + kt * 16 + 4 * g) : 0;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float x = MASK ? __builtin_fmaf(acc[s2][j], c2, kt4[j]) - mref[sub]
-                           : __builtin_fmaf(acc[s2][j], c2, -mref[sub]);
-            if constexpr (CM) x = j > lim ? -INFINITY : x;
-            sst[sub] += __builtin_amdgcn_exp2f(x);
+            for (int j = 0; j < 4; ++j) {
+              float x = MASK ? __builtin_fmaf(acc[s2][j], c2, kt4[j]) - mref[sub]
+                             : __builtin_fmaf(acc[s2][j], c2, -mref[sub]);
+              if constexpr (CM) x = j > lim ? -INFINITY : x;
+              sst[sub] += __builtin_amdgcn_exp2f(x);
+            }
           }
         }
       }
-    }
-    float mx = sst[0];
+      float mx = sst[0];
 #pragma unroll
-    for (int sub = 1; sub < kSub; ++sub) mx = fmaxf(mx, sst[sub]);
-    if (__builtin_amdgcn_ballot_w64(!(mx <= kLazyLimit)) == 0) {
+      for (int sub = 1; sub < kSub; ++sub) mx = fmaxf(mx, sst[sub]);
+      if (__builtin_amdgcn_ballot_w64(!(mx <= kLazyLimit)) == 0) {
 #pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) ssum[sub] += sst[sub];
-      return;
+        for (int sub = 0; sub < kSub; ++sub) ssum[sub] += sst[sub];
+        return;
+      }
     }
-    // rare, wave-uniform: exact redo with the reference moved to every new maximum
+    // the first stage, or (rare, wave-uniform) an exact redo: the reference moves to every new
+    // maximum
 #pragma unroll 1
     for (int kt = 0; kt < kStage / 16; ++kt) {
       const f32x4 kt4 = key_term(buf, k0, kt);
