@@ -123,3 +123,17 @@ def test_am_value_iteration_on_either_side(iters_v):
     say(f"[case] am sides: R={w.R} n={list(w.n)} m={m} iterations 4 + {iters_v}")
     beta, vc = _run(w, data, kept, m, 4, iters_v)
     _check(w, data, kept, m, beta, vc, 4, iters_v, tag=f"sides v{iters_v}")
+
+
+def test_am_target_key_splits_with_a_ragged_tail():
+    """2048 proxy rows over 4000 keys (63 chunks of 64, the last one partial): the target's keys
+    are split eight ways (seven runs of 8 chunks, one of 7), and the partial targets are added in
+    order by the first value product; 12 + 12 iterations."""
+    w = W.custom("am_ragged", 174, S=1, H=1, G=4, q=512, n=(4000,), dtype="bf16", keys="mixture",
+                 queries="cluster")
+    data = W.build_contiguous(w)
+    m = [801]
+    kept = _kept(np.random.default_rng(9), w, m)
+    say(f"[case] am ragged splits: R={w.R} n={w.n[0]} m={m[0]}")
+    beta, vc = _run(w, data, kept, m, 12, 12)
+    _check(w, data, kept, m, beta, vc, 12, 12, tag="ragged")
