@@ -137,3 +137,38 @@ def test_am_target_key_splits_with_a_ragged_tail():
     say(f"[case] am ragged splits: R={w.R} n={w.n[0]} m={m[0]}")
     beta, vc = _run(w, data, kept, m, 12, 12)
     _check(w, data, kept, m, beta, vc, 12, 12, tag="ragged")
+
+
+def test_am_on_a_segment_of_a_longer_cache():
+    """The fit over one turn inside a longer contiguous cache (seq_starts): keys, values and
+    kept positions are the segment's, [start, start + n); the oracle runs on the sliced rows."""
+    P = _P()
+    import online_compaction_amd as oc
+    w = W.custom("am_segment", 175, S=2, H=2, G=4, q=8, n=(600, 600), dtype="bf16", keys="mixture",
+                 queries="cluster")
+    data = W.build_contiguous(w)
+    starts, lens, m = [150, 40], [300, 129], [60, 31]
+    kept = np.zeros((w.S, w.H, max(m)), dtype=np.int32)
+    rng = np.random.default_rng(11)
+    for s in range(w.S):
+        for h in range(w.H):
+            kept[s, h, :m[s]] = np.sort(rng.choice(lens[s], size=m[s], replace=False))
+    kv = oc.KView(P.device_tensor(data["K"]), oc.KVC_BF16)
+    vv = oc.KView(P.device_tensor(data["V"]), oc.KVC_BF16)
+    shape = oc.Shape(w.S, w.H, w.G, w.q, w.d, w.n_max, np.array(lens, dtype=np.int32), w.logit_scale,
+                     seq_starts=np.array(starts, dtype=np.int32))
+    m_max = max(m)
+    beta = torch.full((w.S, w.H, m_max), 7.0, dtype=torch.float32, device="cuda")
+    vc = torch.full((w.S, w.H, m_max, w.d), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(256, oc.kvc_am_workspace_size(shape, kv, vv, m, False)), dtype=torch.uint8, device="cuda")
+    say(f"[case] am segment: starts={starts} n={lens} m={m} R={w.R}")
+    oc.kvc_am_fit(shape, P.device_tensor(data["Q"]), kv, vv, None, P.device_tensor(kept), m, m_max, 8, 8, beta, vc, ws)
+    torch.cuda.synchronize()
+    beta, vc = beta.cpu().numpy(), vc.cpu().numpy()
+    for s in range(w.S):
+        a, n = starts[s], lens[s]
+        for h in range(w.H):
+            err = check_am_unit(O.unit_rows(data["Q"], s, h, w.G), data["K"][s, h, a:a + n], data["V"][s, h, a:a + n],
+                                None, kept[s, h, :m[s]], beta[s, h], vc[s, h], w.dtype, w.logit_scale, 8, 8,
+                                f"segment s={s} h={h}")
+            say(f"[ok] am segment s={s} h={h}: " + ", ".join(f"{k} {v:.3g}" for k, v in err.items()))
