@@ -1079,10 +1079,11 @@ __device__ __forceinline__ void mg_put8(float* mh, int Np, int r, int c, const f
   *reinterpret_cast<u32x4*>(blk + (((2 * grp) ^ sw) << 4)) = hi;
   *reinterpret_cast<u32x4*>(blk + (((2 * grp + 1) ^ sw) << 4)) = lo;
 }
-// at most 12 of this wave's loads outstanding (the four later stages of the ring), then a barrier
+// at most 6 of this wave's loads outstanding (the two stages after the pair to compute), then a
+// barrier
 __device__ __forceinline__ void step_wait_barrier() {
-  static_assert(3 * (kStepRing - 2) == 12, "the wait count follows the ring depth");
-  asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(kStepRing == 6, "the wait count follows the ring depth");
+  asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 }  // namespace
 
@@ -1130,14 +1131,7 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   f32x4 acc[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int stg = 0; stg < kStepRing - 1; ++stg) issue(stg);
-#pragma unroll 1
-  for (int stg = 0; stg < nst; ++stg) {
-    // this stage's loads are in: at most the later stages' loads (three each) are outstanding;
-    // the barrier also retires every wave's reads of the slot refilled next
-    step_wait_barrier();
-    issue(stg + kStepRing - 1);
+  auto compute = [&](int stg) {
     const uint8_t* slot = sm + (stg % kStepRing) * kStepSlot;
     const int ra = 16 * wr + c16;
     const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
@@ -1151,6 +1145,19 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
       acc[b] = mfma16(ah, bl, acc[b]);
       acc[b] = mfma16(al, bh, acc[b]);
     }
+  };
+  // Two stages per barrier: at the top of the iteration for stages s and s + 1 (s even), both have
+  // landed (only stages s + 2 and s + 3, six loads, may be outstanding) and every wave is past its
+  // reads of stages s - 2 and s - 1, whose slots take stages s + 4 and s + 5.
+#pragma unroll
+  for (int stg = 0; stg < 4; ++stg) issue(stg);
+#pragma unroll 1
+  for (int stg = 0; stg < nst; stg += 2) {
+    step_wait_barrier();
+    issue(stg + 4);
+    issue(stg + 5);
+    compute(stg);
+    if (stg + 1 < nst) compute(stg + 1);
   }
   vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
 
