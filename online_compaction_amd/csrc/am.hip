@@ -313,9 +313,9 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
                                                         float scale, AmCfg C, SeqTable T) {
   constexpr bool kW = MODE == 1 || MODE == 2;  // the pass needs w
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBiasStep * 256];
-  __shared__ float ws_l[2][kBiasStep];
+  __shared__ float ws_l[2][kBiasThreads];  // w of the step's keys (entries 256 .. 511 unused)
   __shared__ float rsum[4][64];          // row sums of the four key quarters
-  __shared__ float xpart[2][kBiasStep];  // column partials of the odd waves, per step parity
+  __shared__ float xpart[2][2][kBiasStep];  // column partials per step parity and wave parity
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
@@ -341,24 +341,33 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
     for (int ks = 0; ks < 4; ++ks) qa[rg][ks] = as_bf16x8(qr[4 * ks + g]);
   }
 
-  // staging of step st: key rows 256 st .. + 255, 8 pieces of 16 bytes per thread
-  u32x4 kr[8];
-  float wr = 0.0f;
-  auto load = [&](int st) {
+  // Staging of key rows 256 st .. + 255 into buffer buf by LDS-DMA: wave w lands the 1 KB pieces
+  // 8 w .. 8 w + 7 (four key rows each), lane L row 4 p + L / 16 of piece p at chunk position
+  // L % 16, so it reads chunk (L % 16) ^ (row & 15) of that row (the layout swz reads). The w of
+  // the step's keys comes through a register (0 past m) and is written by land(), which waits for
+  // every load of the step and ends with the barrier.
+  // (row & 15 repeats every four pieces: piece x + 4 is 16 rows, 256 chunks, further on)
+  int koff[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) kr[x] = kc[(int64_t)st * kBiasStep * 16 + x * kBiasThreads + tid];
-    if (kW && tid < kBiasStep) {
-      const int j = st * kBiasStep + tid;
-      wr = j < m ? wu[j] : 0.0f;
+  for (int x = 0; x < 4; ++x) {
+    const int row = 4 * (8 * wave + x) + (lane >> 4);
+    koff[x] = row * 16 + ((lane & 15) ^ (row & 15));
+  }
+  float wr = 0.0f;
+  auto issue = [&](int st, int buf) {
+    const u32x4* src = kc + (int64_t)st * kBiasStep * 16;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) dma16(src + koff[x & 3] + 256 * (x >> 2), &Ks[buf][(8 * wave + x) * 1024]);
+    if constexpr (kW) {  // every thread loads (clamped), so the step stays free of branches
+      const int j = st * kBiasStep + (tid & (kBiasStep - 1));
+      const float x = wu[min(j, m - 1)];
+      wr = j < m ? x : 0.0f;
     }
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int q16 = x * kBiasThreads + tid;
-      *reinterpret_cast<u32x4*>(&Ks[buf][swz(q16 >> 4, q16 & 15)]) = kr[x];
-    }
-    if (kW && tid < kBiasStep) ws_l[buf][tid] = wr;
+  auto land = [&](int buf) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (kW) ws_l[buf][tid] = wr;
+    __syncthreads();
   };
   // The kept-logit MFMAs of a step (this wave's 32 rows x its 64-key tile of buffer buf;
   // acc[sub][rg] holds rows rb + 16 rg + 4 g + x, key 256 st + 64 kq + 16 sub + c16, and wv[sub]
@@ -367,34 +376,40 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
   // which the step barrier keeps in phase, still overlap their MFMAs with vector work.
   auto mma = [&](int buf, f32x4 (&acc)[4][2], float (&wv)[4]) {
     const uint8_t* kb = Ks[buf];
+    // the key fragments of k-step ks + 1 are read while those of ks feed the MFMAs
+    bf16x8 b[2][4];
+    auto frag = [&](int ks, bf16x8 (&f)[4]) {
 #pragma unroll
-    for (int sub = 0; sub < 4; ++sub) acc[sub][0] = acc[sub][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int sub = 0; sub < 4; ++sub) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&kb[swz(64 * kq + 16 * sub + c16, 4 * ks + g)]);
-        acc[sub][0] = mfma16(qa[0][ks], b, acc[sub][0]);
-        acc[sub][1] = mfma16(qa[1][ks], b, acc[sub][1]);
-      }
+      for (int sub = 0; sub < 4; ++sub)
+        f[sub] = *reinterpret_cast<const bf16x8*>(&kb[swz(64 * kq + 16 * sub + c16, 4 * ks + g)]);
+    };
+    frag(0, b[0]);
     if constexpr (kW) {
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) wv[sub] = ws_l[buf][64 * kq + 16 * sub + c16];
     }
+#pragma unroll
+    for (int sub = 0; sub < 4; ++sub) acc[sub][0] = acc[sub][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) frag(ks + 1, b[(ks + 1) & 1]);
+#pragma unroll
+      for (int sub = 0; sub < 4; ++sub) {
+        acc[sub][0] = mfma16(qa[0][ks], b[ks & 1][sub], acc[sub][0]);
+        acc[sub][1] = mfma16(qa[1][ks], b[ks & 1][sub], acc[sub][1]);
+      }
+    }
   };
-  // E = exp(c q.k - ME) of a step's accumulators, 0 past m when the step reaches it
+  // E = exp(c q.k - ME) of a step's accumulators, 0 past m: a key past m is a zero row of KC, so
+  // its logits are exactly 0 and an offset of -inf in place of -ME makes its E exactly 0
   auto expo = [&](int st, const f32x4 (&acc)[4][2], float (&e)[4][2][4]) {
-    const bool tail = (st + 1) * kBiasStep > m;
 #pragma unroll
     for (int sub = 0; sub < 4; ++sub) {
-      const bool live = st * kBiasStep + 64 * kq + 16 * sub + c16 < m;
+      const float off = st * kBiasStep + 64 * kq + 16 * sub + c16 < m ? -mb : -INFINITY;
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float v = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[sub][rg][x], cl, -mb));
-          e[sub][rg][x] = (tail && !live) ? 0.0f : v;
-        }
+        for (int x = 0; x < 4; ++x) e[sub][rg][x] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[sub][rg][x], cl, off));
     }
   };
   auto interleave = [] {
@@ -434,13 +449,12 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
   if constexpr (MODE == 3) {
     // the largest kept logit c q_i . k_Cj over the tile's rows and the live keys
     float lmax = -INFINITY;
-    load(0);
-    store(0);
-    __syncthreads();
+    issue(0, 0);
+    land(0);
 #pragma unroll 1
     for (int st = 0; st < nsteps; ++st) {
       const bool more = st + 1 < nsteps;
-      if (more) load(st + 1);
+      if (more) issue(st + 1, (st + 1) & 1);
       mma(st & 1, acc0, wv0);
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
@@ -451,16 +465,15 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
           for (int x = 0; x < 4; ++x)
             if (live) lmax = fmaxf(lmax, acc0[sub][rg][x] * scale);
       }
-      if (more) store((st + 1) & 1);
-      __syncthreads();
+      land((st + 1) & 1);
     }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, o));
-    if (lane == 0) xpart[0][wave] = lmax;
+    if (lane == 0) xpart[0][0][wave] = lmax;
     __syncthreads();
     if (tid == 0) {
-      float bm = xpart[0][0];
-      for (int x = 1; x < kBiasThreads / 64; ++x) bm = fmaxf(bm, xpart[0][x]);
+      float bm = xpart[0][0][0];
+      for (int x = 1; x < kBiasThreads / 64; ++x) bm = fmaxf(bm, xpart[0][0][x]);
       const uint32_t key = float_key(bm);
       if (bm > -INFINITY && key > __atomic_load_n(W.mekey + h, __ATOMIC_RELAXED)) atomicMax(W.mekey + h, key);
     }
@@ -481,28 +494,34 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
 #pragma unroll
           for (int x = 0; x < 4; ++x) up[rg][x] = __builtin_fmaf(e[sub][rg][x], wv[sub], up[rg][x]);
     };
-    // step st: loads of st + 1 in flight, MFMAs of st, sums of st - 1, then st + 1 staged
+    // step st >= 1: loads of st + 1 in flight, MFMAs of st beside the sums of st - 1 (one basic
+    // block, so the scheduler can interleave them), then st + 1 staged; step 0 has no sums
+    // (the last step stages its own keys again into the free buffer: no branch in the loop body)
     auto step = [&](int st, f32x4 (&cur)[4][2], float (&wc)[4], f32x4 (&prev)[4][2], float (&wp)[4]) {
-      const bool more = st + 1 < nsteps;
-      if (more) load(st + 1);
+      issue(min(st + 1, nsteps - 1), (st + 1) & 1);
       mma(st & 1, cur, wc);
-      if (st > 0) {
-        post(st - 1, prev, wp);
-        interleave();
-      }
-      if (more) store((st + 1) & 1);
-      __syncthreads();
+      post(st - 1, prev, wp);
+      interleave();
+      land((st + 1) & 1);
     };
-    load(0);
-    store(0);
-    __syncthreads();
+    issue(0, 0);
+    land(0);
+    issue(min(1, nsteps - 1), 1);
+    mma(0, acc0, wv0);
+    land(1);
+    // two steps per iteration with no branch between them (odd steps in acc1, even in acc0)
+    int st = 1;
 #pragma unroll 1
-    for (int st = 0; st < nsteps; st += 2) {
-      step(st, acc0, wv0, acc1, wv1);
-      if (st + 1 < nsteps) step(st + 1, acc1, wv1, acc0, wv0);
+    for (; st + 1 < nsteps; st += 2) {
+      step(st, acc1, wv1, acc0, wv0);
+      step(st + 1, acc0, wv0, acc1, wv1);
     }
-    if (nsteps & 1) post(nsteps - 1, acc0, wv0);
-    else post(nsteps - 1, acc1, wv1);
+    if (st < nsteps) {
+      step(st, acc1, wv1, acc0, wv0);
+      post(st, acc1, wv1);
+    } else {
+      post(nsteps - 1, acc0, wv0);
+    }
     // reduce over the 16 keys of each lane row (c16), then add the four key quarters in order
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg)
@@ -548,14 +567,13 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
     // and out as split rows of P_C (8 keys per group) and of P_C^T (8 rows per group)
     float* Pu = W.P + (int64_t)h * R * W.ldm;
     float* PTu = W.PT + (int64_t)h * W.ldm * W.Rp;
-    load(0);
-    store(0);
-    __syncthreads();
+    issue(0, 0);
+    land(0);
 #pragma unroll 1
     for (int st = 0; st < nsteps; ++st) {
       const int buf = st & 1;
       const bool more = st + 1 < nsteps;
-      if (more) load(st + 1);
+      if (more) issue(st + 1, buf ^ 1);
       mma(buf, acc0, wv0);
       float e[4][2][4];
       expo(st, acc0, e);
@@ -567,11 +585,11 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
           for (int x = 0; x < 4; ++x) e[sub][rg][x] = e[sub][rg][x] * wv0[sub] * rv[rg][x];
       const float ones[2][4] = {{1.0f, 1.0f, 1.0f, 1.0f}, {1.0f, 1.0f, 1.0f, 1.0f}};
       const float gsum = colsum(e, ones);
-      if (wave & 1) xpart[buf][64 * kq + lane] = gsum;
+      if (wave & 1) xpart[buf][1][64 * kq + lane] = gsum;
       __syncthreads();  // every wave is done with the step's keys
       if (!(wave & 1)) {
         const int j = st * kBiasStep + 64 * kq + lane;
-        if (j < W.ldm) part[j] = gsum + xpart[buf][64 * kq + lane];
+        if (j < W.ldm) part[j] = gsum + xpart[buf][1][64 * kq + lane];
       }
       float* pl = reinterpret_cast<float*>(Ks[buf]);
 #pragma unroll
@@ -608,8 +626,7 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
         }
       }
       __syncthreads();  // the tile is out before the buffer is staged again
-      if (more) store(buf ^ 1);
-      __syncthreads();
+      land(buf ^ 1);
     }
     return;
   }
@@ -627,36 +644,38 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
   auto flush = [&](int st) {  // the tile's partial of step st (even waves, after the barrier)
     if (!(wave & 1)) {
       const int j = st * kBiasStep + 64 * kq + lane;
-      if (j < W.ldm) part[j] = gkeep + xpart[st & 1][64 * kq + lane];
+      if (j < W.ldm) part[j] = gkeep + xpart[st & 1][1][64 * kq + lane];
     }
   };
+  // step st >= 1 (step 0 has no column): the partial of st - 2 leaves first, then the MFMAs of
+  // st beside the column of st - 1 in one basic block
   auto stepB = [&](int st, f32x4 (&cur)[4][2], float (&wc)[4], f32x4 (&prev)[4][2]) {
-    const bool more = st + 1 < nsteps;
-    if (more) load(st + 1);
-    mma(st & 1, cur, wc);
+    issue(min(st + 1, nsteps - 1), (st + 1) & 1);
     if (st > 1) flush(st - 2);
-    if (st > 0) {
-      const float gs = column(st - 1, prev);
-      interleave();
-      if (wave & 1) xpart[(st - 1) & 1][64 * kq + lane] = gs;
-      else gkeep = gs;
-    }
-    if (more) store((st + 1) & 1);
-    __syncthreads();
+    mma(st & 1, cur, wc);
+    const float gs = column(st - 1, prev);
+    interleave();
+    xpart[(st - 1) & 1][wave & 1][64 * kq + lane] = gs;
+    gkeep = gs;
+    land((st + 1) & 1);
   };
-  load(0);
-  store(0);
-  __syncthreads();
+  issue(0, 0);
+  land(0);
+  issue(min(1, nsteps - 1), 1);
+  mma(0, acc0, wv0);
+  land(1);
+  int st = 1;
 #pragma unroll 1
-  for (int st = 0; st < nsteps; st += 2) {
-    stepB(st, acc0, wv0, acc1);
-    if (st + 1 < nsteps) stepB(st + 1, acc1, wv1, acc0);
+  for (; st + 1 < nsteps; st += 2) {
+    stepB(st, acc1, wv1, acc0);
+    stepB(st + 1, acc0, wv0, acc1);
   }
+  if (st < nsteps) stepB(st, acc1, wv1, acc0);
   if (nsteps > 1) flush(nsteps - 2);
   {
     const float gs = (nsteps & 1) ? column(nsteps - 1, acc0) : column(nsteps - 1, acc1);
-    if (wave & 1) xpart[(nsteps - 1) & 1][64 * kq + lane] = gs;
-    else gkeep = gs;
+    xpart[(nsteps - 1) & 1][wave & 1][64 * kq + lane] = gs;
+    gkeep = gs;
     __syncthreads();
     flush(nsteps - 1);
   }
