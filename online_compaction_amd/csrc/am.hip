@@ -304,6 +304,16 @@ __global__ __launch_bounds__(256) void am_gather(const uint16_t* __restrict__ k,
 namespace {
 constexpr int kBiasThreads = 512;
 constexpr int kBiasStep = 256;  // kept keys per step (KC rows are padded to a multiple)
+// LDS-DMA load (as dma16) addressed by a wave-uniform base in SGPRs plus a 32-bit per-lane byte
+// offset, with the LDS destination already wave-uniform: no per-lane 64-bit address arithmetic
+// and no read of the destination from a vector register
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_dst)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 }  // namespace
 
 template <int MODE>
@@ -346,18 +356,21 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
   // L % 16, so it reads chunk (L % 16) ^ (row & 15) of that row (the layout swz reads). The w of
   // the step's keys comes through a register (0 past m) and is written by land(), which waits for
   // every load of the step and ends with the barrier.
-  // (row & 15 repeats every four pieces: piece x + 4 is 16 rows, 256 chunks, further on)
-  int koff[4];
+  // (byte offsets from the step's first row; row & 15 repeats every four pieces)
+  uint32_t koff[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const int row = 4 * (8 * wave + x) + (lane >> 4);
-    koff[x] = row * 16 + ((lane & 15) ^ (row & 15));
+    koff[x] = 16u * (row * 16 + ((lane & 15) ^ (row & 15)));
   }
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ks_lds = lds_addr(&Ks[0][0]) + (8 * wave_s) * 1024;
   float wr = 0.0f;
   auto issue = [&](int st, int buf) {
     const u32x4* src = kc + (int64_t)st * kBiasStep * 16;
 #pragma unroll
-    for (int x = 0; x < 8; ++x) dma16(src + koff[x & 3] + 256 * (x >> 2), &Ks[buf][(8 * wave + x) * 1024]);
+    for (int x = 0; x < 8; ++x)
+      dma16_s(src, koff[x & 3] + 4096u * (x >> 2), ks_lds + buf * (kBiasStep * 256) + x * 1024);
     if constexpr (kW) {  // every thread loads (clamped), so the step stays free of branches
       const int j = st * kBiasStep + (tid & (kBiasStep - 1));
       const float x = wu[min(j, m - 1)];
@@ -388,15 +401,14 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) wv[sub] = ws_l[buf][64 * kq + 16 * sub + c16];
     }
-#pragma unroll
-    for (int sub = 0; sub < 4; ++sub) acc[sub][0] = acc[sub][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const f32x4 zero = f32x4{0.0f, 0.0f, 0.0f, 0.0f};  // the first k-step starts from 0
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (ks < 3) frag(ks + 1, b[(ks + 1) & 1]);
 #pragma unroll
       for (int sub = 0; sub < 4; ++sub) {
-        acc[sub][0] = mfma16(qa[0][ks], b[ks & 1][sub], acc[sub][0]);
-        acc[sub][1] = mfma16(qa[1][ks], b[ks & 1][sub], acc[sub][1]);
+        acc[sub][0] = mfma16(qa[0][ks], b[ks & 1][sub], ks ? acc[sub][0] : zero);
+        acc[sub][1] = mfma16(qa[1][ks], b[ks & 1][sub], ks ? acc[sub][1] : zero);
       }
     }
   };
