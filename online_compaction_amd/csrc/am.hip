@@ -1241,15 +1241,38 @@ int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 // ------------------------------------------------------------------------------------------------
 // The Gram matrix of the iteration's side, Mg = X X^T with X = P_C (rows side: Np = Rp rows,
 // contraction over the kept keys) or X = P_C^T (keys side: Np = ldm rows, contraction over the
-// proxy rows), stored as split rows [Np][Np]. Mg is symmetric: a workgroup forms the tile (a, b)
-// with a <= b and writes it and, off the diagonal, its transpose, both through LDS (the tile in
-// float32, pitch 129), in the blocked layout the step kernel reads (mg_put8). Rows and columns of X past its live rows are zero, so are
-// those of Mg. Work item = (seq, head, tile pair), pairs a-major.
+// proxy rows), stored as split rows [Np][Np]. Mg is symmetric: a workgroup forms the 128 x 128
+// tile (a, b) with a <= b and writes it and, off the diagonal, its transpose, both through LDS
+// (the tile in float32, pitch 129), in the blocked layout the step kernel reads (mg_put8). Rows
+// and columns of X past its live rows are zero, so are those of Mg.
+// Eight waves, wave w: rows 64 (w & 1) .. + 63, columns 32 (w >> 1) .. + 31 of the tile (four x
+// two 16 x 16 accumulators), operands split as in am_gemm (three bf16 products). The
+// contraction runs in stages of 32 through a ring of kGramRing LDS slots filled by LDS-DMA
+// kGramRing - 1 stages ahead: a stage is the 128 rows of block a, then the 128 rows of block b,
+// 128 bytes per row in the layout of the step kernel's ring (chunk c of row r at position
+// c ^ step_sw(r)); wave w lands 1 KB pieces 4 w .. 4 w + 3 of the 32 (8 rows each), lane L row
+// L / 8 of its piece at position L % 8, reading chunk (L % 8) ^ step_sw(row) of that row (rows past
+// the live ones read the last live row; their products are dropped). Past the last stage the
+// ring is refilled with the last stage again (never read), which keeps four loads per wave per
+// stage and so the fixed wait counts exact.
+// Work item = (seq, head, tile pair), pairs a-major.
 // ------------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void am_gram(float* __restrict__ ws, AmCfg C, SeqTable T) {
+namespace {
+constexpr int kGramThreads = 512;
+constexpr int kGramRing = 4;
+constexpr int kGramSlot = 2 * kGTile * 128;  // bytes per stage: both row blocks
+// at most 8 of this wave's loads outstanding (the two stages after the one to compute), then a
+// barrier
+__device__ __forceinline__ void gram_wait_barrier() {
+  static_assert(4 * (kGramRing - 2) == 8, "the wait count follows the ring depth");
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+}  // namespace
+
+__global__ __launch_bounds__(kGramThreads) void am_gram(float* __restrict__ ws, AmCfg C, SeqTable T) {
   constexpr int kPitch = kGTile + 1;
-  __shared__ __attribute__((aligned(16))) float tl[kGTile * kPitch];
-  static_assert(sizeof(float) * kGTile * kPitch >= kGLds, "the product stages live in the tile's LDS");
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kGramRing * kGramSlot];
+  static_assert(sizeof(sm) >= sizeof(float) * kGTile * kPitch, "the epilogue tile fits the ring");
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int R = C.R;
@@ -1269,32 +1292,80 @@ __global__ __launch_bounds__(256, 2) void am_gram(float* __restrict__ ws, AmCfg 
   const int xrows = W.rside ? R : ldm;
   const int nst = W.rside ? ldm / 32 : (R + 31) / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int ra = a * kGTile + (tid >> 1), rb = b * kGTile + (tid & 127);
+  const int wr = wave & 1, wc = wave >> 1;
+  // this lane's DMA sources: byte offsets of its rows' first stage from the first row of the
+  // wave's row block (waves 0-3 land block a, waves 4-7 block b; a block's first row is live)
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const int blk = wave_s < 4 ? a : b;
+  const float* Xb = X + (int64_t)blk * kGTile * pitch;
+  uint32_t voff[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int row = 8 * ((4 * wave + x) & 15) + (lane >> 3);
+    const int xr = min(blk * kGTile + row, xrows - 1) - blk * kGTile;
+    voff[x] = 4u * (uint32_t)(xr * pitch + 4 * ((lane & 7) ^ step_sw(row)));
+  }
+  const uint32_t ring = lds_addr(sm) + 4 * wave_s * 1024;
+  auto issue = [&](int stg) {
+    const float* src = Xb + 32 * min(stg, nst - 1);
+    const uint32_t slot = ring + (stg % kGramRing) * kGramSlot;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) dma16_s(src, voff[x], slot + x * 1024);
+  };
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc[x][0] = acc[x][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int stg = 0; stg < kGramRing - 1; ++stg) issue(stg);
+#pragma unroll 1
+  for (int stg = 0; stg < nst; ++stg) {
+    // this stage's loads are in (only the two later stages', four each, may be outstanding); the
+    // barrier also retires every wave's reads of the slot refilled next
+    gram_wait_barrier();
+    issue(stg + kGramRing - 1);
+    const uint8_t* slot = sm + (stg % kGramRing) * kGramSlot;
+    bf16x8 bh[2], bl[2];
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int rbw = 32 * wc + 16 * y + c16;
+      bh[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g)]);
+      bl[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g + 1)]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int ra = 64 * wr + 16 * x + c16;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        acc[x][y] = mfma16(ah, bh[y], acc[x][y]);
+        acc[x][y] = mfma16(ah, bl[y], acc[x][y]);
+        acc[x][y] = mfma16(al, bh[y], acc[x][y]);
+      }
+    }
+  }
+  vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
 
-  f32x4 acc[4][4];
+  float* tl = reinterpret_cast<float*>(sm);
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  tile_mma(X + (int64_t)min(ra, xrows - 1) * pitch, ra < xrows, X + (int64_t)min(rb, xrows - 1) * pitch, rb < xrows,
-           0, nst, acc, reinterpret_cast<uint8_t*>(tl));
-  __syncthreads();  // the stages are done with the LDS
+    for (int y = 0; y < 2; ++y)
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int y = 0; y < 4; ++y)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) tl[(64 * wr + 16 * x + 4 * g + e) * kPitch + 64 * wc + 16 * y + c16] = acc[x][y][e];
+      for (int e = 0; e < 4; ++e) {
+        const int r = 64 * wr + 16 * x + 4 * g + e, c = 32 * wc + 16 * y + c16;
+        const bool live = a * kGTile + r < xrows && b * kGTile + c < xrows;
+        tl[r * kPitch + c] = live ? acc[x][y][e] : 0.0f;
+      }
   __syncthreads();
   float* Mh = W.Mg + (int64_t)h * Np * Np;
-  for (int q = tid; q < kGTile * (kGTile / 8); q += 256) {
+  for (int q = tid; q < kGTile * (kGTile / 8); q += kGramThreads) {
     const int r = q >> 4, gq = q & 15;
     if (a * kGTile + r < Np && b * kGTile + 8 * gq < Np)
       mg_put8(Mh, Np, a * kGTile + r, b * kGTile + 8 * gq, &tl[r * kPitch + 8 * gq]);
   }
   if (a != b) {
-    for (int q = tid; q < kGTile * (kGTile / 8); q += 256) {
+    for (int q = tid; q < kGTile * (kGTile / 8); q += kGramThreads) {
       const int c = q >> 4, gq = q & 15;
       if (b * kGTile + c >= Np || a * kGTile + 8 * gq >= Np) continue;
       float x[8];
@@ -1525,7 +1596,7 @@ hipError_t launch_am_step(float* vc, float* ws, const AmCfg& C, const SeqTable& 
 }
 
 hipError_t launch_am_gram(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
-  am_gram<<<dim3(T.total), dim3(256), 0, st>>>(ws, C, T);
+  am_gram<<<dim3(T.total), dim3(kGramThreads), 0, st>>>(ws, C, T);
   return hipGetLastError();
 }
 

@@ -1,11 +1,11 @@
 """Properties of the generated gfx950 device code that the kernels rely on but no GPU run can
 show: the LDS-DMA loads of the MFMA scoring passes (many rows and few rows) and of the Attention
-Matching value step set M0 themselves in inline assembly, which is only sound while no
+Matching kernels set M0 themselves in inline assembly, which is only sound while no
 compiler-generated instruction reads or writes M0 in those kernels; their stage loops wait for the
 loads they need only (a compiler-placed vmcnt(0) inside the loop would also wait for the loads
 meant to stay in flight); and the kernels that count their LDS-DMA loads in fixed waits (the
-few-row kernels, the value step) issue no other vector-memory access between the first of those
-loads and the last wait."""
+few-row kernels, the value step, the Gram kernel) issue no other vector-memory access between the
+first of those loads and the last wait."""
 import os
 import re
 import subprocess
@@ -161,12 +161,9 @@ def test_few_row_kernels_issue_only_their_dma_loads_before_the_last_wait(small_a
     assert kernels == 6
 
 
-def test_value_step_issues_only_its_dma_loads_in_the_ring(am_asm):
-    """The value step's ring waits with a fixed count (three loads per wave per stage): between
-    its first LDS-DMA load and the wait for all of them, every vector-memory instruction on a
-    path is one of those loads, and the wait for a pair of stages is vmcnt(6) followed by the
-    barrier."""
-    (name, lines), = list(_functions(am_asm, "_ZN3kvc7am_step"))
+def _ring_window(lines):
+    """The code of every block on a control-flow path from a kernel's first LDS-DMA load to its
+    wait for all loads (vmcnt(0) lgkmcnt(0)), cut at both ends."""
     blocks, succ = _blocks(lines)
     body = dict(blocks)
     first_b = next(lab for lab, b in blocks if any(t.startswith("global_load_lds_") for t in b))
@@ -182,8 +179,31 @@ def test_value_step_issues_only_its_dma_loads_in_the_ring(am_asm):
         if lab == last_b:
             b = b[:next(i for i, t in enumerate(b) if t.startswith("s_waitcnt vmcnt(0) lgkmcnt(0)"))]
         code += b
+    return code
+
+
+def test_value_step_issues_only_its_dma_loads_in_the_ring(am_asm):
+    """The value step's ring waits with a fixed count (three loads per wave per stage): between
+    its first LDS-DMA load and the wait for all of them, every vector-memory instruction on a
+    path is one of those loads, and the wait for a pair of stages is vmcnt(6) followed by the
+    barrier."""
+    (name, lines), = list(_functions(am_asm, "_ZN3kvc7am_step"))
+    code = _ring_window(lines)
     other = [t for t in code if re.match(r"(global|buffer|flat|scratch)_", t) and not t.startswith("global_load_lds_")]
     assert not other, f"{name}: other vector-memory accesses among the counted loads: {other[:3]}"
     assert all(t.startswith("global_load_lds_dwordx4") for t in code if t.startswith("global_load_lds_"))
     iw = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(6)"))
+    assert code[iw + 1] == "s_barrier"
+
+
+def test_gram_issues_only_its_dma_loads_in_the_ring(am_asm):
+    """The Gram kernel's ring waits with a fixed count (four loads per wave per stage, two stages
+    in flight): between its first LDS-DMA load and the wait for all of them only those loads
+    touch memory, and the stage wait is vmcnt(8) followed by the barrier."""
+    (name, lines), = list(_functions(am_asm, "_ZN3kvc7am_gram"))
+    code = _ring_window(lines)
+    other = [t for t in code if re.match(r"(global|buffer|flat|scratch)_", t) and not t.startswith("global_load_lds_")]
+    assert not other, f"{name}: other vector-memory accesses among the counted loads: {other[:3]}"
+    assert len([t for t in code if t.startswith("global_load_lds_dwordx4")]) >= 8
+    iw = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(8)"))
     assert code[iw + 1] == "s_barrier"
