@@ -1248,24 +1248,27 @@ int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 // Eight waves, wave w: rows 64 (w & 1) .. + 63, columns 32 (w >> 1) .. + 31 of the tile (four x
 // two 16 x 16 accumulators), operands split as in am_gemm (three bf16 products). The
 // contraction runs in stages of 32 through a ring of kGramRing LDS slots filled by LDS-DMA
-// kGramRing - 1 stages ahead: a stage is the 128 rows of block a, then the 128 rows of block b,
+// kGramRing stages ahead of the stage whose MFMAs run (whose fragments were read into registers
+// one stage earlier): a stage is the 128 rows of block a, then the 128 rows of block b,
 // 128 bytes per row in the layout of the step kernel's ring (chunk c of row r at position
 // c ^ step_sw(r)); wave w lands 1 KB pieces 4 w .. 4 w + 3 of the 32 (8 rows each), lane L row
 // L / 8 of its piece at position L % 8, reading chunk (L % 8) ^ step_sw(row) of that row (rows past
 // the live ones read the last live row; their products are dropped). Past the last stage the
-// ring is refilled with the last stage again (never read), which keeps four loads per wave per
-// stage and so the fixed wait counts exact.
+// ring is refilled with the last stage again (its fragments are read but not used), which keeps
+// four loads per wave per stage and so the fixed wait counts exact.
 // Work item = (seq, head, tile pair), pairs a-major.
 // ------------------------------------------------------------------------------------------------
 namespace {
 constexpr int kGramThreads = 512;
 constexpr int kGramRing = 4;
 constexpr int kGramSlot = 2 * kGTile * 128;  // bytes per stage: both row blocks
-// at most 8 of this wave's loads outstanding (the two stages after the one to compute), then a
-// barrier
+// at most N of this wave's loads outstanding (four per stage), then a barrier
+template <int N>
 __device__ __forceinline__ void gram_wait_barrier() {
-  static_assert(4 * (kGramRing - 2) == 8, "the wait count follows the ring depth");
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(kGramRing == 4, "the wait counts follow the ring depth");
+  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 8, "unsupported count");
 }
 }  // namespace
 
@@ -1312,38 +1315,60 @@ __global__ __launch_bounds__(kGramThreads) void am_gram(float* __restrict__ ws, 
 #pragma unroll
     for (int x = 0; x < 4; ++x) dma16_s(src, voff[x], slot + x * 1024);
   };
-  f32x4 acc[4][2];
-#pragma unroll
-  for (int x = 0; x < 4; ++x) acc[x][0] = acc[x][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int stg = 0; stg < kGramRing - 1; ++stg) issue(stg);
-#pragma unroll 1
-  for (int stg = 0; stg < nst; ++stg) {
-    // this stage's loads are in (only the two later stages', four each, may be outstanding); the
-    // barrier also retires every wave's reads of the slot refilled next
-    gram_wait_barrier();
-    issue(stg + kGramRing - 1);
+  // a stage's fragments (block a: four row fragments, block b: two; high and low halves)
+  struct Frags {
+    bf16x8 ah[4], al[4], bh[2], bl[2];
+  };
+  auto read = [&](int stg, Frags& f) {
     const uint8_t* slot = sm + (stg % kGramRing) * kGramSlot;
-    bf16x8 bh[2], bl[2];
 #pragma unroll
     for (int y = 0; y < 2; ++y) {
       const int rbw = 32 * wc + 16 * y + c16;
-      bh[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g)]);
-      bl[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g + 1)]);
+      f.bh[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g)]);
+      f.bl[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g + 1)]);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int ra = 64 * wr + 16 * x + c16;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+      f.ah[x] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
+      f.al[x] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+    }
+  };
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) acc[x][0] = acc[x][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
 #pragma unroll
       for (int y = 0; y < 2; ++y) {
-        acc[x][y] = mfma16(ah, bh[y], acc[x][y]);
-        acc[x][y] = mfma16(ah, bl[y], acc[x][y]);
-        acc[x][y] = mfma16(al, bh[y], acc[x][y]);
+        acc[x][y] = mfma16(f.ah[x], f.bh[y], acc[x][y]);
+        acc[x][y] = mfma16(f.ah[x], f.bl[y], acc[x][y]);
+        acc[x][y] = mfma16(f.al[x], f.bh[y], acc[x][y]);
       }
-    }
+  };
+  // Stage s's fragments are read into registers one stage early, so their LDS latency hides
+  // behind the MFMAs of stage s - 1: at the top of the iteration for stage s, stage s + 1 has
+  // landed (only stages s + 2 and s + 3, eight loads, may be outstanding), and after the barrier
+  // every wave holds stage s in registers, so its slot takes stage s + 4.
+  Frags f0, f1;
+#pragma unroll
+  for (int stg = 0; stg < kGramRing; ++stg) issue(stg);
+  gram_wait_barrier<12>();
+  read(0, f0);
+  auto iter = [&](int stg, Frags& cur, Frags& nxt) {
+    gram_wait_barrier<8>();
+    issue(stg + kGramRing);
+    read(stg + 1, nxt);
+    mma(cur);
+  };
+  int stg = 0;
+#pragma unroll 1
+  for (; stg + 1 < nst; stg += 2) {
+    iter(stg, f0, f1);
+    iter(stg + 1, f1, f0);
   }
+  if (stg < nst) iter(stg, f0, f1);
   vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
 
   float* tl = reinterpret_cast<float*>(sm);
