@@ -1079,18 +1079,19 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
 // L2. One 64 x 128 output tile per workgroup of eight waves (wave w: rows 16 (w & 3) .. + 15,
 // columns 64 (w >> 2) .. + 63: four 16 x 16 accumulators), operands split as in am_gemm (three
 // bf16 products). The contraction runs in stages of 32 through a ring of kStepRing LDS slots
-// filled by LDS-DMA (global_load_lds_dwordx4, three per wave per stage) kStepRing - 2 stages
-// ahead (deep enough that the bytes in flight cover the memory latency at full rate): a
+// filled by LDS-DMA (global_load_lds_dwordx4, three per wave per stage) kStepRing stages ahead
+// of the stage whose MFMAs run (deep enough that the bytes in flight cover the memory latency
+// at full rate; a stage's fragments are read into registers one stage before its MFMAs): a
 // stage is 64 rows of Mg and the 128 rows of the transpose, 128 bytes per row (the 32 indices'
 // split groups: high half, low half), 16-byte chunk c of row r at position c ^ step_sw(r) (the
 // low three bits of r with bits 0 and 1 swapped), so every ds_read_b128 of an MFMA operand is
 // free of bank conflicts (gfx950 serves such a read in four groups of 16 lanes, group = (lane
 // bit 5, parity of lane bits 2..4), each over 64 banks: the 16 rows read at one chunk position
 // must land in 16 distinct 16-byte slots of a 256-byte window; measured with the LDS
-// bank-conflict counter) (the DMA lands each wave's 1 KB
-// contiguously, so the source address of a lane carries the permutation). Past the last stage
-// the ring is refilled with the last stage again (never read), which keeps three loads per wave
-// per stage and so the fixed wait counts exact.
+// bank-conflict counter). The DMA lands each wave's 1 KB contiguously, so the source address of
+// a lane carries the permutation. Past the last stage the ring is refilled with the last stage
+// again (its fragments are read but not used), which keeps three loads per wave per stage and so
+// the fixed wait counts exact.
 //   mode 0: the new iterate's transpose goes to the other buffer for the next step
 //   mode 1 (last step): rows side, Sx's transpose goes there for the last P_C^T product;
 //           keys side, Vc -= eta Sx
@@ -1115,11 +1116,13 @@ __device__ __forceinline__ void mg_put8(float* mh, int Np, int r, int c, const f
   *reinterpret_cast<u32x4*>(blk + (((2 * grp) ^ sw) << 4)) = hi;
   *reinterpret_cast<u32x4*>(blk + (((2 * grp + 1) ^ sw) << 4)) = lo;
 }
-// at most 6 of this wave's loads outstanding (the two stages after the pair to compute), then a
-// barrier
+// at most N of this wave's loads outstanding (three per stage), then a barrier
+template <int N>
 __device__ __forceinline__ void step_wait_barrier() {
-  static_assert(kStepRing == 6, "the wait count follows the ring depth");
-  asm volatile("s_waitcnt vmcnt(6) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  static_assert(kStepRing == 6, "the wait counts follow the ring depth");
+  if constexpr (N == 15) asm volatile("s_waitcnt vmcnt(15) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 12, "unsupported count");
 }
 }  // namespace
 
@@ -1167,34 +1170,52 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   f32x4 acc[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto compute = [&](int stg) {
+  // a stage's fragments: the wave's 16 rows of Mg and its 64 columns of the iterate, high and low
+  struct Frags {
+    bf16x8 ah, al, bh[4], bl[4];
+  };
+  auto read = [&](int stg, Frags& f) {
     const uint8_t* slot = sm + (stg % kStepRing) * kStepSlot;
     const int ra = 16 * wr + c16;
-    const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
-    const bf16x8 al = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+    f.ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
+    f.al = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int rbw = 64 * wc + 16 * b + c16;
-      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g)]);
-      const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g + 1)]);
-      acc[b] = mfma16(ah, bh, acc[b]);
-      acc[b] = mfma16(ah, bl, acc[b]);
-      acc[b] = mfma16(al, bh, acc[b]);
+      f.bh[b] = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g)]);
+      f.bl[b] = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g + 1)]);
     }
   };
-  // Two stages per barrier: at the top of the iteration for stages s and s + 1 (s even), both have
-  // landed (only stages s + 2 and s + 3, six loads, may be outstanding) and every wave is past its
-  // reads of stages s - 2 and s - 1, whose slots take stages s + 4 and s + 5.
+  auto mma = [&](const Frags& f) {
 #pragma unroll
-  for (int stg = 0; stg < 4; ++stg) issue(stg);
+    for (int b = 0; b < 4; ++b) {
+      acc[b] = mfma16(f.ah, f.bh[b], acc[b]);
+      acc[b] = mfma16(f.ah, f.bl[b], acc[b]);
+      acc[b] = mfma16(f.al, f.bh[b], acc[b]);
+    }
+  };
+  // Stage s's fragments are read into registers one stage early, so their LDS latency hides
+  // behind the MFMAs of stage s - 1: at the top of the iteration for stage s, stage s + 1 has
+  // landed (only stages s + 2 .. s + 5, twelve loads, may be outstanding), and after the barrier
+  // every wave holds stage s in registers, so its slot takes stage s + 6.
+  Frags f0, f1;
+#pragma unroll
+  for (int stg = 0; stg < kStepRing; ++stg) issue(stg);
+  step_wait_barrier<15>();
+  read(0, f0);
+  auto iter = [&](int stg, Frags& cur, Frags& nxt) {
+    step_wait_barrier<12>();
+    issue(stg + kStepRing);
+    read(stg + 1, nxt);
+    mma(cur);
+  };
+  int stg = 0;
 #pragma unroll 1
-  for (int stg = 0; stg < nst; stg += 2) {
-    step_wait_barrier();
-    issue(stg + 4);
-    issue(stg + 5);
-    compute(stg);
-    if (stg + 1 < nst) compute(stg + 1);
+  for (; stg + 1 < nst; stg += 2) {
+    iter(stg, f0, f1);
+    iter(stg + 1, f1, f0);
   }
+  if (stg < nst) iter(stg, f0, f1);
   vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
 
   // epilogue through LDS: the tile's new iterate in float32 rows of 128 (pitch 129)

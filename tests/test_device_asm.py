@@ -183,16 +183,16 @@ def _ring_window(lines):
 
 
 def test_value_step_issues_only_its_dma_loads_in_the_ring(am_asm):
-    """The value step's ring waits with a fixed count (three loads per wave per stage): between
-    its first LDS-DMA load and the wait for all of them, every vector-memory instruction on a
-    path is one of those loads, and the wait for a pair of stages is vmcnt(6) followed by the
-    barrier."""
+    """The value step's ring waits with a fixed count (three loads per wave per stage, four
+    stages in flight): between its first LDS-DMA load and the wait for all of them, every
+    vector-memory instruction on a path is one of those loads, and the stage wait is vmcnt(12)
+    followed by the barrier."""
     (name, lines), = list(_functions(am_asm, "_ZN3kvc7am_step"))
     code = _ring_window(lines)
     other = [t for t in code if re.match(r"(global|buffer|flat|scratch)_", t) and not t.startswith("global_load_lds_")]
     assert not other, f"{name}: other vector-memory accesses among the counted loads: {other[:3]}"
     assert all(t.startswith("global_load_lds_dwordx4") for t in code if t.startswith("global_load_lds_"))
-    iw = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(6)"))
+    iw = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(12)"))
     assert code[iw + 1] == "s_barrier"
 
 
