@@ -1167,6 +1167,18 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
 #pragma unroll
     for (int x = 0; x < 3; ++x) dma16(src[x] + st * sstep[x], slot + (3 * wave + x) * 1024);
   };
+  // the epilogue's operands (this lane's 16 entries of X and of Sx; rows past N are zero) are
+  // loaded before the ring starts, so their latency hides behind the product (they are older
+  // than every ring load, so the ring's in-order waits cover them)
+  float xo[4][4], so[4][4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t ox = ((int64_t)h * Np + blk * kStepRows + 16 * wr + 4 * g + e) * kD + 64 * wc + 16 * b + c16;
+      xo[b][e] = W.X[ox];
+      so[b][e] = W.Sx[ox];
+    }
   f32x4 acc[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -1223,22 +1235,32 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   static_assert(sizeof(sm) >= sizeof(float) * kStepRows * (kD + 1), "the epilogue tile fits the ring");
   const float eta = W.eta[h];
   const bool to_vc = C.mode == 1 && !W.rside;
+  float* vcu = vc_all + unit * C.m_max * (int64_t)kD;
+  float vo[4][4];  // the last step of the keys side: this lane's entries of Vc (rows clamped below m)
+  if (to_vc) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = blk * kStepRows + 16 * wr + 4 * g + e;
+        vo[b][e] = vcu[(int64_t)min(r, m - 1) * kD + 64 * wc + 16 * b + c16];
+      }
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int rl = 16 * wr + 4 * g + e, r = blk * kStepRows + rl, col = 64 * wc + 16 * b + c16;
-      float out = 0.0f;
-      if (r < W.N) {
+      const float xn = xo[b][e] - eta * acc[b][e];
+      const float sum = so[b][e] + xn;
+      const bool live = r < W.N;
+      if (live) {
         const int64_t ox = ((int64_t)h * Np + r) * kD + col;
-        const float xn = W.X[ox] - eta * acc[b][e];
-        const float sum = W.Sx[ox] + xn;
         W.X[ox] = xn;
         W.Sx[ox] = sum;
-        out = C.mode == 1 ? sum : xn;
-        if (to_vc && r < m) vc_all[unit * C.m_max * (int64_t)kD + (int64_t)r * kD + col] -= eta * sum;
+        if (to_vc && r < m) vcu[(int64_t)r * kD + col] = vo[b][e] - eta * sum;
       }
-      tl[rl * (kD + 1) + col] = out;
+      tl[rl * (kD + 1) + col] = live ? (C.mode == 1 ? sum : xn) : 0.0f;
     }
   if (to_vc) return;  // uniform across the block
   __syncthreads();
