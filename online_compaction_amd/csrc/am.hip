@@ -872,95 +872,122 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
 int am_target_blocks(int R) { return (R + kTgtRows - 1) / kTgtRows; }
 
 // ------------------------------------------------------------------------------------------------
-// The value fit's matrix products, one 128 x 128 output tile per workgroup (four waves in a 2 x 2
-// grid, each 64 x 64: sixteen 16 x 16 accumulators), the contraction in stages of 32 through
-// double-buffered LDS with the next stage's global loads in flight during the current stage's
-// MFMAs. Both operands are read by rows along the contraction: out = A B^T.
+// The value fit's matrix products (am_gemm, am_gram): one 128 x 128 output tile per workgroup of
+// eight waves (wave w: rows 64 (w & 1) .. + 63, columns 32 (w >> 1) .. + 31; four x two 16 x 16
+// accumulators). Both operands are read by rows along the contraction: out = A B^T.
 // The float32 operands are stored split (x = hi + lo with hi = bf16(x) and lo = bf16(x - hi),
 // the layout of put_split8), and a product is taken as hi_a hi_b + hi_a lo_b + lo_a hi_b on
 // v_mfma_f32_16x16x32_bf16 with float32 accumulation (the dropped lo_a lo_b and the rounding of
 // lo leave a relative error near 2^-16 per product, against 2^-24 for float32 inputs, at a
 // third of the float32 MFMA's cycles per product).
-// LDS holds, per operand and half, 128 rows of 32 contraction indices (bf16, 64 bytes per row);
-// 16-byte chunk c of row r sits at chunk position c ^ ((r >> 1) & 3), so each MFMA operand read
-// (chunk g of 16 consecutive rows) is free of bank conflicts. Lane group g of an MFMA supplies
-// contraction indices 8g .. 8g + 7 on both operands.
+// The contraction runs in stages of 32 through a ring of kRing LDS slots filled by LDS-DMA
+// kRing stages ahead of the stage whose MFMAs run (a stage's fragments are read into registers
+// one stage before its MFMAs): a stage is the 128 rows of the A block, then the 128 rows of the
+// B block, 128 bytes per row (the 32 indices' split groups: high half, low half), 16-byte chunk
+// c of row r at position c ^ step_sw(r) (the low three bits of r with bits 0 and 1 swapped), so
+// every ds_read_b128 of an MFMA operand is free of bank conflicts (gfx950 serves such a read in
+// four groups of 16 lanes, group = (lane bit 5, parity of lane bits 2..4), each over 64 banks:
+// the 16 rows read at one chunk position must land in 16 distinct 16-byte slots of a 256-byte
+// window; measured with the LDS bank-conflict counter). Wave w lands the 1 KB pieces
+// 4 w .. 4 w + 3 of the 32 (8 rows each; waves 0-3 the A block, 4-7 the B block), lane L row
+// L / 8 of its piece at position L % 8, reading chunk (L % 8) ^ step_sw(row) of that row; rows
+// past a block's live ones read its last live row (the caller drops their products). Past the
+// last stage the ring is refilled with the last stage again (its fragments are read but not
+// used), which keeps four loads per wave per stage and so the fixed wait counts exact.
 // ------------------------------------------------------------------------------------------------
 namespace {
 constexpr int kGTile = 128;
-constexpr int kGLds = 4 * 2 * kGTile * 64;  // bytes: hi and lo of both operands, double-buffered
+constexpr int kRingThreads = 512;
+constexpr int kRing = 4;
+constexpr int kRingSlot = 2 * kGTile * 128;  // bytes per stage: both row blocks
+__device__ __forceinline__ int step_sw(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
+__device__ __forceinline__ int sswz(int row, int chunk) { return row * 128 + ((chunk ^ step_sw(row)) << 4); }
+// at most N of this wave's loads outstanding (four per stage), then a barrier
+template <int N>
+__device__ __forceinline__ void ring_wait_barrier() {
+  static_assert(kRing == 4, "the wait counts follow the ring depth");
+  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  else static_assert(N == 8, "unsupported count");
+}
 
-__device__ __forceinline__ int gswz(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4); }
-
-// acc += A B^T over contraction stages st0 .. st1 - 1 (32 indices each) of one 128 x 128 tile.
-// arow / brow: the split rows of A and B that this thread stages (row tid >> 1 of A, indices
-// 16 (tid & 1) .. + 15 of each stage; row tid & 127 of B, indices 16 (tid >> 7) .. + 15); a row
-// that is not alive is staged as zeros. Every operand is stored split, so a thread's 16 indices
-// are 64 contiguous bytes: high parts of the first 8, their low parts, then the same for the
-// next 8, copied to the high and low LDS tiles unchanged.
-__device__ __forceinline__ void tile_mma(const float* arow, bool alive_a, const float* brow, bool alive_b, int st0,
-                                         int st1, f32x4 (&acc)[4][4], uint8_t* sm) {
-  uint8_t* Ah = sm;
-  uint8_t* Al = sm + 2 * kGTile * 64;
-  uint8_t* Bh = sm + 4 * kGTile * 64;
-  uint8_t* Bl = sm + 6 * kGTile * 64;
-  constexpr int kBuf = kGTile * 64;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int ar = tid >> 1, ak = tid & 1;
-  const int bd = tid & 127, bk = tid >> 7;
-  const u32x4* asrc = reinterpret_cast<const u32x4*>(arow + 16 * ak);
-  const u32x4* bsrc = reinterpret_cast<const u32x4*>(brow + 16 * bk);
-  u32x4 ra[4], rb[4];
-  auto load = [&](int stg) {
-    const int o = stg * 8;  // 32 indices = 8 u32x4 per row
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      ra[c] = asrc[o + c];
-      rb[c] = bsrc[o + c];
-    }
-  };
-  auto store = [&](int buf) {
-    const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      *reinterpret_cast<u32x4*>(&Ah[buf * kBuf + gswz(ar, 2 * ak + c)]) = alive_a ? ra[2 * c] : z;
-      *reinterpret_cast<u32x4*>(&Al[buf * kBuf + gswz(ar, 2 * ak + c)]) = alive_a ? ra[2 * c + 1] : z;
-      *reinterpret_cast<u32x4*>(&Bh[buf * kBuf + gswz(bd, 2 * bk + c)]) = alive_b ? rb[2 * c] : z;
-      *reinterpret_cast<u32x4*>(&Bl[buf * kBuf + gswz(bd, 2 * bk + c)]) = alive_b ? rb[2 * c + 1] : z;
-    }
-  };
+// acc += A B^T over contraction stages st0 .. st1 - 1 of one tile. Xa, Xb: the first rows of
+// the A and B blocks (split rows, pitch floats); la, lb (at least 1): their live rows. sm: the
+// ring (kRing * kRingSlot bytes); when this returns every wave is done with it.
+__device__ __forceinline__ void ring_mma(const float* Xa, int la, const float* Xb, int lb, int pitch, int st0,
+                                         int st1, f32x4 (&acc)[4][2], uint8_t* sm) {
   if (st0 >= st1) return;
-  load(st0);
-  store(0);
-  __syncthreads();
-#pragma unroll 1
-  for (int stg = st0; stg < st1; ++stg) {
-    const int buf = (stg - st0) & 1;
-    const bool more = stg + 1 < st1;
-    if (more) load(stg + 1);
-    bf16x8 bh[4], bl[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
+  const int wr = wave & 1, wc = wave >> 1;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const float* Xw = wave_s < 4 ? Xa : Xb;  // the wave's block
+  const int lw = wave_s < 4 ? la : lb;
+  // this lane's DMA sources: byte offsets of its rows' chunks from the block's first row
+  uint32_t voff[4];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int o = buf * kBuf + gswz(64 * wc + 16 * b + c16, g);
-      bh[b] = *reinterpret_cast<const bf16x8*>(&Bh[o]);
-      bl[b] = *reinterpret_cast<const bf16x8*>(&Bl[o]);
-    }
-#pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int o = buf * kBuf + gswz(64 * wr + 16 * a + c16, g);
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[o]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&Al[o]);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        acc[a][b] = mfma16(ah, bh[b], acc[a][b]);
-        acc[a][b] = mfma16(ah, bl[b], acc[a][b]);
-        acc[a][b] = mfma16(al, bh[b], acc[a][b]);
-      }
-    }
-    if (more) store(buf ^ 1);
-    __syncthreads();
+  for (int x = 0; x < 4; ++x) {
+    const int row = 8 * ((4 * wave + x) & 15) + (lane >> 3);
+    voff[x] = 4u * (uint32_t)(min(row, lw - 1) * pitch + 4 * ((lane & 7) ^ step_sw(row)));
   }
+  const uint32_t ring = lds_addr(sm) + 4 * wave_s * 1024;
+  auto issue = [&](int stg) {
+    const float* src = Xw + 32 * min(stg, st1 - 1);
+    const uint32_t slot = ring + ((stg - st0) % kRing) * kRingSlot;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) dma16_s(src, voff[x], slot + x * 1024);
+  };
+  // a stage's fragments (A block: four row fragments, B block: two; high and low halves)
+  struct Frags {
+    bf16x8 ah[4], al[4], bh[2], bl[2];
+  };
+  auto read = [&](int stg, Frags& f) {
+    const uint8_t* slot = sm + ((stg - st0) % kRing) * kRingSlot;
+#pragma unroll
+    for (int y = 0; y < 2; ++y) {
+      const int rbw = 32 * wc + 16 * y + c16;
+      f.bh[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g)]);
+      f.bl[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g + 1)]);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int ra = 64 * wr + 16 * x + c16;
+      f.ah[x] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
+      f.al[x] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+    }
+  };
+  auto mma = [&](const Frags& f) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int y = 0; y < 2; ++y) {
+        acc[x][y] = mfma16(f.ah[x], f.bh[y], acc[x][y]);
+        acc[x][y] = mfma16(f.ah[x], f.bl[y], acc[x][y]);
+        acc[x][y] = mfma16(f.al[x], f.bh[y], acc[x][y]);
+      }
+  };
+  // Stage s's fragments are read into registers one stage early, so their LDS latency hides
+  // behind the MFMAs of stage s - 1: at the top of the iteration for stage s, stage s + 1 has
+  // landed (only stages s + 2 and s + 3, eight loads, may be outstanding), and after the barrier
+  // every wave holds stage s in registers, so its slot takes stage s + 4.
+  Frags f0, f1;
+#pragma unroll
+  for (int k = 0; k < kRing; ++k) issue(st0 + k);
+  ring_wait_barrier<12>();
+  read(st0, f0);
+  auto iter = [&](int stg, Frags& cur, Frags& nxt) {
+    ring_wait_barrier<8>();
+    issue(stg + kRing);
+    read(stg + 1, nxt);
+    mma(cur);
+  };
+  int stg = st0;
+#pragma unroll 1
+  for (; stg + 1 < st1; stg += 2) {
+    iter(stg, f0, f1);
+    iter(stg + 1, f1, f0);
+  }
+  if (stg < st1) iter(stg, f0, f1);
+  vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
 }
 }  // namespace
 
@@ -976,9 +1003,9 @@ __device__ __forceinline__ void tile_mma(const float* arow, bool alive_a, const 
 // Work item = (seq, head, output tile, split), split fastest.
 // ------------------------------------------------------------------------------------------------
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
-                                                  SeqTable T) {
-  __shared__ __attribute__((aligned(16))) uint8_t sm[kGLds];
+__global__ __launch_bounds__(kRingThreads) void am_gemm(float* __restrict__ vc_all, float* __restrict__ ws, AmCfg C,
+                                                       SeqTable T) {
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kRing * kRingSlot];
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
   const int m = T.m[i], s = T.first + i;
@@ -997,32 +1024,27 @@ __global__ __launch_bounds__(256, 2) void am_gemm(float* __restrict__ vc_all, fl
   const int apitch = KIND == 0 ? ldm : W.Rp;
   const float* A = KIND == 0 ? W.P + (int64_t)h * R * ldm : W.PT + (int64_t)h * ldm * W.Rp;
   const float* B = KIND == 0 ? W.VT + (int64_t)h * kD * ldm : (C.xsel ? W.XT1 : W.ZT) + (int64_t)h * kD * W.Rp;
-  const int bpitch = apitch;
   const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
   const int per = (nst + S - 1) / S;
   const int st0 = sp * per, st1 = min(nst, st0 + per);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int arow = tile * kGTile + (tid >> 1);
+  const int wr = wave & 1, wc = wave >> 1;
   const int alim = KIND == 0 ? R : ldm;
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][2];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  tile_mma(A + (int64_t)min(arow, alim - 1) * apitch, arow < alim, B + (int64_t)(tid & 127) * bpitch, true, st0, st1,
-           acc, sm);
+  for (int a = 0; a < 4; ++a) acc[a][0] = acc[a][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  ring_mma(A + (int64_t)tile * kGTile * apitch, alim - tile * kGTile, B, kD, apitch, st0, st1, acc, sm);
 
   const float eta = W.eta[h];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = tile * kGTile + 64 * wr + 16 * a + 4 * g + e;
-        const int col = 64 * wc + 16 * b + c16;
+        const int col = 32 * wc + 16 * b + c16;
         const float v = acc[a][b][e];
         if constexpr (KIND == 0) {  // Z = P_C V0 - Y, kept as split rows of Z^T (zeros past R)
           const int64_t o = (int64_t)h * R * kD + (int64_t)r * kD + col;
@@ -1103,8 +1125,6 @@ constexpr int kStepRows = 64;
 constexpr int kStepThreads = 512;
 constexpr int kStepRing = 6;
 constexpr int kStepA = kStepRows * 128, kStepB = kGTile * 128, kStepSlot = kStepA + kStepB;
-__device__ __forceinline__ int step_sw(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
-__device__ __forceinline__ int sswz(int row, int chunk) { return row * 128 + ((chunk ^ step_sw(row)) << 4); }
 // Mg is stored as the step kernel reads it: per 64-row block and 32-column stage an 8 KB block of
 // 64 rows x 128 bytes (the four 8-column groups, high half then low half), 16-byte chunk c of
 // row r at position c ^ step_sw(r); a stage of a row block is one contiguous read.
@@ -1285,39 +1305,14 @@ int am_gemm_tiles(int rows) { return (rows + kGTile - 1) / kGTile; }
 // The Gram matrix of the iteration's side, Mg = X X^T with X = P_C (rows side: Np = Rp rows,
 // contraction over the kept keys) or X = P_C^T (keys side: Np = ldm rows, contraction over the
 // proxy rows), stored as split rows [Np][Np]. Mg is symmetric: a workgroup forms the 128 x 128
-// tile (a, b) with a <= b and writes it and, off the diagonal, its transpose, both through LDS
-// (the tile in float32, pitch 129), in the blocked layout the step kernel reads (mg_put8). Rows
-// and columns of X past its live rows are zero, so are those of Mg.
-// Eight waves, wave w: rows 64 (w & 1) .. + 63, columns 32 (w >> 1) .. + 31 of the tile (four x
-// two 16 x 16 accumulators), operands split as in am_gemm (three bf16 products). The
-// contraction runs in stages of 32 through a ring of kGramRing LDS slots filled by LDS-DMA
-// kGramRing stages ahead of the stage whose MFMAs run (whose fragments were read into registers
-// one stage earlier): a stage is the 128 rows of block a, then the 128 rows of block b,
-// 128 bytes per row in the layout of the step kernel's ring (chunk c of row r at position
-// c ^ step_sw(r)); wave w lands 1 KB pieces 4 w .. 4 w + 3 of the 32 (8 rows each), lane L row
-// L / 8 of its piece at position L % 8, reading chunk (L % 8) ^ step_sw(row) of that row (rows past
-// the live ones read the last live row; their products are dropped). Past the last stage the
-// ring is refilled with the last stage again (its fragments are read but not used), which keeps
-// four loads per wave per stage and so the fixed wait counts exact.
-// Work item = (seq, head, tile pair), pairs a-major.
+// tile (a, b) with a <= b (ring_mma with row blocks a and b) and writes it and, off the
+// diagonal, its transpose, both through LDS (the tile in float32, pitch 129), in the blocked
+// layout the step kernel reads (mg_put8). Rows and columns of X past its live rows are zero, so
+// are those of Mg. Work item = (seq, head, tile pair), pairs a-major.
 // ------------------------------------------------------------------------------------------------
-namespace {
-constexpr int kGramThreads = 512;
-constexpr int kGramRing = 4;
-constexpr int kGramSlot = 2 * kGTile * 128;  // bytes per stage: both row blocks
-// at most N of this wave's loads outstanding (four per stage), then a barrier
-template <int N>
-__device__ __forceinline__ void gram_wait_barrier() {
-  static_assert(kGramRing == 4, "the wait counts follow the ring depth");
-  if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  else static_assert(N == 8, "unsupported count");
-}
-}  // namespace
-
-__global__ __launch_bounds__(kGramThreads) void am_gram(float* __restrict__ ws, AmCfg C, SeqTable T) {
+__global__ __launch_bounds__(kRingThreads) void am_gram(float* __restrict__ ws, AmCfg C, SeqTable T) {
   constexpr int kPitch = kGTile + 1;
-  __shared__ __attribute__((aligned(16))) uint8_t sm[kGramRing * kGramSlot];
+  __shared__ __attribute__((aligned(16))) uint8_t sm[kRing * kRingSlot];
   static_assert(sizeof(sm) >= sizeof(float) * kGTile * kPitch, "the epilogue tile fits the ring");
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
@@ -1339,80 +1334,12 @@ __global__ __launch_bounds__(kGramThreads) void am_gram(float* __restrict__ ws, 
   const int nst = W.rside ? ldm / 32 : (R + 31) / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int wr = wave & 1, wc = wave >> 1;
-  // this lane's DMA sources: byte offsets of its rows' first stage from the first row of the
-  // wave's row block (waves 0-3 land block a, waves 4-7 block b; a block's first row is live)
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  const int blk = wave_s < 4 ? a : b;
-  const float* Xb = X + (int64_t)blk * kGTile * pitch;
-  uint32_t voff[4];
-#pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int row = 8 * ((4 * wave + x) & 15) + (lane >> 3);
-    const int xr = min(blk * kGTile + row, xrows - 1) - blk * kGTile;
-    voff[x] = 4u * (uint32_t)(xr * pitch + 4 * ((lane & 7) ^ step_sw(row)));
-  }
-  const uint32_t ring = lds_addr(sm) + 4 * wave_s * 1024;
-  auto issue = [&](int stg) {
-    const float* src = Xb + 32 * min(stg, nst - 1);
-    const uint32_t slot = ring + (stg % kGramRing) * kGramSlot;
-#pragma unroll
-    for (int x = 0; x < 4; ++x) dma16_s(src, voff[x], slot + x * 1024);
-  };
-  // a stage's fragments (block a: four row fragments, block b: two; high and low halves)
-  struct Frags {
-    bf16x8 ah[4], al[4], bh[2], bl[2];
-  };
-  auto read = [&](int stg, Frags& f) {
-    const uint8_t* slot = sm + (stg % kGramRing) * kGramSlot;
-#pragma unroll
-    for (int y = 0; y < 2; ++y) {
-      const int rbw = 32 * wc + 16 * y + c16;
-      f.bh[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g)]);
-      f.bl[y] = *reinterpret_cast<const bf16x8*>(&slot[kGTile * 128 + sswz(rbw, 2 * g + 1)]);
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int ra = 64 * wr + 16 * x + c16;
-      f.ah[x] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
-      f.al[x] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
-    }
-  };
   f32x4 acc[4][2];
 #pragma unroll
   for (int x = 0; x < 4; ++x) acc[x][0] = acc[x][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  auto mma = [&](const Frags& f) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int y = 0; y < 2; ++y) {
-        acc[x][y] = mfma16(f.ah[x], f.bh[y], acc[x][y]);
-        acc[x][y] = mfma16(f.ah[x], f.bl[y], acc[x][y]);
-        acc[x][y] = mfma16(f.al[x], f.bh[y], acc[x][y]);
-      }
-  };
-  // Stage s's fragments are read into registers one stage early, so their LDS latency hides
-  // behind the MFMAs of stage s - 1: at the top of the iteration for stage s, stage s + 1 has
-  // landed (only stages s + 2 and s + 3, eight loads, may be outstanding), and after the barrier
-  // every wave holds stage s in registers, so its slot takes stage s + 4.
-  Frags f0, f1;
-#pragma unroll
-  for (int stg = 0; stg < kGramRing; ++stg) issue(stg);
-  gram_wait_barrier<12>();
-  read(0, f0);
-  auto iter = [&](int stg, Frags& cur, Frags& nxt) {
-    gram_wait_barrier<8>();
-    issue(stg + kGramRing);
-    read(stg + 1, nxt);
-    mma(cur);
-  };
-  int stg = 0;
-#pragma unroll 1
-  for (; stg + 1 < nst; stg += 2) {
-    iter(stg, f0, f1);
-    iter(stg + 1, f1, f0);
-  }
-  if (stg < nst) iter(stg, f0, f1);
-  vm_wait_barrier<0>();  // the refills past the last stage are in, and every wave is done with the ring
+  // a block's first row is live (128 (nt - 1) < Np <= xrows rounded up to 64)
+  ring_mma(X + (int64_t)a * kGTile * pitch, xrows - a * kGTile, X + (int64_t)b * kGTile * pitch, xrows - b * kGTile,
+           pitch, 0, nst, acc, sm);
 
   float* tl = reinterpret_cast<float*>(sm);
 #pragma unroll
@@ -1427,13 +1354,13 @@ __global__ __launch_bounds__(kGramThreads) void am_gram(float* __restrict__ ws, 
       }
   __syncthreads();
   float* Mh = W.Mg + (int64_t)h * Np * Np;
-  for (int q = tid; q < kGTile * (kGTile / 8); q += kGramThreads) {
+  for (int q = tid; q < kGTile * (kGTile / 8); q += kRingThreads) {
     const int r = q >> 4, gq = q & 15;
     if (a * kGTile + r < Np && b * kGTile + 8 * gq < Np)
       mg_put8(Mh, Np, a * kGTile + r, b * kGTile + 8 * gq, &tl[r * kPitch + 8 * gq]);
   }
   if (a != b) {
-    for (int q = tid; q < kGTile * (kGTile / 8); q += kGramThreads) {
+    for (int q = tid; q < kGTile * (kGTile / 8); q += kRingThreads) {
       const int c = q >> 4, gq = q & 15;
       if (b * kGTile + c >= Np || a * kGTile + 8 * gq >= Np) continue;
       float x[8];
@@ -1652,7 +1579,7 @@ hipError_t launch_am_target(int layout, const void* q, const void* k, const void
 }
 
 hipError_t launch_am_gemm(int kind, float* vc, float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
-  dim3 grid(T.total), block(256);
+  dim3 grid(T.total), block(kRingThreads);
   if (kind == 0) am_gemm<0><<<grid, block, 0, st>>>(vc, ws, C, T);
   else am_gemm<1><<<grid, block, 0, st>>>(vc, ws, C, T);
   return hipGetLastError();
@@ -1664,7 +1591,7 @@ hipError_t launch_am_step(float* vc, float* ws, const AmCfg& C, const SeqTable& 
 }
 
 hipError_t launch_am_gram(float* ws, const AmCfg& C, const SeqTable& T, hipStream_t st) {
-  am_gram<<<dim3(T.total), dim3(kGramThreads), 0, st>>>(ws, C, T);
+  am_gram<<<dim3(T.total), dim3(kRingThreads), 0, st>>>(ws, C, T);
   return hipGetLastError();
 }
 

@@ -743,18 +743,18 @@ static void am_splits(const kvc_shape* sh, const int32_t* m, int* S1, int* S2, i
     out2 += (int64_t)H * ldm * 128;
     st1 = std::min(st1, am_stages_rows(m[s]));
   }
-  // The split count that minimises rounds of workgroups (two per CU) x stages per split, plus
+  // The split count that minimises rounds of workgroups (one per CU) x stages per split, plus
   // the round trip of the partial products through memory: each split writes the whole output
   // once and the split sum reads it back (8 bytes per output element), priced against a round
-  // of stages, in which the 512 resident workgroups read 16 KB of the left operand each.
+  // of stages, in which the 256 resident workgroups read 16 KB of the left operand each.
   // Fewer splits on a tie.
   auto pick = [](int64_t tiles, int stages, int64_t out) {
     if (tiles == 0) return 1;
-    const double part = 8.0 * (double)out / (512.0 * 16384.0);
+    const double part = 8.0 * (double)out / (256.0 * 16384.0);
     int best = 1;
     double best_cost = 1e300;
     for (int sp = 1; sp <= 8 && sp <= std::max(1, stages / 4); ++sp) {
-      const int64_t rounds = (tiles * sp + 511) / 512, per = (stages + sp - 1) / sp;
+      const int64_t rounds = (tiles * sp + 255) / 256, per = (stages + sp - 1) / sp;
       const double cost = (double)(rounds * per) + (sp > 1 ? sp * part : 0.0);
       if (cost < best_cost) {
         best_cost = cost;

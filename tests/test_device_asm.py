@@ -4,8 +4,8 @@ Matching kernels set M0 themselves in inline assembly, which is only sound while
 compiler-generated instruction reads or writes M0 in those kernels; their stage loops wait for the
 loads they need only (a compiler-placed vmcnt(0) inside the loop would also wait for the loads
 meant to stay in flight); and the kernels that count their LDS-DMA loads in fixed waits (the
-few-row kernels, the value step, the Gram kernel) issue no other vector-memory access between the
-first of those loads and the last wait."""
+few-row kernels, the value step, the Gram kernel and the value products) issue no other
+vector-memory access between the first of those loads and the last wait."""
 import os
 import re
 import subprocess
@@ -196,14 +196,17 @@ def test_value_step_issues_only_its_dma_loads_in_the_ring(am_asm):
     assert code[iw + 1] == "s_barrier"
 
 
-def test_gram_issues_only_its_dma_loads_in_the_ring(am_asm):
-    """The Gram kernel's ring waits with a fixed count (four loads per wave per stage, two stages
-    in flight): between its first LDS-DMA load and the wait for all of them only those loads
-    touch memory, and the stage wait is vmcnt(8) followed by the barrier."""
-    (name, lines), = list(_functions(am_asm, "_ZN3kvc7am_gram"))
-    code = _ring_window(lines)
-    other = [t for t in code if re.match(r"(global|buffer|flat|scratch)_", t) and not t.startswith("global_load_lds_")]
-    assert not other, f"{name}: other vector-memory accesses among the counted loads: {other[:3]}"
-    assert len([t for t in code if t.startswith("global_load_lds_dwordx4")]) >= 8
-    iw = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(8)"))
-    assert code[iw + 1] == "s_barrier"
+def test_ring_products_issue_only_their_dma_loads_in_the_ring(am_asm):
+    """The tile products' ring (the Gram kernel and both value products) waits with a fixed count
+    (four loads per wave per stage, two stages in flight): between the first LDS-DMA load and the
+    wait for all of them only those loads touch memory, and the stage wait is vmcnt(8) followed
+    by the barrier."""
+    funcs = list(_functions(am_asm, "_ZN3kvc7am_gram")) + list(_functions(am_asm, "_ZN3kvc7am_gemm"))
+    assert len(funcs) == 3
+    for name, lines in funcs:
+        code = _ring_window(lines)
+        other = [t for t in code if re.match(r"(global|buffer|flat|scratch)_", t) and not t.startswith("global_load_lds_")]
+        assert not other, f"{name}: other vector-memory accesses among the counted loads: {other[:3]}"
+        assert len([t for t in code if t.startswith("global_load_lds_dwordx4")]) >= 8, name
+        iw = next(i for i, t in enumerate(code) if t.startswith("s_waitcnt vmcnt(8)"))
+        assert code[iw + 1] == "s_barrier", name
