@@ -31,11 +31,12 @@
 // St that of the target's keys,
 // Np the padded rows of the iteration's side (Rp or ldm); every array starts on a 256-byte
 // boundary):
-//   P [H][R][ldm] | PT [H][ldm][Rp] | Y [St][H][R][128] | ZT [H][128][Rp] | VT [H][128][ldm] |
+//   P [H][R128][ldm] | PT [H][L128][Rp] | Y [St][H][R][128] | ZT [H][128][Rp] | VT [H][128][ldm] |
 //   Zp [S1 > 1 ? S1 : 0][H][R][128] | Up [S2 > 1 ? S2 : 0][H][ldm][128] | part [H][NR][ldm] |
 //   b [H][ldm] | Mz [H] | eta [H] | ME [H] | ME as an ordered integer key [H] | Mg [H][Np][Np] |
 //   X, Sx [H][Np][128] | XT1 [H][128][Np] |
 //   KC [H][ldk][128] bf16 (ldk = m rounded up to 256)
+// (R128 and L128: R and ldm rounded up to 128; P and PT are held in the blocked split layout.)
 // Columns m .. ldm-1 of P_C hold zeros, so tiles never need a column bound on it.
 #include <type_traits>
 
@@ -52,6 +53,7 @@ constexpr int kD = kHeadDim;
 constexpr int kRowChunk = 64;  // rows per partial column sum
 
 __host__ __device__ constexpr int64_t pad64(int64_t x) { return (x + 63) & ~int64_t(63); }
+__host__ __device__ constexpr int64_t pad128(int64_t x) { return (x + 127) & ~int64_t(127); }
 __host__ __device__ constexpr int64_t pad256(int64_t x) { return (x + 255) & ~int64_t(255); }
 
 // E / P_C [H][R][ldm], PT [H][ldm][Rp], ZT [H][128][Rp] and VT [H][128][ldm] (Rp = R rounded up
@@ -97,6 +99,22 @@ __device__ __forceinline__ void put_split8(float* row, int g, const float* x) {
   d[0] = hi;
   d[1] = lo;
 }
+// The blocked split layout of P_C and P_C^T, as the tile products (ring_mma) read them: per
+// 128-row block and 32-column stage a 16 KB block of 128 rows x 128 bytes (the four 8-column
+// groups of the split layout, high half then low half), 16-byte chunk c of row r at position
+// c ^ step_sw(r) (the low three bits of r with bits 0 and 1 swapped: the bank-conflict-free
+// placement of the products' LDS ring); blocks stage-major within a row block, so a row block
+// of a matrix with ncols columns spans 128 ncols floats (rows past the last live row of the last
+// block are never written and never reach a kept product).
+__device__ __forceinline__ int step_sw(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
+__device__ __forceinline__ void blk_put8(float* base, int ncols, int r, int c, const float* x) {
+  u32x4 hi, lo;
+  split8(x, hi, lo);
+  const int row = r & 127, grp = (c & 31) >> 3, sw = step_sw(row);
+  uint8_t* blk = reinterpret_cast<uint8_t*>(base) + (((int64_t)(r >> 7) * (ncols >> 5) + (c >> 5)) << 14) + row * 128;
+  *reinterpret_cast<u32x4*>(blk + (((2 * grp) ^ sw) << 4)) = hi;
+  *reinterpret_cast<u32x4*>(blk + (((2 * grp + 1) ^ sw) << 4)) = lo;
+}
 // element k of a split row
 __device__ __forceinline__ void put_split1(float* row, int k, float x) {
   uint16_t* d = reinterpret_cast<uint16_t*>(row + 8 * (k >> 3));
@@ -116,8 +134,8 @@ __device__ __forceinline__ AmWs am_ws(float* ws, const SeqTable& T, int i, const
   w.Np = w.rside ? (int)Rp : (int)ldm;
   const int64_t Np = w.Np;
   w.P = ws + T.off[i];
-  w.PT = w.P + pad64(H * R * ldm);
-  w.Y = w.PT + pad64(H * ldm * Rp);
+  w.PT = w.P + pad64(H * pad128(R) * ldm);
+  w.Y = w.PT + pad64(H * pad128(ldm) * Rp);
   w.ZT = w.Y + C.St * pad64(H * R * kD);
   w.VT = w.ZT + pad64(H * kD * Rp);
   w.Zp = w.VT + pad64(H * kD * ldm);
@@ -154,7 +172,8 @@ int64_t am_seq_floats(int H, int R, int n, int m, int S1, int S2, int St) {
   const int64_t ldm = pad64(m), nr = (R + kRowChunk - 1) / kRowChunk, Rp = pad64(R);
   const int64_t Np = am_rows_side(R, m) ? Rp : ldm;
   const int64_t rk = pad64((int64_t)H * R * kD), xk = pad64((int64_t)H * Np * kD);
-  return pad64((int64_t)H * R * ldm) + pad64((int64_t)H * ldm * Rp) + St * rk + pad64((int64_t)H * kD * Rp) +
+  return pad64((int64_t)H * pad128(R) * ldm) + pad64((int64_t)H * pad128(ldm) * Rp) + St * rk +
+         pad64((int64_t)H * kD * Rp) +
          pad64((int64_t)H * kD * ldm) + (S1 > 1 ? S1 : 0) * rk +
          (S2 > 1 ? S2 : 0) * pad64((int64_t)H * ldm * kD) + pad64((int64_t)H * nr * ldm) +
          pad64((int64_t)H * ldm) + pad64(4 * (int64_t)H) + pad64((int64_t)H * Np * Np) + 3 * xk + pad64((int64_t)H * pad256(m) * (kD / 2));
@@ -576,9 +595,9 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
     // pass C, one step at a time: P_C of the tile's 64 rows x 256 keys, its column partials, then
     // the tile through LDS (in place of the step's keys once every wave has used them; row r at
     // float r * 256 + (key ^ 16 ((r >> 2) & 3)), so the lane groups' rows spread over the banks)
-    // and out as split rows of P_C (8 keys per group) and of P_C^T (8 rows per group)
-    float* Pu = W.P + (int64_t)h * R * W.ldm;
-    float* PTu = W.PT + (int64_t)h * W.ldm * W.Rp;
+    // and out in the blocked split layout of P_C (8 keys per group) and of P_C^T (8 rows per group)
+    float* Pu = W.P + (int64_t)h * pad128(R) * W.ldm;
+    float* PTu = W.PT + (int64_t)h * pad128(W.ldm) * W.Rp;
     issue(0, 0);
     land(0);
 #pragma unroll 1
@@ -621,7 +640,7 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
           float x[8];
 #pragma unroll
           for (int k = 0; k < 8; ++k) x[k] = pl[r * kBiasStep + ((8 * gq + k) ^ (16 * ((r >> 2) & 3)))];
-          put_split8(Pu + (int64_t)row * W.ldm + st * kBiasStep, gq, x);
+          blk_put8(Pu, W.ldm, row, st * kBiasStep + 8 * gq, x);
         }
       }
       for (int qq = tid; qq < kBiasStep * 8; qq += kBiasThreads) {  // rows of P_C^T
@@ -634,7 +653,7 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
             const int r = 8 * gq + k;
             x[k] = pl[r * kBiasStep + (c ^ (16 * ((r >> 2) & 3)))];
           }
-          put_split8(PTu + (int64_t)key * W.Rp + rt * 64, gq, x);
+          blk_put8(PTu, W.Rp, key, rt * 64 + 8 * gq, x);
         }
       }
       __syncthreads();  // the tile is out before the buffer is staged again
@@ -900,7 +919,6 @@ constexpr int kGTile = 128;
 constexpr int kRingThreads = 512;
 constexpr int kRing = 4;
 constexpr int kRingSlot = 2 * kGTile * 128;  // bytes per stage: both row blocks
-__device__ __forceinline__ int step_sw(int r) { return ((r & 1) << 1) | ((r >> 1) & 1) | (r & 4); }
 __device__ __forceinline__ int sswz(int row, int chunk) { return row * 128 + ((chunk ^ step_sw(row)) << 4); }
 // at most N of this wave's loads outstanding (four per stage), then a barrier
 template <int N>
@@ -911,27 +929,31 @@ __device__ __forceinline__ void ring_wait_barrier() {
   else static_assert(N == 8, "unsupported count");
 }
 
-// acc += A B^T over contraction stages st0 .. st1 - 1 of one tile. Xa, Xb: the first rows of
-// the A and B blocks (split rows, pitch floats); la, lb (at least 1): their live rows. sm: the
-// ring (kRing * kRingSlot bytes); when this returns every wave is done with it.
-__device__ __forceinline__ void ring_mma(const float* Xa, int la, const float* Xb, int lb, int pitch, int st0,
+// acc += A B^T over contraction stages st0 .. st1 - 1 of one tile. Xa, Xb: the A and B row
+// blocks, each either in the blocked split layout (blk_put8; pitch 0: a stage is 16 KB in the
+// ring's order already) or as split rows with a pitch of pa / pb floats (the lane reads chunk
+// (L % 8) ^ step_sw(row) of its row; la, lb (at least 1): the live rows, later rows read the last
+// live one). sm: the ring (kRing * kRingSlot bytes); when this returns every wave is done with it.
+__device__ __forceinline__ void ring_mma(const float* Xa, int la, int pa, const float* Xb, int lb, int pb, int st0,
                                          int st1, f32x4 (&acc)[4][2], uint8_t* sm) {
   if (st0 >= st1) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
   const int wr = wave & 1, wc = wave >> 1;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const float* Xw = wave_s < 4 ? Xa : Xb;  // the wave's block
-  const int lw = wave_s < 4 ? la : lb;
-  // this lane's DMA sources: byte offsets of its rows' chunks from the block's first row
+  const int lw = wave_s < 4 ? la : lb, pw = wave_s < 4 ? pa : pb;
+  const int sstep = pw ? 32 : 4096;  // floats per stage
+  // this lane's DMA sources: byte offsets from the block's first stage
   uint32_t voff[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int row = 8 * ((4 * wave + x) & 15) + (lane >> 3);
-    voff[x] = 4u * (uint32_t)(min(row, lw - 1) * pitch + 4 * ((lane & 7) ^ step_sw(row)));
+    const int piece = (4 * wave + x) & 15, row = 8 * piece + (lane >> 3);
+    voff[x] = pw ? 4u * (uint32_t)(min(row, lw - 1) * pw + 4 * ((lane & 7) ^ step_sw(row)))
+                 : 16u * (uint32_t)(64 * piece + lane);
   }
   const uint32_t ring = lds_addr(sm) + 4 * wave_s * 1024;
   auto issue = [&](int stg) {
-    const float* src = Xw + 32 * min(stg, st1 - 1);
+    const float* src = Xw + (int64_t)sstep * min(stg, st1 - 1);
     const uint32_t slot = ring + ((stg - st0) % kRing) * kRingSlot;
 #pragma unroll
     for (int x = 0; x < 4; ++x) dma16_s(src, voff[x], slot + x * 1024);
@@ -1022,7 +1044,7 @@ __global__ __launch_bounds__(kRingThreads) void am_gemm(float* __restrict__ vc_a
   const int64_t unit = (int64_t)s * C.H + h;
   // A rows (pitch apitch) and B rows (the 128 columns of the right operand, pitch bpitch)
   const int apitch = KIND == 0 ? ldm : W.Rp;
-  const float* A = KIND == 0 ? W.P + (int64_t)h * R * ldm : W.PT + (int64_t)h * ldm * W.Rp;
+  const float* A = KIND == 0 ? W.P + (int64_t)h * pad128(R) * ldm : W.PT + (int64_t)h * pad128(ldm) * W.Rp;
   const float* B = KIND == 0 ? W.VT + (int64_t)h * kD * ldm : (C.xsel ? W.XT1 : W.ZT) + (int64_t)h * kD * W.Rp;
   const int nst = KIND == 0 ? ldm / 32 : (R + 31) / 32;
   const int per = (nst + S - 1) / S;
@@ -1034,7 +1056,7 @@ __global__ __launch_bounds__(kRingThreads) void am_gemm(float* __restrict__ vc_a
   f32x4 acc[4][2];
 #pragma unroll
   for (int a = 0; a < 4; ++a) acc[a][0] = acc[a][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  ring_mma(A + (int64_t)tile * kGTile * apitch, alim - tile * kGTile, B, kD, apitch, st0, st1, acc, sm);
+  ring_mma(A + (int64_t)tile * kGTile * apitch, alim - tile * kGTile, 0, B, kD, apitch, st0, st1, acc, sm);
 
   const float eta = W.eta[h];
 #pragma unroll
@@ -1328,7 +1350,7 @@ __global__ __launch_bounds__(kRingThreads) void am_gram(float* __restrict__ ws, 
     ++a;
   }
   const int b = a + p;
-  const float* X = W.rside ? W.P + (int64_t)h * R * ldm : W.PT + (int64_t)h * ldm * W.Rp;
+  const float* X = W.rside ? W.P + (int64_t)h * pad128(R) * ldm : W.PT + (int64_t)h * pad128(ldm) * W.Rp;
   const int pitch = W.rside ? ldm : W.Rp;
   const int xrows = W.rside ? R : ldm;
   const int nst = W.rside ? ldm / 32 : (R + 31) / 32;
@@ -1337,9 +1359,8 @@ __global__ __launch_bounds__(kRingThreads) void am_gram(float* __restrict__ ws, 
   f32x4 acc[4][2];
 #pragma unroll
   for (int x = 0; x < 4; ++x) acc[x][0] = acc[x][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // a block's first row is live (128 (nt - 1) < Np <= xrows rounded up to 64)
-  ring_mma(X + (int64_t)a * kGTile * pitch, xrows - a * kGTile, X + (int64_t)b * kGTile * pitch, xrows - b * kGTile,
-           pitch, 0, nst, acc, sm);
+  ring_mma(X + (int64_t)a * kGTile * pitch, xrows - a * kGTile, 0, X + (int64_t)b * kGTile * pitch, xrows - b * kGTile,
+           0, 0, nst, acc, sm);
 
   float* tl = reinterpret_cast<float*>(sm);
 #pragma unroll
