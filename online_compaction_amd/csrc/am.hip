@@ -720,7 +720,7 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
 // a workgroup re-reads only its share of K and V, and there are C.St times as many of them.
 // Eight waves: wave w owns rows 32 w .. + 31 of the block (two 16-row fragments) and all 128
 // output columns. Per 64-key chunk, staged through double-buffered LDS (key and value rows alike
-// as bf16 rows, chunk c of row r at c ^ (r & 15)):
+// as bf16 rows, chunk c of key row r at c ^ (r & 15), of value row r at c ^ 2 (r & 7)):
 //   S^T = K Q^T   per row fragment 16 v_mfma_f32_16x16x32_bf16 (the fragment's query rows stay in
 //                 registers as the B operand; a key fragment read serves both row fragments), so
 //                 lane (g, c16) holds row c16's logits of keys 16 sub + 4 g + x;
@@ -740,11 +740,16 @@ constexpr int kTgtRows = 256;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16;
 
+// Value rows in LDS: 16-byte chunk c of key row r at position c ^ 2 (r & 7). A transposing read
+// (8 bytes per lane; gfx950 serves such reads as two groups of 32 lanes over 64 banks) then has
+// each 32-lane group's 8 keys x 2 chunks land on the 16 distinct chunk positions of a 256-byte
+// window: free of bank conflicts (with the score kernels' c ^ (r & 15) it took two cycles).
+__device__ __forceinline__ int vswz(int row, int chunk) { return row * 256 + ((chunk ^ (2 * (row & 7))) << 4); }
 // four consecutive bf16 values of one value column (keys k0 .. k0 + 3) for each lane of a
 // 16-lane group: lane j addresses key k0 + j / 4, columns col0 + 4 (j % 4) .. + 3
 __device__ __forceinline__ v4i16 tr_read(const uint8_t* rows, int k0, int col0, int j) {
   const int key = k0 + (j >> 2), col = col0 + 4 * (j & 3);
-  const uint8_t* p = rows + swz(key, col >> 3) + 8 * ((col >> 2) & 1);
+  const uint8_t* p = rows + vswz(key, col >> 3) + 8 * ((col >> 2) & 1);
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16)(__attribute__((address_space(3))) const void*)p);
 }
 }  // namespace
@@ -809,7 +814,7 @@ __global__ __launch_bounds__(kTgtThreads, 1) void am_target(const uint16_t* __re
     for (int x = 0; x < 2; ++x) {
       const int key = x * 32 + (tid >> 4), ch = tid & 15;
       *reinterpret_cast<u32x4*>(&Ks[buf][swz(key, ch)]) = kr[x];
-      *reinterpret_cast<u32x4*>(&Vs[buf][swz(key, ch)]) = vr[x];
+      *reinterpret_cast<u32x4*>(&Vs[buf][vswz(key, ch)]) = vr[x];
     }
   };
 
