@@ -1125,9 +1125,10 @@ __global__ __launch_bounds__(kRingThreads) void am_gemm(float* __restrict__ vc_a
 // side), with its epilogue fused: no split of the contraction, so no partial products. The
 // product is bound by reading Mg (4 bytes per entry, once per step); its right operand, the
 // iterate's transpose (split rows [128][Np]), is shared by all row tiles of a unit and read from
-// L2. One 64 x 128 output tile per workgroup of eight waves (wave w: rows 16 (w & 3) .. + 15,
-// columns 64 (w >> 2) .. + 63: four 16 x 16 accumulators), operands split as in am_gemm (three
-// bf16 products). The contraction runs in stages of 32 through a ring of kStepRing LDS slots
+// L2. One 64 x 128 output tile per workgroup of eight waves (wave w: rows 32 (w & 1) .. + 31,
+// columns 32 (w >> 1) .. + 31: two x two 16 x 16 accumulators, eight operand reads per stage),
+// operands split as in am_gemm (three bf16 products). The contraction runs in stages of 32
+// through a ring of kStepRing LDS slots
 // filled by LDS-DMA (global_load_lds_dwordx4, three per wave per stage) kStepRing stages ahead
 // of the stage whose MFMAs run (deep enough that the bytes in flight cover the memory latency
 // at full rate; a stage's fragments are read into registers one stage before its MFMAs): a
@@ -1189,7 +1190,7 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   const float* B = am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel) + (int64_t)h * kD * Np;
   const int nst = Np / 32;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 4, c16 = lane & 15;
-  const int wr = wave & 3, wc = wave >> 2;
+  const int wr = wave & 1, wc = wave >> 1;  // the wave's 32 rows and 32 columns of the tile
   // this lane's DMA sources: the three 1 KB pieces (8 rows x 128 bytes) of a stage that wave w
   // lands are pieces 3 w .. 3 w + 2 of the 24 (8 of A, then 16 of B); lane L lands row L / 8 of
   // its piece at position L % 8. A is stored in that order already (a stage is 8 KB further on);
@@ -1217,41 +1218,51 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   // the epilogue's operands (this lane's 16 entries of X and of Sx; rows past N are zero) are
   // loaded before the ring starts, so their latency hides behind the product (they are older
   // than every ring load, so the ring's in-order waits cover them)
-  float xo[4][4], so[4][4];
+  // accumulator (a, b) of the wave, element e: tile row 32 wr + 16 a + 4 g + e, column
+  // 32 wc + 16 b + c16
+  float xo[2][2][4], so[2][2][4];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t ox = ((int64_t)h * Np + blk * kStepRows + 16 * wr + 4 * g + e) * kD + 64 * wc + 16 * b + c16;
-      xo[b][e] = W.X[ox];
-      so[b][e] = W.Sx[ox];
-    }
-  f32x4 acc[4];
+    for (int b = 0; b < 2; ++b)
 #pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-  // a stage's fragments: the wave's 16 rows of Mg and its 64 columns of the iterate, high and low
+      for (int e = 0; e < 4; ++e) {
+        const int64_t ox = ((int64_t)h * Np + blk * kStepRows + 32 * wr + 16 * a + 4 * g + e) * kD + 32 * wc +
+                           16 * b + c16;
+        xo[a][b][e] = W.X[ox];
+        so[a][b][e] = W.Sx[ox];
+      }
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) acc[a][0] = acc[a][1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  // a stage's fragments: the wave's 32 rows of Mg and its 32 columns of the iterate, high and low
   struct Frags {
-    bf16x8 ah, al, bh[4], bl[4];
+    bf16x8 ah[2], al[2], bh[2], bl[2];
   };
   auto read = [&](int stg, Frags& f) {
     const uint8_t* slot = sm + (stg % kStepRing) * kStepSlot;
-    const int ra = 16 * wr + c16;
-    f.ah = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
-    f.al = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int rbw = 64 * wc + 16 * b + c16;
+    for (int a = 0; a < 2; ++a) {
+      const int ra = 32 * wr + 16 * a + c16;
+      f.ah[a] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g)]);
+      f.al[a] = *reinterpret_cast<const bf16x8*>(&slot[sswz(ra, 2 * g + 1)]);
+    }
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int rbw = 32 * wc + 16 * b + c16;
       f.bh[b] = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g)]);
       f.bl[b] = *reinterpret_cast<const bf16x8*>(&slot[kStepA + sswz(rbw, 2 * g + 1)]);
     }
   };
   auto mma = [&](const Frags& f) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      acc[b] = mfma16(f.ah, f.bh[b], acc[b]);
-      acc[b] = mfma16(f.ah, f.bl[b], acc[b]);
-      acc[b] = mfma16(f.al, f.bh[b], acc[b]);
-    }
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        acc[a][b] = mfma16(f.ah[a], f.bh[b], acc[a][b]);
+        acc[a][b] = mfma16(f.ah[a], f.bl[b], acc[a][b]);
+        acc[a][b] = mfma16(f.al[a], f.bh[b], acc[a][b]);
+      }
   };
   // Stage s's fragments are read into registers one stage early, so their LDS latency hides
   // behind the MFMAs of stage s - 1: at the top of the iteration for stage s, stage s + 1 has
@@ -1283,32 +1294,36 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   const float eta = W.eta[h];
   const bool to_vc = C.mode == 1 && !W.rside;
   float* vcu = vc_all + unit * C.m_max * (int64_t)kD;
-  float vo[4][4];  // the last step of the keys side: this lane's entries of Vc (rows clamped below m)
+  float vo[2][2][4];  // the last step of the keys side: this lane's entries of Vc (rows clamped below m)
   if (to_vc) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = blk * kStepRows + 16 * wr + 4 * g + e;
-        vo[b][e] = vcu[(int64_t)min(r, m - 1) * kD + 64 * wc + 16 * b + c16];
-      }
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = blk * kStepRows + 32 * wr + 16 * a + 4 * g + e;
+          vo[a][b][e] = vcu[(int64_t)min(r, m - 1) * kD + 32 * wc + 16 * b + c16];
+        }
   }
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int rl = 16 * wr + 4 * g + e, r = blk * kStepRows + rl, col = 64 * wc + 16 * b + c16;
-      const float xn = xo[b][e] - eta * acc[b][e];
-      const float sum = so[b][e] + xn;
-      const bool live = r < W.N;
-      if (live) {
-        const int64_t ox = ((int64_t)h * Np + r) * kD + col;
-        W.X[ox] = xn;
-        W.Sx[ox] = sum;
-        if (to_vc && r < m) vcu[(int64_t)r * kD + col] = vo[b][e] - eta * sum;
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rl = 32 * wr + 16 * a + 4 * g + e, r = blk * kStepRows + rl, col = 32 * wc + 16 * b + c16;
+        const float xn = xo[a][b][e] - eta * acc[a][b][e];
+        const float sum = so[a][b][e] + xn;
+        const bool live = r < W.N;
+        if (live) {
+          const int64_t ox = ((int64_t)h * Np + r) * kD + col;
+          W.X[ox] = xn;
+          W.Sx[ox] = sum;
+          if (to_vc && r < m) vcu[(int64_t)r * kD + col] = vo[a][b][e] - eta * sum;
+        }
+        tl[rl * (kD + 1) + col] = live ? (C.mode == 1 ? sum : xn) : 0.0f;
       }
-      tl[rl * (kD + 1) + col] = live ? (C.mode == 1 ? sum : xn) : 0.0f;
-    }
   if (to_vc) return;  // uniform across the block
   __syncthreads();
   float* dst = am_xt(W.XT1, W.ZT, W.VT, W.rside, C.xsel ^ 1) + (int64_t)h * kD * Np + blk * kStepRows;
