@@ -238,7 +238,10 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       float sst[kSub];
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub) sst[sub] = 0.0f;
-#pragma unroll 1
+      // the four 16-key tiles unrolled (fewer branches and loop instructions per stage) where
+      // the registers allow it: outside the slot map, and with a bias only for paged keys
+      // without the causal mask
+#pragma unroll((LAYOUT != kSlots && (!BIAS || (LAYOUT == kPaged && !CAUSAL))) ? kStage / 16 : 1)
       for (int kt = 0; kt < kStage / 16; ++kt) {
         f32x4 kt4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (MASK) kt4 = key_term(buf, k0, kt);
