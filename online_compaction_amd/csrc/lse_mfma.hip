@@ -24,6 +24,14 @@ constexpr int kLseBufs = 3;             // LDS stage buffers (two loads in fligh
 
 }  // namespace
 
+// 16-key tiles per unrolled step of the cheap form: all four (fewer branches and loop instructions
+// per stage) where the registers allow it, outside the slot map and, with a bias, only for paged
+// keys without the causal mask
+template <int LAYOUT, bool BIAS, bool CAUSAL>
+constexpr int lse_lazy_unroll() {
+  return (LAYOUT != kSlots && (!BIAS || (LAYOUT == kPaged && !CAUSAL))) ? kStage / 16 : 1;
+}
+
 // ------------------------------------------------------------------------------------------------
 // Per proxy row, partial (reference, sum) of 2^(log2e * l_rj) over one key chunk, with the
 // reference exponent moved only when a tile's sum would leave the float range (see below).
@@ -238,10 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       float sst[kSub];
 #pragma unroll
       for (int sub = 0; sub < kSub; ++sub) sst[sub] = 0.0f;
-      // the four 16-key tiles unrolled (fewer branches and loop instructions per stage) where
-      // the registers allow it: outside the slot map, and with a bias only for paged keys
-      // without the causal mask
-#pragma unroll((LAYOUT != kSlots && (!BIAS || (LAYOUT == kPaged && !CAUSAL))) ? kStage / 16 : 1)
+#pragma unroll lse_lazy_unroll<LAYOUT, BIAS, CAUSAL>()
       for (int kt = 0; kt < kStage / 16; ++kt) {
         f32x4 kt4 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (MASK) kt4 = key_term(buf, k0, kt);
