@@ -120,18 +120,26 @@ class Shape:
     def c(self):
         lens = np.ascontiguousarray(np.asarray(self.seq_lens, dtype=np.int32))
         starts = None
-        sp = None
         if self.seq_starts is not None:
             starts = np.ascontiguousarray(np.asarray(self.seq_starts, dtype=np.int32))
-            sp = starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         if self.row_pos is not None and not isinstance(self.row_pos, int):
             if str(self.row_pos.dtype) != "torch.int32":
                 raise ValueError(f"row_pos: int32 tensor required, got {self.row_pos.dtype}")
             _need(self.row_pos, self.num_seqs * self.num_kv_heads * self.group * self.num_queries * 4, "row_pos")
+        rp = _ptr(self.row_pos)
+        # the struct of the previous call is reused while every field holds the same values (numpy's
+        # ctypes pointers cost a few microseconds per call)
+        key = (self.num_seqs, self.num_kv_heads, self.group, self.num_queries, self.head_dim, self.n_max,
+               lens.tobytes(), None if starts is None else starts.tobytes(), float(self.scale), rp)
+        hit = self.__dict__.get("_c_cached")
+        if hit is not None and hit[0] == key:
+            return hit[1], hit[2]
+        sp = None if starts is None else starts.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
         sh = _Shape(self.num_seqs, self.num_kv_heads, self.group, self.num_queries, self.head_dim, self.n_max,
-                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(self.scale), sp,
-                    _ptr(self.row_pos))
-        return sh, (lens, starts)  # keep the arrays alive while `sh` is used
+                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), float(self.scale), sp, rp)
+        keep = (lens, starts)  # keeps the arrays alive while `sh` is used
+        self.__dict__["_c_cached"] = (key, sh, keep)
+        return sh, keep
 
 
 @dataclass
@@ -174,6 +182,9 @@ def _stream(stream):
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
     import torch
+    raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)  # the handle without a Stream object
+    if raw is not None:
+        return raw(torch.cuda.current_device())
     return torch.cuda.current_stream().cuda_stream
 
 
