@@ -323,16 +323,6 @@ __global__ __launch_bounds__(256) void am_gather(const uint16_t* __restrict__ k,
 namespace {
 constexpr int kBiasThreads = 512;
 constexpr int kBiasStep = 256;  // kept keys per step (KC rows are padded to a multiple)
-// LDS-DMA load (as dma16) addressed by a wave-uniform base in SGPRs plus a 32-bit per-lane byte
-// offset, with the LDS destination already wave-uniform: no per-lane 64-bit address arithmetic
-// and no read of the destination from a vector register
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_dst) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_dst)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
 }  // namespace
 
 template <int MODE>

@@ -32,6 +32,13 @@ constexpr int lse_lazy_unroll() {
   return (LAYOUT != kSlots && (!BIAS || (LAYOUT == kPaged && !CAUSAL))) ? kStage / 16 : 1;
 }
 
+// whether full stages are loaded from scalar bases and run in a loop of their own (unmasked,
+// without a bias or the causal mask, outside the slot map)
+template <int LAYOUT, bool BIAS, bool CAUSAL>
+constexpr bool lse_scalar_dma() {
+  return !BIAS && !CAUSAL && LAYOUT != kSlots;
+}
+
 // ------------------------------------------------------------------------------------------------
 // Per proxy row, partial (reference, sum) of 2^(log2e * l_rj) over one key chunk, with the
 // reference exponent moved only when a tile's sum would leave the float range (see below).
@@ -149,19 +156,55 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // XOR-swizzled) plus, with a bias, one 4-byte load of its 16 keys' bias. Keys past the chunk
   // load the chunk's last row (finite bytes, masked in the epilogue).
   // paged, a full stage: lane row j's key is 64 st further on, so its block-table slot moves by 4
-  // per stage and its place inside the block (and so its offset past the block's start) stays
-  int slot0[4], loff[4];
+  // per stage and its place inside the block (and so its byte offset koff[j] past the block's
+  // start, below) stays
+  int slot0[4];
   if constexpr (LAYOUT == kPaged) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = (wave * 4 + j) * 4 + (lane >> 4), pos = ko + kbeg + row;
-      slot0[j] = (pos >> 4) - blk0;
-      loff[j] = ((pos & 15) * H + h) * (kHeadDim / 8) + ((lane & 15) ^ (row & 15));
+    for (int j = 0; j < 4; ++j) slot0[j] = ((ko + kbeg + (wave * 4 + j) * 4 + (lane >> 4)) >> 4) - blk0;
+  }
+  // A full stage of a contiguous cache, or of a paged one whose segment starts 4-aligned (each
+  // load's four rows then lie in one block), is addressed from scalar bases (the stage's first
+  // key row, or the block's start) plus per-lane byte offsets that are the same for every stage,
+  // and its LDS destinations are scalar: its loads cost no vector instructions beyond reading the
+  // four block numbers.
+  constexpr bool kSdma = lse_scalar_dma<LAYOUT, BIAS, CAUSAL>();
+  const bool sdma = kSdma && (LAYOUT != kPaged || (ko & 3) == 0);
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t ks_lds = lds_addr(&ks_[0][0]) + wave_s * 4 * 1024;
+  uint32_t koff[4];
+  int sl0[4];  // paged: the block-table slot of load j's rows at stage 0 (the same for all its lanes)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 4 + (lane >> 4), chunk = (lane & 15) ^ (row & 15);
+    if constexpr (LAYOUT == kPaged) {
+      koff[j] = (((ko + kbeg + row) & 15) * H + h) * 256 + chunk * 16;
+      sl0[j] = ((ko + kbeg + (wave_s * 4 + j) * 4) >> 4) - blk0;
+    } else {
+      koff[j] = row * 256 + chunk * 16;
+      sl0[j] = 0;
     }
   }
   auto issue = [&](int st) {
     const int k0 = kbeg + st * kStage;
     const int b = st % kLseBufs;
+    if (kSdma && sdma && k0 + kStage <= kend) {
+      if constexpr (LAYOUT == kPaged) {
+        int e[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) e[j] = idx[sl0[j] + 4 * st];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t blk = __builtin_amdgcn_readfirstlane(e[j]);
+          dma16_s(k + blk * (16 * H * kHeadDim), koff[j], ks_lds + b * (kStage * 256) + j * 1024);
+        }
+      } else {
+        const uint16_t* base = k + (unit * n_max + ko + k0) * kHeadDim;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16_s(base, koff[j], ks_lds + b * (kStage * 256) + j * 1024);
+      }
+      return;
+    }
     // the four sources first (their table entries are LDS reads that then complete together),
     // then the four loads
     const u32x4* src[4];
@@ -169,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
       const u32x4* pool = reinterpret_cast<const u32x4*>(k);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        src[j] = pool + (int64_t)idx[slot0[j] + 4 * st] * (16 * H * (kHeadDim / 8)) + loff[j];
+        src[j] = pool + (int64_t)idx[slot0[j] + 4 * st] * (16 * H * (kHeadDim / 8)) + (koff[j] >> 4);
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -321,7 +364,20 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   if (nst > 0) issue(0);  // (causal rows may leave a workgroup nothing to do)
   if (nst > 1) issue(1);
-  for (int st = 0; st < nst; ++st) {
+  // the stages that need no per-key term run in a loop of their own (one code path, so the sums
+  // stay in place from one stage to the next); the masked last stage, and every stage of the
+  // other variants, follow in the general loop
+  const int nplain = kSdma ? (kend - kbeg) / kStage : 0;
+  for (int st = 0; st < nplain; ++st) {
+    if (st + 1 < nst) {
+      vm_wait_barrier<kLoadsPerStage>();
+    } else {
+      vm_wait_barrier<0>();
+    }
+    if (st + 2 < nst) issue(st + 2);
+    stage(st % kLseBufs, kbeg + st * kStage, std::false_type{}, std::false_type{});
+  }
+  for (int st = nplain; st < nst; ++st) {
     if (st + 1 < nst) {
       vm_wait_barrier<kLoadsPerStage>();
     } else {

@@ -62,6 +62,17 @@ __device__ __forceinline__ void dma4(const float* src, const void* dst) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr(dst));
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
 }
+// The same loads addressed by a wave-uniform base in SGPRs plus a 32-bit per-lane byte offset,
+// with the LDS destination already wave-uniform: no per-lane 64-bit address arithmetic and no
+// read of the destination from a vector register.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_dst)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_dst)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Wait until at most N of this wave's vector-memory loads are outstanding (the LDS-DMA loads

@@ -24,6 +24,20 @@ namespace {
 #endif
 constexpr int kBufs = 3;  // LDS stage buffers (two loads in flight)
 
+// 16-row tiles per unrolled step of a stage: all four (their LDS offsets become immediates), but
+// one at a time where the registers would not hold them (nine key subtiles per wave, or the
+// biased causal slot-map variant)
+template <int LAYOUT, bool BIAS, bool CAUSAL, int KSUB>
+constexpr int score_rt_unroll() {
+  return (KSUB == 9 || (CAUSAL && BIAS && LAYOUT == kSlots)) ? 1 : kStage / 16;
+}
+// whether full stages of rows are loaded from a scalar base and run in a loop of their own (stored
+// row order, and registers to spare: not with nine biased key subtiles per wave)
+template <bool BIAS, bool CAUSAL, int KSUB>
+constexpr bool score_scalar_dma() {
+  return !CAUSAL && !(BIAS && KSUB == 9);
+}
+
 }  // namespace
 
 // ------------------------------------------------------------------------------------------------
@@ -101,10 +115,28 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   // A stage (64 proxy rows) goes global -> LDS without passing through registers: each wave
   // issues 4 16-byte-per-lane LDS-DMA loads (4 rows each, the lane's chunk chosen so the rows
   // land XOR-swizzled) and one 4-byte load of its 16 rows' LSE. Rows past R load row R - 1
-  // (finite bytes, masked in the epilogue).
+  // (finite bytes, masked in the epilogue). A full stage of rows in stored order is addressed
+  // from the stage's first row (a scalar base) plus per-lane offsets that are the same for every
+  // stage, and its LDS destinations are scalar too, so its loads cost no vector instructions.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t qs_lds = lds_addr(&qs[0][0]) + wave_s * 4 * 1024, ls_lds = lds_addr(&lss[0][0]) + wave_s * 16 * 4;
+  uint32_t qoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = (wave * 4 + j) * 4 + (lane >> 4);
+    qoff[j] = row * 256 + (((lane & 15) ^ (row & 15)) << 4);
+  }
+  const uint32_t loff = (wave * 16 + lane) * 4;
   auto issue = [&](int st) {
     const int r0 = st * kStage;
     const int b = st % kBufs;
+    if (score_scalar_dma<BIAS, CAUSAL, KSUB>() && r0 + kStage <= R) {
+      const uint16_t* qb0 = qu + (int64_t)r0 * kHeadDim;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dma16_s(qb0, qoff[j], qs_lds + b * (kStage * 256) + j * 1024);
+      if (lane < 16) dma4_s(lu + r0, loff, ls_lds + b * (kStage * 4));
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = (wave * 4 + j) * 4 + (lane >> 4);
@@ -131,7 +163,7 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   auto stage = [&](int buf, int r0, auto masked, auto causal) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr bool CM = decltype(causal)::value;  // mask element by element (rows near the keys)
-#pragma unroll 1
+#pragma unroll score_rt_unroll<LAYOUT, BIAS, CAUSAL, KSUB>()
     for (int rt = 0; rt < kStage / 16; ++rt) {
       const int row = rt * 16 + c16;
       bf16x8 a[4];
@@ -181,7 +213,21 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   issue(0);
   if (nst > 1) issue(1);
-  for (int st = 0; st < nst; ++st) {
+  // Without the causal mask the stages whose rows are all live run in a loop of their own (one
+  // code path, so the row sums stay in place from one stage to the next); the masked last stage
+  // and every causal stage follow in the general loop (all stages, with nine biased key
+  // subtiles per wave, whose registers would not hold the second copy).
+  const int nfull = score_scalar_dma<BIAS, CAUSAL, KSUB>() ? R / kStage : 0;
+  for (int st = 0; st < nfull; ++st) {
+    if (st + 1 < nst) {
+      vm_wait_barrier<kLoadsPerStage>();
+    } else {
+      vm_wait_barrier<0>();
+    }
+    if (st + 2 < nst) issue(st + 2);
+    stage(st % kBufs, st * kStage, std::false_type{}, std::false_type{});
+  }
+  for (int st = nfull; st < nst; ++st) {
     if (st + 1 < nst) {
       vm_wait_barrier<kLoadsPerStage>();
     } else {
