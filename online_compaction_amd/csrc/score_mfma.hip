@@ -31,8 +31,9 @@ template <int LAYOUT, bool BIAS, bool CAUSAL, int KSUB>
 constexpr int score_rt_unroll() {
   return (KSUB == 9 || (CAUSAL && BIAS && LAYOUT == kSlots)) ? 1 : kStage / 16;
 }
-// whether full stages of rows are loaded from a scalar base and run in a loop of their own (stored
-// row order, and registers to spare: not with nine biased key subtiles per wave)
+// whether full stages of rows are loaded from a scalar base, run in a loop of their own and form
+// their rows' exponent offsets once per wave (stored row order, and registers to spare: not with
+// nine biased key subtiles per wave)
 template <bool BIAS, bool CAUSAL, int KSUB>
 constexpr bool score_scalar_dma() {
   return !CAUSAL && !(BIAS && KSUB == 9);
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   __shared__ __attribute__((aligned(16))) uint8_t qs[kBufs][kStage * 256];
   __shared__ __attribute__((aligned(16))) float lss[kBufs][kStage];
   __shared__ __attribute__((aligned(16))) int32_t pss[CAUSAL ? kBufs : 1][kStage];
+  // a plain stage's exponent offsets, one row per lane, each wave its own copy
+  __shared__ __attribute__((aligned(16))) float nbw[4][kStage];
 
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int i = find_seq(T, t);
@@ -163,13 +166,19 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
   auto stage = [&](int buf, int r0, auto masked, auto causal) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr bool CM = decltype(causal)::value;  // mask element by element (rows near the keys)
+    constexpr bool PLAIN = !MASK && !CM && score_scalar_dma<BIAS, CAUSAL, KSUB>();
+    if constexpr (PLAIN) {
+      // lane l forms row l's offset once for the wave (LDS accesses of one wave complete in order,
+      // so its own reads below see the write)
+      nbw[wave][lane] = __builtin_fmaf(lss[buf][lane], -pl2, kSqOffset);
+    }
 #pragma unroll score_rt_unroll<LAYOUT, BIAS, CAUSAL, KSUB>()
     for (int rt = 0; rt < kStage / 16; ++rt) {
       const int row = rt * 16 + c16;
       bf16x8 a[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) a[ks] = *reinterpret_cast<const bf16x8*>(&qs[buf][swz(row, 4 * ks + g)]);
-      f32x4 nb4 = *reinterpret_cast<const f32x4*>(&lss[buf][rt * 16 + 4 * g]);
+      f32x4 nb4 = *reinterpret_cast<const f32x4*>(PLAIN ? &nbw[wave][rt * 16 + 4 * g] : &lss[buf][rt * 16 + 4 * g]);
       int32_t p4[4] = {0, 0, 0, 0};
       if constexpr (CM) {
         const int4 pv = *reinterpret_cast<const int4*>(&pss[buf][rt * 16 + 4 * g]);
@@ -178,11 +187,13 @@ __global__ __launch_bounds__(kThreads, KVC_SCORE_OCC) void score_mfma(
         p4[2] = pv.z;
         p4[3] = pv.w;
       }
+      if constexpr (!PLAIN) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        nb4[e] = __builtin_fmaf(nb4[e], -pl2, kSqOffset);
-        if constexpr (MASK)
-          if (r0 + rt * 16 + 4 * g + e >= R) nb4[e] = -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+          nb4[e] = __builtin_fmaf(nb4[e], -pl2, kSqOffset);
+          if constexpr (MASK)
+            if (r0 + rt * 16 + 4 * g + e >= R) nb4[e] = -INFINITY;
+        }
       }
       f32x4 acc[kScoreSub];
 #pragma unroll
