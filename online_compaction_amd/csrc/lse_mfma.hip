@@ -170,6 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // four block numbers.
   constexpr bool kSdma = lse_scalar_dma<LAYOUT, BIAS, CAUSAL>();
   const bool sdma = kSdma && (LAYOUT != kPaged || (ko & 3) == 0);
+  const bool blk16 = (ko & 15) == 0;  // paged: a full stage's 64 rows are four whole blocks
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ks_lds = lds_addr(&ks_[0][0]) + wave_s * 4 * 1024;
   uint32_t koff[4];
@@ -190,13 +191,20 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     const int b = st % kLseBufs;
     if (kSdma && sdma && k0 + kStage <= kend) {
       if constexpr (LAYOUT == kPaged) {
-        int e[4];
+        if (blk16) {  // the wave's 16 rows are one block
+          const int64_t blk = __builtin_amdgcn_readfirstlane(idx[sl0[0] + 4 * st]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) e[j] = idx[sl0[j] + 4 * st];
+          for (int j = 0; j < 4; ++j)
+            dma16_s(k + blk * (16 * H * kHeadDim), koff[j], ks_lds + b * (kStage * 256) + j * 1024);
+        } else {
+          int e[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int64_t blk = __builtin_amdgcn_readfirstlane(e[j]);
-          dma16_s(k + blk * (16 * H * kHeadDim), koff[j], ks_lds + b * (kStage * 256) + j * 1024);
+          for (int j = 0; j < 4; ++j) e[j] = idx[sl0[j] + 4 * st];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int64_t blk = __builtin_amdgcn_readfirstlane(e[j]);
+            dma16_s(k + blk * (16 * H * kHeadDim), koff[j], ks_lds + b * (kStage * 256) + j * 1024);
+          }
         }
       } else {
         const uint16_t* base = k + (unit * n_max + ko + k0) * kHeadDim;
@@ -307,7 +315,12 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
               float x = MASK ? __builtin_fmaf(acc[s2][j], c2, kt4[j]) - mref[sub]
                              : __builtin_fmaf(acc[s2][j], c2, -mref[sub]);
               if constexpr (CM) x = j > lim ? -INFINITY : x;
-              sst[sub] += __builtin_amdgcn_exp2f(x);
+              const float e = __builtin_amdgcn_exp2f(x);
+              // unrolled, the first term is the stage sum's start (e >= +0, so 0 + e == e)
+              if constexpr (lse_lazy_unroll<LAYOUT, BIAS, CAUSAL>() == kStage / 16)
+                sst[sub] = (kt == 0 && j == 0) ? e : sst[sub] + e;
+              else
+                sst[sub] += e;
             }
           }
         }
