@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
                                                         float scale, AmCfg C, SeqTable T) {
   constexpr bool kW = MODE == 1 || MODE == 2;  // the pass needs w
   __shared__ __attribute__((aligned(16))) uint8_t Ks[2][kBiasStep * 256];
-  __shared__ float ws_l[2][kBiasThreads];  // w of the step's keys (entries 256 .. 511 unused)
+  __shared__ __attribute__((aligned(16))) float ws_l[2][kBiasStep];  // w of the step's keys
   __shared__ float rsum[4][64];          // row sums of the four key quarters
   __shared__ float xpart[2][2][kBiasStep];  // column partials per step parity and wave parity
   const int t = xcd_remap(blockIdx.x, gridDim.x);
@@ -363,8 +363,8 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
   // Staging of key rows 256 st .. + 255 into buffer buf by LDS-DMA: wave w lands the 1 KB pieces
   // 8 w .. 8 w + 7 (four key rows each), lane L row 4 p + L / 16 of piece p at chunk position
   // L % 16, so it reads chunk (L % 16) ^ (row & 15) of that row (the layout swz reads). The w of
-  // the step's keys comes through a register (0 past m) and is written by land(), which waits for
-  // every load of the step and ends with the barrier.
+  // the step's keys lands beside them; land() waits for every load of the step and ends with the
+  // barrier.
   // (byte offsets from the step's first row; row & 15 repeats every four pieces)
   uint32_t koff[4];
 #pragma unroll
@@ -374,21 +374,20 @@ __global__ __launch_bounds__(kBiasThreads) void am_bias(const uint16_t* __restri
   }
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ks_lds = lds_addr(&Ks[0][0]) + (8 * wave_s) * 1024;
-  float wr = 0.0f;
   auto issue = [&](int st, int buf) {
     const u32x4* src = kc + (int64_t)st * kBiasStep * 16;
 #pragma unroll
     for (int x = 0; x < 8; ++x)
       dma16_s(src, koff[x & 3] + 4096u * (x >> 2), ks_lds + buf * (kBiasStep * 256) + x * 1024);
-    if constexpr (kW) {  // every thread loads (clamped), so the step stays free of branches
-      const int j = st * kBiasStep + (tid & (kBiasStep - 1));
-      const float x = wu[min(j, m - 1)];
-      wr = j < m ? x : 0.0f;
+    if constexpr (kW) {
+      // the step's w by LDS-DMA too (waves 0..3, 64 keys each; clamped to the last kept key past
+      // m, where E is exactly 0): a register load here would make the compiler wait for every
+      // load in flight, the next step's keys included, before this step's arithmetic
+      if (wave < 4) dma4(wu + min(st * kBiasStep + 64 * wave + lane, m - 1), &ws_l[buf][64 * wave]);
     }
   };
   auto land = [&](int buf) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (kW) ws_l[buf][tid] = wr;
     __syncthreads();
   };
   // The kept-logit MFMAs of a step (this wave's 32 rows x its 64-key tile of buffer buf;
