@@ -325,10 +325,12 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
           }
         }
       }
-      float mx = sst[0];
+      // the stage sums are +0 or positive (or inf / NaN after an overflow), so their bit patterns
+      // order like their values and every non-finite one lies above the limit's
+      uint32_t mx = __float_as_uint(sst[0]);
 #pragma unroll
-      for (int sub = 1; sub < kSub; ++sub) mx = fmaxf(mx, sst[sub]);
-      if (__builtin_amdgcn_ballot_w64(!(mx <= kLazyLimit)) == 0) {
+      for (int sub = 1; sub < kSub; ++sub) mx = max(mx, __float_as_uint(sst[sub]));
+      if (__builtin_amdgcn_ballot_w64(mx > __float_as_uint(kLazyLimit)) == 0) {
 #pragma unroll
         for (int sub = 0; sub < kSub; ++sub) ssum[sub] += sst[sub];
         return;
