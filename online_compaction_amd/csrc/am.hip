@@ -1184,25 +1184,29 @@ __global__ __launch_bounds__(kStepThreads) void am_step(float* __restrict__ vc_a
   // lands are pieces 3 w .. 3 w + 2 of the 24 (8 of A, then 16 of B); lane L lands row L / 8 of
   // its piece at position L % 8. A is stored in that order already (a stage is 8 KB further on);
   // for B the lane reads chunk (L % 8) ^ step_sw(row) of its row (a stage is 32 floats on).
-  const u32x4* src[3];
-  int sstep[3];  // u32x4 per stage
+  // The loads are addressed from the stage's start in A or B (scalar) plus per-lane byte offsets
+  // fixed for the whole ring, into scalar LDS destinations.
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t voff[3];
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
     const int piece = 3 * wave + x;
     if (piece < 8) {
-      src[x] = reinterpret_cast<const u32x4*>(A) + piece * 64 + lane;
-      sstep[x] = 512;
+      voff[x] = (piece * 64 + lane) * 16;
     } else {
       const int row = 8 * (piece - 8) + (lane >> 3);
-      src[x] = reinterpret_cast<const u32x4*>(B + (int64_t)row * Np) + ((lane & 7) ^ step_sw(row));
-      sstep[x] = 8;
+      voff[x] = row * Np * 4 + (((lane & 7) ^ step_sw(row)) << 4);
     }
   }
+  const uint32_t ring_lds = lds_addr(sm) + 3 * wave_s * 1024;
   auto issue = [&](int stg) {
     const int st = min(stg, nst - 1);
-    uint8_t* slot = sm + (stg % kStepRing) * kStepSlot;
+    const uint32_t slot = ring_lds + (stg % kStepRing) * kStepSlot;
 #pragma unroll
-    for (int x = 0; x < 3; ++x) dma16(src[x] + st * sstep[x], slot + (3 * wave + x) * 1024);
+    for (int x = 0; x < 3; ++x) {
+      const bool in_a = 3 * wave_s + x < 8;  // (wave-uniform)
+      dma16_s(in_a ? A + (int64_t)st * 2048 : B + st * 32, voff[x], slot + x * 1024);
+    }
   };
   // the epilogue's operands (this lane's 16 entries of X and of Sx; rows past N are zero) are
   // loaded before the ring starts, so their latency hides behind the product (they are older
