@@ -32,11 +32,16 @@ constexpr int lse_lazy_unroll() {
   return (LAYOUT != kSlots && (!BIAS || (LAYOUT == kPaged && !CAUSAL))) ? kStage / 16 : 1;
 }
 
-// whether full stages are loaded from scalar bases and run in a loop of their own (unmasked,
-// without a bias or the causal mask, outside the slot map)
+// whether full stages are loaded from scalar bases (without the causal mask, outside the slot map)
 template <int LAYOUT, bool BIAS, bool CAUSAL>
 constexpr bool lse_scalar_dma() {
-  return !BIAS && !CAUSAL && LAYOUT != kSlots;
+  return !CAUSAL && LAYOUT != kSlots;
+}
+// whether the stages that need no per-key term run in a loop of their own (as above, and without
+// a bias, which every stage adds)
+template <int LAYOUT, bool BIAS, bool CAUSAL>
+constexpr bool lse_plain_loop() {
+  return !BIAS && lse_scalar_dma<LAYOUT, BIAS, CAUSAL>();
 }
 
 // ------------------------------------------------------------------------------------------------
@@ -173,6 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   const bool blk16 = (ko & 15) == 0;  // paged: a full stage's 64 rows are four whole blocks
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t ks_lds = lds_addr(&ks_[0][0]) + wave_s * 4 * 1024;
+  const uint32_t kts_lds = lds_addr(&kts[0][0]) + wave_s * 16 * 4;
   uint32_t koff[4];
   int sl0[4];  // paged: the block-table slot of load j's rows at stage 0 (the same for all its lanes)
 #pragma unroll
@@ -210,6 +216,9 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
         const uint16_t* base = k + (unit * n_max + ko + k0) * kHeadDim;
 #pragma unroll
         for (int j = 0; j < 4; ++j) dma16_s(base, koff[j], ks_lds + b * (kStage * 256) + j * 1024);
+      }
+      if constexpr (BIAS) {
+        if (lane < 16) dma4_s(bias + (int64_t)s * n_max + k0, (wave * 16 + lane) * 4, kts_lds + b * (kStage * 4));
       }
       return;
     }
@@ -382,7 +391,7 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // the stages that need no per-key term run in a loop of their own (one code path, so the sums
   // stay in place from one stage to the next); the masked last stage, and every stage of the
   // other variants, follow in the general loop
-  const int nplain = kSdma ? (kend - kbeg) / kStage : 0;
+  const int nplain = lse_plain_loop<LAYOUT, BIAS, CAUSAL>() ? (kend - kbeg) / kStage : 0;
   for (int st = 0; st < nplain; ++st) {
     if (st + 1 < nst) {
       vm_wait_barrier<kLoadsPerStage>();
