@@ -340,7 +340,7 @@ def serialized_bound_from_profile(launch_ms: float, check_source: bool = True):
 
 
 def measured_ceilings() -> dict:
-    """What the box reaches outside this library, for context beside the spec peaks: a plain
+    """What the machine reaches outside this library, for context beside the spec peaks: a plain
     1 GiB device-to-device copy (torch; read + write bytes per second) and a square bf16 matrix
     product of 8192 (torch.mm on contiguous operands, float32 accumulation). Timed after the
     benchmark's own timed region, a few repetitions each."""
