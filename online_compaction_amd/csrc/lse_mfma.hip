@@ -250,8 +250,9 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // FMA, one exp2 and one add per logit against the current mref) into stage sums; if any lane's
   // stage sum leaves [0, 2^64] (a logit rose more than about 60 above its mref) the whole wave
   // discards them and redoes the stage exactly, moving mref to every new maximum. The wave's
-  // first stage, which has no reference yet, takes the exact form directly. Terms never exceed 2^64 and the largest one seen is at least 1, so the dominant
-  // terms neither overflow nor underflow.
+  // first stage starts mref at one of the lane's own logits of that stage (below), or takes the
+  // exact form directly. Terms never exceed 2^64 and the largest one seen is about 1 or more, so
+  // the dominant terms neither overflow nor underflow.
   float mref[kSub], ssum[kSub];
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
@@ -293,15 +294,27 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     return t4;
   };
   auto row_pos = [&](int sub) -> int { return pls[wave * kPerWave + sub * 16 + c16]; };
-  // The wave's first stage has no reference yet and runs the exact form at once.
+  // The wave's first stage has no reference yet. In a stage without per-key terms whose cheap
+  // form is unrolled, each lane takes the largest of its own first four logits of the stage per
+  // row as its reference and runs the cheap form with the usual check; otherwise the first stage
+  // runs the exact form at once.
   bool fresh = true;
-  auto stage = [&](int buf, int k0, auto masked, auto causal) {
+  auto stage = [&](int buf, int k0, auto masked, auto causal, auto seeded) {
     constexpr bool MASK = decltype(masked)::value;
     constexpr bool CM = decltype(causal)::value;  // mask element by element (rows near the keys)
     // a masked tile is formed in halves, so that the row positions fit beside the accumulators
     constexpr int NH = CM ? 2 : 1, NS = kSub / NH;
-    const bool exact = fresh;
+    constexpr bool kSeed = decltype(seeded)::value;  // (the wave's first stage, unmasked, unrolled)
+    const bool exact = fresh && !kSeed;
     fresh = false;
+    if constexpr (kSeed) {  // the references from the stage's first tile (its MFMAs formed once more below)
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) {
+        f32x4 acc[1];
+        tile_acc(buf, 0, sub, acc);
+        mref[sub] = fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])) * c2;
+      }
+    }
     if (!exact) {
       float sst[kSub];
 #pragma unroll
@@ -392,15 +405,23 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
   // stay in place from one stage to the next); the masked last stage, and every stage of the
   // other variants, follow in the general loop
   const int nplain = lse_plain_loop<LAYOUT, BIAS, CAUSAL>() ? (kend - kbeg) / kStage : 0;
-  for (int st = 0; st < nplain; ++st) {
+  auto plain_step = [&](int st, auto seeded) {
     if (st + 1 < nst) {
       vm_wait_barrier<kLoadsPerStage>();
     } else {
       vm_wait_barrier<0>();
     }
     if (st + 2 < nst) issue(st + 2);
-    stage(st % kLseBufs, kbeg + st * kStage, std::false_type{}, std::false_type{});
+    stage(st % kLseBufs, kbeg + st * kStage, std::false_type{}, std::false_type{}, seeded);
+  };
+  int st0 = 0;
+  if constexpr (lse_lazy_unroll<LAYOUT, BIAS, CAUSAL>() == kStage / 16) {
+    if (nplain > 0) {  // the wave's first stage, seeded (every wave starts at the chunk's first key)
+      plain_step(0, std::true_type{});
+      st0 = 1;
+    }
   }
+  for (int st = st0; st < nplain; ++st) plain_step(st, std::false_type{});
   for (int st = nplain; st < nst; ++st) {
     if (st + 1 < nst) {
       vm_wait_barrier<kLoadsPerStage>();
@@ -412,16 +433,16 @@ __global__ __launch_bounds__(kThreads, 2) void lse_partials_mfma(
     if constexpr (CAUSAL) {
       if (wpmax < k0) continue;  // no row of the wave sees a key of this stage
       if (wpmin < k0 + kStage - 1) {
-        stage(st % kLseBufs, k0, std::true_type{}, std::true_type{});
+        stage(st % kLseBufs, k0, std::true_type{}, std::true_type{}, std::false_type{});
         continue;
       }
     }
     // the bias, dead slots and the keys past the chunk enter through the per-key term; other
     // stages skip it
     if (BIAS || LAYOUT == kSlots || k0 + kStage > kend) {
-      stage(st % kLseBufs, k0, std::true_type{}, std::false_type{});
+      stage(st % kLseBufs, k0, std::true_type{}, std::false_type{}, std::false_type{});
     } else {
-      stage(st % kLseBufs, k0, std::false_type{}, std::false_type{});
+      stage(st % kLseBufs, k0, std::false_type{}, std::false_type{}, std::false_type{});
     }
   }
 
